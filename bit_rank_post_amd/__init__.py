@@ -1,0 +1,148 @@
+"""Python binding of libtileq.so, the MI355X (gfx950) TileQ MoE forward.
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+behind the C ABI (include/tileq.h).  Device buffers and streams come from
+PyTorch tensors (``tensor.data_ptr()``, ``torch.cuda.current_stream()``).
+The library must be built first (``python -m bit_rank_post_amd.build``);
+loading fails loudly if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtileq.so")
+
+TQ_F16, TQ_BF16, TQ_F32 = 0, 1, 2
+TQ_SINGLE, TQ_SWIGLU = 0, 1
+P_SINGLE, P_GATE, P_UP, P_DOWN = 0, 0, 1, 2
+STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHIP",
+          5: "TQ_EUNSUPPORTED", 6: "TQ_ESTATE"}
+EXPORTS = ["tq_layer_create", "tq_upload_proj", "tq_upload_shared_expert",
+           "tq_workspace_size", "tq_forward", "tq_layer_destroy", "tq_last_error",
+           "tq_abi_version", "tq_layer_set_path", "tq_debug_route", "tq_debug_dequant"]
+
+
+class TileQError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {text}")
+        self.status = status
+        self.text = text
+
+
+class ProjDesc(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("tile_of_expert", ctypes.POINTER(ctypes.c_int32)),
+                ("U", ctypes.c_void_p), ("sigma", ctypes.c_void_p), ("V", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libtileq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} missing: run python -m bit_rank_post_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.tq_layer_create.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(vp)]
+        L.tq_upload_proj.argtypes = [vp, i32, ctypes.POINTER(ProjDesc), vp]
+        L.tq_upload_shared_expert.argtypes = [vp, i32, vp, vp, vp, vp]
+        L.tq_workspace_size.argtypes = [vp, i32, i32, ctypes.POINTER(sz)]
+        L.tq_forward.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, vp, sz, vp]
+        L.tq_layer_destroy.argtypes = [vp]
+        L.tq_last_error.restype = ctypes.c_char_p
+        L.tq_abi_version.restype = i32
+        L.tq_layer_set_path.argtypes = [vp, i32]
+        L.tq_debug_route.argtypes = [vp, i32, vp, i32, i32, vp, sz] + [vp] * 7 + [vp]
+        L.tq_debug_dequant.argtypes = [vp, i32, i32, vp, vp]
+        for name in EXPORTS:
+            if name not in ("tq_last_error", "tq_abi_version"):
+                getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise TileQError(fn, status, lib().tq_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+
+
+class Layer:
+    """An uploaded MoE layer (owns its device weights)."""
+
+    def __init__(self, kind: int, act: int, d_model: int, d_ff: int, K: int):
+        h = ctypes.c_void_p()
+        _check("tq_layer_create", lib().tq_layer_create(kind, act, d_model, d_ff, K,
+                                                        ctypes.byref(h)))
+        self.h = h
+        self.kind, self.act, self.d_model, self.d_ff, self.K = kind, act, d_model, d_ff, K
+
+    def upload_proj(self, which, *, K, M, N, d_in, d_out, rank, group, tile_of_expert,
+                    U, sigma, V, codes, scales, zeros, stream=None):
+        """tile_of_expert: host sequence of K ints; the rest device tensors."""
+        tiles = (ctypes.c_int32 * len(tile_of_expert))(*[int(t) for t in tile_of_expert])
+        d = ProjDesc(K, M, N, d_in, d_out, rank, group,
+                     ctypes.cast(tiles, ctypes.POINTER(ctypes.c_int32)),
+                     _ptr(U), _ptr(sigma), _ptr(V), _ptr(codes), _ptr(scales), _ptr(zeros))
+        _check("tq_upload_proj", lib().tq_upload_proj(self.h, which, ctypes.byref(d),
+                                                      _stream(stream)))
+
+    def upload_shared_expert(self, d_ff_shared, wg, wu, wd, stream=None):
+        _check("tq_upload_shared_expert", lib().tq_upload_shared_expert(
+            self.h, d_ff_shared, _ptr(wg), _ptr(wu), _ptr(wd), _stream(stream)))
+
+    def set_path(self, path: int):
+        _check("tq_layer_set_path", lib().tq_layer_set_path(self.h, path))
+
+    def workspace_size(self, T: int, topk: int) -> int:
+        n = ctypes.c_size_t()
+        _check("tq_workspace_size", lib().tq_workspace_size(self.h, T, topk, ctypes.byref(n)))
+        return n.value
+
+    def forward(self, x, T, ids, gates, topk, y, y_dtype, ws, stream=None):
+        _check("tq_forward", lib().tq_forward(self.h, _ptr(x), T, _ptr(ids), _ptr(gates), topk,
+                                              _ptr(y), y_dtype, _ptr(ws),
+                                              ws.numel() * ws.element_size(), _stream(stream)))
+
+    def debug_route(self, which, ids, T, topk, ws, cnt, off, perm, inv, col_off, col_tok,
+                    slot2col, stream=None):
+        _check("tq_debug_route", lib().tq_debug_route(
+            self.h, which, _ptr(ids), T, topk, _ptr(ws), ws.numel() * ws.element_size(),
+            _ptr(cnt), _ptr(off), _ptr(perm), _ptr(inv), _ptr(col_off), _ptr(col_tok),
+            _ptr(slot2col), _stream(stream)))
+
+    def debug_dequant(self, which, expert, w_out, stream=None):
+        _check("tq_debug_dequant", lib().tq_debug_dequant(self.h, which, expert, _ptr(w_out),
+                                                          _stream(stream)))
+
+    def close(self):
+        if getattr(self, "h", None) is not None and self.h.value:
+            lib().tq_layer_destroy(self.h)
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass

@@ -1,0 +1,704 @@
+// Host runtime of the TileQ MoE forward: the C ABI of include/tileq.h.
+//
+// Validation happens on the host before any device work; forward only
+// enqueues kernels on the caller's stream (no allocation, no sync, no read
+// back) and picks the decode or prefill kernels from (T, topk, K) alone.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "tileq.h"
+#include "tq_internal.h"
+
+using namespace tq;
+
+namespace {
+
+thread_local std::string g_err;
+
+tq_status fail(tq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIPCHK(expr)                                                          \
+  do {                                                                        \
+    hipError_t e_ = (expr);                                                   \
+    if (e_ != hipSuccess)                                                     \
+      return fail(TQ_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));    \
+  } while (0)
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct ProjHost {
+  bool uploaded = false;
+  ProjDev dev{};
+  std::vector<int> tile;
+};
+
+void free_proj(ProjHost& p) {
+  if (!p.uploaded) return;
+  (void)hipFree(p.dev.codes);
+  (void)hipFree(p.dev.sz);
+  (void)hipFree(p.dev.U);
+  (void)hipFree(p.dev.Vt);
+  (void)hipFree(p.dev.sigma);
+  (void)hipFree(p.dev.m_of);
+  (void)hipFree(p.dev.n_of);
+  p = ProjHost{};
+}
+
+}  // namespace
+
+struct tq_layer {
+  tq_kind kind;
+  tq_dtype act;
+  int d_model, d_ff, K;
+  ProjHost proj[3];
+  SharedDev shared{};
+  int path_override = 0;
+};
+
+namespace {
+
+int nproj(const tq_layer* L) { return L->kind == TQ_SINGLE ? 1 : 3; }
+
+void proj_dims(const tq_layer* L, int which, int* d_in, int* d_out) {
+  if (L->kind == TQ_SINGLE || which != TQ_P_DOWN) {
+    *d_in = L->d_model;
+    *d_out = L->d_ff;
+  } else {
+    *d_in = L->d_ff;
+    *d_out = L->d_model;
+  }
+}
+
+// ---- workspace plan --------------------------------------------------------
+struct Plan {
+  int T, k, S, path, bm_gemm, rt_col, max_tiles_gemm;
+  size_t flags, cnt, off, perm, inv, tile_gemm, tile_colx, colmask, cntw, rank;
+  size_t col_off[2], col_tok[2], slot2col[2], tile_col[2];
+  size_t P[3];
+  int nsplit[3];
+  int rows_cap;
+  size_t ex, hamax, h, dres, hs, ys;
+  size_t total;
+};
+
+int choose_path(const tq_layer* L, int T, int k) {
+  if (L->path_override == 1 || L->path_override == 2) return L->path_override;
+  const long S = (long)T * k;
+  return (S <= 16L * L->K) ? 1 : 2;
+}
+
+int choose_nsplit(int path, long rows, int d_in) {
+  if (path != 1) return 1;
+  const int nsteps = d_in >> 5;
+  const long tiles = (rows + 15) / 16 + 8;
+  long want = (512 + tiles - 1) / tiles;
+  want = std::max(1L, std::min(want, (long)std::max(1, nsteps / 8)));
+  return (int)want;
+}
+
+Plan make_plan(const tq_layer* L, int T, int k, int path) {
+  Plan p{};
+  p.T = T;
+  p.k = k;
+  p.S = T * k;
+  p.path = path;
+  p.bm_gemm = (path == 1) ? 16 : 128;
+  p.rt_col = (path == 1) ? 16 : 64;
+  p.max_tiles_gemm = (p.S + p.bm_gemm - 1) / p.bm_gemm + L->K;
+  const int S = p.S, K = L->K;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  p.flags = take(256);
+  p.cnt = take(sizeof(int) * K);
+  p.off = take(sizeof(int) * (K + 1));
+  p.perm = take(sizeof(int) * S);
+  p.inv = take(sizeof(int) * S);
+  p.tile_gemm = take(sizeof(int) * (K + 1));
+  p.tile_colx = take(sizeof(int) * (K + 1));
+  p.colmask = take(sizeof(int) * std::max(T, 1));
+  p.cntw = take(sizeof(int) * (size_t)((S + 63) / 64) * K);
+  p.rank = take(sizeof(int) * S);
+  const int ncol = (L->kind == TQ_SINGLE) ? 1 : 2;
+  for (int c = 0; c < 2; ++c) {
+    const int N = (c < ncol && L->proj[c].uploaded) ? L->proj[c].dev.N : 1;
+    p.col_off[c] = take(sizeof(int) * (N + 1));
+    p.col_tok[c] = take(sizeof(int) * S);
+    p.slot2col[c] = take(sizeof(int) * S);
+    p.tile_col[c] = take(sizeof(int) * (N + 1));
+  }
+  p.rows_cap = S;
+  for (int q = 0; q < 3; ++q) {
+    p.nsplit[q] = 1;
+    p.P[q] = 0;
+    if (q >= nproj(L)) continue;
+    const ProjDev& d = L->proj[q].dev;
+    p.nsplit[q] = choose_nsplit(path, S, d.d_in);
+    if (d.r_pad > 0) p.P[q] = take((size_t)p.nsplit[q] * S * d.r_pad * sizeof(float));
+  }
+  const bool bf = (L->act == TQ_BF16);
+  p.ex = take(sizeof(int) * (bf ? std::max(T, 1) : 1));
+  p.hamax = take(sizeof(unsigned) * ((bf && L->kind == TQ_SWIGLU) ? S : 1));
+  p.h = take(L->kind == TQ_SWIGLU ? (size_t)S * L->d_ff * 2 : 0);
+  int d_in_last, d_out_last;
+  proj_dims(L, nproj(L) - 1, &d_in_last, &d_out_last);
+  p.dres = take((size_t)S * d_out_last * sizeof(float));
+  if (L->shared.d_ff > 0) {
+    p.hs = take((size_t)T * L->shared.d_ff * 2);
+    p.ys = take((size_t)T * L->d_model * sizeof(float));
+  }
+  p.total = o;
+  return p;
+}
+
+tq_status check_ready(const tq_layer* L) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  for (int q = 0; q < nproj(L); ++q)
+    if (!L->proj[q].uploaded)
+      return fail(TQ_ESTATE, "projection %d has not been uploaded", q);
+  return TQ_OK;
+}
+
+tq_status check_tokens(int T, int topk) {
+  if (T < 0) return fail(TQ_ESHAPE, "T = %d < 0", T);
+  if (topk < 1 || topk > 32) return fail(TQ_ESHAPE, "topk = %d outside [1, 32]", topk);
+  if ((long)T * topk > (1L << 20)) return fail(TQ_ESHAPE, "T*topk = %ld > 2^20", (long)T * topk);
+  return TQ_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+void fill_route(const tq_layer* L, const Plan& p, const int* ids, void* ws, RouteArgs& r) {
+  r = RouteArgs{};
+  r.ids = ids;
+  r.T = p.T;
+  r.k = p.k;
+  r.S = p.S;
+  r.K = L->K;
+  r.ncol = (L->kind == TQ_SINGLE) ? 1 : 2;
+  for (int c = 0; c < r.ncol; ++c) {
+    r.n_of[c] = L->proj[c].dev.n_of;
+    r.N[c] = L->proj[c].dev.N;
+    r.col_off[c] = at<int>(ws, p.col_off[c]);
+    r.col_tok[c] = at<int>(ws, p.col_tok[c]);
+    r.slot2col[c] = at<int>(ws, p.slot2col[c]);
+    r.tile_col[c] = at<int>(ws, p.tile_col[c]);
+  }
+  r.bm_gemm = p.bm_gemm;
+  r.rt_col = p.rt_col;
+  r.flags = at<int>(ws, p.flags);
+  r.cnt = at<int>(ws, p.cnt);
+  r.off = at<int>(ws, p.off);
+  r.perm = at<int>(ws, p.perm);
+  r.inv = at<int>(ws, p.inv);
+  r.tile_gemm = at<int>(ws, p.tile_gemm);
+  r.tile_colx = at<int>(ws, p.tile_colx);
+  r.cntw = at<int>(ws, p.cntw);
+  r.rank = at<int>(ws, p.rank);
+  r.colmask = at<int>(ws, p.colmask);
+  if (L->act == TQ_BF16 && L->kind == TQ_SWIGLU) {
+    r.zero_init = at<unsigned>(ws, p.hamax);
+    r.zero_n = p.S;
+  }
+}
+
+ColArgs col_args_x(const tq_layer* L, const Plan& p, int c, const void* x, void* ws) {
+  const ProjDev& d = L->proj[c].dev;
+  ColArgs a{};
+  a.A = x;
+  a.lda = d.d_in;
+  a.seg_off = at<int>(ws, p.col_off[c]);
+  a.tile_off = at<int>(ws, p.tile_col[c]);
+  a.row_src = at<int>(ws, p.col_tok[c]);
+  a.seg_vblk = nullptr;
+  a.nseg = d.N;
+  a.Vt = d.Vt;
+  a.r_pad = d.r_pad;
+  a.d_in = d.d_in;
+  a.nsplit = p.nsplit[c];
+  a.steps_per_split = ((d.d_in >> 5) + p.nsplit[c] - 1) / p.nsplit[c];
+  a.P = at<float>(ws, p.P[c]);
+  a.rows_cap = p.rows_cap;
+  return a;
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+const char* tq_last_error(void) { return g_err.c_str(); }
+
+int32_t tq_abi_version(void) { return 1; }
+
+tq_status tq_layer_create(tq_kind kind, tq_dtype act, int32_t d_model, int32_t d_ff, int32_t K,
+                          tq_layer** out) {
+  if (!out) return fail(TQ_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (kind != TQ_SINGLE && kind != TQ_SWIGLU) return fail(TQ_EINVAL, "unknown kind %d", (int)kind);
+  if (act != TQ_F16 && act != TQ_BF16) return fail(TQ_EINVAL, "act must be TQ_F16 or TQ_BF16");
+  if (d_model <= 0 || d_ff <= 0 || K <= 0)
+    return fail(TQ_ESHAPE, "d_model, d_ff and K must be positive");
+  if (K > 256) return fail(TQ_ESHAPE, "K = %d > 256", K);
+  tq_layer* L = new (std::nothrow) tq_layer();
+  if (!L) return fail(TQ_ENOMEM, "host allocation failed");
+  L->kind = kind;
+  L->act = act;
+  L->d_model = d_model;
+  L->d_ff = d_ff;
+  L->K = K;
+  *out = L;
+  return TQ_OK;
+}
+
+tq_status tq_layer_set_path(tq_layer* L, int32_t path) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (path < 0 || path > 2) return fail(TQ_EINVAL, "path must be 0, 1 or 2");
+  L->path_override = path;
+  return TQ_OK;
+}
+
+tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void* stream) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (!d) return fail(TQ_EINVAL, "descriptor is NULL");
+  if (which < 0 || which >= nproj(L)) return fail(TQ_EINVAL, "projection %d not in this layer", which);
+  int d_in, d_out;
+  proj_dims(L, which, &d_in, &d_out);
+  if (d->K != L->K) return fail(TQ_ESHAPE, "K = %d, layer has %d experts", d->K, L->K);
+  if (d->d_in != d_in || d->d_out != d_out)
+    return fail(TQ_ESHAPE, "projection %d must be %d -> %d, got %d -> %d", which, d_in, d_out,
+                d->d_in, d->d_out);
+  if (d->M <= 0 || d->N <= 0) return fail(TQ_ESHAPE, "grid %d x %d", d->M, d->N);
+  if ((long)d->M * d->N > 1024) return fail(TQ_ESHAPE, "M*N = %ld > 1024", (long)d->M * d->N);
+  if (d->K > d->M * d->N) return fail(TQ_ESHAPE, "K = %d > M*N = %d", d->K, d->M * d->N);
+  if (d->N > 32) return fail(TQ_ESHAPE, "N = %d > 32", d->N);
+  if (d_in % 128) return fail(TQ_ESHAPE, "d_in = %d not a multiple of 128", d_in);
+  if (d_out % 16) return fail(TQ_ESHAPE, "d_out = %d not a multiple of 16", d_out);
+  if (d->group <= 0 || d->group % 32 || d_in % d->group)
+    return fail(TQ_ESHAPE, "group = %d must be a multiple of 32 dividing d_in", d->group);
+  if (d->rank < 0 || d->rank > 128) return fail(TQ_ESHAPE, "rank = %d outside [0, 128]", d->rank);
+  if (!d->tile_of_expert) return fail(TQ_EINVAL, "tile_of_expert is NULL");
+  if (!d->codes || !d->scales || !d->zeros) return fail(TQ_EINVAL, "codes/scales/zeros NULL");
+  if (d->rank > 0 && (!d->U || !d->V || !d->sigma)) return fail(TQ_EINVAL, "U/V/sigma NULL");
+  std::vector<int> seen(d->M * d->N, -1);
+  for (int e = 0; e < d->K; ++e) {
+    const int t = d->tile_of_expert[e];
+    if (t < 0 || t >= d->M * d->N)
+      return fail(TQ_EINVAL, "expert %d: tile %d outside [0, %d)", e, t, d->M * d->N);
+    if (seen[t] >= 0)
+      return fail(TQ_EINVAL, "experts %d and %d share tile %d (the map must be injective)",
+                  seen[t], e, t);
+    seen[t] = e;
+  }
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  ProjHost np;
+  ProjDev& v = np.dev;
+  v.K = d->K;
+  v.M = d->M;
+  v.N = d->N;
+  v.d_in = d_in;
+  v.d_out = d_out;
+  v.rank = d->rank;
+  v.r_pad = (d->rank + 31) / 32 * 32;
+  v.group = d->group;
+  v.ng = d_in / d->group;
+  v.nrb = d_out / 16;
+  v.nsteps = d_in / 32;
+  np.tile.assign(d->tile_of_expert, d->tile_of_expert + d->K);
+  std::vector<int> m_of(d->K), n_of(d->K);
+  for (int e = 0; e < d->K; ++e) {
+    m_of[e] = np.tile[e] / d->N;
+    n_of[e] = np.tile[e] % d->N;
+  }
+  const size_t ncode = (size_t)d->K * d_out * (d_in / 16);
+  const size_t nsz = (size_t)d->K * d_out * v.ng;
+  int* bad = nullptr;
+  auto cleanup = [&]() {
+    (void)hipFree(v.codes);
+    (void)hipFree(v.sz);
+    (void)hipFree(v.U);
+    (void)hipFree(v.Vt);
+    (void)hipFree(v.sigma);
+    (void)hipFree(v.m_of);
+    (void)hipFree(v.n_of);
+    (void)hipFree(bad);
+  };
+#define UPCHK(expr)                                                            \
+  do {                                                                         \
+    hipError_t e_ = (expr);                                                    \
+    if (e_ != hipSuccess) {                                                    \
+      cleanup();                                                               \
+      return fail(e_ == hipErrorOutOfMemory ? TQ_ENOMEM : TQ_EHIP, "%s failed: %s", #expr, \
+                  hipGetErrorString(e_));                                      \
+    }                                                                          \
+  } while (0)
+  UPCHK(hipMalloc(&v.codes, ncode * 4));
+  UPCHK(hipMalloc(&v.sz, nsz * 4));
+  UPCHK(hipMalloc(&v.m_of, sizeof(int) * d->K));
+  UPCHK(hipMalloc(&v.n_of, sizeof(int) * d->K));
+  UPCHK(hipMalloc(&bad, sizeof(int)));
+  if (v.r_pad > 0) {
+    UPCHK(hipMalloc(&v.U, (size_t)d->M * d_out * v.r_pad * 2));
+    UPCHK(hipMalloc(&v.Vt, (size_t)d->N * v.r_pad * d_in * 2));
+    UPCHK(hipMalloc(&v.sigma, (size_t)v.r_pad * 4));
+  }
+  UPCHK(hipMemsetAsync(bad, 0, sizeof(int), s));
+  launch_repack_codes(d->codes, v.codes, d->K, d_out, d_in, s);
+  launch_pack_sz(d->scales, d->zeros, v.sz, d->K, d_out, v.ng, bad, s);
+  UPCHK(hipGetLastError());
+  if (v.r_pad > 0) {
+    launch_pad_u(d->U, v.U, d->M * d_out, d->rank, v.r_pad, s);
+    launch_transpose_v(d->V, v.Vt, d->N, d_in, d->rank, v.r_pad, s);
+    UPCHK(hipGetLastError());
+    UPCHK(hipMemsetAsync(v.sigma, 0, (size_t)v.r_pad * 4, s));
+    UPCHK(hipMemcpyAsync(v.sigma, d->sigma, (size_t)d->rank * 4, hipMemcpyDeviceToDevice, s));
+  }
+  UPCHK(hipMemcpyAsync(v.m_of, m_of.data(), sizeof(int) * d->K, hipMemcpyHostToDevice, s));
+  UPCHK(hipMemcpyAsync(v.n_of, n_of.data(), sizeof(int) * d->K, hipMemcpyHostToDevice, s));
+  int hbad = 0;
+  UPCHK(hipMemcpyAsync(&hbad, bad, sizeof(int), hipMemcpyDeviceToHost, s));
+  UPCHK(hipStreamSynchronize(s));
+  (void)hipFree(bad);
+  bad = nullptr;
+  if (hbad) {
+    cleanup();
+    return fail(TQ_EINVAL, "%s%s", (hbad & 1) ? "scale not finite or |s| >= 1024; " : "",
+                (hbad & 2) ? "zero point not an integer in [0, 3]" : "");
+  }
+#undef UPCHK
+  free_proj(L->proj[which]);
+  np.uploaded = true;
+  L->proj[which] = np;
+  return TQ_OK;
+}
+
+tq_status tq_upload_shared_expert(tq_layer* L, int32_t d_ff_shared, const void* wg, const void* wu,
+                                  const void* wd, void* stream) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (L->kind != TQ_SWIGLU) return fail(TQ_EINVAL, "shared expert needs a SWIGLU layer");
+  if (L->act != TQ_F16) return fail(TQ_EUNSUPPORTED, "shared expert supported for f16 layers only");
+  if (!wg || !wu || !wd) return fail(TQ_EINVAL, "weights NULL");
+  if (d_ff_shared <= 0 || d_ff_shared % 128)
+    return fail(TQ_ESHAPE, "d_ff_shared = %d must be a positive multiple of 128", d_ff_shared);
+  if (L->d_model % 128) return fail(TQ_ESHAPE, "d_model must be a multiple of 128");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t n = (size_t)d_ff_shared * L->d_model * 2;
+  SharedDev sd{};
+  sd.d_ff = d_ff_shared;
+  HIPCHK(hipMalloc(&sd.wg, n));
+  HIPCHK(hipMalloc(&sd.wu, n));
+  HIPCHK(hipMalloc(&sd.wd, n));
+  HIPCHK(hipMemcpyAsync(sd.wg, wg, n, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(sd.wu, wu, n, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(sd.wd, wd, n, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipStreamSynchronize(s));
+  if (L->shared.d_ff) {
+    (void)hipFree(L->shared.wg);
+    (void)hipFree(L->shared.wu);
+    (void)hipFree(L->shared.wd);
+  }
+  L->shared = sd;
+  return TQ_OK;
+}
+
+tq_status tq_workspace_size(const tq_layer* L, int32_t T, int32_t topk, size_t* bytes) {
+  tq_status st = check_ready(L);
+  if (st != TQ_OK) return st;
+  if (!bytes) return fail(TQ_EINVAL, "bytes is NULL");
+  st = check_tokens(T, topk);
+  if (st != TQ_OK) return st;
+  *bytes = std::max(make_plan(L, T, topk, 1).total, make_plan(L, T, topk, 2).total);
+  return TQ_OK;
+}
+
+tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t* topk_ids,
+                     const float* topk_w, int32_t topk, void* y, tq_dtype y_dtype, void* ws,
+                     size_t ws_bytes, void* stream) {
+  tq_status st = check_ready(L);
+  if (st != TQ_OK) return st;
+  st = check_tokens(T, topk);
+  if (st != TQ_OK) return st;
+  if (y_dtype != TQ_F16 && y_dtype != TQ_BF16 && y_dtype != TQ_F32)
+    return fail(TQ_EINVAL, "unknown y_dtype %d", (int)y_dtype);
+  if (T == 0) return TQ_OK;
+  if (!x || !topk_ids || !topk_w || !y || !ws) return fail(TQ_EINVAL, "NULL buffer");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(TQ_EINVAL, "ws not 256-byte aligned");
+  const int path = choose_path(L, T, topk);
+  const Plan p = make_plan(L, T, topk, path);
+  size_t need = 0;
+  tq_workspace_size(L, T, topk, &need);
+  if (ws_bytes < need) return fail(TQ_ESHAPE, "ws_bytes = %zu < %zu", ws_bytes, need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Act act = (L->act == TQ_F16) ? ACT_F16 : ACT_BF16;
+  const bool bf = (act == ACT_BF16);
+
+  RouteArgs ra;
+  fill_route(L, p, topk_ids, ws, ra);
+  launch_route(ra, s);
+  int* ex = nullptr;
+  if (bf) {
+    ex = at<int>(ws, p.ex);
+    launch_row_exponent(x, T, L->d_model, ex, s);
+  }
+
+  const int K = L->K;
+  int d_in_last, d_out_last;
+  proj_dims(L, nproj(L) - 1, &d_in_last, &d_out_last);
+  float* dres = at<float>(ws, p.dres);
+  const int max_col_tiles = (p.S + p.rt_col - 1) / p.rt_col + 32 + K;
+
+  if (L->kind == TQ_SINGLE) {
+    const ProjDev& d = L->proj[0].dev;
+    if (d.r_pad > 0) {
+      ColArgs ca = col_args_x(L, p, 0, x, ws);
+      launch_colproj(&ca, 1, p.rt_col, max_col_tiles, act, s);
+    }
+    GemmArgs ga{};
+    ga.K = K;
+    ga.d_in = d.d_in;
+    ga.d_out = d.d_out;
+    ga.topk = topk;
+    ga.S = p.S;
+    ga.A = x;
+    ga.gather = 1;
+    ga.perm = at<int>(ws, p.perm);
+    ga.off = at<int>(ws, p.off);
+    ga.cnt = at<int>(ws, p.cnt);
+    ga.tile_off = at<int>(ws, p.tile_gemm);
+    ga.ex = ex;
+    ga.p[0] = d;
+    ga.dres = dres;
+    ga.gates = topk_w;
+    launch_gemm(ga, MODE_RES, path, act, p.max_tiles_gemm, s);
+    CombineArgs cb{};
+    cb.T = T;
+    cb.topk = topk;
+    cb.K = K;
+    cb.d_out = d.d_out;
+    cb.M = d.M;
+    cb.r_pad = d.r_pad;
+    cb.ids = topk_ids;
+    cb.gates = topk_w;
+    cb.inv = at<int>(ws, p.inv);
+    cb.prow = at<int>(ws, p.slot2col[0]);
+    cb.m_of = d.m_of;
+    cb.P = d.r_pad ? at<float>(ws, p.P[0]) : nullptr;
+    cb.nsplit = p.nsplit[0];
+    cb.rows_cap = p.rows_cap;
+    cb.sigma = d.sigma;
+    cb.U = d.U;
+    cb.dres = dres;
+    cb.ys = nullptr;
+    cb.y = y;
+    cb.y_dtype = (int)y_dtype;
+    launch_combine(cb, act, s);
+  } else {
+    const ProjDev& dg = L->proj[0].dev;
+    const ProjDev& du = L->proj[1].dev;
+    const ProjDev& dd = L->proj[2].dev;
+    // column stage of gate and up (unique (column, token) pairs)
+    {
+      ColArgs ca[2];
+      int n = 0;
+      if (dg.r_pad > 0) ca[n++] = col_args_x(L, p, 0, x, ws);
+      if (du.r_pad > 0) ca[n++] = col_args_x(L, p, 1, x, ws);
+      if (n) launch_colproj(ca, n, p.rt_col, max_col_tiles, act, s);
+    }
+    void* h = at<void>(ws, p.h);
+    unsigned* hamax = bf ? at<unsigned>(ws, p.hamax) : nullptr;
+    {
+      GemmArgs ga{};
+      ga.K = K;
+      ga.d_in = dg.d_in;
+      ga.d_out = dg.d_out;
+      ga.topk = topk;
+      ga.S = p.S;
+      ga.A = x;
+      ga.gather = 1;
+      ga.perm = at<int>(ws, p.perm);
+      ga.off = at<int>(ws, p.off);
+      ga.cnt = at<int>(ws, p.cnt);
+      ga.tile_off = at<int>(ws, p.tile_gemm);
+      ga.ex = ex;
+      ga.p[0] = dg;
+      ga.p[1] = du;
+      for (int c = 0; c < 2; ++c) {
+        ga.P[c] = L->proj[c].dev.r_pad ? at<float>(ws, p.P[c]) : nullptr;
+        ga.nsplit[c] = p.nsplit[c];
+        ga.rows_cap[c] = p.rows_cap;
+        ga.slot2col[c] = at<int>(ws, p.slot2col[c]);
+      }
+      ga.h = h;
+      ga.hamax_out = hamax;
+      launch_gemm(ga, MODE_GATEUP, path, act, p.max_tiles_gemm, s);
+    }
+    // column stage of down: one row per slot (h differs per expert)
+    if (dd.r_pad > 0) {
+      ColArgs ca{};
+      ca.A = h;
+      ca.lda = dd.d_in;
+      ca.seg_off = at<int>(ws, p.off);
+      ca.tile_off = at<int>(ws, p.tile_colx);
+      ca.row_src = nullptr;
+      ca.seg_vblk = dd.n_of;
+      ca.nseg = K;
+      ca.Vt = dd.Vt;
+      ca.r_pad = dd.r_pad;
+      ca.d_in = dd.d_in;
+      ca.nsplit = p.nsplit[2];
+      ca.steps_per_split = ((dd.d_in >> 5) + p.nsplit[2] - 1) / p.nsplit[2];
+      ca.P = at<float>(ws, p.P[2]);
+      ca.rows_cap = p.rows_cap;
+      launch_colproj(&ca, 1, p.rt_col, max_col_tiles, act, s);
+    }
+    float* ys = nullptr;
+    if (L->shared.d_ff > 0) {
+      DenseArgs da{};
+      da.T = T;
+      da.d_in = L->d_model;
+      da.d_out = L->shared.d_ff;
+      da.X = x;
+      da.W0 = L->shared.wg;
+      da.W1 = L->shared.wu;
+      da.out_h = at<void>(ws, p.hs);
+      launch_dense(da, 1, s);
+      DenseArgs db{};
+      db.T = T;
+      db.d_in = L->shared.d_ff;
+      db.d_out = L->d_model;
+      db.X = at<void>(ws, p.hs);
+      db.W0 = L->shared.wd;
+      db.out_f = at<float>(ws, p.ys);
+      launch_dense(db, 0, s);
+      ys = at<float>(ws, p.ys);
+    }
+    {
+      GemmArgs ga{};
+      ga.K = K;
+      ga.d_in = dd.d_in;
+      ga.d_out = dd.d_out;
+      ga.topk = topk;
+      ga.S = p.S;
+      ga.A = h;
+      ga.gather = 0;
+      ga.perm = at<int>(ws, p.perm);
+      ga.off = at<int>(ws, p.off);
+      ga.cnt = at<int>(ws, p.cnt);
+      ga.tile_off = at<int>(ws, p.tile_gemm);
+      ga.hamax = hamax;
+      ga.p[0] = dd;
+      ga.dres = dres;
+      ga.gates = topk_w;
+      launch_gemm(ga, MODE_RES, path, act, p.max_tiles_gemm, s);
+    }
+    CombineArgs cb{};
+    cb.T = T;
+    cb.topk = topk;
+    cb.K = K;
+    cb.d_out = dd.d_out;
+    cb.M = dd.M;
+    cb.r_pad = dd.r_pad;
+    cb.ids = topk_ids;
+    cb.gates = topk_w;
+    cb.inv = at<int>(ws, p.inv);
+    cb.prow = at<int>(ws, p.inv);
+    cb.m_of = dd.m_of;
+    cb.P = dd.r_pad ? at<float>(ws, p.P[2]) : nullptr;
+    cb.nsplit = p.nsplit[2];
+    cb.rows_cap = p.rows_cap;
+    cb.sigma = dd.sigma;
+    cb.U = dd.U;
+    cb.dres = dres;
+    cb.ys = ys;
+    cb.y = y;
+    cb.y_dtype = (int)y_dtype;
+    launch_combine(cb, act, s);
+  }
+  HIPCHK(hipGetLastError());
+  return TQ_OK;
+}
+
+tq_status tq_layer_destroy(tq_layer* L) {
+  if (!L) return TQ_OK;
+  (void)hipDeviceSynchronize();
+  for (int q = 0; q < 3; ++q) free_proj(L->proj[q]);
+  if (L->shared.d_ff) {
+    (void)hipFree(L->shared.wg);
+    (void)hipFree(L->shared.wu);
+    (void)hipFree(L->shared.wd);
+  }
+  delete L;
+  return TQ_OK;
+}
+
+tq_status tq_debug_route(const tq_layer* L, int32_t which, const int32_t* topk_ids, int32_t T,
+                         int32_t topk, void* ws, size_t ws_bytes, int32_t* cnt, int32_t* off,
+                         int32_t* perm, int32_t* inv, int32_t* col_off, int32_t* col_tok,
+                         int32_t* slot2col, void* stream) {
+  tq_status st = check_ready(L);
+  if (st != TQ_OK) return st;
+  st = check_tokens(T, topk);
+  if (st != TQ_OK) return st;
+  if (T == 0) return fail(TQ_ESHAPE, "T = 0");
+  const int ncol = (L->kind == TQ_SINGLE) ? 1 : 2;
+  if (which < 0 || which >= ncol) return fail(TQ_EINVAL, "which = %d has no column list", which);
+  if (!topk_ids || !ws || !cnt || !off || !perm || !inv || !col_off || !col_tok || !slot2col)
+    return fail(TQ_EINVAL, "NULL buffer");
+  size_t need = 0;
+  tq_workspace_size(L, T, topk, &need);
+  if (ws_bytes < need) return fail(TQ_ESHAPE, "ws_bytes = %zu < %zu", ws_bytes, need);
+  const Plan p = make_plan(L, T, topk, choose_path(L, T, topk));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  RouteArgs ra;
+  fill_route(L, p, topk_ids, ws, ra);
+  launch_route(ra, s);
+  HIPCHK(hipGetLastError());
+  const size_t S = (size_t)p.S;
+  const int N = L->proj[which].dev.N;
+  HIPCHK(hipMemcpyAsync(cnt, at<int>(ws, p.cnt), sizeof(int) * L->K, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(off, at<int>(ws, p.off), sizeof(int) * (L->K + 1), hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(perm, at<int>(ws, p.perm), sizeof(int) * S, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(inv, at<int>(ws, p.inv), sizeof(int) * S, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(col_off, at<int>(ws, p.col_off[which]), sizeof(int) * (N + 1),
+                        hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(col_tok, at<int>(ws, p.col_tok[which]), sizeof(int) * S,
+                        hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(slot2col, at<int>(ws, p.slot2col[which]), sizeof(int) * S,
+                        hipMemcpyDeviceToDevice, s));
+  return TQ_OK;
+}
+
+tq_status tq_debug_dequant(const tq_layer* L, int32_t which, int32_t expert, void* w_out,
+                           void* stream) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (which < 0 || which >= nproj(L)) return fail(TQ_EINVAL, "projection %d not in layer", which);
+  if (!L->proj[which].uploaded) return fail(TQ_ESTATE, "projection %d not uploaded", which);
+  if (expert < 0 || expert >= L->K) return fail(TQ_EINVAL, "expert %d outside [0, %d)", expert, L->K);
+  if (!w_out) return fail(TQ_EINVAL, "w_out is NULL");
+  launch_debug_dequant(L->proj[which].dev, expert, w_out, reinterpret_cast<hipStream_t>(stream));
+  HIPCHK(hipGetLastError());
+  return TQ_OK;
+}
+
+}  // extern "C"

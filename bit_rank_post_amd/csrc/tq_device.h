@@ -1,0 +1,175 @@
+// Device-side helpers for the gfx950 kernels: vector types, MFMA wrappers,
+// the in-register 2-bit unpack and exact dequantization, reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+typedef _Float16 half_t;
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// C[16x16] += A[16x32] * B[32x16].  Operand layout (wave64): lane l holds
+// A[row l%16][k 8*(l/16) .. +7], B[k 8*(l/16) .. +7][col l%16]; the result
+// lane l holds C[row 4*(l/16)+v][col l%16], v = 0..3.
+__device__ __forceinline__ f32x4 mfma16(const half8v& a, const half8v& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8v& a, const bf16x8v& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T> struct Vec8;
+template <> struct Vec8<half_t> { typedef half8v type; };
+template <> struct Vec8<__bf16> { typedef bf16x8v type; };
+
+__device__ __forceinline__ half8v as_half8(u32x4 v) { return __builtin_bit_cast(half8v, v); }
+__device__ __forceinline__ u32x4 as_u32x4(half8v v) { return __builtin_bit_cast(u32x4, v); }
+
+// ---- 2-bit unpack ---------------------------------------------------------
+// A dword holds the 16 codes of two consecutive MFMA k-steps of one lane
+// (8 inputs per step).  For step b (0 or 1) and input j = 2v + h of the step,
+// the code sits at bit 16*h + pos(b, v) with pos(0, .) = {4, 6, 8, 0} and
+// pos(1, .) = {10, 12, 14, 2}.  Each output register is a packed fp16 pair
+// whose halves are 1 + q*c (exponent bits of 1.0 OR-ed over the code placed in
+// the mantissa), with class c = 1/64, 1/16 or 1/4 given by the mantissa
+// position.  One and-or per pair; two shifts per dword.
+//   out[0..3] : step b=0, classes {1/64, 1/16, 1/4, 1/64}
+//   out[4..7] : step b=1, classes {1/64, 1/16, 1/4, 1/16}
+__device__ __forceinline__ void unpack16(uint32_t D, uint32_t out[8]) {
+  const uint32_t M4 = 0x00300030u, M6 = 0x00C000C0u, M8 = 0x03000300u;
+  const uint32_t ONE = 0x3C003C00u;
+  const uint32_t E = D >> 6, F = D << 4;
+  out[0] = (D & M4) | ONE;
+  out[1] = (D & M6) | ONE;
+  out[2] = (D & M8) | ONE;
+  out[3] = (F & M4) | ONE;
+  out[4] = (E & M4) | ONE;
+  out[5] = (E & M6) | ONE;
+  out[6] = (E & M8) | ONE;
+  out[7] = (F & M6) | ONE;
+}
+
+// Per (row, group) constants turning 1 + q*c into the dequantized weight
+// RND_f16(s * (q - z)):  ((1 + q c) - (1 + z c)) is exact (Sterbenz), equals
+// (q - z) c, and the product with s/c (exact: power-of-two scaling, |s| < 1024)
+// rounds the exact value (q - z) s once.
+struct DeqConst {
+  half2v nz64, nz16, nz4;   // -(1 + z/64), -(1 + z/16), -(1 + z/4)
+  half2v s64, s16, s4;      // 64 s, 16 s, 4 s
+};
+
+__device__ __forceinline__ DeqConst deq_const(uint32_t szw) {
+  const half_t s = __builtin_bit_cast(half_t, (uint16_t)(szw & 0xFFFFu));
+  const half_t z = __builtin_bit_cast(half_t, (uint16_t)(szw >> 16));
+  const float sf = (float)s, zf = (float)z;
+  DeqConst c;
+  const half_t a = (half_t)(-(1.0f + zf * 0.015625f));
+  const half_t b = (half_t)(-(1.0f + zf * 0.0625f));
+  const half_t d = (half_t)(-(1.0f + zf * 0.25f));
+  const half_t e = (half_t)(sf * 64.0f), f = (half_t)(sf * 16.0f), g = (half_t)(sf * 4.0f);
+  c.nz64 = half2v{a, a};
+  c.nz16 = half2v{b, b};
+  c.nz4 = half2v{d, d};
+  c.s64 = half2v{e, e};
+  c.s16 = half2v{f, f};
+  c.s4 = half2v{g, g};
+  return c;
+}
+
+__device__ __forceinline__ uint32_t deq_pair(uint32_t m, half2v nz, half2v sc) {
+  half2v v = __builtin_bit_cast(half2v, m);
+  v = v + nz;        // exact
+  v = v * sc;        // one rounding of (q - z) s
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Dequantized A operands of the two k-steps held by dword D.
+__device__ __forceinline__ void deq_dword(uint32_t D, const DeqConst& c0, const DeqConst& c1,
+                                          half8v& a0, half8v& a1) {
+  uint32_t m[8];
+  unpack16(D, m);
+  u32x4 r0, r1;
+  r0[0] = deq_pair(m[0], c0.nz64, c0.s64);
+  r0[1] = deq_pair(m[1], c0.nz16, c0.s16);
+  r0[2] = deq_pair(m[2], c0.nz4, c0.s4);
+  r0[3] = deq_pair(m[3], c0.nz64, c0.s64);
+  r1[0] = deq_pair(m[4], c1.nz64, c1.s64);
+  r1[1] = deq_pair(m[5], c1.nz16, c1.s16);
+  r1[2] = deq_pair(m[6], c1.nz4, c1.s4);
+  r1[3] = deq_pair(m[7], c1.nz16, c1.s16);
+  a0 = as_half8(r0);
+  a1 = as_half8(r1);
+}
+
+// ---- reductions -----------------------------------------------------------
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan over the block (blockDim.x multiple of 64, <= 1024).
+// s_w: shared int[17].  Returns the exclusive prefix; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_w, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  int inc = wave_incl_scan_i(v, lane);
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < nw; ++i) {
+      int t = s_w[i];
+      s_w[i] = run;
+      run += t;
+    }
+    s_w[16] = run;
+  }
+  __syncthreads();
+  int res = s_w[w] + inc - v;
+  *total = s_w[16];
+  __syncthreads();
+  return res;
+}
+
+// Segment of `tile` in a tile prefix toff[0..nseg] (toff[0] = 0,
+// non-decreasing): the number of entries toff[1..nseg] <= tile, or -1 when
+// tile >= toff[nseg].  Called by every thread; uses *s_res.
+__device__ __forceinline__ int find_segment(const int* toff, int nseg, int tile, int* s_res) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int c = 0;
+    for (int i = lane + 1; i <= nseg; i += 64) c += (toff[i] <= tile) ? 1 : 0;
+    c = wave_sum_i(c);
+    if (lane == 0) *s_res = (tile < toff[nseg]) ? c : -1;
+  }
+  __syncthreads();
+  return *s_res;
+}
+
+// fp32 -> storage type (round to nearest even)
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ half_t from_f32<half_t>(float v) { return (half_t)v; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
+
+template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }
+
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
+
+}  // namespace tq

@@ -1,0 +1,159 @@
+// Internal declarations shared by the host runtime (tileq_host.cpp) and the
+// gfx950 kernels (*.hip).  Plain structs of device pointers and sizes; no
+// torch, no HIP types beyond hipStream_t.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq {
+
+enum Act { ACT_F16 = 0, ACT_BF16 = 1 };
+
+// Device image of one uploaded projection.
+//   codes : repacked 2-bit codes, per expert nrb row blocks of 16 rows; within a
+//           row block, step groups of 8 MFMA k-steps (32 inputs each, the last
+//           group may hold 4); a group stores, for each of the 64 lanes, the
+//           lane's codes of those steps contiguously (16 B, or 8 B in a 4-step
+//           tail).  Lane l owns row 16*rb + l%16 and inputs 32*step + 8*(l/16)
+//           + 0..7 of every step (the A-operand layout of
+//           v_mfma_f32_16x16x32_f16).  Bit positions inside a dword: see
+//           unpack16() in tq_device.h.
+//   sz    : [K][nrb][ng][16] u32, scale bits | zero bits << 16 (fp16 each)
+//   U     : [M*d_out][r_pad] act, r zero-padded to a multiple of 32
+//   Vt    : [N][r_pad][d_in] act (V_n transposed, zero-padded rows)
+//   sigma : [r_pad] f32, zero padded
+struct ProjDev {
+  int K, M, N, d_in, d_out, rank, r_pad, group, ng, nrb, nsteps;
+  uint32_t* codes;
+  uint32_t* sz;
+  void* U;
+  void* Vt;
+  float* sigma;
+  int* m_of;
+  int* n_of;
+};
+
+struct SharedDev {
+  int d_ff;       // 0: no shared expert
+  void* wg;       // [d_ff][d_model] f16
+  void* wu;
+  void* wd;       // [d_model][d_ff] f16
+};
+
+// ---- routing --------------------------------------------------------------
+struct RouteArgs {
+  const int* ids;
+  int T, k, S, K;
+  int ncol;                      // column lists to build (1 single, 2 gate+up)
+  const int* n_of[2];
+  int N[2];
+  int bm_gemm;                   // GEMM slot-tile height
+  int rt_col;                    // column-stage row-tile height
+  int* flags;                    // [0] = dropped slot count
+  int* cnt;                      // [K]
+  int* off;                      // [K+1]
+  int* perm;                     // [S]
+  int* inv;                      // [S]
+  int* tile_gemm;                // [K+1] prefix of ceil(cnt/bm_gemm)
+  int* tile_colx;                // [K+1] prefix of ceil(cnt/rt_col) (down column stage)
+  int* col_off[2];               // [N+1]
+  int* col_tok[2];               // [S]
+  int* slot2col[2];              // [S]
+  int* tile_col[2];              // [N+1] prefix of ceil(col count/rt_col)
+  int* cntw;                     // scratch [ceil(S/64)][K]
+  int* rank;                     // scratch [S]
+  int* colmask;                  // scratch [T]
+  unsigned* zero_init;           // optional region zeroed by the kernel
+  int zero_n;
+};
+void launch_route(const RouteArgs& a, hipStream_t s);
+
+// ---- column stage: P[split][row][r] = sum_{k in split} a_row[k] V_n[k][r] --
+struct ColArgs {
+  const void* A;                 // activations, row stride lda
+  int lda;
+  const int* seg_off;            // [nseg+1] row offsets
+  const int* tile_off;           // [nseg+1] tile prefix (rt rows per tile)
+  const int* row_src;            // row -> activation row (nullptr: identity)
+  const int* seg_vblk;           // segment -> V block (nullptr: segment id)
+  int nseg;
+  const void* Vt;
+  int r_pad, d_in;
+  int nsplit, steps_per_split;
+  float* P;
+  int rows_cap;                  // rows per split slab
+};
+void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
+                    hipStream_t s);
+
+// ---- residual grouped GEMM (+ low-rank K-extension, SwiGLU) ---------------
+enum GemmMode { MODE_GATEUP = 0, MODE_RES = 1 };
+struct GemmArgs {
+  int K, d_in, d_out, topk, S;
+  const void* A;                 // x [T][d_in] (gather by token) or h [S][d_in]
+  int gather;                    // 1: row of slot = token of perm[pos]; 0: pos
+  const int* perm;
+  const int* off;
+  const int* cnt;
+  const int* tile_off;           // [K+1]
+  const int* ex;                 // per-activation-row exponent (bf16) or nullptr
+  const unsigned* hamax;         // per-pos |h| max bits (bf16 down) or nullptr
+  // projections (1 for RES, 2 for GATEUP)
+  ProjDev p[2];
+  // low-rank extension (GATEUP): P partials of each projection
+  const float* P[2];
+  int nsplit[2];
+  int rows_cap[2];
+  const int* slot2col[2];
+  // outputs
+  void* h;                       // GATEUP: [S][d_out] act
+  unsigned* hamax_out;           // GATEUP bf16: atomic max of |h| per pos
+  float* dres;                   // RES: [S][d_out] f32 (gate weight applied)
+  const float* gates;            // RES: topk weights [T*topk]
+};
+void launch_gemm(const GemmArgs& a, GemmMode mode, int path, Act act, int max_tiles,
+                 hipStream_t s);
+
+// ---- combine: y_t = sum_j dres[inv(t,j)] + U_cat S_t (+ shared) ------------
+struct CombineArgs {
+  int T, topk, K, d_out, M, r_pad;
+  const int* ids;
+  const float* gates;
+  const int* inv;
+  const int* prow;               // slot -> row of P (inv for down, slot2col for single)
+  const int* m_of;
+  const float* P;
+  int nsplit, rows_cap;
+  const float* sigma;
+  const void* U;
+  const float* dres;
+  const float* ys;               // shared expert output [T][d_out] f32 or nullptr
+  void* y;
+  int y_dtype;                   // 0 f16, 1 bf16, 2 f32
+};
+void launch_combine(const CombineArgs& a, Act act, hipStream_t s);
+
+// ---- dense fp16 shared expert --------------------------------------------
+struct DenseArgs {
+  int T, d_in, d_out;
+  const void* X;                 // [T][d_in] f16
+  const void* W0;                // [d_out][d_in] f16
+  const void* W1;                // second weight (dual SwiGLU) or nullptr
+  void* out_h;                   // dual: [T][d_out] f16
+  float* out_f;                  // single: [T][d_out] f32
+};
+void launch_dense(const DenseArgs& a, int dual, hipStream_t s);
+
+// ---- upload-time kernels --------------------------------------------------
+void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, int d_in,
+                         hipStream_t s);
+void launch_pack_sz(const uint16_t* scales, const uint16_t* zeros, uint32_t* dst,
+                    int K, int d_out, int ng, int* bad, hipStream_t s);
+void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStream_t s);
+void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_pad,
+                        hipStream_t s);
+void launch_debug_dequant(const ProjDev& p, int expert, void* w_out, hipStream_t s);
+void launch_row_exponent(const void* X, int rows, int cols, int* ex, hipStream_t s);
+
+}  // namespace tq

@@ -1,0 +1,186 @@
+// Upload-time kernels: re-lay the stored projection (section 2.1 step 5 of the
+// "TileQ" technical summary: shared factors U, Sigma, V and the quantized
+// per-expert residual) into the layouts the forward kernels read.
+#include "tq_device.h"
+
+namespace tq {
+
+// Bit position inside a dword of input j = 2v + h of step b (see unpack16).
+__device__ __forceinline__ int code_bit(int b, int v, int h) {
+  const int pos0[4] = {4, 6, 8, 0};
+  const int pos1[4] = {10, 12, 14, 2};
+  return 16 * h + (b ? pos1[v] : pos0[v]);
+}
+
+// One thread per output dword of the repacked layout.
+__global__ void repack_codes_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                    int K, int d_out, int d_in) {
+  const int nsteps = d_in >> 5;
+  const size_t words_per_expert = (size_t)d_out * (d_in >> 4);
+  const size_t total = words_per_expert * K;
+  const size_t words_per_rb = (size_t)nsteps * 32;     // 64 lanes * nsteps * 2 B / 4 B
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int e = (int)(idx / words_per_expert);
+    const size_t rem = idx - (size_t)e * words_per_expert;
+    const int rb = (int)(rem / words_per_rb);
+    const int w = (int)(rem - (size_t)rb * words_per_rb);     // dword within row block
+    const int sg = w >> 8;                                    // 256 dwords per full group
+    const int gs = min(8, nsteps - (sg << 3));
+    const int wi = w - (sg << 8);
+    const int dpl = gs >> 1;                                  // dwords per lane
+    const int lane = wi / dpl, d = wi - lane * dpl;
+    const int row = rb * 16 + (lane & 15);
+    const uint32_t* srow = src + (size_t)e * words_per_expert + (size_t)row * (d_in >> 4);
+    uint32_t out = 0u;
+    for (int b = 0; b < 2; ++b) {
+      const int step = (sg << 3) + 2 * d + b;
+      for (int j = 0; j < 8; ++j) {
+        const int k = step * 32 + 8 * (lane >> 4) + j;
+        const uint32_t q = (srow[k >> 4] >> (2 * (k & 15))) & 3u;
+        out |= q << code_bit(b, j >> 1, j & 1);
+      }
+    }
+    dst[idx] = out;
+  }
+}
+
+void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, int d_in,
+                         hipStream_t s) {
+  const size_t total = (size_t)K * d_out * (d_in >> 4);
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(repack_codes_kernel, dim3(blocks), dim3(256), 0, s, src, dst, K, d_out, d_in);
+}
+
+// scales/zeros [K][d_out][ng] -> [K][nrb][ng][16] (s | z << 16); flags
+// non-finite or |s| >= 1024 scales and non-integer or out-of-range zeros.
+__global__ void pack_sz_kernel(const uint16_t* __restrict__ sc, const uint16_t* __restrict__ zr,
+                               uint32_t* __restrict__ dst, int K, int d_out, int ng, int* bad) {
+  const size_t total = (size_t)K * d_out * ng;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int g = (int)(idx % ng);
+    const size_t eo = idx / ng;
+    const int o = (int)(eo % d_out), e = (int)(eo / d_out);
+    const uint16_t sb = sc[idx], zb = zr[idx];
+    const float s = (float)__builtin_bit_cast(half_t, sb);
+    const float z = (float)__builtin_bit_cast(half_t, zb);
+    const bool ok_s = (fabsf(s) < 1024.0f);                  // false for inf/nan too
+    const bool ok_z = (z == rintf(z)) && z >= 0.0f && z <= 3.0f;
+    if (!ok_s) atomicOr(bad, 1);
+    if (!ok_z) atomicOr(bad, 2);
+    const size_t out = (((size_t)e * (d_out >> 4) + (o >> 4)) * ng + g) * 16 + (o & 15);
+    dst[out] = (uint32_t)sb | ((uint32_t)zb << 16);
+  }
+}
+
+void launch_pack_sz(const uint16_t* scales, const uint16_t* zeros, uint32_t* dst, int K,
+                    int d_out, int ng, int* bad, hipStream_t s) {
+  const size_t total = (size_t)K * d_out * ng;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_sz_kernel, dim3(blocks), dim3(256), 0, s, scales, zeros, dst, K,
+                     d_out, ng, bad);
+}
+
+// U [rows][r] -> [rows][r_pad] zero padded (2-byte elements)
+__global__ void pad_u_kernel(const uint16_t* __restrict__ U, uint16_t* __restrict__ dst,
+                             int rows, int r, int r_pad) {
+  const size_t total = (size_t)rows * r_pad;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % r_pad);
+    const size_t row = i / r_pad;
+    dst[i] = (c < r) ? U[row * r + c] : (uint16_t)0;
+  }
+}
+
+void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStream_t s) {
+  const size_t total = (size_t)rows * r_pad;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(pad_u_kernel, dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(U), reinterpret_cast<uint16_t*>(dst),
+                     rows, r, r_pad);
+}
+
+// V [N*d_in][r] -> Vt [N][r_pad][d_in]
+__global__ void transpose_v_kernel(const uint16_t* __restrict__ V, uint16_t* __restrict__ dst,
+                                   int N, int d_in, int r, int r_pad) {
+  const size_t total = (size_t)N * r_pad * d_in;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int k = (int)(i % d_in);
+    const size_t nc = i / d_in;
+    const int c = (int)(nc % r_pad), n = (int)(nc / r_pad);
+    dst[i] = (c < r) ? V[((size_t)n * d_in + k) * r + c] : (uint16_t)0;
+  }
+}
+
+void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_pad,
+                        hipStream_t s) {
+  const size_t total = (size_t)N * r_pad * d_in;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(transpose_v_kernel, dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(V), reinterpret_cast<uint16_t*>(dst), N,
+                     d_in, r, r_pad);
+}
+
+// Dequantized weights of one expert through the forward's own unpack path:
+// one wave per (row block, step group); lane l writes its 8 inputs per step.
+__global__ void debug_dequant_kernel(ProjDev p, int e, half_t* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int nsg = (p.nsteps + 7) >> 3;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= p.nrb * nsg) return;
+  const int rb = item / nsg, sg = item - rb * nsg;
+  const int gs = min(8, p.nsteps - (sg << 3));
+  const size_t codes_per_expert = (size_t)p.d_out * (p.d_in >> 4);
+  const uint32_t* base = p.codes + (size_t)e * codes_per_expert +
+                         (((size_t)rb * p.nsteps + (sg << 3)) * 64 + lane * gs) / 2;
+  const int row = rb * 16 + (lane & 15);
+  const int gsteps = p.group >> 5;
+  for (int d = 0; d < (gs >> 1); ++d) {
+    const int s0 = (sg << 3) + 2 * d;
+    const size_t zb = (((size_t)e * p.nrb + rb) * p.ng) * 16 + (lane & 15);
+    const DeqConst c0 = deq_const(p.sz[zb + (size_t)(s0 / gsteps) * 16]);
+    const DeqConst c1 = deq_const(p.sz[zb + (size_t)((s0 + 1) / gsteps) * 16]);
+    half8v a0, a1;
+    deq_dword(base[d], c0, c1, a0, a1);
+    half_t* out = w + (size_t)row * p.d_in + s0 * 32 + 8 * (lane >> 4);
+    *reinterpret_cast<half8v*>(out) = a0;
+    *reinterpret_cast<half8v*>(out + 32) = a1;
+  }
+}
+
+void launch_debug_dequant(const ProjDev& p, int expert, void* w_out, hipStream_t s) {
+  const int nsg = (p.nsteps + 7) >> 3;
+  const int items = p.nrb * nsg;
+  hipLaunchKernelGGL(debug_dequant_kernel, dim3((items + 3) / 4), dim3(256), 0, s, p, expert,
+                     reinterpret_cast<half_t*>(w_out));
+}
+
+// Per-row exponent E with max|x_row| * 2^-E in [2^14, 2^15) (0 for a zero
+// row): bfloat16 rows scaled by 2^-E are exact in fp16 down to 2^-15 of the
+// row maximum.
+__global__ void row_exponent_kernel(const uint16_t* __restrict__ X, int rows, int cols,
+                                    int* __restrict__ ex) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float m = 0.f;
+  for (int c = lane; c < cols; c += 64)
+    m = fmaxf(m, fabsf(__uint_as_float((uint32_t)X[(size_t)row * cols + c] << 16)));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) {
+    int e2 = 0;
+    if (m > 0.f) frexpf(m, &e2);
+    ex[row] = (m > 0.f) ? e2 - 15 : 0;
+  }
+}
+
+void launch_row_exponent(const void* X, int rows, int cols, int* ex, hipStream_t s) {
+  hipLaunchKernelGGL(row_exponent_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(X), rows, cols, ex);
+}
+
+}  // namespace tq

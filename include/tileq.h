@@ -1,0 +1,186 @@
+/*
+ * tileq.h -- C ABI of the MI355X (gfx950) TileQ MoE expert forward.
+ *
+ * Method: "TileQ: Efficient Low-Rank Quantization of Mixture-of-Experts with
+ * 2D Tiling" (gist.science technical summary).
+ *   - Section 2.1, step 4: the K experts of a projection are tiles of one
+ *     block matrix W_big on an M x N grid.
+ *   - Section 2.1, step 5, and "Key Technical Insight": W_big is factored
+ *     once, U Sigma V^T; the experts of grid row m share the left (output
+ *     space) block U_m, the experts of grid column n share the right (input
+ *     space) block V_n, and each expert keeps a quantized residual.  So the
+ *     weight of expert e at tile (m, n) is  W_e = U_m Sigma V_n^T + R_e.
+ *   - Section 2.2 ("Efficient Fused Sparse Low-Rank Inference"): the forward
+ *     takes the whole token batch and the routing weights, projects onto a
+ *     shared factor once, applies routing weights in rank space through an
+ *     in-place accumulation buffer, and multiplies by the other shared factor
+ *     in one batched product.
+ *
+ * Two calls carry the method: tq_upload_proj() (the tile map, the shared
+ * factors and the packed 2-bit residual of one projection) and tq_forward()
+ * (token activations plus top-k routing).  Everything else is set-up,
+ * workspace sizing and test hooks.
+ *
+ * Conventions for every call:
+ *   - Every call returns a tq_status and never aborts across the ABI; the text
+ *     of the last non-OK status of the calling thread is tq_last_error().
+ *   - "DEVICE" pointers are device memory of the current HIP device; "HOST"
+ *     pointers are read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Storage formats: f16 = IEEE binary16, bf16 = bfloat16 (both 2 bytes);
+ *     integers little endian.
+ */
+#ifndef TILEQ_H
+#define TILEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tq_layer tq_layer; /* opaque; owns the uploaded device weights */
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* invalid argument value (map, pointer, dtype, ...) */
+  TQ_ESHAPE = 2,        /* shapes inconsistent or unsupported sizes          */
+  TQ_ENOMEM = 3,        /* device allocation failed                          */
+  TQ_EHIP = 4,          /* a HIP runtime call failed (text in last_error)    */
+  TQ_EUNSUPPORTED = 5,  /* valid request this library does not implement     */
+  TQ_ESTATE = 6         /* call order (e.g. forward before every upload)     */
+} tq_status;
+
+typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2 } tq_dtype;
+
+/* TQ_SINGLE: one projection  y_t = sum_j g_tj W_e x_t.
+ * TQ_SWIGLU: gate, up and down projections,
+ *            h = RND_act(silu(W_gate,e x) * (W_up,e x)),
+ *            y_t = sum_j g_tj W_down,e h_tj  (+ optional dense shared expert). */
+typedef enum { TQ_SINGLE = 0, TQ_SWIGLU = 1 } tq_kind;
+
+/* projection selectors */
+#define TQ_P_SINGLE 0
+#define TQ_P_GATE 0
+#define TQ_P_UP 1
+#define TQ_P_DOWN 2
+
+/* One projection as stored after the offline quantization of section 2.1.
+ * Sizes: K experts on an M x N grid (K <= M*N <= 1024, K <= 256), d_in and
+ * d_out the projection's input and output widths, rank r >= 0, residual group
+ * size G along d_in.  Requirements: d_in % 128 == 0, d_out % 16 == 0,
+ * G % 32 == 0, d_in % G == 0, r <= 128.
+ *   tile_of_expert HOST   int32 [K]: tile index m*N + n of each expert;
+ *                         must be injective and in [0, M*N) (empty tiles allowed).
+ *   U      DEVICE act   [M*d_out][r] row-major; block m = rows m*d_out ...
+ *   sigma  DEVICE f32   [r] (the diagonal of Sigma; any order accepted)
+ *   V      DEVICE act   [N*d_in][r]  row-major; block n = rows n*d_in ...
+ *   codes  DEVICE u32   [K][d_out][d_in/16]: 2-bit code of input i at bits
+ *                       2*(i%16) .. 2*(i%16)+1 of word i/16
+ *   scales DEVICE f16   [K][d_out][d_in/G]   finite, |s| < 1024
+ *   zeros  DEVICE f16   [K][d_out][d_in/G]   integer zero points 0..3
+ * The residual weight is R_e[o][i] = s[e][o][i/G] * (q[e][o][i] - z[e][o][i/G]).
+ * U, V may be NULL when r == 0. */
+typedef struct {
+  int32_t K, M, N, d_in, d_out, rank, group;
+  const int32_t *tile_of_expert;
+  const void *U;
+  const float *sigma;
+  const void *V;
+  const uint32_t *codes;
+  const uint16_t *scales;
+  const uint16_t *zeros;
+} tq_proj_desc;
+
+/* Create an empty layer.  act: TQ_F16 or TQ_BF16, the dtype of activations, of
+ * U and V and of the SwiGLU intermediate.  SINGLE: d_model = d_in,
+ * d_ff = d_out of the one projection.  SWIGLU: gate/up are d_model -> d_ff,
+ * down is d_ff -> d_model.  No device memory is touched.
+ * Errors: TQ_EINVAL (bad kind/dtype, out == NULL), TQ_ESHAPE (sizes <= 0). */
+tq_status tq_layer_create(tq_kind kind, tq_dtype act, int32_t d_model, int32_t d_ff,
+                          int32_t K, tq_layer **out);
+
+/* Call (1): upload one projection (section 2.1 step 5: "the resulting shared
+ * low-rank factors (U, V, Sigma) are stored, and the residual error for each
+ * expert is quantized").  The map is validated on the host before any device
+ * work; the device arrays are copied (and re-laid-out) into library-owned
+ * memory on `stream`; scales/zeros are validated on the device, after which
+ * the call synchronizes `stream` and returns.  The caller may free its arrays
+ * when the call returns.  Re-uploading a projection replaces it.
+ * Errors: TQ_EINVAL (non-injective or out-of-range map, NULL pointers,
+ * non-integer zero or out-of-range scale), TQ_ESHAPE (sizes inconsistent with
+ * the layer or the requirements above), TQ_ENOMEM, TQ_EHIP. */
+tq_status tq_upload_proj(tq_layer *L, int32_t which, const tq_proj_desc *d, void *stream);
+
+/* Optional dense shared expert, added to every token with weight 1 (SWIGLU
+ * layers with act = TQ_F16 only): wg, wu DEVICE f16 [d_ff_shared][d_model],
+ * wd DEVICE f16 [d_model][d_ff_shared]; d_ff_shared % 128 == 0.  Copied like
+ * tq_upload_proj.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EUNSUPPORTED, TQ_ENOMEM, TQ_EHIP. */
+tq_status tq_upload_shared_expert(tq_layer *L, int32_t d_ff_shared, const void *wg,
+                                  const void *wu, const void *wd, void *stream);
+
+/* Bytes of device workspace tq_forward needs for T tokens with top-k routing
+ * (valid for both execution paths).  Errors: TQ_ESHAPE (T < 0, topk < 1 or
+ * T*topk > 2^20), TQ_ESTATE (a projection not uploaded yet). */
+tq_status tq_workspace_size(const tq_layer *L, int32_t T, int32_t topk, size_t *bytes);
+
+/* Call (2): the forward (section 2.2) for T tokens.
+ *   x        DEVICE act [T][d_in of the first projection]
+ *   topk_ids DEVICE int32 [T][topk] expert ids; an id outside [0, K) makes
+ *            that slot contribute nothing and is counted (see below)
+ *   topk_w   DEVICE f32 [T][topk] routing weights, applied as given
+ *   y        DEVICE y_dtype [T][d_out of the last projection]; written once,
+ *            rounded to nearest-even from fp32 accumulation
+ *   ws       DEVICE workspace of at least tq_workspace_size() bytes, 256-byte
+ *            aligned.  After the call, ((int32_t*)ws)[0] holds the number of
+ *            slots whose id was outside [0, K).
+ * Only enqueues work on `stream`: no allocation, no synchronization, no read
+ * back, so it can be captured in a HIP graph.  T == 0 is a no-op.  Buffers may
+ * not overlap.  Concurrent calls must use distinct workspaces.
+ * Errors (all checked before any launch): TQ_EINVAL (NULL pointers, y_dtype),
+ * TQ_ESHAPE (T, topk, ws_bytes too small), TQ_ESTATE, TQ_EHIP (launch failure). */
+tq_status tq_forward(const tq_layer *L, const void *x, int32_t T, const int32_t *topk_ids,
+                     const float *topk_w, int32_t topk, void *y, tq_dtype y_dtype,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Free the layer and its device memory (synchronizes the device first).
+ * NULL is accepted. */
+tq_status tq_layer_destroy(tq_layer *L);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char *tq_last_error(void);
+
+/* ABI version (increments on incompatible changes). */
+int32_t tq_abi_version(void);
+
+/* ---- test hooks (exported and documented as such) ---------------------- */
+
+/* Execution path: 0 = automatic (chosen on the host from T, topk and K),
+ * 1 = decode kernels (16-slot tiles), 2 = prefill kernels (large tiles). */
+tq_status tq_layer_set_path(tq_layer *L, int32_t path);
+
+/* Run only the routing/grouping step of tq_forward (the expert grouping of
+ * section 2.2 that replaces per-token sparse dispatch) and copy its lists to
+ * caller buffers (all DEVICE int32):
+ *   cnt[K], off[K+1], perm[T*topk] (slots t*topk+j ordered by (expert, slot);
+ *   entries past off[K] are unspecified), inv[T*topk] (position of each slot,
+ *   -1 if dropped), col_off[N+1], col_tok[T*topk], slot2col[T*topk]: the
+ *   unique (column n of the expert, token t) pairs of projection `which`
+ *   sorted by (n, t), and each slot's index into them (-1 if dropped).
+ * `which` must be TQ_P_GATE/TQ_P_UP (SWIGLU) or TQ_P_SINGLE.  ws as tq_forward. */
+tq_status tq_debug_route(const tq_layer *L, int32_t which, const int32_t *topk_ids, int32_t T,
+                         int32_t topk, void *ws, size_t ws_bytes, int32_t *cnt, int32_t *off,
+                         int32_t *perm, int32_t *inv, int32_t *col_off, int32_t *col_tok,
+                         int32_t *slot2col, void *stream);
+
+/* Write the dequantized residual weights of one expert exactly as the forward
+ * multiplies them: w_out DEVICE f16 [d_out][d_in],
+ * w[o][i] = RND_f16(s * (q - z)) (one rounding of the exact product). */
+tq_status tq_debug_dequant(const tq_layer *L, int32_t which, int32_t expert, void *w_out,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TILEQ_H */

@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer work is compared bit for bit (routing lists; dequantized weights), the
+forward output within max|dy| <= 2e-3 * ||y_oracle||_inf (fp16 in, fp32
+accumulation; bf16 outputs additionally get half a bf16 ulp).  Full-size
+configurations are checked on sampled tokens, whose outputs the oracle
+computes from explicitly built expert weights."""
+import numpy as np
+import pytest
+import torch
+
+import bit_rank_post_amd as tq
+import synth
+from bit_rank_post_amd import io as tqio
+from oracle import tileq_ref as R
+from tests import pins
+from tests.gpu_util import assert_parity, need_gpu, run_forward, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    need_gpu()
+
+
+# ---------------------------------------------------------------------------
+# integer work: dequantized weights and routing lists, bit-exact
+
+
+def single_layer_from(p):
+    return dict(kind="single", act=p["act"], K=p["K"], d_model=p["d_in"], d_ff=p["d_out"],
+                proj=dict(single=p), shared=None)
+
+
+def test_dequant_exhaustive_fp16_scales():
+    """Every finite fp16 scale with |s| < 1024 (both signs) x every integer
+    zero point x every code, through the forward's own unpack path."""
+    sbits = np.concatenate([np.arange(0x0000, 0x6400), np.arange(0x8000, 0xE400)]).astype(np.uint16)
+    rows, G, d_in = len(sbits), 32, 128
+    s = np.repeat(sbits[:, None], 4, axis=1).view(np.float16)[None]
+    z = np.tile(np.arange(4, dtype=np.float16), (rows, 1))[None]
+    i = np.arange(d_in)[None, :]
+    o = np.arange(rows)[:, None]
+    q = ((i + o + i // 4) % 4)[None]
+    p = pins.proj_from(q, s, z, np.zeros((rows, 0), np.float16), [],
+                       np.zeros((d_in, 0), np.float16), [0], 1, 1, G)
+    L = tqio.upload_layer(single_layer_from(p))
+    w = torch.empty((rows, d_in), dtype=torch.float16, device="cuda")
+    L.debug_dequant(0, 0, w)
+    torch.cuda.synchronize()
+    got = w.cpu().numpy().view(np.uint16)
+    want = R.deq_canonical(q[0], s[0], z[0], G, "f16").astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5])
+
+
+@pytest.mark.parametrize("G,d_in,d_out,K", [(64, 1408, 64, 3), (128, 4096, 32, 2), (32, 384, 48, 2)])
+def test_dequant_random_groups(G, d_in, d_out, K):
+    rng = np.random.default_rng(G + d_in)
+    q = rng.integers(0, 4, (K, d_out, d_in))
+    s = rng.uniform(1e-4, 0.5, (K, d_out, d_in // G)).astype(np.float16)
+    z = rng.integers(0, 4, (K, d_out, d_in // G)).astype(np.float16)
+    p = pins.proj_from(q, s, z, np.zeros((d_out, 0), np.float16), [],
+                       np.zeros((d_in, 0), np.float16), list(range(K)), 1, K, G)
+    L = tqio.upload_layer(single_layer_from(p))
+    for e in range(K):
+        w = torch.empty((d_out, d_in), dtype=torch.float16, device="cuda")
+        L.debug_dequant(0, e, w)
+        torch.cuda.synchronize()
+        want = R.deq_canonical(q[e], s[e], z[e], G, "f16").astype(np.float16)
+        assert np.array_equal(w.cpu().numpy().view(np.uint16), want.view(np.uint16)), e
+
+
+def test_upload_rejects_bad_zero_and_scale():
+    p, _ = pins.random_struct(2, 1, 2, 128, 16, 0, 32, seed=1)
+    p2 = dict(p)
+    z = p["zeros"].copy()
+    z[1, 3, 2] = np.float16(1.5)
+    p2["zeros"] = z
+    with pytest.raises(tq.TileQError, match="zero point"):
+        tqio.upload_layer(single_layer_from(p2))
+    p3 = dict(p)
+    s = p["scales"].copy()
+    s[0, 0, 0] = np.float16(np.inf)
+    p3["scales"] = s
+    with pytest.raises(tq.TileQError, match="scale"):
+        tqio.upload_layer(single_layer_from(p3))
+
+
+def route_layer(K, M, N, seed):
+    p, _ = pins.random_struct(K, M, N, 128, 16, 16, 32, seed=seed)
+    return tqio.upload_layer(single_layer_from(p)), p
+
+
+def check_route_device(L, p, ids):
+    T, k = ids.shape
+    S = T * k
+    K, N = p["K"], p["N"]
+    dev = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device="cuda")
+    cnt, off, perm, inv = dev(K), dev(K + 1), dev(S), dev(S)
+    col_off, col_tok, s2c = dev(N + 1), dev(S), dev(S)
+    ws = tqio.workspace(L, T, k)
+    idd = torch.from_numpy(ids.astype(np.int32)).cuda()
+    L.debug_route(0, idd, T, k, ws, cnt, off, perm, inv, col_off, col_tok, s2c)
+    torch.cuda.synchronize()
+    n_of = p["tile_of_expert"] % N
+    r = R.route(ids, K, n_of)
+    h = lambda t: t.cpu().numpy().astype(np.int64)
+    assert np.array_equal(h(cnt), r["cnt"])
+    assert np.array_equal(h(off), r["off"])
+    P = int(r["off"][-1])
+    assert np.array_equal(h(perm)[:P], r["perm"])
+    assert np.array_equal(h(inv), r["inv"])
+    co = h(col_off)
+    assert np.array_equal(co[:len(r["col_off"])], r["col_off"])
+    npairs = len(r["col_pairs"])
+    assert np.array_equal(h(col_tok)[:npairs], r["col_pairs"][:, 1])
+    assert np.array_equal(h(s2c), r["slot2col"])
+
+
+def test_route_bitexact_cases():
+    rng = np.random.default_rng(5)
+    L8, p8 = route_layer(8, 2, 4, 11)
+    cases = [rng.integers(0, 8, (64, 2)), np.full((40, 2), 5), np.array([[3, 3]]),
+             np.array([[1, 1], [1, 2], [2, 1]]), rng.integers(0, 3, (300, 4)),
+             np.array([[9, -2], [4, 8], [7, 7], [0, 100]]),           # dropped ids
+             rng.integers(0, 8, (16384, 2))]                          # T*k = 32768
+    for ids in cases:
+        say(f"  route case {ids.shape}")
+        check_route_device(L8, p8, ids)
+    L64, p64 = route_layer(64, 8, 8, 12)
+    cfg = synth.CONFIG_BY_NAME["fine64_zipf_mixed4160"]
+    _, ids, _ = synth.make_tokens(cfg, 4160)                           # Zipf(1.1) top-6
+    check_route_device(L64, p64, ids)
+    check_route_device(L64, p64, rng.integers(0, 64, (1, 6)))
+
+
+def test_dropped_ids_counted():
+    p, _ = pins.random_struct(8, 2, 4, 128, 32, 8, 32, seed=3)
+    L = tqio.upload_layer(single_layer_from(p))
+    x, ids, g = pins.tokens(128, 8, 2, 10, seed=4)
+    ids = ids.copy()
+    ids[2, 1] = 8
+    ids[7, 0] = -3
+    y, dropped = run_forward(L, x, ids, g, "f16")
+    assert dropped == 2
+    assert_parity(y, R.forward_single(p, x, ids, g), what="dropped ids")
+
+# ---------------------------------------------------------------------------
+# forward parity
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("y_dtype", ["f32", "f16"])
+def test_tiny_config(path, y_dtype):
+    cfg = synth.CONFIG_BY_NAME["tiny"]
+    layer = synth.make_layer(cfg)
+    x, ids, g = synth.make_tokens(cfg, 64)
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    y, dropped = run_forward(L, x, ids, g, cfg.act, y_dtype)
+    assert dropped == 0
+    assert_parity(y, R.forward(layer, x, ids, g), y_dtype, what=f"tiny path={path} y={y_dtype}")
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_special_cases_single(path):
+    """Zero rank (pure dequant GEMM), zero residual (pure low rank), the
+    textbook K = M = N = 1 case, duplicates and ragged tails on the device."""
+    cases = {
+        "rank0": pins.random_struct(8, 2, 4, 256, 64, 0, 64, seed=31)[0],
+        "zero_residual": pins.random_struct(8, 2, 4, 256, 64, 16, 64, seed=32, zero_res=True)[0],
+        "textbook": pins.random_struct(1, 1, 1, 384, 48, 20, 128, seed=33)[0],
+        "rank48_G32": pins.random_struct(6, 3, 3, 1408, 80, 48, 32, seed=34)[0],
+    }
+    for name, p in cases.items():
+        L = tqio.upload_layer(single_layer_from(p))
+        L.set_path(path)
+        for T, k in [(1, 1), (37, p["K"] > 1 and 2 or 1), (200, 1)]:
+            x, ids, g = pins.tokens(p["d_in"], p["K"], k, T, seed=T + k)
+            if name == "textbook":
+                g = np.ones_like(g)
+            y, _ = run_forward(L, x, ids, g, "f16")
+            assert_parity(y, R.forward_single(p, x, ids, g), what=f"{name} T={T} k={k}")
+        # duplicates: the same expert twice in a token
+        x, ids1, g1 = pins.tokens(p["d_in"], p["K"], 1, 9, seed=99)
+        ids = np.ascontiguousarray(np.concatenate([ids1, ids1], axis=1))
+        g = np.ascontiguousarray(np.concatenate([g1, 0.5 * g1], axis=1))
+        y, _ = run_forward(L, x, ids, g, "f16")
+        assert_parity(y, R.forward_single(p, x, ids, g), what=f"{name} duplicates")
+
+
+def test_token_permutation_device():
+    p, _ = pins.random_struct(8, 2, 4, 256, 64, 16, 64, seed=41)
+    L = tqio.upload_layer(single_layer_from(p))
+    x, ids, g = pins.tokens(256, 8, 2, 50, seed=42)
+    y, _ = run_forward(L, x, ids, g, "f16")
+    pi = np.random.default_rng(0).permutation(50)
+    y2, _ = run_forward(L, x[pi], ids[pi], g[pi], "f16")
+    assert_parity(y2, y[pi], what="token permutation")
+
+
+def small_swiglu(act, seed, K=8, M=2, N=4, d_model=256, d_ff=384, r=16, G=64):
+    ss = np.random.SeedSequence(seed).spawn(3)
+    proj = {n: synth.make_proj(K, M, N, di, do, r, G, act, s)
+            for (n, (di, do)), s in zip([("gate", (d_model, d_ff)), ("up", (d_model, d_ff)),
+                                         ("down", (d_ff, d_model))], ss)}
+    return dict(kind="swiglu", act=act, K=K, d_model=d_model, d_ff=d_ff, proj=proj, shared=None)
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("path", [1, 2])
+def test_small_swiglu(act, path):
+    layer = small_swiglu(act, 7)
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    for T, k in [(1, 2), (45, 2), (300, 3)]:
+        x, ids, g = synth.make_custom_tokens(256, 8, k, T, act, seed=T)
+        y, _ = run_forward(L, x, ids, g, act, "f32")
+        assert_parity(y, R.forward(layer, x, ids, g), what=f"swiglu {act} path={path} T={T}")
+
+
+def test_qwen15_prefill512_with_shared_expert():
+    cfg = synth.CONFIG_BY_NAME["qwen15_moe_prefill512"]
+    layer = synth.make_layer(cfg)
+    x, ids, g = synth.make_tokens(cfg, 512)
+    L = tqio.upload_layer(layer)
+    y, _ = run_forward(L, x, ids, g, cfg.act, "f16")
+    say("  oracle (all 512 tokens)")
+    assert_parity(y, R.forward(layer, x, ids, g), "f16", what="qwen15 prefill512")
+
+
+def test_fine64_zipf_mixed4160_sampled():
+    cfg = synth.CONFIG_BY_NAME["fine64_zipf_mixed4160"]
+    layer = synth.make_layer(cfg)
+    x, ids, g = synth.make_tokens(cfg, 4160)
+    L = tqio.upload_layer(layer)
+    y, _ = run_forward(L, x, ids, g, cfg.act, "f16")
+    tok = np.concatenate([np.arange(0, 4096, 37), np.arange(4096, 4160)])
+    say(f"  oracle on {len(tok)} sampled tokens")
+    assert_parity(y[tok], R.forward(layer, x, ids, g, tokens=tok), "f16",
+                  what="fine64 zipf 4160 (sampled)")
+
+
+@pytest.fixture(scope="module")
+def mixtral_f16():
+    cfg = synth.CONFIG_BY_NAME["mixtral8x7b_decode"]
+    layer = synth.make_layer(cfg)
+    return cfg, layer, tqio.upload_layer(layer)
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_mixtral_decode(mixtral_f16, B):
+    cfg, layer, L = mixtral_f16
+    x, ids, g = synth.make_tokens(cfg, B)
+    y, _ = run_forward(L, x, ids, g, cfg.act, "f16")
+    tok = np.arange(B) if B <= 2 else np.array([0, B // 2, B - 1])
+    assert_parity(y[tok], R.forward(layer, x, ids, g, tokens=tok, keep_weights=False), "f16",
+                  what=f"mixtral decode B={B} (sampled)")
+
+
+def test_mixtral_prefill16k_bf16_sampled():
+    cfg = synth.CONFIG_BY_NAME["mixtral8x7b_prefill16k_bf16"]
+    layer = synth.make_layer(cfg)
+    x, ids, g = synth.make_tokens(cfg, 16384)
+    L = tqio.upload_layer(layer)
+    ws = tqio.workspace(L, 16384, 2)
+    y32, _ = run_forward(L, x, ids, g, cfg.act, "f32", ws=ws)
+    yb, _ = run_forward(L, x, ids, g, cfg.act, "bf16", ws=ws)
+    # sample tokens whose experts fall in a few experts (bounded oracle cost)
+    hot = np.argsort(-np.bincount(ids.reshape(-1), minlength=8))[:3]
+    cand = np.nonzero(np.all(np.isin(ids, hot), axis=1))[0]
+    tok = np.concatenate([cand[:4], cand[-2:], [0]])
+    say(f"  oracle on tokens {tok.tolist()}")
+    ref = R.forward(layer, x, ids, g, tokens=tok, keep_weights=False)
+    assert_parity(y32[tok], ref, "f32", what="mixtral prefill16k bf16 (y f32)")
+    assert_parity(yb[tok], ref, "bf16", what="mixtral prefill16k bf16 (y bf16)")
