@@ -21,7 +21,10 @@ STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHI
           5: "TQ_EUNSUPPORTED", 6: "TQ_ESTATE"}
 EXPORTS = ["tq_layer_create", "tq_upload_proj", "tq_upload_shared_expert",
            "tq_workspace_size", "tq_forward", "tq_layer_destroy", "tq_last_error",
-           "tq_abi_version", "tq_layer_set_path", "tq_debug_route", "tq_debug_dequant"]
+           "tq_abi_version", "tq_layer_set_path", "tq_debug_route", "tq_debug_dequant",
+           "tq_profile_enable", "tq_profile_read"]
+STAGES = ["route", "row_exponent", "column_stage_in", "gemm_in", "column_stage_down",
+          "shared_expert", "gemm_down", "combine"]
 
 
 class TileQError(RuntimeError):
@@ -63,6 +66,8 @@ def lib():
         L.tq_layer_set_path.argtypes = [vp, i32]
         L.tq_debug_route.argtypes = [vp, i32, vp, i32, i32, vp, sz] + [vp] * 7 + [vp]
         L.tq_debug_dequant.argtypes = [vp, i32, i32, vp, vp]
+        L.tq_profile_enable.argtypes = [vp, i32]
+        L.tq_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
         for name in EXPORTS:
             if name not in ("tq_last_error", "tq_abi_version"):
                 getattr(L, name).restype = i32
@@ -135,6 +140,15 @@ class Layer:
     def debug_dequant(self, which, expert, w_out, stream=None):
         _check("tq_debug_dequant", lib().tq_debug_dequant(self.h, which, expert, _ptr(w_out),
                                                           _stream(stream)))
+
+    def profile_enable(self, on: bool = True):
+        _check("tq_profile_enable", lib().tq_profile_enable(self.h, 1 if on else 0))
+
+    def profile_read(self):
+        """Stage durations (ms) of the last profiled forward, keyed by STAGES."""
+        ms = (ctypes.c_float * 8)()
+        _check("tq_profile_read", lib().tq_profile_read(self.h, ms))
+        return dict(zip(STAGES, list(ms)))
 
     def close(self):
         if getattr(self, "h", None) is not None and self.h.value:

@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
   typedef typename Vec8<T>::type V8;
   const ColArgs& a = args.c[blockIdx.z];
   __shared__ int s_res;
+  __shared__ int s_last;
   __shared__ float s_red[(WR == 1) ? 4 * 16 * 128 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
@@ -106,6 +107,36 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
           const int row = rbase + 4 * (lane >> 4) + v;
           if (row < row_end) P[(size_t)row * a.r_pad + 16 * f + (lane & 15)] = acc[f][v];
         }
+      }
+    }
+  }
+  // split-K: the last workgroup of a tile to arrive sums the slabs in slab
+  // order into slab 0 (deterministic; no float atomics)
+  if (a.nsplit > 1) {
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(&a.counters[tile], 1) == a.nsplit - 1) ? 1 : 0;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    for (int i = tid; i < rt * a.r_pad; i += 256) {
+      const int r = i / a.r_pad, c = i - r * a.r_pad;
+      const int row = row0 + r;
+      if (row < row_end) {
+        // slabs summed in slab order; loads issued 8 at a time
+        const float* src = a.P + (size_t)row * a.r_pad + c;
+        const size_t slab = (size_t)a.rows_cap * a.r_pad;
+        float v = 0.f;
+        int sp = 0;
+        for (; sp + 8 <= a.nsplit; sp += 8) {
+          float t[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) t[u] = __builtin_nontemporal_load(src + (sp + u) * slab);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v += t[u];
+        }
+        for (; sp < a.nsplit; ++sp) v += __builtin_nontemporal_load(src + sp * slab);
+        a.P[(size_t)row * a.r_pad + c] = v;
       }
     }
   }

@@ -67,6 +67,10 @@ struct tq_layer {
   ProjHost proj[3];
   SharedDev shared{};
   int path_override = 0;
+  // stage timing (benchmark hook)
+  bool prof = false;
+  mutable bool prof_recorded = false;
+  hipEvent_t ev[9] = {};
 };
 
 namespace {
@@ -85,20 +89,34 @@ void proj_dims(const tq_layer* L, int which, int* d_in, int* d_out) {
 
 // ---- workspace plan --------------------------------------------------------
 struct Plan {
-  int T, k, S, path, bm_gemm, rt_col, max_tiles_gemm;
+  int T, k, S, path, bm_gemm, rt_col, max_tiles_gemm, max_col_tiles;
   size_t flags, cnt, off, perm, inv, tile_gemm, tile_colx, colmask, cntw, rank;
   size_t col_off[2], col_tok[2], slot2col[2], tile_col[2];
   size_t P[3];
   int nsplit[3];
   int rows_cap;
-  size_t ex, hamax, h, dres, hs, ys;
+  size_t zero_base, hamax, counters;   // contiguous region zeroed by the route kernel
+  int zero_n;
+  size_t ex, h, dres, hs, ys;
+  size_t xp, sums_x, ex_x, hp, sums_h, ex_h;   // decode activation preparation
   size_t total;
 };
 
+// The decode kernel covers groups that do not straddle its 256-input stages
+// and needs one group size for the projections that share an input.
+bool decode_ok(const tq_layer* L) {
+  for (int q = 0; q < nproj(L); ++q)
+    if (L->proj[q].dev.group > 256) return false;
+  if (L->kind == TQ_SWIGLU && L->proj[0].dev.group != L->proj[1].dev.group) return false;
+  return true;
+}
+
 int choose_path(const tq_layer* L, int T, int k) {
-  if (L->path_override == 1 || L->path_override == 2) return L->path_override;
-  const long S = (long)T * k;
-  return (S <= 16L * L->K) ? 1 : 2;
+  int path;
+  if (L->path_override == 1 || L->path_override == 2) path = L->path_override;
+  else path = ((long)T * k <= 16L * L->K) ? 1 : 2;
+  if (path == 1 && !decode_ok(L)) path = 2;
+  return path;
 }
 
 int choose_nsplit(int path, long rows, int d_in) {
@@ -110,6 +128,15 @@ int choose_nsplit(int path, long rows, int d_in) {
   return (int)want;
 }
 
+// waves splitting the k-range of the same rows in the decode kernel
+int choose_kw(const tq_layer* L, int q, int S) {
+  const long active = std::min<long>(L->K, S);
+  const long nrb = L->proj[q].dev.nrb;
+  for (int kw = 1; kw < 4; kw *= 2)
+    if (active * nrb * kw >= 4096) return kw;
+  return 4;
+}
+
 Plan make_plan(const tq_layer* L, int T, int k, int path) {
   Plan p{};
   p.T = T;
@@ -119,6 +146,7 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.bm_gemm = (path == 1) ? 16 : 128;
   p.rt_col = (path == 1) ? 16 : 64;
   p.max_tiles_gemm = (p.S + p.bm_gemm - 1) / p.bm_gemm + L->K;
+  p.max_col_tiles = (p.S + p.rt_col - 1) / p.rt_col + 32 + L->K;
   const int S = p.S, K = L->K;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -154,8 +182,13 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
     if (d.r_pad > 0) p.P[q] = take((size_t)p.nsplit[q] * S * d.r_pad * sizeof(float));
   }
   const bool bf = (L->act == TQ_BF16);
+  // zeroed region: |h| maxima (bf16 SwiGLU, prefill) + split-K tile counters
+  const int nham = (bf && L->kind == TQ_SWIGLU) ? S : 0;
+  p.zero_n = nham + 3 * p.max_col_tiles;
+  p.zero_base = take(sizeof(unsigned) * p.zero_n);
+  p.hamax = p.zero_base;
+  p.counters = p.zero_base + sizeof(unsigned) * nham;
   p.ex = take(sizeof(int) * (bf ? std::max(T, 1) : 1));
-  p.hamax = take(sizeof(unsigned) * ((bf && L->kind == TQ_SWIGLU) ? S : 1));
   p.h = take(L->kind == TQ_SWIGLU ? (size_t)S * L->d_ff * 2 : 0);
   int d_in_last, d_out_last;
   proj_dims(L, nproj(L) - 1, &d_in_last, &d_out_last);
@@ -163,6 +196,18 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   if (L->shared.d_ff > 0) {
     p.hs = take((size_t)T * L->shared.d_ff * 2);
     p.ys = take((size_t)T * L->d_model * sizeof(float));
+  }
+  if (path == 1) {
+    const ProjDev& d0 = L->proj[0].dev;
+    p.xp = take((size_t)T * L->d_model * 2);
+    p.sums_x = take((size_t)T * (L->d_model / d0.group) * 2 * sizeof(float));
+    p.ex_x = take(sizeof(int) * T);
+    if (L->kind == TQ_SWIGLU) {
+      const ProjDev& dd = L->proj[2].dev;
+      p.hp = take((size_t)S * L->d_ff * 2);
+      p.sums_h = take((size_t)S * (L->d_ff / dd.group) * 2 * sizeof(float));
+      p.ex_h = take(sizeof(int) * S);
+    }
   }
   p.total = o;
   return p;
@@ -216,12 +261,11 @@ void fill_route(const tq_layer* L, const Plan& p, const int* ids, void* ws, Rout
   r.cntw = at<int>(ws, p.cntw);
   r.rank = at<int>(ws, p.rank);
   r.colmask = at<int>(ws, p.colmask);
-  if (L->act == TQ_BF16 && L->kind == TQ_SWIGLU) {
-    r.zero_init = at<unsigned>(ws, p.hamax);
-    r.zero_n = p.S;
-  }
+  r.zero_init = at<unsigned>(ws, p.zero_base);
+  r.zero_n = p.zero_n;
 }
 
+// column stage over the unique (column, token) pairs of projection c (input x)
 ColArgs col_args_x(const tq_layer* L, const Plan& p, int c, const void* x, void* ws) {
   const ProjDev& d = L->proj[c].dev;
   ColArgs a{};
@@ -239,6 +283,29 @@ ColArgs col_args_x(const tq_layer* L, const Plan& p, int c, const void* x, void*
   a.steps_per_split = ((d.d_in >> 5) + p.nsplit[c] - 1) / p.nsplit[c];
   a.P = at<float>(ws, p.P[c]);
   a.rows_cap = p.rows_cap;
+  a.counters = at<int>(ws, p.counters) + c * p.max_col_tiles;
+  return a;
+}
+
+// column stage of the down projection: one row per slot position (h)
+ColArgs col_args_down(const tq_layer* L, const Plan& p, const void* h, void* ws) {
+  const ProjDev& d = L->proj[2].dev;
+  ColArgs a{};
+  a.A = h;
+  a.lda = d.d_in;
+  a.seg_off = at<int>(ws, p.off);
+  a.tile_off = at<int>(ws, p.tile_colx);
+  a.row_src = nullptr;
+  a.seg_vblk = d.n_of;
+  a.nseg = L->K;
+  a.Vt = d.Vt;
+  a.r_pad = d.r_pad;
+  a.d_in = d.d_in;
+  a.nsplit = p.nsplit[2];
+  a.steps_per_split = ((d.d_in >> 5) + p.nsplit[2] - 1) / p.nsplit[2];
+  a.P = at<float>(ws, p.P[2]);
+  a.rows_cap = p.rows_cap;
+  a.counters = at<int>(ws, p.counters) + 2 * p.max_col_tiles;
   return a;
 }
 
@@ -452,32 +519,83 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const Act act = (L->act == TQ_F16) ? ACT_F16 : ACT_BF16;
   const bool bf = (act == ACT_BF16);
+  const bool dec = (path == 1);
+  const bool swiglu = (L->kind == TQ_SWIGLU);
+  const int K = L->K;
+  auto mark = [&](int i) {
+    if (L->prof) (void)hipEventRecord(L->ev[i], s);
+  };
 
+  // (a1) routing / grouping
+  mark(0);
   RouteArgs ra;
   fill_route(L, p, topk_ids, ws, ra);
   launch_route(ra, s);
+  mark(1);
+  // activation preparation: decode = class-scaled fp16 copy + group sums;
+  // prefill bf16 = per-row exponents for the exact fp16 staging
   int* ex = nullptr;
-  if (bf) {
+  if (dec) {
+    PrepArgs pa{};
+    pa.X = x;
+    pa.d = L->d_model;
+    pa.G = L->proj[0].dev.group;
+    pa.Xp = at<void>(ws, p.xp);
+    pa.sums = at<float>(ws, p.sums_x);
+    pa.ex = at<int>(ws, p.ex_x);
+    launch_act_prep(pa, T, act, s);
+  } else if (bf) {
     ex = at<int>(ws, p.ex);
     launch_row_exponent(x, T, L->d_model, ex, s);
   }
-
-  const int K = L->K;
-  int d_in_last, d_out_last;
-  proj_dims(L, nproj(L) - 1, &d_in_last, &d_out_last);
+  mark(2);
+  // (a2) column stage of the projection(s) reading x
+  {
+    ColArgs ca[2];
+    int n = 0;
+    const int ncol = swiglu ? 2 : 1;
+    for (int c = 0; c < ncol; ++c)
+      if (L->proj[c].dev.r_pad > 0) ca[n++] = col_args_x(L, p, c, x, ws);
+    if (n) launch_colproj(ca, n, p.rt_col, p.max_col_tiles, act, s);
+  }
+  mark(3);
   float* dres = at<float>(ws, p.dres);
-  const int max_col_tiles = (p.S + p.rt_col - 1) / p.rt_col + 32 + K;
-
-  if (L->kind == TQ_SINGLE) {
-    const ProjDev& d = L->proj[0].dev;
-    if (d.r_pad > 0) {
-      ColArgs ca = col_args_x(L, p, 0, x, ws);
-      launch_colproj(&ca, 1, p.rt_col, max_col_tiles, act, s);
+  void* h = swiglu ? at<void>(ws, p.h) : nullptr;
+  unsigned* hamax = (bf && swiglu && !dec) ? at<unsigned>(ws, p.hamax) : nullptr;
+  // (a3 + a4 + a5) residual GEMM of the input projection(s)
+  if (dec) {
+    DecArgs da{};
+    da.K = K;
+    da.d_in = L->d_model;
+    da.d_out = L->proj[0].dev.d_out;
+    da.topk = topk;
+    da.perm = at<int>(ws, p.perm);
+    da.off = at<int>(ws, p.off);
+    da.cnt = at<int>(ws, p.cnt);
+    da.gather = 1;
+    da.rows = T;
+    da.Xp = at<void>(ws, p.xp);
+    da.sums = at<float>(ws, p.sums_x);
+    da.ex = at<int>(ws, p.ex_x);
+    da.p[0] = L->proj[0].dev;
+    if (swiglu) {
+      da.p[1] = L->proj[1].dev;
+      for (int c = 0; c < 2; ++c) {
+        da.P[c] = L->proj[c].dev.r_pad ? at<float>(ws, p.P[c]) : nullptr;
+        da.slot2col[c] = at<int>(ws, p.slot2col[c]);
+      }
+      da.h = h;
+      launch_gemm_decode(da, MODE_GATEUP, choose_kw(L, 0, p.S), act, s);
+    } else {
+      da.dres = dres;
+      da.gates = topk_w;
+      launch_gemm_decode(da, MODE_RES, choose_kw(L, 0, p.S), act, s);
     }
+  } else {
     GemmArgs ga{};
     ga.K = K;
-    ga.d_in = d.d_in;
-    ga.d_out = d.d_out;
+    ga.d_in = L->d_model;
+    ga.d_out = L->proj[0].dev.d_out;
     ga.topk = topk;
     ga.S = p.S;
     ga.A = x;
@@ -487,92 +605,45 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     ga.cnt = at<int>(ws, p.cnt);
     ga.tile_off = at<int>(ws, p.tile_gemm);
     ga.ex = ex;
-    ga.p[0] = d;
-    ga.dres = dres;
-    ga.gates = topk_w;
-    launch_gemm(ga, MODE_RES, path, act, p.max_tiles_gemm, s);
-    CombineArgs cb{};
-    cb.T = T;
-    cb.topk = topk;
-    cb.K = K;
-    cb.d_out = d.d_out;
-    cb.M = d.M;
-    cb.r_pad = d.r_pad;
-    cb.ids = topk_ids;
-    cb.gates = topk_w;
-    cb.inv = at<int>(ws, p.inv);
-    cb.prow = at<int>(ws, p.slot2col[0]);
-    cb.m_of = d.m_of;
-    cb.P = d.r_pad ? at<float>(ws, p.P[0]) : nullptr;
-    cb.nsplit = p.nsplit[0];
-    cb.rows_cap = p.rows_cap;
-    cb.sigma = d.sigma;
-    cb.U = d.U;
-    cb.dres = dres;
-    cb.ys = nullptr;
-    cb.y = y;
-    cb.y_dtype = (int)y_dtype;
-    launch_combine(cb, act, s);
-  } else {
-    const ProjDev& dg = L->proj[0].dev;
-    const ProjDev& du = L->proj[1].dev;
-    const ProjDev& dd = L->proj[2].dev;
-    // column stage of gate and up (unique (column, token) pairs)
-    {
-      ColArgs ca[2];
-      int n = 0;
-      if (dg.r_pad > 0) ca[n++] = col_args_x(L, p, 0, x, ws);
-      if (du.r_pad > 0) ca[n++] = col_args_x(L, p, 1, x, ws);
-      if (n) launch_colproj(ca, n, p.rt_col, max_col_tiles, act, s);
-    }
-    void* h = at<void>(ws, p.h);
-    unsigned* hamax = bf ? at<unsigned>(ws, p.hamax) : nullptr;
-    {
-      GemmArgs ga{};
-      ga.K = K;
-      ga.d_in = dg.d_in;
-      ga.d_out = dg.d_out;
-      ga.topk = topk;
-      ga.S = p.S;
-      ga.A = x;
-      ga.gather = 1;
-      ga.perm = at<int>(ws, p.perm);
-      ga.off = at<int>(ws, p.off);
-      ga.cnt = at<int>(ws, p.cnt);
-      ga.tile_off = at<int>(ws, p.tile_gemm);
-      ga.ex = ex;
-      ga.p[0] = dg;
-      ga.p[1] = du;
+    ga.p[0] = L->proj[0].dev;
+    if (swiglu) {
+      ga.p[1] = L->proj[1].dev;
       for (int c = 0; c < 2; ++c) {
         ga.P[c] = L->proj[c].dev.r_pad ? at<float>(ws, p.P[c]) : nullptr;
-        ga.nsplit[c] = p.nsplit[c];
+        ga.nsplit[c] = 1;
         ga.rows_cap[c] = p.rows_cap;
         ga.slot2col[c] = at<int>(ws, p.slot2col[c]);
       }
       ga.h = h;
       ga.hamax_out = hamax;
       launch_gemm(ga, MODE_GATEUP, path, act, p.max_tiles_gemm, s);
+    } else {
+      ga.dres = dres;
+      ga.gates = topk_w;
+      launch_gemm(ga, MODE_RES, path, act, p.max_tiles_gemm, s);
     }
-    // column stage of down: one row per slot (h differs per expert)
+  }
+  mark(4);
+  float* ys = nullptr;
+  if (swiglu) {
+    const ProjDev& dd = L->proj[2].dev;
+    // (a2) column stage of down: one row per slot
     if (dd.r_pad > 0) {
-      ColArgs ca{};
-      ca.A = h;
-      ca.lda = dd.d_in;
-      ca.seg_off = at<int>(ws, p.off);
-      ca.tile_off = at<int>(ws, p.tile_colx);
-      ca.row_src = nullptr;
-      ca.seg_vblk = dd.n_of;
-      ca.nseg = K;
-      ca.Vt = dd.Vt;
-      ca.r_pad = dd.r_pad;
-      ca.d_in = dd.d_in;
-      ca.nsplit = p.nsplit[2];
-      ca.steps_per_split = ((dd.d_in >> 5) + p.nsplit[2] - 1) / p.nsplit[2];
-      ca.P = at<float>(ws, p.P[2]);
-      ca.rows_cap = p.rows_cap;
-      launch_colproj(&ca, 1, p.rt_col, max_col_tiles, act, s);
+      ColArgs ca = col_args_down(L, p, h, ws);
+      launch_colproj(&ca, 1, p.rt_col, p.max_col_tiles, act, s);
     }
-    float* ys = nullptr;
+    if (dec) {
+      PrepArgs pa{};
+      pa.X = h;
+      pa.d = L->d_ff;
+      pa.G = dd.group;
+      pa.Xp = at<void>(ws, p.hp);
+      pa.sums = at<float>(ws, p.sums_h);
+      pa.ex = at<int>(ws, p.ex_h);
+      launch_act_prep(pa, p.S, act, s);
+    }
+    mark(5);
+    // (a6) dense shared expert
     if (L->shared.d_ff > 0) {
       DenseArgs da{};
       da.T = T;
@@ -593,7 +664,27 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       launch_dense(db, 0, s);
       ys = at<float>(ws, p.ys);
     }
-    {
+    mark(6);
+    // (a4) residual GEMM of down
+    if (dec) {
+      DecArgs da{};
+      da.K = K;
+      da.d_in = dd.d_in;
+      da.d_out = dd.d_out;
+      da.topk = topk;
+      da.perm = at<int>(ws, p.perm);
+      da.off = at<int>(ws, p.off);
+      da.cnt = at<int>(ws, p.cnt);
+      da.gather = 0;
+      da.rows = p.S;
+      da.Xp = at<void>(ws, p.hp);
+      da.sums = at<float>(ws, p.sums_h);
+      da.ex = at<int>(ws, p.ex_h);
+      da.p[0] = dd;
+      da.dres = dres;
+      da.gates = topk_w;
+      launch_gemm_decode(da, MODE_RES, choose_kw(L, 2, p.S), act, s);
+    } else {
       GemmArgs ga{};
       ga.K = K;
       ga.d_in = dd.d_in;
@@ -612,36 +703,70 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       ga.gates = topk_w;
       launch_gemm(ga, MODE_RES, path, act, p.max_tiles_gemm, s);
     }
+  } else {
+    mark(5);
+    mark(6);
+  }
+  mark(7);
+  // (a3 rank-space part + a5) combine
+  {
+    const int q = swiglu ? 2 : 0;
+    const ProjDev& d = L->proj[q].dev;
     CombineArgs cb{};
     cb.T = T;
     cb.topk = topk;
     cb.K = K;
-    cb.d_out = dd.d_out;
-    cb.M = dd.M;
-    cb.r_pad = dd.r_pad;
+    cb.d_out = d.d_out;
+    cb.M = d.M;
+    cb.r_pad = d.r_pad;
     cb.ids = topk_ids;
     cb.gates = topk_w;
     cb.inv = at<int>(ws, p.inv);
-    cb.prow = at<int>(ws, p.inv);
-    cb.m_of = dd.m_of;
-    cb.P = dd.r_pad ? at<float>(ws, p.P[2]) : nullptr;
-    cb.nsplit = p.nsplit[2];
+    cb.prow = swiglu ? at<int>(ws, p.inv) : at<int>(ws, p.slot2col[0]);
+    cb.m_of = d.m_of;
+    cb.P = d.r_pad ? at<float>(ws, p.P[q]) : nullptr;
+    cb.nsplit = 1;
     cb.rows_cap = p.rows_cap;
-    cb.sigma = dd.sigma;
-    cb.U = dd.U;
+    cb.sigma = d.sigma;
+    cb.U = d.U;
     cb.dres = dres;
     cb.ys = ys;
     cb.y = y;
     cb.y_dtype = (int)y_dtype;
     launch_combine(cb, act, s);
   }
+  mark(8);
+  if (L->prof) L->prof_recorded = true;
   HIPCHK(hipGetLastError());
+  return TQ_OK;
+}
+
+tq_status tq_profile_enable(tq_layer* L, int32_t on) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (on && !L->prof) {
+    for (int i = 0; i < 9; ++i) HIPCHK(hipEventCreate(&L->ev[i]));
+    L->prof = true;
+  } else if (!on && L->prof) {
+    for (int i = 0; i < 9; ++i) (void)hipEventDestroy(L->ev[i]);
+    L->prof = false;
+  }
+  L->prof_recorded = false;
+  return TQ_OK;
+}
+
+tq_status tq_profile_read(const tq_layer* L, float* stage_ms) {
+  if (!L || !stage_ms) return fail(TQ_EINVAL, "NULL argument");
+  if (!L->prof || !L->prof_recorded) return fail(TQ_ESTATE, "no profiled forward recorded");
+  HIPCHK(hipEventSynchronize(L->ev[8]));
+  for (int i = 0; i < 8; ++i) HIPCHK(hipEventElapsedTime(&stage_ms[i], L->ev[i], L->ev[i + 1]));
   return TQ_OK;
 }
 
 tq_status tq_layer_destroy(tq_layer* L) {
   if (!L) return TQ_OK;
   (void)hipDeviceSynchronize();
+  if (L->prof)
+    for (int i = 0; i < 9; ++i) (void)hipEventDestroy(L->ev[i]);
   for (int q = 0; q < 3; ++q) free_proj(L->proj[q]);
   if (L->shared.d_ff) {
     (void)hipFree(L->shared.wg);

@@ -57,6 +57,43 @@ __device__ __forceinline__ void unpack16(uint32_t D, uint32_t out[8]) {
   out[7] = (F & M6) | ONE;
 }
 
+// ---- buffer loads ----------------------------------------------------------
+// Raw buffer resource over [base, base + bytes): the load address is an SGPR
+// base + 32-bit lane offset + uniform SGPR offset, and a read past the end
+// returns zeros (no fault).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// (a & m) | c in one VALU op (the compiler otherwise emits an and plus an or).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+
+// unpack16 into the two MFMA A operands (step b = 0 and b = 1) of dword D.
+__device__ __forceinline__ void unpack16_frags(uint32_t D, u32x4& f0, u32x4& f1) {
+  const uint32_t M4 = 0x00300030u, M6 = 0x00C000C0u, M8 = 0x03000300u;
+  const uint32_t ONE = 0x3C003C00u;
+  const uint32_t E = D >> 6, F = D << 4;
+  f0[0] = and_or(D, M4, ONE);
+  f0[1] = and_or(D, M6, ONE);
+  f0[2] = and_or(D, M8, ONE);
+  f0[3] = and_or(F, M4, ONE);
+  f1[0] = and_or(E, M4, ONE);
+  f1[1] = and_or(E, M6, ONE);
+  f1[2] = and_or(E, M8, ONE);
+  f1[3] = and_or(F, M6, ONE);
+}
+
 // Per (row, group) constants turning 1 + q*c into the dequantized weight
 // RND_f16(s * (q - z)):  ((1 + q c) - (1 + z c)) is exact (Sterbenz), equals
 // (q - z) c, and the product with s/c (exact: power-of-two scaling, |s| < 1024)

@@ -83,6 +83,7 @@ struct ColArgs {
   int nsplit, steps_per_split;
   float* P;
   int rows_cap;                  // rows per split slab
+  int* counters;                 // per-tile arrival counters (nsplit > 1), zeroed
 };
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
                     hipStream_t s);
@@ -114,6 +115,37 @@ struct GemmArgs {
 };
 void launch_gemm(const GemmArgs& a, GemmMode mode, int path, Act act, int max_tiles,
                  hipStream_t s);
+
+// ---- decode streaming residual kernel --------------------------------------
+struct DecArgs {
+  int K, d_in, d_out, topk;
+  const int* perm;
+  const int* off;
+  const int* cnt;
+  int gather;                    // 1: activation row of a slot = its token; 0: pos
+  const void* Xp;                // class-scaled fp16 activations [rows][d_in]
+  int rows;                      // rows of Xp / sums / ex
+  const float* sums;             // [rows][d_in/G][2]: (X~_g, X'_g)
+  const int* ex;                 // [rows] row exponent E
+  ProjDev p[2];
+  const float* P[2];             // column-stage results [rows][r_pad] (GATEUP)
+  const int* slot2col[2];
+  void* h;                       // GATEUP out [S][d_out] act
+  float* dres;                   // RES out [S][d_out] f32
+  const float* gates;
+};
+void launch_gemm_decode(const DecArgs& a, GemmMode mode, int kw, Act act, hipStream_t s);
+
+// ---- activation preparation for the decode kernel ---------------------------
+struct PrepArgs {
+  const void* X;                 // [*][d] act
+  int d, G;
+  const int* row_src;            // output row -> input row (nullptr: identity)
+  void* Xp;                      // [rows][d] f16: x~ / c
+  float* sums;                   // [rows][d/G][2]
+  int* ex;                       // [rows]
+};
+void launch_act_prep(const PrepArgs& a, int rows, Act act, hipStream_t s);
 
 // ---- combine: y_t = sum_j dres[inv(t,j)] + U_cat S_t (+ shared) ------------
 struct CombineArgs {

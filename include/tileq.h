@@ -180,6 +180,18 @@ tq_status tq_debug_route(const tq_layer *L, int32_t which, const int32_t *topk_i
 tq_status tq_debug_dequant(const tq_layer *L, int32_t which, int32_t expert, void *w_out,
                            void *stream);
 
+/* Stage timing for benchmarks: with profiling on, tq_forward records a HIP
+ * event on `stream` before its first stage and after each of its stages
+ * (pre-created events: the forward still allocates nothing).  Stage order:
+ * 0 routing, 1 bf16 row exponents, 2 column stage of the input projection(s),
+ * 3 residual GEMM of gate+up (SWIGLU) or of the single projection,
+ * 4 column stage of down, 5 shared expert, 6 residual GEMM of down, 7 combine
+ * (stages a layer does not run take ~0 ms).  tq_profile_read waits for the
+ * last recorded forward and writes its 8 stage durations in ms.
+ * Errors: TQ_EINVAL, TQ_ESTATE (read without a profiled forward), TQ_EHIP. */
+tq_status tq_profile_enable(tq_layer *L, int32_t on);
+tq_status tq_profile_read(const tq_layer *L, float *stage_ms);
+
 #ifdef __cplusplus
 }
 #endif
