@@ -28,7 +28,6 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
   typedef typename Vec8<T>::type V8;
   const ColArgs& a = args.c[blockIdx.z];
   __shared__ int s_res;
-  __shared__ int s_last;
   __shared__ float s_red[(WR == 1) ? 4 * 16 * 128 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
@@ -57,21 +56,47 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
 #pragma unroll
   for (int f = 0; f < 8; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int kstart = (WR == 4) ? st0 : st0 + wave;
-  const int kstride = (WR == 4) ? 1 : 4;
-  for (int st = kstart; st < st1; st += kstride) {
-    V8 av;
-    if (rvalid) {
-      av = *reinterpret_cast<const V8*>(arow + st * 32);
-    } else {
-      av = __builtin_bit_cast(V8, u32x4{0u, 0u, 0u, 0u});
+  if (WR == 1) {
+    // decode shape: the 4 waves split the (at most 16) k-steps of the slab;
+    // every load of a wave is issued before its MFMAs (buffer loads; a step
+    // outside the slab reads zeros through an out-of-range offset)
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, 0x7FFFFFF0u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.Vt, 0x7FFFFFF0u);
+    const uint32_t BAD = 0x7FFFFFF0u;
+    const uint32_t avo = rvalid ? ((uint32_t)src * a.lda + 8 * (lane >> 4)) * 2u : BAD;
+    const uint32_t vvo = ((uint32_t)vblk * a.r_pad * a.d_in + (lane & 15) * a.d_in + 8 * (lane >> 4)) * 2u;
+    u32x4 av[4], bv[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int st = st0 + wave + 4 * i;
+      const bool ok = st < st1;
+      av[i] = bload128(ra, ok ? avo : BAD, ok ? st * 64u : 0u);
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+        if (f < nfrag)
+          bv[i][f] = bload128(rv, ok ? vvo + 16u * f * a.d_in * 2u : BAD, ok ? st * 64u : 0u);
     }
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      if (f < nfrag) {
-        const V8 bv = *reinterpret_cast<const V8*>(
-            vt + (size_t)(16 * f + (lane & 15)) * a.d_in + st * 32 + 8 * (lane >> 4));
-        acc[f] = mfma16(av, bv, acc[f]);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+        if (f < nfrag)
+          acc[f] = mfma16(__builtin_bit_cast(V8, av[i]), __builtin_bit_cast(V8, bv[i][f]), acc[f]);
+  } else {
+    for (int st = st0; st < st1; ++st) {
+      V8 avv;
+      if (rvalid) {
+        avv = *reinterpret_cast<const V8*>(arow + st * 32);
+      } else {
+        avv = __builtin_bit_cast(V8, u32x4{0u, 0u, 0u, 0u});
+      }
+#pragma unroll
+      for (int f = 0; f < 8; ++f) {
+        if (f < nfrag) {
+          const V8 bvv = *reinterpret_cast<const V8*>(
+              vt + (size_t)(16 * f + (lane & 15)) * a.d_in + st * 32 + 8 * (lane >> 4));
+          acc[f] = mfma16(avv, bvv, acc[f]);
+        }
       }
     }
   }
@@ -110,36 +135,34 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
       }
     }
   }
-  // split-K: the last workgroup of a tile to arrive sums the slabs in slab
-  // order into slab 0 (deterministic; no float atomics)
-  if (a.nsplit > 1) {
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&a.counters[tile], 1) == a.nsplit - 1) ? 1 : 0;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int i = tid; i < rt * a.r_pad; i += 256) {
-      const int r = i / a.r_pad, c = i - r * a.r_pad;
-      const int row = row0 + r;
-      if (row < row_end) {
-        // slabs summed in slab order; loads issued 8 at a time
-        const float* src = a.P + (size_t)row * a.r_pad + c;
-        const size_t slab = (size_t)a.rows_cap * a.r_pad;
-        float v = 0.f;
-        int sp = 0;
-        for (; sp + 8 <= a.nsplit; sp += 8) {
-          float t[8];
+}
+
+// Split-K reduction of the column stage: slab 0 += slabs 1.. (in slab
+// order, deterministic).  Rows past the segment total are skipped.
+struct RedArgs {
+  float* P[2];
+  const int* total[2];           // device row count of each projection
+  int r_pad[2];
+  int nsplit, rows_cap;
+};
+
+__global__ __launch_bounds__(256) void colproj_reduce_kernel(RedArgs a) {
+  const int z = blockIdx.y;
+  const int rp = a.r_pad[z];
+  const int rows = *a.total[z];
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * rp) return;
+  const size_t slab = (size_t)a.rows_cap * rp;
+  float* P = a.P[z];
+  float v = 0.f;
+  for (int sp = 0; sp < a.nsplit; sp += 16) {
+    float t[16];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) t[u] = __builtin_nontemporal_load(src + (sp + u) * slab);
+    for (int u = 0; u < 16; ++u) t[u] = (sp + u < a.nsplit) ? P[i + (sp + u) * slab] : 0.f;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v += t[u];
-        }
-        for (; sp < a.nsplit; ++sp) v += __builtin_nontemporal_load(src + sp * slab);
-        a.P[(size_t)row * a.r_pad + c] = v;
-      }
-    }
+    for (int u = 0; u < 16; ++u) v += t[u];
   }
+  P[i] = v;
 }
 
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act, hipStream_t s) {
@@ -153,6 +176,20 @@ void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
   } else {
     if (rt == 16) hipLaunchKernelGGL((colproj_kernel<__bf16, 1>), grid, dim3(256), 0, s, args);
     else hipLaunchKernelGGL((colproj_kernel<__bf16, 4>), grid, dim3(256), 0, s, args);
+  }
+  if (a[0].nsplit > 1) {
+    RedArgs r{};
+    int rp_max = 0;
+    for (int z = 0; z < nproj; ++z) {
+      r.P[z] = a[z].P;
+      r.total[z] = a[z].seg_off + a[z].nseg;
+      r.r_pad[z] = a[z].r_pad;
+      rp_max = a[z].r_pad > rp_max ? a[z].r_pad : rp_max;
+    }
+    r.nsplit = a[0].nsplit;
+    r.rows_cap = a[0].rows_cap;
+    const dim3 rg((unsigned)(((size_t)a[0].rows_cap * rp_max + 255) / 256), nproj);
+    hipLaunchKernelGGL(colproj_reduce_kernel, rg, dim3(256), 0, s, r);
   }
 }
 

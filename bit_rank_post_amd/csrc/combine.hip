@@ -21,8 +21,12 @@ template <typename T, typename YT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   typedef typename Vec8<T>::type V8;
   constexpr int SLD = 128 + 8;
+  constexpr int KMAX = 32;
   __shared__ __attribute__((aligned(16))) T s_hi[16 * SLD];
   __shared__ __attribute__((aligned(16))) T s_lo[16 * SLD];
+  __shared__ int s_m[16 * KMAX];        // grid row of each slot's expert (-1: none)
+  __shared__ int s_row[16 * KMAX];      // row of P of each slot
+  __shared__ float s_g[16 * KMAX];      // routing weight of each slot
   __shared__ int s_active;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -34,36 +38,48 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
   if (a.r_pad > 0) {
     const int rp = a.r_pad;
+    // per-slot data of the tile, once
+    for (int i = tid; i < 16 * k; i += 256) {
+      const int tt = i / k, j = i - tt * k;
+      const int t = t0 + tt;
+      int m = -1, row = 0;
+      float g = 0.f;
+      if (t < a.T) {
+        const int s = t * k + j;
+        const int e = a.ids[s];
+        if (e >= 0 && e < a.K) {
+          m = a.m_of[e];
+          row = a.prow[s];
+          g = a.gates[s];
+        }
+      }
+      s_m[tt * KMAX + j] = m;
+      s_row[tt * KMAX + j] = row;
+      s_g[tt * KMAX + j] = g;
+    }
     for (int m = 0; m < a.M; ++m) {
       __syncthreads();
-      if (tid == 0) s_active = 0;
+      if (tid == 0) {
+        int any = 0;
+        for (int i = 0; i < 16 * k && !any; ++i) any = (s_m[(i / k) * KMAX + i % k] == m);
+        s_active = any;
+      }
       __syncthreads();
-      bool any = false;
+      if (!s_active) continue;
+      // S[t][m][:] = Sigma * sum_{j : row(e_tj) = m} g_tj p_tj, split hi + lo
       for (int i = tid; i < 16 * rp; i += 256) {
         const int tt = i / rp, c = i - tt * rp;
-        const int t = t0 + tt;
         float v = 0.f;
-        if (t < a.T) {
-          for (int j = 0; j < k; ++j) {
-            const int s = t * k + j;
-            const int e = a.ids[s];
-            if (e < 0 || e >= a.K || a.m_of[e] != m) continue;
-            const int row = a.prow[s];
-            float p = 0.f;
-            for (int sp = 0; sp < a.nsplit; ++sp)
-              p += a.P[((size_t)sp * a.rows_cap + row) * rp + c];
-            v += a.gates[s] * p;
-            any = true;
-          }
-          v *= a.sigma[c];
-        }
+        for (int j = 0; j < k; ++j)
+          if (s_m[tt * KMAX + j] == m)
+            v += s_g[tt * KMAX + j] * a.P[(size_t)s_row[tt * KMAX + j] * rp + c];
+        v *= a.sigma[c];
         const T hi = from_f32<T>(v);
         s_hi[tt * SLD + c] = hi;
         s_lo[tt * SLD + c] = from_f32<T>(v - to_f32(hi));
       }
-      if (any) s_active = 1;
       __syncthreads();
-      if (s_active && ovalid) {
+      if (ovalid) {
         const T* up = reinterpret_cast<const T*>(a.U) +
                       ((size_t)m * a.d_out + o_w + l16) * rp + 8 * lg;
         for (int s2 = 0; s2 < rp; s2 += 32) {

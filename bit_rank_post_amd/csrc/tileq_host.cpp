@@ -119,13 +119,12 @@ int choose_path(const tq_layer* L, int T, int k) {
   return path;
 }
 
+// column stage split-K for decode: slabs of 16 k-steps (512 inputs), one
+// batch of loads per wave
 int choose_nsplit(int path, long rows, int d_in) {
+  (void)rows;
   if (path != 1) return 1;
-  const int nsteps = d_in >> 5;
-  const long tiles = (rows + 15) / 16 + 8;
-  long want = (512 + tiles - 1) / tiles;
-  want = std::max(1L, std::min(want, (long)std::max(1, nsteps / 8)));
-  return (int)want;
+  return std::max(1, ((d_in >> 5) + 15) / 16);
 }
 
 // waves splitting the k-range of the same rows in the decode kernel

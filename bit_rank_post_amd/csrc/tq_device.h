@@ -166,20 +166,17 @@ __device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
 // s_w: shared int[17].  Returns the exclusive prefix; *total gets the sum.
 __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
-  int inc = wave_incl_scan_i(v, lane);
+  const int inc = wave_incl_scan_i(v, lane);
   if (lane == 63) s_w[w] = inc;
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < nw; ++i) {
-      int t = s_w[i];
-      s_w[i] = run;
-      run += t;
-    }
-    s_w[16] = run;
+  if (w == 0) {
+    const int t = (lane < nw) ? s_w[lane] : 0;
+    const int i2 = wave_incl_scan_i(t, lane);
+    if (lane < nw) s_w[lane] = i2 - t;
+    if (lane == nw - 1) s_w[16] = i2;
   }
   __syncthreads();
-  int res = s_w[w] + inc - v;
+  const int res = s_w[w] + inc - v;
   *total = s_w[16];
   __syncthreads();
   return res;
