@@ -40,25 +40,38 @@ WORKLOADS = {
     "mixtral_decode": ("mixtral8x7b_decode", 32),
     "mixtral_decode_b1": ("mixtral8x7b_decode", 1),
     "mixtral_decode_b8": ("mixtral8x7b_decode", 8),
+    "mixtral_decode_b64": ("mixtral8x7b_decode", 64),
     "qwen15_prefill512": ("qwen15_moe_prefill512", 512),
     "fine64_mixed4160": ("fine64_zipf_mixed4160", 4160),
     "mixtral_prefill16k": ("mixtral8x7b_prefill16k_bf16", 16384),
     "tiny": ("tiny", 64),
 }
 
-KERNEL_SOURCES = ["bit_rank_post_amd/csrc/moe_gemm.hip", "bit_rank_post_amd/csrc/tq_device.h",
-                  "bit_rank_post_amd/csrc/tq_internal.h"]
+# sources of the dominant kernel of each path (the traffic summary is only
+# used while it was taken on these exact sources)
+KERNEL_SOURCES = {
+    "decode": ["bit_rank_post_amd/csrc/gemm_decode.hip", "bit_rank_post_amd/csrc/tq_device.h",
+               "bit_rank_post_amd/csrc/tq_internal.h"],
+    "prefill": ["bit_rank_post_amd/csrc/moe_gemm.hip", "bit_rank_post_amd/csrc/tq_device.h",
+                "bit_rank_post_amd/csrc/tq_internal.h"],
+}
+KERNEL_NAMES = {
+    "decode": "gemm_dec_kernel (gate+up streaming 2-bit residual GEMV/MFMA with low-rank "
+              "row stage and SwiGLU epilogue)",
+    "prefill": "moe_gemm_kernel (gate+up grouped 2-bit dequant MFMA GEMM with low-rank "
+               "K-extension and SwiGLU epilogue)",
+}
 
 
-def kernel_hash():
+def kernel_hash(path_name):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[path_name]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload):
+def traffic_from_profile(workload, path_name):
     """HBM bytes per launch of the dominant kernel from a committed counter
     summary, if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_dominant_{workload}.txt")
@@ -69,7 +82,7 @@ def traffic_from_profile(workload):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != kernel_hash():
+    if kv.get("source_sha256") != kernel_hash(path_name):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -179,7 +192,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one 256 MiB device copy (counter calibration)")
+                    help="also run one 256 MiB elementwise copy kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -263,10 +276,13 @@ def main():
     stages_ms = {kk: v / args.steps for kk, v in acc.items()}
 
     if args.calibrate_copy:
-        a = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+        # one elementwise kernel of known traffic (reads 256 MiB, writes
+        # 256 MiB): scales the FETCH_SIZE / WRITE_SIZE counters to bytes
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
-        b.copy_(a)
+        torch.abs(a, out=b)
         torch.cuda.synchronize()
+        del a, b
 
     work = algorithmic(layer, ids, T)
     dom_ms = stages_ms["gemm_in"]
@@ -279,9 +295,10 @@ def main():
         achieved = work["dom_flops"] / (dom_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_F16_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_F16_TFLOPS, 4))
-    tr = traffic_from_profile(args.workload)
+    path_name = "decode" if decode else "prefill"
+    tr = traffic_from_profile(args.workload, path_name)
     roof["traffic"] = tr
-    roof["kernel"] = "moe_gemm_kernel (gate+up residual GEMM with low-rank K-extension, SwiGLU)"
+    roof["kernel"] = KERNEL_NAMES[path_name]
     roof["kernel_ms"] = round(dom_ms, 5)
     roof["algorithmic_bytes_per_launch"] = work["dom_bytes"]
     roof["algorithmic_flops_per_launch"] = work["dom_flops"]
@@ -318,7 +335,7 @@ def main():
                           "algorithmic_flops": work["total_flops"],
                           "achieved_GBps": round(whole_gbs, 1),
                           "active_experts": work["active_experts"]},
-        "kernel_source_sha256": kernel_hash(),
+        "kernel_source_sha256": kernel_hash(path_name),
     }
     print(json.dumps(out))
 

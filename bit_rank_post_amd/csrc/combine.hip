@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   for (int j = 0; j < k; ++j) {
     const int pos = a.inv[t * k + j];
     if (pos < 0) continue;
-    v += *reinterpret_cast<const f32x4*>(a.dres + (size_t)pos * a.d_out + o);
+    for (int c = 0; c < a.nks; ++c)
+      v += *reinterpret_cast<const f32x4*>(a.dres + ((size_t)c * a.S + pos) * a.d_out + o);
   }
   if (a.ys) v += *reinterpret_cast<const f32x4*>(a.ys + (size_t)t * a.d_out + o);
   YT* y = reinterpret_cast<YT*>(a.y) + (size_t)t * a.d_out + o;

@@ -4,73 +4,145 @@
 // "TileQ" technical summary, section 4 (Inference Latency, Decode): decode is
 // memory bound; the layout is contiguous and read with wide vector accesses.
 //
-// Work: a workgroup (4 waves) owns 4/KW row fragments (16 rows each) of one
-// expert -- in MODE_GATEUP the gate and the up rows together -- and KW waves
-// split the k-stages of a fragment.  A stage is 8 MFMA k-steps (256 inputs).
-// Per stage-time every wave issues, DEPTH stage-times ahead, buffer loads for
-// its codes (16 B per lane per projection), a share of the stage's
-// activations, its rows' scale/zero words and a share of the group sums; when
-// they land it writes the shared parts to a double-buffered LDS slot, the
-// workgroup synchronizes, and the MFMAs read their B operands and fold
-// constants from LDS.  Only codes stay in registers, so the HBM stream is
-// DEPTH stages deep per wave.
+// Work: a workgroup of WAVES waves owns WAVES row fragments (16 rows each) of
+// one expert -- in MODE_GATEUP the gate and the up rows together -- and walks
+// a range of k-stages (8 MFMA k-steps = 256 inputs each).  Everything a stage
+// needs (each wave's codes, the stage's activations shared by all waves, the
+// scale/zero words and the activation group sums) is brought straight into
+// LDS by buffer loads with the LDS destination (no registers in between), in
+// a ring of DEPTH + 1 slots: DEPTH stages are in flight while one is
+// computed.  Each wave waits for its own loads with an explicit vmcnt (loads
+// complete in issue order) before the stage's barrier; the barrier carries
+// no memory fence, which would wait for every load in flight.
 //
 // The codes enter v_mfma_f32_16x16x32_f16 as the raw packed values 1 + q*c
 // (one and-or per pair, no dequantization) against the class-scaled
-// activations x' = x~/c from act_prep.hip; each quantization group's fp32
-// partial is folded with acc += s * (C_g - X'_g - z * X~_g).
+// activations x' = x~/c from act_prep.hip, so a group's fp32 partial is
+// C_g = X'_g + sum q x~ and the residual output of a row is
+//     sum_g s_g (C_g - X'_g - z_g X~_g)
+//   = sum_g s_g C_g  -  sum_g (s_g X'_g + s_g z_g X~_g).
+// The first sum costs one fma per group; the second is a small product
+// (rows x 2 NG) . (2 NG x columns) per stage, done by v_mfma_f32_16x16x4_f32
+// into a separate accumulator.
 // Epilogue: undo the row scaling 2^E, add the low-rank row stage U_m Sigma p
 // as MFMA K-steps (MODE_GATEUP; p from the column stage), then SwiGLU into h,
-// or (MODE_RES) the slot's routing weight into the fp32 per-slot buffer.
+// or (MODE_RES) the slot's routing weight into the fp32 per-slot buffer of
+// the workgroup's k-range (split-K slabs, summed by the combine kernel).
 #include "tq_device.h"
 
 namespace tq {
 
-constexpr int DEPTH = 3;          // stage-times of loads in flight per wave
-constexpr int ALD = 256 + 8;      // LDS activation row stride (halves)
+typedef __attribute__((address_space(3))) void lds_t;
 
-template <int NP, int KW>
-struct DecRing {
-  u32x4 code[NP];
-  u32x4 act[2 * KW];              // this thread's share of the stage activations
-  u32x2 sz[NP];                   // scale/zero words of this wave's rows
-  u32x2 sum;                      // one (X~, X') pair of the group sums
+// out-of-range voffset: the load returns zeros and reads no memory (only the
+// vector offset is range checked, so every scalar offset stays in range)
+constexpr uint32_t OOB = 0x7FFFFFF0u;
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                     uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 4, voff, soff, 0, 0);
+}
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// workgroup barrier without a memory fence; the empty asm statements keep
+// the compiler from moving LDS accesses across it
+__device__ __forceinline__ void bar_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS slot layout (bytes) for NP projections, WAVES waves, NG groups/stage
+template <int NP, int WAVES, int NG>
+struct DecSlot {
+  static constexpr int NSZ = NG >= 4 ? NG / 4 : 1;   // dword loads per (wave, proj)
+  static constexpr int SZW = NSZ * 64;               // words per (wave, proj)
+  static constexpr int NSUM = NG >= 2 ? NG / 2 : 1;  // dword loads of the group sums
+  static constexpr int NACT = WAVES >= 8 ? 1 : 8 / WAVES;   // activation loads per wave
+  static constexpr int CODE = 0;                     // [WAVES][NP][64 lanes] x 16 B
+  static constexpr int ACT = CODE + WAVES * NP * 1024;   // [8 k-steps][64 lanes] x 16 B
+  static constexpr int SZ = ACT + 8 * 1024;          // [WAVES][NP][SZW] x 4 B
+  static constexpr int SUM = SZ + WAVES * NP * SZW * 4;  // [NG][16 cols] float2
+  static constexpr int BYTES = SUM + NSUM * 256;
+  // loads per wave per stage (the same for every wave)
+  static constexpr int NI = NP + NACT + NP * NSZ + 1;
 };
 
-template <int NP, int KW, int NG>
-struct DecLds {
-  static constexpr int ACT = KW * 16 * ALD * 2;           // bytes
-  static constexpr int SUM = KW * 16 * NG * 8;
-  static constexpr int SZ = 4 * NP * NG * 64;
-  static constexpr int SLOT = ACT + SUM + SZ;
-};
+// ring length: as many slots as fit about 150 KB of LDS, at most DMAX + 1
+template <int BYTES, int DMAX>
+constexpr int ring_depth() {
+  return (150 * 1024 / BYTES - 1 < DMAX) ? 150 * 1024 / BYTES - 1 : DMAX;
+}
 
-template <typename T, int MODE, int KW, int GS>
-__global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs a) {
+template <typename T, int MODE, int GS, int WAVES, int DMAX>
+__global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
   typedef typename Vec8<T>::type V8;
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
-  constexpr int RPW = 4 / KW;            // row fragments per workgroup
   constexpr int NG = 8 / GS;             // groups per stage
-  typedef DecLds<NP, KW, NG> LD;
-  __shared__ __attribute__((aligned(16))) char lds[2 * LD::SLOT];
-  __shared__ float s_red[(KW > 1) ? (KW - 1) * RPW * NP * 256 : 1];
+  typedef DecSlot<NP, WAVES, NG> SL;
+  constexpr int DEPTH = ring_depth<SL::BYTES, DMAX>();
+  constexpr int NSLOT = DEPTH + 1;
+  static_assert(DEPTH >= 2, "ring depth");
+  static_assert(SL::NI * (DEPTH - 1) < 64, "vmcnt range");
+  static_assert(NSLOT <= 8, "ring length");
+  static_assert(WAVES % 8 == 0 || 8 % WAVES == 0, "activation loads per wave");
+  constexpr int NCORR = (2 * NG + 3) / 4;   // fp32 MFMAs of the group correction
+  __shared__ __attribute__((aligned(16))) char s0[SL::BYTES];
+  __shared__ __attribute__((aligned(16))) char s1[SL::BYTES];
+  __shared__ __attribute__((aligned(16))) char s2[NSLOT > 2 ? SL::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char s3[NSLOT > 3 ? SL::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char s4[NSLOT > 4 ? SL::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char s5[NSLOT > 5 ? SL::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char s6[NSLOT > 6 ? SL::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char s7[NSLOT > 7 ? SL::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char s_dummy[1024];  // target of unused loads
+  char* const slot[8] = {s0, s1, s2, s3, s4, s5, s6, s7};
 
-  const int e = blockIdx.x;
+  // Workgroup -> (expert, row-fragment group, k-chunk).  Consecutive
+  // workgroups go to the 8 XCDs in turn; the mapping gives every XCD an equal
+  // share of every expert's rows (all XCDs stream even when one or two
+  // experts are active), and consecutive workgroups of one XCD take different
+  // experts.
+  const int nrb = a.d_out >> 4;
+  const int nby = (nrb + WAVES - 1) / WAVES;
+  const int nby8 = (nby + 7) >> 3;
+  const int wg = blockIdx.x, q = wg >> 3;
+  const int e = q % a.K;
+  const int jq = q / a.K;
+  const int ks = jq / nby8;
+  const int by = (jq - ks * nby8) * 8 + (wg & 7);
+  if (by >= nby) return;
   const int cnt = a.cnt[e];
   if (cnt == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l16 = lane & 15, lg = lane >> 4;
-  const int rsub = wave / KW, kw = wave - rsub * KW;
-  const int nrb = a.d_out >> 4;
-  const int rb_raw = blockIdx.y * RPW + rsub;
+  const int rb_raw = by * WAVES + wave;
   const bool rvalid = rb_raw < nrb;
   const int rb = rvalid ? rb_raw : nrb - 1;          // clamped: loads stay in bounds
   const int nsteps = a.d_in >> 5;
   const int nfull = nsteps >> 3;
-  const bool tail = (nsteps & 7) != 0;
+  // k-chunk of this workgroup: stages [k0, k0 + ntau); the 4-step tail stage
+  // (d_in % 256 == 128) goes with the last chunk
+  const int k0 = (int)(((long)nfull * ks) / a.nks);
+  const int ntau = (int)(((long)nfull * (ks + 1)) / a.nks) - k0;
+  const bool tail = ((nsteps & 7) != 0) && ks == a.nks - 1;
   const int ng = a.p[0].ng;
-  const int ntau = (nfull + KW - 1) / KW;            // stage-times
+  // Stage order is rotated per workgroup (stage-time tau works on stage
+  // k0 + (tau + r0) mod ntau): workgroups running together on an XCD read
+  // different activation chunks and code pages instead of all hitting the
+  // same L2 channels.
+  const int r0 = ntau > 0 ? q % ntau : 0;
   const size_t cpe = (size_t)a.d_out * (a.d_in >> 4);
 
   __amdgpu_buffer_rsrc_t rc[NP], rs[NP];
@@ -90,79 +162,100 @@ __global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs a) {
     const int ncol = min(16, cnt - t0);
     const bool cvalid = l16 < ncol;
     const int pos = a.off[e] + t0 + (cvalid ? l16 : 0);
-    const int slot = a.perm[pos];
-    const int arow = a.gather ? slot / a.topk : pos;
+    const int slotid = a.perm[pos];
+    const int arow = a.gather ? slotid / a.topk : pos;
 
-    // this thread's shares of the shared per-stage-time loads (invalid columns
-    // read the tile's first column; MFMA columns are independent and those
-    // are never stored)
-    uint32_t act_voff[2 * KW];
-    int act_lds[2 * KW];
-#pragma unroll
-    for (int i = 0; i < 2 * KW; ++i) {
-      const int c = tid + 256 * i;                     // 16 B chunk of [KW][16][256]
-      const int ks = c >> 9, col = (c >> 5) & 15, kc = c & 31;
-      const int cc = (col < ncol) ? col : 0;
-      const int r = a.gather ? a.perm[a.off[e] + t0 + cc] / a.topk : a.off[e] + t0 + cc;
-      act_voff[i] = ((uint32_t)r * a.d_in + ks * 256 + kc * 8) * 2u;
-      act_lds[i] = ((ks * 16 + col) * ALD + kc * 8) * 2;
-    }
-    const int nsum = KW * NG * 16;                     // (stage, group, column) triples
-    const int sidx = tid % nsum;
-    uint32_t sum_voff;
-    int sum_lds;
+    // per-lane load offsets (columns past the tile's slots are not loaded:
+    // their MFMA columns are never stored, and columns do not mix)
+    // activations: lane = (lg, col) of k-step j; the k-step adds 64 bytes
+    const uint32_t act_vo = cvalid ? ((uint32_t)arow * a.d_in + 8 * lg) * 2u : OOB;
+    // group sums: word w = 64 * wave + lane of the stage's [NG][16][2] table
+    uint32_t sum_vo = OOB;
     {
-      const int col = sidx & 15, gis = sidx >> 4;      // gis = ks * NG + gi
-      const int cc = (col < ncol) ? col : 0;
-      const int r = a.gather ? a.perm[a.off[e] + t0 + cc] / a.topk : a.off[e] + t0 + cc;
-      sum_voff = ((uint32_t)r * ng + gis) * 8u;
-      sum_lds = LD::ACT + (gis * 16 + col) * 8;
+      const int w = 64 * wave + lane;
+      const int gi = w >> 5, col = (w >> 1) & 15, comp = w & 1;
+      if (wave < SL::NSUM && gi < NG && col < ncol) {
+        const int r = a.gather ? a.perm[a.off[e] + t0 + col] / a.topk : a.off[e] + t0 + col;
+        sum_vo = (((uint32_t)r * ng + gi) * 2u + comp) * 4u;
+      }
     }
-    const int szl = lane % (NG * 8);                   // u32x2 index within NG*16 words
-    const int sz_lds = LD::ACT + LD::SUM + (wave * NP) * NG * 64 + szl * 8;
 
-    auto issue = [&](int tau, DecRing<NP, KW>& R) {
-      const int st = tau * KW + kw;
+    auto issue = [&](int b, char* base) {
+      const bool live = b < ntau;
+      int tr = b + r0;
+      tr = (tr >= ntau) ? tr - ntau : tr;
+      const int st = live ? k0 + tr : 0;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) R.code[p] = bload128(rc[p], lane * 16u, st * 1024u);
+      for (int p = 0; p < NP; ++p)
+        dma16(rc[p], base + SL::CODE + (wave * NP + p) * 1024, live ? lane * 16u : OOB, st * 1024u);
 #pragma unroll
-      for (int i = 0; i < 2 * KW; ++i) R.act[i] = bload128(rx, act_voff[i], tau * KW * 512u);
+      for (int i = 0; i < SL::NACT; ++i) {
+        const int j = wave * SL::NACT + i;      // k-step; waves past the 8th load nothing
+        dma16(rx, j < 8 ? base + SL::ACT + j * 1024 : s_dummy,
+              (live && j < 8 && act_vo != OOB) ? act_vo + j * 64u : OOB, st * 512u);
+      }
 #pragma unroll
-      for (int p = 0; p < NP; ++p) R.sz[p] = bload64(rs[p], szl * 8u, st * NG * 64u);
-      R.sum = bload64(rsm, sum_voff, tau * KW * NG * 8u);
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < SL::NSZ; ++i) {
+          const int w = 64 * i + lane;
+          dma4(rs[p], base + SL::SZ + ((wave * NP + p) * SL::SZW + 64 * i) * 4,
+               (live && w < NG * 16) ? w * 4u : OOB, st * NG * 64u);
+        }
+      dma4(rsm, wave < SL::NSUM ? base + SL::SUM + wave * 256 : s_dummy,
+           live ? sum_vo : OOB, st * NG * 8u);
     };
-    auto deposit = [&](const DecRing<NP, KW>& R, int sl) {
-      char* base = lds + sl * LD::SLOT;
-#pragma unroll
-      for (int i = 0; i < 2 * KW; ++i) *reinterpret_cast<u32x4*>(base + act_lds[i]) = R.act[i];
-      *reinterpret_cast<u32x2*>(base + sum_lds) = R.sum;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) *reinterpret_cast<u32x2*>(base + sz_lds + p * NG * 64) = R.sz[p];
-    };
 
-    f32x4 acc[NP];
+    f32x4 acc[NP], corr[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < NP; ++p) {
+      acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+      corr[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
+    // acc += s_g * C_g for the wave's rows 4 lg + v
     auto fold = [&](const f32x4 (&C)[NP], const char* base, int gi) {
-      const float2 xs = *reinterpret_cast<const float2*>(
-          base + LD::ACT + ((kw * NG + gi) * 16 + l16) * 8);
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(
-            base + LD::ACT + LD::SUM + ((wave * NP + p) * NG + gi) * 64 + lg * 16);
+            base + SL::SZ + ((wave * NP + p) * SL::SZW + gi * 16 + 4 * lg) * 4);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float sc = (float)__builtin_bit_cast(half_t, (uint16_t)(w[v] & 0xFFFFu));
-          const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(w[v] >> 16));
-          acc[p][v] += sc * (C[p][v] - xs.y - z * xs.x);
+        for (int v = 0; v < 4; ++v)
+          acc[p][v] += (float)__builtin_bit_cast(half_t, (uint16_t)(w[v] & 0xFFFFu)) * C[p][v];
+      }
+    };
+
+    // corr += A . B with A[row][t] = s_t (t < NG) or s z of group t - NG, and
+    // B[t][col] = X'_t resp. X~_(t - NG): MFMA m covers terms t = 4 m + lg
+    auto correction = [&](const char* base) {
+#pragma unroll
+      for (int m = 0; m < NCORR; ++m) {
+        const int t = 4 * m + lg;
+        const int g = (t < NG) ? t : t - NG;
+        float bx = 0.f;
+        if (t < 2 * NG)
+          bx = *reinterpret_cast<const float*>(base + SL::SUM + ((g * 16 + l16) * 2 + (t < NG)) * 4);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          float av = 0.f;
+          if (t < 2 * NG) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(
+                base + SL::SZ + ((wave * NP + p) * SL::SZW + g * 16 + l16) * 4);
+            const float sc = (float)__builtin_bit_cast(half_t, (uint16_t)(w & 0xFFFFu));
+            const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(w >> 16));
+            av = (t < NG) ? sc : sc * z;
+          }
+          corr[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bx, corr[p], 0, 0, 0);
         }
       }
     };
 
-    auto compute = [&](const u32x4 (&code)[NP], int sl) {
-      const char* base = lds + sl * LD::SLOT;
-      const char* ab = base + ((kw * 16 + l16) * ALD + 8 * lg) * 2;
+    auto compute = [&](const char* base) {
+      u32x4 code[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        code[p] = *reinterpret_cast<const u32x4*>(base + SL::CODE + ((wave * NP + p) * 64 + lane) * 16);
+      const char* ab = base + SL::ACT + lane * 16;
       f32x4 C[NP];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -172,7 +265,7 @@ __global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs a) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const int j = 2 * d + b;
-          const half8v bv = *reinterpret_cast<const half8v*>(ab + j * 64);
+          const half8v bv = *reinterpret_cast<const half8v*>(ab + j * 1024);
           if (j % GS == 0) {
 #pragma unroll
             for (int p = 0; p < NP; ++p) C[p] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -182,33 +275,39 @@ __global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs a) {
           if (j % GS == GS - 1) fold(C, base, j / GS);
         }
       }
+      correction(base);
     };
 
-    // full stages: ring of DEPTH stage-times in registers, double-buffered LDS
+    // full stages.  Ring: batch b lands in slot b % NSLOT; at stage-time tau
+    // the wave waits for batch tau (DEPTH - 1 newer batches may stay in
+    // flight), the barrier makes every wave's part visible, the stage is
+    // computed, then batch tau + DEPTH is issued into the slot of tau - 1,
+    // which every wave finished before this barrier.  Slots are distinct LDS
+    // arrays indexed by constants: the ring is unrolled by its length and
+    // whole rounds always run (stage-times past the end only wait and issue
+    // empty loads), so the loop has a single back edge and the compiler's
+    // own wait counts stay exact.
     if (ntau > 0) {
-      DecRing<NP, KW> R[DEPTH];
 #pragma unroll
-      for (int u = 0; u < DEPTH; ++u) issue(u, R[u]);
-      for (int t = 0; t < ntau; t += DEPTH) {
+      for (int b = 0; b < DEPTH; ++b) issue(b, slot[b]);
+      for (int t = 0; t < ntau; t += NSLOT) {
 #pragma unroll
-        for (int u = 0; u < DEPTH; ++u) {
+        for (int u = 0; u < NSLOT; ++u) {
           const int tau = t + u;
-          if (tau >= ntau) break;
-          const int sl = tau & 1;
-          deposit(R[u], sl);
-          u32x4 code[NP];
-#pragma unroll
-          for (int p = 0; p < NP; ++p) code[p] = R[u].code[p];
-          issue(tau + DEPTH, R[u]);        // refill the slot; past the end the buffers read zeros
-          __syncthreads();
-          if (tau * KW + kw < nfull) compute(code, sl);
+          wait_vm<SL::NI * (DEPTH - 1)>();
+          bar_nofence();
+          if (tau < ntau) compute(slot[u]);
+          issue(tau + DEPTH, slot[(u + DEPTH) % NSLOT]);
         }
       }
-      __syncthreads();
+      // every load has landed and every wave is done with the ring before
+      // the next tile reuses it
+      wait_vm<0>();
+      bar_nofence();
     }
 
     // 4-step tail stage (d_in % 256 == 128; then GS <= 4): direct loads
-    if (tail && kw == nfull % KW) {
+    if (tail) {
       const int st = nfull;
       const half_t* xrow = reinterpret_cast<const half_t*>(a.Xp) + (size_t)arow * a.d_in + 8 * lg;
       const float* srow = a.sums + (size_t)arow * ng * 2;
@@ -252,32 +351,12 @@ __global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs a) {
       }
     }
 
-    if constexpr (KW > 1) {
-      if (kw > 0) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            s_red[(((rsub * (KW - 1) + kw - 1) * NP + p) * 64 + lane) * 4 + v] = acc[p][v];
-      }
-      __syncthreads();
-      if (kw == 0) {
-#pragma unroll
-        for (int q = 0; q < KW - 1; ++q)
-#pragma unroll
-          for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[p][v] += s_red[(((rsub * (KW - 1) + q) * NP + p) * 64 + lane) * 4 + v];
-      }
-    }
-
-    if (kw == 0 && rvalid) {
+    if (rvalid) {
       const int E = a.ex[arow];
 #pragma unroll
       for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[p][v] = ldexpf(acc[p][v], E);
+        for (int v = 0; v < 4; ++v) acc[p][v] = ldexpf(acc[p][v] - corr[p][v], E);
       const int o = rb * 16 + 4 * lg;
       if constexpr (MODE == MODE_GATEUP) {
 #pragma unroll
@@ -287,7 +366,7 @@ __global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs a) {
           const int rp = pd.r_pad;
           const T* up = reinterpret_cast<const T*>(pd.U) +
                         ((size_t)pd.m_of[e] * a.d_out + rb * 16 + l16) * rp + 8 * lg;
-          const int col = a.slot2col[p][slot];
+          const int col = a.slot2col[p][slotid];
           const float* prow = a.P[p] + (size_t)col * rp + 8 * lg;
           const float* sg = pd.sigma + 8 * lg;
           for (int s2 = 0; s2 < rp; s2 += 32) {
@@ -313,44 +392,56 @@ __global__ __launch_bounds__(256) void gemm_dec_kernel(DecArgs a) {
         }
       } else {
         if (cvalid) {
-          const float g = a.gates[slot];
-          *reinterpret_cast<f32x4*>(a.dres + (size_t)pos * a.d_out + o) = acc[0] * g;
+          const float g = a.gates[slotid];
+          *reinterpret_cast<f32x4*>(a.dres + ((size_t)ks * a.S + pos) * a.d_out + o) = acc[0] * g;
         }
       }
     }
-    if constexpr (KW > 1) __syncthreads();
   }
 }
 
-template <typename T, int MODE, int KW>
+template <typename T, int MODE, int GS, int WAVES, int DMAX>
+static void dec_launch(const DecArgs& a, hipStream_t s) {
+  constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
+  constexpr int BYTES = DecSlot<NP, WAVES, 8 / GS>::BYTES;
+  if constexpr (WAVES > 8 && ring_depth<BYTES, DMAX>() < 2) {
+    // slots too large for a ring of three: fall back to 8 waves
+    dec_launch<T, MODE, GS, 8, DMAX>(a, s);
+  } else {
+    const int nrb = a.d_out >> 4;
+    const int nby = (nrb + WAVES - 1) / WAVES;
+    const dim3 grid(a.K * ((nby + 7) / 8) * 8 * a.nks);
+    hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, GS, WAVES, DMAX>), grid, dim3(64 * WAVES), 0, s, a);
+  }
+}
+
+template <typename T, int MODE, int WAVES, int DMAX>
 static void dec_gs(const DecArgs& a, hipStream_t s) {
-  const int nrb = a.d_out >> 4;
-  const dim3 grid(a.K, (nrb + (4 / KW) - 1) / (4 / KW));
   switch (a.p[0].group >> 5) {
-    case 1: hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, KW, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, KW, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, KW, 4>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, KW, 8>), grid, dim3(256), 0, s, a); break;
+    case 1: dec_launch<T, MODE, 1, WAVES, DMAX>(a, s); break;
+    case 2: dec_launch<T, MODE, 2, WAVES, DMAX>(a, s); break;
+    case 4: dec_launch<T, MODE, 4, WAVES, DMAX>(a, s); break;
+    default: dec_launch<T, MODE, 8, WAVES, DMAX>(a, s); break;
   }
 }
 
 template <typename T, int MODE>
-static void dec_kw(const DecArgs& a, int kw, hipStream_t s) {
-  // the group-sum table of a stage-time (KW * NG * 16 entries) must fit the
-  // 256 threads of a workgroup: KW = 4 needs groups of >= 64 inputs
-  if (kw == 4 && (a.p[0].group >> 5) == 1) kw = 2;
-  if (kw == 1) dec_gs<T, MODE, 1>(a, s);
-  else if (kw == 2) dec_gs<T, MODE, 2>(a, s);
-  else dec_gs<T, MODE, 4>(a, s);
+static void dec_waves(const DecArgs& a, hipStream_t s) {
+  if (a.waves == 16) dec_gs<T, MODE, 16, 6>(a, s);
+  else dec_gs<T, MODE, 8, 6>(a, s);
 }
 
-void launch_gemm_decode(const DecArgs& a, GemmMode mode, int kw, Act act, hipStream_t s) {
+// Ring depth: as many slots as fit the LDS budget (at most 7).  With 16 waves
+// a gate/up slot holds 32 KB of codes (3 slots), a down / single slot 16 KB
+// (5 slots); with 8 waves 16 resp. 8 KB (5 resp. 7 slots).  One workgroup
+// per CU either way.
+void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s) {
   if (act == ACT_F16) {
-    if (mode == MODE_GATEUP) dec_kw<half_t, MODE_GATEUP>(a, kw, s);
-    else dec_kw<half_t, MODE_RES>(a, kw, s);
+    if (mode == MODE_GATEUP) dec_waves<half_t, MODE_GATEUP>(a, s);
+    else dec_waves<half_t, MODE_RES>(a, s);
   } else {
-    if (mode == MODE_GATEUP) dec_kw<__bf16, MODE_GATEUP>(a, kw, s);
-    else dec_kw<__bf16, MODE_RES>(a, kw, s);
+    if (mode == MODE_GATEUP) dec_waves<__bf16, MODE_GATEUP>(a, s);
+    else dec_waves<__bf16, MODE_RES>(a, s);
   }
 }
 

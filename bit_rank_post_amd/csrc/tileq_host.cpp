@@ -90,12 +90,13 @@ void proj_dims(const tq_layer* L, int which, int* d_in, int* d_out) {
 // ---- workspace plan --------------------------------------------------------
 struct Plan {
   int T, k, S, path, bm_gemm, rt_col, max_tiles_gemm, max_col_tiles;
+  int nks;                       // k-chunks (fp32 slabs) of the last projection's residual
   size_t flags, cnt, off, perm, inv, tile_gemm, tile_colx, colmask, cntw, rank;
   size_t col_off[2], col_tok[2], slot2col[2], tile_col[2];
   size_t P[3];
   int nsplit[3];
   int rows_cap;
-  size_t zero_base, hamax, counters;   // contiguous region zeroed by the route kernel
+  size_t zero_base, hamax;       // region zeroed by the route kernel
   int zero_n;
   size_t ex, h, dres, hs, ys;
   size_t xp, sums_x, ex_x, hp, sums_h, ex_h;   // decode activation preparation
@@ -105,8 +106,10 @@ struct Plan {
 // The decode kernel covers groups that do not straddle its 256-input stages
 // and needs one group size for the projections that share an input.
 bool decode_ok(const tq_layer* L) {
-  for (int q = 0; q < nproj(L); ++q)
-    if (L->proj[q].dev.group > 256) return false;
+  for (int q = 0; q < nproj(L); ++q) {
+    const int g = L->proj[q].dev.group;
+    if (g > 256 || (g & (g - 1)) != 0) return false;   // 32, 64, 128 or 256
+  }
   if (L->kind == TQ_SWIGLU && L->proj[0].dev.group != L->proj[1].dev.group) return false;
   return true;
 }
@@ -116,6 +119,9 @@ int choose_path(const tq_layer* L, int T, int k) {
   if (L->path_override == 1 || L->path_override == 2) path = L->path_override;
   else path = ((long)T * k <= 16L * L->K) ? 1 : 2;
   if (path == 1 && !decode_ok(L)) path = 2;
+  // the decode kernel addresses its activation rows with 32-bit buffer
+  // offsets below 2^31
+  if (path == 1 && (long)T * k * std::max(L->d_model, L->d_ff) * 2 >= 0x7FFFFFF0L) path = 2;
   return path;
 }
 
@@ -127,13 +133,26 @@ int choose_nsplit(int path, long rows, int d_in) {
   return std::max(1, ((d_in >> 5) + 15) / 16);
 }
 
-// waves splitting the k-range of the same rows in the decode kernel
-int choose_kw(const tq_layer* L, int q, int S) {
+// k-chunks of the decode kernel for a down / single projection: enough
+// 16-wave workgroups (one per CU at a time) that every CU streams even when
+// only a few experts are active; each chunk keeps at least 4 stages.  Each
+// chunk writes its own fp32 slab of per-slot outputs.
+int choose_nks(const tq_layer* L, int q, int S) {
+  const ProjDev& d = L->proj[q].dev;
   const long active = std::min<long>(L->K, S);
-  const long nrb = L->proj[q].dev.nrb;
-  for (int kw = 1; kw < 4; kw *= 2)
-    if (active * nrb * kw >= 4096) return kw;
-  return 4;
+  const long wgs = active * ((d.nrb + 15) / 16);
+  const int nfull = (d.d_in >> 5) >> 3;
+  int nks = 1;
+  while (nks < 8 && wgs * nks < 512 && nfull / (2 * nks) >= 4) nks *= 2;
+  return nks;
+}
+
+// waves per decode workgroup: 16 (four per SIMD) when that still gives every
+// CU a workgroup, else 8
+int choose_waves(const tq_layer* L, int q, int S, int nks) {
+  const long active = std::min<long>(L->K, S);
+  const long wg16 = active * ((L->proj[q].dev.nrb + 15) / 16) * nks;
+  return wg16 >= 256 ? 16 : 8;
 }
 
 Plan make_plan(const tq_layer* L, int T, int k, int path) {
@@ -181,17 +200,17 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
     if (d.r_pad > 0) p.P[q] = take((size_t)p.nsplit[q] * S * d.r_pad * sizeof(float));
   }
   const bool bf = (L->act == TQ_BF16);
-  // zeroed region: |h| maxima (bf16 SwiGLU, prefill) + split-K tile counters
+  // zeroed region: |h| maxima (bf16 SwiGLU, prefill)
   const int nham = (bf && L->kind == TQ_SWIGLU) ? S : 0;
-  p.zero_n = nham + 3 * p.max_col_tiles;
-  p.zero_base = take(sizeof(unsigned) * p.zero_n);
+  p.zero_n = nham;
+  p.zero_base = take(sizeof(unsigned) * std::max(p.zero_n, 1));
   p.hamax = p.zero_base;
-  p.counters = p.zero_base + sizeof(unsigned) * nham;
   p.ex = take(sizeof(int) * (bf ? std::max(T, 1) : 1));
   p.h = take(L->kind == TQ_SWIGLU ? (size_t)S * L->d_ff * 2 : 0);
   int d_in_last, d_out_last;
   proj_dims(L, nproj(L) - 1, &d_in_last, &d_out_last);
-  p.dres = take((size_t)S * d_out_last * sizeof(float));
+  p.nks = (path == 1) ? choose_nks(L, nproj(L) - 1, S) : 1;
+  p.dres = take((size_t)p.nks * S * d_out_last * sizeof(float));
   if (L->shared.d_ff > 0) {
     p.hs = take((size_t)T * L->shared.d_ff * 2);
     p.ys = take((size_t)T * L->d_model * sizeof(float));
@@ -282,7 +301,6 @@ ColArgs col_args_x(const tq_layer* L, const Plan& p, int c, const void* x, void*
   a.steps_per_split = ((d.d_in >> 5) + p.nsplit[c] - 1) / p.nsplit[c];
   a.P = at<float>(ws, p.P[c]);
   a.rows_cap = p.rows_cap;
-  a.counters = at<int>(ws, p.counters) + c * p.max_col_tiles;
   return a;
 }
 
@@ -304,7 +322,6 @@ ColArgs col_args_down(const tq_layer* L, const Plan& p, const void* h, void* ws)
   a.steps_per_split = ((d.d_in >> 5) + p.nsplit[2] - 1) / p.nsplit[2];
   a.P = at<float>(ws, p.P[2]);
   a.rows_cap = p.rows_cap;
-  a.counters = at<int>(ws, p.counters) + 2 * p.max_col_tiles;
   return a;
 }
 
@@ -584,11 +601,17 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
         da.slot2col[c] = at<int>(ws, p.slot2col[c]);
       }
       da.h = h;
-      launch_gemm_decode(da, MODE_GATEUP, choose_kw(L, 0, p.S), act, s);
+      da.nks = 1;
+      da.S = p.S;
+      da.waves = choose_waves(L, 0, p.S, 1);
+      launch_gemm_decode(da, MODE_GATEUP, act, s);
     } else {
       da.dres = dres;
       da.gates = topk_w;
-      launch_gemm_decode(da, MODE_RES, choose_kw(L, 0, p.S), act, s);
+      da.nks = p.nks;
+      da.S = p.S;
+      da.waves = choose_waves(L, 0, p.S, p.nks);
+      launch_gemm_decode(da, MODE_RES, act, s);
     }
   } else {
     GemmArgs ga{};
@@ -682,7 +705,10 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.p[0] = dd;
       da.dres = dres;
       da.gates = topk_w;
-      launch_gemm_decode(da, MODE_RES, choose_kw(L, 2, p.S), act, s);
+      da.nks = p.nks;
+      da.S = p.S;
+      da.waves = choose_waves(L, 2, p.S, p.nks);
+      launch_gemm_decode(da, MODE_RES, act, s);
     } else {
       GemmArgs ga{};
       ga.K = K;
@@ -729,6 +755,8 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     cb.sigma = d.sigma;
     cb.U = d.U;
     cb.dres = dres;
+    cb.nks = p.nks;
+    cb.S = p.S;
     cb.ys = ys;
     cb.y = y;
     cb.y_dtype = (int)y_dtype;

@@ -83,7 +83,6 @@ struct ColArgs {
   int nsplit, steps_per_split;
   float* P;
   int rows_cap;                  // rows per split slab
-  int* counters;                 // per-tile arrival counters (nsplit > 1), zeroed
 };
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
                     hipStream_t s);
@@ -131,10 +130,13 @@ struct DecArgs {
   const float* P[2];             // column-stage results [rows][r_pad] (GATEUP)
   const int* slot2col[2];
   void* h;                       // GATEUP out [S][d_out] act
-  float* dres;                   // RES out [S][d_out] f32
+  float* dres;                   // RES out [nks][S][d_out] f32 (one slab per k-chunk)
   const float* gates;
+  int nks;                       // k-chunks (RES; 1 for GATEUP)
+  int S;                         // slots (slab stride of dres)
+  int waves;                     // waves per workgroup: 8 or 16 (16 rows each)
 };
-void launch_gemm_decode(const DecArgs& a, GemmMode mode, int kw, Act act, hipStream_t s);
+void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s);
 
 // ---- activation preparation for the decode kernel ---------------------------
 struct PrepArgs {
@@ -159,7 +161,8 @@ struct CombineArgs {
   int nsplit, rows_cap;
   const float* sigma;
   const void* U;
-  const float* dres;
+  const float* dres;             // [nks][S][d_out]
+  int nks, S;
   const float* ys;               // shared expert output [T][d_out] f32 or nullptr
   void* y;
   int y_dtype;                   // 0 f16, 1 bf16, 2 f32
