@@ -52,13 +52,13 @@ WORKLOADS = {
 KERNEL_SOURCES = {
     "decode": ["bit_rank_post_amd/csrc/gemm_decode.hip", "bit_rank_post_amd/csrc/tq_device.h",
                "bit_rank_post_amd/csrc/tq_internal.h"],
-    "prefill": ["bit_rank_post_amd/csrc/moe_gemm.hip", "bit_rank_post_amd/csrc/tq_device.h",
+    "prefill": ["bit_rank_post_amd/csrc/gemm_prefill.hip", "bit_rank_post_amd/csrc/tq_device.h",
                 "bit_rank_post_amd/csrc/tq_internal.h"],
 }
 KERNEL_NAMES = {
     "decode": "gemm_dec_kernel (gate+up streaming 2-bit residual GEMV/MFMA with low-rank "
               "row stage and SwiGLU epilogue)",
-    "prefill": "moe_gemm_kernel (gate+up grouped 2-bit dequant MFMA GEMM with low-rank "
+    "prefill": "gemm_pre_kernel (gate+up grouped 2-bit dequant MFMA GEMM with low-rank "
                "K-extension and SwiGLU epilogue)",
 }
 

@@ -32,36 +32,6 @@
 
 namespace tq {
 
-typedef __attribute__((address_space(3))) void lds_t;
-
-// out-of-range voffset: the load returns zeros and reads no memory (only the
-// vector offset is range checked, so every scalar offset stays in range)
-constexpr uint32_t OOB = 0x7FFFFFF0u;
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
-                                      uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
-                                     uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 4, voff, soff, 0, 0);
-}
-
-// wait until at most N vector-memory loads of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
-// workgroup barrier without a memory fence; the empty asm statements keep
-// the compiler from moving LDS accesses across it
-__device__ __forceinline__ void bar_nofence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // LDS slot layout (bytes) for NP projections, WAVES waves, NG groups/stage
 template <int NP, int WAVES, int NG>
 struct DecSlot {

@@ -1,0 +1,398 @@
+// Prefill-path grouped 2-bit residual GEMM, with the low-rank row stage folded
+// in as extra MFMA k-steps and the epilogues fused.
+//
+// "TileQ" technical summary, section 2.1 step 5: each expert's weight is the
+// shared low-rank block plus its quantized residual; section 2.2: the
+// low-rank part is done once per shared factor for all active experts (here
+// the column stage computed p = V_n^T x once per (column, token) beforehand),
+// the residual product is per expert, over the whole batch.
+//
+// Work item (one workgroup of 8 waves) = (expert, tile of BN = 16 NF of that
+// expert's slots, 16 RF WAVES output rows).  Each wave owns RF 16-row
+// fragments (of both gate and up in MODE_GATEUP) against all NF token
+// fragments.  K advances in stages of 128 inputs (4 MFMA k-steps); each
+// stage's activation tile (BN x 128, fp16), the waves' codes and their
+// scale/zero words arrive in LDS by buffer loads with the LDS destination, in
+// a ring of DEPTH + 1 slots, so loads run DEPTH stages ahead of the MFMAs.
+// The codes of a k-step pair are unpacked in registers into the exact fp16
+// weights RND_f16(s (q - z)) (deq_dword) and fed to v_mfma_f32_16x16x32_f16.
+//
+// MODE_GATEUP: gate and up rows of the same expert together; the row stage
+//   U_m (Sigma p) follows as extra k-steps (U_m rows as A, Sigma p split into
+//   a high and a low part in the activation dtype as B); then
+//   h = RND_act(silu(gate) * up).
+// MODE_RES: one projection (down, or single); result times the slot's routing
+//   weight into the fp32 per-slot buffer summed by the combine kernel.
+// Activations are fp16 here; bfloat16 rows were converted exactly to fp16
+// after a per-row power-of-two scaling 2^-E (rows_to_f16), undone on the
+// fp32 result.
+#include "tq_device.h"
+
+namespace tq {
+
+constexpr int PF_WAVES = 8;
+
+// GS: k-steps per quantization group when G is a power of two >= 32
+// (1, 2, 4, 8); GS = 0: any G (constants per k-step).  NGS: groups a stage
+// needs constants for (k-step granularity when GS <= 1).
+template <int GS> struct PfGroups { static constexpr int NGS = (GS <= 1) ? 4 : (GS == 2 ? 2 : 1); };
+
+// LDS slot layout (bytes).  Scale/zero words of a wave and projection: word
+// gi * SZG + r * 16 + row for group slot gi, fragment r, row; loaded by NSZ
+// dword loads of 64 lanes.
+template <int NP, int RF, int NF, int GS>
+struct PfSlot {
+  static constexpr int NGS = PfGroups<GS>::NGS;
+  static constexpr int SZG = (GS == 0) ? 64 : RF * 16;
+  static constexpr int NSZ = (GS == 0) ? 4 : (NGS * RF * 16 + 63) / 64;
+  static constexpr int B = 0;                                  // [4][NF][64] x 16 B
+  static constexpr int CODE = B + 4 * NF * 1024;                // [W][RF][NP][2][64] x 4 B
+  static constexpr int SZ = CODE + PF_WAVES * RF * NP * 2 * 256;   // [W][NP][NSZ][64] x 4 B
+  static constexpr int BYTES = SZ + PF_WAVES * NP * NSZ * 256;
+  static constexpr int NB = 4 * NF / PF_WAVES;                 // activation loads per wave
+  static constexpr int NI = NB + RF * NP * 2 + NP * NSZ;       // loads per wave per stage
+};
+
+template <typename T, int MODE, int RF, int NF, int GS>
+__global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
+  typedef typename Vec8<T>::type V8;
+  constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
+  constexpr int BN = 16 * NF;
+  constexpr int NGS = PfGroups<GS>::NGS;
+  typedef PfSlot<NP, RF, NF, GS> SL;
+  constexpr int DEPTH = 2;
+  constexpr int NSLOT = DEPTH + 1;
+  static_assert(NSLOT * SL::BYTES <= 160 * 1024 - 2048, "LDS budget");
+  static_assert(SL::NI * (DEPTH - 1) < 64, "vmcnt range");
+  static_assert(RF * 16 <= 64, "scale/zero load covers the wave's rows");
+  __shared__ __attribute__((aligned(16))) char s0[SL::BYTES];
+  __shared__ __attribute__((aligned(16))) char s1[SL::BYTES];
+  __shared__ __attribute__((aligned(16))) char s2[SL::BYTES];
+  __shared__ int s_src[BN];
+  __shared__ int s_exp[BN];
+  __shared__ int s_res;
+  char* const slot[3] = {s0, s1, s2};
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int nrb = a.d_out >> 4;
+  const int rows_per_wg = 16 * RF * PF_WAVES;
+  const int nrt = (a.d_out + rows_per_wg - 1) / rows_per_wg;
+  const int rt = blockIdx.x % nrt;
+  const int tq = blockIdx.x / nrt;
+  // the routing tiles hold 128 slots; with 64-slot tiles each is done in two
+  // halves (tile_half)
+  const int tile = a.tile_half ? tq >> 1 : tq;
+  const int e = find_segment(a.tile_off, a.K, tile, &s_res);
+  if (e < 0) return;
+  const int lt = tile - a.tile_off[e];
+  const int pos0 = a.off[e] + lt * 128 + (a.tile_half ? (tq & 1) * 64 : 0);
+  const int nv = min(BN, a.cnt[e] - (pos0 - a.off[e]));
+  if (nv <= 0) return;
+  const int rb0 = rt * RF * PF_WAVES + wave * RF;     // first row block of this wave
+
+  if (tid < BN) {
+    int src = -1, ex = 0;
+    if (tid < nv) {
+      const int pos = pos0 + tid;
+      src = a.gather ? a.perm[pos] / a.topk : pos;
+      if (a.ex) ex = a.ex[src];
+    }
+    s_src[tid] = src;
+    s_exp[tid] = ex;
+  }
+  __syncthreads();
+
+  const int nstage = a.d_in >> 7;
+  const int nfull = a.d_in >> 8;                  // full 8-step code groups
+  const bool has_tail = (a.d_in & 255) != 0;      // last stage is a 4-step tail group
+  const int ng = a.p[0].ng;
+  const int G = a.p[0].group;
+  const size_t cpe = (size_t)a.d_out * (a.d_in >> 4);
+
+  const int row_lo = s_src[0];
+  const int row_hi = s_src[max(nv - 1, 0)];
+  // per-lane load offsets
+  // activations: load i of this wave is (k-step j, token fragment f)
+  uint32_t b_vo[SL::NB];
+#pragma unroll
+  for (int i = 0; i < SL::NB; ++i) {
+    const int q = wave * SL::NB + i;
+    const int j = q / NF, f = q - j * NF;
+    const int src = s_src[16 * f + l16];
+    b_vo[i] = (src >= 0) ? ((uint32_t)(src - row_lo) * a.d_in + 32 * j + 8 * lg) * 2u : OOB;
+  }
+  // codes and scale/zero words: one buffer per (fragment, projection)
+  __amdgpu_buffer_rsrc_t rc[RF][NP], rs[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+#pragma unroll
+    for (int r = 0; r < RF; ++r) {
+      const int rb = min(rb0 + r, nrb - 1);
+      rc[r][p] = make_rsrc(a.p[p].codes + (size_t)e * cpe + (size_t)rb * (a.d_in >> 4) * 16,
+                           (uint32_t)(a.d_in >> 4) * 64u);
+    }
+    const int rbc = min(rb0, nrb - 1);
+    rs[p] = make_rsrc(a.p[p].sz + ((size_t)e * nrb + rbc) * ng * 16,
+                      (uint32_t)(min(RF, nrb - rbc) * ng * 64));
+  }
+  // activation rows of the tile, addressed from its first row (rows ascend
+  // inside a tile)
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(
+      reinterpret_cast<const half_t*>(a.A) + (size_t)max(row_lo, 0) * a.d_in,
+      (uint32_t)min<size_t>((size_t)(row_hi - row_lo + 1) * a.d_in * 2u, (size_t)OOB));
+  // scale/zero loads: load n, lane l -> word w = 64 n + l = gi * SZG + r * 16 + row
+  uint32_t sz_vo[SL::NSZ];
+#pragma unroll
+  for (int n = 0; n < SL::NSZ; ++n) {
+    const int w = 64 * n + lane;
+    const int gi = w / SL::SZG, r = (w % SL::SZG) >> 4, row = w & 15;
+    const bool ok = gi < NGS && r < RF && rb0 + r < nrb;
+    const int gofs = (GS == 0) ? 0 : gi;       // generic G: one load per group slot
+    sz_vo[n] = ok ? (((uint32_t)(r * ng + gofs)) * 16u + row) * 4u : OOB;
+  }
+  // stage order rotated by row tile: workgroups that share an activation tile
+  // start at different stages
+  const int r0 = rt % nstage;
+
+  auto issue = [&](int b, char* base) {
+    const bool live = b < nstage;
+    int st = b + r0;
+    st = (st >= nstage) ? st - nstage : st;
+    st = live ? st : 0;
+#pragma unroll
+    for (int i = 0; i < SL::NB; ++i) {
+      const int q = wave * SL::NB + i;
+      dma16(rx, base + SL::B + q * 1024, live ? b_vo[i] : OOB, st * 256u);
+    }
+    const bool tl = has_tail && st == nstage - 1;
+    const uint32_t c_vo = tl ? lane * 8u : lane * 16u;
+    const uint32_t c_so = tl ? nfull * 1024u : (st >> 1) * 1024u + (st & 1) * 8u;
+#pragma unroll
+    for (int r = 0; r < RF; ++r)
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          dma4(rc[r][p], base + SL::CODE + (((wave * RF + r) * NP + p) * 2 + i) * 256,
+               live ? c_vo + i * 4u : OOB, c_so);
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int n = 0; n < SL::NSZ; ++n) {
+        // first group of the stage (power-of-two G: the stage's groups are
+        // consecutive), or the group of k-step n (any G)
+        const int g = (GS == 0) ? (st * 128 + n * 32) / G : (st * 128) / (32 * (GS == 0 ? 1 : GS));
+        dma4(rs[p], base + SL::SZ + ((wave * NP + p) * SL::NSZ + n) * 256,
+             live ? sz_vo[n] : OOB, g * 64u);
+      }
+  };
+
+  f32x4 acc[NP][RF][NF];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int r = 0; r < RF; ++r)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[p][r][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const char* base) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      half8v bfr[2][NF];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          bfr[b][f] = *reinterpret_cast<const half8v*>(
+              base + SL::B + (((2 * d + b) * NF + f) * 64 + lane) * 16);
+#pragma unroll
+      for (int r = 0; r < RF; ++r)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const uint32_t D = *reinterpret_cast<const uint32_t*>(
+              base + SL::CODE + (((wave * RF + r) * NP + p) * 2 + d) * 256 + lane * 4);
+          // scale/zero words of this lane's row for k-steps 2d and 2d+1
+          const int gi0 = (NGS == 4) ? 2 * d : (NGS == 2 ? d : 0);
+          const int gi1 = (NGS == 4) ? 2 * d + 1 : gi0;
+          const char* zb = base + SL::SZ + (wave * NP + p) * SL::NSZ * 256 + (r * 16 + l16) * 4;
+          const DeqConst c0 = deq_const(*reinterpret_cast<const uint32_t*>(zb + gi0 * SL::SZG * 4));
+          half8v a0, a1;
+          if (gi1 == gi0) {
+            deq_dword(D, c0, c0, a0, a1);
+          } else {
+            const DeqConst c1 = deq_const(*reinterpret_cast<const uint32_t*>(zb + gi1 * SL::SZG * 4));
+            deq_dword(D, c0, c1, a0, a1);
+          }
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            acc[p][r][f] = mfma16(a0, bfr[0][f], acc[p][r][f]);
+            acc[p][r][f] = mfma16(a1, bfr[1][f], acc[p][r][f]);
+          }
+        }
+    }
+  };
+
+  // ring over stages (see gemm_decode.hip for the protocol): whole rounds
+  // always run, stage-times past the end only wait and issue empty loads
+#pragma unroll
+  for (int b = 0; b < DEPTH; ++b) issue(b, slot[b]);
+  for (int t = 0; t < nstage; t += NSLOT) {
+#pragma unroll
+    for (int u = 0; u < NSLOT; ++u) {
+      const int tau = t + u;
+      wait_vm<SL::NI * (DEPTH - 1)>();
+      bar_nofence();
+      if (tau < nstage) compute(slot[u]);
+      issue(tau + DEPTH, slot[(u + DEPTH) % NSLOT]);
+    }
+  }
+  wait_vm<0>();
+  __syncthreads();
+
+  // undo the per-row power-of-two scaling of converted bfloat16 rows
+  if (a.ex) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int ex = s_exp[16 * f + l16];
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int r = 0; r < RF; ++r)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[p][r][f][v] = ldexpf(acc[p][r][f][v], ex);
+    }
+  }
+
+  if constexpr (MODE == MODE_GATEUP) {
+    // low-rank row stage as extra k-steps: A = U_m rows, B = Sigma p (hi, lo)
+    constexpr int EXT_LD = 64 + 8;      // rank chunk of 64 (+ pad), halves
+    static_assert(2 * BN * EXT_LD * 2 <= SL::BYTES, "row-stage staging fits a slot");
+    T* s_ext = reinterpret_cast<T*>(s0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const ProjDev& pd = a.p[p];
+      const int rp = pd.r_pad;
+      if (pd.rank == 0) continue;
+      const int m = pd.m_of[e];
+      for (int rc0 = 0; rc0 < rp; rc0 += 64) {
+        const int rw = min(64, rp - rc0);
+        __syncthreads();
+        for (int i = tid; i < BN * rw; i += 64 * PF_WAVES) {
+          const int row = i / rw, c = i - row * rw;
+          T hi = from_f32<T>(0.f), lo = from_f32<T>(0.f);
+          if (row < nv) {
+            const int slotid = a.perm[pos0 + row];
+            const int col = a.slot2col[p][slotid];
+            float v = 0.f;
+            for (int sp = 0; sp < a.nsplit[p]; ++sp)
+              v += a.P[p][((size_t)sp * a.rows_cap[p] + col) * rp + rc0 + c];
+            v *= pd.sigma[rc0 + c];
+            hi = from_f32<T>(v);
+            lo = from_f32<T>(v - to_f32(hi));
+          }
+          s_ext[row * EXT_LD + c] = hi;
+          s_ext[BN * EXT_LD + row * EXT_LD + c] = lo;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < RF; ++r) {
+          if (rb0 + r >= nrb) continue;
+          const T* up = reinterpret_cast<const T*>(pd.U) +
+                        ((size_t)m * a.d_out + (rb0 + r) * 16 + l16) * rp + rc0 + 8 * lg;
+          for (int s2 = 0; s2 < rw; s2 += 32) {
+            const V8 av = *reinterpret_cast<const V8*>(up + s2);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              const T* bp = &s_ext[(16 * f + l16) * EXT_LD + s2 + 8 * lg];
+              const V8 bh = *reinterpret_cast<const V8*>(bp);
+              const V8 bl = *reinterpret_cast<const V8*>(bp + BN * EXT_LD);
+              acc[p][r][f] = mfma16(av, bh, acc[p][r][f]);
+              acc[p][r][f] = mfma16(av, bl, acc[p][r][f]);
+            }
+          }
+        }
+      }
+    }
+    // SwiGLU epilogue: h = RND_act(silu(gate) * up), stored per slot position
+    T* h = reinterpret_cast<T*>(a.h);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int row = 16 * f + l16;
+      if (row >= nv) continue;
+      const int pos = pos0 + row;
+#pragma unroll
+      for (int r = 0; r < RF; ++r) {
+        if (rb0 + r >= nrb) continue;
+        const int o = (rb0 + r) * 16 + 4 * lg;
+        T hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) hv[v] = from_f32<T>(silu_f(acc[0][r][f][v]) * acc[1][r][f][v]);
+        *reinterpret_cast<u32x2*>(h + (size_t)pos * a.d_out + o) = __builtin_bit_cast(u32x2, hv);
+      }
+    }
+  } else {
+    // gated per-slot residual output (fp32)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int row = 16 * f + l16;
+      if (row >= nv) continue;
+      const int pos = pos0 + row;
+      const float g = a.gates[a.perm[pos]];
+#pragma unroll
+      for (int r = 0; r < RF; ++r) {
+        if (rb0 + r >= nrb) continue;
+        const int o = (rb0 + r) * 16 + 4 * lg;
+        *reinterpret_cast<f32x4*>(a.dres + (size_t)pos * a.d_out + o) = acc[0][r][f] * g;
+      }
+    }
+  }
+}
+
+template <int NP, int RF, int NF, int GS>
+constexpr bool pre_fits() {
+  return 3 * PfSlot<NP, RF, NF, GS>::BYTES <= 160 * 1024 - 2048;
+}
+
+template <typename T, int MODE, int RF, int NF, int GS>
+static void pre_launch(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
+  const int rows_per_wg = 16 * RF * PF_WAVES;
+  const int nrt = (a.d_out + rows_per_wg - 1) / rows_per_wg;
+  if constexpr (pre_fits<NP, RF, NF, GS>()) {
+    const dim3 grid(max_tiles * nrt), block(64 * PF_WAVES);
+    hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS>), grid, block, 0, s, a);
+  } else {
+    // a 128-slot tile is twice a 64-slot tile: same grid, two passes
+    static_assert(NF == 8, "smaller tiles always fit");
+    GemmArgs b = a;
+    b.tile_half = 1;
+    const dim3 grid(2 * max_tiles * nrt), block(64 * PF_WAVES);
+    hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, 4, GS>), grid, block, 0, s, b);
+  }
+}
+
+template <typename T, int MODE, int RF, int NF>
+static void pre_gs(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  const int G = a.p[0].group;
+  const bool pow2 = (G & (G - 1)) == 0;
+  if (!pow2 || G > 256) pre_launch<T, MODE, RF, NF, 0>(a, max_tiles, s);
+  else if (G == 32) pre_launch<T, MODE, RF, NF, 1>(a, max_tiles, s);
+  else if (G == 64) pre_launch<T, MODE, RF, NF, 2>(a, max_tiles, s);
+  else if (G == 128) pre_launch<T, MODE, RF, NF, 4>(a, max_tiles, s);
+  else pre_launch<T, MODE, RF, NF, 8>(a, max_tiles, s);
+}
+
+void launch_gemm_prefill(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
+                         hipStream_t s) {
+  if (act == ACT_F16) {
+    if (mode == MODE_GATEUP) pre_gs<half_t, MODE_GATEUP, 2, 8>(a, max_tiles, s);
+    else pre_gs<half_t, MODE_RES, 4, 8>(a, max_tiles, s);
+  } else {
+    if (mode == MODE_GATEUP) pre_gs<__bf16, MODE_GATEUP, 2, 8>(a, max_tiles, s);
+    else pre_gs<__bf16, MODE_RES, 4, 8>(a, max_tiles, s);
+  }
+}
+
+}  // namespace tq

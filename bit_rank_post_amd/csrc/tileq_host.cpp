@@ -96,9 +96,10 @@ struct Plan {
   size_t P[3];
   int nsplit[3];
   int rows_cap;
-  size_t zero_base, hamax;       // region zeroed by the route kernel
+  size_t zero_base;              // region zeroed by the route kernel (unused: 0 words)
   int zero_n;
   size_t ex, h, dres, hs, ys;
+  size_t x16, ex_h16, h16;       // prefill, bfloat16 activations
   size_t xp, sums_x, ex_x, hp, sums_h, ex_h;   // decode activation preparation
   size_t total;
 };
@@ -200,12 +201,15 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
     if (d.r_pad > 0) p.P[q] = take((size_t)p.nsplit[q] * S * d.r_pad * sizeof(float));
   }
   const bool bf = (L->act == TQ_BF16);
-  // zeroed region: |h| maxima (bf16 SwiGLU, prefill)
-  const int nham = (bf && L->kind == TQ_SWIGLU) ? S : 0;
-  p.zero_n = nham;
-  p.zero_base = take(sizeof(unsigned) * std::max(p.zero_n, 1));
-  p.hamax = p.zero_base;
-  p.ex = take(sizeof(int) * (bf ? std::max(T, 1) : 1));
+  p.zero_n = 0;
+  p.zero_base = take(sizeof(unsigned));
+  // prefill with bfloat16 activations: exact fp16 copies of x and h scaled by
+  // per-row powers of two (the MFMA kernels read fp16)
+  const bool bfpre = bf && path == 2;
+  p.ex = take(sizeof(int) * (bfpre ? std::max(T, 1) : 1));
+  p.x16 = take(bfpre ? (size_t)T * L->d_model * 2 : 0);
+  p.ex_h16 = take(sizeof(int) * ((bfpre && L->kind == TQ_SWIGLU) ? std::max(S, 1) : 1));
+  p.h16 = take((bfpre && L->kind == TQ_SWIGLU) ? (size_t)S * L->d_ff * 2 : 0);
   p.h = take(L->kind == TQ_SWIGLU ? (size_t)S * L->d_ff * 2 : 0);
   int d_in_last, d_out_last;
   proj_dims(L, nproj(L) - 1, &d_in_last, &d_out_last);
@@ -532,6 +536,10 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   size_t need = 0;
   tq_workspace_size(L, T, topk, &need);
   if (ws_bytes < need) return fail(TQ_ESHAPE, "ws_bytes = %zu < %zu", ws_bytes, need);
+  // activation rows are addressed with 32-bit byte offsets below 2^31
+  if ((long)T * L->d_model * 2 >= 0x7FFFFFF0L)
+    return fail(TQ_EUNSUPPORTED, "T * d_model * 2 = %ld bytes of activations >= 2^31",
+                (long)T * L->d_model * 2);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const Act act = (L->act == TQ_F16) ? ACT_F16 : ACT_BF16;
   const bool bf = (act == ACT_BF16);
@@ -562,7 +570,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     launch_act_prep(pa, T, act, s);
   } else if (bf) {
     ex = at<int>(ws, p.ex);
-    launch_row_exponent(x, T, L->d_model, ex, s);
+    launch_rows_to_f16(x, T, L->d_model, nullptr, ex, at<void>(ws, p.x16), s);
   }
   mark(2);
   // (a2) column stage of the projection(s) reading x
@@ -577,7 +585,6 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   mark(3);
   float* dres = at<float>(ws, p.dres);
   void* h = swiglu ? at<void>(ws, p.h) : nullptr;
-  unsigned* hamax = (bf && swiglu && !dec) ? at<unsigned>(ws, p.hamax) : nullptr;
   // (a3 + a4 + a5) residual GEMM of the input projection(s)
   if (dec) {
     DecArgs da{};
@@ -620,7 +627,8 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     ga.d_out = L->proj[0].dev.d_out;
     ga.topk = topk;
     ga.S = p.S;
-    ga.A = x;
+    ga.A = bf ? at<void>(ws, p.x16) : x;
+    ga.rows = T;
     ga.gather = 1;
     ga.perm = at<int>(ws, p.perm);
     ga.off = at<int>(ws, p.off);
@@ -637,12 +645,11 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
         ga.slot2col[c] = at<int>(ws, p.slot2col[c]);
       }
       ga.h = h;
-      ga.hamax_out = hamax;
-      launch_gemm(ga, MODE_GATEUP, path, act, p.max_tiles_gemm, s);
+      launch_gemm_prefill(ga, MODE_GATEUP, act, p.max_tiles_gemm, s);
     } else {
       ga.dres = dres;
       ga.gates = topk_w;
-      launch_gemm(ga, MODE_RES, path, act, p.max_tiles_gemm, s);
+      launch_gemm_prefill(ga, MODE_RES, act, p.max_tiles_gemm, s);
     }
   }
   mark(4);
@@ -716,17 +723,24 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       ga.d_out = dd.d_out;
       ga.topk = topk;
       ga.S = p.S;
-      ga.A = h;
       ga.gather = 0;
+      ga.rows = p.S;
+      if (bf) {
+        // exact fp16 copy of h for the MFMA kernel
+        launch_rows_to_f16(h, p.S, L->d_ff, nullptr, at<int>(ws, p.ex_h16), at<void>(ws, p.h16), s);
+        ga.A = at<void>(ws, p.h16);
+        ga.ex = at<int>(ws, p.ex_h16);
+      } else {
+        ga.A = h;
+      }
       ga.perm = at<int>(ws, p.perm);
       ga.off = at<int>(ws, p.off);
       ga.cnt = at<int>(ws, p.cnt);
       ga.tile_off = at<int>(ws, p.tile_gemm);
-      ga.hamax = hamax;
       ga.p[0] = dd;
       ga.dres = dres;
       ga.gates = topk_w;
-      launch_gemm(ga, MODE_RES, path, act, p.max_tiles_gemm, s);
+      launch_gemm_prefill(ga, MODE_RES, act, p.max_tiles_gemm, s);
     }
   } else {
     mark(5);
@@ -820,6 +834,10 @@ tq_status tq_debug_route(const tq_layer* L, int32_t which, const int32_t* topk_i
   size_t need = 0;
   tq_workspace_size(L, T, topk, &need);
   if (ws_bytes < need) return fail(TQ_ESHAPE, "ws_bytes = %zu < %zu", ws_bytes, need);
+  // activation rows are addressed with 32-bit byte offsets below 2^31
+  if ((long)T * L->d_model * 2 >= 0x7FFFFFF0L)
+    return fail(TQ_EUNSUPPORTED, "T * d_model * 2 = %ld bytes of activations >= 2^31",
+                (long)T * L->d_model * 2);
   const Plan p = make_plan(L, T, topk, choose_path(L, T, topk));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   RouteArgs ra;

@@ -72,6 +72,41 @@ __device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
+// ---- loads with an LDS destination (buffer_load ... lds) --------------------
+// Each lane's bytes land at lds + lane * size; the LDS pointer must be
+// wave-uniform.  Loads complete in issue order; a wave waits for its own with
+// wait_vm<N>() and makes them visible to the workgroup with a barrier.
+typedef __attribute__((address_space(3))) void lds_t;
+
+// out-of-range voffset: the load returns zeros and reads no memory (only the
+// vector offset is range checked, so every scalar offset must stay in range)
+constexpr uint32_t OOB = 0x7FFFFFF0u;
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                     uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t*)lds, 4, voff, soff, 0, 0);
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// workgroup barrier without a memory fence (a fenced barrier waits for every
+// load in flight); the empty asm statements keep the compiler from moving
+// LDS accesses across it
+__device__ __forceinline__ void bar_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // (a & m) | c in one VALU op (the compiler otherwise emits an and plus an or).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   uint32_t r;

@@ -97,8 +97,7 @@ struct GemmArgs {
   const int* off;
   const int* cnt;
   const int* tile_off;           // [K+1]
-  const int* ex;                 // per-activation-row exponent (bf16) or nullptr
-  const unsigned* hamax;         // per-pos |h| max bits (bf16 down) or nullptr
+  const int* ex;                 // per-row exponent of converted bf16 rows, or nullptr
   // projections (1 for RES, 2 for GATEUP)
   ProjDev p[2];
   // low-rank extension (GATEUP): P partials of each projection
@@ -108,12 +107,18 @@ struct GemmArgs {
   const int* slot2col[2];
   // outputs
   void* h;                       // GATEUP: [S][d_out] act
-  unsigned* hamax_out;           // GATEUP bf16: atomic max of |h| per pos
   float* dres;                   // RES: [S][d_out] f32 (gate weight applied)
   const float* gates;            // RES: topk weights [T*topk]
+  int rows;                      // rows of A
+  int tile_half;                 // set by the launcher: 64-slot halves of 128-slot tiles
 };
-void launch_gemm(const GemmArgs& a, GemmMode mode, int path, Act act, int max_tiles,
-                 hipStream_t s);
+// prefill grouped GEMM; A is fp16 (bfloat16 rows converted by rows_to_f16,
+// exponents in ex); tiles of 128 slots (route bm_gemm = 128)
+void launch_gemm_prefill(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
+                         hipStream_t s);
+// bfloat16 rows -> fp16 rows scaled by 2^-E, max|row| * 2^-E in [2^14, 2^15)
+void launch_rows_to_f16(const void* X, int rows, int d, const int* row_src, int* ex,
+                        void* Y, hipStream_t s);
 
 // ---- decode streaming residual kernel --------------------------------------
 struct DecArgs {
@@ -189,6 +194,5 @@ void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStrea
 void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_pad,
                         hipStream_t s);
 void launch_debug_dequant(const ProjDev& p, int expert, void* w_out, hipStream_t s);
-void launch_row_exponent(const void* X, int rows, int cols, int* ex, hipStream_t s);
 
 }  // namespace tq

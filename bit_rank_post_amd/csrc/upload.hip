@@ -158,29 +158,54 @@ void launch_debug_dequant(const ProjDev& p, int expert, void* w_out, hipStream_t
                      reinterpret_cast<half_t*>(w_out));
 }
 
-// Per-row exponent E with max|x_row| * 2^-E in [2^14, 2^15) (0 for a zero
-// row): bfloat16 rows scaled by 2^-E are exact in fp16 down to 2^-15 of the
-// row maximum.
-__global__ void row_exponent_kernel(const uint16_t* __restrict__ X, int rows, int cols,
-                                    int* __restrict__ ex) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
+// bfloat16 row -> fp16 row scaled by 2^-E with max|x| * 2^-E in [2^14, 2^15):
+// exact for every element down to 2^-24 of the scaled range (8 significant
+// bits fit in 11).  One workgroup (256 threads) per row, d % 8 == 0.
+__global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ X, int d,
+                                                          const int* __restrict__ row_src,
+                                                          int* __restrict__ ex, half_t* __restrict__ Y) {
+  __shared__ float s_red[4];
+  const int row = blockIdx.x;
+  const int src = row_src ? row_src[row] : row;
+  const int tid = threadIdx.x;
+  const uint16_t* xr = X + (size_t)src * d;
   float m = 0.f;
-  for (int c = lane; c < cols; c += 64)
-    m = fmaxf(m, fabsf(__uint_as_float((uint32_t)X[(size_t)row * cols + c] << 16)));
+  for (int c = tid; c < (d >> 3); c += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m = fmaxf(m, fabsf(__uint_as_float(v[q] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(v[q] & 0xFFFF0000u)));
+    }
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if (lane == 0) {
-    int e2 = 0;
-    if (m > 0.f) frexpf(m, &e2);
-    ex[row] = (m > 0.f) ? e2 - 15 : 0;
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  int e2 = 0;
+  if (m > 0.f) frexpf(m, &e2);
+  const int E = (m > 0.f) ? e2 - 15 : 0;
+  if (tid == 0) ex[row] = E;
+  half_t* yr = Y + (size_t)row * d;
+  for (int c = tid; c < (d >> 3); c += 256) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * c);
+    half8v o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = (half_t)ldexpf(__uint_as_float(v[q] << 16), -E);
+      o[2 * q + 1] = (half_t)ldexpf(__uint_as_float(v[q] & 0xFFFF0000u), -E);
+    }
+    *reinterpret_cast<half8v*>(yr + 8 * c) = o;
   }
 }
 
-void launch_row_exponent(const void* X, int rows, int cols, int* ex, hipStream_t s) {
-  hipLaunchKernelGGL(row_exponent_kernel, dim3((rows + 3) / 4), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t*>(X), rows, cols, ex);
+void launch_rows_to_f16(const void* X, int rows, int d, const int* row_src, int* ex, void* Y,
+                        hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(rows_to_f16_kernel, dim3(rows), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(X), d, row_src, ex,
+                     reinterpret_cast<half_t*>(Y));
 }
 
 }  // namespace tq

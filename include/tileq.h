@@ -139,7 +139,8 @@ tq_status tq_workspace_size(const tq_layer *L, int32_t T, int32_t topk, size_t *
  * back, so it can be captured in a HIP graph.  T == 0 is a no-op.  Buffers may
  * not overlap.  Concurrent calls must use distinct workspaces.
  * Errors (all checked before any launch): TQ_EINVAL (NULL pointers, y_dtype),
- * TQ_ESHAPE (T, topk, ws_bytes too small), TQ_ESTATE, TQ_EHIP (launch failure). */
+ * TQ_ESHAPE (T, topk, ws_bytes too small), TQ_ESTATE, TQ_EUNSUPPORTED
+ * (T * d_model * 2 >= 2^31 bytes of activations), TQ_EHIP (launch failure). */
 tq_status tq_forward(const tq_layer *L, const void *x, int32_t T, const int32_t *topk_ids,
                      const float *topk_w, int32_t topk, void *y, tq_dtype y_dtype,
                      void *ws, size_t ws_bytes, void *stream);
