@@ -21,9 +21,14 @@ __device__ __forceinline__ float class_inv(int k) {
   return (v == 0) ? 64.f : (v == 1) ? 16.f : (v == 2) ? 4.f : (b ? 16.f : 64.f);
 }
 
-// One workgroup (256 threads) per row.  Each thread owns 8-element chunks.
+// One workgroup (256 threads) per row; thread tid owns the 8-element chunks
+// tid + 256 i.  The row is read once (up to 8 chunks per thread stay in
+// registers between the maximum and the conversion; longer rows re-read the
+// rest).
 template <typename T>
 __global__ __launch_bounds__(256) void act_prep_kernel(PrepArgs a) {
+  typedef typename Vec8<T>::type V8;
+  constexpr int KEEP = 8;
   __shared__ float s_red[4];
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -31,10 +36,19 @@ __global__ __launch_bounds__(256) void act_prep_kernel(PrepArgs a) {
   if (src < 0) return;
   const T* xr = reinterpret_cast<const T*>(a.X) + (size_t)src * a.d;
   const int nch = a.d >> 3;
-  // amax
+  V8 kept[KEEP];
   float m = 0.f;
-  for (int c = tid; c < nch; c += 256) {
-    const typename Vec8<T>::type v = *reinterpret_cast<const typename Vec8<T>::type*>(xr + 8 * c);
+#pragma unroll
+  for (int i = 0; i < KEEP; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nch) {
+      kept[i] = *reinterpret_cast<const V8*>(xr + 8 * c);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)kept[i][j]));
+    }
+  }
+  for (int c = tid + 256 * KEEP; c < nch; c += 256) {
+    const V8 v = *reinterpret_cast<const V8*>(xr + 8 * c);
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf((float)v[j]));
   }
@@ -47,15 +61,14 @@ __global__ __launch_bounds__(256) void act_prep_kernel(PrepArgs a) {
   if (m > 0.f) frexpf(m, &e2);
   const int E = (m > 0.f) ? e2 - 9 : 0;
   if (tid == 0) a.ex[row] = E;
-  // scaled, class-scaled copy and group sums; a group is G/8 consecutive chunks
-  const int cpg = a.G >> 3;                     // chunks per group (4, 8, 16, 32)
+  // scaled, class-scaled copy and group sums; a group is G/8 consecutive
+  // chunks, i.e. G/8 consecutive threads of one wave (G <= 256)
+  const int cpg = a.G >> 3;
   half_t* xo = reinterpret_cast<half_t*>(a.Xp) + (size_t)row * a.d;
   float* sums = a.sums + (size_t)row * (a.d / a.G) * 2;
-  for (int base = 0; base < nch; base += 256) {
-    const int c = base + tid;
+  auto emit = [&](int c, const V8& v) {
     float st = 0.f, sp = 0.f;
     if (c < nch) {
-      const typename Vec8<T>::type v = *reinterpret_cast<const typename Vec8<T>::type*>(xr + 8 * c);
       half8v o;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -67,18 +80,25 @@ __global__ __launch_bounds__(256) void act_prep_kernel(PrepArgs a) {
       }
       *reinterpret_cast<half8v*>(xo + 8 * c) = o;
     }
-    // reduce over the cpg lanes of a group (groups align with lane groups:
-    // 256 threads cover whole groups since cpg divides 64 or 64 divides cpg)
-    if (cpg <= 64) {
-      for (int o2 = 1; o2 < cpg; o2 <<= 1) {
-        st += __shfl_xor(st, o2, 64);
-        sp += __shfl_xor(sp, o2, 64);
-      }
-      if (c < nch && (c % cpg) == 0) {
-        sums[2 * (c / cpg)] = st;
-        sums[2 * (c / cpg) + 1] = sp;
-      }
+    for (int o2 = 1; o2 < cpg; o2 <<= 1) {
+      st += __shfl_xor(st, o2, 64);
+      sp += __shfl_xor(sp, o2, 64);
     }
+    if (c < nch && (c % cpg) == 0) {
+      sums[2 * (c / cpg)] = st;
+      sums[2 * (c / cpg) + 1] = sp;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < KEEP; ++i) {
+    const int c = tid + 256 * i;
+    if (256 * i < nch) emit(c, kept[i]);      // whole-block condition: shuffles stay uniform
+  }
+  for (int base = 256 * KEEP; base < nch; base += 256) {
+    const int c = base + tid;
+    V8 v{};
+    if (c < nch) v = *reinterpret_cast<const V8*>(xr + 8 * c);
+    emit(c, v);
   }
 }
 

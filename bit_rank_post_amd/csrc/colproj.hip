@@ -12,7 +12,9 @@
 // MFMA 16x16x32 in the activation dtype, fp32 accumulation.  A operand =
 // activation rows (16 rows x 32 inputs), B operand = V_n^T rows (r-columns).
 // Split-K over `nsplit` slabs: slab s holds the partial sum over its k-range;
-// consumers add the slabs (deterministic, no float atomics).
+// consumers add the slabs (deterministic, no float atomics).  The stored rank
+// vectors are already multiplied by Sigma (in fp32), which every consumer
+// needs.
 #include "tq_device.h"
 
 namespace tq {
@@ -31,11 +33,21 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
   __shared__ float s_red[(WR == 1) ? 4 * 16 * 128 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
-  const int seg = find_segment(a.tile_off, a.nseg, tile, &s_res);
-  if (seg < 0) return;
   const int rt = 16 * WR;
-  const int row0 = a.seg_off[seg] + (tile - a.tile_off[seg]) * rt;
-  const int row_end = a.seg_off[seg + 1];
+  int seg, row0, row_end;
+  if (a.ap_T > 0) {
+    // every (column, token) pair: column seg owns rows seg * T ... seg * T + T - 1
+    const int tpc = (a.ap_T + rt - 1) / rt;
+    seg = tile / tpc;
+    if (seg >= a.nseg) return;
+    row0 = seg * a.ap_T + (tile - seg * tpc) * rt;
+    row_end = (seg + 1) * a.ap_T;
+  } else {
+    seg = find_segment(a.tile_off, a.nseg, tile, &s_res);
+    if (seg < 0) return;
+    row0 = a.seg_off[seg] + (tile - a.tile_off[seg]) * rt;
+    row_end = a.seg_off[seg + 1];
+  }
   const int vblk = a.seg_vblk ? a.seg_vblk[seg] : seg;
   const int nfrag = a.r_pad >> 4;
 
@@ -48,9 +60,9 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
   const int myrow = rbase + (lane & 15);
   const bool rvalid = myrow < row_end;
   int src = 0;
-  if (rvalid) src = a.row_src ? a.row_src[myrow] : myrow;
+  if (rvalid) src = (a.ap_T > 0) ? myrow - seg * a.ap_T : (a.row_src ? a.row_src[myrow] : myrow);
   const T* arow = reinterpret_cast<const T*>(a.A) + (size_t)src * a.lda + 8 * (lane >> 4);
-  const T* vt = reinterpret_cast<const T*>(a.Vt) + (size_t)vblk * a.r_pad * a.d_in;
+  const T* vt = reinterpret_cast<const T*>(a.Vt) + (size_t)vblk * a.r_pad * a.d_in;   // [steps][r_pad][32]
 
   f32x4 acc[8];
 #pragma unroll
@@ -64,7 +76,7 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.Vt, 0x7FFFFFF0u);
     const uint32_t BAD = 0x7FFFFFF0u;
     const uint32_t avo = rvalid ? ((uint32_t)src * a.lda + 8 * (lane >> 4)) * 2u : BAD;
-    const uint32_t vvo = ((uint32_t)vblk * a.r_pad * a.d_in + (lane & 15) * a.d_in + 8 * (lane >> 4)) * 2u;
+    const uint32_t vvo = ((uint32_t)vblk * a.r_pad * a.d_in + (lane & 15) * 32 + 8 * (lane >> 4)) * 2u;
     u32x4 av[4], bv[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -74,7 +86,7 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
 #pragma unroll
       for (int f = 0; f < 8; ++f)
         if (f < nfrag)
-          bv[i][f] = bload128(rv, ok ? vvo + 16u * f * a.d_in * 2u : BAD, ok ? st * 64u : 0u);
+          bv[i][f] = bload128(rv, ok ? vvo + 1024u * f : BAD, ok ? st * a.r_pad * 64u : 0u);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -94,7 +106,7 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
       for (int f = 0; f < 8; ++f) {
         if (f < nfrag) {
           const V8 bvv = *reinterpret_cast<const V8*>(
-              vt + (size_t)(16 * f + (lane & 15)) * a.d_in + st * 32 + 8 * (lane >> 4));
+              vt + ((size_t)st * a.r_pad + 16 * f + (lane & 15)) * 32 + 8 * (lane >> 4));
           acc[f] = mfma16(avv, bvv, acc[f]);
         }
       }
@@ -120,7 +132,7 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) v += s_red[(w * 16 + r) * 128 + c];
-        P[(size_t)row * a.r_pad + c] = v;
+        P[(size_t)row * a.r_pad + c] = v * a.sigma[c];
       }
     }
   } else {
@@ -130,7 +142,8 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int row = rbase + 4 * (lane >> 4) + v;
-          if (row < row_end) P[(size_t)row * a.r_pad + 16 * f + (lane & 15)] = acc[f][v];
+          if (row < row_end)
+            P[(size_t)row * a.r_pad + 16 * f + (lane & 15)] = acc[f][v] * a.sigma[16 * f + (lane & 15)];
         }
       }
     }
@@ -141,7 +154,8 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
 // order, deterministic).  Rows past the segment total are skipped.
 struct RedArgs {
   float* P[2];
-  const int* total[2];           // device row count of each projection
+  const int* total[2];           // device row count of each projection (or nullptr)
+  int total_host[2];             // row count when total is nullptr
   int r_pad[2];
   int nsplit, rows_cap;
 };
@@ -149,7 +163,7 @@ struct RedArgs {
 __global__ __launch_bounds__(256) void colproj_reduce_kernel(RedArgs a) {
   const int z = blockIdx.y;
   const int rp = a.r_pad[z];
-  const int rows = *a.total[z];
+  const int rows = a.total[z] ? *a.total[z] : a.total_host[z];
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (size_t)rows * rp) return;
   const size_t slab = (size_t)a.rows_cap * rp;
@@ -182,7 +196,8 @@ void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
     int rp_max = 0;
     for (int z = 0; z < nproj; ++z) {
       r.P[z] = a[z].P;
-      r.total[z] = a[z].seg_off + a[z].nseg;
+      r.total[z] = (a[z].ap_T > 0) ? nullptr : a[z].seg_off + a[z].nseg;
+      r.total_host[z] = a[z].nseg * a[z].ap_T;
       r.r_pad[z] = a[z].r_pad;
       rp_max = a[z].r_pad > rp_max ? a[z].r_pad : rp_max;
     }

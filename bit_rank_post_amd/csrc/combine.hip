@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         const int e = a.ids[s];
         if (e >= 0 && e < a.K) {
           m = a.m_of[e];
-          row = a.prow[s];
+          row = (a.ap_T > 0) ? a.n_of[e] * a.ap_T + t : a.prow[s];
           g = a.gates[s];
         }
       }
@@ -66,14 +66,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
       __syncthreads();
       if (!s_active) continue;
-      // S[t][m][:] = Sigma * sum_{j : row(e_tj) = m} g_tj p_tj, split hi + lo
+      // S[t][m][:] = sum_{j : row(e_tj) = m} g_tj (Sigma p_tj), split hi + lo
       for (int i = tid; i < 16 * rp; i += 256) {
         const int tt = i / rp, c = i - tt * rp;
         float v = 0.f;
         for (int j = 0; j < k; ++j)
           if (s_m[tt * KMAX + j] == m)
             v += s_g[tt * KMAX + j] * a.P[(size_t)s_row[tt * KMAX + j] * rp + c];
-        v *= a.sigma[c];
         const T hi = from_f32<T>(v);
         s_hi[tt * SLD + c] = hi;
         s_lo[tt * SLD + c] = from_f32<T>(v - to_f32(hi));

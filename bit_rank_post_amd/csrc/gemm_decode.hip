@@ -336,15 +336,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
           const int rp = pd.r_pad;
           const T* up = reinterpret_cast<const T*>(pd.U) +
                         ((size_t)pd.m_of[e] * a.d_out + rb * 16 + l16) * rp + 8 * lg;
-          const int col = a.slot2col[p][slotid];
-          const float* prow = a.P[p] + (size_t)col * rp + 8 * lg;
-          const float* sg = pd.sigma + 8 * lg;
+          const int col = (a.ap_T > 0) ? pd.n_of[e] * a.ap_T + slotid / a.topk : a.slot2col[p][slotid];
+          const float* prow = a.P[p] + (size_t)col * rp + 8 * lg;     // Sigma p
           for (int s2 = 0; s2 < rp; s2 += 32) {
             const V8 av = *reinterpret_cast<const V8*>(up + s2);
             V8 bh, bl;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              const float v = prow[s2 + i] * sg[s2 + i];
+              const float v = prow[s2 + i];
               const T hi = from_f32<T>(v);
               bh[i] = hi;
               bl[i] = from_f32<T>(v - to_f32(hi));

@@ -288,7 +288,6 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
             float v = 0.f;
             for (int sp = 0; sp < a.nsplit[p]; ++sp)
               v += a.P[p][((size_t)sp * a.rows_cap[p] + col) * rp + rc0 + c];
-            v *= pd.sigma[rc0 + c];
             hi = from_f32<T>(v);
             lo = from_f32<T>(v - to_f32(hi));
           }

@@ -91,6 +91,7 @@ void proj_dims(const tq_layer* L, int which, int* d_in, int* d_out) {
 struct Plan {
   int T, k, S, path, bm_gemm, rt_col, max_tiles_gemm, max_col_tiles;
   int nks;                       // k-chunks (fp32 slabs) of the last projection's residual
+  int ap_T;                      // decode: column stage over all (column, token) pairs
   size_t flags, cnt, off, perm, inv, tile_gemm, tile_colx, colmask, cntw, rank;
   size_t col_off[2], col_tok[2], slot2col[2], tile_col[2];
   size_t P[3];
@@ -166,6 +167,13 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.rt_col = (path == 1) ? 16 : 64;
   p.max_tiles_gemm = (p.S + p.bm_gemm - 1) / p.bm_gemm + L->K;
   p.max_col_tiles = (p.S + p.rt_col - 1) / p.rt_col + 32 + L->K;
+  // decode: the column stage of the input projection(s) covers every
+  // (column, token) pair, so it does not wait for the routing lists
+  int nmax = 1;
+  for (int c = 0; c < ((L->kind == TQ_SINGLE) ? 1 : 2); ++c)
+    if (L->proj[c].uploaded) nmax = std::max(nmax, L->proj[c].dev.N);
+  p.ap_T = (path == 1) ? T : 0;
+  if (path == 1) p.max_col_tiles = std::max(p.max_col_tiles, nmax * ((T + p.rt_col - 1) / p.rt_col));
   const int S = p.S, K = L->K;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -191,14 +199,14 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
     p.slot2col[c] = take(sizeof(int) * S);
     p.tile_col[c] = take(sizeof(int) * (N + 1));
   }
-  p.rows_cap = S;
+  p.rows_cap = (path == 1) ? std::max(S, nmax * T) : S;
   for (int q = 0; q < 3; ++q) {
     p.nsplit[q] = 1;
     p.P[q] = 0;
     if (q >= nproj(L)) continue;
     const ProjDev& d = L->proj[q].dev;
     p.nsplit[q] = choose_nsplit(path, S, d.d_in);
-    if (d.r_pad > 0) p.P[q] = take((size_t)p.nsplit[q] * S * d.r_pad * sizeof(float));
+    if (d.r_pad > 0) p.P[q] = take((size_t)p.nsplit[q] * p.rows_cap * d.r_pad * sizeof(float));
   }
   const bool bf = (L->act == TQ_BF16);
   p.zero_n = 0;
@@ -303,8 +311,10 @@ ColArgs col_args_x(const tq_layer* L, const Plan& p, int c, const void* x, void*
   a.d_in = d.d_in;
   a.nsplit = p.nsplit[c];
   a.steps_per_split = ((d.d_in >> 5) + p.nsplit[c] - 1) / p.nsplit[c];
+  a.sigma = d.sigma;
   a.P = at<float>(ws, p.P[c]);
   a.rows_cap = p.rows_cap;
+  a.ap_T = p.ap_T;
   return a;
 }
 
@@ -324,6 +334,7 @@ ColArgs col_args_down(const tq_layer* L, const Plan& p, const void* h, void* ws)
   a.d_in = d.d_in;
   a.nsplit = p.nsplit[2];
   a.steps_per_split = ((d.d_in >> 5) + p.nsplit[2] - 1) / p.nsplit[2];
+  a.sigma = d.sigma;
   a.P = at<float>(ws, p.P[2]);
   a.rows_cap = p.rows_cap;
   return a;
@@ -549,11 +560,11 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   auto mark = [&](int i) {
     if (L->prof) (void)hipEventRecord(L->ev[i], s);
   };
-
   // (a1) routing / grouping
   mark(0);
   RouteArgs ra;
   fill_route(L, p, topk_ids, ws, ra);
+  if (p.ap_T > 0) ra.ncol = 0;     // decode: no column lists (every pair is computed)
   launch_route(ra, s);
   mark(1);
   // activation preparation: decode = class-scaled fp16 copy + group sums;
@@ -610,6 +621,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.h = h;
       da.nks = 1;
       da.S = p.S;
+      da.ap_T = p.ap_T;
       da.waves = choose_waves(L, 0, p.S, 1);
       launch_gemm_decode(da, MODE_GATEUP, act, s);
     } else {
@@ -762,11 +774,12 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     cb.gates = topk_w;
     cb.inv = at<int>(ws, p.inv);
     cb.prow = swiglu ? at<int>(ws, p.inv) : at<int>(ws, p.slot2col[0]);
+    cb.ap_T = swiglu ? 0 : p.ap_T;
+    cb.n_of = d.n_of;
     cb.m_of = d.m_of;
     cb.P = d.r_pad ? at<float>(ws, p.P[q]) : nullptr;
     cb.nsplit = 1;
     cb.rows_cap = p.rows_cap;
-    cb.sigma = d.sigma;
     cb.U = d.U;
     cb.dres = dres;
     cb.nks = p.nks;
@@ -841,7 +854,7 @@ tq_status tq_debug_route(const tq_layer* L, int32_t which, const int32_t* topk_i
   const Plan p = make_plan(L, T, topk, choose_path(L, T, topk));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   RouteArgs ra;
-  fill_route(L, p, topk_ids, ws, ra);
+  fill_route(L, p, topk_ids, ws, ra);     // always with the column lists
   launch_route(ra, s);
   HIPCHK(hipGetLastError());
   const size_t S = (size_t)p.S;

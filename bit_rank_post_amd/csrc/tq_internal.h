@@ -21,7 +21,8 @@ enum Act { ACT_F16 = 0, ACT_BF16 = 1 };
 //           unpack16() in tq_device.h.
 //   sz    : [K][nrb][ng][16] u32, scale bits | zero bits << 16 (fp16 each)
 //   U     : [M*d_out][r_pad] act, r zero-padded to a multiple of 32
-//   Vt    : [N][r_pad][d_in] act (V_n transposed, zero-padded rows)
+//   Vt    : [N][d_in/32][r_pad][32] act (V_n transposed per 32-input k-step,
+//           zero-padded ranks)
 //   sigma : [r_pad] f32, zero padded
 struct ProjDev {
   int K, M, N, d_in, d_out, rank, r_pad, group, ng, nrb, nsteps;
@@ -69,7 +70,7 @@ struct RouteArgs {
 };
 void launch_route(const RouteArgs& a, hipStream_t s);
 
-// ---- column stage: P[split][row][r] = sum_{k in split} a_row[k] V_n[k][r] --
+// ---- column stage: P[split][row][r] = sigma_r sum_{k in split} a_row[k] V_n[k][r]
 struct ColArgs {
   const void* A;                 // activations, row stride lda
   int lda;
@@ -81,8 +82,11 @@ struct ColArgs {
   const void* Vt;
   int r_pad, d_in;
   int nsplit, steps_per_split;
+  const float* sigma;            // [r_pad]: P holds Sigma (V_n^T a)
   float* P;
   int rows_cap;                  // rows per split slab
+  int ap_T;                      // > 0: every (column, token) pair, row = n * ap_T + t
+                                 // (no work lists; seg_off/tile_off/row_src unused)
 };
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
                     hipStream_t s);
@@ -132,7 +136,7 @@ struct DecArgs {
   const float* sums;             // [rows][d_in/G][2]: (X~_g, X'_g)
   const int* ex;                 // [rows] row exponent E
   ProjDev p[2];
-  const float* P[2];             // column-stage results [rows][r_pad] (GATEUP)
+  const float* P[2];             // column-stage results Sigma p, [rows][r_pad] (GATEUP)
   const int* slot2col[2];
   void* h;                       // GATEUP out [S][d_out] act
   float* dres;                   // RES out [nks][S][d_out] f32 (one slab per k-chunk)
@@ -140,6 +144,7 @@ struct DecArgs {
   int nks;                       // k-chunks (RES; 1 for GATEUP)
   int S;                         // slots (slab stride of dres)
   int waves;                     // waves per workgroup: 8 or 16 (16 rows each)
+  int ap_T;                      // GATEUP: P rows are (column, token) pairs n * ap_T + t
 };
 void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s);
 
@@ -161,10 +166,11 @@ struct CombineArgs {
   const float* gates;
   const int* inv;
   const int* prow;               // slot -> row of P (inv for down, slot2col for single)
+  int ap_T;                      // single projection, all-pairs P: row = n_of[e] * ap_T + t
+  const int* n_of;
   const int* m_of;
   const float* P;
   int nsplit, rows_cap;
-  const float* sigma;
   const void* U;
   const float* dres;             // [nks][S][d_out]
   int nks, S;

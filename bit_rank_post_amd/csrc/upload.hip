@@ -102,15 +102,20 @@ void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStrea
                      rows, r, r_pad);
 }
 
-// V [N*d_in][r] -> Vt [N][r_pad][d_in]
+// V [N*d_in][r] -> Vt [N][d_in/32][r_pad][32]: for each 32-input k-step, the
+// k-step's inputs of every rank contiguous (one 1 KB block per 16 ranks)
 __global__ void transpose_v_kernel(const uint16_t* __restrict__ V, uint16_t* __restrict__ dst,
                                    int N, int d_in, int r, int r_pad) {
   const size_t total = (size_t)N * r_pad * d_in;
+  const int nsteps = d_in >> 5;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (size_t)gridDim.x * blockDim.x) {
-    const int k = (int)(i % d_in);
-    const size_t nc = i / d_in;
-    const int c = (int)(nc % r_pad), n = (int)(nc / r_pad);
+    const int kk = (int)(i & 31);
+    const size_t q = i >> 5;
+    const int c = (int)(q % r_pad);
+    const size_t ns = q / r_pad;
+    const int st = (int)(ns % nsteps), n = (int)(ns / nsteps);
+    const int k = st * 32 + kk;
     dst[i] = (c < r) ? V[((size_t)n * d_in + k) * r + c] : (uint16_t)0;
   }
 }
