@@ -9,7 +9,8 @@
 // products: the input meets V first, as y = W x requires; see the design
 // notes on the summary's wording.)
 //
-// MFMA 16x16x32 in the activation dtype, fp32 accumulation.  A operand =
+// Prefill shape (the decode column stage is in decode_stages.hip).  MFMA
+// 16x16x32 in the activation dtype, fp32 accumulation.  A operand =
 // activation rows (16 rows x 32 inputs), B operand = V_n^T rows (r-columns).
 // Split-K over `nsplit` slabs: slab s holds the partial sum over its k-range;
 // consumers add the slabs (deterministic, no float atomics).  The stored rank
@@ -19,21 +20,19 @@
 
 namespace tq {
 
-// WR = row fragments per workgroup (4 waves).  WR == 4: each wave owns 16
-// rows; WR == 1: the 4 waves split the k-steps of the slab and reduce in LDS.
+// 4 waves, each owning 16 rows of a 64-row tile, over the whole k-range.
 struct ColArgs2 {
   ColArgs c[2];
 };
 
-template <typename T, int WR>
+template <typename T>
 __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
   typedef typename Vec8<T>::type V8;
   const ColArgs& a = args.c[blockIdx.z];
   __shared__ int s_res;
-  __shared__ float s_red[(WR == 1) ? 4 * 16 * 128 : 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = blockIdx.x;
-  const int rt = 16 * WR;
+  constexpr int rt = 64;
   int seg, row0, row_end;
   if (a.ap_T > 0) {
     // every (column, token) pair: column seg owns rows seg * T ... seg * T + T - 1
@@ -50,13 +49,11 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
   }
   const int vblk = a.seg_vblk ? a.seg_vblk[seg] : seg;
   const int nfrag = a.r_pad >> 4;
-
   const int split = blockIdx.y;
   const int st0 = split * a.steps_per_split;
   const int st1 = min(a.d_in >> 5, st0 + a.steps_per_split);
 
-  // this wave's rows and k-steps
-  const int rbase = (WR == 4) ? row0 + 16 * wave : row0;
+  const int rbase = row0 + 16 * wave;
   const int myrow = rbase + (lane & 15);
   const bool rvalid = myrow < row_end;
   int src = 0;
@@ -67,84 +64,28 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
   f32x4 acc[8];
 #pragma unroll
   for (int f = 0; f < 8; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (WR == 1) {
-    // decode shape: the 4 waves split the (at most 16) k-steps of the slab;
-    // every load of a wave is issued before its MFMAs (buffer loads; a step
-    // outside the slab reads zeros through an out-of-range offset)
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, 0x7FFFFFF0u);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.Vt, 0x7FFFFFF0u);
-    const uint32_t BAD = 0x7FFFFFF0u;
-    const uint32_t avo = rvalid ? ((uint32_t)src * a.lda + 8 * (lane >> 4)) * 2u : BAD;
-    const uint32_t vvo = ((uint32_t)vblk * a.r_pad * a.d_in + (lane & 15) * 32 + 8 * (lane >> 4)) * 2u;
-    u32x4 av[4], bv[4][8];
+  for (int st = st0; st < st1; ++st) {
+    V8 avv;
+    if (rvalid) avv = *reinterpret_cast<const V8*>(arow + st * 32);
+    else avv = __builtin_bit_cast(V8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int st = st0 + wave + 4 * i;
-      const bool ok = st < st1;
-      av[i] = bload128(ra, ok ? avo : BAD, ok ? st * 64u : 0u);
-#pragma unroll
-      for (int f = 0; f < 8; ++f)
-        if (f < nfrag)
-          bv[i][f] = bload128(rv, ok ? vvo + 1024u * f : BAD, ok ? st * a.r_pad * 64u : 0u);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int f = 0; f < 8; ++f)
-        if (f < nfrag)
-          acc[f] = mfma16(__builtin_bit_cast(V8, av[i]), __builtin_bit_cast(V8, bv[i][f]), acc[f]);
-  } else {
-    for (int st = st0; st < st1; ++st) {
-      V8 avv;
-      if (rvalid) {
-        avv = *reinterpret_cast<const V8*>(arow + st * 32);
-      } else {
-        avv = __builtin_bit_cast(V8, u32x4{0u, 0u, 0u, 0u});
-      }
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        if (f < nfrag) {
-          const V8 bvv = *reinterpret_cast<const V8*>(
-              vt + ((size_t)st * a.r_pad + 16 * f + (lane & 15)) * 32 + 8 * (lane >> 4));
-          acc[f] = mfma16(avv, bvv, acc[f]);
-        }
+    for (int f = 0; f < 8; ++f) {
+      if (f < nfrag) {
+        const V8 bvv = *reinterpret_cast<const V8*>(
+            vt + ((size_t)st * a.r_pad + 16 * f + (lane & 15)) * 32 + 8 * (lane >> 4));
+        acc[f] = mfma16(avv, bvv, acc[f]);
       }
     }
   }
-
   float* P = a.P + (size_t)split * a.rows_cap * a.r_pad;
-  if (WR == 1) {
-    // reduce the 4 waves' partials: s_red[wave][row 0..15][r]
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      if (f < nfrag) {
+  for (int f = 0; f < 8; ++f) {
+    if (f < nfrag) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          s_red[(wave * 16 + 4 * (lane >> 4) + v) * 128 + 16 * f + (lane & 15)] = acc[f][v];
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < 16 * a.r_pad; i += 256) {
-      const int r = i / a.r_pad, c = i - r * a.r_pad;
-      const int row = row0 + r;
-      if (row < row_end) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) v += s_red[(w * 16 + r) * 128 + c];
-        P[(size_t)row * a.r_pad + c] = v * a.sigma[c];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      if (f < nfrag) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = rbase + 4 * (lane >> 4) + v;
-          if (row < row_end)
-            P[(size_t)row * a.r_pad + 16 * f + (lane & 15)] = acc[f][v] * a.sigma[16 * f + (lane & 15)];
-        }
+      for (int v = 0; v < 4; ++v) {
+        const int row = rbase + 4 * (lane >> 4) + v;
+        if (row < row_end)
+          P[(size_t)row * a.r_pad + 16 * f + (lane & 15)] = acc[f][v] * a.sigma[16 * f + (lane & 15)];
       }
     }
   }
@@ -179,33 +120,32 @@ __global__ __launch_bounds__(256) void colproj_reduce_kernel(RedArgs a) {
   P[i] = v;
 }
 
+void launch_colproj_reduce(const ColArgs* a, int nproj, hipStream_t s) {
+  if (a[0].nsplit <= 1) return;
+  RedArgs r{};
+  int rp_max = 0;
+  for (int z = 0; z < nproj; ++z) {
+    r.P[z] = a[z].P;
+    r.total[z] = (a[z].ap_T > 0) ? nullptr : a[z].seg_off + a[z].nseg;
+    r.total_host[z] = a[z].nseg * a[z].ap_T;
+    r.r_pad[z] = a[z].r_pad;
+    rp_max = a[z].r_pad > rp_max ? a[z].r_pad : rp_max;
+  }
+  r.nsplit = a[0].nsplit;
+  r.rows_cap = a[0].rows_cap;
+  const dim3 rg((unsigned)(((size_t)a[0].rows_cap * rp_max + 255) / 256), nproj);
+  hipLaunchKernelGGL(colproj_reduce_kernel, rg, dim3(256), 0, s, r);
+}
+
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act, hipStream_t s) {
+  (void)rt;                      // 64-row tiles
   ColArgs2 args;
   args.c[0] = a[0];
   args.c[1] = a[nproj > 1 ? 1 : 0];
   const dim3 grid(max_tiles, a[0].nsplit, nproj);
-  if (act == ACT_F16) {
-    if (rt == 16) hipLaunchKernelGGL((colproj_kernel<half_t, 1>), grid, dim3(256), 0, s, args);
-    else hipLaunchKernelGGL((colproj_kernel<half_t, 4>), grid, dim3(256), 0, s, args);
-  } else {
-    if (rt == 16) hipLaunchKernelGGL((colproj_kernel<__bf16, 1>), grid, dim3(256), 0, s, args);
-    else hipLaunchKernelGGL((colproj_kernel<__bf16, 4>), grid, dim3(256), 0, s, args);
-  }
-  if (a[0].nsplit > 1) {
-    RedArgs r{};
-    int rp_max = 0;
-    for (int z = 0; z < nproj; ++z) {
-      r.P[z] = a[z].P;
-      r.total[z] = (a[z].ap_T > 0) ? nullptr : a[z].seg_off + a[z].nseg;
-      r.total_host[z] = a[z].nseg * a[z].ap_T;
-      r.r_pad[z] = a[z].r_pad;
-      rp_max = a[z].r_pad > rp_max ? a[z].r_pad : rp_max;
-    }
-    r.nsplit = a[0].nsplit;
-    r.rows_cap = a[0].rows_cap;
-    const dim3 rg((unsigned)(((size_t)a[0].rows_cap * rp_max + 255) / 256), nproj);
-    hipLaunchKernelGGL(colproj_reduce_kernel, rg, dim3(256), 0, s, r);
-  }
+  if (act == ACT_F16) hipLaunchKernelGGL((colproj_kernel<half_t>), grid, dim3(256), 0, s, args);
+  else hipLaunchKernelGGL((colproj_kernel<__bf16>), grid, dim3(256), 0, s, args);
+  launch_colproj_reduce(a, nproj, s);
 }
 
 }  // namespace tq

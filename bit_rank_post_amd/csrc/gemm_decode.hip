@@ -66,6 +66,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
   static_assert(SL::NI * (DEPTH - 1) < 64, "vmcnt range");
   static_assert(NSLOT <= 8, "ring length");
   static_assert(WAVES % 8 == 0 || 8 % WAVES == 0, "activation loads per wave");
+  static_assert(MODE != MODE_GATEUP || SL::BYTES >= NP * 2 * 16 * (128 + 8) * 2, "row-stage staging");
   constexpr int NCORR = (2 * NG + 3) / 4;   // fp32 MFMAs of the group correction
   __shared__ __attribute__((aligned(16))) char s0[SL::BYTES];
   __shared__ __attribute__((aligned(16))) char s1[SL::BYTES];
@@ -321,6 +322,82 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
       }
     }
 
+    // Row stage of the gate/up projections (MODE_GATEUP): U_m (Sigma p) as
+    // extra MFMA K-steps with p split into hi + lo halves of the activation
+    // type.  The workgroup's columns are the same for every wave, so Sigma p
+    // is gathered once per workgroup: every thread loads whole float4 runs of
+    // all split-K slabs at once (slabs past the count read zeros), adds them
+    // in slab order and writes hi/lo into slot 0 of the (drained) ring.  The
+    // U fragments of each wave are loaded before that, in the same round trip.
+    constexpr int RC = 4;                  // rank chunks of 32 (r_pad <= 128)
+    constexpr int NTH = 64 * WAVES;
+    constexpr int IMAX = (16 * 32 + NTH - 1) / NTH;   // float4 runs per thread
+    constexpr int SPMAX = 4;               // slabs loaded together
+    V8 uf[NP][RC];
+    if constexpr (MODE == MODE_GATEUP) {
+      T* sh = reinterpret_cast<T*>(s0);    // [NP][hi, lo][16 columns][r_pad + 8]
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const ProjDev& pd = a.p[p];
+        if (pd.rank == 0) continue;
+        const int rp = pd.r_pad;
+        const T* up = reinterpret_cast<const T*>(pd.U) +
+                      ((size_t)pd.m_of[e] * a.d_out + rb * 16 + l16) * rp + 8 * lg;
+#pragma unroll
+        for (int c = 0; c < RC; ++c)
+          if (32 * c < rp) uf[p][c] = *reinterpret_cast<const V8*>(up + 32 * c);
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const ProjDev& pd = a.p[p];
+        if (pd.rank == 0) continue;
+        const int rp = pd.r_pad, q4 = rp >> 2, rps = rp + 8;
+        // P row of this lane's column (lanes 0..15 are read below)
+        const int mycol = !cvalid ? -1
+                          : (a.ap_T > 0) ? pd.n_of[e] * a.ap_T + slotid / a.topk
+                                         : a.slot2col[p][slotid];
+        const __amdgpu_buffer_rsrc_t rp4 = make_rsrc(a.P[p], OOB);
+        const uint32_t slab = (uint32_t)a.p_rows_cap * rp * 4u;
+        const int ns = a.p_nsplit;
+        f32x4 ld[IMAX][SPMAX];
+        int cix[IMAX], kix[IMAX];
+        bool ok[IMAX];
+#pragma unroll
+        for (int j = 0; j < IMAX; ++j) {
+          const int i = tid + j * NTH;
+          ok[j] = i < 16 * q4;
+          const int c = ok[j] ? i / q4 : 0;
+          cix[j] = c;
+          kix[j] = i - c * q4;
+          const int col = __shfl(mycol, c, 64);
+          const bool live = ok[j] && col >= 0;
+          const uint32_t vo = ((uint32_t)col * rp + 4 * kix[j]) * 4u;
+#pragma unroll
+          for (int sp = 0; sp < SPMAX; ++sp)
+            ld[j][sp] = __builtin_bit_cast(f32x4, bload128(rp4, (live && sp < ns) ? vo + sp * slab : OOB, 0u));
+          for (int sp = SPMAX; sp < ns; ++sp)       // more slabs than one batch: serial
+            ld[j][SPMAX - 1] += __builtin_bit_cast(f32x4, bload128(rp4, live ? vo + sp * slab : OOB, 0u));
+        }
+#pragma unroll
+        for (int j = 0; j < IMAX; ++j) {
+          if (!ok[j]) continue;
+          f32x4 f = ld[j][0];
+#pragma unroll
+          for (int sp = 1; sp < SPMAX; ++sp) f += ld[j][sp];
+          T hi[4], lo[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            hi[v] = from_f32<T>(f[v]);
+            lo[v] = from_f32<T>(f[v] - to_f32(hi[v]));
+          }
+          T* d0 = sh + ((2 * p) * 16 + cix[j]) * rps + 4 * kix[j];
+          *reinterpret_cast<u32x2*>(d0) = __builtin_bit_cast(u32x2, hi);
+          *reinterpret_cast<u32x2*>(d0 + 16 * rps) = __builtin_bit_cast(u32x2, lo);
+        }
+      }
+      __syncthreads();
+    }
+
     if (rvalid) {
       const int E = a.ex[arow];
 #pragma unroll
@@ -329,27 +406,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
         for (int v = 0; v < 4; ++v) acc[p][v] = ldexpf(acc[p][v] - corr[p][v], E);
       const int o = rb * 16 + 4 * lg;
       if constexpr (MODE == MODE_GATEUP) {
+        const T* sh = reinterpret_cast<const T*>(s0);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           const ProjDev& pd = a.p[p];
           if (pd.rank == 0) continue;
-          const int rp = pd.r_pad;
-          const T* up = reinterpret_cast<const T*>(pd.U) +
-                        ((size_t)pd.m_of[e] * a.d_out + rb * 16 + l16) * rp + 8 * lg;
-          const int col = (a.ap_T > 0) ? pd.n_of[e] * a.ap_T + slotid / a.topk : a.slot2col[p][slotid];
-          const float* prow = a.P[p] + (size_t)col * rp + 8 * lg;     // Sigma p
-          for (int s2 = 0; s2 < rp; s2 += 32) {
-            const V8 av = *reinterpret_cast<const V8*>(up + s2);
-            V8 bh, bl;
+          const int rp = pd.r_pad, rps = rp + 8;
+          const T* bh = sh + ((2 * p) * 16 + l16) * rps + 8 * lg;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float v = prow[s2 + i];
-              const T hi = from_f32<T>(v);
-              bh[i] = hi;
-              bl[i] = from_f32<T>(v - to_f32(hi));
+          for (int c = 0; c < RC; ++c) {
+            if (32 * c < rp) {
+              acc[p] = mfma16(uf[p][c], *reinterpret_cast<const V8*>(bh + 32 * c), acc[p]);
+              acc[p] = mfma16(uf[p][c], *reinterpret_cast<const V8*>(bh + 16 * rps + 32 * c), acc[p]);
             }
-            acc[p] = mfma16(av, bh, acc[p]);
-            acc[p] = mfma16(av, bl, acc[p]);
           }
         }
         if (cvalid) {
@@ -365,6 +434,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
           *reinterpret_cast<f32x4*>(a.dres + ((size_t)ks * a.S + pos) * a.d_out + o) = acc[0] * g;
         }
       }
+    }
+    // slot 0 holds the gathered Sigma p until every wave has used it
+    if constexpr (MODE == MODE_GATEUP) {
+      if (t0 + 16 < cnt) __syncthreads();
     }
   }
 }

@@ -92,6 +92,7 @@ struct Plan {
   int T, k, S, path, bm_gemm, rt_col, max_tiles_gemm, max_col_tiles;
   int nks;                       // k-chunks (fp32 slabs) of the last projection's residual
   int ap_T;                      // decode: column stage over all (column, token) pairs
+  int col_tiles_x, col_tiles_down;   // decode column-stage tiles
   size_t flags, cnt, off, perm, inv, tile_gemm, tile_colx, colmask, cntw, rank;
   size_t col_off[2], col_tok[2], slot2col[2], tile_col[2];
   size_t P[3];
@@ -127,12 +128,11 @@ int choose_path(const tq_layer* L, int T, int k) {
   return path;
 }
 
-// column stage split-K for decode: slabs of 16 k-steps (512 inputs), one
-// batch of loads per wave
+// column stage split-K for decode: slabs of 1024 inputs
 int choose_nsplit(int path, long rows, int d_in) {
   (void)rows;
   if (path != 1) return 1;
-  return std::max(1, ((d_in >> 5) + 15) / 16);
+  return decode_col_splits(d_in);
 }
 
 // k-chunks of the decode kernel for a down / single projection: enough
@@ -174,6 +174,10 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
     if (L->proj[c].uploaded) nmax = std::max(nmax, L->proj[c].dev.N);
   p.ap_T = (path == 1) ? T : 0;
   if (path == 1) p.max_col_tiles = std::max(p.max_col_tiles, nmax * ((T + p.rt_col - 1) / p.rt_col));
+  // decode column-stage tiles (16 rows): every (column, token) pair for the
+  // input projection(s); per-expert slot tiles for down
+  p.col_tiles_x = nmax * ((T + 15) / 16);
+  p.col_tiles_down = (p.S + 15) / 16 + L->K;
   const int S = p.S, K = L->K;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -567,31 +571,37 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   if (p.ap_T > 0) ra.ncol = 0;     // decode: no column lists (every pair is computed)
   launch_route(ra, s);
   mark(1);
-  // activation preparation: decode = class-scaled fp16 copy + group sums;
-  // prefill bf16 = per-row exponents for the exact fp16 staging
+  // activation preparation (decode: class-scaled fp16 copy + group sums;
+  // prefill bf16: exact fp16 copy) and (a2) the column stage of the
+  // projection(s) reading x
   int* ex = nullptr;
-  if (dec) {
-    PrepArgs pa{};
-    pa.X = x;
-    pa.d = L->d_model;
-    pa.G = L->proj[0].dev.group;
-    pa.Xp = at<void>(ws, p.xp);
-    pa.sums = at<float>(ws, p.sums_x);
-    pa.ex = at<int>(ws, p.ex_x);
-    launch_act_prep(pa, T, act, s);
-  } else if (bf) {
-    ex = at<int>(ws, p.ex);
-    launch_rows_to_f16(x, T, L->d_model, nullptr, ex, at<void>(ws, p.x16), s);
-  }
-  mark(2);
-  // (a2) column stage of the projection(s) reading x
   {
     ColArgs ca[2];
     int n = 0;
     const int ncol = swiglu ? 2 : 1;
     for (int c = 0; c < ncol; ++c)
       if (L->proj[c].dev.r_pad > 0) ca[n++] = col_args_x(L, p, c, x, ws);
-    if (n) launch_colproj(ca, n, p.rt_col, p.max_col_tiles, act, s);
+    if (dec) {
+      PrepArgs pa{};
+      pa.X = x;
+      pa.d = L->d_model;
+      pa.G = L->proj[0].dev.group;
+      pa.Xp = at<void>(ws, p.xp);
+      pa.sums = at<float>(ws, p.sums_x);
+      pa.ex = at<int>(ws, p.ex_x);
+      // one launch; gate/up add the column-stage slabs themselves, the single
+      // projection's combine reads reduced rows
+      launch_prep_col(&pa, T, ca, n, p.col_tiles_x, act, s);
+      mark(2);
+      if (n && !swiglu) launch_colproj_reduce(ca, n, s);
+    } else {
+      if (bf) {
+        ex = at<int>(ws, p.ex);
+        launch_rows_to_f16(x, T, L->d_model, nullptr, ex, at<void>(ws, p.x16), s);
+      }
+      mark(2);
+      if (n) launch_colproj(ca, n, p.rt_col, p.max_col_tiles, act, s);
+    }
   }
   mark(3);
   float* dres = at<float>(ws, p.dres);
@@ -622,6 +632,8 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.nks = 1;
       da.S = p.S;
       da.ap_T = p.ap_T;
+      da.p_nsplit = p.nsplit[0];
+      da.p_rows_cap = p.rows_cap;
       da.waves = choose_waves(L, 0, p.S, 1);
       launch_gemm_decode(da, MODE_GATEUP, act, s);
     } else {
@@ -668,11 +680,10 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   float* ys = nullptr;
   if (swiglu) {
     const ProjDev& dd = L->proj[2].dev;
-    // (a2) column stage of down: one row per slot
-    if (dd.r_pad > 0) {
-      ColArgs ca = col_args_down(L, p, h, ws);
-      launch_colproj(&ca, 1, p.rt_col, p.max_col_tiles, act, s);
-    }
+    // (a2) column stage of down: one row per slot (decode: one launch with
+    // the activation preparation of h)
+    ColArgs ca = col_args_down(L, p, h, ws);
+    const int ncd = dd.r_pad > 0 ? 1 : 0;
     if (dec) {
       PrepArgs pa{};
       pa.X = h;
@@ -681,7 +692,10 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       pa.Xp = at<void>(ws, p.hp);
       pa.sums = at<float>(ws, p.sums_h);
       pa.ex = at<int>(ws, p.ex_h);
-      launch_act_prep(pa, p.S, act, s);
+      launch_prep_col(&pa, p.S, &ca, ncd, p.col_tiles_down, act, s);
+      if (ncd) launch_colproj_reduce(&ca, 1, s);
+    } else if (ncd) {
+      launch_colproj(&ca, 1, p.rt_col, p.max_col_tiles, act, s);
     }
     mark(5);
     // (a6) dense shared expert

@@ -90,6 +90,8 @@ struct ColArgs {
 };
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
                     hipStream_t s);
+// split-K reduction of the column stage: slab 0 += slabs 1..nsplit-1
+void launch_colproj_reduce(const ColArgs* a, int nproj, hipStream_t s);
 
 // ---- residual grouped GEMM (+ low-rank K-extension, SwiGLU) ---------------
 enum GemmMode { MODE_GATEUP = 0, MODE_RES = 1 };
@@ -145,6 +147,7 @@ struct DecArgs {
   int S;                         // slots (slab stride of dres)
   int waves;                     // waves per workgroup: 8 or 16 (16 rows each)
   int ap_T;                      // GATEUP: P rows are (column, token) pairs n * ap_T + t
+  int p_nsplit, p_rows_cap;      // GATEUP: P slabs to add, rows per slab
 };
 void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s);
 
@@ -157,7 +160,12 @@ struct PrepArgs {
   float* sums;                   // [rows][d/G][2]
   int* ex;                       // [rows]
 };
-void launch_act_prep(const PrepArgs& a, int rows, Act act, hipStream_t s);
+// decode: activation preparation of `prep_rows` rows and the column stage of
+// `ncol` projections (col_tiles 16-row tiles x slabs of 1024 inputs) in one
+// launch; prep may be nullptr
+void launch_prep_col(const PrepArgs* prep, int prep_rows, const ColArgs* col, int ncol,
+                     int col_tiles, Act act, hipStream_t s);
+int decode_col_splits(int d_in);
 
 // ---- combine: y_t = sum_j dres[inv(t,j)] + U_cat S_t (+ shared) ------------
 struct CombineArgs {
