@@ -35,37 +35,55 @@ namespace tq {
 // LDS slot layout (bytes) for NP projections, WAVES waves, NG groups/stage
 template <int NP, int WAVES, int NG>
 struct DecSlot {
-  static constexpr int NSZ = NG >= 4 ? NG / 4 : 1;   // dword loads per (wave, proj)
-  static constexpr int SZW = NSZ * 64;               // words per (wave, proj)
+  // scale/zero words of a stage: per projection a [WAVES][NG][16 rows] table,
+  // brought in by 64-word loads that the waves share out
+  static constexpr int NSZP = (WAVES * NG + 3) / 4;  // 64-word loads per projection
+  static constexpr int NSZW = (NP * NSZP + WAVES - 1) / WAVES;   // ... per wave
   static constexpr int NSUM = NG >= 2 ? NG / 2 : 1;  // dword loads of the group sums
-  static constexpr int NACT = WAVES >= 8 ? 1 : 8 / WAVES;   // activation loads per wave
+  static constexpr int NACT = (8 + WAVES - 1) / WAVES;   // activation loads per wave
   static constexpr int CODE = 0;                     // [WAVES][NP][64 lanes] x 16 B
   static constexpr int ACT = CODE + WAVES * NP * 1024;   // [8 k-steps][64 lanes] x 16 B
-  static constexpr int SZ = ACT + 8 * 1024;          // [WAVES][NP][SZW] x 4 B
-  static constexpr int SUM = SZ + WAVES * NP * SZW * 4;  // [NG][16 cols] float2
+  static constexpr int SZ = ACT + 8 * 1024;          // [NP][NSZP * 64] x 4 B
+  static constexpr int SUM = SZ + NP * NSZP * 256;   // [NG][16 cols] float2
   static constexpr int BYTES = SUM + NSUM * 256;
   // loads per wave per stage (the same for every wave)
-  static constexpr int NI = NP + NACT + NP * NSZ + 1;
+  static constexpr int NI = NP + NACT + NSZW + 1;
 };
 
-// ring length: as many slots as fit about 150 KB of LDS, at most DMAX + 1
-template <int BYTES, int DMAX>
+// Two workgroups share a CU when an 8-wave workgroup's ring of three slots
+// fits half the LDS: then one workgroup's routing reads, ring fill and
+// epilogue overlap the other's streaming.
+template <int BYTES, int WAVES>
+constexpr bool dec_dual() {
+  return WAVES <= 8 && 3 * BYTES + 1024 <= 80 * 1024;
+}
+
+// ring length: as many slots as fit the LDS budget (half the LDS for two
+// workgroups per CU, else about 150 KB), at most DMAX + 1
+template <int BYTES, int DMAX, bool DUAL>
 constexpr int ring_depth() {
-  return (150 * 1024 / BYTES - 1 < DMAX) ? 150 * 1024 / BYTES - 1 : DMAX;
+  constexpr int budget = DUAL ? 79 * 1024 : 150 * 1024;
+  return (budget / BYTES - 1 < DMAX) ? budget / BYTES - 1 : DMAX;
+}
+
+template <int MODE, int GS, int WAVES>
+constexpr bool dec_dual_cfg() {
+  return dec_dual<DecSlot<(MODE == MODE_GATEUP) ? 2 : 1, WAVES, 8 / GS>::BYTES, WAVES>();
 }
 
 template <typename T, int MODE, int GS, int WAVES, int DMAX>
-__global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
+__global__ __launch_bounds__(64 * WAVES, (dec_dual_cfg<MODE, GS, WAVES>() ? 4 : 1))
+void gemm_dec_kernel(DecArgs a) {
   typedef typename Vec8<T>::type V8;
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int NG = 8 / GS;             // groups per stage
   typedef DecSlot<NP, WAVES, NG> SL;
-  constexpr int DEPTH = ring_depth<SL::BYTES, DMAX>();
+  constexpr bool DUAL = dec_dual<SL::BYTES, WAVES>();
+  constexpr int DEPTH = ring_depth<SL::BYTES, DMAX, DUAL>();
   constexpr int NSLOT = DEPTH + 1;
   static_assert(DEPTH >= 2, "ring depth");
   static_assert(SL::NI * (DEPTH - 1) < 64, "vmcnt range");
   static_assert(NSLOT <= 8, "ring length");
-  static_assert(WAVES % 8 == 0 || 8 % WAVES == 0, "activation loads per wave");
   static_assert(MODE != MODE_GATEUP || SL::BYTES >= NP * 2 * 16 * (128 + 8) * 2, "row-stage staging");
   constexpr int NCORR = (2 * NG + 3) / 4;   // fp32 MFMAs of the group correction
   __shared__ __attribute__((aligned(16))) char s0[SL::BYTES];
@@ -76,7 +94,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) char s5[NSLOT > 5 ? SL::BYTES : 16];
   __shared__ __attribute__((aligned(16))) char s6[NSLOT > 6 ? SL::BYTES : 16];
   __shared__ __attribute__((aligned(16))) char s7[NSLOT > 7 ? SL::BYTES : 16];
-  __shared__ __attribute__((aligned(16))) char s_dummy[1024];  // target of unused loads
+  // target of unused loads (activation loads past the 8th k-step are 16 B
+  // per lane, the others 4 B)
+  __shared__ __attribute__((aligned(16))) char s_dummy[WAVES * SL::NACT > 8 ? 1024 : 256];
   char* const slot[8] = {s0, s1, s2, s3, s4, s5, s6, s7};
 
   // Workgroup -> (expert, row-fragment group, k-chunk).  Consecutive
@@ -93,11 +113,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
   const int ks = jq / nby8;
   const int by = (jq - ks * nby8) * 8 + (wg & 7);
   if (by >= nby) return;
-  const int cnt = a.cnt[e];
-  if (cnt == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l16 = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int rb_raw = by * WAVES + wave;
   const bool rvalid = rb_raw < nrb;
   const int rb = rvalid ? rb_raw : nrb - 1;          // clamped: loads stay in bounds
@@ -124,57 +142,111 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
     cbase[p] = a.p[p].codes + (size_t)e * cpe + (size_t)rb * nsteps * 32;
     szb[p] = a.p[p].sz + ((size_t)e * nrb + rb) * ng * 16;
     rc[p] = make_rsrc(cbase[p], (uint32_t)nsteps * 128u);
-    rs[p] = make_rsrc(szb[p], (uint32_t)ng * 64u);
+    rs[p] = make_rsrc(a.p[p].sz + (size_t)e * nrb * ng * 16, (uint32_t)nrb * ng * 64u);
+  }
+  // scale/zero loads of this wave: load i = wave + WAVES * k of the stage
+  // covers words 64 (i mod NSZP) + lane of projection i / NSZP's table, i.e.
+  // (wave' = w / (16 NG), group w / 16 mod NG, row w mod 16)
+  uint32_t sz_vo[SL::NSZW];
+  int sz_p[SL::NSZW], sz_lds[SL::NSZW];
+#pragma unroll
+  for (int k = 0; k < SL::NSZW; ++k) {
+    const int i = wave + WAVES * k;
+    const bool ok = i < NP * SL::NSZP;
+    sz_p[k] = ok ? i / SL::NSZP : 0;
+    sz_lds[k] = ok ? SL::SZ + i * 256 : -1;
+    const int w = (ok ? i - sz_p[k] * SL::NSZP : 0) * 64 + lane;
+    const int wv = w / (16 * NG), g = (w / 16) % NG, row = w & 15;
+    const int rbw = min(by * WAVES + wv, nrb - 1);
+    sz_vo[k] = (ok && wv < WAVES) ? (((uint32_t)rbw * ng + g) * 16u + row) * 4u : OOB;
   }
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.Xp, (uint32_t)a.rows * a.d_in * 2u);
   const __amdgpu_buffer_rsrc_t rsm = make_rsrc(a.sums, (uint32_t)a.rows * ng * 8u);
 
+  // Loads of batch b (stage-time b of the ring) into the slot at base: the
+  // expert's codes and scale/zero words (known before the routing) ...
+  auto issue_w = [&](int b, char* base) {
+    const bool live = b < ntau;
+    int tr = b + r0;
+    tr = (tr >= ntau) ? tr - ntau : tr;
+    const int st = live ? k0 + tr : 0;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      dma16(rc[p], base + SL::CODE + (wave * NP + p) * 1024, live ? lane * 16u : OOB, st * 1024u);
+#pragma unroll
+    for (int k = 0; k < SL::NSZW; ++k)
+      dma4(sz_p[k] == 0 ? rs[0] : rs[NP - 1], sz_lds[k] >= 0 ? base + sz_lds[k] : s_dummy,
+           live ? sz_vo[k] : OOB, st * NG * 64u);
+  };
+  // ... and the activations and group sums of the column tile's slots
+  uint32_t act_vo = OOB, sum_vo = OOB;
+  auto issue_x = [&](int b, char* base) {
+    const bool live = b < ntau;
+    int tr = b + r0;
+    tr = (tr >= ntau) ? tr - ntau : tr;
+    const int st = live ? k0 + tr : 0;
+#pragma unroll
+    for (int i = 0; i < SL::NACT; ++i) {
+      const int j = wave * SL::NACT + i;      // k-step; loads past the 8th step load nothing
+      dma16(rx, j < 8 ? base + SL::ACT + j * 1024 : s_dummy,
+            (live && j < 8 && act_vo != OOB) ? act_vo + j * 64u : OOB, st * 512u);
+    }
+    dma4(rsm, wave < SL::NSUM ? base + SL::SUM + wave * 256 : s_dummy,
+         live ? sum_vo : OOB, st * NG * 8u);
+  };
+
+  // With the expert expected to be routed to (a.spec), the codes of the
+  // first DEPTH stages are requested before the routing reads return.
+  const bool spec = a.spec && ntau > 0;
+  if (spec) {
+#pragma unroll
+    for (int b = 0; b < DEPTH; ++b) issue_w(b, slot[b]);
+  }
+
+  // routing reads, none waiting for another: the expert's slot count and
+  // offset, and the slot ids of its first 16 positions (entries past the
+  // count are stale and never used)
+  const int* etab = a.etab + (size_t)e * a.S;
+  const int cnt = a.cnt[e];
+  const int offe = a.off[e];
+  const int sl_first = etab[min(l16, a.S - 1)];
+  // tile row / column of the expert (row stage of MODE_GATEUP)
+  int m_e[NP], n_e[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const bool lr = MODE == MODE_GATEUP && a.p[p].rank > 0;
+    m_e[p] = lr ? a.p[p].m_of[e] : 0;
+    n_e[p] = lr ? a.p[p].n_of[e] : 0;
+  }
+  if (cnt == 0) {
+    wait_vm<0>();                          // no load may land after the workgroup ends
+    return;
+  }
+
   for (int t0 = 0; t0 < cnt; t0 += 16) {
     const int ncol = min(16, cnt - t0);
     const bool cvalid = l16 < ncol;
-    const int pos = a.off[e] + t0 + (cvalid ? l16 : 0);
-    const int slotid = a.perm[pos];
+    const int pos = offe + t0 + (cvalid ? l16 : 0);
+    int slotid = (t0 == 0) ? sl_first : etab[min(t0 + l16, a.S - 1)];
+    slotid = cvalid ? slotid : __shfl(slotid, 0, 64);    // column 0 always holds a slot
     const int arow = a.gather ? slotid / a.topk : pos;
+    const int E = a.ex[arow];              // row exponent, used by the epilogue
 
     // per-lane load offsets (columns past the tile's slots are not loaded:
     // their MFMA columns are never stored, and columns do not mix)
     // activations: lane = (lg, col) of k-step j; the k-step adds 64 bytes
-    const uint32_t act_vo = cvalid ? ((uint32_t)arow * a.d_in + 8 * lg) * 2u : OOB;
+    act_vo = cvalid ? ((uint32_t)arow * a.d_in + 8 * lg) * 2u : OOB;
     // group sums: word w = 64 * wave + lane of the stage's [NG][16][2] table
-    uint32_t sum_vo = OOB;
+    sum_vo = OOB;
     {
       const int w = 64 * wave + lane;
       const int gi = w >> 5, col = (w >> 1) & 15, comp = w & 1;
-      if (wave < SL::NSUM && gi < NG && col < ncol) {
-        const int r = a.gather ? a.perm[a.off[e] + t0 + col] / a.topk : a.off[e] + t0 + col;
-        sum_vo = (((uint32_t)r * ng + gi) * 2u + comp) * 4u;
-      }
+      const int r = a.gather ? __shfl(slotid, col, 64) / a.topk : offe + t0 + col;
+      if (wave < SL::NSUM && gi < NG && col < ncol) sum_vo = (((uint32_t)r * ng + gi) * 2u + comp) * 4u;
     }
-
     auto issue = [&](int b, char* base) {
-      const bool live = b < ntau;
-      int tr = b + r0;
-      tr = (tr >= ntau) ? tr - ntau : tr;
-      const int st = live ? k0 + tr : 0;
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-        dma16(rc[p], base + SL::CODE + (wave * NP + p) * 1024, live ? lane * 16u : OOB, st * 1024u);
-#pragma unroll
-      for (int i = 0; i < SL::NACT; ++i) {
-        const int j = wave * SL::NACT + i;      // k-step; waves past the 8th load nothing
-        dma16(rx, j < 8 ? base + SL::ACT + j * 1024 : s_dummy,
-              (live && j < 8 && act_vo != OOB) ? act_vo + j * 64u : OOB, st * 512u);
-      }
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int i = 0; i < SL::NSZ; ++i) {
-          const int w = 64 * i + lane;
-          dma4(rs[p], base + SL::SZ + ((wave * NP + p) * SL::SZW + 64 * i) * 4,
-               (live && w < NG * 16) ? w * 4u : OOB, st * NG * 64u);
-        }
-      dma4(rsm, wave < SL::NSUM ? base + SL::SUM + wave * 256 : s_dummy,
-           live ? sum_vo : OOB, st * NG * 8u);
+      issue_w(b, base);
+      issue_x(b, base);
     };
 
     f32x4 acc[NP], corr[NP];
@@ -189,7 +261,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(
-            base + SL::SZ + ((wave * NP + p) * SL::SZW + gi * 16 + 4 * lg) * 4);
+            base + SL::SZ + (p * SL::NSZP * 64 + (wave * NG + gi) * 16 + 4 * lg) * 4);
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           acc[p][v] += (float)__builtin_bit_cast(half_t, (uint16_t)(w[v] & 0xFFFFu)) * C[p][v];
@@ -211,7 +283,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
           float av = 0.f;
           if (t < 2 * NG) {
             const uint32_t w = *reinterpret_cast<const uint32_t*>(
-                base + SL::SZ + ((wave * NP + p) * SL::SZW + g * 16 + l16) * 4);
+                base + SL::SZ + (p * SL::NSZP * 64 + (wave * NG + g) * 16 + l16) * 4);
             const float sc = (float)__builtin_bit_cast(half_t, (uint16_t)(w & 0xFFFFu));
             const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(w >> 16));
             av = (t < NG) ? sc : sc * z;
@@ -259,13 +331,23 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
     // empty loads), so the loop has a single back edge and the compiler's
     // own wait counts stay exact.
     if (ntau > 0) {
+      // prologue: batches 0 .. DEPTH-1 (their codes may already be in flight)
+      if (spec && t0 == 0) {
 #pragma unroll
-      for (int b = 0; b < DEPTH; ++b) issue(b, slot[b]);
+        for (int b = 0; b < DEPTH; ++b) issue_x(b, slot[b]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < DEPTH; ++b) issue(b, slot[b]);
+      }
       for (int t = 0; t < ntau; t += NSLOT) {
 #pragma unroll
         for (int u = 0; u < NSLOT; ++u) {
           const int tau = t + u;
-          wait_vm<SL::NI * (DEPTH - 1)>();
+          // first round: at most u * NI loads were issued after batch u's
+          // last one whichever way the prologue went; later rounds: the
+          // DEPTH - 1 newer batches
+          if (t == 0 && u < DEPTH - 1) wait_vm_first<SL::NI, DEPTH - 1>(u);
+          else wait_vm<SL::NI * (DEPTH - 1)>();
           bar_nofence();
           if (tau < ntau) compute(slot[u]);
           issue(tau + DEPTH, slot[(u + DEPTH) % NSLOT]);
@@ -328,69 +410,74 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
     // is gathered once per workgroup: every thread loads whole float4 runs of
     // all split-K slabs at once (slabs past the count read zeros), adds them
     // in slab order and writes hi/lo into slot 0 of the (drained) ring.  The
-    // U fragments of each wave are loaded before that, in the same round trip.
+    // U fragments of each wave go out right after, in the same round trip.
+    // Every address here derives from an opaque copy of the thread id, so
+    // none of it is computed ahead and held in registers across the ring.
     constexpr int RC = 4;                  // rank chunks of 32 (r_pad <= 128)
     constexpr int NTH = 64 * WAVES;
     constexpr int IMAX = (16 * 32 + NTH - 1) / NTH;   // float4 runs per thread
     constexpr int SPMAX = 4;               // slabs loaded together
     V8 uf[NP][RC];
     if constexpr (MODE == MODE_GATEUP) {
+      const int tid_e = opaque(tid);
+      const int l16e = tid_e & 15, lge = (tid_e >> 4) & 3;
       T* sh = reinterpret_cast<T*>(s0);    // [NP][hi, lo][16 columns][r_pad + 8]
+      const int tok = slotid / a.topk;     // P row of the column = (n, token)
+      const int ns = a.p_nsplit;
+      f32x4 ld[NP][IMAX][SPMAX];
+      int cix[NP][IMAX], kix[NP][IMAX];
+      bool ok[NP][IMAX];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const ProjDev& pd = a.p[p];
+        const int rp = pd.r_pad, q4 = rp >> 2;
+        const int mycol = (cvalid && pd.rank > 0) ? n_e[p] * a.ap_T + tok : -1;
+        const __amdgpu_buffer_rsrc_t rp4 = make_rsrc(a.P[p], OOB);
+        const uint32_t slab = (uint32_t)a.p_rows_cap * rp * 4u;
+#pragma unroll
+        for (int j = 0; j < IMAX; ++j) {
+          const int i = tid_e + j * NTH;
+          ok[p][j] = pd.rank > 0 && i < 16 * q4;
+          const int c = ok[p][j] ? i / q4 : 0;
+          cix[p][j] = c;
+          kix[p][j] = i - c * q4;
+          const int col = __shfl(mycol, c, 64);   // lane c holds column c
+          const bool live = ok[p][j] && col >= 0;
+          const uint32_t vo = ((uint32_t)col * rp + 4 * kix[p][j]) * 4u;
+#pragma unroll
+          for (int sp = 0; sp < SPMAX; ++sp)
+            ld[p][j][sp] = __builtin_bit_cast(f32x4, bload128(rp4, (live && sp < ns) ? vo + sp * slab : OOB, 0u));
+          for (int sp = SPMAX; sp < ns; ++sp)       // more slabs than one batch: serial
+            ld[p][j][SPMAX - 1] += __builtin_bit_cast(f32x4, bload128(rp4, live ? vo + sp * slab : OOB, 0u));
+        }
+      }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const ProjDev& pd = a.p[p];
         if (pd.rank == 0) continue;
         const int rp = pd.r_pad;
         const T* up = reinterpret_cast<const T*>(pd.U) +
-                      ((size_t)pd.m_of[e] * a.d_out + rb * 16 + l16) * rp + 8 * lg;
+                      ((size_t)m_e[p] * a.d_out + rb * 16 + l16e) * rp + 8 * lge;
 #pragma unroll
         for (int c = 0; c < RC; ++c)
           if (32 * c < rp) uf[p][c] = *reinterpret_cast<const V8*>(up + 32 * c);
       }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const ProjDev& pd = a.p[p];
-        if (pd.rank == 0) continue;
-        const int rp = pd.r_pad, q4 = rp >> 2, rps = rp + 8;
-        // P row of this lane's column (lanes 0..15 are read below)
-        const int mycol = !cvalid ? -1
-                          : (a.ap_T > 0) ? pd.n_of[e] * a.ap_T + slotid / a.topk
-                                         : a.slot2col[p][slotid];
-        const __amdgpu_buffer_rsrc_t rp4 = make_rsrc(a.P[p], OOB);
-        const uint32_t slab = (uint32_t)a.p_rows_cap * rp * 4u;
-        const int ns = a.p_nsplit;
-        f32x4 ld[IMAX][SPMAX];
-        int cix[IMAX], kix[IMAX];
-        bool ok[IMAX];
+        const int rps = a.p[p].r_pad + 8;
 #pragma unroll
         for (int j = 0; j < IMAX; ++j) {
-          const int i = tid + j * NTH;
-          ok[j] = i < 16 * q4;
-          const int c = ok[j] ? i / q4 : 0;
-          cix[j] = c;
-          kix[j] = i - c * q4;
-          const int col = __shfl(mycol, c, 64);
-          const bool live = ok[j] && col >= 0;
-          const uint32_t vo = ((uint32_t)col * rp + 4 * kix[j]) * 4u;
+          if (!ok[p][j]) continue;
+          f32x4 f = ld[p][j][0];
 #pragma unroll
-          for (int sp = 0; sp < SPMAX; ++sp)
-            ld[j][sp] = __builtin_bit_cast(f32x4, bload128(rp4, (live && sp < ns) ? vo + sp * slab : OOB, 0u));
-          for (int sp = SPMAX; sp < ns; ++sp)       // more slabs than one batch: serial
-            ld[j][SPMAX - 1] += __builtin_bit_cast(f32x4, bload128(rp4, live ? vo + sp * slab : OOB, 0u));
-        }
-#pragma unroll
-        for (int j = 0; j < IMAX; ++j) {
-          if (!ok[j]) continue;
-          f32x4 f = ld[j][0];
-#pragma unroll
-          for (int sp = 1; sp < SPMAX; ++sp) f += ld[j][sp];
+          for (int sp = 1; sp < SPMAX; ++sp) f += ld[p][j][sp];
           T hi[4], lo[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             hi[v] = from_f32<T>(f[v]);
             lo[v] = from_f32<T>(f[v] - to_f32(hi[v]));
           }
-          T* d0 = sh + ((2 * p) * 16 + cix[j]) * rps + 4 * kix[j];
+          T* d0 = sh + ((2 * p) * 16 + cix[p][j]) * rps + 4 * kix[p][j];
           *reinterpret_cast<u32x2*>(d0) = __builtin_bit_cast(u32x2, hi);
           *reinterpret_cast<u32x2*>(d0 + 16 * rps) = __builtin_bit_cast(u32x2, lo);
         }
@@ -399,7 +486,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
     }
 
     if (rvalid) {
-      const int E = a.ex[arow];
 #pragma unroll
       for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -407,12 +493,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_dec_kernel(DecArgs a) {
       const int o = rb * 16 + 4 * lg;
       if constexpr (MODE == MODE_GATEUP) {
         const T* sh = reinterpret_cast<const T*>(s0);
+        const int tid_e = opaque(tid);
+        const int l16e = tid_e & 15, lge = (tid_e >> 4) & 3;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           const ProjDev& pd = a.p[p];
           if (pd.rank == 0) continue;
           const int rp = pd.r_pad, rps = rp + 8;
-          const T* bh = sh + ((2 * p) * 16 + l16) * rps + 8 * lg;
+          const T* bh = sh + ((2 * p) * 16 + l16e) * rps + 8 * lge;
 #pragma unroll
           for (int c = 0; c < RC; ++c) {
             if (32 * c < rp) {
@@ -446,7 +534,7 @@ template <typename T, int MODE, int GS, int WAVES, int DMAX>
 static void dec_launch(const DecArgs& a, hipStream_t s) {
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int BYTES = DecSlot<NP, WAVES, 8 / GS>::BYTES;
-  if constexpr (WAVES > 8 && ring_depth<BYTES, DMAX>() < 2) {
+  if constexpr (WAVES > 8 && ring_depth<BYTES, DMAX, false>() < 2) {
     // slots too large for a ring of three: fall back to 8 waves
     dec_launch<T, MODE, GS, 8, DMAX>(a, s);
   } else {
@@ -469,14 +557,37 @@ static void dec_gs(const DecArgs& a, hipStream_t s) {
 
 template <typename T, int MODE>
 static void dec_waves(const DecArgs& a, hipStream_t s) {
-  if (a.waves == 16) dec_gs<T, MODE, 16, 6>(a, s);
-  else dec_gs<T, MODE, 8, 6>(a, s);
+  if constexpr (MODE == MODE_GATEUP) {
+    switch (a.waves) {
+      case 16: dec_gs<T, MODE, 16, 6>(a, s); break;
+      case 14: dec_gs<T, MODE, 14, 6>(a, s); break;
+      case 12: dec_gs<T, MODE, 12, 6>(a, s); break;
+      default: dec_gs<T, MODE, 8, 6>(a, s); break;
+    }
+  } else {
+    if (a.waves == 16) dec_gs<T, MODE, 16, 6>(a, s);
+    else dec_gs<T, MODE, 8, 6>(a, s);
+  }
 }
 
 // Ring depth: as many slots as fit the LDS budget (at most 7).  With 16 waves
 // a gate/up slot holds 32 KB of codes (3 slots), a down / single slot 16 KB
 // (5 slots); with 8 waves 16 resp. 8 KB (5 resp. 7 slots).  One workgroup
 // per CU either way.
+template <int MODE>
+static bool dual_gs(int group) {
+  switch (group >> 5) {
+    case 1: return dec_dual_cfg<MODE, 1, 8>();
+    case 2: return dec_dual_cfg<MODE, 2, 8>();
+    case 4: return dec_dual_cfg<MODE, 4, 8>();
+    default: return dec_dual_cfg<MODE, 8, 8>();
+  }
+}
+
+bool decode_dual(int np, int group) {
+  return np == 2 ? dual_gs<MODE_GATEUP>(group) : dual_gs<MODE_RES>(group);
+}
+
 void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s) {
   if (act == ACT_F16) {
     if (mode == MODE_GATEUP) dec_waves<half_t, MODE_GATEUP>(a, s);

@@ -142,6 +142,7 @@ __global__ __launch_bounds__(1024) void route_kernel(RouteArgs a) {
       const int p = s_off[e] + cntw[(s >> 6) * K + e] + rank[s];
       a.perm[p] = s;
       a.inv[s] = p;
+      if (a.etab) a.etab[e * S + (p - s_off[e])] = s;
     } else {
       a.inv[s] = -1;
     }

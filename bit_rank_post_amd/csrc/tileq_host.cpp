@@ -93,7 +93,7 @@ struct Plan {
   int nks;                       // k-chunks (fp32 slabs) of the last projection's residual
   int ap_T;                      // decode: column stage over all (column, token) pairs
   int col_tiles_x, col_tiles_down;   // decode column-stage tiles
-  size_t flags, cnt, off, perm, inv, tile_gemm, tile_colx, colmask, cntw, rank;
+  size_t flags, cnt, off, perm, inv, etab, tile_gemm, tile_colx, colmask, cntw, rank;
   size_t col_off[2], col_tok[2], slot2col[2], tile_col[2];
   size_t P[3];
   int nsplit[3];
@@ -149,12 +149,52 @@ int choose_nks(const tq_layer* L, int q, int S) {
   return nks;
 }
 
-// waves per decode workgroup: 16 (four per SIMD) when that still gives every
-// CU a workgroup, else 8
-int choose_waves(const tq_layer* L, int q, int S, int nks) {
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Waves (16-row fragments) per decode workgroup.  The grid runs in
+// ceil(wgs / (CUs x workgroups per CU)) rounds and a round lasts about as
+// long as one workgroup streams its rows.  Cost of a choice = rounds x (bytes
+// of one stage of the workgroup, in KB: W x NP KB of codes + 8 KB of
+// activations, plus a fixed per-workgroup cost of about 12 KB-equivalents per
+// stage for ring fill, routing reads and epilogue).  8-wave workgroups run
+// two per CU when their ring fits half the LDS; then the fixed cost of one is
+// hidden behind the other's streaming.  The input projections may use 8, 12,
+// 14 or 16 waves; single-projection launches 8 or 16.
+int choose_waves(const tq_layer* L, int q, int S, int nks, int np) {
   const long active = std::min<long>(L->K, S);
-  const long wg16 = active * ((L->proj[q].dev.nrb + 15) / 16) * nks;
-  return wg16 >= 256 ? 16 : 8;
+  const int nrb = L->proj[q].dev.nrb;
+  const long cus = device_cus();
+  const bool dual = decode_dual(np, L->proj[q].dev.group);
+  static const int cand2[] = {16, 14, 12, 8};
+  static const int cand1[] = {16, 8};
+  const int* cand = (np == 2) ? cand2 : cand1;
+  const int nc = (np == 2) ? 4 : 2;
+  int best = 16;
+  long best_cost = -1;
+  for (int i = 0; i < nc; ++i) {
+    const int w = cand[i];
+    const long per_cu = (w <= 8 && dual) ? 2 : 1;
+    const long wgs = active * ((nrb + w - 1) / w) * nks;
+    const long rounds = (wgs + cus * per_cu - 1) / (cus * per_cu);
+    const long cost = rounds * (w * np + 8 + (per_cu == 2 ? 0 : 12));
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = w;
+    }
+  }
+  return best;
 }
 
 Plan make_plan(const tq_layer* L, int T, int k, int path) {
@@ -190,6 +230,7 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.off = take(sizeof(int) * (K + 1));
   p.perm = take(sizeof(int) * S);
   p.inv = take(sizeof(int) * S);
+  p.etab = take(sizeof(int) * (size_t)K * S);
   p.tile_gemm = take(sizeof(int) * (K + 1));
   p.tile_colx = take(sizeof(int) * (K + 1));
   p.colmask = take(sizeof(int) * std::max(T, 1));
@@ -290,6 +331,7 @@ void fill_route(const tq_layer* L, const Plan& p, const int* ids, void* ws, Rout
   r.off = at<int>(ws, p.off);
   r.perm = at<int>(ws, p.perm);
   r.inv = at<int>(ws, p.inv);
+  r.etab = (p.path == 1) ? at<int>(ws, p.etab) : nullptr;
   r.tile_gemm = at<int>(ws, p.tile_gemm);
   r.tile_colx = at<int>(ws, p.tile_colx);
   r.cntw = at<int>(ws, p.cntw);
@@ -613,7 +655,8 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     da.d_in = L->d_model;
     da.d_out = L->proj[0].dev.d_out;
     da.topk = topk;
-    da.perm = at<int>(ws, p.perm);
+    da.etab = at<int>(ws, p.etab);
+    da.spec = p.S >= 2 * K;  // nearly every expert is routed to
     da.off = at<int>(ws, p.off);
     da.cnt = at<int>(ws, p.cnt);
     da.gather = 1;
@@ -634,14 +677,14 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.ap_T = p.ap_T;
       da.p_nsplit = p.nsplit[0];
       da.p_rows_cap = p.rows_cap;
-      da.waves = choose_waves(L, 0, p.S, 1);
+      da.waves = choose_waves(L, 0, p.S, 1, 2);
       launch_gemm_decode(da, MODE_GATEUP, act, s);
     } else {
       da.dres = dres;
       da.gates = topk_w;
       da.nks = p.nks;
       da.S = p.S;
-      da.waves = choose_waves(L, 0, p.S, p.nks);
+      da.waves = choose_waves(L, 0, p.S, p.nks, 1);
       launch_gemm_decode(da, MODE_RES, act, s);
     }
   } else {
@@ -727,7 +770,8 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.d_in = dd.d_in;
       da.d_out = dd.d_out;
       da.topk = topk;
-      da.perm = at<int>(ws, p.perm);
+      da.etab = at<int>(ws, p.etab);
+      da.spec = p.S >= 2 * K;  // nearly every expert is routed to
       da.off = at<int>(ws, p.off);
       da.cnt = at<int>(ws, p.cnt);
       da.gather = 0;
@@ -740,7 +784,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.gates = topk_w;
       da.nks = p.nks;
       da.S = p.S;
-      da.waves = choose_waves(L, 2, p.S, p.nks);
+      da.waves = choose_waves(L, 2, p.S, p.nks, 1);
       launch_gemm_decode(da, MODE_RES, act, s);
     } else {
       GemmArgs ga{};

@@ -98,6 +98,24 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+// wait_vm<u * NI>() for u in [0, UMAX); u must fold to a constant (an
+// unrolled loop index)
+template <int NI, int UMAX, int U = 0>
+__device__ __forceinline__ void wait_vm_first(int u) {
+  if constexpr (U < UMAX) {
+    if (u == U) wait_vm<U * NI>();
+    else wait_vm_first<NI, UMAX, U + 1>(u);
+  }
+}
+
+// x, unknown to the optimizer from here on: values derived from it are
+// computed where they are used instead of being hoisted out of loops (and
+// held in registers across them)
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // workgroup barrier without a memory fence (a fenced barrier waits for every
 // load in flight); the empty asm statements keep the compiler from moving
 // LDS accesses across it

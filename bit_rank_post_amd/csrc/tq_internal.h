@@ -56,6 +56,7 @@ struct RouteArgs {
   int* off;                      // [K+1]
   int* perm;                     // [S]
   int* inv;                      // [S]
+  int* etab;                     // optional [K][S]: slot ids of expert e at e * S + c
   int* tile_gemm;                // [K+1] prefix of ceil(cnt/bm_gemm)
   int* tile_colx;                // [K+1] prefix of ceil(cnt/rt_col) (down column stage)
   int* col_off[2];               // [N+1]
@@ -129,7 +130,7 @@ void launch_rows_to_f16(const void* X, int rows, int d, const int* row_src, int*
 // ---- decode streaming residual kernel --------------------------------------
 struct DecArgs {
   int K, d_in, d_out, topk;
-  const int* perm;
+  const int* etab;               // [K][S] slot ids of each expert, in position order
   const int* off;
   const int* cnt;
   int gather;                    // 1: activation row of a slot = its token; 0: pos
@@ -145,11 +146,15 @@ struct DecArgs {
   const float* gates;
   int nks;                       // k-chunks (RES; 1 for GATEUP)
   int S;                         // slots (slab stride of dres)
-  int waves;                     // waves per workgroup: 8 or 16 (16 rows each)
+  int waves;                     // waves per workgroup (16 rows each): 8, 12, 14 or 16 (GATEUP), 8 or 16
   int ap_T;                      // GATEUP: P rows are (column, token) pairs n * ap_T + t
   int p_nsplit, p_rows_cap;      // GATEUP: P slabs to add, rows per slab
+  int spec;                      // 1: request the first stages' codes before the routing reads return
 };
 void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s);
+// true when 8-wave decode workgroups of np projections and this group size
+// run two per CU
+bool decode_dual(int np, int group);
 
 // ---- activation preparation for the decode kernel ---------------------------
 struct PrepArgs {
