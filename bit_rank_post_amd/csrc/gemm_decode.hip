@@ -84,7 +84,7 @@ void gemm_dec_kernel(DecArgs a) {
   static_assert(DEPTH >= 2, "ring depth");
   static_assert(SL::NI * (DEPTH - 1) < 64, "vmcnt range");
   static_assert(NSLOT <= 8, "ring length");
-  static_assert(MODE != MODE_GATEUP || SL::BYTES >= NP * 2 * 16 * (128 + 8) * 2, "row-stage staging");
+  static_assert(SL::BYTES >= NP * 2 * 16 * (128 + 8) * 2, "row-stage staging");
   constexpr int NCORR = (2 * NG + 3) / 4;   // fp32 MFMAs of the group correction
   __shared__ __attribute__((aligned(16))) char s0[SL::BYTES];
   __shared__ __attribute__((aligned(16))) char s1[SL::BYTES];
@@ -214,7 +214,7 @@ void gemm_dec_kernel(DecArgs a) {
   int m_e[NP], n_e[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const bool lr = MODE == MODE_GATEUP && a.p[p].rank > 0;
+    const bool lr = a.P[p] != nullptr && a.p[p].rank > 0;
     m_e[p] = lr ? a.p[p].m_of[e] : 0;
     n_e[p] = lr ? a.p[p].n_of[e] : 0;
   }
@@ -404,25 +404,29 @@ void gemm_dec_kernel(DecArgs a) {
       }
     }
 
-    // Row stage of the gate/up projections (MODE_GATEUP): U_m (Sigma p) as
-    // extra MFMA K-steps with p split into hi + lo halves of the activation
-    // type.  The workgroup's columns are the same for every wave, so Sigma p
-    // is gathered once per workgroup: every thread loads whole float4 runs of
-    // all split-K slabs at once (slabs past the count read zeros), adds them
-    // in slab order and writes hi/lo into slot 0 of the (drained) ring.  The
-    // U fragments of each wave go out right after, in the same round trip.
-    // Every address here derives from an opaque copy of the thread id, so
-    // none of it is computed ahead and held in registers across the ring.
+    // Row stage U_m (Sigma p) as extra MFMA K-steps, p split into hi + lo
+    // halves of the activation type: the gate/up projections of MODE_GATEUP,
+    // and in MODE_RES the projection when P is given, done by the workgroups
+    // of the first k-chunk.  P row of a column: its (tile column, token) pair
+    // when ap_T > 0, else the slot's position.  The workgroup's columns
+    // are the same for every wave, so Sigma p is gathered once per workgroup:
+    // every thread loads whole float4 runs of all split-K slabs at once
+    // (slabs past the count read zeros), adds them in slab order and writes
+    // hi/lo into slot 0 of the (drained) ring.  The U fragments of each wave
+    // go out right after, in the same round trip.  Every address here
+    // derives from an opaque copy of the thread id, so none of it is computed
+    // ahead and held in registers across the ring.
     constexpr int RC = 4;                  // rank chunks of 32 (r_pad <= 128)
     constexpr int NTH = 64 * WAVES;
     constexpr int IMAX = (16 * 32 + NTH - 1) / NTH;   // float4 runs per thread
-    constexpr int SPMAX = 4;               // slabs loaded together
+    constexpr int SPMAX = (NP == 2) ? 4 : 16;          // slabs loaded together
     V8 uf[NP][RC];
-    if constexpr (MODE == MODE_GATEUP) {
+    const bool rowstage = (MODE == MODE_GATEUP) || (ks == 0 && a.P[0] != nullptr && a.p[0].rank > 0);
+    if (rowstage) {
       const int tid_e = opaque(tid);
       const int l16e = tid_e & 15, lge = (tid_e >> 4) & 3;
       T* sh = reinterpret_cast<T*>(s0);    // [NP][hi, lo][16 columns][r_pad + 8]
-      const int tok = slotid / a.topk;     // P row of the column = (n, token)
+      const int tok = slotid / a.topk;
       const int ns = a.p_nsplit;
       f32x4 ld[NP][IMAX][SPMAX];
       int cix[NP][IMAX], kix[NP][IMAX];
@@ -431,7 +435,8 @@ void gemm_dec_kernel(DecArgs a) {
       for (int p = 0; p < NP; ++p) {
         const ProjDev& pd = a.p[p];
         const int rp = pd.r_pad, q4 = rp >> 2;
-        const int mycol = (cvalid && pd.rank > 0) ? n_e[p] * a.ap_T + tok : -1;
+        const int prow = (a.ap_T > 0) ? n_e[p] * a.ap_T + tok : pos;
+        const int mycol = (cvalid && pd.rank > 0) ? prow : -1;
         const __amdgpu_buffer_rsrc_t rp4 = make_rsrc(a.P[p], OOB);
         const uint32_t slab = (uint32_t)a.p_rows_cap * rp * 4u;
 #pragma unroll
@@ -491,7 +496,7 @@ void gemm_dec_kernel(DecArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[p][v] = ldexpf(acc[p][v] - corr[p][v], E);
       const int o = rb * 16 + 4 * lg;
-      if constexpr (MODE == MODE_GATEUP) {
+      if (rowstage) {
         const T* sh = reinterpret_cast<const T*>(s0);
         const int tid_e = opaque(tid);
         const int l16e = tid_e & 15, lge = (tid_e >> 4) & 3;
@@ -509,24 +514,26 @@ void gemm_dec_kernel(DecArgs a) {
             }
           }
         }
+      }
+      // output addresses from opaque copies: computed here, not held across the ring
+      const int pos_e = opaque(pos), o_e = opaque(o);
+      if constexpr (MODE == MODE_GATEUP) {
         if (cvalid) {
           T hv[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) hv[v] = from_f32<T>(silu_f(acc[0][v]) * acc[1][v]);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(a.h) + (size_t)pos * a.d_out + o) =
+          *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(a.h) + (size_t)pos_e * a.d_out + o_e) =
               __builtin_bit_cast(u32x2, hv);
         }
       } else {
         if (cvalid) {
-          const float g = a.gates[slotid];
-          *reinterpret_cast<f32x4*>(a.dres + ((size_t)ks * a.S + pos) * a.d_out + o) = acc[0] * g;
+          const float g = a.gates[opaque(slotid)];
+          *reinterpret_cast<f32x4*>(a.dres + ((size_t)ks * a.S + pos_e) * a.d_out + o_e) = acc[0] * g;
         }
       }
     }
     // slot 0 holds the gathered Sigma p until every wave has used it
-    if constexpr (MODE == MODE_GATEUP) {
-      if (t0 + 16 < cnt) __syncthreads();
-    }
+    if (rowstage && t0 + 16 < cnt) __syncthreads();
   }
 }
 

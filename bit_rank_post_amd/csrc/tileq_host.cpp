@@ -631,11 +631,10 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       pa.Xp = at<void>(ws, p.xp);
       pa.sums = at<float>(ws, p.sums_x);
       pa.ex = at<int>(ws, p.ex_x);
-      // one launch; gate/up add the column-stage slabs themselves, the single
-      // projection's combine reads reduced rows
+      // one launch; the residual kernels add the column-stage slabs
+      // themselves
       launch_prep_col(&pa, T, ca, n, p.col_tiles_x, act, s);
       mark(2);
-      if (n && !swiglu) launch_colproj_reduce(ca, n, s);
     } else {
       if (bf) {
         ex = at<int>(ws, p.ex);
@@ -684,6 +683,11 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.gates = topk_w;
       da.nks = p.nks;
       da.S = p.S;
+      // row stage in the first k-chunk's workgroups
+      da.P[0] = L->proj[0].dev.r_pad ? at<float>(ws, p.P[0]) : nullptr;
+      da.ap_T = p.ap_T;
+      da.p_nsplit = p.nsplit[0];
+      da.p_rows_cap = p.rows_cap;
       da.waves = choose_waves(L, 0, p.S, p.nks, 1);
       launch_gemm_decode(da, MODE_RES, act, s);
     }
@@ -736,7 +740,6 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       pa.sums = at<float>(ws, p.sums_h);
       pa.ex = at<int>(ws, p.ex_h);
       launch_prep_col(&pa, p.S, &ca, ncd, p.col_tiles_down, act, s);
-      if (ncd) launch_colproj_reduce(&ca, 1, s);
     } else if (ncd) {
       launch_colproj(&ca, 1, p.rt_col, p.max_col_tiles, act, s);
     }
@@ -784,6 +787,11 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.gates = topk_w;
       da.nks = p.nks;
       da.S = p.S;
+      // row stage (P rows = slot positions) in the first k-chunk's workgroups
+      da.P[0] = dd.r_pad ? at<float>(ws, p.P[2]) : nullptr;
+      da.ap_T = 0;
+      da.p_nsplit = p.nsplit[2];
+      da.p_rows_cap = p.rows_cap;
       da.waves = choose_waves(L, 2, p.S, p.nks, 1);
       launch_gemm_decode(da, MODE_RES, act, s);
     } else {
@@ -827,7 +835,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     cb.K = K;
     cb.d_out = d.d_out;
     cb.M = d.M;
-    cb.r_pad = d.r_pad;
+    cb.r_pad = dec ? 0 : d.r_pad;     // decode: the residual kernel added the row stage
     cb.ids = topk_ids;
     cb.gates = topk_w;
     cb.inv = at<int>(ws, p.inv);
