@@ -1,8 +1,11 @@
 // Decode-path companion stages of the residual kernels, fused per dependency
-// level into one launch of 1024-thread workgroups:
-//   before gate/up:  activation preparation of x   + column stage of gate/up
-//   before down:     activation preparation of h   + column stage of down
-// (the two halves of a launch are independent of each other).
+// level into one launch of 256-thread workgroups:
+//   before gate/up:  routing (one workgroup, small batches), activation
+//                    preparation of x, column stage of gate/up
+//   before down:     activation preparation of h + column stage of down
+// (the parts of a launch do not read each other's results).  Many small
+// workgroups spread the few hundred KB each part reads over the CUs: one
+// CU's load path, not HBM, bounds a workgroup that reads a lot.
 //
 // Activation preparation.  The decode residual kernel feeds the 2-bit codes
 // to the MFMA without dequantizing them: each packed fp16 half holds 1 + q*c
@@ -16,38 +19,31 @@
 //
 // Column stage ("TileQ" technical summary, section 2.2: the batch is
 // projected onto a shared factor once): P[slab][row][:] = Sigma (V_n^T a_row)
-// over the slab's 1024 inputs, for the rows of a 16-row tile.  A workgroup's
-// 16 waves are 4 rank-fragment groups x 4 k-groups; the k-groups meet in LDS.
-// Consumers add the slabs (deterministic, no atomics).
-#include "tq_device.h"
+// over the slab's 1024 inputs, for the rows of a 16-row tile.  A workgroup
+// takes one rank-fragment group of a (tile, slab); its 4 waves are k-groups
+// that meet in LDS.  Consumers add the slabs (deterministic, no atomics).
+#include "route_body.h"
 
 namespace tq {
 
-constexpr int DS_THREADS = 1024;
+constexpr int DS_THREADS = 256;
 constexpr int DS_SLAB_STEPS = 32;        // 32 k-steps = 1024 inputs per slab
 
-// 1/c of input k: step parity b = (k/32) % 2, pair v = (k % 8) / 2.
-__device__ __forceinline__ float class_inv(int k) {
-  const int b = (k >> 5) & 1, v = (k & 7) >> 1;
-  // b = 0: {64, 16, 4, 64};  b = 1: {64, 16, 4, 16}
-  return (v == 0) ? 64.f : (v == 1) ? 16.f : (v == 2) ? 4.f : (b ? 16.f : 64.f);
-}
-
-// Four rows per workgroup, 256 threads per row; thread t of a row owns the
-// 8-element chunks t + 256 i.  The row is read once (up to 8 chunks per
-// thread stay in registers; longer rows re-read the rest).
-template <typename T>
-__device__ void prep_rows(const PrepArgs& a, int rows, int blk, float* s_red /*[16]*/) {
+// One row per workgroup; thread t owns the 8-element chunks t + 256 i.  The
+// row is read once (up to 8 chunks per thread stay in registers; longer rows
+// re-read the rest).
+template <typename T, int CPG>
+__device__ void prep_row(const PrepArgs& a, int rows, int blk, float* s_red /*[4]*/) {
   typedef typename Vec8<T>::type V8;
   constexpr int KEEP = 8;
-  const int sub = threadIdx.x >> 8, tid = threadIdx.x & 255;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int row = blk * 4 + sub;
+  const int row = blk;
   int src = -1;
   if (row < rows) src = a.row_src ? a.row_src[row] : row;
-  const bool ok = src >= 0;
-  const T* xr = reinterpret_cast<const T*>(a.X) + (size_t)(ok ? src : 0) * a.d;
-  const int nch = ok ? (a.d >> 3) : 0;
+  if (src < 0) return;                   // uniform over the workgroup
+  const T* xr = reinterpret_cast<const T*>(a.X) + (size_t)src * a.d;
+  const int nch = a.d >> 3;
   V8 kept[KEEP];
   float m = 0.f;
 #pragma unroll
@@ -66,40 +62,41 @@ __device__ void prep_rows(const PrepArgs& a, int rows, int blk, float* s_red /*[
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if (lane == 0) s_red[sub * 4 + wv] = m;
+  if (lane == 0) s_red[wv] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(s_red[sub * 4], s_red[sub * 4 + 1]), fmaxf(s_red[sub * 4 + 2], s_red[sub * 4 + 3]));
-  if (!ok) return;                       // no barrier follows
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   int e2 = 0;
   if (m > 0.f) frexpf(m, &e2);
   const int E = (m > 0.f) ? e2 - 9 : 0;
   if (tid == 0) a.ex[row] = E;
-  // scaled, class-scaled copy and group sums; a group is G/8 consecutive
-  // chunks, i.e. G/8 consecutive threads of one wave (G <= 256)
-  const int cpg = a.G >> 3;
+  // scaled, class-scaled copy and group sums; a group is CPG = G/8
+  // consecutive chunks, i.e. CPG consecutive lanes of one wave (G <= 256)
   half_t* xo = reinterpret_cast<half_t*>(a.Xp) + (size_t)row * a.d;
   float* sums = a.sums + (size_t)row * (a.d / a.G) * 2;
   auto emit = [&](int c, const V8& v) {
     float st = 0.f, sp = 0.f;
     if (c < nch) {
+      // 1/c of input k = 8c + j: with step parity b = (k/32) % 2 = (c/4) % 2
+      // and pair v = (k % 8) / 2 = j / 2, 1/c = 64, 16, 4 for v = 0, 1, 2 and
+      // 16 (b = 1) or 64 (b = 0) for v = 3
+      const float inv3 = ((c >> 2) & 1) ? 16.f : 64.f;
       half8v o;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
+        const float inv = (j < 2) ? 64.f : (j < 4) ? 16.f : (j < 6) ? 4.f : inv3;
         const half_t xt = (half_t)ldexpf((float)v[j], -E);
-        const half_t xp = (half_t)((float)xt * class_inv(8 * c + j));
+        const half_t xp = (half_t)((float)xt * inv);
         o[j] = xp;
         st += (float)xt;
         sp += (float)xp;
       }
       *reinterpret_cast<half8v*>(xo + 8 * c) = o;
     }
-    for (int o2 = 1; o2 < cpg; o2 <<= 1) {
-      st += __shfl_xor(st, o2, 64);
-      sp += __shfl_xor(sp, o2, 64);
-    }
-    if (c < nch && (c % cpg) == 0) {
-      sums[2 * (c / cpg)] = st;
-      sums[2 * (c / cpg) + 1] = sp;
+    st = group_sum<CPG>(st);
+    sp = group_sum<CPG>(sp);
+    if (c < nch && (c % CPG) == 0) {
+      sums[2 * (c / CPG)] = st;
+      sums[2 * (c / CPG) + 1] = sp;
     }
   };
 #pragma unroll
@@ -113,19 +110,29 @@ __device__ void prep_rows(const PrepArgs& a, int rows, int blk, float* s_red /*[
   }
 }
 
-// Column stage for one (16-row tile, 1024-input slab).  Waves: rank-fragment
-// group fg = w & 3 (fragments fg, fg + 4 of r_pad / 16), k-group kg = w >> 2
-// (k-steps kg + 4 i of the slab).  All loads of a wave are issued before its
-// MFMAs; steps outside the slab and rows outside the tile read zeros through
-// out-of-range offsets.
 template <typename T>
-__device__ void col_tile(const ColArgs& a, int blk, int* s_res, float* s_red /*[4][16][128]*/) {
+__device__ void prep_rows(const PrepArgs& a, int rows, int blk, float* s_red) {
+  switch (a.G >> 3) {
+    case 4: prep_row<T, 4>(a, rows, blk, s_red); break;
+    case 8: prep_row<T, 8>(a, rows, blk, s_red); break;
+    case 16: prep_row<T, 16>(a, rows, blk, s_red); break;
+    default: prep_row<T, 32>(a, rows, blk, s_red); break;
+  }
+}
+
+// Column stage for one (16-row tile, 1024-input slab, rank-fragment group
+// fg: fragments fg and fg + 4 of r_pad / 16).  Wave w is k-group w (k-steps
+// w + 4 i of the slab).  All loads of a wave are issued before its MFMAs;
+// steps outside the slab, rows outside the tile and missing fragments read
+// zeros through out-of-range offsets.
+template <typename T>
+__device__ void col_tile(const ColArgs& a, int blk, int* s_res, float* s_red /*[4][16][32]*/) {
   typedef typename Vec8<T>::type V8;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int fg = w & 3, kg = w >> 2;
-  const int split = blk % a.nsplit;
-  const int tile = blk / a.nsplit;
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fg = blk & 3;
+  const int split = (blk >> 2) % a.nsplit;
+  const int tile = (blk >> 2) / a.nsplit;
   int seg, row0, row_end;
   if (a.ap_T > 0) {
     const int tpc = (a.ap_T + 15) >> 4;
@@ -175,24 +182,22 @@ __device__ void col_tile(const ColArgs& a, int blk, int* s_res, float* s_red /*[
     for (int q = 0; q < 2; ++q)
       if (fg + 4 * q < nfrag)
         acc[q] = mfma16(__builtin_bit_cast(V8, av[i]), __builtin_bit_cast(V8, bv[i][q]), acc[q]);
-  // k-groups meet in LDS: s_red[kg][row][rank]
+  // k-groups meet in LDS: s_red[kg][row][q][16]
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int f = fg + 4 * q;
-    if (f < nfrag) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        s_red[(kg * 16 + 4 * (lane >> 4) + v) * 128 + 16 * f + (lane & 15)] = acc[q][v];
-    }
+    for (int v = 0; v < 4; ++v)
+      s_red[(kg * 16 + 4 * (lane >> 4) + v) * 32 + 16 * q + (lane & 15)] = acc[q][v];
   }
   __syncthreads();
   float* P = a.P + (size_t)split * a.rows_cap * a.r_pad;
-  for (int i = tid; i < 16 * a.r_pad; i += DS_THREADS) {
-    const int r = i / a.r_pad, c = i - r * a.r_pad;
+  for (int i = tid; i < 16 * 32; i += DS_THREADS) {
+    const int r = i >> 5, qc = i & 31;
+    const int f = fg + 4 * (qc >> 4), c = 16 * f + (qc & 15);
     const int row = row0 + r;
-    if (row < row_end) {
-      const float v = s_red[r * 128 + c] + s_red[(16 + r) * 128 + c] +
-                      s_red[(32 + r) * 128 + c] + s_red[(48 + r) * 128 + c];
+    if (row < row_end && f < nfrag) {
+      const float v = s_red[r * 32 + qc] + s_red[(16 + r) * 32 + qc] +
+                      s_red[(32 + r) * 32 + qc] + s_red[(48 + r) * 32 + qc];
       P[(size_t)row * a.r_pad + c] = v * a.sigma[c];
     }
   }
@@ -203,13 +208,26 @@ struct PrepColArgs {
   int prep_rows, prep_blocks;
   ColArgs col[2];
   int ncol, col_blocks;          // column-stage blocks per projection (tiles x slabs)
+  int route;                     // 1: workgroup 0 runs the routing (independent of the rest)
+  RouteArgs ra;
 };
+
+constexpr int DS_ROUTE_SMAX = 1024;
+constexpr int DS_LDS_FLOATS = 5680;      // >= routing scratch, 4 x 16 x 32 reduction, 4 maxima
 
 template <typename T>
 __global__ __launch_bounds__(DS_THREADS) void prep_col_kernel(PrepColArgs a) {
-  __shared__ float s_red[4 * 16 * 128];
+  __shared__ float s_red[DS_LDS_FLOATS];
   __shared__ int s_res;
-  const int b = blockIdx.x;
+  static_assert(route_lds_ints(DS_ROUTE_SMAX) <= DS_LDS_FLOATS && 4 * 16 * 32 <= DS_LDS_FLOATS, "LDS");
+  int b = blockIdx.x;
+  if (a.route) {
+    if (b == 0) {
+      route_block<DS_ROUTE_SMAX, DS_THREADS>(a.ra, reinterpret_cast<int*>(s_red));
+      return;
+    }
+    --b;
+  }
   if (b < a.prep_blocks) {
     prep_rows<T>(a.prep, a.prep_rows, b, s_red);
   } else {
@@ -221,18 +239,26 @@ __global__ __launch_bounds__(DS_THREADS) void prep_col_kernel(PrepColArgs a) {
 
 int decode_col_splits(int d_in) { return ((d_in >> 5) + DS_SLAB_STEPS - 1) / DS_SLAB_STEPS; }
 
+bool prep_col_can_route(const RouteArgs& ra) {
+  return ra.S <= DS_ROUTE_SMAX && ra.T <= DS_ROUTE_SMAX && ((ra.S + 63) / 64) * ra.K <= DS_ROUTE_SMAX;
+}
+
 void launch_prep_col(const PrepArgs* prep, int prep_rows, const ColArgs* col, int ncol,
-                     int col_tiles, Act act, hipStream_t s) {
+                     int col_tiles, const RouteArgs* route, Act act, hipStream_t s) {
   PrepColArgs a{};
+  if (route) {
+    a.route = 1;
+    a.ra = *route;
+  }
   if (prep) {
     a.prep = *prep;
     a.prep_rows = prep_rows;
-    a.prep_blocks = (prep_rows + 3) / 4;
+    a.prep_blocks = prep_rows;
   }
   a.ncol = ncol;
   for (int z = 0; z < ncol; ++z) a.col[z] = col[z];
-  a.col_blocks = ncol ? col_tiles * col[0].nsplit : 0;
-  const int blocks = a.prep_blocks + ncol * a.col_blocks;
+  a.col_blocks = ncol ? col_tiles * col[0].nsplit * 4 : 0;   // x 4 rank-fragment groups
+  const int blocks = a.route + a.prep_blocks + ncol * a.col_blocks;
   if (blocks == 0) return;
   if (act == ACT_F16)
     hipLaunchKernelGGL(prep_col_kernel<half_t>, dim3(blocks), dim3(DS_THREADS), 0, s, a);

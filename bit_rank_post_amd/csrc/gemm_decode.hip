@@ -105,7 +105,10 @@ void gemm_dec_kernel(DecArgs a) {
   // experts are active), and consecutive workgroups of one XCD take different
   // experts.
   const int nrb = a.d_out >> 4;
-  const int nby = (nrb + WAVES - 1) / WAVES;
+  // a.rows_per (<= WAVES) waves of a workgroup own row fragments; the others
+  // only help with the shared loads
+  const int rpw = a.rows_per;
+  const int nby = (nrb + rpw - 1) / rpw;
   const int nby8 = (nby + 7) >> 3;
   const int wg = blockIdx.x, q = wg >> 3;
   const int e = q % a.K;
@@ -116,8 +119,8 @@ void gemm_dec_kernel(DecArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int rb_raw = by * WAVES + wave;
-  const bool rvalid = rb_raw < nrb;
+  const int rb_raw = by * rpw + wave;
+  const bool rvalid = wave < rpw && rb_raw < nrb;
   const int rb = rvalid ? rb_raw : nrb - 1;          // clamped: loads stay in bounds
   const int nsteps = a.d_in >> 5;
   const int nfull = nsteps >> 3;
@@ -157,8 +160,8 @@ void gemm_dec_kernel(DecArgs a) {
     sz_lds[k] = ok ? SL::SZ + i * 256 : -1;
     const int w = (ok ? i - sz_p[k] * SL::NSZP : 0) * 64 + lane;
     const int wv = w / (16 * NG), g = (w / 16) % NG, row = w & 15;
-    const int rbw = min(by * WAVES + wv, nrb - 1);
-    sz_vo[k] = (ok && wv < WAVES) ? (((uint32_t)rbw * ng + g) * 16u + row) * 4u : OOB;
+    const int rbw = min(by * rpw + wv, nrb - 1);
+    sz_vo[k] = (ok && wv < rpw) ? (((uint32_t)rbw * ng + g) * 16u + row) * 4u : OOB;
   }
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.Xp, (uint32_t)a.rows * a.d_in * 2u);
   const __amdgpu_buffer_rsrc_t rsm = make_rsrc(a.sums, (uint32_t)a.rows * ng * 8u);
@@ -172,7 +175,7 @@ void gemm_dec_kernel(DecArgs a) {
     const int st = live ? k0 + tr : 0;
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      dma16(rc[p], base + SL::CODE + (wave * NP + p) * 1024, live ? lane * 16u : OOB, st * 1024u);
+      dma16(rc[p], base + SL::CODE + (wave * NP + p) * 1024, (live && rvalid) ? lane * 16u : OOB, st * 1024u);
 #pragma unroll
     for (int k = 0; k < SL::NSZW; ++k)
       dma4(sz_p[k] == 0 ? rs[0] : rs[NP - 1], sz_lds[k] >= 0 ? base + sz_lds[k] : s_dummy,
@@ -203,32 +206,39 @@ void gemm_dec_kernel(DecArgs a) {
     for (int b = 0; b < DEPTH; ++b) issue_w(b, slot[b]);
   }
 
-  // routing reads, none waiting for another: the expert's slot count and
-  // offset, and the slot ids of its first 16 positions (entries past the
-  // count are stale and never used)
+  // routing reads, none waiting for another and all scalar (they do not
+  // queue behind the code loads above): the expert's slot count and offset,
+  // the slot ids of its first 16 positions (entries past the count are stale
+  // and never used; the table has 16 entries of padding) and its tile row /
+  // column (row stage)
   const int* etab = a.etab + (size_t)e * a.S;
-  const int cnt = a.cnt[e];
-  const int offe = a.off[e];
-  const int sl_first = etab[min(l16, a.S - 1)];
-  // tile row / column of the expert (row stage of MODE_GATEUP)
+  const int cnt = sload(a.cnt, e);
+  const int offe = sload(a.off, e);
+  const int sl_first = sload16(etab, 0, l16);
   int m_e[NP], n_e[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const bool lr = a.P[p] != nullptr && a.p[p].rank > 0;
-    m_e[p] = lr ? a.p[p].m_of[e] : 0;
-    n_e[p] = lr ? a.p[p].n_of[e] : 0;
+    m_e[p] = lr ? sload(a.p[p].m_of, e) : 0;
+    n_e[p] = lr ? sload(a.p[p].n_of, e) : 0;
   }
   if (cnt == 0) {
     wait_vm<0>();                          // no load may land after the workgroup ends
     return;
   }
 
-  for (int t0 = 0; t0 < cnt; t0 += 16) {
+  // One column tile (16 slot positions from t0).  The first tile is a
+  // straight-line copy ahead of the loop over further tiles: reached from a
+  // loop header, the compiler's waits would count loads of an earlier tile
+  // and stall on the code loads in flight.
+  auto tile = [&](const int t0) __attribute__((always_inline)) {
     const int ncol = min(16, cnt - t0);
     const bool cvalid = l16 < ncol;
     const int pos = offe + t0 + (cvalid ? l16 : 0);
-    int slotid = (t0 == 0) ? sl_first : etab[min(t0 + l16, a.S - 1)];
-    slotid = cvalid ? slotid : __shfl(slotid, 0, 64);    // column 0 always holds a slot
+    // (no cross-lane reads here: an LDS-pipe instruction would make the
+    // compiler wait for the code loads above to land)
+    int slotid = (t0 == 0) ? sl_first : sload16(etab, t0, l16);
+    slotid = cvalid ? slotid : sload(etab, t0);          // column 0 always holds a slot
     const int arow = a.gather ? slotid / a.topk : pos;
     const int E = a.ex[arow];              // row exponent, used by the epilogue
 
@@ -241,7 +251,7 @@ void gemm_dec_kernel(DecArgs a) {
     {
       const int w = 64 * wave + lane;
       const int gi = w >> 5, col = (w >> 1) & 15, comp = w & 1;
-      const int r = a.gather ? __shfl(slotid, col, 64) / a.topk : offe + t0 + col;
+      const int r = a.gather ? sload16(etab, t0, col) / a.topk : offe + t0 + col;
       if (wave < SL::NSUM && gi < NG && col < ncol) sum_vo = (((uint32_t)r * ng + gi) * 2u + comp) * 4u;
     }
     auto issue = [&](int b, char* base) {
@@ -323,9 +333,10 @@ void gemm_dec_kernel(DecArgs a) {
 
     // full stages.  Ring: batch b lands in slot b % NSLOT; at stage-time tau
     // the wave waits for batch tau (DEPTH - 1 newer batches may stay in
-    // flight), the barrier makes every wave's part visible, the stage is
-    // computed, then batch tau + DEPTH is issued into the slot of tau - 1,
-    // which every wave finished before this barrier.  Slots are distinct LDS
+    // flight) and for its own LDS reads, the barrier makes every wave's part
+    // visible and every wave's reads of stage tau - 1 complete, batch
+    // tau + DEPTH is issued into the slot of tau - 1, and the stage is
+    // computed while DEPTH batches are in flight.  Slots are distinct LDS
     // arrays indexed by constants: the ring is unrolled by its length and
     // whole rounds always run (stage-times past the end only wait and issue
     // empty loads), so the loop has a single back edge and the compiler's
@@ -348,26 +359,30 @@ void gemm_dec_kernel(DecArgs a) {
           // DEPTH - 1 newer batches
           if (t == 0 && u < DEPTH - 1) wait_vm_first<SL::NI, DEPTH - 1>(u);
           else wait_vm<SL::NI * (DEPTH - 1)>();
+          wait_lgkm0();          // this wave's reads of the slot refilled below are done
           bar_nofence();
-          if (tau < ntau) compute(slot[u]);
           issue(tau + DEPTH, slot[(u + DEPTH) % NSLOT]);
+          if (tau < ntau && rvalid) compute(slot[u]);
         }
       }
       // every load has landed and every wave is done with the ring before
-      // the next tile reuses it
+      // the next tile (or the row stage) reuses it
       wait_vm<0>();
+      wait_lgkm0();
       bar_nofence();
     }
 
     // 4-step tail stage (d_in % 256 == 128; then GS <= 4): direct loads
-    if (tail) {
+    if (tail && rvalid) {
+      // addresses from opaque copies: computed here, not held across the ring
       const int st = nfull;
-      const half_t* xrow = reinterpret_cast<const half_t*>(a.Xp) + (size_t)arow * a.d_in + 8 * lg;
-      const float* srow = a.sums + (size_t)arow * ng * 2;
+      const int lane_t = opaque(lane), lg_t = lane_t >> 4, arow_t = opaque(arow);
+      const half_t* xrow = reinterpret_cast<const half_t*>(a.Xp) + (size_t)arow_t * a.d_in + 8 * lg_t;
+      const float* srow = a.sums + (size_t)arow_t * ng * 2;
       u32x2 cd[NP];
 #pragma unroll
       for (int p = 0; p < NP; ++p)
-        cd[p] = *reinterpret_cast<const u32x2*>(cbase[p] + st * 256 + lane * 2);
+        cd[p] = *reinterpret_cast<const u32x2*>(cbase[p] + st * 256 + lane_t * 2);
       half8v bt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bt[j] = *reinterpret_cast<const half8v*>(xrow + (8 * st + j) * 32);
@@ -391,7 +406,7 @@ void gemm_dec_kernel(DecArgs a) {
             const float Xt = srow[2 * g], Xq = srow[2 * g + 1];
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-              const u32x4 w = *reinterpret_cast<const u32x4*>(szb[p] + (size_t)g * 16 + 4 * lg);
+              const u32x4 w = *reinterpret_cast<const u32x4*>(szb[p] + (size_t)g * 16 + 4 * lg_t);
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
                 const float sc = (float)__builtin_bit_cast(half_t, (uint16_t)(w[v] & 0xFFFFu));
@@ -534,7 +549,9 @@ void gemm_dec_kernel(DecArgs a) {
     }
     // slot 0 holds the gathered Sigma p until every wave has used it
     if (rowstage && t0 + 16 < cnt) __syncthreads();
-  }
+  };
+  tile(0);
+  for (int t0 = 16; t0 < cnt; t0 += 16) tile(t0);
 }
 
 template <typename T, int MODE, int GS, int WAVES, int DMAX>
@@ -545,10 +562,12 @@ static void dec_launch(const DecArgs& a, hipStream_t s) {
     // slots too large for a ring of three: fall back to 8 waves
     dec_launch<T, MODE, GS, 8, DMAX>(a, s);
   } else {
-    const int nrb = a.d_out >> 4;
-    const int nby = (nrb + WAVES - 1) / WAVES;
-    const dim3 grid(a.K * ((nby + 7) / 8) * 8 * a.nks);
-    hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, GS, WAVES, DMAX>), grid, dim3(64 * WAVES), 0, s, a);
+    DecArgs b = a;
+    b.rows_per = (a.rows_per >= 1 && a.rows_per <= WAVES) ? a.rows_per : WAVES;
+    const int nrb = b.d_out >> 4;
+    const int nby = (nrb + b.rows_per - 1) / b.rows_per;
+    const dim3 grid(b.K * ((nby + 7) / 8) * 8 * b.nks);
+    hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, GS, WAVES, DMAX>), grid, dim3(64 * WAVES), 0, s, b);
   }
 }
 

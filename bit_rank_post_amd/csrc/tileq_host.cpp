@@ -163,16 +163,18 @@ int device_cus() {
   return cus[dev];
 }
 
-// Waves (16-row fragments) per decode workgroup.  The grid runs in
-// ceil(wgs / (CUs x workgroups per CU)) rounds and a round lasts about as
-// long as one workgroup streams its rows.  Cost of a choice = rounds x (bytes
-// of one stage of the workgroup, in KB: W x NP KB of codes + 8 KB of
-// activations, plus a fixed per-workgroup cost of about 12 KB-equivalents per
-// stage for ring fill, routing reads and epilogue).  8-wave workgroups run
-// two per CU when their ring fits half the LDS; then the fixed cost of one is
-// hidden behind the other's streaming.  The input projections may use 8, 12,
-// 14 or 16 waves; single-projection launches 8 or 16.
-int choose_waves(const tq_layer* L, int q, int S, int nks, int np) {
+// Waves per decode workgroup and how many of them own a 16-row fragment.
+// The grid runs in ceil(wgs / (CUs x workgroups per CU)) rounds and a round
+// lasts about as long as one workgroup streams its rows.  Cost of a choice =
+// rounds x (bytes of one stage of the workgroup, in KB: rows x NP KB of codes
+// + 8 KB of activations, plus a fixed per-workgroup cost of about 12
+// KB-equivalents per stage for ring fill, routing reads and epilogue).
+// 8-wave workgroups run two per CU when their ring fits half the LDS; then
+// the fixed cost of one is hidden behind the other's streaming, and leaving
+// one wave without rows can make the rounds come out even.  The input
+// projections may use 8, 12, 14 or 16 waves; single-projection launches 8 or
+// 16.
+void choose_waves(const tq_layer* L, int q, int S, int nks, int np, int* waves, int* rows_per) {
   const long active = std::min<long>(L->K, S);
   const int nrb = L->proj[q].dev.nrb;
   const long cus = device_cus();
@@ -181,20 +183,23 @@ int choose_waves(const tq_layer* L, int q, int S, int nks, int np) {
   static const int cand1[] = {16, 8};
   const int* cand = (np == 2) ? cand2 : cand1;
   const int nc = (np == 2) ? 4 : 2;
-  int best = 16;
+  *waves = 16;
+  *rows_per = 16;
   long best_cost = -1;
   for (int i = 0; i < nc; ++i) {
     const int w = cand[i];
-    const long per_cu = (w <= 8 && dual) ? 2 : 1;
-    const long wgs = active * ((nrb + w - 1) / w) * nks;
-    const long rounds = (wgs + cus * per_cu - 1) / (cus * per_cu);
-    const long cost = rounds * (w * np + 8 + (per_cu == 2 ? 0 : 12));
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best = w;
+    const long per_cu = (w == 8 && dual) ? 2 : 1;
+    for (int r = w; r >= (per_cu == 2 ? w - 1 : w); --r) {
+      const long wgs = active * ((nrb + r - 1) / r) * nks;
+      const long rounds = (wgs + cus * per_cu - 1) / (cus * per_cu);
+      const long cost = rounds * (r * np + 8 + (per_cu == 2 ? 0 : 12));
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        *waves = w;
+        *rows_per = r;
+      }
     }
   }
-  return best;
 }
 
 Plan make_plan(const tq_layer* L, int T, int k, int path) {
@@ -230,7 +235,7 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.off = take(sizeof(int) * (K + 1));
   p.perm = take(sizeof(int) * S);
   p.inv = take(sizeof(int) * S);
-  p.etab = take(sizeof(int) * (size_t)K * S);
+  p.etab = take(sizeof(int) * ((size_t)K * S + 16));   // + 16: whole 16-entry reads
   p.tile_gemm = take(sizeof(int) * (K + 1));
   p.tile_colx = take(sizeof(int) * (K + 1));
   p.colmask = take(sizeof(int) * std::max(T, 1));
@@ -611,7 +616,10 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   RouteArgs ra;
   fill_route(L, p, topk_ids, ws, ra);
   if (p.ap_T > 0) ra.ncol = 0;     // decode: no column lists (every pair is computed)
-  launch_route(ra, s);
+  // decode with a small batch: the routing runs as one workgroup of the
+  // activation-preparation / column-stage launch (neither reads the other)
+  const bool fuse_route = dec && prep_col_can_route(ra);
+  if (!fuse_route) launch_route(ra, s);
   mark(1);
   // activation preparation (decode: class-scaled fp16 copy + group sums;
   // prefill bf16: exact fp16 copy) and (a2) the column stage of the
@@ -633,7 +641,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       pa.ex = at<int>(ws, p.ex_x);
       // one launch; the residual kernels add the column-stage slabs
       // themselves
-      launch_prep_col(&pa, T, ca, n, p.col_tiles_x, act, s);
+      launch_prep_col(&pa, T, ca, n, p.col_tiles_x, fuse_route ? &ra : nullptr, act, s);
       mark(2);
     } else {
       if (bf) {
@@ -676,7 +684,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.ap_T = p.ap_T;
       da.p_nsplit = p.nsplit[0];
       da.p_rows_cap = p.rows_cap;
-      da.waves = choose_waves(L, 0, p.S, 1, 2);
+      choose_waves(L, 0, p.S, 1, 2, &da.waves, &da.rows_per);
       launch_gemm_decode(da, MODE_GATEUP, act, s);
     } else {
       da.dres = dres;
@@ -688,7 +696,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.ap_T = p.ap_T;
       da.p_nsplit = p.nsplit[0];
       da.p_rows_cap = p.rows_cap;
-      da.waves = choose_waves(L, 0, p.S, p.nks, 1);
+      choose_waves(L, 0, p.S, p.nks, 1, &da.waves, &da.rows_per);
       launch_gemm_decode(da, MODE_RES, act, s);
     }
   } else {
@@ -739,7 +747,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       pa.Xp = at<void>(ws, p.hp);
       pa.sums = at<float>(ws, p.sums_h);
       pa.ex = at<int>(ws, p.ex_h);
-      launch_prep_col(&pa, p.S, &ca, ncd, p.col_tiles_down, act, s);
+      launch_prep_col(&pa, p.S, &ca, ncd, p.col_tiles_down, nullptr, act, s);
     } else if (ncd) {
       launch_colproj(&ca, 1, p.rt_col, p.max_col_tiles, act, s);
     }
@@ -792,7 +800,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.ap_T = 0;
       da.p_nsplit = p.nsplit[2];
       da.p_rows_cap = p.rows_cap;
-      da.waves = choose_waves(L, 2, p.S, p.nks, 1);
+      choose_waves(L, 2, p.S, p.nks, 1, &da.waves, &da.rows_per);
       launch_gemm_decode(da, MODE_RES, act, s);
     } else {
       GemmArgs ga{};

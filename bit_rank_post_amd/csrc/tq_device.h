@@ -98,6 +98,9 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+// wait until every LDS / scalar-memory operation of this wave has completed
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // wait_vm<u * NI>() for u in [0, UMAX); u must fold to a constant (an
 // unrolled loop index)
 template <int NI, int UMAX, int U = 0>
@@ -105,6 +108,26 @@ __device__ __forceinline__ void wait_vm_first(int u) {
   if constexpr (U < UMAX) {
     if (u == U) wait_vm<U * NI>();
     else wait_vm_first<NI, UMAX, U + 1>(u);
+  }
+}
+
+// Reads of data that no workgroup of the running kernel writes, at
+// wave-uniform addresses: through the constant address space they become
+// scalar loads, counted apart from the vector-memory loads in flight.
+typedef __attribute__((address_space(4))) const int cint_t;
+__device__ __forceinline__ int sload(const int* p, int i) {
+  return ((cint_t*)p)[i];
+}
+
+// Lane l of a wave gets p[i0 + l % 16]: 16 wave-uniform scalar loads and a
+// select chain (no array, so nothing goes through private memory).
+template <int I = 0>
+__device__ __forceinline__ int sload16(const int* p, int i0, int l16, int r = 0) {
+  if constexpr (I == 16) {
+    return r;
+  } else {
+    const int v = sload(p, i0 + I);
+    return sload16<I + 1>(p, i0, l16, (l16 == I) ? v : r);
   }
 }
 
@@ -212,6 +235,24 @@ __device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
     int t = __shfl_up(v, o, 64);
     if (lane >= o) v += t;
   }
+  return v;
+}
+
+// Sum over aligned groups of G lanes (G = 1, 2, 4, 8, 16 or 32): DPP moves
+// inside 16-lane rows (xor 1, xor 2, half-row mirror, row mirror), one
+// shuffle across rows for 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32, "group size");
+  if constexpr (G >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+  if constexpr (G >= 16) v += dpp_f<0x140>(v);  // row_mirror
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
   return v;
 }
 

@@ -146,7 +146,8 @@ struct DecArgs {
   const float* gates;
   int nks;                       // k-chunks (RES; 1 for GATEUP)
   int S;                         // slots (slab stride of dres)
-  int waves;                     // waves per workgroup (16 rows each): 8, 12, 14 or 16 (GATEUP), 8 or 16
+  int waves;                     // waves per workgroup: 8, 12, 14 or 16 (GATEUP), 8 or 16
+  int rows_per;                  // waves that own a 16-row fragment (<= waves)
   int ap_T;                      // GATEUP: P rows are (column, token) pairs n * ap_T + t
   int p_nsplit, p_rows_cap;      // GATEUP: P slabs to add, rows per slab
   int spec;                      // 1: request the first stages' codes before the routing reads return
@@ -169,7 +170,9 @@ struct PrepArgs {
 // `ncol` projections (col_tiles 16-row tiles x slabs of 1024 inputs) in one
 // launch; prep may be nullptr
 void launch_prep_col(const PrepArgs* prep, int prep_rows, const ColArgs* col, int ncol,
-                     int col_tiles, Act act, hipStream_t s);
+                     int col_tiles, const RouteArgs* route, Act act, hipStream_t s);
+// true when the decode companion launch can also run the routing (small batch)
+bool prep_col_can_route(const RouteArgs& ra);
 int decode_col_splits(int d_in);
 
 // ---- combine: y_t = sum_j dres[inv(t,j)] + U_cat S_t (+ shared) ------------
