@@ -266,49 +266,45 @@ void gemm_dec_kernel(DecArgs a) {
       corr[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // acc += s_g * C_g for the wave's rows 4 lg + v
-    auto fold = [&](const f32x4 (&C)[NP], const char* base, int gi) {
+    // One stage: every LDS read first (the codes, the 8 activation k-steps,
+    // the scale/zero words and the group sums), then the arithmetic, so the
+    // reads overlap instead of each waiting for the one before.
+    //   acc  += s_g * C_g                 for the wave's rows 4 lg + v
+    //   corr += A . B   with A[row][t] = s_t (t < NG) or s z of group t - NG
+    //                   and B[t][col] = X'_t resp. X~_(t - NG); MFMA m of the
+    //                   fp32 product covers terms t = 4 m + lg
+    auto compute = [&](const char* base) {
+      u32x4 code[NP];
+      half8v bv[8];
+      u32x4 szw[NP][NG];
+      float cbx[NCORR];
+      uint32_t cw[NP][NCORR];
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(
-            base + SL::SZ + (p * SL::NSZP * 64 + (wave * NG + gi) * 16 + 4 * lg) * 4);
+      for (int p = 0; p < NP; ++p)
+        code[p] = *reinterpret_cast<const u32x4*>(base + SL::CODE + ((wave * NP + p) * 64 + lane) * 16);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          acc[p][v] += (float)__builtin_bit_cast(half_t, (uint16_t)(w[v] & 0xFFFFu)) * C[p][v];
-      }
-    };
-
-    // corr += A . B with A[row][t] = s_t (t < NG) or s z of group t - NG, and
-    // B[t][col] = X'_t resp. X~_(t - NG): MFMA m covers terms t = 4 m + lg
-    auto correction = [&](const char* base) {
+      for (int j = 0; j < 8; ++j)
+        bv[j] = *reinterpret_cast<const half8v*>(base + SL::ACT + lane * 16 + j * 1024);
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+          szw[p][gi] = *reinterpret_cast<const u32x4*>(
+              base + SL::SZ + (p * SL::NSZP * 64 + (wave * NG + gi) * 16 + 4 * lg) * 4);
 #pragma unroll
       for (int m = 0; m < NCORR; ++m) {
         const int t = 4 * m + lg;
         const int g = (t < NG) ? t : t - NG;
-        float bx = 0.f;
+        cbx[m] = 0.f;
         if (t < 2 * NG)
-          bx = *reinterpret_cast<const float*>(base + SL::SUM + ((g * 16 + l16) * 2 + (t < NG)) * 4);
+          cbx[m] = *reinterpret_cast<const float*>(base + SL::SUM + ((g * 16 + l16) * 2 + (t < NG)) * 4);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          float av = 0.f;
-          if (t < 2 * NG) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(
-                base + SL::SZ + (p * SL::NSZP * 64 + (wave * NG + g) * 16 + l16) * 4);
-            const float sc = (float)__builtin_bit_cast(half_t, (uint16_t)(w & 0xFFFFu));
-            const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(w >> 16));
-            av = (t < NG) ? sc : sc * z;
-          }
-          corr[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bx, corr[p], 0, 0, 0);
-        }
+        for (int p = 0; p < NP; ++p)
+          cw[p][m] = (t < 2 * NG) ? *reinterpret_cast<const uint32_t*>(
+                                        base + SL::SZ + (p * SL::NSZP * 64 + (wave * NG + g) * 16 + l16) * 4)
+                                  : 0u;
       }
-    };
 
-    auto compute = [&](const char* base) {
-      u32x4 code[NP];
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-        code[p] = *reinterpret_cast<const u32x4*>(base + SL::CODE + ((wave * NP + p) * 64 + lane) * 16);
-      const char* ab = base + SL::ACT + lane * 16;
       f32x4 C[NP];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -318,17 +314,33 @@ void gemm_dec_kernel(DecArgs a) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const int j = 2 * d + b;
-          const half8v bv = *reinterpret_cast<const half8v*>(ab + j * 1024);
           if (j % GS == 0) {
 #pragma unroll
             for (int p = 0; p < NP; ++p) C[p] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
 #pragma unroll
-          for (int p = 0; p < NP; ++p) C[p] = mfma16(as_half8(fr[p][b]), bv, C[p]);
-          if (j % GS == GS - 1) fold(C, base, j / GS);
+          for (int p = 0; p < NP; ++p) C[p] = mfma16(as_half8(fr[p][b]), bv[j], C[p]);
+          if (j % GS == GS - 1) {
+            const int gi = j / GS;
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                acc[p][v] += (float)__builtin_bit_cast(half_t, (uint16_t)(szw[p][gi][v] & 0xFFFFu)) * C[p][v];
+          }
         }
       }
-      correction(base);
+#pragma unroll
+      for (int m = 0; m < NCORR; ++m) {
+        const int t = 4 * m + lg;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const float sc = (float)__builtin_bit_cast(half_t, (uint16_t)(cw[p][m] & 0xFFFFu));
+          const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(cw[p][m] >> 16));
+          const float av = (t < 2 * NG) ? ((t < NG) ? sc : sc * z) : 0.f;
+          corr[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, cbx[m], corr[p], 0, 0, 0);
+        }
+      }
     };
 
     // full stages.  Ring: batch b lands in slot b % NSLOT; at stage-time tau
