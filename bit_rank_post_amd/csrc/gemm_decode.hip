@@ -4,20 +4,21 @@
 // "TileQ" technical summary, section 4 (Inference Latency, Decode): decode is
 // memory bound; the layout is contiguous and read with wide vector accesses.
 //
-// Work: a workgroup of WAVES waves owns WAVES row fragments (16 rows each) of
-// one expert -- in MODE_GATEUP the gate and the up rows together -- and walks
-// a range of k-stages (8 MFMA k-steps = 256 inputs each).  Everything a stage
+// Work: a workgroup of WAVES waves, rows_per of which own a row fragment (16
+// rows each) of one expert -- in MODE_GATEUP the gate and the up rows
+// together -- walks a range of k-stages (8 MFMA k-steps = 256 inputs each).  Everything a stage
 // needs (each wave's codes, the stage's activations shared by all waves, the
 // scale/zero words and the activation group sums) is brought straight into
 // LDS by buffer loads with the LDS destination (no registers in between), in
 // a ring of DEPTH + 1 slots: DEPTH stages are in flight while one is
-// computed.  Each wave waits for its own loads with an explicit vmcnt (loads
+// computed.  Two 8-wave workgroups share a CU when their ring fits half the
+// LDS.  Each wave waits for its own loads with an explicit vmcnt (loads
 // complete in issue order) before the stage's barrier; the barrier carries
 // no memory fence, which would wait for every load in flight.
 //
 // The codes enter v_mfma_f32_16x16x32_f16 as the raw packed values 1 + q*c
 // (one and-or per pair, no dequantization) against the class-scaled
-// activations x' = x~/c from act_prep.hip, so a group's fp32 partial is
+// activations x' = x~/c (decode_stages.hip), so a group's fp32 partial is
 // C_g = X'_g + sum q x~ and the residual output of a row is
 //     sum_g s_g (C_g - X'_g - z_g X~_g)
 //   = sum_g s_g C_g  -  sum_g (s_g X'_g + s_g z_g X~_g).
@@ -25,9 +26,10 @@
 // (rows x 2 NG) . (2 NG x columns) per stage, done by v_mfma_f32_16x16x4_f32
 // into a separate accumulator.
 // Epilogue: undo the row scaling 2^E, add the low-rank row stage U_m Sigma p
-// as MFMA K-steps (MODE_GATEUP; p from the column stage), then SwiGLU into h,
-// or (MODE_RES) the slot's routing weight into the fp32 per-slot buffer of
-// the workgroup's k-range (split-K slabs, summed by the combine kernel).
+// as MFMA K-steps (MODE_GATEUP; in MODE_RES by the first k-chunk when P is
+// given; p from the column stage), then SwiGLU into h, or (MODE_RES) the
+// slot's routing weight into the fp32 per-slot buffer of the workgroup's
+// k-range (split-K slabs, summed by the combine kernel).
 #include "tq_device.h"
 
 namespace tq {
