@@ -102,24 +102,43 @@ void gemm_dec_kernel(DecArgs a) {
   char* const slot[8] = {s0, s1, s2, s3, s4, s5, s6, s7};
 
   // Workgroup -> (expert, row-fragment group, k-chunk).  Consecutive
-  // workgroups go to the 8 XCDs in turn; the mapping gives every XCD an equal
-  // share of every expert's rows (all XCDs stream even when one or two
-  // experts are active), and consecutive workgroups of one XCD take different
-  // experts.
+  // workgroups go to the 8 XCDs in turn.  With every expert expected to be
+  // routed to (a.spec), consecutive workgroups of one XCD take different
+  // experts and every XCD gets an equal share of every expert's rows.  Else
+  // (compact mapping, a.arec) the workgroups of active expert i come i-th:
+  // the routing's record says which expert that is, and the workgroups past
+  // the active ones end at once instead of being interleaved with the work.
   const int nrb = a.d_out >> 4;
   // a.rows_per (<= WAVES) waves of a workgroup own row fragments; the others
   // only help with the shared loads
   const int rpw = a.rows_per;
   const int nby = (nrb + rpw - 1) / rpw;
   const int nby8 = (nby + 7) >> 3;
-  const int wg = blockIdx.x, q = wg >> 3;
-  const int e = q % a.K;
-  const int jq = q / a.K;
-  const int ks = jq / nby8;
-  const int by = (jq - ks * nby8) * 8 + (wg & 7);
-  if (by >= nby) return;
+  const int wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
+  int e, ks, by, q, cnt = 0, offe = 0;
+  const int* rec = nullptr;
+  if (a.arec) {
+    const int ue = nby8 * 8 * a.nks;               // workgroups per expert
+    const int ei = wg / ue, rem = wg - ei * ue;
+    rec = a.arec + ei * ROUTE_AREC;
+    const int na = sload(a.arec, a.K * ROUTE_AREC);
+    e = sload(rec, 0);
+    cnt = sload(rec, 1);
+    offe = sload(rec, 2);
+    ks = rem / (nby8 * 8);
+    by = rem - ks * nby8 * 8;
+    q = rem >> 3;
+    if (ei >= na || by >= nby) return;
+  } else {
+    q = wg >> 3;
+    e = q % a.K;
+    const int jq = q / a.K;
+    ks = jq / nby8;
+    by = (jq - ks * nby8) * 8 + (wg & 7);
+    if (by >= nby) return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int rb_raw = by * rpw + wave;
   const bool rvalid = wave < rpw && rb_raw < nrb;
@@ -214,9 +233,11 @@ void gemm_dec_kernel(DecArgs a) {
   // and never used; the table has 16 entries of padding) and its tile row /
   // column (row stage)
   const int* etab = a.etab + (size_t)e * a.S;
-  const int cnt = sload(a.cnt, e);
-  const int offe = sload(a.off, e);
-  const int sl_first = sload16(etab, 0, l16);
+  if (!rec) {
+    cnt = sload(a.cnt, e);
+    offe = sload(a.off, e);
+  }
+  const int sl_first = rec ? sload16(rec + 4, 0, l16) : sload16(etab, 0, l16);
   int m_e[NP], n_e[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -239,8 +260,9 @@ void gemm_dec_kernel(DecArgs a) {
     const int pos = offe + t0 + (cvalid ? l16 : 0);
     // (no cross-lane reads here: an LDS-pipe instruction would make the
     // compiler wait for the code loads above to land)
-    int slotid = (t0 == 0) ? sl_first : sload16(etab, t0, l16);
-    slotid = cvalid ? slotid : sload(etab, t0);          // column 0 always holds a slot
+    const int* slp = (rec && t0 == 0) ? rec + 4 : etab + t0;   // slot ids from position t0
+    int slotid = (t0 == 0) ? sl_first : sload16(slp, 0, l16);
+    slotid = cvalid ? slotid : sload(slp, 0);            // column 0 always holds a slot
     const int arow = a.gather ? slotid / a.topk : pos;
     const int E = a.ex[arow];              // row exponent, used by the epilogue
 
@@ -253,7 +275,7 @@ void gemm_dec_kernel(DecArgs a) {
     {
       const int w = 64 * wave + lane;
       const int gi = w >> 5, col = (w >> 1) & 15, comp = w & 1;
-      const int r = a.gather ? sload16(etab, t0, col) / a.topk : offe + t0 + col;
+      const int r = a.gather ? sload16(slp, 0, col) / a.topk : offe + t0 + col;
       if (wave < SL::NSUM && gi < NG && col < ncol) sum_vo = (((uint32_t)r * ng + gi) * 2u + comp) * 4u;
     }
     auto issue = [&](int b, char* base) {

@@ -16,6 +16,7 @@ __device__ void route_block(const RouteArgs& a, int* lds) {
   constexpr int NW = NT / 64;
   constexpr bool SMALL = SMAX > 0;
   int* s_seg = lds;                  // [1024]
+  int* s_arank = s_seg + 512;        // [K]: rank of expert e among the active ones (-1: none)
   int* s_tot = s_seg + 1024;         // [257]
   int* s_off = s_tot + 257;          // [257]
   int* s_w = s_off + 257;            // [17]
@@ -101,9 +102,12 @@ __device__ void route_block(const RouteArgs& a, int* lds) {
       sg += g[q];
       sx += x[q];
     }
+    int na = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) na += (c[q] > 0);
     const int ic = wave_incl_scan_i(sc, lane), ig = wave_incl_scan_i(sg, lane),
-              ix = wave_incl_scan_i(sx, lane);
-    int rc = ic - sc, rg = ig - sg, rx = ix - sx;
+              ix = wave_incl_scan_i(sx, lane), ia = wave_incl_scan_i(na, lane);
+    int rc = ic - sc, rg = ig - sg, rx = ix - sx, ra = ia - na;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
@@ -113,11 +117,20 @@ __device__ void route_block(const RouteArgs& a, int* lds) {
         s_off[e] = rc;
         a.tile_gemm[e] = rg;
         a.tile_colx[e] = rx;
+        s_arank[e] = (c[q] > 0) ? ra : -1;
+        if (a.arec && c[q] > 0) {
+          int* r = a.arec + ra * ROUTE_AREC;
+          r[0] = e;
+          r[1] = c[q];
+          r[2] = rc;
+        }
       }
       rc += c[q];
       rg += g[q];
       rx += x[q];
+      ra += (c[q] > 0);
     }
+    if (a.arec && lane == 63) a.arec[K * ROUTE_AREC] = ia;   // number of active experts
     const int tc = __shfl(ic, 63, 64), tgl = __shfl(ig, 63, 64), tx = __shfl(ix, 63, 64);
     if (lane == 0) {
       a.off[K] = tc;
@@ -136,6 +149,7 @@ __device__ void route_block(const RouteArgs& a, int* lds) {
       a.perm[p] = s;
       a.inv[s] = p;
       if (a.etab) a.etab[e * S + (p - s_off[e])] = s;
+      if (a.arec && p - s_off[e] < 16) a.arec[s_arank[e] * ROUTE_AREC + 4 + (p - s_off[e])] = s;
     } else {
       a.inv[s] = -1;
     }

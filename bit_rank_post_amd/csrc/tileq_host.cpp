@@ -93,7 +93,7 @@ struct Plan {
   int nks;                       // k-chunks (fp32 slabs) of the last projection's residual
   int ap_T;                      // decode: column stage over all (column, token) pairs
   int col_tiles_x, col_tiles_down;   // decode column-stage tiles
-  size_t flags, cnt, off, perm, inv, etab, tile_gemm, tile_colx, colmask, cntw, rank;
+  size_t flags, cnt, off, perm, inv, etab, arec, tile_gemm, tile_colx, colmask, cntw, rank;
   size_t col_off[2], col_tok[2], slot2col[2], tile_col[2];
   size_t P[3];
   int nsplit[3];
@@ -236,6 +236,7 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.perm = take(sizeof(int) * S);
   p.inv = take(sizeof(int) * S);
   p.etab = take(sizeof(int) * ((size_t)K * S + 16));   // + 16: whole 16-entry reads
+  p.arec = take(sizeof(int) * ((size_t)K * ROUTE_AREC + 1));
   p.tile_gemm = take(sizeof(int) * (K + 1));
   p.tile_colx = take(sizeof(int) * (K + 1));
   p.colmask = take(sizeof(int) * std::max(T, 1));
@@ -337,6 +338,7 @@ void fill_route(const tq_layer* L, const Plan& p, const int* ids, void* ws, Rout
   r.perm = at<int>(ws, p.perm);
   r.inv = at<int>(ws, p.inv);
   r.etab = (p.path == 1) ? at<int>(ws, p.etab) : nullptr;
+  r.arec = (p.path == 1) ? at<int>(ws, p.arec) : nullptr;
   r.tile_gemm = at<int>(ws, p.tile_gemm);
   r.tile_colx = at<int>(ws, p.tile_colx);
   r.cntw = at<int>(ws, p.cntw);
@@ -664,6 +666,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     da.topk = topk;
     da.etab = at<int>(ws, p.etab);
     da.spec = p.S >= 2 * K;  // nearly every expert is routed to
+    da.arec = da.spec ? nullptr : at<int>(ws, p.arec);  // else: active experts first
     da.off = at<int>(ws, p.off);
     da.cnt = at<int>(ws, p.cnt);
     da.gather = 1;
@@ -783,6 +786,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.topk = topk;
       da.etab = at<int>(ws, p.etab);
       da.spec = p.S >= 2 * K;  // nearly every expert is routed to
+      da.arec = da.spec ? nullptr : at<int>(ws, p.arec);  // else: active experts first
       da.off = at<int>(ws, p.off);
       da.cnt = at<int>(ws, p.cnt);
       da.gather = 0;

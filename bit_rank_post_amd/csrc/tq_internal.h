@@ -57,6 +57,7 @@ struct RouteArgs {
   int* perm;                     // [S]
   int* inv;                      // [S]
   int* etab;                     // optional [K][S]: slot ids of expert e at e * S + c
+  int* arec;                     // optional [K][ROUTE_AREC] + 1: active-expert records, see below
   int* tile_gemm;                // [K+1] prefix of ceil(cnt/bm_gemm)
   int* tile_colx;                // [K+1] prefix of ceil(cnt/rt_col) (down column stage)
   int* col_off[2];               // [N+1]
@@ -70,6 +71,10 @@ struct RouteArgs {
   int zero_n;
 };
 void launch_route(const RouteArgs& a, hipStream_t s);
+// Active-expert record i (i < number of active experts, stored after the K
+// records): expert id, slot count, offset, 0, slot ids of its first 16
+// positions (entries past the count are stale).
+constexpr int ROUTE_AREC = 20;
 
 // ---- column stage: P[split][row][r] = sigma_r sum_{k in split} a_row[k] V_n[k][r]
 struct ColArgs {
@@ -151,6 +156,7 @@ struct DecArgs {
   int ap_T;                      // GATEUP: P rows are (column, token) pairs n * ap_T + t
   int p_nsplit, p_rows_cap;      // GATEUP: P slabs to add, rows per slab
   int spec;                      // 1: request the first stages' codes before the routing reads return
+  const int* arec;               // active-expert records (compact mapping) or nullptr
 };
 void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s);
 // true when 8-wave decode workgroups of np projections and this group size
