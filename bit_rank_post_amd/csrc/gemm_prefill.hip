@@ -53,6 +53,13 @@ struct PfSlot {
   static constexpr int NI = NB + RF * NP * 2 + NP * NSZ;       // loads per wave per stage
 };
 
+// Super-block of row tiles x slot tiles that one XCD's 32 CUs (one
+// workgroup each) work on together: up to 8 row tiles, 32 workgroups.
+__host__ __device__ inline void pf_superblock(int nrt, int* sbr, int* sbc) {
+  *sbr = nrt < 8 ? nrt : 8;
+  *sbc = 32 / *sbr;
+}
+
 template <typename T, int MODE, int RF, int NF, int GS>
 __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   typedef typename Vec8<T>::type V8;
@@ -79,8 +86,20 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   const int nrb = a.d_out >> 4;
   const int rows_per_wg = 16 * RF * PF_WAVES;
   const int nrt = (a.d_out + rows_per_wg - 1) / rows_per_wg;
-  const int rt = blockIdx.x % nrt;
-  const int tq = blockIdx.x / nrt;
+  // Workgroup -> (row tile rt, slot-tile unit tq).  Workgroup W runs on XCD
+  // W mod 8; the 32 CUs of an XCD work on a super-block of SBR row tiles x
+  // SBC slot tiles together, all on the same stage order, so each stage's
+  // codes (per row tile) and activations (per slot tile) come from HBM once
+  // per XCD and are shared through its L2.
+  int sbr, sbc;
+  pf_superblock(nrt, &sbr, &sbc);
+  const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
+  const int sbl = li / (sbr * sbc), within = li - sbl * (sbr * sbc);
+  const int sb = sbl * 8 + xcd;
+  const int nrtb = (nrt + sbr - 1) / sbr;
+  const int rt = (sb % nrtb) * sbr + within % sbr;
+  const int tq = (sb / nrtb) * sbc + within / sbr;
+  if (rt >= nrt || tq >= a.ntq) return;
   // the routing tiles hold 128 slots; with 64-slot tiles each is done in two
   // halves (tile_half)
   const int tile = a.tile_half ? tq >> 1 : tq;
@@ -152,9 +171,8 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
     const int gofs = (GS == 0) ? 0 : gi;       // generic G: one load per group slot
     sz_vo[n] = ok ? (((uint32_t)(r * ng + gofs)) * 16u + row) * 4u : OOB;
   }
-  // stage order rotated by row tile: workgroups that share an activation tile
-  // start at different stages
-  const int r0 = rt % nstage;
+  // stage order rotated by super-block (the same inside one)
+  const int r0 = sb % nstage;
 
   auto issue = [&](int b, char* base) {
     const bool live = b < nstage;
@@ -354,20 +372,29 @@ constexpr bool pre_fits() {
   return 3 * PfSlot<NP, RF, NF, GS>::BYTES <= 160 * 1024 - 2048;
 }
 
+static int pf_grid(int nrt, int ntq) {
+  int sbr, sbc;
+  pf_superblock(nrt, &sbr, &sbc);
+  const int nsb = ((nrt + sbr - 1) / sbr) * ((ntq + sbc - 1) / sbc);
+  return ((nsb + 7) / 8) * 8 * sbr * sbc;
+}
+
 template <typename T, int MODE, int RF, int NF, int GS>
 static void pre_launch(const GemmArgs& a, int max_tiles, hipStream_t s) {
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   const int rows_per_wg = 16 * RF * PF_WAVES;
   const int nrt = (a.d_out + rows_per_wg - 1) / rows_per_wg;
+  GemmArgs b = a;
   if constexpr (pre_fits<NP, RF, NF, GS>()) {
-    const dim3 grid(max_tiles * nrt), block(64 * PF_WAVES);
-    hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS>), grid, block, 0, s, a);
+    b.ntq = max_tiles;
+    const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
+    hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS>), grid, block, 0, s, b);
   } else {
-    // a 128-slot tile is twice a 64-slot tile: same grid, two passes
+    // a 128-slot tile is twice a 64-slot tile: two units per tile
     static_assert(NF == 8, "smaller tiles always fit");
-    GemmArgs b = a;
     b.tile_half = 1;
-    const dim3 grid(2 * max_tiles * nrt), block(64 * PF_WAVES);
+    b.ntq = 2 * max_tiles;
+    const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
     hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, 4, GS>), grid, block, 0, s, b);
   }
 }

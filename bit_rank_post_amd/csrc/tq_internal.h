@@ -123,6 +123,7 @@ struct GemmArgs {
   const float* gates;            // RES: topk weights [T*topk]
   int rows;                      // rows of A
   int tile_half;                 // set by the launcher: 64-slot halves of 128-slot tiles
+  int ntq;                       // set by the launcher: slot-tile units of the grid
 };
 // prefill grouped GEMM; A is fp16 (bfloat16 rows converted by rows_to_f16,
 // exponents in ex); tiles of 128 slots (route bm_gemm = 128)
