@@ -78,14 +78,26 @@ __global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
     }
   }
   float* P = a.P + (size_t)split * a.rows_cap * a.r_pad;
+  T* PH = reinterpret_cast<T*>(P);
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     if (f < nfrag) {
+      const float sg = a.sigma[16 * f + (lane & 15)];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = rbase + 4 * (lane >> 4) + v;
-        if (row < row_end)
-          P[(size_t)row * a.r_pad + 16 * f + (lane & 15)] = acc[f][v] * a.sigma[16 * f + (lane & 15)];
+        if (row >= row_end) continue;
+        const float val = acc[f][v] * sg;
+        if (a.hilo) {
+          // the operand of the row stage's MFMAs: value = high + low, both in
+          // the activation dtype
+          const T hi = from_f32<T>(val);
+          T* dst = PH + (size_t)row * 2 * a.r_pad + 16 * f + (lane & 15);
+          dst[0] = hi;
+          dst[a.r_pad] = from_f32<T>(val - to_f32(hi));
+        } else {
+          P[(size_t)row * a.r_pad + 16 * f + (lane & 15)] = val;
+        }
       }
     }
   }

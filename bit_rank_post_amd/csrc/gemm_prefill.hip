@@ -77,6 +77,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char s2[SL::BYTES];
   __shared__ int s_src[BN];
   __shared__ int s_exp[BN];
+  __shared__ int s_col[NP][BN];     // GATEUP: column-stage row of each slot (-1: none)
   __shared__ int s_res;
   char* const slot[3] = {s0, s1, s2};
 
@@ -112,14 +113,24 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   const int rb0 = rt * RF * PF_WAVES + wave * RF;     // first row block of this wave
 
   if (tid < BN) {
-    int src = -1, ex = 0;
+    int src = -1, ex = 0, col[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) col[p] = -1;
     if (tid < nv) {
       const int pos = pos0 + tid;
-      src = a.gather ? a.perm[pos] / a.topk : pos;
+      const int slotid = a.perm[pos];
+      src = a.gather ? slotid / a.topk : pos;
       if (a.ex) ex = a.ex[src];
+      if constexpr (MODE == MODE_GATEUP) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          if (a.P[p]) col[p] = a.slot2col[p][slotid];
+      }
     }
     s_src[tid] = src;
     s_exp[tid] = ex;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) s_col[p][tid] = col[p];
   }
   __syncthreads();
 
@@ -216,6 +227,26 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
       for (int f = 0; f < NF; ++f) acc[p][r][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const char* base) {
+    // the stage's code dwords and scale/zero words are read first, so the
+    // first fragment's dequantization waits for them alone
+    uint32_t cw[2][RF][NP];
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int r = 0; r < RF; ++r)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          cw[d][r][p] = *reinterpret_cast<const uint32_t*>(
+              base + SL::CODE + (((wave * RF + r) * NP + p) * 2 + d) * 256 + lane * 4);
+    uint32_t zw[RF][NP][NGS];
+#pragma unroll
+    for (int r = 0; r < RF; ++r)
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int g = 0; g < NGS; ++g)
+          zw[r][p][g] = *reinterpret_cast<const uint32_t*>(
+              base + SL::SZ + (wave * NP + p) * SL::NSZ * 256 + (g * SL::SZG + r * 16 + l16) * 4);
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       half8v bfr[2][NF];
@@ -229,25 +260,21 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
       for (int r = 0; r < RF; ++r)
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const uint32_t D = *reinterpret_cast<const uint32_t*>(
-              base + SL::CODE + (((wave * RF + r) * NP + p) * 2 + d) * 256 + lane * 4);
           // scale/zero words of this lane's row for k-steps 2d and 2d+1
           const int gi0 = (NGS == 4) ? 2 * d : (NGS == 2 ? d : 0);
           const int gi1 = (NGS == 4) ? 2 * d + 1 : gi0;
-          const char* zb = base + SL::SZ + (wave * NP + p) * SL::NSZ * 256 + (r * 16 + l16) * 4;
-          const DeqConst c0 = deq_const(*reinterpret_cast<const uint32_t*>(zb + gi0 * SL::SZG * 4));
+          const DeqConst c0 = deq_const(zw[r][p][gi0]);
           half8v a0, a1;
           if (gi1 == gi0) {
-            deq_dword(D, c0, c0, a0, a1);
+            deq_dword(cw[d][r][p], c0, c0, a0, a1);
           } else {
-            const DeqConst c1 = deq_const(*reinterpret_cast<const uint32_t*>(zb + gi1 * SL::SZG * 4));
-            deq_dword(D, c0, c1, a0, a1);
+            const DeqConst c1 = deq_const(zw[r][p][gi1]);
+            deq_dword(cw[d][r][p], c0, c1, a0, a1);
           }
 #pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            acc[p][r][f] = mfma16(a0, bfr[0][f], acc[p][r][f]);
-            acc[p][r][f] = mfma16(a1, bfr[1][f], acc[p][r][f]);
-          }
+          for (int f = 0; f < NF; ++f) acc[p][r][f] = mfma16(a0, bfr[0][f], acc[p][r][f]);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) acc[p][r][f] = mfma16(a1, bfr[1][f], acc[p][r][f]);
         }
     }
   };
@@ -284,53 +311,83 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   }
 
   if constexpr (MODE == MODE_GATEUP) {
-    // low-rank row stage as extra k-steps: A = U_m rows, B = Sigma p (hi, lo)
-    constexpr int EXT_LD = 64 + 8;      // rank chunk of 64 (+ pad), halves
-    static_assert(2 * BN * EXT_LD * 2 <= SL::BYTES, "row-stage staging fits a slot");
-    T* s_ext = reinterpret_cast<T*>(s0);
+    // Low-rank row stage as extra k-steps: A = U_m rows (straight from global
+    // memory in the A-fragment layout), B = Sigma p of each slot as a high
+    // and a low part in the activation dtype (the column stage wrote them so,
+    // row [high r_pad | low r_pad]).  One pass per block of up to KBB rank
+    // steps of each projection: the wave's U fragments are requested, the
+    // slots' rows are gathered into the idle ring by LDS-destination loads
+    // as 1 KB B fragments (unit = one projection's rank step: [hi|lo][NF]
+    // fragments), then the MFMAs run.
+    constexpr int KBB = 4;                          // rank steps per projection and pass
+    constexpr int NU = NP * KBB;                    // units per pass
+    constexpr int UB = 2 * NF * 1024;               // bytes of a unit
+    constexpr int UPS = SL::BYTES / UB;             // units per ring slot
+    constexpr int CPW = NU * 2 * NF / PF_WAVES;     // fragment loads per wave and pass
+    static_assert(NSLOT * UPS >= NU, "one pass of units fits the ring");
+    static_assert(CPW * PF_WAVES == NU * 2 * NF, "fragment loads split evenly over the waves");
+    int nk[NP], rp[NP];
+    size_t mrow[NP];
+    __amdgpu_buffer_rsrc_t rph[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const ProjDev& pd = a.p[p];
-      const int rp = pd.r_pad;
-      if (pd.rank == 0) continue;
-      const int m = pd.m_of[e];
-      for (int rc0 = 0; rc0 < rp; rc0 += 64) {
-        const int rw = min(64, rp - rc0);
-        __syncthreads();
-        for (int i = tid; i < BN * rw; i += 64 * PF_WAVES) {
-          const int row = i / rw, c = i - row * rw;
-          T hi = from_f32<T>(0.f), lo = from_f32<T>(0.f);
-          if (row < nv) {
-            const int slotid = a.perm[pos0 + row];
-            const int col = a.slot2col[p][slotid];
-            float v = 0.f;
-            for (int sp = 0; sp < a.nsplit[p]; ++sp)
-              v += a.P[p][((size_t)sp * a.rows_cap[p] + col) * rp + rc0 + c];
-            hi = from_f32<T>(v);
-            lo = from_f32<T>(v - to_f32(hi));
+      rp[p] = a.p[p].r_pad;
+      nk[p] = (a.p[p].rank > 0 && a.P[p]) ? rp[p] >> 5 : 0;
+      mrow[p] = nk[p] ? (size_t)a.p[p].m_of[e] * a.d_out : 0;
+      rph[p] = make_rsrc(a.P[p], nk[p] ? (uint32_t)((size_t)a.p_rows * rp[p] * 4u) : 0u);
+    }
+    const int nkmax = (NP > 1) ? max(nk[0], nk[NP - 1]) : nk[0];
+    auto slot_of = [&](int i) { return i == 0 ? s0 : (i == 1 ? s1 : s2); };
+    for (int kb0 = 0; kb0 < nkmax; kb0 += KBB) {
+      V8 uf[NP][RF][KBB];
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int r = 0; r < RF; ++r)
+#pragma unroll
+          for (int i = 0; i < KBB; ++i) {
+            uf[p][r][i] = __builtin_bit_cast(V8, u32x4{0u, 0u, 0u, 0u});
+            if (kb0 + i < nk[p] && rb0 + r < nrb) {
+              const T* up = reinterpret_cast<const T*>(a.p[p].U) +
+                            (mrow[p] + (rb0 + r) * 16 + l16) * rp[p] + (kb0 + i) * 32 + 8 * lg;
+              uf[p][r][i] = *reinterpret_cast<const V8*>(up);
+            }
           }
-          s_ext[row * EXT_LD + c] = hi;
-          s_ext[BN * EXT_LD + row * EXT_LD + c] = lo;
-        }
-        __syncthreads();
+      __syncthreads();             // nothing reads the ring any more
 #pragma unroll
-        for (int r = 0; r < RF; ++r) {
-          if (rb0 + r >= nrb) continue;
-          const T* up = reinterpret_cast<const T*>(pd.U) +
-                        ((size_t)m * a.d_out + (rb0 + r) * 16 + l16) * rp + rc0 + 8 * lg;
-          for (int s2 = 0; s2 < rw; s2 += 32) {
-            const V8 av = *reinterpret_cast<const V8*>(up + s2);
+      for (int i = 0; i < CPW; ++i) {
+        const int c = wave * CPW + i;              // (unit, hi/lo, fragment)
+        const int u = c / (2 * NF), hl = (c / NF) & 1, f = c % NF;
+        const int p = (NP > 1) ? u / KBB : 0, kb = kb0 + u % KBB;
+        const int np = (NP > 1 && p) ? nk[NP - 1] : nk[0];
+        const int rpp = (NP > 1 && p) ? rp[NP - 1] : rp[0];
+        const int col = s_col[p][16 * f + l16];
+        const uint32_t vo = (kb < np && col >= 0)
+                                ? ((uint32_t)col * rpp * 2u + hl * rpp + kb * 32 + 8 * lg) * 2u
+                                : OOB;
+        dma16((NP > 1 && p) ? rph[NP - 1] : rph[0],
+              slot_of(u / UPS) + (u % UPS) * UB + (hl * NF + f) * 1024, vo, 0u);
+      }
+      wait_vm<0>();
+      __syncthreads();
 #pragma unroll
-            for (int f = 0; f < NF; ++f) {
-              const T* bp = &s_ext[(16 * f + l16) * EXT_LD + s2 + 8 * lg];
-              const V8 bh = *reinterpret_cast<const V8*>(bp);
-              const V8 bl = *reinterpret_cast<const V8*>(bp + BN * EXT_LD);
-              acc[p][r][f] = mfma16(av, bh, acc[p][r][f]);
-              acc[p][r][f] = mfma16(av, bl, acc[p][r][f]);
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < KBB; ++i) {
+          if (kb0 + i >= nk[p]) continue;
+          const int u = p * KBB + i;
+          const char* ub = slot_of(u / UPS) + (u % UPS) * UB + lane * 16;
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const V8 bh = *reinterpret_cast<const V8*>(ub + f * 1024);
+            const V8 bl = *reinterpret_cast<const V8*>(ub + (NF + f) * 1024);
+#pragma unroll
+            for (int r = 0; r < RF; ++r) {
+              acc[p][r][f] = mfma16(uf[p][r][i], bh, acc[p][r][f]);
+              acc[p][r][f] = mfma16(uf[p][r][i], bl, acc[p][r][f]);
             }
           }
         }
-      }
     }
     // SwiGLU epilogue: h = RND_act(silu(gate) * up), stored per slot position
     T* h = reinterpret_cast<T*>(a.h);

@@ -368,6 +368,9 @@ ColArgs col_args_x(const tq_layer* L, const Plan& p, int c, const void* x, void*
   a.P = at<float>(ws, p.P[c]);
   a.rows_cap = p.rows_cap;
   a.ap_T = p.ap_T;
+  // prefill SwiGLU: the gate/up GEMM reads Sigma p as its MFMA operand
+  // (split-K is decode-only, so the one slab is final)
+  a.hilo = (p.path != 1 && L->kind == TQ_SWIGLU && p.nsplit[c] == 1) ? 1 : 0;
   return a;
 }
 
@@ -722,10 +725,10 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       ga.p[1] = L->proj[1].dev;
       for (int c = 0; c < 2; ++c) {
         ga.P[c] = L->proj[c].dev.r_pad ? at<float>(ws, p.P[c]) : nullptr;
-        ga.nsplit[c] = 1;
-        ga.rows_cap[c] = p.rows_cap;
+        if (ga.P[c] && p.nsplit[c] != 1) return fail(TQ_EUNSUPPORTED, "prefill column stage must be one slab");
         ga.slot2col[c] = at<int>(ws, p.slot2col[c]);
       }
+      ga.p_rows = p.rows_cap;
       ga.h = h;
       launch_gemm_prefill(ga, MODE_GATEUP, act, p.max_tiles_gemm, s);
     } else {

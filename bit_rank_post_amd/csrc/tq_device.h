@@ -43,18 +43,19 @@ __device__ __forceinline__ u32x4 as_u32x4(half8v v) { return __builtin_bit_cast(
 // position.  One and-or per pair; two shifts per dword.
 //   out[0..3] : step b=0, classes {1/64, 1/16, 1/4, 1/64}
 //   out[4..7] : step b=1, classes {1/64, 1/16, 1/4, 1/16}
+__device__ __forceinline__ uint32_t and_or_s(uint32_t a, uint32_t m, uint32_t c);
 __device__ __forceinline__ void unpack16(uint32_t D, uint32_t out[8]) {
   const uint32_t M4 = 0x00300030u, M6 = 0x00C000C0u, M8 = 0x03000300u;
   const uint32_t ONE = 0x3C003C00u;
   const uint32_t E = D >> 6, F = D << 4;
-  out[0] = (D & M4) | ONE;
-  out[1] = (D & M6) | ONE;
-  out[2] = (D & M8) | ONE;
-  out[3] = (F & M4) | ONE;
-  out[4] = (E & M4) | ONE;
-  out[5] = (E & M6) | ONE;
-  out[6] = (E & M8) | ONE;
-  out[7] = (F & M6) | ONE;
+  out[0] = and_or_s(D, M4, ONE);
+  out[1] = and_or_s(D, M6, ONE);
+  out[2] = and_or_s(D, M8, ONE);
+  out[3] = and_or_s(F, M4, ONE);
+  out[4] = and_or_s(E, M4, ONE);
+  out[5] = and_or_s(E, M6, ONE);
+  out[6] = and_or_s(E, M8, ONE);
+  out[7] = and_or_s(F, M6, ONE);
 }
 
 // ---- buffer loads ----------------------------------------------------------
@@ -152,6 +153,13 @@ __device__ __forceinline__ void bar_nofence() {
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   uint32_t r;
   asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+
+// The same, free to be scheduled and merged like ordinary arithmetic.
+__device__ __forceinline__ uint32_t and_or_s(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
   return r;
 }
 

@@ -91,6 +91,8 @@ struct ColArgs {
   const float* sigma;            // [r_pad]: P holds Sigma (V_n^T a)
   float* P;
   int rows_cap;                  // rows per split slab
+  int hilo;                      // 1 (nsplit 1 only): each row of P holds Sigma (V_n^T a)
+                                 // as [high part | low part] in the activation dtype
   int ap_T;                      // > 0: every (column, token) pair, row = n * ap_T + t
                                  // (no work lists; seg_off/tile_off/row_src unused)
 };
@@ -112,10 +114,11 @@ struct GemmArgs {
   const int* ex;                 // per-row exponent of converted bf16 rows, or nullptr
   // projections (1 for RES, 2 for GATEUP)
   ProjDev p[2];
-  // low-rank extension (GATEUP): P partials of each projection
+  // low-rank extension (GATEUP): Sigma p rows of each projection as written
+  // by the column stage with hilo set ([row][high r_pad | low r_pad] in the
+  // activation dtype, p_rows rows) and the column-stage row of every slot
   const float* P[2];
-  int nsplit[2];
-  int rows_cap[2];
+  int p_rows;
   const int* slot2col[2];
   // outputs
   void* h;                       // GATEUP: [S][d_out] act
