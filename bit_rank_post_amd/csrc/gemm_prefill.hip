@@ -129,8 +129,10 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
     }
     s_src[tid] = src;
     s_exp[tid] = ex;
+    if constexpr (MODE == MODE_GATEUP) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) s_col[p][tid] = col[p];
+      for (int p = 0; p < NP; ++p) s_col[p][tid] = col[p];
+    }
   }
   __syncthreads();
 
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
               uf[p][r][i] = *reinterpret_cast<const V8*>(up);
             }
           }
-      __syncthreads();             // nothing reads the ring any more
+      bar_nofence();               // nothing reads the ring any more (the U loads stay in flight)
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
         const int c = wave * CPW + i;              // (unit, hi/lo, fragment)

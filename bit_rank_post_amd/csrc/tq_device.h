@@ -306,6 +306,13 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return
 
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }
 
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
+// silu(v) = v / (1 + e^-v) from the hardware base-2 exponential and
+// reciprocal (each within about one ulp in fp32; the result is rounded to the
+// activation dtype afterwards).  v -> -inf: e^-v overflows to inf and the
+// reciprocal to 0.
+__device__ __forceinline__ float silu_f(float v) {
+  const float e = __builtin_amdgcn_exp2f(v * -1.4426950408889634f);
+  return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 }  // namespace tq
