@@ -20,84 +20,260 @@
 
 namespace tq {
 
-// 4 waves, each owning 16 rows of a 64-row tile, over the whole k-range.
-struct ColArgs2 {
-  ColArgs c[2];
+// ---- dense weights x gathered activation rows (prefill) ---------------------
+// out(row n, m) = sum_k W[m][k] a[src(n)][k] for weight rows m of one M tile
+// and a tile of 128 activation rows.  Both operands stream through LDS in a
+// ring of RG_NSLOT slots of 64 inputs (two MFMA k-steps): per stage, 128
+// weight rows and 128 activation rows arrive by 16-byte loads with the LDS
+// destination, already in MFMA fragment order (one 1 KB fragment per load
+// instruction), RG_DEPTH stages ahead of the MFMAs.  8 waves: wave (wm, wn)
+// takes weight fragments wm and wm + 4 against activation fragments
+// 4 wn .. 4 wn + 3.
+//   RG_COL:   column stage, W = V_n^T of the row's segment (rank rows), out =
+//             Sigma-scaled rank vectors (fp32, or high/low parts).
+//   RG_DUAL:  dense SwiGLU input: fragments 0-3 from W0 (gate), 4-7 from W1
+//             (up) for the same 64 output rows; out = RND_act(silu(g) u).
+//   RG_PLAIN: dense single projection, 128 output rows, fp32 out; split-K
+//             over blockIdx.z into separate slabs.
+enum RgMode { RG_COL = 0, RG_DUAL = 1, RG_PLAIN = 2 };
+constexpr int RG_WAVES = 8;
+constexpr int RG_KS = 2;                         // k-steps per stage
+constexpr int RG_NSLOT = 4, RG_DEPTH = 3;
+constexpr int RG_A = 0;                          // [KS][8 frags][64 lanes] x 16 B
+constexpr int RG_B = RG_KS * 8 * 1024;           // [KS][8 frags][64 lanes] x 16 B
+constexpr int RG_BYTES = 2 * RG_KS * 8 * 1024;   // 32 KB per slot
+constexpr int RG_NI = 2 * RG_KS * 8 / RG_WAVES;  // loads per wave per stage
+
+struct RgArgs {
+  ColArgs c[2];                  // RG_COL: per projection (blockIdx.z)
+  DenseArgs d;                   // RG_DUAL / RG_PLAIN
+  int nsplit;                    // RG_PLAIN: k-splits (blockIdx.z), slab stride T * d_out
+  int ntiles;                    // row tiles of the grid (before the XCD remap)
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void colproj_kernel(ColArgs2 args) {
+template <typename T, int MODE>
+__global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   typedef typename Vec8<T>::type V8;
-  const ColArgs& a = args.c[blockIdx.z];
+  __shared__ __attribute__((aligned(16))) char s0[RG_BYTES];
+  __shared__ __attribute__((aligned(16))) char s1[RG_BYTES];
+  __shared__ __attribute__((aligned(16))) char s2[RG_BYTES];
+  __shared__ __attribute__((aligned(16))) char s3[RG_BYTES];
+  __shared__ int s_src[128];
   __shared__ int s_res;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x;
-  constexpr int rt = 64;
-  int seg, row0, row_end;
-  if (a.ap_T > 0) {
-    // every (column, token) pair: column seg owns rows seg * T ... seg * T + T - 1
-    const int tpc = (a.ap_T + rt - 1) / rt;
-    seg = tile / tpc;
-    if (seg >= a.nseg) return;
-    row0 = seg * a.ap_T + (tile - seg * tpc) * rt;
-    row_end = (seg + 1) * a.ap_T;
-  } else {
-    seg = find_segment(a.tile_off, a.nseg, tile, &s_res);
+  char* const slot[RG_NSLOT] = {s0, s1, s2, s3};
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wm = wave & 3, wn = wave >> 2;
+
+  // row tile: consecutive tiles on one XCD (workgroup W runs on XCD W mod 8),
+  // so the workgroups of one segment share its weights in that XCD's L2
+  const int per = (args.ntiles + 7) >> 3;
+  const int tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (tile >= args.ntiles) return;
+
+  int n0, n_end, d_in, M, lda;
+  const void* X;
+  const char* wbase[2];
+  uint32_t wbytes, wrs, wks;           // weight buffer size, row and k-step strides (bytes)
+  int st0 = 0, st1;
+  const ColArgs* ca = nullptr;
+  if constexpr (MODE == RG_COL) {
+    ca = &args.c[blockIdx.z];
+    const ColArgs& a = *ca;
+    const int seg = find_segment(a.tile_off, a.nseg, tile, &s_res);
     if (seg < 0) return;
-    row0 = a.seg_off[seg] + (tile - a.tile_off[seg]) * rt;
-    row_end = a.seg_off[seg + 1];
-  }
-  const int vblk = a.seg_vblk ? a.seg_vblk[seg] : seg;
-  const int nfrag = a.r_pad >> 4;
-  const int split = blockIdx.y;
-  const int st0 = split * a.steps_per_split;
-  const int st1 = min(a.d_in >> 5, st0 + a.steps_per_split);
-
-  const int rbase = row0 + 16 * wave;
-  const int myrow = rbase + (lane & 15);
-  const bool rvalid = myrow < row_end;
-  int src = 0;
-  if (rvalid) src = (a.ap_T > 0) ? myrow - seg * a.ap_T : (a.row_src ? a.row_src[myrow] : myrow);
-  const T* arow = reinterpret_cast<const T*>(a.A) + (size_t)src * a.lda + 8 * (lane >> 4);
-  const T* vt = reinterpret_cast<const T*>(a.Vt) + (size_t)vblk * a.r_pad * a.d_in;   // [steps][r_pad][32]
-
-  f32x4 acc[8];
-#pragma unroll
-  for (int f = 0; f < 8; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int st = st0; st < st1; ++st) {
-    V8 avv;
-    if (rvalid) avv = *reinterpret_cast<const V8*>(arow + st * 32);
-    else avv = __builtin_bit_cast(V8, u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      if (f < nfrag) {
-        const V8 bvv = *reinterpret_cast<const V8*>(
-            vt + ((size_t)st * a.r_pad + 16 * f + (lane & 15)) * 32 + 8 * (lane >> 4));
-        acc[f] = mfma16(avv, bvv, acc[f]);
-      }
+    n0 = a.seg_off[seg] + (tile - a.tile_off[seg]) * 128;
+    n_end = a.seg_off[seg + 1];
+    const int vblk = a.seg_vblk ? a.seg_vblk[seg] : seg;
+    d_in = a.d_in;
+    M = a.r_pad;
+    lda = a.lda;
+    X = a.A;
+    const size_t vsz = (size_t)(d_in >> 5) * a.r_pad * 64;
+    wbase[0] = wbase[1] = reinterpret_cast<const char*>(a.Vt) + (size_t)vblk * vsz;
+    wbytes = (uint32_t)vsz;
+    wrs = 64u;
+    wks = (uint32_t)a.r_pad * 64u;
+    st1 = d_in >> 6;
+    if (tid < 128) {
+      const int n = n0 + tid;
+      s_src[tid] = (n < n_end) ? (a.row_src ? a.row_src[n] : n) : -1;
+    }
+  } else {
+    const DenseArgs& a = args.d;
+    n0 = tile * 128;
+    n_end = a.T;
+    d_in = a.d_in;
+    M = a.d_out;
+    lda = a.d_in;
+    X = a.X;
+    wbase[0] = reinterpret_cast<const char*>(a.W0);
+    wbase[1] = reinterpret_cast<const char*>(MODE == RG_DUAL ? a.W1 : a.W0);
+    wbytes = (uint32_t)((size_t)M * d_in * 2);
+    wrs = (uint32_t)d_in * 2u;
+    wks = 64u;
+    const int nst = d_in >> 6;
+    const int sps = (nst + args.nsplit - 1) / args.nsplit;
+    st0 = blockIdx.z * sps;
+    st1 = min(nst, st0 + sps);
+    if (tid < 128) {
+      const int n = n0 + tid;
+      s_src[tid] = (n < n_end) ? n : -1;
     }
   }
-  float* P = a.P + (size_t)split * a.rows_cap * a.r_pad;
-  T* PH = reinterpret_cast<T*>(P);
+  // weight rows of this M tile: RG_DUAL 64 output rows (x2 matrices), else 128
+  const int m0 = blockIdx.y * (MODE == RG_DUAL ? 64 : 128);
+  __syncthreads();
+  const int nv = min(128, n_end - n0);
+  const int row_lo = s_src[0];
+  const int row_hi = s_src[max(nv - 1, 0)];
+
+  // per-lane offsets of this wave's loads: load q = wave * NI + i; q < 16:
+  // weight fragment (k-step q / 8, fragment q % 8), else activation fragment
+  uint32_t vo[RG_NI];
+  bool isw[RG_NI];
+  int wsel[RG_NI], ks_of[RG_NI], fr_of[RG_NI];
 #pragma unroll
-  for (int f = 0; f < 8; ++f) {
-    if (f < nfrag) {
-      const float sg = a.sigma[16 * f + (lane & 15)];
+  for (int i = 0; i < RG_NI; ++i) {
+    const int q = wave * RG_NI + i;
+    const bool w = q < 16;
+    const int qq = w ? q : q - 16;
+    const int ks = qq >> 3, f = qq & 7;
+    isw[i] = w;
+    ks_of[i] = ks;
+    fr_of[i] = f;
+    if (w) {
+      // weight row of fragment f
+      int m;
+      if (MODE == RG_DUAL) {
+        wsel[i] = f >> 2;
+        m = m0 + 16 * (f & 3) + l16;
+      } else {
+        wsel[i] = 0;
+        m = m0 + 16 * f + l16;
+      }
+      // blocked V^T: the k-step goes into the uniform offset
+      vo[i] = (m < M) ? (uint32_t)m * wrs + (MODE == RG_COL ? 0u : (uint32_t)ks * 64u) + lg * 16u
+                      : OOB;
+    } else {
+      wsel[i] = 0;
+      const int src = s_src[16 * f + l16];
+      vo[i] = (src >= 0) ? ((uint32_t)(src - row_lo) * lda + ks * 32 + 8 * lg) * 2u : OOB;
+    }
+  }
+  __amdgpu_buffer_rsrc_t rw[2];
+  rw[0] = make_rsrc(wbase[0], wbytes);
+  rw[1] = make_rsrc(wbase[1], wbytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(
+      reinterpret_cast<const T*>(X) + (size_t)max(row_lo, 0) * lda,
+      (uint32_t)min<size_t>((size_t)(row_hi - row_lo + 1) * lda * 2u, (size_t)OOB));
+  const int nstage = st1 - st0;
+
+  auto issue = [&](int b, char* base) {
+    const bool live = b < nstage;
+    const int st = st0 + (live ? b : 0);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = rbase + 4 * (lane >> 4) + v;
-        if (row >= row_end) continue;
-        const float val = acc[f][v] * sg;
+    for (int i = 0; i < RG_NI; ++i) {
+      char* dst = base + (isw[i] ? RG_A : RG_B) + (ks_of[i] * 8 + fr_of[i]) * 1024;
+      if (isw[i]) {
+        // k-step offset: blocked V^T layout moves by whole k-step blocks,
+        // row-major weights by 128 bytes per stage
+        const uint32_t so = (MODE == RG_COL) ? (uint32_t)(2 * st + ks_of[i]) * wks
+                                             : (uint32_t)st * 128u;
+        dma16(wsel[i] ? rw[1] : rw[0], dst, live ? vo[i] : OOB, so);
+      } else {
+        dma16(rx, dst, live ? vo[i] : OOB, (uint32_t)st * 128u);
+      }
+    }
+  };
+
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const char* base) {
+#pragma unroll
+    for (int ks = 0; ks < RG_KS; ++ks) {
+      const V8 a0 = *reinterpret_cast<const V8*>(base + RG_A + (ks * 8 + wm) * 1024 + lane * 16);
+      const V8 a1 = *reinterpret_cast<const V8*>(base + RG_A + (ks * 8 + wm + 4) * 1024 + lane * 16);
+      V8 b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const V8*>(base + RG_B + (ks * 8 + 4 * wn + j) * 1024 + lane * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[0][j] = mfma16(a0, b[j], acc[0][j]);
+        acc[1][j] = mfma16(a1, b[j], acc[1][j]);
+      }
+    }
+  };
+
+  // ring over stages (protocol of the grouped residual GEMMs): whole rounds,
+  // stage-times past the end only wait and issue empty loads
+#pragma unroll
+  for (int b = 0; b < RG_DEPTH; ++b) issue(b, slot[b]);
+  for (int t = 0; t < nstage; t += RG_NSLOT) {
+#pragma unroll
+    for (int u = 0; u < RG_NSLOT; ++u) {
+      const int tau = t + u;
+      wait_vm<RG_NI * (RG_DEPTH - 1)>();
+      bar_nofence();
+      if (tau < nstage) compute(slot[u]);
+      issue(tau + RG_DEPTH, slot[(u + RG_DEPTH) % RG_NSLOT]);
+    }
+  }
+  wait_vm<0>();
+
+  // epilogue: lane holds out(row n0 + 16 (4 wn + j) + l16, weight rows
+  // m(i) + 4 lg + v) in acc[i][j][v]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int nl = 16 * (4 * wn + j) + l16;
+    const int n = n0 + nl;
+    if (nl >= nv) continue;
+    if constexpr (MODE == RG_COL) {
+      const ColArgs& a = *ca;
+      T* PH = reinterpret_cast<T*>(a.P);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int m = 16 * (wm + 4 * i) + 4 * lg;
+        if (m >= a.r_pad) continue;
+        const f32x4 sg = *reinterpret_cast<const f32x4*>(a.sigma + m);
+        const f32x4 v = acc[i][j] * sg;
         if (a.hilo) {
-          // the operand of the row stage's MFMAs: value = high + low, both in
-          // the activation dtype
-          const T hi = from_f32<T>(val);
-          T* dst = PH + (size_t)row * 2 * a.r_pad + 16 * f + (lane & 15);
-          dst[0] = hi;
-          dst[a.r_pad] = from_f32<T>(val - to_f32(hi));
+          T hi[4], lo[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            hi[c] = from_f32<T>(v[c]);
+            lo[c] = from_f32<T>(v[c] - to_f32(hi[c]));
+          }
+          T* dst = PH + (size_t)n * 2 * a.r_pad + m;
+          *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, hi);
+          *reinterpret_cast<u32x2*>(dst + a.r_pad) = __builtin_bit_cast(u32x2, lo);
         } else {
-          P[(size_t)row * a.r_pad + 16 * f + (lane & 15)] = val;
+          *reinterpret_cast<f32x4*>(a.P + (size_t)n * a.r_pad + m) = v;
         }
+      }
+    } else if constexpr (MODE == RG_DUAL) {
+      const DenseArgs& a = args.d;
+      const int o = m0 + 16 * wm + 4 * lg;
+      if (o >= a.d_out) continue;
+      half_t hv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) hv[v] = (half_t)(silu_f(acc[0][j][v]) * acc[1][j][v]);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<half_t*>(a.out_h) + (size_t)n * a.d_out + o) =
+          __builtin_bit_cast(u32x2, hv);
+    } else {
+      const DenseArgs& a = args.d;
+      float* out = a.out_f + (size_t)blockIdx.z * a.T * a.d_out;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int o = m0 + 16 * (wm + 4 * i) + 4 * lg;
+        if (o >= a.d_out) continue;
+        *reinterpret_cast<f32x4*>(out + (size_t)n * a.d_out + o) = acc[i][j];
       }
     }
   }
@@ -150,14 +326,30 @@ void launch_colproj_reduce(const ColArgs* a, int nproj, hipStream_t s) {
 }
 
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act, hipStream_t s) {
-  (void)rt;                      // 64-row tiles
-  ColArgs2 args;
+  (void)rt;                      // 128-row tiles
+  RgArgs args{};
   args.c[0] = a[0];
   args.c[1] = a[nproj > 1 ? 1 : 0];
-  const dim3 grid(max_tiles, a[0].nsplit, nproj);
-  if (act == ACT_F16) hipLaunchKernelGGL((colproj_kernel<half_t>), grid, dim3(256), 0, s, args);
-  else hipLaunchKernelGGL((colproj_kernel<__bf16>), grid, dim3(256), 0, s, args);
+  args.ntiles = max_tiles;
+  const dim3 grid((unsigned)(((max_tiles + 7) / 8) * 8), 1, nproj);
+  if (act == ACT_F16) hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_COL>), grid, dim3(64 * RG_WAVES), 0, s, args);
+  else hipLaunchKernelGGL((rowgemm_kernel<__bf16, RG_COL>), grid, dim3(64 * RG_WAVES), 0, s, args);
   launch_colproj_reduce(a, nproj, s);
+}
+
+void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s) {
+  RgArgs args{};
+  args.d = a;
+  args.nsplit = dual ? 1 : nsplit;
+  args.ntiles = (a.T + 127) / 128;
+  const unsigned gx = (unsigned)(((args.ntiles + 7) / 8) * 8);
+  if (dual) {
+    const dim3 grid(gx, (a.d_out + 63) / 64, 1);
+    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_DUAL>), grid, dim3(64 * RG_WAVES), 0, s, args);
+  } else {
+    const dim3 grid(gx, (a.d_out + 127) / 128, args.nsplit);
+    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_PLAIN>), grid, dim3(64 * RG_WAVES), 0, s, args);
+  }
 }
 
 }  // namespace tq

@@ -1,5 +1,4 @@
-// Combine stage of the fused forward for down / single projections, and the
-// dense fp16 shared expert.
+// Combine stage of the fused forward for down / single projections.
 //
 // "TileQ" technical summary, section 2.2: routing weights are applied to the
 // rank-space projections of the active tiles and accumulated in place
@@ -102,7 +101,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (int c = 0; c < a.nks; ++c)
       v += *reinterpret_cast<const f32x4*>(a.dres + ((size_t)c * a.S + pos) * a.d_out + o);
   }
-  if (a.ys) v += *reinterpret_cast<const f32x4*>(a.ys + (size_t)t * a.d_out + o);
+  if (a.ys)
+    for (int c = 0; c < a.nys; ++c)
+      v += *reinterpret_cast<const f32x4*>(a.ys + ((size_t)c * a.T + t) * a.d_out + o);
   YT* y = reinterpret_cast<YT*>(a.y) + (size_t)t * a.d_out + o;
   if constexpr (__is_same(YT, float)) {
     *reinterpret_cast<f32x4*>(y) = v;
@@ -125,92 +126,6 @@ void launch_combine(const CombineArgs& a, Act act, hipStream_t s) {
     else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<__bf16, __bf16>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((combine_kernel<__bf16, float>), grid, dim3(256), 0, s, a);
   }
-}
-
-// ---- dense fp16 shared expert (applied to every token, weight 1) ----------
-// Tile: 16*BMF tokens x 64*RF output rows; A operand = weight rows read
-// directly (16 B per lane per k-step), B operand = token activations staged in
-// LDS.  DUAL: gate and up weights together, epilogue h = RND_f16(silu(g)*u).
-constexpr int DKS = 4;
-constexpr int DLD = DKS * 32 + 8;
-
-template <int DUAL, int BMF, int RF>
-__global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
-  constexpr int NP = DUAL ? 2 : 1;
-  constexpr int BMS = 16 * BMF;
-  __shared__ __attribute__((aligned(16))) half_t s_x[BMS * DLD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int t0 = blockIdx.x * BMS;
-  const int o_w = blockIdx.y * (64 * RF) + wave * (16 * RF);
-  f32x4 acc[NP][RF][BMF];
-#pragma unroll
-  for (int p = 0; p < NP; ++p)
-#pragma unroll
-    for (int r = 0; r < RF; ++r)
-#pragma unroll
-      for (int f = 0; f < BMF; ++f) acc[p][r][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool rvalid[RF];
-#pragma unroll
-  for (int r = 0; r < RF; ++r) rvalid[r] = (o_w + 16 * r) < a.d_out;
-  const half_t* W[2] = {reinterpret_cast<const half_t*>(a.W0),
-                        reinterpret_cast<const half_t*>(DUAL ? a.W1 : a.W0)};
-  const int nsteps = a.d_in >> 5;
-  for (int st = 0; st < nsteps; st += DKS) {
-    __syncthreads();
-    for (int i = tid; i < BMS * 16; i += 256) {
-      const int row = i >> 4, c = i & 15;
-      const int t = t0 + row;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (t < a.T)
-        v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const half_t*>(a.X) +
-                                            (size_t)t * a.d_in + st * 32 + 8 * c);
-      *reinterpret_cast<u32x4*>(&s_x[row * DLD + 8 * c]) = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < DKS; ++j) {
-      half8v bf[BMF];
-#pragma unroll
-      for (int f = 0; f < BMF; ++f)
-        bf[f] = *reinterpret_cast<const half8v*>(&s_x[(16 * f + l16) * DLD + j * 32 + 8 * lg]);
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int r = 0; r < RF; ++r) {
-          if (!rvalid[r]) continue;
-          const half8v av = *reinterpret_cast<const half8v*>(
-              W[p] + (size_t)(o_w + 16 * r + l16) * a.d_in + (st + j) * 32 + 8 * lg);
-#pragma unroll
-          for (int f = 0; f < BMF; ++f) acc[p][r][f] = mfma16(av, bf[f], acc[p][r][f]);
-        }
-    }
-  }
-#pragma unroll
-  for (int f = 0; f < BMF; ++f) {
-    const int t = t0 + 16 * f + l16;
-    if (t >= a.T) continue;
-#pragma unroll
-    for (int r = 0; r < RF; ++r) {
-      if (!rvalid[r]) continue;
-      const int o = o_w + 16 * r + 4 * lg;
-      if constexpr (DUAL) {
-        half_t hv[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) hv[v] = (half_t)(silu_f(acc[0][r][f][v]) * acc[NP - 1][r][f][v]);
-        *reinterpret_cast<u32x2*>(reinterpret_cast<half_t*>(a.out_h) + (size_t)t * a.d_out + o) =
-            __builtin_bit_cast(u32x2, hv);
-      } else {
-        *reinterpret_cast<f32x4*>(a.out_f + (size_t)t * a.d_out + o) = acc[0][r][f];
-      }
-    }
-  }
-}
-
-void launch_dense(const DenseArgs& a, int dual, hipStream_t s) {
-  const dim3 grid((a.T + 63) / 64, (a.d_out + 127) / 128);
-  if (dual) hipLaunchKernelGGL((dense_kernel<1, 4, 2>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((dense_kernel<0, 4, 2>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace tq

@@ -101,6 +101,7 @@ struct Plan {
   size_t zero_base;              // region zeroed by the route kernel (unused: 0 words)
   int zero_n;
   size_t ex, h, dres, hs, ys;
+  int nys;                       // k-split slabs of the shared expert's down output
   size_t x16, ex_h16, h16;       // prefill, bfloat16 activations
   size_t xp, sums_x, ex_x, hp, sums_h, ex_h;   // decode activation preparation
   size_t total;
@@ -209,7 +210,7 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.S = T * k;
   p.path = path;
   p.bm_gemm = (path == 1) ? 16 : 128;
-  p.rt_col = (path == 1) ? 16 : 64;
+  p.rt_col = (path == 1) ? 16 : 128;
   p.max_tiles_gemm = (p.S + p.bm_gemm - 1) / p.bm_gemm + L->K;
   p.max_col_tiles = (p.S + p.rt_col - 1) / p.rt_col + 32 + L->K;
   // decode: the column stage of the input projection(s) covers every
@@ -274,9 +275,15 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   proj_dims(L, nproj(L) - 1, &d_in_last, &d_out_last);
   p.nks = (path == 1) ? choose_nks(L, nproj(L) - 1, S) : 1;
   p.dres = take((size_t)p.nks * S * d_out_last * sizeof(float));
+  p.nys = 1;
   if (L->shared.d_ff > 0) {
+    // shared down projection: k-splits until the grid has about one
+    // workgroup per CU, each split keeping at least 8 stages of 64 inputs
+    const long tiles = (long)(L->d_model / 128) * ((T + 127) / 128);
+    const int nst = L->shared.d_ff / 64;
+    while (p.nys < 16 && tiles * p.nys * 2 <= device_cus() && nst / (2 * p.nys) >= 8) p.nys *= 2;
     p.hs = take((size_t)T * L->shared.d_ff * 2);
-    p.ys = take((size_t)T * L->d_model * sizeof(float));
+    p.ys = take((size_t)p.nys * T * L->d_model * sizeof(float));
   }
   if (path == 1) {
     const ProjDev& d0 = L->proj[0].dev;
@@ -768,7 +775,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       da.W0 = L->shared.wg;
       da.W1 = L->shared.wu;
       da.out_h = at<void>(ws, p.hs);
-      launch_dense(da, 1, s);
+      launch_dense(da, 1, 1, s);
       DenseArgs db{};
       db.T = T;
       db.d_in = L->shared.d_ff;
@@ -776,7 +783,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       db.X = at<void>(ws, p.hs);
       db.W0 = L->shared.wd;
       db.out_f = at<float>(ws, p.ys);
-      launch_dense(db, 0, s);
+      launch_dense(db, 0, p.nys, s);
       ys = at<float>(ws, p.ys);
     }
     mark(6);
@@ -866,6 +873,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     cb.nks = p.nks;
     cb.S = p.S;
     cb.ys = ys;
+    cb.nys = p.nys;
     cb.y = y;
     cb.y_dtype = (int)y_dtype;
     launch_combine(cb, act, s);

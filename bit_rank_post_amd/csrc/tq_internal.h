@@ -96,6 +96,7 @@ struct ColArgs {
   int ap_T;                      // > 0: every (column, token) pair, row = n * ap_T + t
                                  // (no work lists; seg_off/tile_off/row_src unused)
 };
+// prefill column stage (ap_T == 0): tiles of 128 rows (route rt_col 128)
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
                     hipStream_t s);
 // split-K reduction of the column stage: slab 0 += slabs 1..nsplit-1
@@ -200,7 +201,8 @@ struct CombineArgs {
   const void* U;
   const float* dres;             // [nks][S][d_out]
   int nks, S;
-  const float* ys;               // shared expert output [T][d_out] f32 or nullptr
+  const float* ys;               // shared expert output [nys][T][d_out] f32 slabs or nullptr
+  int nys;
   void* y;
   int y_dtype;                   // 0 f16, 1 bf16, 2 f32
 };
@@ -215,7 +217,9 @@ struct DenseArgs {
   void* out_h;                   // dual: [T][d_out] f16
   float* out_f;                  // single: [T][d_out] f32
 };
-void launch_dense(const DenseArgs& a, int dual, hipStream_t s);
+// dual: SwiGLU input (W0 gate, W1 up) -> out_h; else fp32 out_f in nsplit
+// k-split slabs [nsplit][T][d_out]
+void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s);
 
 // ---- upload-time kernels --------------------------------------------------
 void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, int d_in,
