@@ -10,34 +10,49 @@
 //     l_t = sum_m U_m S[t][m]           (one GEMM with K = M * r),
 // to which the gated residual outputs of the token's slots are added:
 //     y_t = sum_j dres[pos(t, j)] + l_t (+ shared expert).
-// S is built in LDS per 16-token tile and grid row (split into a high and a
-// low part in the activation dtype for the MFMA), never in HBM.
+// S is built in LDS per 16-token tile (split into a high and a low part in
+// the activation dtype for the MFMA), never in HBM.
 #include "tq_device.h"
 
 namespace tq {
 
+// Workgroup: 16 tokens x a range of output chunks (64 outputs, 16 per wave).
+// The rank-space vectors S[t][m] of the grid rows m active in the tile are
+// built once in LDS (high and low parts) when they fit CB_LDS bytes, then
+// every chunk of the range runs its MFMAs against them; otherwise they are
+// rebuilt per chunk and grid row.
+constexpr int CB_KMAX = 32;                 // slots per token
+constexpr int CB_MMAX = 1024;               // grid rows
+constexpr int CB_LDS = 64 * 1024;           // resident S budget (dynamic LDS, at most)
+
 template <typename T, typename YT>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int cpw, int lds_bytes) {
   typedef typename Vec8<T>::type V8;
-  constexpr int SLD = 128 + 8;
-  constexpr int KMAX = 32;
-  __shared__ __attribute__((aligned(16))) T s_hi[16 * SLD];
-  __shared__ __attribute__((aligned(16))) T s_lo[16 * SLD];
-  __shared__ int s_m[16 * KMAX];        // grid row of each slot's expert (-1: none)
-  __shared__ int s_row[16 * KMAX];      // row of P of each slot
-  __shared__ float s_g[16 * KMAX];      // routing weight of each slot
-  __shared__ int s_active;
+  constexpr int KR = 8;                     // slots per token held in registers
+  constexpr int UG = 8;                     // U fragments requested together
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
+  __shared__ int s_i[16 * CB_KMAX];         // active-row index of each slot (-1: none)
+  __shared__ int s_row[16 * CB_KMAX];       // row of P of each slot
+  __shared__ float s_g[16 * CB_KMAX];       // routing weight of each slot
+  __shared__ unsigned s_bits[CB_MMAX / 32];
+  __shared__ int s_base[CB_MMAX / 32];
+  __shared__ int s_ml[16 * CB_KMAX];        // active grid rows, ascending
+  __shared__ int s_nact;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int t0 = blockIdx.x * 16;
-  const int o_w = blockIdx.y * 64 + wave * 16;
-  const bool ovalid = o_w < a.d_out;
   const int k = a.topk;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int rp = a.r_pad;
+  const int SLD = rp + 8;
+  T* s_hi = reinterpret_cast<T*>(s_dyn);
 
-  if (a.r_pad > 0) {
-    const int rp = a.r_pad;
-    // per-slot data of the tile, once
+  int nact = 0;
+  bool resident = false;
+  if (rp > 0) {
+    for (int i = tid; i < CB_MMAX / 32; i += 256) s_bits[i] = 0u;
+    __syncthreads();
+    // per-slot data of the tile, once (s_i holds the grid row until the
+    // active rows are numbered)
     for (int i = tid; i < 16 * k; i += 256) {
       const int tt = i / k, j = i - tt * k;
       const int t = t0 + tt;
@@ -50,81 +65,227 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
           m = a.m_of[e];
           row = (a.ap_T > 0) ? a.n_of[e] * a.ap_T + t : a.prow[s];
           g = a.gates[s];
+          atomicOr(&s_bits[m >> 5], 1u << (m & 31));
         }
       }
-      s_m[tt * KMAX + j] = m;
-      s_row[tt * KMAX + j] = row;
-      s_g[tt * KMAX + j] = g;
+      s_i[tt * CB_KMAX + j] = m;
+      s_row[tt * CB_KMAX + j] = row;
+      s_g[tt * CB_KMAX + j] = g;
     }
-    for (int m = 0; m < a.M; ++m) {
-      __syncthreads();
-      if (tid == 0) {
-        int any = 0;
-        for (int i = 0; i < 16 * k && !any; ++i) any = (s_m[(i / k) * KMAX + i % k] == m);
-        s_active = any;
-      }
-      __syncthreads();
-      if (!s_active) continue;
-      // S[t][m][:] = sum_{j : row(e_tj) = m} g_tj (Sigma p_tj), split hi + lo
-      for (int i = tid; i < 16 * rp; i += 256) {
-        const int tt = i / rp, c = i - tt * rp;
-        float v = 0.f;
-        for (int j = 0; j < k; ++j)
-          if (s_m[tt * KMAX + j] == m)
-            v += s_g[tt * KMAX + j] * a.P[(size_t)s_row[tt * KMAX + j] * rp + c];
-        const T hi = from_f32<T>(v);
-        s_hi[tt * SLD + c] = hi;
-        s_lo[tt * SLD + c] = from_f32<T>(v - to_f32(hi));
-      }
-      __syncthreads();
-      if (ovalid) {
-        const T* up = reinterpret_cast<const T*>(a.U) +
-                      ((size_t)m * a.d_out + o_w + l16) * rp + 8 * lg;
-        for (int s2 = 0; s2 < rp; s2 += 32) {
-          const V8 av = *reinterpret_cast<const V8*>(up + s2);
-          const V8 bh = *reinterpret_cast<const V8*>(&s_hi[l16 * SLD + s2 + 8 * lg]);
-          const V8 bl = *reinterpret_cast<const V8*>(&s_lo[l16 * SLD + s2 + 8 * lg]);
-          acc = mfma16(av, bh, acc);
-          acc = mfma16(av, bl, acc);
-        }
+    __syncthreads();
+    // active grid rows in ascending order (wave 0, one bitmap word per lane)
+    static_assert(CB_MMAX / 32 <= 64, "bitmap words fit one wave");
+    if (wave == 0) {
+      const unsigned wd = (lane < CB_MMAX / 32) ? s_bits[lane] : 0u;
+      const int c = __popc(wd);
+      const int inc = wave_incl_scan_i(c, lane);
+      int pos = inc - c;
+      if (lane < CB_MMAX / 32) s_base[lane] = pos;
+      for (unsigned w = wd; w; w &= w - 1) s_ml[pos++] = lane * 32 + __ffs(w) - 1;
+      if (lane == 63) s_nact = inc;
+    }
+    __syncthreads();
+    nact = s_nact;
+    resident = (size_t)nact * 16 * SLD * 2 * sizeof(T) <= (size_t)lds_bytes;
+    for (int i = tid; i < 16 * k; i += 256) {
+      const int tt = i / k, j = i - tt * k;
+      const int m = s_i[tt * CB_KMAX + j];
+      if (m >= 0) {
+        const unsigned below = s_bits[m >> 5] & ((1u << (m & 31)) - 1u);
+        s_i[tt * CB_KMAX + j] = s_base[m >> 5] + __popc(below);
       }
     }
+    __syncthreads();
   }
-  if (!ovalid) return;
-  const int t = t0 + l16;
-  if (t >= a.T) return;
-  const int o = o_w + 4 * lg;
-  f32x4 v = acc;
-  for (int j = 0; j < k; ++j) {
-    const int pos = a.inv[t * k + j];
-    if (pos < 0) continue;
-    for (int c = 0; c < a.nks; ++c)
-      v += *reinterpret_cast<const f32x4*>(a.dres + ((size_t)c * a.S + pos) * a.d_out + o);
-  }
-  if (a.ys)
-    for (int c = 0; c < a.nys; ++c)
-      v += *reinterpret_cast<const f32x4*>(a.ys + ((size_t)c * a.T + t) * a.d_out + o);
-  YT* y = reinterpret_cast<YT*>(a.y) + (size_t)t * a.d_out + o;
-  if constexpr (__is_same(YT, float)) {
-    *reinterpret_cast<f32x4*>(y) = v;
-  } else {
-    YT r[4];
+  // S[t][m_i][:] = sum_{j : row(e_tj) = m_i} g_tj (Sigma p_tj) for active rows
+  // i0 <= i < i1 (LDS block i - i0), split into high and low parts.  Item =
+  // (token, 4 ranks): the token's slot vectors are requested together, then
+  // summed per active row.
+  auto build = [&](int i0, int i1) {
+    T* s_lo = s_hi + (size_t)(i1 - i0) * 16 * SLD;
+    const int nc4 = rp >> 2;
+    for (int q = tid; q < 16 * nc4; q += 256) {
+      const int tt = q / nc4, c = 4 * (q - tt * nc4);
+      if (k <= KR) {
+        f32x4 pv[KR];
+        int ij[KR];
+        float gj[KR];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = from_f32<YT>(v[q]);
-    *reinterpret_cast<u32x2*>(y) = __builtin_bit_cast(u32x2, r);
+        for (int j = 0; j < KR; ++j) {
+          ij[j] = (j < k) ? s_i[tt * CB_KMAX + j] : -1;
+          gj[j] = (j < k) ? s_g[tt * CB_KMAX + j] : 0.f;
+          pv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (ij[j] >= i0 && ij[j] < i1)
+            pv[j] = *reinterpret_cast<const f32x4*>(a.P + (size_t)s_row[tt * CB_KMAX + j] * rp + c);
+        }
+        for (int i = i0; i < i1; ++i) {
+          f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < KR; ++j)
+            if (ij[j] == i) v += gj[j] * pv[j];
+          T hi[4], lo[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            hi[u] = from_f32<T>(v[u]);
+            lo[u] = from_f32<T>(v[u] - to_f32(hi[u]));
+          }
+          const int o = ((i - i0) * 16 + tt) * SLD + c;
+          *reinterpret_cast<u32x2*>(&s_hi[o]) = __builtin_bit_cast(u32x2, hi);
+          *reinterpret_cast<u32x2*>(&s_lo[o]) = __builtin_bit_cast(u32x2, lo);
+        }
+      } else {
+        for (int i = i0; i < i1; ++i) {
+          f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < k; ++j)
+            if (s_i[tt * CB_KMAX + j] == i)
+              v += s_g[tt * CB_KMAX + j] *
+                   *reinterpret_cast<const f32x4*>(a.P + (size_t)s_row[tt * CB_KMAX + j] * rp + c);
+          T hi[4], lo[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            hi[u] = from_f32<T>(v[u]);
+            lo[u] = from_f32<T>(v[u] - to_f32(hi[u]));
+          }
+          const int o = ((i - i0) * 16 + tt) * SLD + c;
+          *reinterpret_cast<u32x2*>(&s_hi[o]) = __builtin_bit_cast(u32x2, hi);
+          *reinterpret_cast<u32x2*>(&s_lo[o]) = __builtin_bit_cast(u32x2, lo);
+        }
+      }
+    }
+  };
+  // MFMAs of active rows i0 <= i < i1 for output rows o_w .. o_w + 15; the
+  // U fragments (one per active row and 32 ranks) are requested UG at a time
+  auto lowrank = [&](int i0, int i1, int o_w, f32x4& acc) {
+    const T* s_lo = s_hi + (size_t)(i1 - i0) * 16 * SLD;
+    const int nf = (i1 - i0) * (rp >> 5);
+    int fi = i0, fs = 0;                    // (active row, rank offset) of fragment f0
+    for (int f0 = 0; f0 < nf; f0 += UG) {
+      V8 uf[UG];
+      int bo[UG];
+      int ci = fi, cs = fs;
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        if (f0 + u < nf) {
+          uf[u] = *reinterpret_cast<const V8*>(reinterpret_cast<const T*>(a.U) +
+                                               ((size_t)s_ml[ci] * a.d_out + o_w + l16) * rp +
+                                               cs + 8 * lg);
+          bo[u] = ((ci - i0) * 16 + l16) * SLD + cs + 8 * lg;
+        }
+        cs += 32;
+        if (cs == rp) {
+          cs = 0;
+          ++ci;
+        }
+      }
+      fi = ci;
+      fs = cs;
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        if (f0 + u < nf) {
+          const V8 bh = *reinterpret_cast<const V8*>(&s_hi[bo[u]]);
+          const V8 bl = *reinterpret_cast<const V8*>(&s_lo[bo[u]]);
+          acc = mfma16(uf[u], bh, acc);
+          acc = mfma16(uf[u], bl, acc);
+        }
+      }
+    }
+  };
+  if (resident && nact > 0) {
+    build(0, nact);
+    __syncthreads();
+  }
+
+  const int nch = (a.d_out + 63) >> 6;
+  const int c0 = blockIdx.y * cpw, c1 = min(nch, c0 + cpw);
+  const int t = t0 + l16;
+  // positions of the token's slots (constant over the chunks)
+  int pj[KR];
+#pragma unroll
+  for (int j = 0; j < KR; ++j) pj[j] = (t < a.T && j < k) ? a.inv[t * k + j] : -1;
+  for (int ch = c0; ch < c1; ++ch) {
+    const int o_w = ch * 64 + wave * 16;
+    const bool ovalid = o_w < a.d_out;
+    const int o = o_w + 4 * lg;
+    // residual outputs of the token's slots and the shared expert, requested
+    // before the MFMAs
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ovalid && t < a.T) {
+      if (k <= KR) {
+        f32x4 dv[KR];
+#pragma unroll
+        for (int j = 0; j < KR; ++j) {
+          dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (pj[j] >= 0) dv[j] = *reinterpret_cast<const f32x4*>(a.dres + (size_t)pj[j] * a.d_out + o);
+        }
+        for (int c = 1; c < a.nks; ++c)
+#pragma unroll
+          for (int j = 0; j < KR; ++j)
+            if (pj[j] >= 0)
+              dv[j] += *reinterpret_cast<const f32x4*>(a.dres + ((size_t)c * a.S + pj[j]) * a.d_out + o);
+#pragma unroll
+        for (int j = 0; j < KR; ++j) v += dv[j];
+      } else {
+        for (int j = 0; j < k; ++j) {
+          const int pos = a.inv[t * k + j];
+          if (pos < 0) continue;
+          for (int c = 0; c < a.nks; ++c)
+            v += *reinterpret_cast<const f32x4*>(a.dres + ((size_t)c * a.S + pos) * a.d_out + o);
+        }
+      }
+      if (a.ys)
+        for (int c = 0; c < a.nys; ++c)
+          v += *reinterpret_cast<const f32x4*>(a.ys + ((size_t)c * a.T + t) * a.d_out + o);
+    }
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (resident) {
+      if (ovalid) lowrank(0, nact, o_w, acc);
+    } else {
+      for (int i = 0; i < nact; ++i) {
+        __syncthreads();
+        build(i, i + 1);
+        __syncthreads();
+        if (ovalid) lowrank(i, i + 1, o_w, acc);
+      }
+    }
+    if (!ovalid || t >= a.T) continue;
+    v += acc;
+    YT* y = reinterpret_cast<YT*>(a.y) + (size_t)t * a.d_out + o;
+    if constexpr (__is_same(YT, float)) {
+      *reinterpret_cast<f32x4*>(y) = v;
+    } else {
+      YT r[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[q] = from_f32<YT>(v[q]);
+      *reinterpret_cast<u32x2*>(y) = __builtin_bit_cast(u32x2, r);
+    }
   }
 }
 
 void launch_combine(const CombineArgs& a, Act act, hipStream_t s) {
-  const dim3 grid((a.T + 15) / 16, (a.d_out + 63) / 64);
+  // output chunks per workgroup: about 4 workgroups per CU over the grid
+  const int tiles = (a.T + 15) / 16;
+  const int nch = (a.d_out + 63) / 64;
+  int os = (1024 + tiles - 1) / tiles;
+  os = os < 1 ? 1 : (os > nch ? nch : os);
+  const int cpw = (nch + os - 1) / os;
+  const dim3 grid(tiles, (nch + cpw - 1) / cpw);
+  // LDS: S of every grid row a tile can touch (min(M, 16 k)) if that fits
+  // CB_LDS, else one grid row at a time
+  size_t lds = 0;
+  if (a.r_pad > 0) {
+    const size_t per_row = (size_t)16 * (a.r_pad + 8) * 2 * 2;
+    const int rows = a.M < 16 * a.topk ? a.M : 16 * a.topk;
+    lds = (size_t)rows * per_row <= (size_t)CB_LDS ? (size_t)rows * per_row : per_row;
+  }
+  const int lb = (int)lds;
   if (act == ACT_F16) {
-    if (a.y_dtype == 0) hipLaunchKernelGGL((combine_kernel<half_t, half_t>), grid, dim3(256), 0, s, a);
-    else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<half_t, __bf16>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<half_t, float>), grid, dim3(256), 0, s, a);
+    if (a.y_dtype == 0) hipLaunchKernelGGL((combine_kernel<half_t, half_t>), grid, dim3(256), lds, s, a, cpw, lb);
+    else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<half_t, __bf16>), grid, dim3(256), lds, s, a, cpw, lb);
+    else hipLaunchKernelGGL((combine_kernel<half_t, float>), grid, dim3(256), lds, s, a, cpw, lb);
   } else {
-    if (a.y_dtype == 0) hipLaunchKernelGGL((combine_kernel<__bf16, half_t>), grid, dim3(256), 0, s, a);
-    else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<__bf16, __bf16>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<__bf16, float>), grid, dim3(256), 0, s, a);
+    if (a.y_dtype == 0) hipLaunchKernelGGL((combine_kernel<__bf16, half_t>), grid, dim3(256), lds, s, a, cpw, lb);
+    else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<__bf16, __bf16>), grid, dim3(256), lds, s, a, cpw, lb);
+    else hipLaunchKernelGGL((combine_kernel<__bf16, float>), grid, dim3(256), lds, s, a, cpw, lb);
   }
 }
 

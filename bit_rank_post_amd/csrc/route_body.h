@@ -11,6 +11,61 @@ namespace tq {
 // 1024) and takes its LDS from the caller: route_lds_ints(SMAX) ints.
 __host__ __device__ constexpr int route_lds_ints(int smax) { return 1024 + 257 + 257 + 17 + 4 * smax; }
 
+// Expert offsets, tile prefixes and active-expert records from the slot
+// counts s_tot[K], on one wave (4 experts per lane, K <= 256).  s_off[K+1]
+// and s_arank[K] (LDS copies for a later phase) may be nullptr.
+__device__ __forceinline__ void route_expert_offsets(const RouteArgs& a, const int* s_tot,
+                                                     int* s_off, int* s_arank, int lane) {
+  const int K = a.K;
+  int c[4], g[4], x[4], sc = 0, sg = 0, sx = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    c[q] = (e < K) ? s_tot[e] : 0;
+    g[q] = (c[q] + a.bm_gemm - 1) / a.bm_gemm;
+    x[q] = (c[q] + a.rt_col - 1) / a.rt_col;
+    sc += c[q];
+    sg += g[q];
+    sx += x[q];
+  }
+  int na = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) na += (c[q] > 0);
+  const int ic = wave_incl_scan_i(sc, lane), ig = wave_incl_scan_i(sg, lane),
+            ix = wave_incl_scan_i(sx, lane), ia = wave_incl_scan_i(na, lane);
+  int rc = ic - sc, rg = ig - sg, rx = ix - sx, ra = ia - na;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    if (e < K) {
+      a.cnt[e] = c[q];
+      a.off[e] = rc;
+      if (s_off) s_off[e] = rc;
+      a.tile_gemm[e] = rg;
+      a.tile_colx[e] = rx;
+      if (s_arank) s_arank[e] = (c[q] > 0) ? ra : -1;
+      if (a.arec && c[q] > 0) {
+        int* r = a.arec + ra * ROUTE_AREC;
+        r[0] = e;
+        r[1] = c[q];
+        r[2] = rc;
+      }
+    }
+    rc += c[q];
+    rg += g[q];
+    rx += x[q];
+    ra += (c[q] > 0);
+  }
+  if (a.arec && lane == 63) a.arec[K * ROUTE_AREC] = ia;   // number of active experts
+  const int tc = __shfl(ic, 63, 64), tgl = __shfl(ig, 63, 64), tx = __shfl(ix, 63, 64);
+  if (lane == 0) {
+    a.off[K] = tc;
+    if (s_off) s_off[K] = tc;
+    a.tile_gemm[K] = tgl;
+    a.tile_colx[K] = tx;
+  }
+}
+
 template <int SMAX, int NT>
 __device__ void route_block(const RouteArgs& a, int* lds) {
   constexpr int NW = NT / 64;
@@ -90,55 +145,7 @@ __device__ void route_block(const RouteArgs& a, int* lds) {
   }
   __syncthreads();
   // expert offsets and tile prefixes: wave 0, 4 experts per lane
-  if (wave == 0) {
-    int c[4], g[4], x[4], sc = 0, sg = 0, sx = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      c[q] = (e < K) ? s_tot[e] : 0;
-      g[q] = (c[q] + a.bm_gemm - 1) / a.bm_gemm;
-      x[q] = (c[q] + a.rt_col - 1) / a.rt_col;
-      sc += c[q];
-      sg += g[q];
-      sx += x[q];
-    }
-    int na = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) na += (c[q] > 0);
-    const int ic = wave_incl_scan_i(sc, lane), ig = wave_incl_scan_i(sg, lane),
-              ix = wave_incl_scan_i(sx, lane), ia = wave_incl_scan_i(na, lane);
-    int rc = ic - sc, rg = ig - sg, rx = ix - sx, ra = ia - na;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      if (e < K) {
-        a.cnt[e] = c[q];
-        a.off[e] = rc;
-        s_off[e] = rc;
-        a.tile_gemm[e] = rg;
-        a.tile_colx[e] = rx;
-        s_arank[e] = (c[q] > 0) ? ra : -1;
-        if (a.arec && c[q] > 0) {
-          int* r = a.arec + ra * ROUTE_AREC;
-          r[0] = e;
-          r[1] = c[q];
-          r[2] = rc;
-        }
-      }
-      rc += c[q];
-      rg += g[q];
-      rx += x[q];
-      ra += (c[q] > 0);
-    }
-    if (a.arec && lane == 63) a.arec[K * ROUTE_AREC] = ia;   // number of active experts
-    const int tc = __shfl(ic, 63, 64), tgl = __shfl(ig, 63, 64), tx = __shfl(ix, 63, 64);
-    if (lane == 0) {
-      a.off[K] = tc;
-      s_off[K] = tc;
-      a.tile_gemm[K] = tgl;
-      a.tile_colx[K] = tx;
-    }
-  }
+  if (wave == 0) route_expert_offsets(a, s_tot, s_off, s_arank, lane);
   __syncthreads();
 
   // (C) positions

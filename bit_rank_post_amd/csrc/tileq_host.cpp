@@ -93,7 +93,7 @@ struct Plan {
   int nks;                       // k-chunks (fp32 slabs) of the last projection's residual
   int ap_T;                      // decode: column stage over all (column, token) pairs
   int col_tiles_x, col_tiles_down;   // decode column-stage tiles
-  size_t flags, cnt, off, perm, inv, etab, arec, tile_gemm, tile_colx, colmask, cntw, rank;
+  size_t flags, cnt, off, perm, inv, etab, arec, tile_gemm, tile_colx, colmask, cntw, rank, wgcnt, dropw;
   size_t col_off[2], col_tok[2], slot2col[2], tile_col[2];
   size_t P[3];
   int nsplit[3];
@@ -240,7 +240,9 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.arec = take(sizeof(int) * ((size_t)K * ROUTE_AREC + 1));
   p.tile_gemm = take(sizeof(int) * (K + 1));
   p.tile_colx = take(sizeof(int) * (K + 1));
-  p.colmask = take(sizeof(int) * std::max(T, 1));
+  p.colmask = take(sizeof(int) * 2 * std::max(T, 1));
+  p.wgcnt = take(sizeof(int) * 2 * 32 * ((S + 1023) / 1024 + 1));
+  p.dropw = take(sizeof(int) * ((S + 1023) / 1024 + 1));
   p.cntw = take(sizeof(int) * (size_t)((S + 63) / 64) * K);
   p.rank = take(sizeof(int) * S);
   const int ncol = (L->kind == TQ_SINGLE) ? 1 : 2;
@@ -351,6 +353,8 @@ void fill_route(const tq_layer* L, const Plan& p, const int* ids, void* ws, Rout
   r.cntw = at<int>(ws, p.cntw);
   r.rank = at<int>(ws, p.rank);
   r.colmask = at<int>(ws, p.colmask);
+  r.wgcnt = at<int>(ws, p.wgcnt);
+  r.dropw = at<int>(ws, p.dropw);
   r.zero_init = at<unsigned>(ws, p.zero_base);
   r.zero_n = p.zero_n;
 }

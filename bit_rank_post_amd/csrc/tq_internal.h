@@ -66,7 +66,9 @@ struct RouteArgs {
   int* tile_col[2];              // [N+1] prefix of ceil(col count/rt_col)
   int* cntw;                     // scratch [ceil(S/64)][K]
   int* rank;                     // scratch [S]
-  int* colmask;                  // scratch [T]
+  int* colmask;                  // scratch [2][T]
+  int* wgcnt;                    // scratch [2][ceil(S/1024)][32] (multi-workgroup path)
+  int* dropw;                    // scratch [ceil(S/1024)]
   unsigned* zero_init;           // optional region zeroed by the kernel
   int zero_n;
 };

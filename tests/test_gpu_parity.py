@@ -125,7 +125,11 @@ def test_route_bitexact_cases():
     cases = [rng.integers(0, 8, (64, 2)), np.full((40, 2), 5), np.array([[3, 3]]),
              np.array([[1, 1], [1, 2], [2, 1]]), rng.integers(0, 3, (300, 4)),
              np.array([[9, -2], [4, 8], [7, 7], [0, 100]]),           # dropped ids
-             rng.integers(0, 8, (16384, 2))]                          # T*k = 32768
+             rng.integers(0, 8, (16384, 2)),                          # T*k = 32768
+             rng.integers(0, 8, (65, 2)),                             # smallest multi-workgroup case
+             rng.integers(0, 8, (1025, 1)),                           # two slot workgroups, ragged
+             np.where(rng.random((2000, 3)) < 0.05, -1,               # dropped ids, repeats
+                      rng.integers(0, 9, (2000, 3)))]
     for ids in cases:
         say(f"  route case {ids.shape}")
         check_route_device(L8, p8, ids)
@@ -173,6 +177,9 @@ def test_special_cases_single(path):
         "zero_residual": pins.random_struct(8, 2, 4, 256, 64, 16, 64, seed=32, zero_res=True)[0],
         "textbook": pins.random_struct(1, 1, 1, 384, 48, 20, 128, seed=33)[0],
         "rank48_G32": pins.random_struct(6, 3, 3, 1408, 80, 48, 32, seed=34)[0],
+        # 32 grid rows at rank 128: the combine's rank-space tile does not
+        # fit LDS at once and is built one grid row at a time
+        "tall_grid_r128": pins.random_struct(32, 32, 1, 256, 64, 128, 64, seed=35)[0],
     }
     for name, p in cases.items():
         L = tqio.upload_layer(single_layer_from(p))
