@@ -77,10 +77,12 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   const char* wbase[2];
   uint32_t wbytes, wrs, wks;           // weight buffer size, row and k-step strides (bytes)
   int st0 = 0, st1;
-  const ColArgs* ca = nullptr;
+  // (a copy, not a pointer into the kernel arguments: the fields stay scalar)
+  ColArgs ca{};
   if constexpr (MODE == RG_COL) {
-    ca = &args.c[blockIdx.z];
-    const ColArgs& a = *ca;
+    if (blockIdx.z) ca = args.c[1];
+    else ca = args.c[0];
+    const ColArgs& a = ca;
     const int seg = find_segment(a.tile_off, a.nseg, tile, &s_res);
     if (seg < 0) return;
     n0 = a.seg_off[seg] + (tile - a.tile_off[seg]) * 128;
@@ -114,7 +116,8 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
     wrs = (uint32_t)d_in * 2u;
     wks = 64u;
     const int nst = d_in >> 6;
-    const int sps = (nst + args.nsplit - 1) / args.nsplit;
+    // (uniform: the division may be done in vector registers)
+    const int sps = __builtin_amdgcn_readfirstlane((nst + args.nsplit - 1) / args.nsplit);
     st0 = blockIdx.z * sps;
     st1 = min(nst, st0 + sps);
     if (tid < 128) {
@@ -126,8 +129,9 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   const int m0 = blockIdx.y * (MODE == RG_DUAL ? 64 : 128);
   __syncthreads();
   const int nv = min(128, n_end - n0);
-  const int row_lo = s_src[0];
-  const int row_hi = s_src[max(nv - 1, 0)];
+  // (uniform: the activation buffer resource lives in scalar registers)
+  const int row_lo = __builtin_amdgcn_readfirstlane(s_src[0]);
+  const int row_hi = __builtin_amdgcn_readfirstlane(s_src[max(nv - 1, 0)]);
 
   // per-lane offsets of this wave's loads: load q = wave * NI + i; q < 16:
   // weight fragment (k-step q / 8, fragment q % 8), else activation fragment
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
 
   auto issue = [&](int b, char* base) {
     const bool live = b < nstage;
-    const int st = st0 + (live ? b : 0);
+    const int st = __builtin_amdgcn_readfirstlane(st0 + (live ? b : 0));   // a scalar offset
 #pragma unroll
     for (int i = 0; i < RG_NI; ++i) {
       char* dst = base + (isw[i] ? RG_A : RG_B) + (ks_of[i] * 8 + fr_of[i]) * 1024;
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
     const int n = n0 + nl;
     if (nl >= nv) continue;
     if constexpr (MODE == RG_COL) {
-      const ColArgs& a = *ca;
+      const ColArgs& a = ca;
       T* PH = reinterpret_cast<T*>(a.P);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
