@@ -183,32 +183,29 @@ __device__ __forceinline__ void unpack16_frags(uint32_t D, u32x4& f0, u32x4& f1)
 // (q - z) c, and the product with s/c (exact: power-of-two scaling, |s| < 1024)
 // rounds the exact value (q - z) s once.
 struct DeqConst {
-  half2v nz64, nz16, nz4;   // -(1 + z/64), -(1 + z/16), -(1 + z/4)
-  half2v s64, s16, s4;      // 64 s, 16 s, 4 s
+  half2v k64, k16, k4;      // (c^-1 s, -(1 + z c)) for c = 1/64, 1/16, 1/4
 };
 
+// From the (s, z) word: (64 s, -(1 + z/64)) in one packed fma, then each
+// next class by (x/4, 4 y + 3); every value is exact (powers of two, z an
+// integer in 0..3, |64 s| <= 65504).  The scale lanes add -0, which keeps
+// the sign of a zero scale.
 __device__ __forceinline__ DeqConst deq_const(uint32_t szw) {
-  const half_t s = __builtin_bit_cast(half_t, (uint16_t)(szw & 0xFFFFu));
-  const half_t z = __builtin_bit_cast(half_t, (uint16_t)(szw >> 16));
-  const float sf = (float)s, zf = (float)z;
+  const half2v sz = __builtin_bit_cast(half2v, szw);
   DeqConst c;
-  const half_t a = (half_t)(-(1.0f + zf * 0.015625f));
-  const half_t b = (half_t)(-(1.0f + zf * 0.0625f));
-  const half_t d = (half_t)(-(1.0f + zf * 0.25f));
-  const half_t e = (half_t)(sf * 64.0f), f = (half_t)(sf * 16.0f), g = (half_t)(sf * 4.0f);
-  c.nz64 = half2v{a, a};
-  c.nz16 = half2v{b, b};
-  c.nz4 = half2v{d, d};
-  c.s64 = half2v{e, e};
-  c.s16 = half2v{f, f};
-  c.s4 = half2v{g, g};
+  c.k64 = __builtin_elementwise_fma(sz, half2v{(half_t)64.0f, (half_t)-0.015625f},
+                                    half2v{(half_t)-0.0f, (half_t)-1.0f});
+  c.k16 = __builtin_elementwise_fma(c.k64, half2v{(half_t)0.25f, (half_t)4.0f},
+                                    half2v{(half_t)-0.0f, (half_t)3.0f});
+  c.k4 = __builtin_elementwise_fma(c.k16, half2v{(half_t)0.25f, (half_t)4.0f},
+                                   half2v{(half_t)-0.0f, (half_t)3.0f});
   return c;
 }
 
-__device__ __forceinline__ uint32_t deq_pair(uint32_t m, half2v nz, half2v sc) {
+__device__ __forceinline__ uint32_t deq_pair(uint32_t m, half2v k) {
   half2v v = __builtin_bit_cast(half2v, m);
-  v = v + nz;        // exact
-  v = v * sc;        // one rounding of (q - z) s
+  v = v + half2v{k.y, k.y};   // exact
+  v = v * half2v{k.x, k.x};   // one rounding of (q - z) s
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -218,14 +215,14 @@ __device__ __forceinline__ void deq_dword(uint32_t D, const DeqConst& c0, const 
   uint32_t m[8];
   unpack16(D, m);
   u32x4 r0, r1;
-  r0[0] = deq_pair(m[0], c0.nz64, c0.s64);
-  r0[1] = deq_pair(m[1], c0.nz16, c0.s16);
-  r0[2] = deq_pair(m[2], c0.nz4, c0.s4);
-  r0[3] = deq_pair(m[3], c0.nz64, c0.s64);
-  r1[0] = deq_pair(m[4], c1.nz64, c1.s64);
-  r1[1] = deq_pair(m[5], c1.nz16, c1.s16);
-  r1[2] = deq_pair(m[6], c1.nz4, c1.s4);
-  r1[3] = deq_pair(m[7], c1.nz16, c1.s16);
+  r0[0] = deq_pair(m[0], c0.k64);
+  r0[1] = deq_pair(m[1], c0.k16);
+  r0[2] = deq_pair(m[2], c0.k4);
+  r0[3] = deq_pair(m[3], c0.k64);
+  r1[0] = deq_pair(m[4], c1.k64);
+  r1[1] = deq_pair(m[5], c1.k16);
+  r1[2] = deq_pair(m[6], c1.k4);
+  r1[3] = deq_pair(m[7], c1.k16);
   a0 = as_half8(r0);
   a1 = as_half8(r1);
 }
