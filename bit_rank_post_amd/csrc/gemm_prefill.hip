@@ -445,17 +445,20 @@ static void pre_launch(const GemmArgs& a, int max_tiles, hipStream_t s) {
   const int nrt = (a.d_out + rows_per_wg - 1) / rows_per_wg;
   GemmArgs b = a;
   if constexpr (pre_fits<NP, RF, NF, GS>()) {
-    b.ntq = max_tiles;
-    const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
-    hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS>), grid, block, 0, s, b);
-  } else {
-    // a 128-slot tile is twice a 64-slot tile: two units per tile
-    static_assert(NF == 8, "smaller tiles always fit");
-    b.tile_half = 1;
-    b.ntq = 2 * max_tiles;
-    const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
-    hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, 4, GS>), grid, block, 0, s, b);
+    if (!a.narrow) {
+      b.ntq = max_tiles;
+      const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
+      hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS>), grid, block, 0, s, b);
+      return;
+    }
   }
+  // a 128-slot tile as two 64-slot units (when the wide ring does not fit,
+  // or when experts hold few slots: half the MFMA work on padding)
+  static_assert(NF == 8, "smaller tiles always fit");
+  b.tile_half = 1;
+  b.ntq = 2 * max_tiles;
+  const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
+  hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, 4, GS>), grid, block, 0, s, b);
 }
 
 template <typename T, int MODE, int RF, int NF>

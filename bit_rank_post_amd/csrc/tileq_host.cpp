@@ -731,6 +731,8 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     ga.cnt = at<int>(ws, p.cnt);
     ga.tile_off = at<int>(ws, p.tile_gemm);
     ga.ex = ex;
+    // fewer than 64 slots per expert on average: 64-slot tiles
+    ga.narrow = (long)p.S < 64L * K ? 1 : 0;
     ga.p[0] = L->proj[0].dev;
     if (swiglu) {
       ga.p[1] = L->proj[1].dev;
@@ -844,6 +846,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       ga.p[0] = dd;
       ga.dres = dres;
       ga.gates = topk_w;
+      ga.narrow = (long)p.S < 64L * K ? 1 : 0;
       launch_gemm_prefill(ga, MODE_RES, act, p.max_tiles_gemm, s);
     }
   } else {

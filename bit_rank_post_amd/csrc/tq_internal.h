@@ -128,6 +128,7 @@ struct GemmArgs {
   float* dres;                   // RES: [S][d_out] f32 (gate weight applied)
   const float* gates;            // RES: topk weights [T*topk]
   int rows;                      // rows of A
+  int narrow;                    // host: few slots per expert, use 64-slot halves
   int tile_half;                 // set by the launcher: 64-slot halves of 128-slot tiles
   int ntq;                       // set by the launcher: slot-tile units of the grid
 };
