@@ -66,6 +66,10 @@ struct tq_layer {
   int d_model, d_ff, K;
   ProjHost proj[3];
   SharedDev shared{};
+  // the shared expert runs on a second stream of the layer's device, forked
+  // from and joined back into the forward's stream by events
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   int path_override = 0;
   // stage timing (benchmark hook)
   bool prof = false;
@@ -584,6 +588,11 @@ tq_status tq_upload_shared_expert(tq_layer* L, int32_t d_ff_shared, const void* 
     (void)hipFree(L->shared.wd);
   }
   L->shared = sd;
+  if (!L->side) {
+    HIPCHK(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
+    HIPCHK(hipEventCreateWithFlags(&L->fork_ev, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&L->join_ev, hipEventDisableTiming));
+  }
   return TQ_OK;
 }
 
@@ -627,6 +636,33 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   auto mark = [&](int i) {
     if (L->prof) (void)hipEventRecord(L->ev[i], s);
   };
+  // (a6) dense shared expert on the layer's side stream: it reads only x
+  // and writes only its own buffers, so it overlaps the routed path; the
+  // combine waits for it
+  float* ys = nullptr;
+  if (L->shared.d_ff > 0) {
+    HIPCHK(hipEventRecord(L->fork_ev, s));
+    HIPCHK(hipStreamWaitEvent(L->side, L->fork_ev, 0));
+    DenseArgs da{};
+    da.T = T;
+    da.d_in = L->d_model;
+    da.d_out = L->shared.d_ff;
+    da.X = x;
+    da.W0 = L->shared.wg;
+    da.W1 = L->shared.wu;
+    da.out_h = at<void>(ws, p.hs);
+    launch_dense(da, 1, 1, L->side);
+    DenseArgs db{};
+    db.T = T;
+    db.d_in = L->shared.d_ff;
+    db.d_out = L->d_model;
+    db.X = at<void>(ws, p.hs);
+    db.W0 = L->shared.wd;
+    db.out_f = at<float>(ws, p.ys);
+    launch_dense(db, 0, p.nys, L->side);
+    HIPCHK(hipEventRecord(L->join_ev, L->side));
+    ys = at<float>(ws, p.ys);
+  }
   // (a1) routing / grouping
   mark(0);
   RouteArgs ra;
@@ -751,7 +787,6 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     }
   }
   mark(4);
-  float* ys = nullptr;
   if (swiglu) {
     const ProjDev& dd = L->proj[2].dev;
     // (a2) column stage of down: one row per slot (decode: one launch with
@@ -771,27 +806,8 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       launch_colproj(&ca, 1, p.rt_col, p.max_col_tiles, act, s);
     }
     mark(5);
-    // (a6) dense shared expert
-    if (L->shared.d_ff > 0) {
-      DenseArgs da{};
-      da.T = T;
-      da.d_in = L->d_model;
-      da.d_out = L->shared.d_ff;
-      da.X = x;
-      da.W0 = L->shared.wg;
-      da.W1 = L->shared.wu;
-      da.out_h = at<void>(ws, p.hs);
-      launch_dense(da, 1, 1, s);
-      DenseArgs db{};
-      db.T = T;
-      db.d_in = L->shared.d_ff;
-      db.d_out = L->d_model;
-      db.X = at<void>(ws, p.hs);
-      db.W0 = L->shared.wd;
-      db.out_f = at<float>(ws, p.ys);
-      launch_dense(db, 0, p.nys, s);
-      ys = at<float>(ws, p.ys);
-    }
+    // (a6) dense shared expert: launched on the side stream at the start of
+    // the forward (below); the combine waits for it
     mark(6);
     // (a4) residual GEMM of down
     if (dec) {
@@ -855,6 +871,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   }
   mark(7);
   // (a3 rank-space part + a5) combine
+  if (L->shared.d_ff > 0) HIPCHK(hipStreamWaitEvent(s, L->join_ev, 0));
   {
     const int q = swiglu ? 2 : 0;
     const ProjDev& d = L->proj[q].dev;
@@ -923,6 +940,9 @@ tq_status tq_layer_destroy(tq_layer* L) {
     (void)hipFree(L->shared.wu);
     (void)hipFree(L->shared.wd);
   }
+  if (L->side) (void)hipStreamDestroy(L->side);
+  if (L->fork_ev) (void)hipEventDestroy(L->fork_ev);
+  if (L->join_ev) (void)hipEventDestroy(L->join_ev);
   delete L;
   return TQ_OK;
 }

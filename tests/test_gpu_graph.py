@@ -21,7 +21,8 @@ def gpu():
 
 
 @pytest.mark.parametrize("which,T,path", [("tiny", 64, 1), ("tiny", 64, 2),
-                                          ("swiglu", 24, 1), ("swiglu", 300, 2)])
+                                          ("swiglu", 24, 1), ("swiglu", 300, 2),
+                                          ("shared", 24, 1), ("shared", 300, 2)])
 def test_graph_replay_matches_eager(which, T, path):
     if which == "tiny":
         cfg = synth.CONFIG_BY_NAME["tiny"]
@@ -30,6 +31,10 @@ def test_graph_replay_matches_eager(which, T, path):
         act, d_out = cfg.act, cfg.d_ff
     else:
         layer = small_swiglu("f16", 3)
+        if which == "shared":
+            # the shared expert runs on the layer's second stream: the capture
+            # must follow the fork and the join
+            layer["shared"] = synth.make_shared(256, 384, np.random.SeedSequence(11))
         x, ids, g = synth.make_custom_tokens(256, 8, 2, T, "f16", seed=5)
         act, d_out = "f16", 256
     L = tqio.upload_layer(layer)

@@ -228,6 +228,18 @@ def test_small_swiglu(act, path):
         assert_parity(y, R.forward(layer, x, ids, g), what=f"swiglu {act} path={path} T={T}")
 
 
+@pytest.mark.parametrize("path,T", [(1, 24), (2, 300)])
+def test_small_swiglu_with_shared_expert(path, T):
+    """The shared expert (on the layer's second stream) at decode and prefill."""
+    layer = small_swiglu("f16", 9)
+    layer["shared"] = synth.make_shared(256, 384, np.random.SeedSequence(12))
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    x, ids, g = synth.make_custom_tokens(256, 8, 2, T, "f16", seed=T + 1)
+    y, _ = run_forward(L, x, ids, g, "f16", "f32")
+    assert_parity(y, R.forward(layer, x, ids, g), what=f"swiglu + shared path={path} T={T}")
+
+
 def test_qwen15_prefill512_with_shared_expert():
     cfg = synth.CONFIG_BY_NAME["qwen15_moe_prefill512"]
     layer = synth.make_layer(cfg)
