@@ -123,49 +123,101 @@ __global__ __launch_bounds__(RM_NT) void route_scan_kernel(RouteArgs a, int nb) 
     d = wave_sum_i(d);
     if (lane == 0) a.flags[0] = d;
   }
-  // (B) per expert, exclusive prefix of the chunk counts over chunks: one
-  //     wave per expert, lanes own contiguous chunk ranges (loads in
-  //     independent batches of 8)
+  // (B) per expert, exclusive prefix of the chunk counts over chunks: a wave
+  //     per expert, lanes own contiguous chunk ranges.  A wave takes its
+  //     experts EB at a time with every load of the batch in flight at once
+  //     and the values kept for the second pass (up to 8 chunks per lane).
+  constexpr int EB = 4, CH = 8;
   const int seglen = (W + 63) >> 6;
-  for (int e = wave; e < K; e += NW) {
-    const int w0 = lane * seglen, w1 = min(W, w0 + seglen);
-    int sum = 0;
-    for (int wb = w0; wb < w1; wb += 8) {
-      int v[8];
+  if (seglen <= CH) {
+    for (int e0 = wave * EB; e0 < K; e0 += NW * EB) {
+      int v[EB][CH];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (wb + u < w1) ? a.cntw[(size_t)(wb + u) * K + e] : 0;
+      for (int q = 0; q < EB; ++q)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += v[u];
-    }
-    const int inc = wave_incl_scan_i(sum, lane);
-    int run = inc - sum;
-    for (int wb = w0; wb < w1; wb += 8) {
-      int v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (wb + u < w1) ? a.cntw[(size_t)(wb + u) * K + e] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (wb + u < w1) {
-          a.cntw[(size_t)(wb + u) * K + e] = run;
-          run += v[u];
+        for (int u = 0; u < CH; ++u) {
+          const int w = lane * seglen + u;
+          v[q][u] = (e0 + q < K && u < seglen && w < W) ? a.cntw[(size_t)w * K + e0 + q] : 0;
         }
+#pragma unroll
+      for (int q = 0; q < EB; ++q) {
+        int sum = 0;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) sum += v[q][u];
+        const int inc = wave_incl_scan_i(sum, lane);
+        int run = inc - sum;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          const int w = lane * seglen + u;
+          if (e0 + q < K && u < seglen && w < W) a.cntw[(size_t)w * K + e0 + q] = run;
+          run += v[q][u];
+        }
+        if (lane == 63 && e0 + q < K) s_tot[e0 + q] = inc;
+      }
     }
-    if (lane == 63) s_tot[e] = inc;
+  } else {
+    for (int e = wave; e < K; e += NW) {
+      const int w0 = lane * seglen, w1 = min(W, w0 + seglen);
+      int sum = 0;
+      for (int wb = w0; wb < w1; wb += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (wb + u < w1) ? a.cntw[(size_t)(wb + u) * K + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+      }
+      const int inc = wave_incl_scan_i(sum, lane);
+      int run = inc - sum;
+      for (int wb = w0; wb < w1; wb += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (wb + u < w1) ? a.cntw[(size_t)(wb + u) * K + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (wb + u < w1) {
+            a.cntw[(size_t)(wb + u) * K + e] = run;
+            run += v[u];
+          }
+      }
+      if (lane == 63) s_tot[e] = inc;
+    }
   }
   // per (projection, grid column): exclusive prefix of the workgroup counts,
-  // in place
-  for (int q = wave; q < a.ncol * 32; q += NW) {
-    const int c = q >> 5, n = q & 31;
-    if (n >= (c ? a.N[1] : a.N[0])) continue;
-    int run = 0;
-    for (int b0 = 0; b0 < nb; b0 += 64) {
-      const int bb = b0 + lane;
-      const int v = (bb < nb) ? a.wgcnt[(c * nb + bb) * 32 + n] : 0;
-      const int inc = wave_incl_scan_i(v, lane);
-      if (bb < nb) a.wgcnt[(c * nb + bb) * 32 + n] = run + inc - v;
-      run += __shfl(inc, 63, 64);
+  // in place; a wave takes its pairs PB at a time (nb <= 64: one load per
+  // lane and pair, all in flight at once)
+  constexpr int PB = 4;
+  if (nb <= 64) {
+    for (int q0 = wave * PB; q0 < a.ncol * 32; q0 += NW * PB) {
+      int v[PB];
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int c = (q0 + q) >> 5, n = (q0 + q) & 31;
+        const bool ok = q0 + q < a.ncol * 32 && n < (c ? a.N[1] : a.N[0]) && lane < nb;
+        v[q] = ok ? a.wgcnt[(c * nb + lane) * 32 + n] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int c = (q0 + q) >> 5, n = (q0 + q) & 31;
+        if (!(q0 + q < a.ncol * 32 && n < (c ? a.N[1] : a.N[0]))) continue;
+        const int inc = wave_incl_scan_i(v[q], lane);
+        if (lane < nb) a.wgcnt[(c * nb + lane) * 32 + n] = inc - v[q];
+        if (lane == 63) s_ctot[c][n] = inc;
+      }
     }
-    if (lane == 0) s_ctot[c][n] = run;
+  } else {
+    for (int q = wave; q < a.ncol * 32; q += NW) {
+      const int c = q >> 5, n = q & 31;
+      if (n >= (c ? a.N[1] : a.N[0])) continue;
+      int run = 0;
+      for (int b0 = 0; b0 < nb; b0 += 64) {
+        const int bb = b0 + lane;
+        const int v = (bb < nb) ? a.wgcnt[(c * nb + bb) * 32 + n] : 0;
+        const int inc = wave_incl_scan_i(v, lane);
+        if (bb < nb) a.wgcnt[(c * nb + bb) * 32 + n] = run + inc - v;
+        run += __shfl(inc, 63, 64);
+      }
+      if (lane == 0) s_ctot[c][n] = run;
+    }
   }
   __syncthreads();
   if (wave == 0) route_expert_offsets(a, s_tot, nullptr, nullptr, lane);
