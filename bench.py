@@ -203,8 +203,8 @@ def main():
                     help="also run one 256 MiB elementwise copy kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (see the design notes for how the path would shard).", file=sys.stderr)
+        print(f"bench.py: the forward runs on one GPU only; --gpus {args.gpus} is not "
+              "supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,21 +1,18 @@
-// Column stage of the fused low-rank forward.
+// Column stage of the fused low-rank forward, and the dense shared expert.
 //
 // "TileQ" technical summary, section 2.2 (Mechanism): the batch is projected
 // onto a shared factor once.  Here that is P[row][:] = V_n^T a_row for every
 // row of a column's work list: for gate/up/single projections a row is a
 // unique (column n, token t) pair, so V_n^T x_t is computed once for all the
 // experts of column n that token t routes to; for the down projection a row
-// is a slot (its input h differs per expert).  (Order of the two factor
-// products: the input meets V first, as y = W x requires; see the design
-// notes on the summary's wording.)
+// is a slot (its input h differs per expert).  The input meets V first, as
+// y = W x requires.
 //
-// Prefill shape (the decode column stage is in decode_stages.hip).  MFMA
-// 16x16x32 in the activation dtype, fp32 accumulation.  A operand =
-// activation rows (16 rows x 32 inputs), B operand = V_n^T rows (r-columns).
-// Split-K over `nsplit` slabs: slab s holds the partial sum over its k-range;
-// consumers add the slabs (deterministic, no float atomics).  The stored rank
-// vectors are already multiplied by Sigma (in fp32), which every consumer
-// needs.
+// Prefill shape (the decode column stage is in decode_stages.hip): one
+// workgroup covers the whole k-range of its rows.  MFMA 16x16x32 in the
+// activation dtype, fp32 accumulation; A operand = V_n^T rows (rank rows),
+// B operand = activation rows.  The stored rank vectors are already
+// multiplied by Sigma (in fp32), which every consumer needs.
 #include "tq_device.h"
 
 namespace tq {
@@ -283,52 +280,6 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   }
 }
 
-// Split-K reduction of the column stage: slab 0 += slabs 1.. (in slab
-// order, deterministic).  Rows past the segment total are skipped.
-struct RedArgs {
-  float* P[2];
-  const int* total[2];           // device row count of each projection (or nullptr)
-  int total_host[2];             // row count when total is nullptr
-  int r_pad[2];
-  int nsplit, rows_cap;
-};
-
-__global__ __launch_bounds__(256) void colproj_reduce_kernel(RedArgs a) {
-  const int z = blockIdx.y;
-  const int rp = a.r_pad[z];
-  const int rows = a.total[z] ? *a.total[z] : a.total_host[z];
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (size_t)rows * rp) return;
-  const size_t slab = (size_t)a.rows_cap * rp;
-  float* P = a.P[z];
-  float v = 0.f;
-  for (int sp = 0; sp < a.nsplit; sp += 16) {
-    float t[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) t[u] = (sp + u < a.nsplit) ? P[i + (sp + u) * slab] : 0.f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) v += t[u];
-  }
-  P[i] = v;
-}
-
-void launch_colproj_reduce(const ColArgs* a, int nproj, hipStream_t s) {
-  if (a[0].nsplit <= 1) return;
-  RedArgs r{};
-  int rp_max = 0;
-  for (int z = 0; z < nproj; ++z) {
-    r.P[z] = a[z].P;
-    r.total[z] = (a[z].ap_T > 0) ? nullptr : a[z].seg_off + a[z].nseg;
-    r.total_host[z] = a[z].nseg * a[z].ap_T;
-    r.r_pad[z] = a[z].r_pad;
-    rp_max = a[z].r_pad > rp_max ? a[z].r_pad : rp_max;
-  }
-  r.nsplit = a[0].nsplit;
-  r.rows_cap = a[0].rows_cap;
-  const dim3 rg((unsigned)(((size_t)a[0].rows_cap * rp_max + 255) / 256), nproj);
-  hipLaunchKernelGGL(colproj_reduce_kernel, rg, dim3(256), 0, s, r);
-}
-
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act, hipStream_t s) {
   (void)rt;                      // 128-row tiles
   RgArgs args{};
@@ -338,7 +289,6 @@ void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
   const dim3 grid((unsigned)(((max_tiles + 7) / 8) * 8), 1, nproj);
   if (act == ACT_F16) hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_COL>), grid, dim3(64 * RG_WAVES), 0, s, args);
   else hipLaunchKernelGGL((rowgemm_kernel<__bf16, RG_COL>), grid, dim3(64 * RG_WAVES), 0, s, args);
-  launch_colproj_reduce(a, nproj, s);
 }
 
 void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s) {

@@ -98,11 +98,10 @@ struct ColArgs {
   int ap_T;                      // > 0: every (column, token) pair, row = n * ap_T + t
                                  // (no work lists; seg_off/tile_off/row_src unused)
 };
-// prefill column stage (ap_T == 0): tiles of 128 rows (route rt_col 128)
+// prefill column stage (ap_T == 0, nsplit == 1: one workgroup covers the
+// whole k-range of its rows): tiles of 128 rows (route rt_col 128)
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
                     hipStream_t s);
-// split-K reduction of the column stage: slab 0 += slabs 1..nsplit-1
-void launch_colproj_reduce(const ColArgs* a, int nproj, hipStream_t s);
 
 // ---- residual grouped GEMM (+ low-rank K-extension, SwiGLU) ---------------
 enum GemmMode { MODE_GATEUP = 0, MODE_RES = 1 };

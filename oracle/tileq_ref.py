@@ -21,7 +21,7 @@ The oracle does none of the fusion of section 2.2: it builds each used expert
 weight W_e explicitly in fp64 and applies it per routed slot, which is the
 plain definition the fused forward must reproduce up to rounding order.
 
-Readings where the pages are silent (all listed in the design notes):
+Readings where the pages are silent:
   * residual R_e[o, i] = s_e[o, i//G] * (q_e[o, i] - z_e[o, i//G]), 2-bit
     codes q packed 16 per uint32 (code i at bits 2*(i % 16)), group G along
     d_in, fp16 scale s and integer zero point z;
