@@ -34,12 +34,10 @@ namespace tq {
 //             over blockIdx.z into separate slabs.
 enum RgMode { RG_COL = 0, RG_DUAL = 1, RG_PLAIN = 2 };
 constexpr int RG_WAVES = 8;
-constexpr int RG_KS = 2;                         // k-steps per stage
 constexpr int RG_NSLOT = 4, RG_DEPTH = 3;
-constexpr int RG_A = 0;                          // [KS][8 frags][64 lanes] x 16 B
-constexpr int RG_B = RG_KS * 8 * 1024;           // [KS][8 frags][64 lanes] x 16 B
-constexpr int RG_BYTES = 2 * RG_KS * 8 * 1024;   // 32 KB per slot
-constexpr int RG_NI = 2 * RG_KS * 8 / RG_WAVES;  // loads per wave per stage
+constexpr int RG_COL_KS = 1;                     // column stage: 16 KB slots, two workgroups per CU
+constexpr int RG_A = 0;                          // [KS][8 frags][64 lanes] x 16 B, then
+                                                 // the activations, the same
 
 struct RgArgs {
   ColArgs c[2];                  // RG_COL: per projection (blockIdx.z)
@@ -48,9 +46,16 @@ struct RgArgs {
   int ntiles;                    // row tiles of the grid (before the XCD remap)
 };
 
-template <typename T, int MODE>
+// KS: MFMA k-steps (32 inputs) per stage: 2 (32 KB slots, one workgroup per
+// CU) or 1 (16 KB slots, two workgroups per CU)
+template <typename T, int MODE, int KS>
 __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   typedef typename Vec8<T>::type V8;
+  constexpr int RG_KS = KS;
+  constexpr int RG_B = RG_KS * 8 * 1024;
+  constexpr int RG_BYTES = 2 * RG_KS * 8 * 1024;
+  constexpr int RG_NI = 2 * RG_KS * 8 / RG_WAVES;   // loads per wave per stage
+  constexpr int SIN = 32 * KS;                       // inputs per stage
   __shared__ __attribute__((aligned(16))) char s0[RG_BYTES];
   __shared__ __attribute__((aligned(16))) char s1[RG_BYTES];
   __shared__ __attribute__((aligned(16))) char s2[RG_BYTES];
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
     wbytes = (uint32_t)vsz;
     wrs = 64u;
     wks = (uint32_t)a.r_pad * 64u;
-    st1 = d_in >> 6;
+    st1 = d_in / SIN;
     if (tid < 128) {
       const int n = n0 + tid;
       s_src[tid] = (n < n_end) ? (a.row_src ? a.row_src[n] : n) : -1;
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
     wbytes = (uint32_t)((size_t)M * d_in * 2);
     wrs = (uint32_t)d_in * 2u;
     wks = 64u;
-    const int nst = d_in >> 6;
+    const int nst = d_in / SIN;
     // (uniform: the division may be done in vector registers)
     const int sps = __builtin_amdgcn_readfirstlane((nst + args.nsplit - 1) / args.nsplit);
     st0 = blockIdx.z * sps;
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   const int row_lo = __builtin_amdgcn_readfirstlane(s_src[0]);
   const int row_hi = __builtin_amdgcn_readfirstlane(s_src[max(nv - 1, 0)]);
 
-  // per-lane offsets of this wave's loads: load q = wave * NI + i; q < 16:
+  // per-lane offsets of this wave's loads: load q = wave * NI + i; q < 8 KS:
   // weight fragment (k-step q / 8, fragment q % 8), else activation fragment
   uint32_t vo[RG_NI];
   bool isw[RG_NI];
@@ -138,8 +143,8 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
 #pragma unroll
   for (int i = 0; i < RG_NI; ++i) {
     const int q = wave * RG_NI + i;
-    const bool w = q < 16;
-    const int qq = w ? q : q - 16;
+    const bool w = q < 8 * RG_KS;
+    const int qq = w ? q : q - 8 * RG_KS;
     const int ks = qq >> 3, f = qq & 7;
     isw[i] = w;
     ks_of[i] = ks;
@@ -180,11 +185,11 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
       if (isw[i]) {
         // k-step offset: blocked V^T layout moves by whole k-step blocks,
         // row-major weights by 128 bytes per stage
-        const uint32_t so = (MODE == RG_COL) ? (uint32_t)(2 * st + ks_of[i]) * wks
-                                             : (uint32_t)st * 128u;
+        const uint32_t so = (MODE == RG_COL) ? (uint32_t)(KS * st + ks_of[i]) * wks
+                                             : (uint32_t)st * (SIN * 2u);
         dma16(wsel[i] ? rw[1] : rw[0], dst, live ? vo[i] : OOB, so);
       } else {
-        dma16(rx, dst, live ? vo[i] : OOB, (uint32_t)st * 128u);
+        dma16(rx, dst, live ? vo[i] : OOB, (uint32_t)st * (SIN * 2u));
       }
     }
   };
@@ -287,8 +292,8 @@ void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
   args.c[1] = a[nproj > 1 ? 1 : 0];
   args.ntiles = max_tiles;
   const dim3 grid((unsigned)(((max_tiles + 7) / 8) * 8), 1, nproj);
-  if (act == ACT_F16) hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_COL>), grid, dim3(64 * RG_WAVES), 0, s, args);
-  else hipLaunchKernelGGL((rowgemm_kernel<__bf16, RG_COL>), grid, dim3(64 * RG_WAVES), 0, s, args);
+  if (act == ACT_F16) hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_COL, RG_COL_KS>), grid, dim3(64 * RG_WAVES), 0, s, args);
+  else hipLaunchKernelGGL((rowgemm_kernel<__bf16, RG_COL, RG_COL_KS>), grid, dim3(64 * RG_WAVES), 0, s, args);
 }
 
 void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s) {
@@ -299,10 +304,10 @@ void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s) {
   const unsigned gx = (unsigned)(((args.ntiles + 7) / 8) * 8);
   if (dual) {
     const dim3 grid(gx, (a.d_out + 63) / 64, 1);
-    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_DUAL>), grid, dim3(64 * RG_WAVES), 0, s, args);
+    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_DUAL, 2>), grid, dim3(64 * RG_WAVES), 0, s, args);
   } else {
     const dim3 grid(gx, (a.d_out + 127) / 128, args.nsplit);
-    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_PLAIN>), grid, dim3(64 * RG_WAVES), 0, s, args);
+    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_PLAIN, 2>), grid, dim3(64 * RG_WAVES), 0, s, args);
   }
 }
 
