@@ -11,6 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtileq.so")
 
@@ -21,7 +23,7 @@ STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHI
           5: "TQ_EUNSUPPORTED", 6: "TQ_ESTATE"}
 EXPORTS = ["tq_layer_create", "tq_upload_proj", "tq_upload_shared_expert",
            "tq_workspace_size", "tq_forward", "tq_layer_destroy", "tq_last_error",
-           "tq_abi_version", "tq_layer_set_path", "tq_debug_route", "tq_debug_dequant",
+           "tq_abi_version", "tq_layer_set_path", "tq_debug_route", "tq_debug_dequant", "tq_debug_row_bound",
            "tq_profile_enable", "tq_profile_read"]
 STAGES = ["route", "row_exponent", "column_stage_in", "gemm_in", "column_stage_down",
           "shared_expert", "gemm_down", "combine"]
@@ -66,6 +68,7 @@ def lib():
         L.tq_layer_set_path.argtypes = [vp, i32]
         L.tq_debug_route.argtypes = [vp, i32, vp, i32, i32, vp, sz] + [vp] * 7 + [vp]
         L.tq_debug_dequant.argtypes = [vp, i32, i32, vp, vp]
+        L.tq_debug_row_bound.argtypes = [vp, i32, vp]
         L.tq_profile_enable.argtypes = [vp, i32]
         L.tq_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
         for name in EXPORTS:
@@ -140,6 +143,13 @@ class Layer:
     def debug_dequant(self, which, expert, w_out, stream=None):
         _check("tq_debug_dequant", lib().tq_debug_dequant(self.h, which, expert, _ptr(w_out),
                                                           _stream(stream)))
+
+    def debug_row_bound(self, which):
+        """Per-expert bound on the effective weight's row sums of |W| (numpy f32 [K])."""
+        out = np.zeros(self.K, np.float32)
+        _check("tq_debug_row_bound", lib().tq_debug_row_bound(
+            self.h, which, out.ctypes.data_as(ctypes.c_void_p)))
+        return out
 
     def profile_enable(self, on: bool = True):
         _check("tq_profile_enable", lib().tq_profile_enable(self.h, 1 if on else 0))

@@ -393,11 +393,23 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
     }
     // SwiGLU epilogue: h = RND_act(silu(gate) * up), stored per slot position
     T* h = reinterpret_cast<T*>(a.h);
+    // fp16 copy for bfloat16 layers: |silu(g) u| <= |g||u| <= B_g B_u max|x|^2
+    // with B the row bounds of |W| (< 2^bg, 2^bu) and max|x| < 2^(ex + 15),
+    // so h * 2^-(bg + bu + 2 ex + 15) stays below 2^15
+    int bgu = 0;
+    if (a.h16) {
+      int bg, bu;
+      frexpf(a.p[0].l1max[e], &bg);
+      frexpf(a.p[1].l1max[e], &bu);
+      bgu = bg + bu + 15;
+    }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int row = 16 * f + l16;
       if (row >= nv) continue;
       const int pos = pos0 + row;
+      const int eh = bgu + 2 * s_exp[row];
+      if (a.h16 && rt == 0 && wave == 0 && lg == 0) a.exh[pos] = eh;
 #pragma unroll
       for (int r = 0; r < RF; ++r) {
         if (rb0 + r >= nrb) continue;
@@ -406,6 +418,13 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) hv[v] = from_f32<T>(silu_f(acc[0][r][f][v]) * acc[1][r][f][v]);
         *reinterpret_cast<u32x2*>(h + (size_t)pos * a.d_out + o) = __builtin_bit_cast(u32x2, hv);
+        if (a.h16) {
+          half_t hs[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) hs[v] = (half_t)ldexpf(to_f32(hv[v]), -eh);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<half_t*>(a.h16) + (size_t)pos * a.d_out + o) =
+              __builtin_bit_cast(u32x2, hs);
+        }
       }
     }
   } else {

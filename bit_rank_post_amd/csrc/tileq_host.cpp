@@ -55,6 +55,7 @@ void free_proj(ProjHost& p) {
   (void)hipFree(p.dev.sigma);
   (void)hipFree(p.dev.m_of);
   (void)hipFree(p.dev.n_of);
+  (void)hipFree(p.dev.l1max);
   p = ProjHost{};
 }
 
@@ -503,6 +504,7 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
   const size_t ncode = (size_t)d->K * d_out * (d_in / 16);
   const size_t nsz = (size_t)d->K * d_out * v.ng;
   int* bad = nullptr;
+  float* vn = nullptr;
   auto cleanup = [&]() {
     (void)hipFree(v.codes);
     (void)hipFree(v.sz);
@@ -511,7 +513,9 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
     (void)hipFree(v.sigma);
     (void)hipFree(v.m_of);
     (void)hipFree(v.n_of);
+    (void)hipFree(v.l1max);
     (void)hipFree(bad);
+    (void)hipFree(vn);
   };
 #define UPCHK(expr)                                                            \
   do {                                                                         \
@@ -527,6 +531,8 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
   UPCHK(hipMalloc(&v.m_of, sizeof(int) * d->K));
   UPCHK(hipMalloc(&v.n_of, sizeof(int) * d->K));
   UPCHK(hipMalloc(&bad, sizeof(int)));
+  UPCHK(hipMalloc(&v.l1max, sizeof(float) * d->K));
+  if (d->rank > 0) UPCHK(hipMalloc(&vn, sizeof(float) * d->N * d->rank));
   if (v.r_pad > 0) {
     UPCHK(hipMalloc(&v.U, (size_t)d->M * d_out * v.r_pad * 2));
     UPCHK(hipMalloc(&v.Vt, (size_t)d->N * v.r_pad * d_in * 2));
@@ -545,11 +551,36 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
   }
   UPCHK(hipMemcpyAsync(v.m_of, m_of.data(), sizeof(int) * d->K, hipMemcpyHostToDevice, s));
   UPCHK(hipMemcpyAsync(v.n_of, n_of.data(), sizeof(int) * d->K, hipMemcpyHostToDevice, s));
+  {
+    RowBoundArgs rb{};
+    rb.codes = d->codes;
+    rb.scales = d->scales;
+    rb.zeros = d->zeros;
+    rb.U = d->U;
+    rb.sigma = d->sigma;
+    rb.V = d->V;
+    rb.m_of = v.m_of;
+    rb.n_of = v.n_of;
+    rb.K = d->K;
+    rb.N = d->N;
+    rb.d_out = d_out;
+    rb.d_in = d_in;
+    rb.G = d->group;
+    rb.r = d->rank;
+    rb.bf = L->act == TQ_BF16 ? 1 : 0;
+    rb.vn = vn;
+    rb.l1max = v.l1max;
+    UPCHK(hipMemsetAsync(v.l1max, 0, sizeof(float) * d->K, s));
+    launch_row_bound(rb, s);
+    UPCHK(hipGetLastError());
+  }
   int hbad = 0;
   UPCHK(hipMemcpyAsync(&hbad, bad, sizeof(int), hipMemcpyDeviceToHost, s));
   UPCHK(hipStreamSynchronize(s));
   (void)hipFree(bad);
   bad = nullptr;
+  (void)hipFree(vn);
+  vn = nullptr;
   if (hbad) {
     cleanup();
     return fail(TQ_EINVAL, "%s%s", (hbad & 1) ? "scale not finite or |s| >= 1024; " : "",
@@ -779,6 +810,11 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       }
       ga.p_rows = p.rows_cap;
       ga.h = h;
+      if (bf) {
+        // fp16 copy of h for down, scaled by a bound known before h is
+        ga.h16 = at<void>(ws, p.h16);
+        ga.exh = at<int>(ws, p.ex_h16);
+      }
       launch_gemm_prefill(ga, MODE_GATEUP, act, p.max_tiles_gemm, s);
     } else {
       ga.dres = dres;
@@ -848,8 +884,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
       ga.gather = 0;
       ga.rows = p.S;
       if (bf) {
-        // exact fp16 copy of h for the MFMA kernel
-        launch_rows_to_f16(h, p.S, L->d_ff, nullptr, at<int>(ws, p.ex_h16), at<void>(ws, p.h16), s);
+        // the fp16 copy of h the gate/up kernel wrote beside it
         ga.A = at<void>(ws, p.h16);
         ga.ex = at<int>(ws, p.ex_h16);
       } else {
@@ -997,6 +1032,15 @@ tq_status tq_debug_dequant(const tq_layer* L, int32_t which, int32_t expert, voi
   if (!w_out) return fail(TQ_EINVAL, "w_out is NULL");
   launch_debug_dequant(L->proj[which].dev, expert, w_out, reinterpret_cast<hipStream_t>(stream));
   HIPCHK(hipGetLastError());
+  return TQ_OK;
+}
+
+tq_status tq_debug_row_bound(const tq_layer* L, int32_t which, float* l1_out) {
+  if (!L) return fail(TQ_EINVAL, "layer is NULL");
+  if (which < 0 || which >= nproj(L)) return fail(TQ_EINVAL, "projection %d not in layer", which);
+  if (!L->proj[which].uploaded) return fail(TQ_ESTATE, "projection %d not uploaded", which);
+  if (!l1_out) return fail(TQ_EINVAL, "l1_out is NULL");
+  HIPCHK(hipMemcpy(l1_out, L->proj[which].dev.l1max, sizeof(float) * L->K, hipMemcpyDeviceToHost));
   return TQ_OK;
 }
 

@@ -33,6 +33,7 @@ struct ProjDev {
   float* sigma;
   int* m_of;
   int* n_of;
+  float* l1max;   // [K] bound on max_o sum_i |W_e[o][i]| (effective weight)
 };
 
 struct SharedDev {
@@ -124,6 +125,10 @@ struct GemmArgs {
   const int* slot2col[2];
   // outputs
   void* h;                       // GATEUP: [S][d_out] act
+  // GATEUP, bfloat16 layers: also h * 2^-exh[pos] as fp16 (the operand of
+  // down), exh from the weights' row bounds and the token's exponent ex
+  void* h16;
+  int* exh;
   float* dres;                   // RES: [S][d_out] f32 (gate weight applied)
   const float* gates;            // RES: topk weights [T*topk]
   int rows;                      // rows of A
@@ -228,6 +233,21 @@ void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, i
                          hipStream_t s);
 void launch_pack_sz(const uint16_t* scales, const uint16_t* zeros, uint32_t* dst,
                     int K, int d_out, int ng, int* bad, hipStream_t s);
+// per-expert bound on the effective weight's row sums of |W| (upload time)
+struct RowBoundArgs {
+  const uint32_t* codes;         // user layout [K][d_out][d_in/16]
+  const uint16_t* scales;        // [K][d_out][d_in/G] f16
+  const uint16_t* zeros;
+  const void* U;                 // [M*d_out][r] activation dtype (r > 0)
+  const float* sigma;            // [r]
+  const void* V;                 // [N*d_in][r]
+  const int* m_of;               // [K] device
+  const int* n_of;
+  int K, N, d_out, d_in, G, r, bf;
+  float* vn;                     // scratch [N][r]
+  float* l1max;                  // [K], zero on entry
+};
+void launch_row_bound(const RowBoundArgs& b, hipStream_t s);
 void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStream_t s);
 void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_pad,
                         hipStream_t s);

@@ -129,6 +129,86 @@ void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_
                      d_in, r, r_pad);
 }
 
+// Bound on the effective weight's rows, W_e = U_m Sigma V_n^T + R_e (the
+// tiled decomposition of section 2.1): for every expert, an upper bound on
+// max_o sum_i |W_e[o][i]| by the triangle inequality,
+//   sum_i |R_e[o][i]| + sum_r |U_m[o][r]| |sigma_r| sum_i |V_n[i][r]|.
+// Used to pick a power-of-two scale for intermediates before they are known.
+__device__ __forceinline__ float act_bits_to_f32(uint16_t b, int bf) {
+  return bf ? __uint_as_float((uint32_t)b << 16) : (float)__builtin_bit_cast(half_t, (uint16_t)(b));
+}
+
+// vn[n][c] = sum_i |V[n*d_in + i][c]|; one workgroup per n, 8 input phases x
+// 128 ranks, the phases summed in a fixed order.
+__global__ __launch_bounds__(1024) void vnorm_kernel(const uint16_t* __restrict__ V, int d_in, int r,
+                                                     int bf, float* __restrict__ vn) {
+  __shared__ float s_part[8][128];
+  const int n = blockIdx.x, c = threadIdx.x & 127, ph = threadIdx.x >> 7;
+  float acc = 0.f;
+  if (c < r)
+    for (int i = ph; i < d_in; i += 8)
+      acc += fabsf(act_bits_to_f32(V[((size_t)n * d_in + i) * r + c], bf));
+  s_part[ph][c] = acc;
+  __syncthreads();
+  if (ph == 0 && c < r) {
+    float t = 0.f;
+    for (int q = 0; q < 8; ++q) t += s_part[q][c];
+    vn[(size_t)n * r + c] = t;
+  }
+}
+
+// One wave per (expert, output row); the row sums meet in l1max[e] by an
+// integer max over the (non-negative) float bit patterns.
+__global__ __launch_bounds__(256) void row_l1_kernel(const uint32_t* __restrict__ codes,
+                                                     const uint16_t* __restrict__ scales,
+                                                     const uint16_t* __restrict__ zeros,
+                                                     const uint16_t* __restrict__ U,
+                                                     const float* __restrict__ sigma,
+                                                     const float* __restrict__ vn,
+                                                     const int* __restrict__ m_of,
+                                                     const int* __restrict__ n_of, int K, int d_out,
+                                                     int d_in, int G, int r, int bf,
+                                                     uint32_t* __restrict__ l1max) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (size_t)K * d_out) return;
+  const int e = (int)(row / d_out), o = (int)(row % d_out);
+  const int nw = d_in >> 4, ng = d_in / G;
+  float acc = 0.f;
+  for (int w = lane; w < nw; w += 64) {
+    const uint32_t word = codes[row * nw + w];
+    const int g = (w << 4) / G;                   // G % 16 == 0: one group per word
+    const float sa = fabsf((float)__builtin_bit_cast(half_t, (uint16_t)(scales[row * ng + g])));
+    const int z = (int)(float)__builtin_bit_cast(half_t, (uint16_t)(zeros[row * ng + g]));
+    int cnt = 0;
+    for (int j = 0; j < 16; ++j) cnt += abs((int)((word >> (2 * j)) & 3u) - z);
+    acc += sa * (float)cnt;
+  }
+  if (r > 0) {
+    const size_t urow = (size_t)m_of[e] * d_out + o;
+    const int n = n_of[e];
+    for (int c = lane; c < r; c += 64)
+      acc += fabsf(act_bits_to_f32(U[urow * r + c], bf)) * fabsf(sigma[c]) * vn[(size_t)n * r + c];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) {
+    if (!(acc <= 3.0e38f)) acc = 3.0e38f;        // overflow or NaN: the largest finite bound
+    atomicMax(l1max + e, __float_as_uint(acc));
+  }
+}
+
+void launch_row_bound(const RowBoundArgs& b, hipStream_t s) {
+  if (b.r > 0)
+    hipLaunchKernelGGL(vnorm_kernel, dim3(b.N), dim3(1024), 0, s,
+                       reinterpret_cast<const uint16_t*>(b.V), b.d_in, b.r, b.bf, b.vn);
+  const size_t rows = (size_t)b.K * b.d_out;
+  hipLaunchKernelGGL(row_l1_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, b.codes,
+                     b.scales, b.zeros, reinterpret_cast<const uint16_t*>(b.U), b.sigma, b.vn,
+                     b.m_of, b.n_of, b.K, b.d_out, b.d_in, b.G, b.r, b.bf,
+                     reinterpret_cast<uint32_t*>(b.l1max));
+}
+
 // Dequantized weights of one expert through the forward's own unpack path:
 // one wave per (row block, step group); lane l writes its 8 inputs per step.
 __global__ void debug_dequant_kernel(ProjDev p, int e, half_t* __restrict__ w) {

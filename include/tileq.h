@@ -181,6 +181,16 @@ tq_status tq_debug_route(const tq_layer *L, int32_t which, const int32_t *topk_i
 tq_status tq_debug_dequant(const tq_layer *L, int32_t which, int32_t expert, void *w_out,
                            void *stream);
 
+/* Copy the per-expert row bound of one projection to l1_out (HOST f32 [K]):
+ * an upper bound on max_o sum_i |W_e[o][i]| of the effective weight
+ * W_e = U_m Sigma V_n^T + R_e (section 2.1), the sum over the residual's
+ * |s (q - z)| plus sum_r |U_m[o][r]| |sigma_r| sum_i |V_n[i][r]|, computed
+ * in fp32 at upload (the largest finite fp32 where that overflows).  The
+ * forward of bfloat16 SWIGLU layers at prefill scales its fp16 copy of the
+ * intermediate h by a power of two derived from the gate and up bounds.
+ * Synchronous.  Errors: TQ_EINVAL, TQ_ESTATE (not uploaded), TQ_EHIP. */
+tq_status tq_debug_row_bound(const tq_layer *L, int32_t which, float *l1_out);
+
 /* Stage timing for benchmarks: with profiling on, tq_forward records a HIP
  * event on `stream` before its first stage and after each of its stages
  * (pre-created events: the forward still allocates nothing).  Stage order:

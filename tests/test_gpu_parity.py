@@ -228,6 +228,53 @@ def test_small_swiglu(act, path):
         assert_parity(y, R.forward(layer, x, ids, g), what=f"swiglu {act} path={path} T={T}")
 
 
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_row_bound(act):
+    """The per-expert bound on sum_i |W_e[o][i]| of the effective weight: the
+    triangle-inequality sum recomputed here from the stored arrays, and not
+    below the oracle's explicitly built weights' largest row sum."""
+    layer = small_swiglu(act, 21)
+    L = tqio.upload_layer(layer)
+    for which, name in enumerate(("gate", "up", "down")):
+        proj = layer["proj"][name]
+        got = L.debug_row_bound(which).astype(np.float64)
+        r, M, N = proj["rank"], proj["M"], proj["N"]
+        d_out, d_in = proj["d_out"], proj["d_in"]
+        U = R.to_f64(proj["U"], act).reshape(M, d_out, r)
+        V = R.to_f64(proj["V"], act).reshape(N, d_in, r)
+        sig = np.abs(np.asarray(proj["sigma"], np.float64))
+        for e in range(proj["K"]):
+            t = int(proj["tile_of_expert"][e])
+            m, n = t // N, t % N
+            res = np.abs(R.expert_residual(proj, e)).sum(axis=1)
+            lr = (np.abs(U[m]) * sig) @ np.abs(V[n]).sum(axis=0)
+            want = float((res + lr).max())
+            true = float(np.abs(R.expert_weight(proj, e)).sum(axis=1).max())
+            assert abs(got[e] - want) <= 1e-4 * want, (name, e, got[e], want)
+            assert got[e] >= true * (1 - 1e-5), (name, e, got[e], true)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_bf16_swiglu_token_magnitudes(path):
+    """bfloat16 tokens far outside the fp16 range (powers of two from 2^-40 to
+    2^40 per token group): every group within the bar relative to its own
+    outputs (the fp16 operands carry per-row power-of-two exponents)."""
+    layer = small_swiglu("bf16", 23)
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    T = 24 if path == 1 else 300
+    x, ids, g = synth.make_custom_tokens(256, 8, 2, T, "bf16", seed=31)
+    shifts = np.array([-40, -12, 0, 9, 40])
+    grp = np.arange(T) % len(shifts)
+    x32 = synth.act_as_f32(x, "bf16") * np.ldexp(1.0, shifts[grp])[:, None].astype(np.float32)
+    xs = synth.to_act(x32, "bf16")
+    y, _ = run_forward(L, xs, ids, g, "bf16", "f32")
+    ref = R.forward(layer, xs, ids, g)
+    for i, sh in enumerate(shifts):
+        rows = grp == i
+        assert_parity(y[rows], ref[rows], what=f"bf16 tokens x 2^{sh} path={path}")
+
+
 @pytest.mark.parametrize("path,T", [(1, 24), (2, 300)])
 def test_small_swiglu_with_shared_expert(path, T):
     """The shared expert (on the layer's second stream) at decode and prefill."""
