@@ -141,17 +141,22 @@ int choose_nsplit(int path, long rows, int d_in) {
   return decode_col_splits(d_in);
 }
 
-// k-chunks of the decode kernel for a down / single projection: enough
-// 16-wave workgroups (one per CU at a time) that every CU streams even when
-// only a few experts are active; each chunk keeps at least 4 stages.  Each
-// chunk writes its own fp32 slab of per-slot outputs.
+int device_cus();
+
+// k-chunks of the decode kernel for a down / single projection: the most
+// (up to 8, each chunk keeping at least 4 stages) for which the active
+// experts' 16-row fragments times the chunks still fit one round of the grid
+// (16 rows per CU: two 8-wave workgroups or one of 16 waves).  A second round
+// costs more than longer chunks: every workgroup pays a fixed start (routing
+// reads, first batch) and epilogue.  Each chunk writes its own fp32 slab of
+// per-slot outputs.
 int choose_nks(const tq_layer* L, int q, int S) {
   const ProjDev& d = L->proj[q].dev;
   const long active = std::min<long>(L->K, S);
-  const long wgs = active * ((d.nrb + 15) / 16);
+  const long cus = device_cus();
   const int nfull = (d.d_in >> 5) >> 3;
   int nks = 1;
-  while (nks < 8 && wgs * nks < 512 && nfull / (2 * nks) >= 4) nks *= 2;
+  while (nks < 8 && active * d.nrb * (2L * nks) <= 16L * cus && nfull / (2 * nks) >= 4) nks *= 2;
   return nks;
 }
 
