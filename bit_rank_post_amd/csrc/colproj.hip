@@ -9,7 +9,10 @@
 // y = W x requires.
 //
 // Prefill shape (the decode column stage is in decode_stages.hip): one
-// workgroup covers the whole k-range of its rows.  MFMA 16x16x32 in the
+// workgroup covers the whole k-range of its rows, except for the column
+// stage that feeds the combine, which may split the k-range over
+// blockIdx.z into fp32 slabs (summed by the combine) when its tiles alone
+// would leave half the grid's workgroup slots empty.  MFMA 16x16x32 in the
 // activation dtype, fp32 accumulation; A operand = V_n^T rows (rank rows),
 // B operand = activation rows.  The stored rank vectors are already
 // multiplied by Sigma (in fp32), which every consumer needs.
@@ -79,6 +82,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   const char* wbase[2];
   uint32_t wbytes, wrs, wks;           // weight buffer size, row and k-step strides (bytes)
   int st0 = 0, st1;
+  int sp = 0;                          // RG_COL k-split (fp32 slab) of this workgroup
   // (a copy, not a pointer into the kernel arguments: the fields stay scalar)
   ColArgs ca{};
   if constexpr (MODE == RG_COL) {
@@ -100,6 +104,13 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
     wrs = 64u;
     wks = (uint32_t)a.r_pad * 64u;
     st1 = d_in / SIN;
+    if (a.nsplit > 1) {
+      // one projection split over blockIdx.z into k-ranges, each its own slab
+      sp = blockIdx.z;
+      const int sps = __builtin_amdgcn_readfirstlane((st1 + a.nsplit - 1) / a.nsplit);
+      st0 = min(st1, sp * sps);
+      st1 = min(st1, st0 + sps);
+    }
     if (tid < 128) {
       const int n = n0 + tid;
       s_src[tid] = (n < n_end) ? (a.row_src ? a.row_src[n] : n) : -1;
@@ -260,7 +271,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
           *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, hi);
           *reinterpret_cast<u32x2*>(dst + a.r_pad) = __builtin_bit_cast(u32x2, lo);
         } else {
-          *reinterpret_cast<f32x4*>(a.P + (size_t)n * a.r_pad + m) = v;
+          *reinterpret_cast<f32x4*>(a.P + ((size_t)sp * a.rows_cap + n) * a.r_pad + m) = v;
         }
       }
     } else if constexpr (MODE == RG_DUAL) {
@@ -291,7 +302,9 @@ void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
   args.c[0] = a[0];
   args.c[1] = a[nproj > 1 ? 1 : 0];
   args.ntiles = max_tiles;
-  const dim3 grid((unsigned)(((max_tiles + 7) / 8) * 8), 1, nproj);
+  // z: the projection (gate, up), or the k-split of a single projection
+  const int nz = nproj > 1 ? nproj : (a[0].nsplit > 1 ? a[0].nsplit : 1);
+  const dim3 grid((unsigned)(((max_tiles + 7) / 8) * 8), 1, nz);
   if (act == ACT_F16) hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_COL, RG_COL_KS>), grid, dim3(64 * RG_WAVES), 0, s, args);
   else hipLaunchKernelGGL((rowgemm_kernel<__bf16, RG_COL, RG_COL_KS>), grid, dim3(64 * RG_WAVES), 0, s, args);
 }

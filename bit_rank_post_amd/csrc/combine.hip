@@ -115,8 +115,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int cpw, in
           ij[j] = (j < k) ? s_i[tt * CB_KMAX + j] : -1;
           gj[j] = (j < k) ? s_g[tt * CB_KMAX + j] : 0.f;
           pv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (ij[j] >= i0 && ij[j] < i1)
-            pv[j] = *reinterpret_cast<const f32x4*>(a.P + (size_t)s_row[tt * CB_KMAX + j] * rp + c);
+          if (ij[j] >= i0 && ij[j] < i1) {
+            const float* pp = a.P + (size_t)s_row[tt * CB_KMAX + j] * rp + c;
+            pv[j] = *reinterpret_cast<const f32x4*>(pp);
+            for (int sp = 1; sp < a.nsplit; ++sp)     // k-split slabs of the column stage
+              pv[j] += *reinterpret_cast<const f32x4*>(pp + (size_t)sp * a.rows_cap * rp);
+          }
         }
         for (int i = i0; i < i1; ++i) {
           f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -137,9 +141,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int cpw, in
         for (int i = i0; i < i1; ++i) {
           f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
           for (int j = 0; j < k; ++j)
-            if (s_i[tt * CB_KMAX + j] == i)
-              v += s_g[tt * CB_KMAX + j] *
-                   *reinterpret_cast<const f32x4*>(a.P + (size_t)s_row[tt * CB_KMAX + j] * rp + c);
+            if (s_i[tt * CB_KMAX + j] == i) {
+              const float* pp = a.P + (size_t)s_row[tt * CB_KMAX + j] * rp + c;
+              f32x4 pj = *reinterpret_cast<const f32x4*>(pp);
+              for (int sp = 1; sp < a.nsplit; ++sp)
+                pj += *reinterpret_cast<const f32x4*>(pp + (size_t)sp * a.rows_cap * rp);
+              v += s_g[tt * CB_KMAX + j] * pj;
+            }
           T hi[4], lo[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -211,19 +219,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int cpw, in
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ovalid && t < a.T) {
       if (k <= KR) {
-        f32x4 dv[KR];
+        // per slot, up to NKB k-chunk slabs requested together (one round
+        // trip per slot instead of one per slab), summed in slab order
+        constexpr int NKB = 8;
 #pragma unroll
         for (int j = 0; j < KR; ++j) {
-          dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (pj[j] >= 0) dv[j] = *reinterpret_cast<const f32x4*>(a.dres + (size_t)pj[j] * a.d_out + o);
+          if (pj[j] < 0) continue;
+          const float* dp = a.dres + (size_t)pj[j] * a.d_out + o;
+          const size_t slab = (size_t)a.S * a.d_out;
+          f32x4 sv[NKB];
+#pragma unroll
+          for (int c = 0; c < NKB; ++c)
+            sv[c] = (c < a.nks) ? *reinterpret_cast<const f32x4*>(dp + c * slab) : f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 dv = sv[0];
+#pragma unroll
+          for (int c = 1; c < NKB; ++c)
+            if (c < a.nks) dv += sv[c];
+          for (int c = NKB; c < a.nks; ++c) dv += *reinterpret_cast<const f32x4*>(dp + c * slab);
+          v += dv;
         }
-        for (int c = 1; c < a.nks; ++c)
-#pragma unroll
-          for (int j = 0; j < KR; ++j)
-            if (pj[j] >= 0)
-              dv[j] += *reinterpret_cast<const f32x4*>(a.dres + ((size_t)c * a.S + pj[j]) * a.d_out + o);
-#pragma unroll
-        for (int j = 0; j < KR; ++j) v += dv[j];
       } else {
         for (int j = 0; j < k; ++j) {
           const int pos = a.inv[t * k + j];

@@ -135,13 +135,35 @@ int choose_path(const tq_layer* L, int T, int k) {
 }
 
 // column stage split-K for decode: slabs of 1024 inputs
-int choose_nsplit(int path, long rows, int d_in) {
-  (void)rows;
-  if (path != 1) return 1;
-  return decode_col_splits(d_in);
-}
-
 int device_cus();
+
+// Column-stage k-splits.  Decode: see decode_col_splits.  Prefill: only the
+// projection whose rank vectors go to the combine as fp32 (down, or the
+// single projection) is split, when its row tiles (about rows / 128 + K)
+// would run one workgroup per CU: n splits of the k-range run in
+// ceil(tiles n / (2 CUs)) rounds of 1/n the length; each extra slab costs the
+// combine a read, charged as 3 % of the unsplit time.  Each split keeps at
+// least 32 k-steps.
+int choose_nsplit(const tq_layer* L, int q, int path, long rows, int d_in) {
+  if (path == 1) return decode_col_splits(d_in);
+  const bool to_combine = (L->kind == TQ_SWIGLU) ? (q == 2) : (q == 0);
+  if (!to_combine) return 1;
+  const long tiles = (rows + 127) / 128 + L->K;
+  const long slots = 2L * device_cus();
+  const int nst = d_in >> 5;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int n = 1; n <= 8; ++n) {
+    if (n > 1 && nst / n < 32) break;
+    const long rounds = (tiles * n + slots - 1) / slots;
+    const double cost = (double)rounds / n + 0.03 * (n - 1);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = n;
+    }
+  }
+  return best;
+}
 
 // k-chunks of the decode kernel for a down / single projection: the most
 // (up to 8, each chunk keeping at least 4 stages) for which the active
@@ -269,7 +291,7 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
     p.P[q] = 0;
     if (q >= nproj(L)) continue;
     const ProjDev& d = L->proj[q].dev;
-    p.nsplit[q] = choose_nsplit(path, S, d.d_in);
+    p.nsplit[q] = choose_nsplit(L, q, path, S, d.d_in);
     if (d.r_pad > 0) p.P[q] = take((size_t)p.nsplit[q] * p.rows_cap * d.r_pad * sizeof(float));
   }
   const bool bf = (L->act == TQ_BF16);
@@ -930,7 +952,7 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
     cb.n_of = d.n_of;
     cb.m_of = d.m_of;
     cb.P = d.r_pad ? at<float>(ws, p.P[q]) : nullptr;
-    cb.nsplit = 1;
+    cb.nsplit = dec ? 1 : p.nsplit[q];   // decode: the residual kernel summed P's slabs
     cb.rows_cap = p.rows_cap;
     cb.U = d.U;
     cb.dres = dres;

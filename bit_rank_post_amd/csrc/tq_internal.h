@@ -99,8 +99,9 @@ struct ColArgs {
   int ap_T;                      // > 0: every (column, token) pair, row = n * ap_T + t
                                  // (no work lists; seg_off/tile_off/row_src unused)
 };
-// prefill column stage (ap_T == 0, nsplit == 1: one workgroup covers the
-// whole k-range of its rows): tiles of 128 rows (route rt_col 128)
+// prefill column stage (ap_T == 0; nsplit > 1 only for an fp32 P consumed
+// by the combine: k-ranges over blockIdx.z, slab stride rows_cap rows):
+// tiles of 128 rows (route rt_col 128)
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
                     hipStream_t s);
 

@@ -275,6 +275,25 @@ def test_bf16_swiglu_token_magnitudes(path):
         assert_parity(y[rows], ref[rows], what=f"bf16 tokens x 2^{sh} path={path}")
 
 
+@pytest.mark.parametrize("kind", ["swiglu", "single"])
+def test_prefill_column_stage_k_split(kind):
+    """Prefill with 2048-wide inputs to the projection whose rank vectors go to
+    the combine: its column stage runs in k-range splits (fp32 slabs summed by
+    the combine)."""
+    if kind == "swiglu":
+        layer = small_swiglu("f16", 41, d_model=256, d_ff=2048)
+        d_in = 256
+    else:
+        layer = single_layer_from(synth.make_proj(8, 2, 4, 2048, 256, 32, 64, "f16",
+                                                  np.random.SeedSequence(43)))
+        d_in = 2048
+    L = tqio.upload_layer(layer)
+    L.set_path(2)
+    x, ids, g = synth.make_custom_tokens(d_in, 8, 2, 300, "f16", seed=44)
+    y, _ = run_forward(L, x, ids, g, "f16", "f32")
+    assert_parity(y, R.forward(layer, x, ids, g), what=f"{kind} prefill, column stage k-split")
+
+
 @pytest.mark.parametrize("path,T", [(1, 24), (2, 300)])
 def test_small_swiglu_with_shared_expert(path, T):
     """The shared expert (on the layer's second stream) at decode and prefill."""
