@@ -197,6 +197,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--scheme", default="tileq",
+                    choices=("tileq", "rank0", "per_expert", "shared_u", "shared_v"),
+                    help="weight-sharing scheme of the low-rank part (as a tile map); "
+                         "the others are comparisons: rank0, per_expert, shared_u, shared_v")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -218,7 +222,8 @@ def main():
     cfg_name, T = WORKLOADS[args.workload]
     cfg = synth.CONFIG_BY_NAME[cfg_name]
     print(f"[bench] generating {cfg_name} (T={T})", file=sys.stderr, flush=True)
-    layer = synth.make_layer(cfg)
+    layer = synth.make_layer(cfg, scheme=args.scheme)
+    pg = layer["proj"]["single" if cfg.kind == "single" else "gate"]
     x, ids, gates = synth.make_tokens(cfg, T)
     copies = max(1, args.copies)
     Ls = [tqio.upload_layer(layer) for _ in range(copies)]
@@ -304,7 +309,8 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_F16_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_F16_TFLOPS, 4))
     path_name = "decode" if decode else "prefill"
-    tr = traffic_from_profile(args.workload, path_name)
+    # (the counter summaries are taken with the grid of the configuration)
+    tr = traffic_from_profile(args.workload, path_name) if args.scheme == "tileq" else None
     roof["traffic"] = tr
     roof["kernel"] = KERNEL_NAMES[path_name]
     roof["kernel_ms"] = round(dom_ms, 5)
@@ -330,8 +336,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg_name}: {cfg.K} experts on {cfg.M}x{cfg.N} grid, "
-                               f"d_model {cfg.d_model}, d_ff {cfg.d_ff}, rank {cfg.rank}, "
+        "config": {"workload": f"{cfg_name}: {cfg.K} experts on {pg['M']}x{pg['N']} grid"
+                               f"{'' if args.scheme == 'tileq' else ' (' + args.scheme + ')'}, "
+                               f"d_model {cfg.d_model}, d_ff {cfg.d_ff}, rank {pg['rank']}, "
                                f"2-bit group-{cfg.group} residual, top-{cfg.topk}, "
                                f"{cfg.act} activations, T={T} tokens, "
                                f"{'decode' if decode else 'prefill'} path",

@@ -161,11 +161,15 @@ def _residual_expert(ss, d_out, d_in, group, std):
 
 
 def make_proj(K, M, N, d_in, d_out, rank, group, act, seedseq,
-              residual_std=0.02, threads=None):
-    """One projection's uploaded arrays (see module docstring)."""
+              residual_std=0.02, threads=None, tiles=None):
+    """One projection's uploaded arrays (see module docstring).  tiles: the
+    expert -> tile map (default: a random injective map)."""
     assert K <= M * N and d_in % group == 0 and d_in % 16 == 0
     ss_map, ss_u, ss_sig, ss_v, ss_res = seedseq.spawn(5)
-    tiles = np.random.default_rng(ss_map).permutation(M * N)[:K].astype(np.int32)
+    if tiles is None:
+        tiles = np.random.default_rng(ss_map).permutation(M * N)[:K].astype(np.int32)
+    else:
+        tiles = np.asarray(tiles, np.int32)
     U = np.random.default_rng(ss_u).standard_normal(
         (M * d_out, rank), dtype=np.float32) / np.float32(np.sqrt(d_out))
     V = np.random.default_rng(ss_v).standard_normal(
@@ -192,15 +196,43 @@ def _streams(cfg: LayerConfig):
     return dict(zip(names, root.spawn(len(names))))
 
 
-def make_layer(cfg: LayerConfig, threads=None, rank=None):
+# Weight-sharing schemes of the low-rank part, all expressed as tile maps
+# (the same kernels and routing serve every one):
+#   tileq       the configuration's M x N grid, random injective map
+#   rank0       no low-rank part (pure 2-bit residual MoE)
+#   per_expert  every expert its own U and V: K x K grid, expert e at (e, e)
+#   shared_u    one U for all experts, V per expert: 1 x K grid, e at (0, e)
+#   shared_v    one V for all experts, U per expert: K x 1 grid, e at (e, 0)
+SCHEMES = ("tileq", "rank0", "per_expert", "shared_u", "shared_v")
+
+
+def scheme_grid(cfg: LayerConfig, scheme: str):
+    """(M, N, tiles or None) of a weight-sharing scheme."""
+    K = cfg.K
+    e = np.arange(K, dtype=np.int32)
+    if scheme in ("tileq", "rank0"):
+        return cfg.M, cfg.N, None
+    if scheme == "per_expert":
+        return K, K, e * K + e
+    if scheme == "shared_u":
+        return 1, K, e
+    if scheme == "shared_v":
+        return K, 1, e
+    raise ValueError(scheme)
+
+
+def make_layer(cfg: LayerConfig, threads=None, rank=None, scheme="tileq"):
     """All weights of a configuration: {"proj": {name: proj}, "shared": ...}."""
     st = _streams(cfg)
     r = cfg.rank if rank is None else rank
+    if scheme == "rank0":
+        r = 0
+    M, N, tiles = scheme_grid(cfg, scheme)
     proj = {}
     for name, (d_in, d_out) in cfg.proj_shapes().items():
         key = "single_or_gate" if name in ("single", "gate") else name
-        proj[name] = make_proj(cfg.K, cfg.M, cfg.N, d_in, d_out, r, cfg.group,
-                               cfg.act, st[key], threads=threads)
+        proj[name] = make_proj(cfg.K, M, N, d_in, d_out, r, cfg.group,
+                               cfg.act, st[key], threads=threads, tiles=tiles)
     layer = dict(kind=cfg.kind, act=cfg.act, K=cfg.K, d_model=cfg.d_model,
                  d_ff=cfg.d_ff, proj=proj, shared=None)
     if cfg.shared_ff:

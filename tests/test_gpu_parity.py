@@ -294,6 +294,28 @@ def test_prefill_column_stage_k_split(kind):
     assert_parity(y, R.forward(layer, x, ids, g), what=f"{kind} prefill, column stage k-split")
 
 
+@pytest.mark.parametrize("scheme", ["per_expert", "shared_u", "shared_v", "rank0"])
+@pytest.mark.parametrize("path", [1, 2])
+def test_weight_schemes(scheme, path):
+    """The comparison schemes of the low-rank part (per-expert factors, one
+    factor shared by all experts, none) as tile maps through the same path."""
+    from types import SimpleNamespace
+    K = 8
+    M, N, tiles = synth.scheme_grid(SimpleNamespace(K=K, M=2, N=4), scheme)
+    r = 0 if scheme == "rank0" else 16
+    ss = np.random.SeedSequence(51).spawn(3)
+    proj = {n: synth.make_proj(K, M, N, di, do, r, 64, "f16", q, tiles=tiles)
+            for (n, (di, do)), q in zip([("gate", (256, 384)), ("up", (256, 384)),
+                                         ("down", (384, 256))], ss)}
+    layer = dict(kind="swiglu", act="f16", K=K, d_model=256, d_ff=384, proj=proj, shared=None)
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    T = 24 if path == 1 else 300
+    x, ids, g = synth.make_custom_tokens(256, K, 2, T, "f16", seed=52)
+    y, _ = run_forward(L, x, ids, g, "f16", "f32")
+    assert_parity(y, R.forward(layer, x, ids, g), what=f"scheme {scheme} path={path}")
+
+
 @pytest.mark.parametrize("path,T", [(1, 24), (2, 300)])
 def test_small_swiglu_with_shared_expert(path, T):
     """The shared expert (on the layer's second stream) at decode and prefill."""

@@ -58,3 +58,24 @@ def test_skewed_routing_shapes():
     cnt = np.bincount(ids.reshape(-1), minlength=8)
     hot = np.sort(cnt)[-4:].sum() / cnt.sum()
     assert 0.6 < hot < 0.8
+
+
+def test_weight_scheme_maps():
+    """Each comparison scheme is an injective tile map on its grid: per-expert
+    factors put expert e alone in grid row e and column e; shared_u puts every
+    expert in grid row 0 (one U), shared_v in grid column 0 (one V)."""
+    cfg = synth.CONFIG_BY_NAME["mixtral8x7b_decode"]
+    K = cfg.K
+    for scheme in synth.SCHEMES:
+        M, N, tiles = synth.scheme_grid(cfg, scheme)
+        if tiles is None:
+            assert (M, N) == (cfg.M, cfg.N)
+            continue
+        assert len(set(tiles.tolist())) == K and tiles.min() >= 0 and tiles.max() < M * N
+        rows, cols = tiles // N, tiles % N
+        if scheme == "per_expert":
+            assert (M, N) == (K, K) and list(rows) == list(range(K)) and list(cols) == list(range(K))
+        elif scheme == "shared_u":
+            assert M == 1 and set(rows.tolist()) == {0} and sorted(cols.tolist()) == list(range(K))
+        else:
+            assert N == 1 and set(cols.tolist()) == {0} and sorted(rows.tolist()) == list(range(K))
