@@ -150,6 +150,34 @@ def deq_canonical(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
     return rnd_act(w32.astype(np.float64), out)
 
 # ----------------------------------------------------------------------------
+# router (upstream of section 2.2, which takes the routing weights as given)
+
+
+def router_topk(logits: np.ndarray, k: int):
+    """Top-k routing of each row of router logits [T][K]: the k largest
+    logits in descending order, ties to the lower expert id, NaN read as
+    -inf; the weights are the softmax over the k selected logits (uniform
+    when the largest selected logit is -inf).  Returns (ids int32 [T][k],
+    weights fp64 [T][k]).  The pages name no router; this is the plain top-k
+    router a fused forward is fed by."""
+    L = np.asarray(logits, np.float64)
+    L = np.where(np.isnan(L), -np.inf, L)
+    T, K = L.shape
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k))
+    for t in range(T):
+        order = sorted(range(K), key=lambda e: (-L[t, e], e))[:k]
+        ids[t] = order
+        v = L[t, order]
+        if v[0] == -np.inf:
+            w[t] = 1.0 / k
+        else:
+            ex = np.exp(v - v[0])
+            w[t] = ex / ex.sum()
+    return ids, w
+
+
+# ----------------------------------------------------------------------------
 # routing lists (the unique grouping the fused forward must build)
 
 

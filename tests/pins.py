@@ -465,9 +465,36 @@ def pin_route(ref):
         check_route(r, ids, 8, n_of)
 
 
+def pin_router(ref):
+    """Router top-k: ids against numpy's stable argsort of -logits (ties to the
+    lower id); weights against scipy's softmax when k = K (then the selected
+    logits are all of them) and, for k < K, the closed-form ratios
+    w_i / w_j = exp(l_i - l_j) with sum 1; k = 1 gives weight 1; NaN logits
+    are never chosen before finite ones; all -inf gives uniform weights."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(71)
+    for K, k in [(8, 2), (60, 4), (64, 6), (256, 8), (5, 5), (16, 1)]:
+        L = rng.standard_normal((40, K))
+        L[:10] = np.round(L[:10] * 2) / 2            # many ties
+        ids, w = ref.router_topk(L, k)
+        want = np.argsort(-L, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, want), (K, k)
+        sel = np.take_along_axis(L, want, axis=1)
+        assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        assert np.allclose(np.log(w[:, 1:] / w[:, :1]), sel[:, 1:] - sel[:, :1], atol=1e-9)
+        if k == K:
+            assert np.allclose(w, np.take_along_axis(softmax(L, axis=1), want, axis=1), atol=1e-12)
+        if k == 1:
+            assert np.all(w == 1.0)
+    L = np.array([[np.nan, 1.0, np.nan, -2.0], [-np.inf] * 4])
+    ids, w = ref.router_topk(L, 2)
+    assert ids[0].tolist() == [1, 3] and ids[1].tolist() == [0, 1]
+    assert np.allclose(w[1], 0.5)
+
+
 ALL_PINS = [pin_unpack_golden, pin_unpack_bytes, pin_residual_golden, pin_deq_golden,
             pin_rnd_f16_vs_numpy, pin_rnd_bf16, pin_silu, pin_p1_factored_block,
             pin_p2_zero_rank, pin_p3_zero_residual, pin_p4_token_perm, pin_p5_slots,
             pin_p6_textbook, pin_p7_grid_relabel, pin_p8_linearity, pin_dropped_ids,
             pin_p11_two_oracles, pin_p12_storage, pin_swiglu_closed_form,
-            pin_shared_closed_form, pin_route]
+            pin_shared_closed_form, pin_route, pin_router]

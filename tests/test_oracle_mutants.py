@@ -135,10 +135,33 @@ def m_deq_double_round(r):
     r.deq_canonical = deq_canonical
 
 
+def m_router_ties_high(r):
+    orig = r.router_topk
+
+    def router_topk(logits, k):
+        L = np.asarray(logits, np.float64)
+        flipped = L[:, ::-1]                       # ties now go to the higher id
+        ids, w = orig(flipped, k)
+        return (L.shape[1] - 1 - ids).astype(np.int32), w
+    r.router_topk = router_topk
+
+
+def m_router_softmax_all(r):
+    orig = r.router_topk
+
+    def router_topk(logits, k):
+        ids, _ = orig(logits, k)
+        L = np.asarray(logits, np.float64)
+        ex = np.exp(L - L.max(axis=1, keepdims=True))
+        w = ex / ex.sum(axis=1, keepdims=True)     # not renormalised over the k
+        return ids, np.take_along_axis(w, ids, axis=1)
+    r.router_topk = router_topk
+
+
 MUTANTS = [m_zero_sign, m_group_index, m_bit_order, m_drop_sigma, m_swap_mn,
            m_tile_stride, m_wrong_expert_residual, m_ignore_gates, m_swiglu_swap,
            m_silu_sign, m_rnd_truncate, m_route_unstable, m_transposed_down,
-           m_deq_double_round]
+           m_deq_double_round, m_router_ties_high, m_router_softmax_all]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
