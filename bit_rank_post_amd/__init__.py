@@ -23,7 +23,7 @@ STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHI
           5: "TQ_EUNSUPPORTED", 6: "TQ_ESTATE"}
 EXPORTS = ["tq_layer_create", "tq_upload_proj", "tq_upload_shared_expert",
            "tq_workspace_size", "tq_forward", "tq_layer_destroy", "tq_last_error",
-           "tq_abi_version", "tq_layer_set_path", "tq_debug_route", "tq_debug_dequant", "tq_debug_row_bound",
+           "tq_abi_version", "tq_layer_set_path", "tq_debug_route", "tq_debug_dequant", "tq_debug_row_bound", "tq_router_topk",
            "tq_profile_enable", "tq_profile_read"]
 STAGES = ["route", "row_exponent", "column_stage_in", "gemm_in", "column_stage_down",
           "shared_expert", "gemm_down", "combine"]
@@ -69,6 +69,7 @@ def lib():
         L.tq_debug_route.argtypes = [vp, i32, vp, i32, i32, vp, sz] + [vp] * 7 + [vp]
         L.tq_debug_dequant.argtypes = [vp, i32, i32, vp, vp]
         L.tq_debug_row_bound.argtypes = [vp, i32, vp]
+        L.tq_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.tq_profile_enable.argtypes = [vp, i32]
         L.tq_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
         for name in EXPORTS:
@@ -94,6 +95,14 @@ def _stream(stream):
         import torch
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+
+
+def router_topk(logits, k, ids, weights, stream=None):
+    """Top-k router on the device: logits f32 [T][K] -> ids int32 [T][k],
+    weights f32 [T][k] (caller-allocated device tensors)."""
+    T, K = logits.shape
+    _check("tq_router_topk", lib().tq_router_topk(_ptr(logits), T, K, k, _ptr(ids), _ptr(weights),
+                                                  _stream(stream)))
 
 
 class Layer:

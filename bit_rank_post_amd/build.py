@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtileq.so")
 SOURCES = ["route.hip", "colproj.hip", "gemm_prefill.hip", "gemm_decode.hip", "decode_stages.hip",
-           "combine.hip", "upload.hip", "tileq_host.cpp"]
+           "combine.hip", "upload.hip", "router.hip", "tileq_host.cpp"]
 
 
 def hipcc():

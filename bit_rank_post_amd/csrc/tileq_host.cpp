@@ -1062,6 +1062,18 @@ tq_status tq_debug_dequant(const tq_layer* L, int32_t which, int32_t expert, voi
   return TQ_OK;
 }
 
+tq_status tq_router_topk(const float* logits, int32_t T, int32_t K, int32_t k, int32_t* ids,
+                         float* weights, void* stream) {
+  if (T < 0) return fail(TQ_ESHAPE, "T = %d < 0", T);
+  if (K < 1 || K > 256) return fail(TQ_ESHAPE, "K = %d outside [1, 256]", K);
+  if (k < 1 || k > K || k > 32) return fail(TQ_ESHAPE, "k = %d outside [1, min(K, 32)]", k);
+  if (T == 0) return TQ_OK;
+  if (!logits || !ids || !weights) return fail(TQ_EINVAL, "NULL pointer");
+  launch_router_topk(logits, T, K, k, ids, weights, reinterpret_cast<hipStream_t>(stream));
+  HIPCHK(hipGetLastError());
+  return TQ_OK;
+}
+
 tq_status tq_debug_row_bound(const tq_layer* L, int32_t which, float* l1_out) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");
   if (which < 0 || which >= nproj(L)) return fail(TQ_EINVAL, "projection %d not in layer", which);

@@ -249,6 +249,9 @@ struct RowBoundArgs {
   float* l1max;                  // [K], zero on entry
 };
 void launch_row_bound(const RowBoundArgs& b, hipStream_t s);
+// top-k router: logits [T][K] (K <= 256) -> ids, weights [T][k] (k <= 32)
+void launch_router_topk(const float* logits, int T, int K, int k, int* ids, float* w,
+                        hipStream_t s);
 void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStream_t s);
 void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_pad,
                         hipStream_t s);

@@ -181,6 +181,18 @@ tq_status tq_debug_route(const tq_layer *L, int32_t which, const int32_t *topk_i
 tq_status tq_debug_dequant(const tq_layer *L, int32_t which, int32_t expert, void *w_out,
                            void *stream);
 
+/* Top-k router feeding tq_forward (section 2.2 takes the routing weights of
+ * the active experts as given; the pages name no router, this is the plain
+ * top-k one).  For each of T rows of logits (DEVICE f32 [T][K]): the k
+ * largest logits in descending order, ties to the lower expert id, NaN read
+ * as -inf, written to ids (DEVICE int32 [T][k]); weights (DEVICE f32 [T][k])
+ * = softmax over the k selected logits (uniform 1/k when the largest
+ * selected logit is -inf).  Asynchronous on `stream`; no layer needed.
+ * Errors: TQ_EINVAL (NULL pointer with T > 0), TQ_ESHAPE (T < 0, K outside
+ * [1, 256], k outside [1, min(K, 32)]), TQ_EHIP. */
+tq_status tq_router_topk(const float *logits, int32_t T, int32_t K, int32_t k, int32_t *ids,
+                         float *weights, void *stream);
+
 /* Copy the per-expert row bound of one projection to l1_out (HOST f32 [K]):
  * an upper bound on max_o sum_i |W_e[o][i]| of the effective weight
  * W_e = U_m Sigma V_n^T + R_e (section 2.1), the sum over the residual's

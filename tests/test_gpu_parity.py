@@ -316,6 +316,49 @@ def test_weight_schemes(scheme, path):
     assert_parity(y, R.forward(layer, x, ids, g), what=f"scheme {scheme} path={path}")
 
 
+@pytest.mark.parametrize("K,k", [(8, 2), (60, 4), (64, 6), (256, 8), (5, 5), (128, 32), (16, 1)])
+def test_router_topk(K, k):
+    """Router: ids bit-exact with the oracle (ties from rounded logits, NaN and
+    -inf rows included), weights within 1e-6; then its outputs drive a
+    forward."""
+    rng = np.random.default_rng(81 + K + k)
+    T = 700
+    L = rng.standard_normal((T, K)).astype(np.float32)
+    L[:100] = np.round(L[:100] * 2) / 2
+    L[100, :] = np.nan
+    L[101, :] = -np.inf
+    L[102, ::2] = np.nan
+    ld = torch.from_numpy(L).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    tq.router_topk(ld, k, ids, w)
+    torch.cuda.synchronize()
+    want_ids, want_w = R.router_topk(L, k)
+    assert np.array_equal(ids.cpu().numpy(), want_ids)
+    err = float(np.max(np.abs(w.cpu().numpy().astype(np.float64) - want_w)))
+    say(f"  router K={K} k={k}: ids exact, max|dw| = {err:.2e}")
+    assert err <= 1e-6
+
+
+def test_router_feeds_forward():
+    layer = small_swiglu("f16", 61)
+    L = tqio.upload_layer(layer)
+    T, k = 300, 2
+    x, _, _ = synth.make_custom_tokens(256, 8, k, T, "f16", seed=62)
+    logits = np.random.default_rng(63).standard_normal((T, 8)).astype(np.float32)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    tq.router_topk(torch.from_numpy(logits).cuda(), k, ids, w)
+    xd = tqio.to_device(x, "f16")
+    y = torch.empty((T, 256), dtype=torch.float32, device="cuda")
+    ws = tqio.workspace(L, T, k)
+    L.forward(xd, T, ids, w, k, y, tq.TQ_F32, ws)
+    torch.cuda.synchronize()
+    rid, rw = R.router_topk(logits, k)
+    assert_parity(y.cpu().numpy().astype(np.float64), R.forward(layer, x, rid, rw),
+                  what="router -> forward")
+
+
 @pytest.mark.parametrize("path,T", [(1, 24), (2, 300)])
 def test_small_swiglu_with_shared_expert(path, T):
     """The shared expert (on the layer's second stream) at decode and prefill."""
