@@ -198,6 +198,28 @@ def test_special_cases_single(path):
         assert_parity(y, R.forward_single(p, x, ids, g), what=f"{name} duplicates")
 
 
+@pytest.mark.parametrize("path", [1, 2])
+def test_empty_and_largest_grid(path):
+    """T = 0 is a no-op; the largest grid the library takes (K = 256 experts
+    on 32 x 32 = 1024 tiles, rank 128, top-8) at both paths."""
+    p, _ = pins.random_struct(256, 32, 32, 128, 32, 128, 64, seed=91)
+    layer = single_layer_from(p)
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    ws = tqio.workspace(L, 1, 8)
+    y0 = torch.full((1, 32), 7.0, device="cuda")
+    e32 = torch.empty((0, 8), dtype=torch.int32, device="cuda")
+    ef = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    L.forward(torch.empty((0, 128), dtype=torch.float16, device="cuda"), 0, e32, ef, 8, y0,
+              tq.TQ_F32, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y0 == 7.0)                 # nothing written
+    T = 200
+    x, ids, g = pins.tokens(128, 256, 8, T, seed=92)
+    y, _ = run_forward(L, x, ids, g, "f16", "f32")
+    assert_parity(y, R.forward_single(p, x, ids, g), what=f"K=256 on 32x32 path={path}")
+
+
 def test_token_permutation_device():
     p, _ = pins.random_struct(8, 2, 4, 256, 64, 16, 64, seed=41)
     L = tqio.upload_layer(single_layer_from(p))
