@@ -25,7 +25,11 @@ constexpr int CB_KMAX = 32;                 // slots per token
 constexpr int CB_MMAX = 1024;               // grid rows
 constexpr int CB_LDS = 64 * 1024;           // resident S budget (dynamic LDS, at most)
 
-template <typename T, typename YT>
+// PERSLOT: the residual outputs of a token are gathered slot by slot with
+// all k-chunk slabs of a slot requested together (few slots, several slabs:
+// decode); else the first slab of every slot is requested together and
+// further slabs follow one round trip each.
+template <typename T, typename YT, bool PERSLOT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int cpw, int lds_bytes) {
   typedef typename Vec8<T>::type V8;
   constexpr int KR = 8;                     // slots per token held in registers
@@ -218,9 +222,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int cpw, in
     // before the MFMAs
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ovalid && t < a.T) {
-      if (k <= KR) {
-        // per slot, up to NKB k-chunk slabs requested together (one round
-        // trip per slot instead of one per slab), summed in slab order
+      if (k <= KR && !PERSLOT) {
+        // the first slab of every slot requested together, further slabs
+        // (if any) one round trip each
+        f32x4 dv[KR];
+#pragma unroll
+        for (int j = 0; j < KR; ++j) {
+          dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (pj[j] >= 0) dv[j] = *reinterpret_cast<const f32x4*>(a.dres + (size_t)pj[j] * a.d_out + o);
+        }
+        for (int c = 1; c < a.nks; ++c)
+#pragma unroll
+          for (int j = 0; j < KR; ++j)
+            if (pj[j] >= 0)
+              dv[j] += *reinterpret_cast<const f32x4*>(a.dres + ((size_t)c * a.S + pj[j]) * a.d_out + o);
+#pragma unroll
+        for (int j = 0; j < KR; ++j) v += dv[j];
+      } else if (k <= KR) {
+        // few slots, several k-chunk slabs (decode): per slot, up to NKB
+        // slabs requested together (one round trip per slot instead of one
+        // per slab), summed in slab order
         constexpr int NKB = 8;
 #pragma unroll
         for (int j = 0; j < KR; ++j) {
@@ -275,6 +296,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int cpw, in
   }
 }
 
+template <bool PERSLOT>
+static void combine_dt(const CombineArgs& a, Act act, dim3 grid, size_t lds, int lb, int cpw,
+                       hipStream_t s) {
+  if (act == ACT_F16) {
+    if (a.y_dtype == 0) hipLaunchKernelGGL((combine_kernel<half_t, half_t, PERSLOT>), grid, dim3(256), lds, s, a, cpw, lb);
+    else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<half_t, __bf16, PERSLOT>), grid, dim3(256), lds, s, a, cpw, lb);
+    else hipLaunchKernelGGL((combine_kernel<half_t, float, PERSLOT>), grid, dim3(256), lds, s, a, cpw, lb);
+  } else {
+    if (a.y_dtype == 0) hipLaunchKernelGGL((combine_kernel<__bf16, half_t, PERSLOT>), grid, dim3(256), lds, s, a, cpw, lb);
+    else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<__bf16, __bf16, PERSLOT>), grid, dim3(256), lds, s, a, cpw, lb);
+    else hipLaunchKernelGGL((combine_kernel<__bf16, float, PERSLOT>), grid, dim3(256), lds, s, a, cpw, lb);
+  }
+}
+
 void launch_combine(const CombineArgs& a, Act act, hipStream_t s) {
   // output chunks per workgroup: about 4 workgroups per CU over the grid
   const int tiles = (a.T + 15) / 16;
@@ -292,15 +327,8 @@ void launch_combine(const CombineArgs& a, Act act, hipStream_t s) {
     lds = (size_t)rows * per_row <= (size_t)CB_LDS ? (size_t)rows * per_row : per_row;
   }
   const int lb = (int)lds;
-  if (act == ACT_F16) {
-    if (a.y_dtype == 0) hipLaunchKernelGGL((combine_kernel<half_t, half_t>), grid, dim3(256), lds, s, a, cpw, lb);
-    else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<half_t, __bf16>), grid, dim3(256), lds, s, a, cpw, lb);
-    else hipLaunchKernelGGL((combine_kernel<half_t, float>), grid, dim3(256), lds, s, a, cpw, lb);
-  } else {
-    if (a.y_dtype == 0) hipLaunchKernelGGL((combine_kernel<__bf16, half_t>), grid, dim3(256), lds, s, a, cpw, lb);
-    else if (a.y_dtype == 1) hipLaunchKernelGGL((combine_kernel<__bf16, __bf16>), grid, dim3(256), lds, s, a, cpw, lb);
-    else hipLaunchKernelGGL((combine_kernel<__bf16, float>), grid, dim3(256), lds, s, a, cpw, lb);
-  }
+  if (a.nks > 1 && a.topk <= 2) combine_dt<true>(a, act, grid, lds, lb, cpw, s);
+  else combine_dt<false>(a, act, grid, lds, lb, cpw, s);
 }
 
 }  // namespace tq
