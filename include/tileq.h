@@ -197,7 +197,7 @@ tq_status tq_router_topk(const float *logits, int32_t T, int32_t K, int32_t k, i
  * an upper bound on max_o sum_i |W_e[o][i]| of the effective weight
  * W_e = U_m Sigma V_n^T + R_e (section 2.1), the sum over the residual's
  * |s (q - z)| plus sum_r |U_m[o][r]| |sigma_r| sum_i |V_n[i][r]|, computed
- * in fp32 at upload (the largest finite fp32 where that overflows).  The
+ * in fp32 at upload (3e38 where that overflows or is NaN).  The
  * forward of bfloat16 SWIGLU layers at prefill scales its fp16 copy of the
  * intermediate h by a power of two derived from the gate and up bounds.
  * Synchronous.  Errors: TQ_EINVAL, TQ_ESTATE (not uploaded), TQ_EHIP. */
