@@ -14,8 +14,11 @@ Prints one JSON line.  `value` is tokens/s of the whole forward; `roofline`
 gives the dominant kernel's achieved algorithmic bandwidth (or MFMA rate)
 from HIP events recorded around that kernel on its own stream, in a second
 pass over the same steps; `cpu_baseline` times the CPU oracle on a bounded
-sample of the same batch.  Other workloads (--workload) are for the builder's
-own measurements; the default line is the reported one.
+sample of the same batch.  The prefill half of the metric is measured in the
+same run and reported in the `prefill` object: the Mixtral-shaped layer at
+rank 128 with 16384 bf16 tokens and 70/30 expert imbalance (ms per step,
+tokens/s, the gate/up kernel's MFMA rate against the dense fp16/bf16 peak).
+Other workloads (--workload) are single measurements without that object.
 """
 from __future__ import annotations
 
@@ -190,6 +193,133 @@ def cpu_baseline(layer, x, ids, gates, n_tok, min_s=10.0):
                        f"building each used expert weight explicitly per chunk ({dt:.1f} s wall)")
 
 
+def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
+    """Time `steps` forwards of a workload (eager launches, then the same steps
+    replayed from HIP graphs), then a profiled pass for the stage durations.
+    Returns the fields of a bench record (without the CPU baseline) and the
+    generated arrays."""
+    import torch
+
+    import bit_rank_post_amd as tq
+    import synth
+    from bit_rank_post_amd import io as tqio
+
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    cfg_name, T = WORKLOADS[workload]
+    cfg = synth.CONFIG_BY_NAME[cfg_name]
+    say(f"generating {cfg_name} (T={T})")
+    layer = synth.make_layer(cfg, scheme=scheme)
+    pg = layer["proj"]["single" if cfg.kind == "single" else "gate"]
+    x, ids, gates = synth.make_tokens(cfg, T)
+    copies = max(1, copies)
+    Ls = [tqio.upload_layer(layer) for _ in range(copies)]
+    xd, idd, gd = tqio.tokens_to_device(x, ids, gates, cfg.act)
+    k = cfg.topk
+    d_out = cfg.d_ff if cfg.kind == "single" else cfg.d_model
+    y = torch.empty((T, d_out), dtype=torch.float16 if cfg.act == "f16" else torch.bfloat16,
+                    device="cuda")
+    ydt = tq.TQ_F16 if cfg.act == "f16" else tq.TQ_BF16
+    ws = tqio.workspace(Ls[0], T, k)
+    decode = Ls[0].forward_path(T, k) == 1
+    say(f"uploaded {copies} copies; path={'decode' if decode else 'prefill'}")
+
+    def step(i):
+        Ls[i % copies].forward(xd, T, idd, gd, k, y, ydt, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = 1e3 * (time.perf_counter() - t0) / steps
+    say(f"timed {steps} steps: {eager_ms * 1e3:.1f} us/step")
+
+    # the same steps replayed from HIP graphs (one captured forward per weight
+    # copy): removes the host launch path and most inter-kernel gaps
+    graph_ms = None
+    try:
+        graphs = []
+        for i in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        graph_ms = 1e3 * (time.perf_counter() - t0) / steps
+        say(f"graph replay: {graph_ms * 1e3:.1f} us/step")
+        del graphs
+    except Exception as exc:  # noqa: BLE001 - report eager numbers only
+        say(f"graph capture unavailable: {exc}")
+
+    # second pass: stage durations from HIP events on the forward's stream
+    for L in Ls:
+        L.profile_enable(True)
+    acc = None
+    for i in range(steps):
+        step(i)
+        st = Ls[i % copies].profile_read()
+        acc = st if acc is None else {kk: acc[kk] + st[kk] for kk in acc}
+    for L in Ls:
+        L.profile_enable(False)
+    stages_ms = {kk: v / steps for kk, v in acc.items()}
+
+    work = algorithmic(layer, ids, T)
+    dom_ms = stages_ms["gemm_in"]
+    if decode:
+        achieved = work["dom_bytes"] / (dom_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4))
+    else:
+        achieved = work["dom_flops"] / (dom_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_F16_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / PEAK_F16_TFLOPS, 4))
+    path_name = "decode" if decode else "prefill"
+    # (the counter summaries are taken with the grid of the configuration)
+    tr = traffic_from_profile(workload, path_name) if scheme == "tileq" else None
+    roof["traffic"] = tr
+    roof["kernel"] = KERNEL_NAMES[path_name]
+    roof["kernel_ms"] = round(dom_ms, 5)
+    roof["algorithmic_bytes_per_launch"] = work["dom_bytes"]
+    roof["algorithmic_flops_per_launch"] = work["dom_flops"]
+
+    # both loops time the same steps of the same forward; the faster execution
+    # mode is reported, the other one beside it
+    use_graph = graph_ms is not None and graph_ms < eager_ms
+    ms = graph_ms if use_graph else eager_ms
+    rec = {
+        "workload": f"{cfg_name}: {cfg.K} experts on {pg['M']}x{pg['N']} grid"
+                    f"{'' if scheme == 'tileq' else ' (' + scheme + ')'}, "
+                    f"d_model {cfg.d_model}, d_ff {cfg.d_ff}, rank {pg['rank']}, "
+                    f"2-bit group-{cfg.group} residual, top-{cfg.topk}, "
+                    f"{cfg.act} activations, T={T} tokens, {path_name} path",
+        "T": T, "dtype": cfg.act, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+        "roofline": roof, "execution": "hip_graph_replay" if use_graph else "eager",
+        "eager_ms_per_step": round(eager_ms, 5),
+        "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
+        "stages_ms": {kk: round(v, 5) for kk, v in stages_ms.items()},
+        "whole_forward": {"algorithmic_bytes": work["total_bytes"],
+                          "algorithmic_flops": work["total_flops"],
+                          "achieved_GBps": round(work["total_bytes"] / (ms * 1e-3) / 1e9, 1),
+                          "achieved_TFLOPs": round(work["total_flops"] / (ms * 1e-3) / 1e12, 2),
+                          "active_experts": work["active_experts"]},
+        "kernel_source_sha256": kernel_hash(path_name),
+        "grid": (pg["M"], pg["N"]),
+    }
+    for L in Ls:
+        L.close()
+    return rec, (layer, x, ids, gates)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +332,9 @@ def main():
                     help="weight-sharing scheme of the low-rank part (as a tile map); "
                          "the others are comparisons: rank0, per_expert, shared_u, shared_v")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill half of the metric (the 16k-token bf16 "
+                         "Mixtral-shaped prefill measured beside the decode line)")
     ap.add_argument("--cpu-tokens", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB elementwise copy kernel (counter calibration)")
@@ -213,80 +346,10 @@ def main():
 
     import torch
 
-    import bit_rank_post_amd as tq
-    import synth
-    from bit_rank_post_amd import io as tqio
-
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    cfg_name, T = WORKLOADS[args.workload]
-    cfg = synth.CONFIG_BY_NAME[cfg_name]
-    print(f"[bench] generating {cfg_name} (T={T})", file=sys.stderr, flush=True)
-    layer = synth.make_layer(cfg, scheme=args.scheme)
-    pg = layer["proj"]["single" if cfg.kind == "single" else "gate"]
-    x, ids, gates = synth.make_tokens(cfg, T)
-    copies = max(1, args.copies)
-    Ls = [tqio.upload_layer(layer) for _ in range(copies)]
-    xd, idd, gd = tqio.tokens_to_device(x, ids, gates, cfg.act)
-    k = cfg.topk
-    d_out = cfg.d_ff if cfg.kind == "single" else cfg.d_model
-    y = torch.empty((T, d_out), dtype=torch.float16 if cfg.act == "f16" else torch.bfloat16,
-                    device="cuda")
-    ydt = tq.TQ_F16 if cfg.act == "f16" else tq.TQ_BF16
-    ws = tqio.workspace(Ls[0], T, k)
-    path = 1 if T * k <= 16 * cfg.K else 2
-    print(f"[bench] uploaded {copies} copies; path={'decode' if path == 1 else 'prefill'}",
-          file=sys.stderr, flush=True)
-
-    def step(i):
-        Ls[i % copies].forward(xd, T, idd, gd, k, y, ydt, ws)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step",
-          file=sys.stderr, flush=True)
-
-    # the same steps replayed from HIP graphs (one captured forward per weight
-    # copy): removes the host launch path and most inter-kernel gaps
-    graph_ms = None
-    try:
-        graphs = []
-        for i in range(copies):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(i)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % copies].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % copies].replay()
-        torch.cuda.synchronize()
-        graph_ms = 1e3 * (time.perf_counter() - t0) / args.steps
-        print(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-        del graphs
-    except Exception as exc:  # noqa: BLE001 - report eager numbers only
-        print(f"[bench] graph capture unavailable: {exc}", file=sys.stderr, flush=True)
-
-    # second pass: stage durations from HIP events on the forward's stream
-    for L in Ls:
-        L.profile_enable(True)
-    acc = None
-    for i in range(args.steps):
-        step(i)
-        st = Ls[i % copies].profile_read()
-        acc = st if acc is None else {kk: acc[kk] + st[kk] for kk in acc}
-    for L in Ls:
-        L.profile_enable(False)
-    stages_ms = {kk: v / args.steps for kk, v in acc.items()}
+    rec, (layer, x, ids, gates) = measure(args.workload, args.steps, args.warmup, args.copies,
+                                          args.scheme)
 
     if args.calibrate_copy:
         # one elementwise kernel of known traffic (reads 256 MiB, writes
@@ -297,64 +360,49 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    work = algorithmic(layer, ids, T)
-    dom_ms = stages_ms["gemm_in"]
-    decode = path == 1
-    if decode:
-        achieved = work["dom_bytes"] / (dom_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4))
-    else:
-        achieved = work["dom_flops"] / (dom_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_F16_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / PEAK_F16_TFLOPS, 4))
-    path_name = "decode" if decode else "prefill"
-    # (the counter summaries are taken with the grid of the configuration)
-    tr = traffic_from_profile(args.workload, path_name) if args.scheme == "tileq" else None
-    roof["traffic"] = tr
-    roof["kernel"] = KERNEL_NAMES[path_name]
-    roof["kernel_ms"] = round(dom_ms, 5)
-    roof["algorithmic_bytes_per_launch"] = work["dom_bytes"]
-    roof["algorithmic_flops_per_launch"] = work["dom_flops"]
+    # the prefill half of the metric, in the same run: the Mixtral-shaped
+    # 16k-token bf16 prefill (compute bound; one weight copy)
+    prefill = None
+    if not args.no_prefill and args.workload == "mixtral_decode" and args.scheme == "tileq":
+        psteps = min(args.steps, 20)
+        pre, _ = measure("mixtral_prefill16k", psteps, min(args.warmup, 3), 1)
+        prefill = {"workload": pre["workload"], "steps": psteps, "dtype": pre["dtype"],
+                   "ms_per_step": round(pre["ms_per_step"], 5),
+                   "tokens_per_s": round(pre["tokens_per_s"], 1),
+                   "roofline": pre["roofline"], "execution": pre["execution"],
+                   "eager_ms_per_step": pre["eager_ms_per_step"],
+                   "graph_ms_per_step": pre["graph_ms_per_step"],
+                   "stages_ms": pre["stages_ms"], "whole_forward": pre["whole_forward"],
+                   "kernel_source_sha256": pre["kernel_source_sha256"]}
 
     cpu = None
     if not args.no_cpu_baseline:
+        T = rec["T"]
         n_tok = args.cpu_tokens or min(T, 4)
-        print(f"[bench] cpu baseline: oracle on {n_tok}-token chunks for about 10 s", file=sys.stderr, flush=True)
+        print(f"[bench] cpu baseline: oracle on {n_tok}-token chunks for about 10 s",
+              file=sys.stderr, flush=True)
         cpu = cpu_baseline(layer, x, ids, gates, n_tok)
 
-    # both loops time the same steps of the same forward; the faster execution
-    # mode is reported, the other one beside it
-    eager_ms = ms_per_step
-    use_graph = graph_ms is not None and graph_ms < eager_ms
-    if use_graph:
-        ms_per_step = graph_ms
-    value = T / (ms_per_step * 1e-3)
-    whole_gbs = work["total_bytes"] / (ms_per_step * 1e-3) / 1e9
+    T = rec["T"]
+    ms_per_step = rec["ms_per_step"]
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "metric": METRIC, "value": round(rec["tokens_per_s"], 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec["dtype"],
         "data": "synthetic",
-        "config": {"workload": f"{cfg_name}: {cfg.K} experts on {pg['M']}x{pg['N']} grid"
-                               f"{'' if args.scheme == 'tileq' else ' (' + args.scheme + ')'}, "
-                               f"d_model {cfg.d_model}, d_ff {cfg.d_ff}, rank {pg['rank']}, "
-                               f"2-bit group-{cfg.group} residual, top-{cfg.topk}, "
-                               f"{cfg.act} activations, T={T} tokens, "
-                               f"{'decode' if decode else 'prefill'} path",
-                   "global_batch": T, "seq_len": 1, "parallelism": "single GPU",
-                   "weight_copies_rotated": copies},
-        "roofline": roof,
+        "config": {"workload": rec["workload"], "global_batch": T, "seq_len": 1,
+                   "parallelism": "single GPU",
+                   "weight_copies_rotated": max(1, args.copies)},
+        "roofline": rec["roofline"],
         "cpu_baseline": cpu,
-        "execution": "hip_graph_replay" if use_graph else "eager",
-        "eager_ms_per_step": round(eager_ms, 5),
-        "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
-        "stages_ms": {kk: round(v, 5) for kk, v in stages_ms.items()},
-        "whole_forward": {"algorithmic_bytes": work["total_bytes"],
-                          "algorithmic_flops": work["total_flops"],
-                          "achieved_GBps": round(whole_gbs, 1),
-                          "active_experts": work["active_experts"]},
-        "kernel_source_sha256": kernel_hash(path_name),
+        "execution": rec["execution"],
+        "eager_ms_per_step": rec["eager_ms_per_step"],
+        "graph_ms_per_step": rec["graph_ms_per_step"],
+        "stages_ms": rec["stages_ms"],
+        "whole_forward": rec["whole_forward"],
+        "kernel_source_sha256": rec["kernel_source_sha256"],
+        "prefill": prefill,
     }
     print(json.dumps(out))
 

@@ -23,7 +23,7 @@ STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHI
           5: "TQ_EUNSUPPORTED", 6: "TQ_ESTATE"}
 EXPORTS = ["tq_layer_create", "tq_upload_proj", "tq_upload_shared_expert",
            "tq_workspace_size", "tq_forward", "tq_layer_destroy", "tq_last_error",
-           "tq_abi_version", "tq_layer_set_path", "tq_debug_route", "tq_debug_dequant", "tq_debug_row_bound", "tq_router_topk",
+           "tq_abi_version", "tq_layer_set_path", "tq_forward_path", "tq_debug_route", "tq_debug_dequant", "tq_debug_row_bound", "tq_router_topk",
            "tq_profile_enable", "tq_profile_read"]
 STAGES = ["route", "row_exponent", "column_stage_in", "gemm_in", "column_stage_down",
           "shared_expert", "gemm_down", "combine"]
@@ -39,9 +39,10 @@ class TileQError(RuntimeError):
 class ProjDesc(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
-                ("rank", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("group", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("tile_of_expert", ctypes.POINTER(ctypes.c_int32)),
-                ("U", ctypes.c_void_p), ("sigma", ctypes.c_void_p), ("V", ctypes.c_void_p),
+                ("U", ctypes.c_void_p), ("sigma", ctypes.c_void_p),
+                ("sigma_dtype", ctypes.c_int32), ("V", ctypes.c_void_p),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p)]
 
@@ -66,6 +67,7 @@ def lib():
         L.tq_last_error.restype = ctypes.c_char_p
         L.tq_abi_version.restype = i32
         L.tq_layer_set_path.argtypes = [vp, i32]
+        L.tq_forward_path.argtypes = [vp, i32, i32, ctypes.POINTER(i32)]
         L.tq_debug_route.argtypes = [vp, i32, vp, i32, i32, vp, sz] + [vp] * 7 + [vp]
         L.tq_debug_dequant.argtypes = [vp, i32, i32, vp, vp]
         L.tq_debug_row_bound.argtypes = [vp, i32, vp]
@@ -116,12 +118,14 @@ class Layer:
         self.kind, self.act, self.d_model, self.d_ff, self.K = kind, act, d_model, d_ff, K
 
     def upload_proj(self, which, *, K, M, N, d_in, d_out, rank, group, tile_of_expert,
-                    U, sigma, V, codes, scales, zeros, stream=None):
-        """tile_of_expert: host sequence of K ints; the rest device tensors."""
+                    U, sigma, V, codes, scales, zeros, bits=2, sigma_dtype=TQ_F32, stream=None):
+        """tile_of_expert: host sequence of K ints; the rest device tensors
+        (sigma f32 or, with sigma_dtype=TQ_F16, f16)."""
         tiles = (ctypes.c_int32 * len(tile_of_expert))(*[int(t) for t in tile_of_expert])
-        d = ProjDesc(K, M, N, d_in, d_out, rank, group,
+        d = ProjDesc(K, M, N, d_in, d_out, rank, group, bits,
                      ctypes.cast(tiles, ctypes.POINTER(ctypes.c_int32)),
-                     _ptr(U), _ptr(sigma), _ptr(V), _ptr(codes), _ptr(scales), _ptr(zeros))
+                     _ptr(U), _ptr(sigma), sigma_dtype, _ptr(V), _ptr(codes), _ptr(scales),
+                     _ptr(zeros))
         _check("tq_upload_proj", lib().tq_upload_proj(self.h, which, ctypes.byref(d),
                                                       _stream(stream)))
 
@@ -131,6 +135,12 @@ class Layer:
 
     def set_path(self, path: int):
         _check("tq_layer_set_path", lib().tq_layer_set_path(self.h, path))
+
+    def forward_path(self, T: int, topk: int) -> int:
+        """1 (decode kernels) or 2 (prefill kernels): the path tq_forward takes."""
+        p = ctypes.c_int32()
+        _check("tq_forward_path", lib().tq_forward_path(self.h, T, topk, ctypes.byref(p)))
+        return p.value
 
     def workspace_size(self, T: int, topk: int) -> int:
         n = ctypes.c_size_t()

@@ -15,7 +15,9 @@
 // scale/zero words arrive in LDS by buffer loads with the LDS destination, in
 // a ring of DEPTH + 1 slots, so loads run DEPTH stages ahead of the MFMAs.
 // The codes of a k-step pair are unpacked in registers into the exact fp16
-// weights RND_f16(s (q - z)) (deq_dword) and fed to v_mfma_f32_16x16x32_f16.
+// weights RND_f16(s (q - z)) (deq_dword; deq_dword_lut, a byte-table lookup,
+// when a scale or zero point is outside the packed arithmetic's range) and
+// fed to v_mfma_f32_16x16x32_f16.
 //
 // MODE_GATEUP: gate and up rows of the same expert together; the row stage
 //   U_m (Sigma p) follows as extra k-steps (U_m rows as A, Sigma p split into
@@ -60,7 +62,7 @@ __host__ __device__ inline void pf_superblock(int nrt, int* sbr, int* sbc) {
   *sbc = 32 / *sbr;
 }
 
-template <typename T, int MODE, int RF, int NF, int GS>
+template <typename T, int MODE, int RF, int NF, int GS, bool LUT>
 __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   typedef typename Vec8<T>::type V8;
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
@@ -265,13 +267,23 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
           // scale/zero words of this lane's row for k-steps 2d and 2d+1
           const int gi0 = (NGS == 4) ? 2 * d : (NGS == 2 ? d : 0);
           const int gi1 = (NGS == 4) ? 2 * d + 1 : gi0;
-          const DeqConst c0 = deq_const(zw[r][p][gi0]);
           half8v a0, a1;
-          if (gi1 == gi0) {
-            deq_dword(cw[d][r][p], c0, c0, a0, a1);
+          if constexpr (LUT) {
+            const DeqLut t0 = deq_lut(zw[r][p][gi0]);
+            if (gi1 == gi0) {
+              deq_dword_lut(cw[d][r][p], t0, t0, a0, a1);
+            } else {
+              const DeqLut t1 = deq_lut(zw[r][p][gi1]);
+              deq_dword_lut(cw[d][r][p], t0, t1, a0, a1);
+            }
           } else {
-            const DeqConst c1 = deq_const(zw[r][p][gi1]);
-            deq_dword(cw[d][r][p], c0, c1, a0, a1);
+            const DeqConst c0 = deq_const(zw[r][p][gi0]);
+            if (gi1 == gi0) {
+              deq_dword(cw[d][r][p], c0, c0, a0, a1);
+            } else {
+              const DeqConst c1 = deq_const(zw[r][p][gi1]);
+              deq_dword(cw[d][r][p], c0, c1, a0, a1);
+            }
           }
 #pragma unroll
           for (int f = 0; f < NF; ++f) acc[p][r][f] = mfma16(a0, bfr[0][f], acc[p][r][f]);
@@ -457,7 +469,7 @@ static int pf_grid(int nrt, int ntq) {
   return ((nsb + 7) / 8) * 8 * sbr * sbc;
 }
 
-template <typename T, int MODE, int RF, int NF, int GS>
+template <typename T, int MODE, int RF, int NF, int GS, bool LUT>
 static void pre_launch(const GemmArgs& a, int max_tiles, hipStream_t s) {
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   const int rows_per_wg = 16 * RF * PF_WAVES;
@@ -467,7 +479,7 @@ static void pre_launch(const GemmArgs& a, int max_tiles, hipStream_t s) {
     if (!a.narrow) {
       b.ntq = max_tiles;
       const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
-      hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS>), grid, block, 0, s, b);
+      hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS, LUT>), grid, block, 0, s, b);
       return;
     }
   }
@@ -477,28 +489,40 @@ static void pre_launch(const GemmArgs& a, int max_tiles, hipStream_t s) {
   b.tile_half = 1;
   b.ntq = 2 * max_tiles;
   const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
-  hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, 4, GS>), grid, block, 0, s, b);
+  hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, 4, GS, LUT>), grid, block, 0, s, b);
 }
 
-template <typename T, int MODE, int RF, int NF>
+template <typename T, int MODE, int RF, int NF, bool LUT>
 static void pre_gs(const GemmArgs& a, int max_tiles, hipStream_t s) {
   const int G = a.p[0].group;
   const bool pow2 = (G & (G - 1)) == 0;
-  if (!pow2 || G > 256) pre_launch<T, MODE, RF, NF, 0>(a, max_tiles, s);
-  else if (G == 32) pre_launch<T, MODE, RF, NF, 1>(a, max_tiles, s);
-  else if (G == 64) pre_launch<T, MODE, RF, NF, 2>(a, max_tiles, s);
-  else if (G == 128) pre_launch<T, MODE, RF, NF, 4>(a, max_tiles, s);
-  else pre_launch<T, MODE, RF, NF, 8>(a, max_tiles, s);
+  if (!pow2 || G > 256) pre_launch<T, MODE, RF, NF, 0, LUT>(a, max_tiles, s);
+  else if (G == 32) pre_launch<T, MODE, RF, NF, 1, LUT>(a, max_tiles, s);
+  else if (G == 64) pre_launch<T, MODE, RF, NF, 2, LUT>(a, max_tiles, s);
+  else if (G == 128) pre_launch<T, MODE, RF, NF, 4, LUT>(a, max_tiles, s);
+  else pre_launch<T, MODE, RF, NF, 8, LUT>(a, max_tiles, s);
+}
+
+// The table dequantization when any projection of the launch has scales or
+// zero points outside the packed-arithmetic range (both give the same
+// canonical weights where both apply).
+template <typename T, int MODE, int RF, int NF>
+static void pre_lut(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
+  bool lut = false;
+  for (int p = 0; p < NP; ++p) lut = lut || a.p[p].deq_lut;
+  if (lut) pre_gs<T, MODE, RF, NF, true>(a, max_tiles, s);
+  else pre_gs<T, MODE, RF, NF, false>(a, max_tiles, s);
 }
 
 void launch_gemm_prefill(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
                          hipStream_t s) {
   if (act == ACT_F16) {
-    if (mode == MODE_GATEUP) pre_gs<half_t, MODE_GATEUP, 2, 8>(a, max_tiles, s);
-    else pre_gs<half_t, MODE_RES, 4, 8>(a, max_tiles, s);
+    if (mode == MODE_GATEUP) pre_lut<half_t, MODE_GATEUP, 2, 8>(a, max_tiles, s);
+    else pre_lut<half_t, MODE_RES, 4, 8>(a, max_tiles, s);
   } else {
-    if (mode == MODE_GATEUP) pre_gs<__bf16, MODE_GATEUP, 2, 8>(a, max_tiles, s);
-    else pre_gs<__bf16, MODE_RES, 4, 8>(a, max_tiles, s);
+    if (mode == MODE_GATEUP) pre_lut<__bf16, MODE_GATEUP, 2, 8>(a, max_tiles, s);
+    else pre_lut<__bf16, MODE_RES, 4, 8>(a, max_tiles, s);
   }
 }
 

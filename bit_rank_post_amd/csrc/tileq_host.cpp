@@ -446,7 +446,7 @@ extern "C" {
 
 const char* tq_last_error(void) { return g_err.c_str(); }
 
-int32_t tq_abi_version(void) { return 1; }
+int32_t tq_abi_version(void) { return 2; }
 
 tq_status tq_layer_create(tq_kind kind, tq_dtype act, int32_t d_model, int32_t d_ff, int32_t K,
                           tq_layer** out) {
@@ -475,6 +475,16 @@ tq_status tq_layer_set_path(tq_layer* L, int32_t path) {
   return TQ_OK;
 }
 
+tq_status tq_forward_path(const tq_layer* L, int32_t T, int32_t topk, int32_t* path) {
+  tq_status st = check_ready(L);
+  if (st != TQ_OK) return st;
+  if (!path) return fail(TQ_EINVAL, "path is NULL");
+  st = check_tokens(T, topk);
+  if (st != TQ_OK) return st;
+  *path = choose_path(L, T, topk);
+  return TQ_OK;
+}
+
 tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void* stream) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");
   if (!d) return fail(TQ_EINVAL, "descriptor is NULL");
@@ -494,6 +504,9 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
   if (d->group <= 0 || d->group % 32 || d_in % d->group)
     return fail(TQ_ESHAPE, "group = %d must be a multiple of 32 dividing d_in", d->group);
   if (d->rank < 0 || d->rank > 128) return fail(TQ_ESHAPE, "rank = %d outside [0, 128]", d->rank);
+  if (d->bits != 2) return fail(TQ_EUNSUPPORTED, "bits = %d: residual codes of 2 bits only", d->bits);
+  if (d->rank > 0 && d->sigma_dtype != TQ_F16 && d->sigma_dtype != TQ_F32)
+    return fail(TQ_EINVAL, "sigma_dtype must be TQ_F16 or TQ_F32");
   if (!d->tile_of_expert) return fail(TQ_EINVAL, "tile_of_expert is NULL");
   if (!d->codes || !d->scales || !d->zeros) return fail(TQ_EINVAL, "codes/scales/zeros NULL");
   if (d->rank > 0 && (!d->U || !d->V || !d->sigma)) return fail(TQ_EINVAL, "U/V/sigma NULL");
@@ -573,8 +586,8 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
     launch_pad_u(d->U, v.U, d->M * d_out, d->rank, v.r_pad, s);
     launch_transpose_v(d->V, v.Vt, d->N, d_in, d->rank, v.r_pad, s);
     UPCHK(hipGetLastError());
-    UPCHK(hipMemsetAsync(v.sigma, 0, (size_t)v.r_pad * 4, s));
-    UPCHK(hipMemcpyAsync(v.sigma, d->sigma, (size_t)d->rank * 4, hipMemcpyDeviceToDevice, s));
+    launch_sigma_to_f32(d->sigma, d->sigma_dtype == TQ_F16 ? 1 : 0, v.sigma, d->rank, v.r_pad, s);
+    UPCHK(hipGetLastError());
   }
   UPCHK(hipMemcpyAsync(v.m_of, m_of.data(), sizeof(int) * d->K, hipMemcpyHostToDevice, s));
   UPCHK(hipMemcpyAsync(v.n_of, n_of.data(), sizeof(int) * d->K, hipMemcpyHostToDevice, s));
@@ -584,7 +597,7 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
     rb.scales = d->scales;
     rb.zeros = d->zeros;
     rb.U = d->U;
-    rb.sigma = d->sigma;
+    rb.sigma = v.sigma;
     rb.V = d->V;
     rb.m_of = v.m_of;
     rb.n_of = v.n_of;
@@ -608,11 +621,12 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
   bad = nullptr;
   (void)hipFree(vn);
   vn = nullptr;
-  if (hbad) {
+  if (hbad & 3) {
     cleanup();
-    return fail(TQ_EINVAL, "%s%s", (hbad & 1) ? "scale not finite or |s| >= 1024; " : "",
-                (hbad & 2) ? "zero point not an integer in [0, 3]" : "");
+    return fail(TQ_EINVAL, "%s%s", (hbad & 1) ? "scale or zero point not finite; " : "",
+                (hbad & 2) ? "a dequantized weight s (q - z) overflows fp16" : "");
   }
+  v.deq_lut = (hbad & 4) ? 1 : 0;
 #undef UPCHK
   free_proj(L->proj[which]);
   np.uploaded = true;
@@ -633,24 +647,37 @@ tq_status tq_upload_shared_expert(tq_layer* L, int32_t d_ff_shared, const void* 
   const size_t n = (size_t)d_ff_shared * L->d_model * 2;
   SharedDev sd{};
   sd.d_ff = d_ff_shared;
-  HIPCHK(hipMalloc(&sd.wg, n));
-  HIPCHK(hipMalloc(&sd.wu, n));
-  HIPCHK(hipMalloc(&sd.wd, n));
-  HIPCHK(hipMemcpyAsync(sd.wg, wg, n, hipMemcpyDeviceToDevice, s));
-  HIPCHK(hipMemcpyAsync(sd.wu, wu, n, hipMemcpyDeviceToDevice, s));
-  HIPCHK(hipMemcpyAsync(sd.wd, wd, n, hipMemcpyDeviceToDevice, s));
-  HIPCHK(hipStreamSynchronize(s));
+  auto drop = [&]() {
+    (void)hipFree(sd.wg);
+    (void)hipFree(sd.wu);
+    (void)hipFree(sd.wd);
+  };
+#define SHCHK(expr)                                                            \
+  do {                                                                         \
+    hipError_t e_ = (expr);                                                    \
+    if (e_ != hipSuccess) {                                                    \
+      drop();                                                                  \
+      return fail(e_ == hipErrorOutOfMemory ? TQ_ENOMEM : TQ_EHIP, "%s failed: %s", #expr, \
+                  hipGetErrorString(e_));                                      \
+    }                                                                          \
+  } while (0)
+  SHCHK(hipMalloc(&sd.wg, n));
+  SHCHK(hipMalloc(&sd.wu, n));
+  SHCHK(hipMalloc(&sd.wd, n));
+  SHCHK(hipMemcpyAsync(sd.wg, wg, n, hipMemcpyDeviceToDevice, s));
+  SHCHK(hipMemcpyAsync(sd.wu, wu, n, hipMemcpyDeviceToDevice, s));
+  SHCHK(hipMemcpyAsync(sd.wd, wd, n, hipMemcpyDeviceToDevice, s));
+  SHCHK(hipStreamSynchronize(s));
+  if (!L->side) SHCHK(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
+  if (!L->fork_ev) SHCHK(hipEventCreateWithFlags(&L->fork_ev, hipEventDisableTiming));
+  if (!L->join_ev) SHCHK(hipEventCreateWithFlags(&L->join_ev, hipEventDisableTiming));
+#undef SHCHK
   if (L->shared.d_ff) {
     (void)hipFree(L->shared.wg);
     (void)hipFree(L->shared.wu);
     (void)hipFree(L->shared.wd);
   }
   L->shared = sd;
-  if (!L->side) {
-    HIPCHK(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
-    HIPCHK(hipEventCreateWithFlags(&L->fork_ev, hipEventDisableTiming));
-    HIPCHK(hipEventCreateWithFlags(&L->join_ev, hipEventDisableTiming));
-  }
   return TQ_OK;
 }
 

@@ -227,6 +227,71 @@ __device__ __forceinline__ void deq_dword(uint32_t D, const DeqConst& c0, const 
   a1 = as_half8(r1);
 }
 
+// ---- dequantization for any finite fp16 scale and zero point --------------
+// The four weights a (row, group) can take, RND_f16(fl32(fl32(q - z) * s))
+// for q = 0..3, are formed once per group in fp32 and kept as a byte table:
+// byte q of `lo` is the low byte of the value for code q, byte q of `hi` its
+// high byte.  A code pair then becomes its two fp16 values with one
+// v_perm_b32 (bytes 0-3 of the selector pick from `lo`, 4-7 from `hi`), so
+// the values are the canonical ones whatever z and s are (a fractional zero
+// point, a scale of any magnitude, a signed zero).
+struct DeqLut {
+  uint32_t lo, hi;
+};
+
+// fp32 value the compiler may not fold into a neighbouring operation: each
+// rounding step below then happens exactly where written (no fused
+// multiply-add, no mixed-precision multiply-convert, no sign-of-zero folding)
+__device__ __forceinline__ float fence_f(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// RND_f16(fl32(fl32(q - z) * s)) as fp16 bits
+__device__ __forceinline__ uint32_t deq_bits(float q, float z, float s) {
+  const float d = fence_f(q - z);
+  const float t = fence_f(d * s);
+  return (uint32_t)__builtin_bit_cast(uint16_t, (half_t)t);   // round to nearest even
+}
+
+__device__ __forceinline__ DeqLut deq_lut(uint32_t szw) {
+  const float s = (float)__builtin_bit_cast(half_t, (uint16_t)(szw & 0xFFFFu));
+  const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(szw >> 16));
+  const uint32_t h0 = deq_bits(0.0f, z, s), h1 = deq_bits(1.0f, z, s);
+  const uint32_t h2 = deq_bits(2.0f, z, s), h3 = deq_bits(3.0f, z, s);
+  const uint32_t h01 = h0 | (h1 << 16), h23 = h2 | (h3 << 16);
+  DeqLut t;
+  t.lo = __builtin_amdgcn_perm(h23, h01, 0x06040200u);   // low bytes of h0, h1, h2, h3
+  t.hi = __builtin_amdgcn_perm(h23, h01, 0x07050301u);   // high bytes
+  return t;
+}
+
+// The fp16 pair of the codes at bit P (low half) and 16 + P (high half) of D.
+template <int P>
+__device__ __forceinline__ uint32_t lut_pair(uint32_t D, const DeqLut& t) {
+  const uint32_t x = (D >> P) & 0x00030003u;                  // q0 | q1 << 16
+  const uint32_t sel = __umul24(x, 0x101u) + 0x04000400u;     // bytes q0, q0 + 4, q1, q1 + 4
+  return __builtin_amdgcn_perm(t.hi, t.lo, sel);
+}
+
+// deq_dword for any scale and zero point: the same operands, from the tables
+// of the groups of k-steps 2d (t0) and 2d + 1 (t1).  Code positions as in
+// unpack16: step 0 pairs at bits 4, 6, 8, 0; step 1 pairs at 10, 12, 14, 2.
+__device__ __forceinline__ void deq_dword_lut(uint32_t D, const DeqLut& t0, const DeqLut& t1,
+                                              half8v& a0, half8v& a1) {
+  u32x4 r0, r1;
+  r0[0] = lut_pair<4>(D, t0);
+  r0[1] = lut_pair<6>(D, t0);
+  r0[2] = lut_pair<8>(D, t0);
+  r0[3] = lut_pair<0>(D, t0);
+  r1[0] = lut_pair<10>(D, t1);
+  r1[1] = lut_pair<12>(D, t1);
+  r1[2] = lut_pair<14>(D, t1);
+  r1[3] = lut_pair<2>(D, t1);
+  a0 = as_half8(r0);
+  a1 = as_half8(r1);
+}
+
 // ---- reductions -----------------------------------------------------------
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll

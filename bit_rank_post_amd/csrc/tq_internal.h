@@ -26,6 +26,9 @@ enum Act { ACT_F16 = 0, ACT_BF16 = 1 };
 //   sigma : [r_pad] f32, zero padded
 struct ProjDev {
   int K, M, N, d_in, d_out, rank, r_pad, group, ng, nrb, nsteps;
+  int deq_lut;    // 1: some scale or zero point is outside the packed dequantization's
+                  // range (zero point not an integer in 0..3, or |s| >= 1024); the
+                  // prefill kernels then dequantize through byte tables (deq_lut)
   uint32_t* codes;
   uint32_t* sz;
   void* U;
@@ -253,6 +256,8 @@ void launch_row_bound(const RowBoundArgs& b, hipStream_t s);
 void launch_router_topk(const float* logits, int T, int K, int k, int* ids, float* w,
                         hipStream_t s);
 void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStream_t s);
+// sigma [r] as f16 (f16 = 1) or f32 -> [r_pad] f32, zero padded
+void launch_sigma_to_f32(const void* src, int f16, float* dst, int r, int r_pad, hipStream_t s);
 void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_pad,
                         hipStream_t s);
 void launch_debug_dequant(const ProjDev& p, int expert, void* w_out, hipStream_t s);

@@ -52,8 +52,12 @@ void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, i
   hipLaunchKernelGGL(repack_codes_kernel, dim3(blocks), dim3(256), 0, s, src, dst, K, d_out, d_in);
 }
 
-// scales/zeros [K][d_out][ng] -> [K][nrb][ng][16] (s | z << 16); flags
-// non-finite or |s| >= 1024 scales and non-integer or out-of-range zeros.
+// scales/zeros [K][d_out][ng] -> [K][nrb][ng][16] (s | z << 16).  Flags in
+// *bad: 1 a scale or zero point that is not finite, 2 a dequantized weight
+// RND_f16((q - z) s) that overflows fp16 for some code q (the prefill kernels
+// multiply fp16 weights), 4 a group outside the packed dequantization's range
+// (zero point not an integer in 0..3, or |s| >= 1024): the projection then
+// dequantizes through byte tables.
 __global__ void pack_sz_kernel(const uint16_t* __restrict__ sc, const uint16_t* __restrict__ zr,
                                uint32_t* __restrict__ dst, int K, int d_out, int ng, int* bad) {
   const size_t total = (size_t)K * d_out * ng;
@@ -65,10 +69,20 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ sc, const uint16_t* 
     const uint16_t sb = sc[idx], zb = zr[idx];
     const float s = (float)__builtin_bit_cast(half_t, sb);
     const float z = (float)__builtin_bit_cast(half_t, zb);
-    const bool ok_s = (fabsf(s) < 1024.0f);                  // false for inf/nan too
-    const bool ok_z = (z == rintf(z)) && z >= 0.0f && z <= 3.0f;
-    if (!ok_s) atomicOr(bad, 1);
-    if (!ok_z) atomicOr(bad, 2);
+    int flag = 0;
+    if (!(fabsf(s) <= 65504.0f) || !(fabsf(z) <= 65504.0f)) flag |= 1;   // inf or nan
+    if (!(fabsf(s) < 1024.0f) || !(z == rintf(z) && z >= 0.0f && z <= 3.0f)) flag |= 4;
+    if (!(flag & 1)) {
+      const uint32_t w = (uint32_t)sb | ((uint32_t)zb << 16);
+      const DeqLut t = deq_lut(w);
+      // an fp16 infinity has all exponent bits set and a zero mantissa
+      const uint32_t h[2] = {t.lo, t.hi};
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t v = ((h[0] >> (8 * q)) & 0xFFu) | (((h[1] >> (8 * q)) & 0xFFu) << 8);
+        if ((v & 0x7FFFu) == 0x7C00u) flag |= 2;
+      }
+    }
+    if (flag) atomicOr(bad, flag);
     const size_t out = (((size_t)e * (d_out >> 4) + (o >> 4)) * ng + g) * 16 + (o & 15);
     dst[out] = (uint32_t)sb | ((uint32_t)zb << 16);
   }
@@ -100,6 +114,21 @@ void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStrea
   hipLaunchKernelGGL(pad_u_kernel, dim3(blocks), dim3(256), 0, s,
                      reinterpret_cast<const uint16_t*>(U), reinterpret_cast<uint16_t*>(dst),
                      rows, r, r_pad);
+}
+
+// sigma [r] (f16 or f32) -> [r_pad] f32, zero padded (f16 -> f32 is exact)
+__global__ void sigma_to_f32_kernel(const void* __restrict__ src, int f16, float* __restrict__ dst,
+                                    int r, int r_pad) {
+  for (int c = threadIdx.x; c < r_pad; c += blockDim.x) {
+    float v = 0.f;
+    if (c < r)
+      v = f16 ? (float)reinterpret_cast<const half_t*>(src)[c] : reinterpret_cast<const float*>(src)[c];
+    dst[c] = v;
+  }
+}
+
+void launch_sigma_to_f32(const void* src, int f16, float* dst, int r, int r_pad, hipStream_t s) {
+  hipLaunchKernelGGL(sigma_to_f32_kernel, dim3(1), dim3(256), 0, s, src, f16, dst, r, r_pad);
 }
 
 // V [N*d_in][r] -> Vt [N][d_in/32][r_pad][32]: for each 32-input k-step, the
@@ -179,10 +208,10 @@ __global__ __launch_bounds__(256) void row_l1_kernel(const uint32_t* __restrict_
     const uint32_t word = codes[row * nw + w];
     const int g = (w << 4) / G;                   // G % 16 == 0: one group per word
     const float sa = fabsf((float)__builtin_bit_cast(half_t, (uint16_t)(scales[row * ng + g])));
-    const int z = (int)(float)__builtin_bit_cast(half_t, (uint16_t)(zeros[row * ng + g]));
-    int cnt = 0;
-    for (int j = 0; j < 16; ++j) cnt += abs((int)((word >> (2 * j)) & 3u) - z);
-    acc += sa * (float)cnt;
+    const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(zeros[row * ng + g]));
+    float cnt = 0.f;
+    for (int j = 0; j < 16; ++j) cnt += fabsf((float)((word >> (2 * j)) & 3u) - z);
+    acc += sa * cnt;
   }
   if (r > 0) {
     const size_t urow = (size_t)m_of[e] * d_out + o;
@@ -226,10 +255,14 @@ __global__ void debug_dequant_kernel(ProjDev p, int e, half_t* __restrict__ w) {
   for (int d = 0; d < (gs >> 1); ++d) {
     const int s0 = (sg << 3) + 2 * d;
     const size_t zb = (((size_t)e * p.nrb + rb) * p.ng) * 16 + (lane & 15);
-    const DeqConst c0 = deq_const(p.sz[zb + (size_t)(s0 / gsteps) * 16]);
-    const DeqConst c1 = deq_const(p.sz[zb + (size_t)((s0 + 1) / gsteps) * 16]);
+    const uint32_t w0 = p.sz[zb + (size_t)(s0 / gsteps) * 16];
+    const uint32_t w1 = p.sz[zb + (size_t)((s0 + 1) / gsteps) * 16];
     half8v a0, a1;
-    deq_dword(base[d], c0, c1, a0, a1);
+    if (p.deq_lut) {
+      deq_dword_lut(base[d], deq_lut(w0), deq_lut(w1), a0, a1);
+    } else {
+      deq_dword(base[d], deq_const(w0), deq_const(w1), a0, a1);
+    }
     half_t* out = w + (size_t)row * p.d_in + s0 * 32 + 8 * (lane >> 4);
     *reinterpret_cast<half8v*>(out) = a0;
     *reinterpret_cast<half8v*>(out + 32) = a1;

@@ -5,7 +5,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import TQ_BF16, TQ_F16, TQ_SINGLE, TQ_SWIGLU, Layer
+from . import TQ_BF16, TQ_F16, TQ_F32, TQ_SINGLE, TQ_SWIGLU, Layer
 
 ACT = {"f16": TQ_F16, "bf16": TQ_BF16}
 PROJ_INDEX = {"single": 0, "gate": 0, "up": 1, "down": 2}
@@ -25,15 +25,20 @@ def to_device(a: np.ndarray, act: str | None = None, device="cuda"):
 
 
 def upload_proj(L: Layer, which: int, p: dict, stream=None):
+    """sigma goes up as stored: float16 arrays as TQ_F16, anything else as f32."""
     act = p["act"]
+    sig = np.asarray(p["sigma"])
+    sig16 = sig.dtype == np.float16
+    sig = sig if sig16 else sig.astype(np.float32)
     dev = dict(U=to_device(p["U"], act) if p["rank"] else None,
                V=to_device(p["V"], act) if p["rank"] else None,
-               sigma=to_device(np.asarray(p["sigma"], np.float32)) if p["rank"] else None,
+               sigma=to_device(sig.view(np.uint16) if sig16 else sig) if p["rank"] else None,
                codes=to_device(p["codes"]),
                scales=to_device(p["scales"].view(np.uint16)),
                zeros=to_device(p["zeros"].view(np.uint16)))
     L.upload_proj(which, K=p["K"], M=p["M"], N=p["N"], d_in=p["d_in"], d_out=p["d_out"],
                   rank=p["rank"], group=p["group"], tile_of_expert=p["tile_of_expert"],
+                  bits=p.get("bits", 2), sigma_dtype=TQ_F16 if sig16 else TQ_F32,
                   stream=stream, **dev)
 
 

@@ -67,26 +67,31 @@ typedef enum { TQ_SINGLE = 0, TQ_SWIGLU = 1 } tq_kind;
 #define TQ_P_DOWN 2
 
 /* One projection as stored after the offline quantization of section 2.1.
- * Sizes: K experts on an M x N grid (K <= M*N <= 1024, K <= 256), d_in and
- * d_out the projection's input and output widths, rank r >= 0, residual group
- * size G along d_in.  Requirements: d_in % 128 == 0, d_out % 16 == 0,
- * G % 32 == 0, d_in % G == 0, r <= 128.
+ * Sizes: K experts on an M x N grid (K <= M*N <= 1024, K <= 256, N <= 32),
+ * d_in and d_out the projection's input and output widths, rank r >= 0,
+ * residual group size G along d_in, code width `bits`.  Requirements:
+ * d_in % 128 == 0, d_out % 16 == 0, G % 32 == 0, d_in % G == 0, r <= 128,
+ * bits == 2.
  *   tile_of_expert HOST   int32 [K]: tile index m*N + n of each expert;
  *                         must be injective and in [0, M*N) (empty tiles allowed).
  *   U      DEVICE act   [M*d_out][r] row-major; block m = rows m*d_out ...
- *   sigma  DEVICE f32   [r] (the diagonal of Sigma; any order accepted)
+ *   sigma  DEVICE sigma_dtype [r] (the diagonal of Sigma, any order);
+ *          sigma_dtype TQ_F16 or TQ_F32 (kept as f32 either way, exactly)
  *   V      DEVICE act   [N*d_in][r]  row-major; block n = rows n*d_in ...
  *   codes  DEVICE u32   [K][d_out][d_in/16]: 2-bit code of input i at bits
  *                       2*(i%16) .. 2*(i%16)+1 of word i/16
- *   scales DEVICE f16   [K][d_out][d_in/G]   finite, |s| < 1024
- *   zeros  DEVICE f16   [K][d_out][d_in/G]   integer zero points 0..3
+ *   scales DEVICE f16   [K][d_out][d_in/G]   any finite value
+ *   zeros  DEVICE f16   [K][d_out][d_in/G]   any finite value (fractional too)
  * The residual weight is R_e[o][i] = s[e][o][i/G] * (q[e][o][i] - z[e][o][i/G]).
- * U, V may be NULL when r == 0. */
+ * The prefill kernels multiply fp16 weights RND_f16(fl32(fl32(q - z) * s)), so
+ * that value must be finite for every code q of every group (checked).
+ * U, V and sigma may be NULL when r == 0. */
 typedef struct {
-  int32_t K, M, N, d_in, d_out, rank, group;
+  int32_t K, M, N, d_in, d_out, rank, group, bits;
   const int32_t *tile_of_expert;
   const void *U;
-  const float *sigma;
+  const void *sigma;
+  int32_t sigma_dtype;
   const void *V;
   const uint32_t *codes;
   const uint16_t *scales;
@@ -101,16 +106,18 @@ typedef struct {
 tq_status tq_layer_create(tq_kind kind, tq_dtype act, int32_t d_model, int32_t d_ff,
                           int32_t K, tq_layer **out);
 
-/* Call (1): upload one projection (section 2.1 step 5: "the resulting shared
- * low-rank factors (U, V, Sigma) are stored, and the residual error for each
- * expert is quantized").  The map is validated on the host before any device
- * work; the device arrays are copied (and re-laid-out) into library-owned
- * memory on `stream`; scales/zeros are validated on the device, after which
- * the call synchronizes `stream` and returns.  The caller may free its arrays
- * when the call returns.  Re-uploading a projection replaces it.
- * Errors: TQ_EINVAL (non-injective or out-of-range map, NULL pointers,
- * non-integer zero or out-of-range scale), TQ_ESHAPE (sizes inconsistent with
- * the layer or the requirements above), TQ_ENOMEM, TQ_EHIP. */
+/* Call (1): upload one projection (TileQ technical summary, section 2.1 step 5
+ * "Quantization": the global factors U, Sigma, V are kept once for the whole
+ * grid and every expert keeps its own quantized residual).  The map is
+ * validated on the host before any device work; the device arrays are copied
+ * (and re-laid-out) into library-owned memory on `stream`; scales/zeros are
+ * validated on the device, after which the call synchronizes `stream` and
+ * returns.  The caller may free its arrays when the call returns.
+ * Re-uploading a projection replaces it.
+ * Errors: TQ_EINVAL (non-injective or out-of-range map, NULL pointers, bad
+ * sigma_dtype, a scale or zero point that is not finite or whose dequantized
+ * weight overflows fp16), TQ_ESHAPE (sizes inconsistent with the layer or the
+ * requirements above), TQ_EUNSUPPORTED (bits other than 2), TQ_ENOMEM, TQ_EHIP. */
 tq_status tq_upload_proj(tq_layer *L, int32_t which, const tq_proj_desc *d, void *stream);
 
 /* Optional dense shared expert, added to every token with weight 1 (SWIGLU
@@ -137,7 +144,11 @@ tq_status tq_workspace_size(const tq_layer *L, int32_t T, int32_t topk, size_t *
  *            slots whose id was outside [0, K).
  * Only enqueues work on `stream`: no allocation, no synchronization, no read
  * back, so it can be captured in a HIP graph.  T == 0 is a no-op.  Buffers may
- * not overlap.  Concurrent calls must use distinct workspaces.
+ * not overlap.  Calls on one layer must not run concurrently (issue them on
+ * one stream, or order them): the layer owns the side stream of its shared
+ * expert, the events that fork it from and join it into the caller's stream,
+ * and the profiling events.  Calls on different layers may run concurrently
+ * when they use distinct workspaces.
  * Errors (all checked before any launch): TQ_EINVAL (NULL pointers, y_dtype),
  * TQ_ESHAPE (T, topk, ws_bytes too small), TQ_ESTATE, TQ_EUNSUPPORTED
  * (T * d_model * 2 >= 2^31 bytes of activations), TQ_EHIP (launch failure). */
@@ -160,6 +171,13 @@ int32_t tq_abi_version(void);
 /* Execution path: 0 = automatic (chosen on the host from T, topk and K),
  * 1 = decode kernels (16-slot tiles), 2 = prefill kernels (large tiles). */
 tq_status tq_layer_set_path(tq_layer *L, int32_t path);
+
+/* The execution path tq_forward takes for T tokens with top-k routing, as
+ * written to *path: 1 = decode kernels (16-slot tiles, streaming residual
+ * GEMV on MFMA), 2 = prefill kernels (grouped dequantizing GEMM).  The choice
+ * depends on T * topk against K, the override above, the group sizes and the
+ * size of the activations.  Errors: TQ_EINVAL, TQ_ESTATE, TQ_ESHAPE. */
+tq_status tq_forward_path(const tq_layer *L, int32_t T, int32_t topk, int32_t *path);
 
 /* Run only the routing/grouping step of tq_forward (the expert grouping of
  * section 2.2 that replaces per-token sparse dispatch) and copy its lists to

@@ -372,6 +372,32 @@ def pin_p12_storage(ref):
     assert abs(pe / sh - 8.0) < 0.02
 
 
+def pin_token_subset(ref):
+    """forward(tokens=t) equals rows t of the whole-batch forward (the sampled
+    full-size checks rest on it): single projection and SwiGLU with a shared
+    expert, subsets in any order, with repeats and dropped ids."""
+    p, _ = random_struct(6, 2, 3, 32, 48, 4, 16, seed=61)
+    x, ids, g = tokens(32, 6, 2, 17, seed=62)
+    ids = ids.copy()
+    ids[4, 1] = 9
+    full = ref.forward_single(p, x, ids, g)
+    for t in ([3], [16, 0, 7], [5, 5, 2], list(range(17))[::-1]):
+        sub = ref.forward_single(p, x, ids, g, tokens=np.array(t))
+        assert np.array_equal(sub, full[t]) or rel_err(sub, full[t]) < 1e-13, t
+    pg, _ = random_struct(4, 2, 2, 32, 16, 3, 16, seed=63)
+    pu, _ = random_struct(4, 2, 2, 32, 16, 3, 16, seed=64)
+    pd, _ = random_struct(4, 2, 2, 16, 32, 3, 16, seed=65)
+    layer = dict(kind="swiglu", act="f16", K=4, d_model=32, d_ff=16,
+                 proj=dict(gate=pg, up=pu, down=pd),
+                 shared=synth.make_shared(32, 16, np.random.SeedSequence(66)))
+    x, ids, g = tokens(32, 4, 2, 11, seed=67)
+    full = ref.forward_swiglu(layer, x, ids, g)
+    for t in ([10], [2, 9, 4], [1, 1]):
+        for keep in (True, False):
+            sub = ref.forward_swiglu(layer, x, ids, g, tokens=np.array(t), keep_weights=keep)
+            assert rel_err(sub, full[t]) < 1e-13, (t, keep)
+
+
 def _identity_shift(d):
     """Codes, scales, zeros of W[o][i] = 1 iff i == (o + 1) % d (one group)."""
     q = np.zeros((1, d, d), np.int64)
@@ -497,4 +523,4 @@ ALL_PINS = [pin_unpack_golden, pin_unpack_bytes, pin_residual_golden, pin_deq_go
             pin_p2_zero_rank, pin_p3_zero_residual, pin_p4_token_perm, pin_p5_slots,
             pin_p6_textbook, pin_p7_grid_relabel, pin_p8_linearity, pin_dropped_ids,
             pin_p11_two_oracles, pin_p12_storage, pin_swiglu_closed_form,
-            pin_shared_closed_form, pin_route, pin_router]
+            pin_shared_closed_form, pin_route, pin_router, pin_token_subset]

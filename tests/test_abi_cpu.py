@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(tq.EXPORTS)
-    assert L.tq_abi_version() == 1
+    assert L.tq_abi_version() == 2
 
 
 def status(fn, *args):
@@ -55,14 +55,15 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
 def desc(**kw):
-    base = dict(K=8, M=2, N=4, d_in=256, d_out=512, rank=16, group=64)
+    base = dict(K=8, M=2, N=4, d_in=256, d_out=512, rank=16, group=64, bits=2, sigma_dtype=2)
     base.update(kw)
     tiles = kw.pop("tiles", list(range(8)))
     base.pop("tiles", None)
     arr = (ctypes.c_int32 * len(tiles))(*tiles)
     d = tq.ProjDesc(base["K"], base["M"], base["N"], base["d_in"], base["d_out"],
-                    base["rank"], base["group"], ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
-                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+                    base["rank"], base["group"], base["bits"],
+                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
+                    FAKE, FAKE, base["sigma_dtype"], FAKE, FAKE, FAKE, FAKE)
     d._keep = arr
     return d
 
@@ -79,6 +80,8 @@ def desc(**kw):
     (dict(rank=-1), 2, b"rank"),
     (dict(rank=129), 2, b"rank"),
     (dict(N=40, M=1), 2, b"N = 40"),
+    (dict(bits=4), 5, b"bits = 4"),
+    (dict(sigma_dtype=1), 1, b"sigma_dtype"),                       # bf16 sigma
 ])
 def test_upload_validation(L, kw, code, text):
     h = ctypes.c_void_p()

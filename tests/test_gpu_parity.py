@@ -72,20 +72,102 @@ def test_dequant_random_groups(G, d_in, d_out, K):
         assert np.array_equal(w.cpu().numpy().view(np.uint16), want.view(np.uint16)), e
 
 
-def test_upload_rejects_bad_zero_and_scale():
+# zero points for the table dequantization: fractional, negative, subnormal,
+# signed zero, beyond the code range; each row of a layer carries one set
+# (one per group), so every scale is tried against four of them
+ZERO_SETS = [(0.5, -1.25, 2.75, 7.0), (2.0 ** -24, -0.0, 3.0, -3.5),
+             (100.5, -1000.0, 0.25, 1.5), (1.5, 1.5, 1.5, 1.5)]
+
+
+@pytest.mark.parametrize("zset", range(len(ZERO_SETS)))
+def test_dequant_exhaustive_general(zset):
+    """Every finite fp16 scale (both signs, any magnitude) against fractional
+    and out-of-range zero points, wherever the dequantized weights stay
+    finite (the others are rejected at upload, tested below): bit-exact with
+    RND_f16(fl32(fl32(q - z) * s)), through the table dequantization."""
+    zs = np.array(ZERO_SETS[zset], np.float16)
+    sbits = np.concatenate([np.arange(0x0000, 0x7C00), np.arange(0x8000, 0xFC00)]).astype(np.uint16)
+    sv = sbits.view(np.float16)
+    G, d_in = 32, 128
+    q4 = np.arange(4)[None, :, None]
+    deq = R.deq_canonical(np.broadcast_to(q4, (len(sv), 4, 4)).reshape(len(sv), 16),
+                          np.repeat(sv[:, None], 4, axis=1),
+                          np.tile(zs, (len(sv), 1)), 4)
+    ok = np.all(np.isfinite(deq), axis=1)
+    sv = sv[ok]
+    rows = len(sv)
+    rows -= rows % 16
+    sv = sv[:rows]
+    s = np.repeat(sv[:, None], 4, axis=1)[None]
+    z = np.tile(zs, (rows, 1))[None]
+    i = np.arange(d_in)[None, :]
+    o = np.arange(rows)[:, None]
+    q = ((i + o + i // 4) % 4)[None]
+    p = pins.proj_from(q, s, z, np.zeros((rows, 0), np.float16), [],
+                       np.zeros((d_in, 0), np.float16), [0], 1, 1, G)
+    say(f"  zero points {ZERO_SETS[zset]}: {rows} scales")
+    L = tqio.upload_layer(single_layer_from(p))
+    w = torch.empty((rows, d_in), dtype=torch.float16, device="cuda")
+    L.debug_dequant(0, 0, w)
+    torch.cuda.synchronize()
+    got = w.cpu().numpy().view(np.uint16)
+    want = R.deq_canonical(q[0], s[0], z[0], G, "f16").astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5])
+
+
+def test_upload_rejects_nonfinite_and_overflow():
     p, _ = pins.random_struct(2, 1, 2, 128, 16, 0, 32, seed=1)
-    p2 = dict(p)
-    z = p["zeros"].copy()
-    z[1, 3, 2] = np.float16(1.5)
-    p2["zeros"] = z
-    with pytest.raises(tq.TileQError, match="zero point"):
-        tqio.upload_layer(single_layer_from(p2))
-    p3 = dict(p)
-    s = p["scales"].copy()
-    s[0, 0, 0] = np.float16(np.inf)
-    p3["scales"] = s
-    with pytest.raises(tq.TileQError, match="scale"):
-        tqio.upload_layer(single_layer_from(p3))
+    for field, val, text in [("zeros", np.inf, "not finite"), ("zeros", np.nan, "not finite"),
+                             ("scales", np.inf, "not finite"), ("scales", np.nan, "not finite"),
+                             ("scales", 60000.0, "overflows"), ("zeros", -30000.0, "overflows")]:
+        p2 = dict(p)
+        a = p[field].copy()
+        a[1, 3, 2] = np.float16(val)
+        if field == "zeros" and val == -30000.0:
+            p2["scales"] = np.full_like(p["scales"], 4.0)     # 4 * 30003 > 65504
+        p2[field] = a
+        with pytest.raises(tq.TileQError, match=text):
+            tqio.upload_layer(single_layer_from(p2))
+
+
+def general_struct(K, M, N, d_in, d_out, rank, G, seed, big=40000.0):
+    """A projection with fractional zero points (some outside the code range),
+    signed scales and, on 1 % of the groups, scales `big` times larger (up to
+    1200 by default): the table dequantization."""
+    p, q = pins.random_struct(K, M, N, d_in, d_out, rank, G, seed)
+    rng = np.random.default_rng(seed + 1000)
+    z = rng.uniform(-2.0, 5.0, p["zeros"].shape).astype(np.float16)
+    s = (rng.uniform(0.001, 0.03, p["scales"].shape) * rng.choice([-1, 1], p["scales"].shape))
+    sel = rng.random(p["scales"].shape) < 0.01
+    s = np.where(sel, s * big, s).astype(np.float16)
+    return pins.proj_from(q, s, z, p["U"], p["sigma"], p["V"], p["tile_of_expert"], M, N, G)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_general_zero_points_and_scales(path):
+    """Forward parity with fractional zero points and large scales (decode
+    multiplies raw codes and corrects per group; prefill dequantizes through
+    byte tables), single projection and SwiGLU, sigma uploaded as f16."""
+    p = general_struct(8, 2, 4, 256, 64, 16, 64, seed=71)
+    L = tqio.upload_layer(single_layer_from(p))
+    L.set_path(path)
+    for T in (5, 150):
+        x, ids, g = pins.tokens(256, 8, 2, T, seed=T)
+        y, _ = run_forward(L, x, ids, g, "f16")
+        assert_parity(y, R.forward_single(p, x, ids, g), what=f"general z/s single T={T}")
+    ss = [general_struct(8, 2, 4, di, do, 16, 64, seed=72 + i, big=10.0)
+          for i, (di, do) in enumerate([(256, 384), (256, 384), (384, 256)])]
+    for q in ss:
+        q["sigma"] = q["sigma"].astype(np.float16)        # sigma_dtype = TQ_F16
+    layer = dict(kind="swiglu", act="f16", K=8, d_model=256, d_ff=384,
+                 proj=dict(gate=ss[0], up=ss[1], down=ss[2]), shared=None)
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    T = 24 if path == 1 else 300
+    x, ids, g = synth.make_custom_tokens(256, 8, 2, T, "f16", seed=73)
+    y, _ = run_forward(L, x, ids, g, "f16", "f32")
+    assert_parity(y, R.forward(layer, x, ids, g), what=f"general z/s swiglu path={path}")
 
 
 def route_layer(K, M, N, seed):
@@ -419,20 +501,46 @@ def test_fine64_zipf_mixed4160_sampled():
 def mixtral_f16():
     cfg = synth.CONFIG_BY_NAME["mixtral8x7b_decode"]
     layer = synth.make_layer(cfg)
-    return cfg, layer, tqio.upload_layer(layer)
+    # the batches B = 1, 8, 32 are prefixes of the 64-token batch (the token
+    # generator extends a smaller batch), so one oracle pass over 64 tokens
+    # gives every token of every batch
+    x, ids, g = synth.make_tokens(cfg, 64)
+    say("  oracle (Mixtral-shaped layer, all 64 tokens)")
+    ref = R.forward(layer, x, ids, g, keep_weights=False)
+    return cfg, layer, tqio.upload_layer(layer), ref
 
 
-@pytest.mark.parametrize("B", [1, 8, 32])
+@pytest.mark.parametrize("B", [1, 8, 32, 64])
 def test_mixtral_decode(mixtral_f16, B):
-    cfg, layer, L = mixtral_f16
+    """Every token of the batch, at each decode batch size of the metric."""
+    cfg, layer, L, ref = mixtral_f16
     x, ids, g = synth.make_tokens(cfg, B)
+    x64, ids64, _ = synth.make_tokens(cfg, 64)
+    assert np.array_equal(ids, ids64[:B]) and np.array_equal(x, x64[:B])
     y, _ = run_forward(L, x, ids, g, cfg.act, "f16")
-    tok = np.arange(B) if B <= 2 else np.array([0, B // 2, B - 1])
-    assert_parity(y[tok], R.forward(layer, x, ids, g, tokens=tok, keep_weights=False), "f16",
-                  what=f"mixtral decode B={B} (sampled)")
+    assert_parity(y, ref[:B], "f16", what=f"mixtral decode B={B} (all tokens)")
 
 
-def test_mixtral_prefill16k_bf16_sampled():
+def tile_tokens(ids, K, tile=128):
+    """For every expert: the tokens of the first slot of its first slot tile,
+    of a slot in the middle of a full tile and of the last slot of its last
+    (ragged) tile, with slots ordered by (expert, token, j) as the routing
+    groups them."""
+    flat = ids.reshape(-1)
+    k = ids.shape[1]
+    tok = set()
+    for e in range(K):
+        slots = np.nonzero(flat == e)[0]               # ascending slot id = (t, j) order
+        if len(slots) == 0:
+            continue
+        last_tile = (len(slots) - 1) // tile
+        picks = [0, len(slots) - 1, min(len(slots) - 1, tile // 2),
+                 last_tile * tile, min(len(slots) - 1, max(0, last_tile - 1) * tile + 77)]
+        tok.update(int(slots[i]) // k for i in picks)
+    return np.array(sorted(tok))
+
+
+def test_mixtral_prefill16k_bf16_every_expert_tile():
     cfg = synth.CONFIG_BY_NAME["mixtral8x7b_prefill16k_bf16"]
     layer = synth.make_layer(cfg)
     x, ids, g = synth.make_tokens(cfg, 16384)
@@ -440,11 +548,12 @@ def test_mixtral_prefill16k_bf16_sampled():
     ws = tqio.workspace(L, 16384, 2)
     y32, _ = run_forward(L, x, ids, g, cfg.act, "f32", ws=ws)
     yb, _ = run_forward(L, x, ids, g, cfg.act, "bf16", ws=ws)
-    # sample tokens whose experts fall in a few experts (bounded oracle cost)
-    hot = np.argsort(-np.bincount(ids.reshape(-1), minlength=8))[:3]
-    cand = np.nonzero(np.all(np.isin(ids, hot), axis=1))[0]
-    tok = np.concatenate([cand[:4], cand[-2:], [0]])
-    say(f"  oracle on tokens {tok.tolist()}")
+    tok = tile_tokens(ids, cfg.K)
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.K)
+    covered = set(ids[tok].reshape(-1).tolist())
+    assert covered == set(np.nonzero(counts)[0].tolist())
+    say(f"  slots per expert {counts.tolist()}; oracle on {len(tok)} tokens covering the "
+        f"first, a full and the last (ragged) 128-slot tile of every expert")
     ref = R.forward(layer, x, ids, g, tokens=tok, keep_weights=False)
     assert_parity(y32[tok], ref, "f32", what="mixtral prefill16k bf16 (y f32)")
     assert_parity(yb[tok], ref, "bf16", what="mixtral prefill16k bf16 (y bf16)")

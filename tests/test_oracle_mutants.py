@@ -158,10 +158,25 @@ def m_router_softmax_all(r):
     r.router_topk = router_topk
 
 
+def m_deq_round_zero(r):
+    orig = r.deq_canonical
+    r.deq_canonical = lambda q, s, z, G, out="f16": orig(q, s, np.rint(np.asarray(z, np.float16)), G, out)
+
+
+def m_subset_sorted(r):
+    """token subsets answered in ascending token order, not the order asked"""
+    fs, fw = r.forward_single, r.forward_swiglu
+    r.forward_single = lambda p, x, ids, g, tokens=None: fs(
+        p, x, ids, g, None if tokens is None else np.sort(tokens))
+    r.forward_swiglu = lambda layer, x, ids, g, tokens=None, keep_weights=True: fw(
+        layer, x, ids, g, None if tokens is None else np.sort(tokens), keep_weights)
+
+
 MUTANTS = [m_zero_sign, m_group_index, m_bit_order, m_drop_sigma, m_swap_mn,
            m_tile_stride, m_wrong_expert_residual, m_ignore_gates, m_swiglu_swap,
            m_silu_sign, m_rnd_truncate, m_route_unstable, m_transposed_down,
-           m_deq_double_round, m_router_ties_high, m_router_softmax_all]
+           m_deq_double_round, m_router_ties_high, m_router_softmax_all, m_deq_round_zero,
+           m_subset_sorted]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
