@@ -89,7 +89,7 @@ def test_dequant_exhaustive_general(zset):
     sbits = np.concatenate([np.arange(0x0000, 0x7C00), np.arange(0x8000, 0xFC00)]).astype(np.uint16)
     sv = sbits.view(np.float16)
     G, d_in = 32, 128
-    q4 = np.arange(4)[None, :, None]
+    q4 = np.arange(4)[None, None, :]           # codes 0..3 inside each of the 4 groups
     deq = R.deq_canonical(np.broadcast_to(q4, (len(sv), 4, 4)).reshape(len(sv), 16),
                           np.repeat(sv[:, None], 4, axis=1),
                           np.tile(zs, (len(sv), 1)), 4)
