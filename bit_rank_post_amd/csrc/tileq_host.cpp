@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -442,6 +443,40 @@ ColArgs col_args_down(const tq_layer* L, const Plan& p, const void* h, void* ws)
 }  // namespace
 
 // ============================================================================
+// Scratch of tq_forward_noalloc: a file-scope device array, one copy per GPU
+// the library runs on (held until the process ends).  In host code `scratch`
+// only names the array; its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64];          // per device id
+
+tq_status scratch_address(void** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(TQ_EUNSUPPORTED, "device id %d >= 64", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255))
+      return fail(TQ_EHIP, "scratch array address %p not 256-byte aligned", p);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return TQ_OK;
+}
+
+tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_t* topk_ids,
+                       const float* topk_w, int32_t topk, void* y, tq_dtype y_dtype, void* ws,
+                       size_t ws_bytes, void* stream);
+
+}  // namespace
+
 extern "C" {
 
 const char* tq_last_error(void) { return g_err.c_str(); }
@@ -694,6 +729,39 @@ tq_status tq_workspace_size(const tq_layer* L, int32_t T, int32_t topk, size_t* 
 tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t* topk_ids,
                      const float* topk_w, int32_t topk, void* y, tq_dtype y_dtype, void* ws,
                      size_t ws_bytes, void* stream) {
+  return forward_impl(L, x, T, topk_ids, topk_w, topk, y, y_dtype, ws, ws_bytes, stream);
+}
+
+tq_status tq_forward_noalloc(const tq_layer* L, const void* x, int32_t T, const int32_t* topk_ids,
+                             const float* topk_w, int32_t topk, void* y, tq_dtype y_dtype,
+                             void* stream) {
+  tq_status st = check_ready(L);
+  if (st != TQ_OK) return st;
+  st = check_tokens(T, topk);
+  if (st != TQ_OK) return st;
+  if (T == 0) return TQ_OK;
+  size_t need = 0;
+  st = tq_workspace_size(L, T, topk, &need);
+  if (st != TQ_OK) return st;
+  if (need > TQ_NOALLOC_SCRATCH_BYTES)
+    return fail(TQ_ESHAPE,
+                "tq_forward_noalloc: T = %d, topk = %d needs %zu bytes of scratch, more than the "
+                "%zu bytes of the library's static scratch array (use tq_forward with a workspace)",
+                T, topk, need, (size_t)TQ_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != TQ_OK) return st;
+  return forward_impl(L, x, T, topk_ids, topk_w, topk, y, y_dtype, ws, TQ_NOALLOC_SCRATCH_BYTES,
+                      stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_t* topk_ids,
+                       const float* topk_w, int32_t topk, void* y, tq_dtype y_dtype, void* ws,
+                       size_t ws_bytes, void* stream) {
   tq_status st = check_ready(L);
   if (st != TQ_OK) return st;
   st = check_tokens(T, topk);
@@ -996,6 +1064,10 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   HIPCHK(hipGetLastError());
   return TQ_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 tq_status tq_profile_enable(tq_layer* L, int32_t on) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");

@@ -156,6 +156,27 @@ tq_status tq_forward(const tq_layer *L, const void *x, int32_t T, const int32_t 
                      const float *topk_w, int32_t topk, void *y, tq_dtype y_dtype,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* Size of the static scratch array behind tq_forward_noalloc (64 MiB per GPU
+ * the library runs on, held until the process ends). */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* tq_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels with the same arguments and results, minus the workspace,
+ * which here is a file-scope device array of TQ_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library.  The call allocates nothing (no hipMalloc, no library
+ * allocation).  Every call on one GPU shares that GPU's array and the array
+ * keeps the last call's contents (the forward never needs it zeroed), so
+ * calls that overlap in time on one GPU -- on any layers, from any thread or
+ * stream -- race: the caller must order them.  The dropped-slot count of
+ * tq_forward is not reported.  Errors: as tq_forward, plus TQ_ESHAPE when
+ * tq_workspace_size(L, T, topk) exceeds TQ_NOALLOC_SCRATCH_BYTES (decode
+ * batches and prefills of a few hundred tokens of the Mixtral- and
+ * Qwen-MoE-shaped layers fit; larger prefills need tq_forward). */
+tq_status tq_forward_noalloc(const tq_layer *L, const void *x, int32_t T,
+                             const int32_t *topk_ids, const float *topk_w, int32_t topk,
+                             void *y, tq_dtype y_dtype, void *stream);
+
 /* Free the layer and its device memory (synchronizes the device first).
  * NULL is accepted. */
 tq_status tq_layer_destroy(tq_layer *L);
