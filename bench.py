@@ -261,6 +261,37 @@ def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
     except Exception as exc:  # noqa: BLE001 - report eager numbers only
         say(f"graph capture unavailable: {exc}")
 
+    # the router in front: router logits -> top-k -> forward, as two calls
+    # (tq_router_topk, then tq_forward) and as one (tq_forward_from_logits,
+    # where at decode the router runs inside the forward's first launch);
+    # logits N(0,1), so the routing is uniform like the workload's
+    router = None
+    if cfg.K <= 256 and k <= min(cfg.K, 32):
+        lg = torch.from_numpy(np.random.default_rng(7).standard_normal(
+            (T, cfg.K)).astype(np.float32)).cuda()
+        ids2 = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        g2 = torch.empty((T, k), dtype=torch.float32, device="cuda")
+
+        def two_calls(i):
+            tq.router_topk(lg, k, ids2, g2)
+            Ls[i % copies].forward(xd, T, ids2, g2, k, y, ydt, ws)
+
+        def one_call(i):
+            Ls[i % copies].forward_from_logits(xd, T, lg, k, ids2, g2, y, ydt, ws)
+
+        rt = {}
+        for name, fn in (("router_then_forward_ms", two_calls), ("forward_from_logits_ms", one_call)):
+            for i in range(warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                fn(i)
+            torch.cuda.synchronize()
+            rt[name] = round(1e3 * (time.perf_counter() - t0) / steps, 5)
+        router = rt
+        say(f"router + forward: {rt}")
+
     # second pass: stage durations from HIP events on the forward's stream
     for L in Ls:
         L.profile_enable(True)
@@ -307,6 +338,7 @@ def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
         "eager_ms_per_step": round(eager_ms, 5),
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
         "stages_ms": {kk: round(v, 5) for kk, v in stages_ms.items()},
+        "router_eager": router,
         "whole_forward": {"algorithmic_bytes": work["total_bytes"],
                           "algorithmic_flops": work["total_flops"],
                           "achieved_GBps": round(work["total_bytes"] / (ms * 1e-3) / 1e9, 1),
@@ -400,6 +432,7 @@ def main():
         "eager_ms_per_step": rec["eager_ms_per_step"],
         "graph_ms_per_step": rec["graph_ms_per_step"],
         "stages_ms": rec["stages_ms"],
+        "router_eager": rec["router_eager"],
         "whole_forward": rec["whole_forward"],
         "kernel_source_sha256": rec["kernel_source_sha256"],
         "prefill": prefill,

@@ -22,7 +22,7 @@ P_SINGLE, P_GATE, P_UP, P_DOWN = 0, 0, 1, 2
 STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHIP",
           5: "TQ_EUNSUPPORTED", 6: "TQ_ESTATE"}
 EXPORTS = ["tq_layer_create", "tq_upload_proj", "tq_upload_shared_expert",
-           "tq_workspace_size", "tq_forward", "tq_forward_noalloc", "tq_layer_destroy", "tq_last_error",
+           "tq_workspace_size", "tq_forward", "tq_forward_from_logits", "tq_forward_noalloc", "tq_layer_destroy", "tq_last_error",
            "tq_abi_version", "tq_layer_set_path", "tq_forward_path", "tq_debug_route", "tq_debug_dequant", "tq_debug_row_bound", "tq_router_topk",
            "tq_profile_enable", "tq_profile_read"]
 STAGES = ["route", "row_exponent", "column_stage_in", "gemm_in", "column_stage_down",
@@ -63,6 +63,7 @@ def lib():
         L.tq_upload_shared_expert.argtypes = [vp, i32, vp, vp, vp, vp]
         L.tq_workspace_size.argtypes = [vp, i32, i32, ctypes.POINTER(sz)]
         L.tq_forward.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, vp, sz, vp]
+        L.tq_forward_from_logits.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, i32, vp, sz, vp]
         L.tq_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, vp]
         L.tq_layer_destroy.argtypes = [vp]
         L.tq_last_error.restype = ctypes.c_char_p
@@ -152,6 +153,14 @@ class Layer:
         _check("tq_forward", lib().tq_forward(self.h, _ptr(x), T, _ptr(ids), _ptr(gates), topk,
                                               _ptr(y), y_dtype, _ptr(ws),
                                               ws.numel() * ws.element_size(), _stream(stream)))
+
+    def forward_from_logits(self, x, T, logits, topk, ids_out, gates_out, y, y_dtype, ws,
+                            stream=None):
+        """Top-k router on the logits, then the forward; the routing lands in
+        ids_out / gates_out."""
+        _check("tq_forward_from_logits", lib().tq_forward_from_logits(
+            self.h, _ptr(x), T, _ptr(logits), topk, _ptr(ids_out), _ptr(gates_out), _ptr(y),
+            y_dtype, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
     def forward_noalloc(self, x, T, ids, gates, topk, y, y_dtype, stream=None):
         """tq_forward on the library's static scratch array (no workspace)."""

@@ -1,7 +1,7 @@
 // Routing / grouping body shared by the routing kernel and the decode
 // companion launch (see route.hip for what it builds).
 #pragma once
-#include "tq_device.h"
+#include "router_body.h"
 
 namespace tq {
 
@@ -87,7 +87,14 @@ __device__ void route_block(const RouteArgs& a, int* lds) {
   int* cntw = a.cntw;
   int* colmask = a.colmask;
   if constexpr (SMALL) {
-    for (int i = tid; i < S; i += NT) s_ids[i] = a.ids[i];
+    if (a.logits) {
+      // the router first (decode companion launch): the picks go straight
+      // into the LDS copy of the ids and out to the caller's id and weight
+      // buffers
+      router_rows(a.logits, T, K, k, wave, NW, const_cast<int*>(a.ids), a.gates_out, s_ids);
+    } else {
+      for (int i = tid; i < S; i += NT) s_ids[i] = a.ids[i];
+    }
     ids = s_ids;
     rank = s_rank;
     cntw = s_cntw;

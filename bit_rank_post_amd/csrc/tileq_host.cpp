@@ -473,7 +473,7 @@ tq_status scratch_address(void** out) {
 
 tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_t* topk_ids,
                        const float* topk_w, int32_t topk, void* y, tq_dtype y_dtype, void* ws,
-                       size_t ws_bytes, void* stream);
+                       size_t ws_bytes, void* stream, const float* logits = nullptr);
 
 }  // namespace
 
@@ -732,6 +732,18 @@ tq_status tq_forward(const tq_layer* L, const void* x, int32_t T, const int32_t*
   return forward_impl(L, x, T, topk_ids, topk_w, topk, y, y_dtype, ws, ws_bytes, stream);
 }
 
+tq_status tq_forward_from_logits(const tq_layer* L, const void* x, int32_t T, const float* logits,
+                                 int32_t topk, int32_t* topk_ids, float* topk_w, void* y,
+                                 tq_dtype y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  tq_status st = check_ready(L);
+  if (st != TQ_OK) return st;
+  if (topk < 1 || topk > std::min(L->K, 32))
+    return fail(TQ_ESHAPE, "topk = %d outside [1, min(K, 32)] (the router picks distinct experts)",
+                topk);
+  if (T > 0 && !logits) return fail(TQ_EINVAL, "logits is NULL");
+  return forward_impl(L, x, T, topk_ids, topk_w, topk, y, y_dtype, ws, ws_bytes, stream, logits);
+}
+
 tq_status tq_forward_noalloc(const tq_layer* L, const void* x, int32_t T, const int32_t* topk_ids,
                              const float* topk_w, int32_t topk, void* y, tq_dtype y_dtype,
                              void* stream) {
@@ -761,7 +773,7 @@ namespace {
 
 tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_t* topk_ids,
                        const float* topk_w, int32_t topk, void* y, tq_dtype y_dtype, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream, const float* logits) {
   tq_status st = check_ready(L);
   if (st != TQ_OK) return st;
   st = check_tokens(T, topk);
@@ -822,8 +834,15 @@ tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_
   fill_route(L, p, topk_ids, ws, ra);
   if (p.ap_T > 0) ra.ncol = 0;     // decode: no column lists (every pair is computed)
   // decode with a small batch: the routing runs as one workgroup of the
-  // activation-preparation / column-stage launch (neither reads the other)
+  // activation-preparation / column-stage launch (neither reads the other);
+  // with router logits given, that workgroup runs the top-k router first
   const bool fuse_route = dec && prep_col_can_route(ra);
+  if (logits && fuse_route) {
+    ra.logits = logits;
+    ra.gates_out = const_cast<float*>(topk_w);
+  } else if (logits) {
+    launch_router_topk(logits, T, K, topk, const_cast<int*>(topk_ids), const_cast<float*>(topk_w), s);
+  }
   if (!fuse_route) launch_route(ra, s);
   mark(1);
   // activation preparation (decode: class-scaled fp16 copy + group sums;

@@ -48,7 +48,10 @@ struct SharedDev {
 
 // ---- routing --------------------------------------------------------------
 struct RouteArgs {
-  const int* ids;
+  const int* ids;                // [T][k]; written by the router first when logits is set
+  const float* logits;           // optional [T][K] router logits: top-k router fused in
+                                 // front (one-workgroup routing only)
+  float* gates_out;              // with logits: the routing weights [T][k]
   int T, k, S, K;
   int ncol;                      // column lists to build (1 single, 2 gate+up)
   const int* n_of[2];

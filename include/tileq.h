@@ -156,6 +156,20 @@ tq_status tq_forward(const tq_layer *L, const void *x, int32_t T, const int32_t 
                      const float *topk_w, int32_t topk, void *y, tq_dtype y_dtype,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* Call (2) fed by router logits: the top-k router of tq_router_topk (below)
+ * followed by tq_forward, in one call.  logits DEVICE f32 [T][K]; the routing
+ * it produces is written to topk_ids (DEVICE int32 [T][topk]) and topk_w
+ * (DEVICE f32 [T][topk]) -- bit-identical to tq_router_topk's -- and used by
+ * the forward.  At decode batch sizes the router runs inside the first launch
+ * of the forward (the workgroup that groups the slots by expert runs it just
+ * before), so it costs no launch of its own; otherwise it is one launch ahead
+ * of the routing.  Other arguments, results and errors as tq_forward, plus
+ * TQ_ESHAPE for topk > min(K, 32). */
+tq_status tq_forward_from_logits(const tq_layer *L, const void *x, int32_t T,
+                                 const float *logits, int32_t topk, int32_t *topk_ids,
+                                 float *topk_w, void *y, tq_dtype y_dtype, void *ws,
+                                 size_t ws_bytes, void *stream);
+
 /* Size of the static scratch array behind tq_forward_noalloc (64 MiB per GPU
  * the library runs on, held until the process ends). */
 #define TQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -107,3 +107,16 @@ def test_state_and_token_checks(L):
     assert L.tq_debug_dequant(h, 0, 0, FAKE, None) == 6
     assert L.tq_layer_destroy(h) == 0
     assert L.tq_layer_destroy(None) == 0
+
+
+def test_forward_variants_validate_on_host(L):
+    h = ctypes.c_void_p()
+    assert L.tq_layer_create(0, 0, 256, 512, 8, ctypes.byref(h)) == 0
+    n = ctypes.c_size_t()
+    # nothing uploaded: both variants refuse before any device work
+    assert L.tq_forward_from_logits(h, FAKE, 4, FAKE, 2, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20,
+                                    None) == 6
+    assert L.tq_forward_noalloc(h, FAKE, 4, FAKE, FAKE, 2, FAKE, 0, None) == 6
+    assert L.tq_forward_path(h, 4, 2, ctypes.byref(ctypes.c_int32())) == 6
+    assert L.tq_workspace_size(h, 4, 2, ctypes.byref(n)) == 6
+    assert L.tq_layer_destroy(h) == 0

@@ -463,6 +463,41 @@ def test_router_feeds_forward():
                   what="router -> forward")
 
 
+@pytest.mark.parametrize("path,T,k", [(1, 1, 2), (1, 24, 2), (1, 64, 2), (2, 300, 2), (1, 16, 8),
+                                      (2, 200, 8)])
+def test_forward_from_logits(path, T, k):
+    """The router fused into the forward (inside the first decode launch at
+    decode batch sizes, one launch ahead otherwise): its ids and weights equal
+    the standalone router's bit for bit, and y equals the two-call forward's
+    bit for bit and the oracle's within the bar."""
+    layer = small_swiglu("f16", 61)
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    x, _, _ = synth.make_custom_tokens(256, 8, k, T, "f16", seed=64 + T)
+    logits = np.random.default_rng(65 + T).standard_normal((T, 8)).astype(np.float32)
+    logits[0, :4] = 0.25                     # ties go to the lower id
+    ld = torch.from_numpy(logits).cuda()
+    xd = tqio.to_device(x, "f16")
+    ids_a = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    w_a = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    y_a = torch.empty((T, 256), dtype=torch.float32, device="cuda")
+    ws = tqio.workspace(L, T, k)
+    L.forward_from_logits(xd, T, ld, k, ids_a, w_a, y_a, tq.TQ_F32, ws)
+    ids_b = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w_b = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    tq.router_topk(ld, k, ids_b, w_b)
+    y_b = torch.empty((T, 256), dtype=torch.float32, device="cuda")
+    L.forward(xd, T, ids_b, w_b, k, y_b, tq.TQ_F32, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_a, ids_b) and torch.equal(w_a, w_b)
+    assert torch.equal(y_a, y_b)
+    rid, rw = R.router_topk(logits, k)
+    assert np.array_equal(ids_a.cpu().numpy(), rid)
+    assert np.max(np.abs(w_a.cpu().numpy() - rw)) <= 1e-6
+    assert_parity(y_a.cpu().numpy().astype(np.float64), R.forward(layer, x, rid, rw),
+                  what=f"router fused into the forward, path={path} T={T} k={k}")
+
+
 @pytest.mark.parametrize("path,T", [(1, 24), (2, 300)])
 def test_small_swiglu_with_shared_expert(path, T):
     """The shared expert (on the layer's second stream) at decode and prefill."""
