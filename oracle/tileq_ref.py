@@ -23,8 +23,10 @@ plain definition the fused forward must reproduce up to rounding order.
 
 Readings where the pages are silent:
   * residual R_e[o, i] = s_e[o, i//G] * (q_e[o, i] - z_e[o, i//G]), 2-bit
-    codes q packed 16 per uint32 (code i at bits 2*(i % 16)), group G along
-    d_in, fp16 scale s and integer zero point z;
+    codes q packed 16 per uint32 (code i at bits 2*(i % 16)) or 3-bit codes
+    (the pages' other residual width, section 4 "Experimental Results") as a
+    little-endian bit string (code i at bits 3i..3i+2), group G along d_in,
+    fp16 scale s and fp16 zero point z;
   * a slot (t, j) whose expert id is outside [0, K) contributes nothing;
   * SwiGLU expert: h = RND_act(silu(W_gate x) * (W_up x)), y = sum_j g W_down h,
     silu(v) = v / (1 + exp(-v)); h is stored in the activation dtype;
@@ -88,13 +90,27 @@ def silu(v: np.ndarray) -> np.ndarray:
 # stored format -> fp64 weights
 
 
-def unpack_codes(codes: np.ndarray, d_in: int) -> np.ndarray:
-    """2-bit codes from uint32 words [..., d_in/16]: code i is bits
-    2*(i % 16) .. 2*(i % 16)+1 of word i // 16."""
+def unpack_codes(codes: np.ndarray, d_in: int, bits: int = 2) -> np.ndarray:
+    """Residual codes from uint32 words.
+
+    bits = 2: words [..., d_in/16]; code i is bits 2*(i % 16) .. 2*(i % 16)+1
+    of word i // 16.
+    bits = 3: words [..., 3*d_in/32] holding the row as one little-endian
+    bit string; code i is bits 3i, 3i+1, 3i+2 of that string (bit n is bit
+    n % 32 of word n // 32), so 32 codes fill 3 words and some codes span
+    two words."""
     codes = np.asarray(codes, dtype=np.uint32)
-    sh = np.arange(16, dtype=np.uint32) * np.uint32(2)
-    q = (codes[..., None] >> sh) & np.uint32(3)
-    return q.reshape(codes.shape[:-1] + (d_in,)).astype(np.int64)
+    if bits == 2:
+        sh = np.arange(16, dtype=np.uint32) * np.uint32(2)
+        q = (codes[..., None] >> sh) & np.uint32(3)
+        return q.reshape(codes.shape[:-1] + (d_in,)).astype(np.int64)
+    if bits == 3:
+        # the bit string, bit n of the row at index n
+        bitpos = np.arange(32, dtype=np.uint32)
+        stream = ((codes[..., None] >> bitpos) & np.uint32(1)).reshape(codes.shape[:-1] + (-1,))
+        b = stream[..., :3 * d_in].reshape(codes.shape[:-1] + (d_in, 3)).astype(np.int64)
+        return b[..., 0] + 2 * b[..., 1] + 4 * b[..., 2]
+    raise ValueError(bits)
 
 
 def residual(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
@@ -129,7 +145,7 @@ def lowrank_block(proj, m: int, n: int) -> np.ndarray:
 
 
 def expert_residual(proj, e: int) -> np.ndarray:
-    q = unpack_codes(proj["codes"][e], proj["d_in"])
+    q = unpack_codes(proj["codes"][e], proj["d_in"], proj.get("bits", 2))
     return residual(q, proj["scales"][e], proj["zeros"][e], proj["group"])
 
 

@@ -13,10 +13,17 @@ stored arrays exactly).
 import math
 
 
-def code_at(words_row, i):
-    """Code of input i from a row of uint32 words (16 codes per word)."""
-    w = int(words_row[i // 16])
-    return (w >> (2 * (i % 16))) & 3
+def code_at(words_row, i, bits=2):
+    """Code of input i from a row of uint32 words: 2-bit codes 16 per word;
+    3-bit codes as a little-endian bit string (bits 3i, 3i+1, 3i+2)."""
+    if bits == 2:
+        w = int(words_row[i // 16])
+        return (w >> (2 * (i % 16))) & 3
+    q = 0
+    for j in range(3):
+        n = 3 * i + j
+        q |= ((int(words_row[n // 32]) >> (n % 32)) & 1) << j
+    return q
 
 
 def weight(p, e, o, i):
@@ -27,7 +34,7 @@ def weight(p, e, o, i):
     for r in range(p["rank"]):
         lr += p["U"][m * p["d_out"] + o][r] * p["sigma"][r] * p["V"][n * p["d_in"] + i][r]
     g = i // p["G"]
-    res = p["s"][e][o][g] * (code_at(p["codes"][e][o], i) - p["z"][e][o][g])
+    res = p["s"][e][o][g] * (code_at(p["codes"][e][o], i, p.get("bits", 2)) - p["z"][e][o][g])
     return lr + res
 
 

@@ -17,7 +17,9 @@ Storage format produced here (the format the C ABI accepts):
   sigma           f32   [r]              descending, values representable in fp16
   V               act   [N*d_in][r]      block n = rows n*d_in ... (n+1)*d_in-1
   codes           u32   [K][d_out][d_in/16]  code of input i at bits 2*(i%16)
-  scales, zeros   f16   [K][d_out][d_in/G]   zeros are integers 0..3
+                  (3-bit variant: [K][d_out][3*d_in/32], code i at bits 3i..3i+2
+                  of the row's little-endian bit string)
+  scales, zeros   f16   [K][d_out][d_in/G]   zeros are integers 0..3 (0..7)
   x               act   [T][d_model]
   ids             int32 [T][k],  gates f32 [T][k]
 "act" is float16, or bfloat16 carried as its uint16 bit pattern.
@@ -110,14 +112,22 @@ def act_as_f32(a: np.ndarray, act: str) -> np.ndarray:
     return (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def pack_codes(q: np.ndarray) -> np.ndarray:
-    """Pack 2-bit codes [..., d_in] (values 0..3) into uint32 words
-    [..., d_in/16]; code i sits at bits 2*(i % 16) of word i // 16."""
+def pack_codes(q: np.ndarray, bits: int = 2) -> np.ndarray:
+    """Pack residual codes [..., d_in] into uint32 words.  bits = 2 (values
+    0..3): [..., d_in/16], code i at bits 2*(i % 16) of word i // 16.
+    bits = 3 (values 0..7): [..., 3*d_in/32], the row as a little-endian bit
+    string with code i at bits 3i .. 3i+2 (bit n = bit n % 32 of word n // 32)."""
     d_in = q.shape[-1]
-    assert d_in % 16 == 0
-    q4 = q.reshape(q.shape[:-1] + (d_in // 16, 16)).astype(np.uint32)
-    shifts = (2 * np.arange(16, dtype=np.uint32))
-    return np.bitwise_or.reduce(q4 << shifts, axis=-1).astype(np.uint32)
+    if bits == 2:
+        assert d_in % 16 == 0
+        q4 = q.reshape(q.shape[:-1] + (d_in // 16, 16)).astype(np.uint32)
+        shifts = (2 * np.arange(16, dtype=np.uint32))
+        return np.bitwise_or.reduce(q4 << shifts, axis=-1).astype(np.uint32)
+    assert bits == 3 and d_in % 32 == 0
+    qb = np.asarray(q, np.uint32)
+    stream = np.stack([(qb >> np.uint32(j)) & np.uint32(1) for j in range(3)], axis=-1)
+    stream = stream.reshape(q.shape[:-1] + (3 * d_in // 32, 32))
+    return np.bitwise_or.reduce(stream << np.arange(32, dtype=np.uint32), axis=-1).astype(np.uint32)
 
 
 def _threads():
@@ -127,43 +137,51 @@ def _threads():
 # projection weights
 
 
-def quantize_rtn_2bit(w: np.ndarray, group: int):
-    """Round-to-nearest asymmetric 2-bit group quantization of w [rows][d_in]
-    along d_in.  Per group: mn = min(min w, 0), mx = max(max w, 0),
-    s = fp16((mx - mn) / 3) (1 where it would be 0), z = clamp(rint(-mn/s), 0, 3),
-    q = clamp(rint(w/s) + z, 0, 3).  Returns (q uint8, s f16, z f16)."""
+def quantize_rtn(w: np.ndarray, group: int, bits: int = 2):
+    """Round-to-nearest asymmetric group quantization of w [rows][d_in] along
+    d_in to codes 0..Q, Q = 2^bits - 1 (the synthetic residuals' generator).
+    Per group: mn = min(min w, 0), mx = max(max w, 0), s = fp16((mx - mn) / Q)
+    (1 where it would be 0), z = clamp(rint(-mn/s), 0, Q),
+    q = clamp(rint(w/s) + z, 0, Q).  Returns (q uint8, s f16, z f16)."""
+    qmax = (1 << bits) - 1
     rows, d_in = w.shape
     wg = w.reshape(rows, d_in // group, group)
     mn = np.minimum(wg.min(axis=2), 0.0)
     mx = np.maximum(wg.max(axis=2), 0.0)
-    s16 = ((mx - mn) / np.float32(3.0)).astype(np.float16)
+    s16 = ((mx - mn) / np.float32(qmax)).astype(np.float16)
     s16[s16 == 0] = np.float16(1.0)
     s32 = s16.astype(np.float32)
-    z = np.clip(np.rint(-mn / s32), 0, 3)
-    q = np.clip(np.rint(wg / s32[..., None]) + z[..., None], 0, 3)
+    z = np.clip(np.rint(-mn / s32), 0, qmax)
+    q = np.clip(np.rint(wg / s32[..., None]) + z[..., None], 0, qmax)
     return q.reshape(rows, d_in).astype(np.uint8), s16, z.astype(np.float16)
 
 
-def _residual_expert(ss, d_out, d_in, group, std):
+def quantize_rtn_2bit(w: np.ndarray, group: int):
+    """quantize_rtn with 2-bit codes."""
+    return quantize_rtn(w, group, 2)
+
+
+def _residual_expert(ss, d_out, d_in, group, std, bits=2):
     rng = np.random.default_rng(ss)
-    codes = np.empty((d_out, d_in // 16), np.uint32)
+    codes = np.empty((d_out, bits * d_in // 32), np.uint32)
     scales = np.empty((d_out, d_in // group), np.float16)
     zeros = np.empty((d_out, d_in // group), np.float16)
     step = max(1, (1 << 22) // d_in)           # bounded temporaries
     for r0 in range(0, d_out, step):
         r1 = min(d_out, r0 + step)
         w = rng.standard_normal((r1 - r0, d_in), dtype=np.float32) * np.float32(std)
-        q, s, z = quantize_rtn_2bit(w, group)
-        codes[r0:r1] = pack_codes(q)
+        q, s, z = quantize_rtn(w, group, bits)
+        codes[r0:r1] = pack_codes(q, bits)
         scales[r0:r1] = s
         zeros[r0:r1] = z
     return codes, scales, zeros
 
 
 def make_proj(K, M, N, d_in, d_out, rank, group, act, seedseq,
-              residual_std=0.02, threads=None, tiles=None):
+              residual_std=0.02, threads=None, tiles=None, bits=2):
     """One projection's uploaded arrays (see module docstring).  tiles: the
-    expert -> tile map (default: a random injective map)."""
+    expert -> tile map (default: a random injective map); bits: residual code
+    width (2, or 3 for the pages' 3-bit setting)."""
     assert K <= M * N and d_in % group == 0 and d_in % 16 == 0
     ss_map, ss_u, ss_sig, ss_v, ss_res = seedseq.spawn(5)
     if tiles is None:
@@ -180,9 +198,9 @@ def make_proj(K, M, N, d_in, d_out, rank, group, act, seedseq,
     res_ss = ss_res.spawn(K)
     with ThreadPoolExecutor(threads or _threads()) as ex:
         parts = list(ex.map(lambda s: _residual_expert(s, d_out, d_in, group,
-                                                       residual_std), res_ss))
+                                                       residual_std, bits), res_ss))
     return dict(K=K, M=M, N=N, d_in=d_in, d_out=d_out, rank=rank, group=group,
-                act=act, tile_of_expert=tiles,
+                bits=bits, act=act, tile_of_expert=tiles,
                 U=to_act(U, act), sigma=np.ascontiguousarray(sig),
                 V=to_act(V, act),
                 codes=np.stack([p[0] for p in parts]),
@@ -221,8 +239,10 @@ def scheme_grid(cfg: LayerConfig, scheme: str):
     raise ValueError(scheme)
 
 
-def make_layer(cfg: LayerConfig, threads=None, rank=None, scheme="tileq"):
-    """All weights of a configuration: {"proj": {name: proj}, "shared": ...}."""
+def make_layer(cfg: LayerConfig, threads=None, rank=None, scheme="tileq", bits=2):
+    """All weights of a configuration: {"proj": {name: proj}, "shared": ...}.
+    bits = 3 gives the 3-bit-residual variant of the configuration (same
+    seeds, codes 0..7)."""
     st = _streams(cfg)
     r = cfg.rank if rank is None else rank
     if scheme == "rank0":
@@ -232,7 +252,7 @@ def make_layer(cfg: LayerConfig, threads=None, rank=None, scheme="tileq"):
     for name, (d_in, d_out) in cfg.proj_shapes().items():
         key = "single_or_gate" if name in ("single", "gate") else name
         proj[name] = make_proj(cfg.K, M, N, d_in, d_out, r, cfg.group,
-                               cfg.act, st[key], threads=threads, tiles=tiles)
+                               cfg.act, st[key], threads=threads, tiles=tiles, bits=bits)
     layer = dict(kind=cfg.kind, act=cfg.act, K=cfg.K, d_model=cfg.d_model,
                  d_ff=cfg.d_ff, proj=proj, shared=None)
     if cfg.shared_ff:

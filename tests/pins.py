@@ -36,21 +36,21 @@ def f64(a, act):
     return synth.act_as_f32(np.asarray(a), act).astype(np.float64)
 
 
-def proj_from(q, s, z, U, sigma, V, tiles, M, N, G, act="f16"):
+def proj_from(q, s, z, U, sigma, V, tiles, M, N, G, act="f16", bits=2):
     K, d_out, d_in = q.shape
     return dict(K=K, M=M, N=N, d_in=d_in, d_out=d_out, rank=U.shape[1],
-                group=G, act=act, tile_of_expert=np.asarray(tiles, np.int32),
+                group=G, bits=bits, act=act, tile_of_expert=np.asarray(tiles, np.int32),
                 U=U, sigma=np.asarray(sigma, np.float32), V=V,
-                codes=synth.pack_codes(q), scales=np.asarray(s, np.float16),
+                codes=synth.pack_codes(q, bits), scales=np.asarray(s, np.float16),
                 zeros=np.asarray(z, np.float16))
 
 
-def random_struct(K, M, N, d_in, d_out, rank, G, seed, act="f16", zero_res=False):
+def random_struct(K, M, N, d_in, d_out, rank, G, seed, act="f16", zero_res=False, bits=2):
     """A projection with random codes, scales, zero points, factors and map.
     Returns (proj, q) where q are the codes before packing."""
     rng = np.random.default_rng(seed)
-    q = rng.integers(0, 4, (K, d_out, d_in))
-    z = rng.integers(0, 4, (K, d_out, d_in // G)).astype(np.float16)
+    q = rng.integers(0, 1 << bits, (K, d_out, d_in))
+    z = rng.integers(0, 1 << bits, (K, d_out, d_in // G)).astype(np.float16)
     s = rng.uniform(0.01, 0.1, (K, d_out, d_in // G)).astype(np.float16)
     if zero_res:
         q = np.repeat(z.astype(np.int64), G, axis=-1)
@@ -58,7 +58,7 @@ def random_struct(K, M, N, d_in, d_out, rank, G, seed, act="f16", zero_res=False
     V = synth.to_act((rng.standard_normal((N * d_in, rank)) / np.sqrt(d_in)).astype(np.float32), act)
     sigma = np.sort(rng.uniform(0.1, 10.0, rank))[::-1].astype(np.float16).astype(np.float32)
     tiles = rng.permutation(M * N)[:K]
-    return proj_from(q, s, z, U, sigma, V, tiles, M, N, G, act), q
+    return proj_from(q, s, z, U, sigma, V, tiles, M, N, G, act, bits), q
 
 
 def residual_from_q(q, s, z, G):
@@ -106,6 +106,65 @@ def pin_unpack_bytes(ref):
     rng = np.random.default_rng(7)
     q0 = rng.integers(0, 4, (5, 96))
     assert np.array_equal(ref.unpack_codes(synth.pack_codes(q0), 96), q0)
+
+
+def pin_unpack3_golden(ref):
+    with open(os.path.join(GOLDEN, "unpack_codes3.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            words, codes = line.split(":")
+            w = np.array([int(x, 16) for x in words.split()], np.uint32)
+            want = [0] * 32
+            for kv in codes.split():
+                i, v = kv.split("=")
+                want[int(i)] = int(v)
+            got = ref.unpack_codes(w[None, :], 32, 3)[0]
+            assert list(got) == want, (words, list(got), want)
+
+
+def pin_unpack3_bytes(ref):
+    """Every byte value at every byte position of a three-word group, against
+    a scalar read of the bit string (code i = sum_j bit(3i + j) 2^j), and the
+    generator's packing round trip."""
+    for pos in range(12):
+        b = np.arange(256, dtype=np.uint32)
+        words = np.zeros((256, 3), np.uint32)
+        words[:, pos // 4] = b << np.uint32(8 * (pos % 4))
+        q = ref.unpack_codes(words, 32, 3)
+        for v in range(256):
+            w = [int(x) for x in words[v]]
+            for i in range(32):
+                want = sum(((w[(3 * i + j) // 32] >> ((3 * i + j) % 32)) & 1) << j for j in range(3))
+                assert q[v, i] == want, (pos, v, i)
+    rng = np.random.default_rng(8)
+    q0 = rng.integers(0, 8, (5, 96))
+    assert np.array_equal(ref.unpack_codes(synth.pack_codes(q0, 3), 96, 3), q0)
+
+
+def pin_p2_zero_rank_3bit(ref):
+    """3-bit residual, rank 0: y_t = sum_j g R_e x_t from the codes before
+    packing; and the closed form x = ones, q = 7, z = 2 -> y_o = 5 sum_g s[o,g] G."""
+    rng = np.random.default_rng(24)
+    K, d_out, d_in, G = 4, 16, 64, 32
+    q = rng.integers(0, 8, (K, d_out, d_in))
+    s = rng.uniform(0.01, 0.1, (K, d_out, d_in // G)).astype(np.float16)
+    z = rng.integers(0, 8, (K, d_out, d_in // G)).astype(np.float16)
+    p = proj_from(q, s, z, np.zeros((2 * d_out, 0), np.float16), [], np.zeros((2 * d_in, 0), np.float16),
+                  [0, 1, 2, 3], 2, 2, G, bits=3)
+    x, ids, g = tokens(d_in, K, 2, 7, seed=25)
+    y = ref.forward_single(p, x, ids, g)
+    R = residual_from_q(q, s, z, G)
+    want = np.zeros_like(y)
+    for t in range(7):
+        for j in range(2):
+            want[t] += g[t, j] * (R[ids[t, j]] @ x[t].astype(np.float64))
+    assert rel_err(y, want) < 1e-12
+    p7 = proj_from(np.full(q.shape, 7), s, np.full(z.shape, 2, np.float16), p["U"], [], p["V"],
+                   [0, 1, 2, 3], 2, 2, G, bits=3)
+    y7 = ref.forward_single(p7, np.ones((1, d_in), np.float16), np.array([[1]]),
+                            np.array([[1.0]], np.float32))
+    assert rel_err(y7[0], 5.0 * s[1].astype(np.float64).sum(axis=1) * G) < 1e-12
 
 
 def _golden_residual():
@@ -328,7 +387,7 @@ def pin_dropped_ids(ref):
 
 def _tiny_lists(p, act):
     return dict(K=p["K"], M=p["M"], N=p["N"], d_in=p["d_in"], d_out=p["d_out"],
-                rank=p["rank"], G=p["group"],
+                rank=p["rank"], G=p["group"], bits=p.get("bits", 2),
                 tile=[int(v) for v in p["tile_of_expert"]],
                 U=f64(p["U"], act).tolist(), V=f64(p["V"], act).tolist(),
                 sigma=[float(v) for v in p["sigma"]],
@@ -346,6 +405,13 @@ def pin_p11_two_oracles(ref):
         yt = tiny_ref.forward_single(_tiny_lists(p, act), f64(x, act).tolist(),
                                      ids.tolist(), g.astype(np.float64).tolist())
         assert rel_err(y, np.array(yt)) < 1e-12
+    # 3-bit residual codes
+    p, _ = random_struct(4, 2, 2, 64, 16, 3, 32, seed=46, bits=3)
+    x, ids, g = tokens(64, 4, 2, 3, seed=47)
+    y = ref.forward_single(p, x, ids, g)
+    yt = tiny_ref.forward_single(_tiny_lists(p, "f16"), f64(x, "f16").tolist(),
+                                 ids.tolist(), g.astype(np.float64).tolist())
+    assert rel_err(y, np.array(yt)) < 1e-12
     # SwiGLU
     act = "f16"
     pg, _ = random_struct(4, 2, 2, 32, 16, 3, 16, seed=40)
@@ -523,4 +589,5 @@ ALL_PINS = [pin_unpack_golden, pin_unpack_bytes, pin_residual_golden, pin_deq_go
             pin_p2_zero_rank, pin_p3_zero_residual, pin_p4_token_perm, pin_p5_slots,
             pin_p6_textbook, pin_p7_grid_relabel, pin_p8_linearity, pin_dropped_ids,
             pin_p11_two_oracles, pin_p12_storage, pin_swiglu_closed_form,
-            pin_shared_closed_form, pin_route, pin_router, pin_token_subset]
+            pin_shared_closed_form, pin_route, pin_router, pin_token_subset, pin_unpack3_golden,
+            pin_unpack3_bytes, pin_p2_zero_rank_3bit]

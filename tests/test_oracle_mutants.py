@@ -172,11 +172,29 @@ def m_subset_sorted(r):
         layer, x, ids, g, None if tokens is None else np.sort(tokens), keep_weights)
 
 
+def m_bit_order3(r):
+    """3-bit codes read most significant bit first"""
+    orig = r.unpack_codes
+
+    def unpack_codes(codes, d_in, bits=2):
+        q = orig(codes, d_in, bits)
+        if bits == 3:
+            q = ((q & 1) << 2) | (q & 2) | (q >> 2)
+        return q
+    r.unpack_codes = unpack_codes
+
+
+def m_bits_ignored(r):
+    """every projection read as 2-bit codes"""
+    orig = r.unpack_codes
+    r.unpack_codes = lambda codes, d_in, bits=2: orig(np.asarray(codes)[..., :d_in // 16], d_in, 2)
+
+
 MUTANTS = [m_zero_sign, m_group_index, m_bit_order, m_drop_sigma, m_swap_mn,
            m_tile_stride, m_wrong_expert_residual, m_ignore_gates, m_swiglu_swap,
            m_silu_sign, m_rnd_truncate, m_route_unstable, m_transposed_down,
            m_deq_double_round, m_router_ties_high, m_router_softmax_all, m_deq_round_zero,
-           m_subset_sorted]
+           m_subset_sorted, m_bit_order3, m_bits_ignored]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
