@@ -17,8 +17,14 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtileq.so")
-SOURCES = ["route.hip", "colproj.hip", "gemm_prefill.hip", "gemm_decode.hip", "decode_stages.hip",
-           "combine.hip", "upload.hip", "router.hip", "tileq_host.cpp"]
+# (source, object name, extra flags): the prefill GEMM is compiled once per
+# residual code width
+SOURCES = [("route.hip", "route", []), ("colproj.hip", "colproj", []),
+           ("gemm_prefill.hip", "gemm_prefill2", ["-DTQ_PREFILL_BITS=2"]),
+           ("gemm_prefill.hip", "gemm_prefill3", ["-DTQ_PREFILL_BITS=3"]),
+           ("gemm_decode.hip", "gemm_decode", []), ("decode_stages.hip", "decode_stages", []),
+           ("combine.hip", "combine", []), ("upload.hip", "upload", []),
+           ("router.hip", "router", []), ("tileq_host.cpp", "tileq_host", [])]
 
 
 def hipcc():
@@ -39,11 +45,11 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     procs = []
     objs = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+    for src, name, extra in SOURCES:
+        obj = os.path.join(BUILD, name + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [cc] + flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc] + flags() + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                                  stderr=subprocess.STDOUT)))
     failed = []

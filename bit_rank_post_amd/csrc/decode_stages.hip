@@ -7,9 +7,10 @@
 // workgroups spread the few hundred KB each part reads over the CUs: one
 // CU's load path, not HBM, bounds a workgroup that reads a lot.
 //
-// Activation preparation.  The decode residual kernel feeds the 2-bit codes
-// to the MFMA without dequantizing them: each packed fp16 half holds 1 + q*c
-// (c = 1/64, 1/16 or 1/4 depending on where the code sits, see unpack16()).
+// Activation preparation.  The decode residual kernel feeds the codes to the
+// MFMA without dequantizing them: each packed fp16 half holds 1 + q*c (c =
+// 1/64, 1/16 or 1/4 for 2-bit codes, see unpack16(), and 1/64, 1/16 or 1/8
+// for 3-bit codes, see raw3_pair(), depending on where the code sits).
 // With the activation entering as x'_k = x~_k / c_k, a group sum of products
 // is  sum_k (1 + q_k c_k) x'_k = X'_g + sum_k q_k x~_k,  so the residual term
 // of a group is s * (C_g - X'_g - z * X~_g).  Per activation row this writes
@@ -28,6 +29,24 @@ namespace tq {
 
 constexpr int DS_THREADS = 256;
 constexpr int DS_SLAB_STEPS = 32;        // 32 k-steps = 1024 inputs per slab
+
+// 1/c of input 8 c + j is 2^e with e the class exponent of its code's
+// mantissa position in the decode kernel's operand, a function of the step
+// within a period of 4 k-steps (s = (c / 4) % 4) and of the pair v = j / 2:
+// e = (prep_class_exponents(bits) >> 3 (4 s + v)) & 7.
+//   2-bit (unpack16): 1/c = 64, 16, 4 for v = 0, 1, 2 and, for v = 3, 64 at
+//   even steps, 16 at odd steps.
+//   3-bit (raw3_pair): pair n = 4 s + v of a 4-step unit has 1/c =
+//   2^(10 - cls3(n)).
+__host__ __device__ constexpr uint64_t prep_class_exponents(int bits) {
+  uint64_t t = 0;
+  for (int n = 0; n < 16; ++n) {
+    const int s = n >> 2, v = n & 3;
+    const int e = (bits == 3) ? 10 - cls3(n) : (v == 0 ? 6 : v == 1 ? 4 : v == 2 ? 2 : ((s & 1) ? 4 : 6));
+    t |= (uint64_t)e << (3 * n);
+  }
+  return t;
+}
 
 // One row per workgroup; thread t owns the 8-element chunks t + 256 i.  The
 // row is read once (up to 8 chunks per thread stay in registers; longer rows
@@ -76,16 +95,13 @@ __device__ void prep_row(const PrepArgs& a, int rows, int blk, float* s_red /*[4
   auto emit = [&](int c, const V8& v) {
     float st = 0.f, sp = 0.f;
     if (c < nch) {
-      // 1/c of input k = 8c + j: with step parity b = (k/32) % 2 = (c/4) % 2
-      // and pair v = (k % 8) / 2 = j / 2, 1/c = 64, 16, 4 for v = 0, 1, 2 and
-      // 16 (b = 1) or 64 (b = 0) for v = 3
-      const float inv3 = ((c >> 2) & 1) ? 16.f : 64.f;
       half8v o;
+      const uint32_t ce = (uint32_t)(a.cls_exp >> (12 * ((c >> 2) & 3)));   // this step's 4 exponents
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float inv = (j < 2) ? 64.f : (j < 4) ? 16.f : (j < 6) ? 4.f : inv3;
+        const int e = (int)((ce >> (3 * (j >> 1))) & 7u);
         const half_t xt = (half_t)ldexpf((float)v[j], -E);
-        const half_t xp = (half_t)((float)xt * inv);
+        const half_t xp = (half_t)ldexpf((float)xt, e);
         o[j] = xp;
         st += (float)xt;
         sp += (float)xp;
@@ -252,6 +268,7 @@ void launch_prep_col(const PrepArgs* prep, int prep_rows, const ColArgs* col, in
   }
   if (prep) {
     a.prep = *prep;
+    a.prep.cls_exp = prep_class_exponents(prep->bits);
     a.prep_rows = prep_rows;
     a.prep_blocks = prep_rows;
   }

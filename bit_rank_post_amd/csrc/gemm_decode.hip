@@ -34,22 +34,27 @@
 
 namespace tq {
 
-// LDS slot layout (bytes) for NP projections, WAVES waves, NG groups/stage
-template <int NP, int WAVES, int NG>
+// LDS slot layout (bytes) for NP projections, WAVES waves, NG groups/stage,
+// BITS-bit codes
+template <int NP, int WAVES, int NG, int BITS>
 struct DecSlot {
+  // codes of a wave and projection per stage: 2-bit 64 lanes x 16 B; 3-bit
+  // 64 lanes x 16 B (dwords 0..3) then dwords 4 and 5 of the 64 lanes
+  static constexpr int CB = (BITS == 3) ? 1536 : 1024;
+  static constexpr int NCL = (BITS == 3) ? 3 : 1;    // code loads per projection
   // scale/zero words of a stage: per projection a [WAVES][NG][16 rows] table,
   // brought in by 64-word loads that the waves share out
   static constexpr int NSZP = (WAVES * NG + 3) / 4;  // 64-word loads per projection
   static constexpr int NSZW = (NP * NSZP + WAVES - 1) / WAVES;   // ... per wave
   static constexpr int NSUM = NG >= 2 ? NG / 2 : 1;  // dword loads of the group sums
   static constexpr int NACT = (8 + WAVES - 1) / WAVES;   // activation loads per wave
-  static constexpr int CODE = 0;                     // [WAVES][NP][64 lanes] x 16 B
-  static constexpr int ACT = CODE + WAVES * NP * 1024;   // [8 k-steps][64 lanes] x 16 B
+  static constexpr int CODE = 0;                     // [WAVES][NP] x CB
+  static constexpr int ACT = CODE + WAVES * NP * CB;     // [8 k-steps][64 lanes] x 16 B
   static constexpr int SZ = ACT + 8 * 1024;          // [NP][NSZP * 64] x 4 B
   static constexpr int SUM = SZ + NP * NSZP * 256;   // [NG][16 cols] float2
   static constexpr int BYTES = SUM + NSUM * 256;
   // loads per wave per stage (the same for every wave)
-  static constexpr int NI = NP + NACT + NSZW + 1;
+  static constexpr int NI = NP * NCL + NACT + NSZW + 1;
 };
 
 // Two workgroups share a CU when an 8-wave workgroup's ring of three slots
@@ -68,18 +73,36 @@ constexpr int ring_depth() {
   return (budget / BYTES - 1 < DMAX) ? budget / BYTES - 1 : DMAX;
 }
 
-template <int MODE, int GS, int WAVES>
+template <int MODE, int GS, int WAVES, int BITS>
 constexpr bool dec_dual_cfg() {
-  return dec_dual<DecSlot<(MODE == MODE_GATEUP) ? 2 : 1, WAVES, 8 / GS>::BYTES, WAVES>();
+  return dec_dual<DecSlot<(MODE == MODE_GATEUP) ? 2 : 1, WAVES, 8 / GS, BITS>::BYTES, WAVES>();
 }
 
-template <typename T, int MODE, int GS, int WAVES, int DMAX>
-__global__ __launch_bounds__(64 * WAVES, (dec_dual_cfg<MODE, GS, WAVES>() ? 4 : 1))
+// Raw A operand (1 + q c per fp16 half) of k-step J of a stage from the
+// lane's code dwords: 2-bit, dword J / 2 (unpack16); 3-bit, unit J / 4 of
+// dwords (0, 1, 2) or (3, 4, 5) (raw3_step).  J folds to a constant.
+template <int BITS>
+__device__ __forceinline__ u32x4 dec_raw(int J, const u32x4& c, uint32_t c4, uint32_t c5) {
+  if constexpr (BITS == 3) {
+    const uint32_t D0 = J < 4 ? c[0] : c[3], D1 = J < 4 ? c[1] : c4, D2 = J < 4 ? c[2] : c5;
+    switch (J & 3) {
+      case 0: return raw3_step<0>(D0, D1, D2);
+      case 1: return raw3_step<1>(D0, D1, D2);
+      case 2: return raw3_step<2>(D0, D1, D2);
+      default: return raw3_step<3>(D0, D1, D2);
+    }
+  } else {
+    return unpack16_step(c[J >> 1], J & 1);
+  }
+}
+
+template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS>
+__global__ __launch_bounds__(64 * WAVES, (dec_dual_cfg<MODE, GS, WAVES, BITS>() ? 4 : 1))
 void gemm_dec_kernel(DecArgs a) {
   typedef typename Vec8<T>::type V8;
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int NG = 8 / GS;             // groups per stage
-  typedef DecSlot<NP, WAVES, NG> SL;
+  typedef DecSlot<NP, WAVES, NG, BITS> SL;
   constexpr bool DUAL = dec_dual<SL::BYTES, WAVES>();
   constexpr int DEPTH = ring_depth<SL::BYTES, DMAX, DUAL>();
   constexpr int NSLOT = DEPTH + 1;
@@ -156,16 +179,18 @@ void gemm_dec_kernel(DecArgs a) {
   // different activation chunks and code pages instead of all hitting the
   // same L2 channels.
   const int r0 = ntau > 0 ? q % ntau : 0;
-  const size_t cpe = (size_t)a.d_out * (a.d_in >> 4);
+  // code dwords per expert, and per row block and k-step (16 rows x 32 inputs)
+  const size_t cpe = (size_t)a.d_out * BITS * (a.d_in >> 5);
+  constexpr int WPS = 16 * BITS;
 
   __amdgpu_buffer_rsrc_t rc[NP], rs[NP];
   const uint32_t* cbase[NP];
   const uint32_t* szb[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    cbase[p] = a.p[p].codes + (size_t)e * cpe + (size_t)rb * nsteps * 32;
+    cbase[p] = a.p[p].codes + (size_t)e * cpe + (size_t)rb * nsteps * WPS;
     szb[p] = a.p[p].sz + ((size_t)e * nrb + rb) * ng * 16;
-    rc[p] = make_rsrc(cbase[p], (uint32_t)nsteps * 128u);
+    rc[p] = make_rsrc(cbase[p], (uint32_t)nsteps * WPS * 4u);
     rs[p] = make_rsrc(a.p[p].sz + (size_t)e * nrb * ng * 16, (uint32_t)nrb * ng * 64u);
   }
   // scale/zero loads of this wave: load i = wave + WAVES * k of the stage
@@ -195,8 +220,14 @@ void gemm_dec_kernel(DecArgs a) {
     tr = (tr >= ntau) ? tr - ntau : tr;
     const int st = live ? k0 + tr : 0;
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
-      dma16(rc[p], base + SL::CODE + (wave * NP + p) * 1024, (live && rvalid) ? lane * 16u : OOB, st * 1024u);
+    for (int p = 0; p < NP; ++p) {
+      char* cb = base + SL::CODE + (wave * NP + p) * SL::CB;
+      dma16(rc[p], cb, (live && rvalid) ? lane * 16u : OOB, st * (uint32_t)SL::CB);
+      if constexpr (BITS == 3) {
+        dma4(rc[p], cb + 1024, (live && rvalid) ? 1024u + lane * 4u : OOB, st * (uint32_t)SL::CB);
+        dma4(rc[p], cb + 1280, (live && rvalid) ? 1280u + lane * 4u : OOB, st * (uint32_t)SL::CB);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < SL::NSZW; ++k)
       dma4(sz_p[k] == 0 ? rs[0] : rs[NP - 1], sz_lds[k] >= 0 ? base + sz_lds[k] : s_dummy,
@@ -299,13 +330,21 @@ void gemm_dec_kernel(DecArgs a) {
     //                   fp32 product covers terms t = 4 m + lg
     auto compute = [&](const char* base) {
       u32x4 code[NP];
+      uint32_t code4[NP], code5[NP];
       half8v bv[8];
       u32x4 szw[NP][NG];
       float cbx[NCORR];
       uint32_t cw[NP][NCORR];
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-        code[p] = *reinterpret_cast<const u32x4*>(base + SL::CODE + ((wave * NP + p) * 64 + lane) * 16);
+      for (int p = 0; p < NP; ++p) {
+        const char* cb = base + SL::CODE + (wave * NP + p) * SL::CB;
+        code[p] = *reinterpret_cast<const u32x4*>(cb + lane * 16);
+        code4[p] = code5[p] = 0u;
+        if constexpr (BITS == 3) {
+          code4[p] = *reinterpret_cast<const uint32_t*>(cb + 1024 + lane * 4);
+          code5[p] = *reinterpret_cast<const uint32_t*>(cb + 1280 + lane * 4);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         bv[j] = *reinterpret_cast<const half8v*>(base + SL::ACT + lane * 16 + j * 1024);
@@ -331,27 +370,21 @@ void gemm_dec_kernel(DecArgs a) {
 
       f32x4 C[NP];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4 fr[NP][2];
+      for (int j = 0; j < 8; ++j) {
+        if (j % GS == 0) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p) unpack16_frags(code[p][d], fr[p][0], fr[p][1]);
+          for (int p = 0; p < NP; ++p) C[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int j = 2 * d + b;
-          if (j % GS == 0) {
+        for (int p = 0; p < NP; ++p)
+          C[p] = mfma16(as_half8(dec_raw<BITS>(j, code[p], code4[p], code5[p])), bv[j], C[p]);
+        if (j % GS == GS - 1) {
+          const int gi = j / GS;
 #pragma unroll
-            for (int p = 0; p < NP; ++p) C[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
+          for (int p = 0; p < NP; ++p)
 #pragma unroll
-          for (int p = 0; p < NP; ++p) C[p] = mfma16(as_half8(fr[p][b]), bv[j], C[p]);
-          if (j % GS == GS - 1) {
-            const int gi = j / GS;
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                acc[p][v] += (float)__builtin_bit_cast(half_t, (uint16_t)(szw[p][gi][v] & 0xFFFFu)) * C[p][v];
-          }
+            for (int v = 0; v < 4; ++v)
+              acc[p][v] += (float)__builtin_bit_cast(half_t, (uint16_t)(szw[p][gi][v] & 0xFFFFu)) * C[p][v];
         }
       }
 #pragma unroll
@@ -415,10 +448,18 @@ void gemm_dec_kernel(DecArgs a) {
       const int lane_t = opaque(lane), lg_t = lane_t >> 4, arow_t = opaque(arow);
       const half_t* xrow = reinterpret_cast<const half_t*>(a.Xp) + (size_t)arow_t * a.d_in + 8 * lg_t;
       const float* srow = a.sums + (size_t)arow_t * ng * 2;
-      u32x2 cd[NP];
+      // the tail group: 2-bit, 8 B per lane; 3-bit, three planes of 64 dwords
+      u32x4 cd[NP];
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-        cd[p] = *reinterpret_cast<const u32x2*>(cbase[p] + st * 256 + lane_t * 2);
+      for (int p = 0; p < NP; ++p) {
+        if constexpr (BITS == 3) {
+          const uint32_t* tb = cbase[p] + st * 384;
+          cd[p] = u32x4{tb[lane_t], tb[64 + lane_t], tb[128 + lane_t], 0u};
+        } else {
+          const u32x2 c2 = *reinterpret_cast<const u32x2*>(cbase[p] + st * 256 + lane_t * 2);
+          cd[p] = u32x4{c2[0], c2[1], 0u, 0u};
+        }
+      }
       half8v bt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bt[j] = *reinterpret_cast<const half8v*>(xrow + (8 * st + j) * 32);
@@ -427,7 +468,10 @@ void gemm_dec_kernel(DecArgs a) {
       for (int d = 0; d < 2; ++d) {
         u32x4 fr[NP][2];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) unpack16_frags(cd[p][d], fr[p][0], fr[p][1]);
+        for (int p = 0; p < NP; ++p) {
+          fr[p][0] = dec_raw<BITS>(2 * d, cd[p], cd[p][2], 0u);
+          fr[p][1] = dec_raw<BITS>(2 * d + 1, cd[p], cd[p][2], 0u);
+        }
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const int j = 2 * d + b;
@@ -590,74 +634,82 @@ void gemm_dec_kernel(DecArgs a) {
   for (int t0 = 16; t0 < cnt; t0 += 16) tile(t0);
 }
 
-template <typename T, int MODE, int GS, int WAVES, int DMAX>
+template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS>
 static void dec_launch(const DecArgs& a, hipStream_t s) {
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
-  constexpr int BYTES = DecSlot<NP, WAVES, 8 / GS>::BYTES;
+  constexpr int BYTES = DecSlot<NP, WAVES, 8 / GS, BITS>::BYTES;
   if constexpr (WAVES > 8 && ring_depth<BYTES, DMAX, false>() < 2) {
     // slots too large for a ring of three: fall back to 8 waves
-    dec_launch<T, MODE, GS, 8, DMAX>(a, s);
+    dec_launch<T, MODE, GS, 8, DMAX, BITS>(a, s);
   } else {
     DecArgs b = a;
     b.rows_per = (a.rows_per >= 1 && a.rows_per <= WAVES) ? a.rows_per : WAVES;
     const int nrb = b.d_out >> 4;
     const int nby = (nrb + b.rows_per - 1) / b.rows_per;
     const dim3 grid(b.K * ((nby + 7) / 8) * 8 * b.nks);
-    hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, GS, WAVES, DMAX>), grid, dim3(64 * WAVES), 0, s, b);
+    hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, GS, WAVES, DMAX, BITS>), grid, dim3(64 * WAVES), 0,
+                       s, b);
   }
 }
 
-template <typename T, int MODE, int WAVES, int DMAX>
+template <typename T, int MODE, int WAVES, int DMAX, int BITS>
 static void dec_gs(const DecArgs& a, hipStream_t s) {
   switch (a.p[0].group >> 5) {
-    case 1: dec_launch<T, MODE, 1, WAVES, DMAX>(a, s); break;
-    case 2: dec_launch<T, MODE, 2, WAVES, DMAX>(a, s); break;
-    case 4: dec_launch<T, MODE, 4, WAVES, DMAX>(a, s); break;
-    default: dec_launch<T, MODE, 8, WAVES, DMAX>(a, s); break;
+    case 1: dec_launch<T, MODE, 1, WAVES, DMAX, BITS>(a, s); break;
+    case 2: dec_launch<T, MODE, 2, WAVES, DMAX, BITS>(a, s); break;
+    case 4: dec_launch<T, MODE, 4, WAVES, DMAX, BITS>(a, s); break;
+    default: dec_launch<T, MODE, 8, WAVES, DMAX, BITS>(a, s); break;
   }
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, int BITS>
 static void dec_waves(const DecArgs& a, hipStream_t s) {
   if constexpr (MODE == MODE_GATEUP) {
     switch (a.waves) {
-      case 16: dec_gs<T, MODE, 16, 6>(a, s); break;
-      case 14: dec_gs<T, MODE, 14, 6>(a, s); break;
-      case 12: dec_gs<T, MODE, 12, 6>(a, s); break;
-      default: dec_gs<T, MODE, 8, 6>(a, s); break;
+      case 16: dec_gs<T, MODE, 16, 6, BITS>(a, s); break;
+      case 14: dec_gs<T, MODE, 14, 6, BITS>(a, s); break;
+      case 12: dec_gs<T, MODE, 12, 6, BITS>(a, s); break;
+      default: dec_gs<T, MODE, 8, 6, BITS>(a, s); break;
     }
   } else {
-    if (a.waves == 16) dec_gs<T, MODE, 16, 6>(a, s);
-    else dec_gs<T, MODE, 8, 6>(a, s);
+    if (a.waves == 16) dec_gs<T, MODE, 16, 6, BITS>(a, s);
+    else dec_gs<T, MODE, 8, 6, BITS>(a, s);
   }
 }
 
 // Ring depth: as many slots as fit the LDS budget (at most 7).  With 16 waves
-// a gate/up slot holds 32 KB of codes (3 slots), a down / single slot 16 KB
-// (5 slots); with 8 waves 16 resp. 8 KB (5 resp. 7 slots).  One workgroup
-// per CU either way.
-template <int MODE>
+// a 2-bit gate/up slot holds 32 KB of codes (3 slots), a down / single slot
+// 16 KB (5 slots); with 8 waves 16 resp. 8 KB (5 resp. 7 slots).  One
+// workgroup per CU either way.  3-bit slots hold 1.5 times the codes.
+template <int MODE, int BITS>
 static bool dual_gs(int group) {
   switch (group >> 5) {
-    case 1: return dec_dual_cfg<MODE, 1, 8>();
-    case 2: return dec_dual_cfg<MODE, 2, 8>();
-    case 4: return dec_dual_cfg<MODE, 4, 8>();
-    default: return dec_dual_cfg<MODE, 8, 8>();
+    case 1: return dec_dual_cfg<MODE, 1, 8, BITS>();
+    case 2: return dec_dual_cfg<MODE, 2, 8, BITS>();
+    case 4: return dec_dual_cfg<MODE, 4, 8, BITS>();
+    default: return dec_dual_cfg<MODE, 8, 8, BITS>();
   }
 }
 
-bool decode_dual(int np, int group) {
-  return np == 2 ? dual_gs<MODE_GATEUP>(group) : dual_gs<MODE_RES>(group);
+bool decode_dual(int np, int group, int bits) {
+  if (bits == 3) return np == 2 ? dual_gs<MODE_GATEUP, 3>(group) : dual_gs<MODE_RES, 3>(group);
+  return np == 2 ? dual_gs<MODE_GATEUP, 2>(group) : dual_gs<MODE_RES, 2>(group);
+}
+
+template <typename T>
+static void dec_bits(const DecArgs& a, GemmMode mode, hipStream_t s) {
+  if (a.p[0].bits == 3) {
+    if (mode == MODE_GATEUP) dec_waves<T, MODE_GATEUP, 3>(a, s);
+    else dec_waves<T, MODE_RES, 3>(a, s);
+  } else {
+    if (mode == MODE_GATEUP) dec_waves<T, MODE_GATEUP, 2>(a, s);
+    else dec_waves<T, MODE_RES, 2>(a, s);
+  }
 }
 
 void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s) {
-  if (act == ACT_F16) {
-    if (mode == MODE_GATEUP) dec_waves<half_t, MODE_GATEUP>(a, s);
-    else dec_waves<half_t, MODE_RES>(a, s);
-  } else {
-    if (mode == MODE_GATEUP) dec_waves<__bf16, MODE_GATEUP>(a, s);
-    else dec_waves<__bf16, MODE_RES>(a, s);
-  }
+  if (act == ACT_F16) dec_bits<half_t>(a, mode, s);
+  else dec_bits<__bf16>(a, mode, s);
 }
 
 }  // namespace tq

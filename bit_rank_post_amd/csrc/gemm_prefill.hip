@@ -42,17 +42,18 @@ template <int GS> struct PfGroups { static constexpr int NGS = (GS <= 1) ? 4 : (
 // LDS slot layout (bytes).  Scale/zero words of a wave and projection: word
 // gi * SZG + r * 16 + row for group slot gi, fragment r, row; loaded by NSZ
 // dword loads of 64 lanes.
-template <int NP, int RF, int NF, int GS>
+template <int NP, int RF, int NF, int GS, int BITS>
 struct PfSlot {
   static constexpr int NGS = PfGroups<GS>::NGS;
   static constexpr int SZG = (GS == 0) ? 64 : RF * 16;
   static constexpr int NSZ = (GS == 0) ? 4 : (NGS * RF * 16 + 63) / 64;
+  static constexpr int NCW = BITS;                             // code dwords per lane per stage
   static constexpr int B = 0;                                  // [4][NF][64] x 16 B
-  static constexpr int CODE = B + 4 * NF * 1024;                // [W][RF][NP][2][64] x 4 B
-  static constexpr int SZ = CODE + PF_WAVES * RF * NP * 2 * 256;   // [W][NP][NSZ][64] x 4 B
+  static constexpr int CODE = B + 4 * NF * 1024;                // [W][RF][NP][NCW][64] x 4 B
+  static constexpr int SZ = CODE + PF_WAVES * RF * NP * NCW * 256;   // [W][NP][NSZ][64] x 4 B
   static constexpr int BYTES = SZ + PF_WAVES * NP * NSZ * 256;
   static constexpr int NB = 4 * NF / PF_WAVES;                 // activation loads per wave
-  static constexpr int NI = NB + RF * NP * 2 + NP * NSZ;       // loads per wave per stage
+  static constexpr int NI = NB + RF * NP * NCW + NP * NSZ;     // loads per wave per stage
 };
 
 // Super-block of row tiles x slot tiles that one XCD's 32 CUs (one
@@ -62,13 +63,13 @@ __host__ __device__ inline void pf_superblock(int nrt, int* sbr, int* sbc) {
   *sbc = 32 / *sbr;
 }
 
-template <typename T, int MODE, int RF, int NF, int GS, bool LUT>
+template <typename T, int MODE, int RF, int NF, int GS, bool LUT, int BITS>
 __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   typedef typename Vec8<T>::type V8;
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int BN = 16 * NF;
   constexpr int NGS = PfGroups<GS>::NGS;
-  typedef PfSlot<NP, RF, NF, GS> SL;
+  typedef PfSlot<NP, RF, NF, GS, BITS> SL;
   constexpr int DEPTH = 2;
   constexpr int NSLOT = DEPTH + 1;
   static_assert(NSLOT * SL::BYTES <= 160 * 1024 - 2048, "LDS budget");
@@ -143,7 +144,9 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   const bool has_tail = (a.d_in & 255) != 0;      // last stage is a 4-step tail group
   const int ng = a.p[0].ng;
   const int G = a.p[0].group;
-  const size_t cpe = (size_t)a.d_out * (a.d_in >> 4);
+  // code dwords per expert, and per row block and k-step (16 rows x 32 inputs)
+  const size_t cpe = (size_t)a.d_out * BITS * (a.d_in >> 5);
+  constexpr int WPS = 16 * BITS;
 
   const int row_lo = s_src[0];
   const int row_hi = s_src[max(nv - 1, 0)];
@@ -164,8 +167,8 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < RF; ++r) {
       const int rb = min(rb0 + r, nrb - 1);
-      rc[r][p] = make_rsrc(a.p[p].codes + (size_t)e * cpe + (size_t)rb * (a.d_in >> 4) * 16,
-                           (uint32_t)(a.d_in >> 4) * 64u);
+      rc[r][p] = make_rsrc(a.p[p].codes + (size_t)e * cpe + (size_t)rb * (a.d_in >> 5) * WPS,
+                           (uint32_t)(a.d_in >> 5) * WPS * 4u);
     }
     const int rbc = min(rb0, nrb - 1);
     rs[p] = make_rsrc(a.p[p].sz + ((size_t)e * nrb + rbc) * ng * 16,
@@ -200,16 +203,33 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
       dma16(rx, base + SL::B + q * 1024, live ? b_vo[i] : OOB, st * 256u);
     }
     const bool tl = has_tail && st == nstage - 1;
-    const uint32_t c_vo = tl ? lane * 8u : lane * 16u;
-    const uint32_t c_so = tl ? nfull * 1024u : (st >> 1) * 1024u + (st & 1) * 8u;
+    // lane offsets of the stage's code dwords: 2-bit, dword 2 (st % 2) + i of
+    // the lane's 16 B of its 8-step group (8 B in a 4-step tail); 3-bit, unit
+    // st % 2 of the group (dwords 0..2 or 3..5, see upload.hip) or the tail's
+    // three planes
+    uint32_t c_vo[SL::NCW];
+    uint32_t c_so;
+    if constexpr (BITS == 3) {
+      c_so = (st >> 1) * 1536u;
+      const bool u1 = (st & 1) != 0;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        c_vo[i] = tl ? i * 256u + lane * 4u
+                     : (u1 ? (i == 0 ? lane * 16u + 12u : 1024u + (i - 1) * 256u + lane * 4u)
+                           : lane * 16u + i * 4u);
+    } else {
+      c_so = tl ? nfull * 1024u : (st >> 1) * 1024u + (st & 1) * 8u;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) c_vo[i] = (tl ? lane * 8u : lane * 16u) + i * 4u;
+    }
 #pragma unroll
     for (int r = 0; r < RF; ++r)
 #pragma unroll
       for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          dma4(rc[r][p], base + SL::CODE + (((wave * RF + r) * NP + p) * 2 + i) * 256,
-               live ? c_vo + i * 4u : OOB, c_so);
+        for (int i = 0; i < SL::NCW; ++i)
+          dma4(rc[r][p], base + SL::CODE + (((wave * RF + r) * NP + p) * SL::NCW + i) * 256,
+               live ? c_vo[i] : OOB, c_so);
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -233,15 +253,15 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   auto compute = [&](const char* base) {
     // the stage's code dwords and scale/zero words are read first, so the
     // first fragment's dequantization waits for them alone
-    uint32_t cw[2][RF][NP];
+    uint32_t cw[SL::NCW][RF][NP];
 #pragma unroll
-    for (int d = 0; d < 2; ++d)
+    for (int d = 0; d < SL::NCW; ++d)
 #pragma unroll
       for (int r = 0; r < RF; ++r)
 #pragma unroll
         for (int p = 0; p < NP; ++p)
           cw[d][r][p] = *reinterpret_cast<const uint32_t*>(
-              base + SL::CODE + (((wave * RF + r) * NP + p) * 2 + d) * 256 + lane * 4);
+              base + SL::CODE + (((wave * RF + r) * NP + p) * SL::NCW + d) * 256 + lane * 4);
     uint32_t zw[RF][NP][NGS];
 #pragma unroll
     for (int r = 0; r < RF; ++r)
@@ -251,6 +271,39 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
         for (int g = 0; g < NGS; ++g)
           zw[r][p][g] = *reinterpret_cast<const uint32_t*>(
               base + SL::SZ + (wave * NP + p) * SL::NSZ * 256 + (g * SL::SZG + r * 16 + l16) * 4);
+    if constexpr (BITS == 3) {
+      // one k-step at a time: its activation fragments, then per (fragment,
+      // projection) the step's dequantized operand and the MFMAs
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        half8v bfr[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          bfr[f] = *reinterpret_cast<const half8v*>(base + SL::B + ((j * NF + f) * 64 + lane) * 16);
+        const int gi = (NGS == 4) ? j : (NGS == 2 ? j >> 1 : 0);
+#pragma unroll
+        for (int r = 0; r < RF; ++r)
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const uint32_t D0 = cw[0][r][p], D1 = cw[1][r][p], D2 = cw[2][r][p];
+            half8v aj;
+            if constexpr (LUT) {
+              const DeqLut3 t = deq_lut3(zw[r][p][gi]);
+              aj = (j == 0) ? lut3_step<0>(D0, D1, D2, t)
+                 : (j == 1) ? lut3_step<1>(D0, D1, D2, t)
+                 : (j == 2) ? lut3_step<2>(D0, D1, D2, t) : lut3_step<3>(D0, D1, D2, t);
+            } else {
+              const DeqConst3 c = deq_const3(zw[r][p][gi]);
+              aj = (j == 0) ? deq3_step<0>(D0, D1, D2, c)
+                 : (j == 1) ? deq3_step<1>(D0, D1, D2, c)
+                 : (j == 2) ? deq3_step<2>(D0, D1, D2, c) : deq3_step<3>(D0, D1, D2, c);
+            }
+#pragma unroll
+            for (int f = 0; f < NF; ++f) acc[p][r][f] = mfma16(aj, bfr[f], acc[p][r][f]);
+          }
+      }
+      return;
+    }
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       half8v bfr[2][NF];
@@ -457,9 +510,9 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   }
 }
 
-template <int NP, int RF, int NF, int GS>
+template <int NP, int RF, int NF, int GS, int BITS>
 constexpr bool pre_fits() {
-  return 3 * PfSlot<NP, RF, NF, GS>::BYTES <= 160 * 1024 - 2048;
+  return 3 * PfSlot<NP, RF, NF, GS, BITS>::BYTES <= 160 * 1024 - 2048;
 }
 
 static int pf_grid(int nrt, int ntq) {
@@ -469,60 +522,76 @@ static int pf_grid(int nrt, int ntq) {
   return ((nsb + 7) / 8) * 8 * sbr * sbc;
 }
 
-template <typename T, int MODE, int RF, int NF, int GS, bool LUT>
+template <typename T, int MODE, int RF, int NF, int GS, bool LUT, int BITS>
 static void pre_launch(const GemmArgs& a, int max_tiles, hipStream_t s) {
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   const int rows_per_wg = 16 * RF * PF_WAVES;
   const int nrt = (a.d_out + rows_per_wg - 1) / rows_per_wg;
   GemmArgs b = a;
-  if constexpr (pre_fits<NP, RF, NF, GS>()) {
+  if constexpr (pre_fits<NP, RF, NF, GS, BITS>()) {
     if (!a.narrow) {
       b.ntq = max_tiles;
       const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
-      hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS, LUT>), grid, block, 0, s, b);
+      hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, NF, GS, LUT, BITS>), grid, block, 0, s, b);
       return;
     }
   }
   // a 128-slot tile as two 64-slot units (when the wide ring does not fit,
   // or when experts hold few slots: half the MFMA work on padding)
   static_assert(NF == 8, "smaller tiles always fit");
+  static_assert(pre_fits<NP, RF, 4, GS, BITS>(), "64-slot tiles fit");
   b.tile_half = 1;
   b.ntq = 2 * max_tiles;
   const dim3 grid(pf_grid(nrt, b.ntq)), block(64 * PF_WAVES);
-  hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, 4, GS, LUT>), grid, block, 0, s, b);
+  hipLaunchKernelGGL((gemm_pre_kernel<T, MODE, RF, 4, GS, LUT, BITS>), grid, block, 0, s, b);
 }
 
-template <typename T, int MODE, int RF, int NF, bool LUT>
+template <typename T, int MODE, int RF, int NF, bool LUT, int BITS>
 static void pre_gs(const GemmArgs& a, int max_tiles, hipStream_t s) {
   const int G = a.p[0].group;
   const bool pow2 = (G & (G - 1)) == 0;
-  if (!pow2 || G > 256) pre_launch<T, MODE, RF, NF, 0, LUT>(a, max_tiles, s);
-  else if (G == 32) pre_launch<T, MODE, RF, NF, 1, LUT>(a, max_tiles, s);
-  else if (G == 64) pre_launch<T, MODE, RF, NF, 2, LUT>(a, max_tiles, s);
-  else if (G == 128) pre_launch<T, MODE, RF, NF, 4, LUT>(a, max_tiles, s);
-  else pre_launch<T, MODE, RF, NF, 8, LUT>(a, max_tiles, s);
+  if (!pow2 || G > 256) {
+    // any group size: 2-bit codes only (upload requires a power of two from
+    // 32 to 256 with 3-bit codes)
+    if constexpr (BITS == 2) pre_launch<T, MODE, RF, NF, 0, LUT, BITS>(a, max_tiles, s);
+  } else if (G == 32) pre_launch<T, MODE, RF, NF, 1, LUT, BITS>(a, max_tiles, s);
+  else if (G == 64) pre_launch<T, MODE, RF, NF, 2, LUT, BITS>(a, max_tiles, s);
+  else if (G == 128) pre_launch<T, MODE, RF, NF, 4, LUT, BITS>(a, max_tiles, s);
+  else pre_launch<T, MODE, RF, NF, 8, LUT, BITS>(a, max_tiles, s);
 }
 
 // The table dequantization when any projection of the launch has scales or
 // zero points outside the packed-arithmetic range (both give the same
 // canonical weights where both apply).
-template <typename T, int MODE, int RF, int NF>
+template <typename T, int MODE, int RF, int NF, int BITS>
 static void pre_lut(const GemmArgs& a, int max_tiles, hipStream_t s) {
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   bool lut = false;
   for (int p = 0; p < NP; ++p) lut = lut || a.p[p].deq_lut;
-  if (lut) pre_gs<T, MODE, RF, NF, true>(a, max_tiles, s);
-  else pre_gs<T, MODE, RF, NF, false>(a, max_tiles, s);
+  if (lut) pre_gs<T, MODE, RF, NF, true, BITS>(a, max_tiles, s);
+  else pre_gs<T, MODE, RF, NF, false, BITS>(a, max_tiles, s);
 }
 
-void launch_gemm_prefill(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
-                         hipStream_t s) {
+// This translation unit holds the kernels of one code width (the build
+// compiles it once per width, TQ_PREFILL_BITS = 2 and 3).
+#ifndef TQ_PREFILL_BITS
+#define TQ_PREFILL_BITS 2
+#endif
+
+#if TQ_PREFILL_BITS == 3
+void launch_gemm_prefill_b3(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
+                            hipStream_t s) {
+#else
+void launch_gemm_prefill_b2(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
+                            hipStream_t s) {
+#endif
+  constexpr int B = TQ_PREFILL_BITS;
   if (act == ACT_F16) {
-    if (mode == MODE_GATEUP) pre_lut<half_t, MODE_GATEUP, 2, 8>(a, max_tiles, s);
-    else pre_lut<half_t, MODE_RES, 4, 8>(a, max_tiles, s);
+    if (mode == MODE_GATEUP) pre_lut<half_t, MODE_GATEUP, 2, 8, B>(a, max_tiles, s);
+    else pre_lut<half_t, MODE_RES, 4, 8, B>(a, max_tiles, s);
   } else {
-    if (mode == MODE_GATEUP) pre_lut<__bf16, MODE_GATEUP, 2, 8>(a, max_tiles, s);
-    else pre_lut<__bf16, MODE_RES, 4, 8>(a, max_tiles, s);
+    if (mode == MODE_GATEUP) pre_lut<__bf16, MODE_GATEUP, 2, 8, B>(a, max_tiles, s);
+    else pre_lut<__bf16, MODE_RES, 4, 8, B>(a, max_tiles, s);
   }
 }
 

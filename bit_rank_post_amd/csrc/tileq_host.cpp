@@ -120,7 +120,11 @@ bool decode_ok(const tq_layer* L) {
     const int g = L->proj[q].dev.group;
     if (g > 256 || (g & (g - 1)) != 0) return false;   // 32, 64, 128 or 256
   }
-  if (L->kind == TQ_SWIGLU && L->proj[0].dev.group != L->proj[1].dev.group) return false;
+  // gate and up read one prepared copy of x: one group size and one class
+  // pattern (code width)
+  if (L->kind == TQ_SWIGLU && (L->proj[0].dev.group != L->proj[1].dev.group ||
+                               L->proj[0].dev.bits != L->proj[1].dev.bits))
+    return false;
   return true;
 }
 
@@ -212,7 +216,8 @@ void choose_waves(const tq_layer* L, int q, int S, int nks, int np, int* waves, 
   const long active = std::min<long>(L->K, S);
   const int nrb = L->proj[q].dev.nrb;
   const long cus = device_cus();
-  const bool dual = decode_dual(np, L->proj[q].dev.group);
+  const int bits = L->proj[q].dev.bits;
+  const bool dual = decode_dual(np, L->proj[q].dev.group, bits);
   static const int cand2[] = {16, 14, 12, 8};
   static const int cand1[] = {16, 8};
   const int* cand = (np == 2) ? cand2 : cand1;
@@ -226,7 +231,7 @@ void choose_waves(const tq_layer* L, int q, int S, int nks, int np, int* waves, 
     for (int r = w; r >= (per_cu == 2 ? w - 1 : w); --r) {
       const long wgs = active * ((nrb + r - 1) / r) * nks;
       const long rounds = (wgs + cus * per_cu - 1) / (cus * per_cu);
-      const long cost = rounds * (r * np + 8 + (per_cu == 2 ? 0 : 12));
+      const long cost = rounds * (r * np * bits + 16 + (per_cu == 2 ? 0 : 24));
       if (best_cost < 0 || cost < best_cost) {
         best_cost = cost;
         *waves = w;
@@ -341,6 +346,10 @@ tq_status check_ready(const tq_layer* L) {
   for (int q = 0; q < nproj(L); ++q)
     if (!L->proj[q].uploaded)
       return fail(TQ_ESTATE, "projection %d has not been uploaded", q);
+  // gate and up are one fused kernel (the SwiGLU epilogue needs both)
+  if (L->kind == TQ_SWIGLU && L->proj[0].dev.bits != L->proj[1].dev.bits)
+    return fail(TQ_EUNSUPPORTED, "gate (%d-bit) and up (%d-bit) codes must have one width",
+                L->proj[0].dev.bits, L->proj[1].dev.bits);
   return TQ_OK;
 }
 
@@ -539,7 +548,11 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
   if (d->group <= 0 || d->group % 32 || d_in % d->group)
     return fail(TQ_ESHAPE, "group = %d must be a multiple of 32 dividing d_in", d->group);
   if (d->rank < 0 || d->rank > 128) return fail(TQ_ESHAPE, "rank = %d outside [0, 128]", d->rank);
-  if (d->bits != 2) return fail(TQ_EUNSUPPORTED, "bits = %d: residual codes of 2 bits only", d->bits);
+  if (d->bits != 2 && d->bits != 3)
+    return fail(TQ_EUNSUPPORTED, "bits = %d: residual codes of 2 or 3 bits only", d->bits);
+  if (d->bits == 3 && (d->group > 256 || (d->group & (d->group - 1)) != 0))
+    return fail(TQ_EUNSUPPORTED, "group = %d: 3-bit codes need a power-of-two group of 32 to 256",
+                d->group);
   if (d->rank > 0 && d->sigma_dtype != TQ_F16 && d->sigma_dtype != TQ_F32)
     return fail(TQ_EINVAL, "sigma_dtype must be TQ_F16 or TQ_F32");
   if (!d->tile_of_expert) return fail(TQ_EINVAL, "tile_of_expert is NULL");
@@ -570,13 +583,14 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
   v.ng = d_in / d->group;
   v.nrb = d_out / 16;
   v.nsteps = d_in / 32;
+  v.bits = d->bits;
   np.tile.assign(d->tile_of_expert, d->tile_of_expert + d->K);
   std::vector<int> m_of(d->K), n_of(d->K);
   for (int e = 0; e < d->K; ++e) {
     m_of[e] = np.tile[e] / d->N;
     n_of[e] = np.tile[e] % d->N;
   }
-  const size_t ncode = (size_t)d->K * d_out * (d_in / 16);
+  const size_t ncode = (size_t)d->K * d_out * d->bits * (d_in / 32);
   const size_t nsz = (size_t)d->K * d_out * v.ng;
   int* bad = nullptr;
   float* vn = nullptr;
@@ -614,8 +628,8 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
     UPCHK(hipMalloc(&v.sigma, (size_t)v.r_pad * 4));
   }
   UPCHK(hipMemsetAsync(bad, 0, sizeof(int), s));
-  launch_repack_codes(d->codes, v.codes, d->K, d_out, d_in, s);
-  launch_pack_sz(d->scales, d->zeros, v.sz, d->K, d_out, v.ng, bad, s);
+  launch_repack_codes(d->codes, v.codes, d->K, d_out, d_in, d->bits, s);
+  launch_pack_sz(d->scales, d->zeros, v.sz, d->K, d_out, v.ng, d->bits, bad, s);
   UPCHK(hipGetLastError());
   if (v.r_pad > 0) {
     launch_pad_u(d->U, v.U, d->M * d_out, d->rank, v.r_pad, s);
@@ -643,6 +657,7 @@ tq_status tq_upload_proj(tq_layer* L, int32_t which, const tq_proj_desc* d, void
     rb.G = d->group;
     rb.r = d->rank;
     rb.bf = L->act == TQ_BF16 ? 1 : 0;
+    rb.bits = d->bits;
     rb.vn = vn;
     rb.l1max = v.l1max;
     UPCHK(hipMemsetAsync(v.l1max, 0, sizeof(float) * d->K, s));
@@ -860,6 +875,7 @@ tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_
       pa.X = x;
       pa.d = L->d_model;
       pa.G = L->proj[0].dev.group;
+      pa.bits = L->proj[0].dev.bits;
       pa.Xp = at<void>(ws, p.xp);
       pa.sums = at<float>(ws, p.sums_x);
       pa.ex = at<int>(ws, p.ex_x);
@@ -975,6 +991,7 @@ tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_
       pa.X = h;
       pa.d = L->d_ff;
       pa.G = dd.group;
+      pa.bits = dd.bits;
       pa.Xp = at<void>(ws, p.hp);
       pa.sums = at<float>(ws, p.sums_h);
       pa.ex = at<int>(ws, p.ex_h);

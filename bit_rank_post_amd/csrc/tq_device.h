@@ -163,6 +163,28 @@ __device__ __forceinline__ uint32_t and_or_s(uint32_t a, uint32_t m, uint32_t c)
   return r;
 }
 
+// The MFMA A operand of step b (0 or 1) of dword D alone (half of
+// unpack16_frags).
+__device__ __forceinline__ u32x4 unpack16_step(uint32_t D, int b) {
+  const uint32_t M4 = 0x00300030u, M6 = 0x00C000C0u, M8 = 0x03000300u;
+  const uint32_t ONE = 0x3C003C00u;
+  u32x4 f;
+  if (b == 0) {
+    const uint32_t F = D << 4;
+    f[0] = and_or(D, M4, ONE);
+    f[1] = and_or(D, M6, ONE);
+    f[2] = and_or(D, M8, ONE);
+    f[3] = and_or(F, M4, ONE);
+  } else {
+    const uint32_t E = D >> 6, F = D << 4;
+    f[0] = and_or(E, M4, ONE);
+    f[1] = and_or(E, M6, ONE);
+    f[2] = and_or(E, M8, ONE);
+    f[3] = and_or(F, M6, ONE);
+  }
+  return f;
+}
+
 // unpack16 into the two MFMA A operands (step b = 0 and b = 1) of dword D.
 __device__ __forceinline__ void unpack16_frags(uint32_t D, u32x4& f0, u32x4& f1) {
   const uint32_t M4 = 0x00300030u, M6 = 0x00C000C0u, M8 = 0x03000300u;
@@ -290,6 +312,149 @@ __device__ __forceinline__ void deq_dword_lut(uint32_t D, const DeqLut& t0, cons
   r1[3] = lut_pair<2>(D, t1);
   a0 = as_half8(r0);
   a1 = as_half8(r1);
+}
+
+// ---- 3-bit codes ------------------------------------------------------------
+// Per lane, a unit of 4 MFMA k-steps (32 codes: the lane's 8 inputs of each
+// step) is three dwords D0, D1, D2.  Pair n = 0..15 is (step n / 4, register
+// n % 4), i.e. inputs 2v and 2v + 1 (v = n % 4) of the step.  Pair n = 5j + f
+// (f < 5) sits in dword j: the low input's code at bits 3f .. 3f + 2, the
+// high input's at 16 + 3f ...; pair 15 is spread over the spare bits: bit b
+// of its low code is bit 15 of dword b, bit b of its high code bit 31.
+// Unpacked into packed fp16 pairs 1 + q c (exponent bits of 1.0 OR-ed over a
+// code placed in the mantissa at bit p, c = 2^(p - 10)):
+//   f = 0: (D << 4) at p = 4     f = 1: (D << 4) at p = 7    f = 2: D at p = 6
+//   f = 3: (D >> 5) at p = 4     f = 4: (D >> 5) at p = 7    pair 15 at p = 4
+// so the class of pair n is p = CLS3[n] below (c = 1/64, 1/8 or 1/16).
+constexpr uint32_t U3_ONE = 0x3C003C00u, U3_M4 = 0x00700070u, U3_M7 = 0x03800380u,
+                   U3_M6 = 0x01C001C0u;
+// mantissa position of pair n's code (4, 6 or 7)
+__host__ __device__ constexpr int cls3(int n) {
+  return n == 15 ? 4 : ((n % 5) == 2 ? 6 : ((n % 5) == 1 || (n % 5) == 4 ? 7 : 4));
+}
+
+// (m & a) | (~m & b) in one v_bfi_b32
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+  return (m & a) | (~m & b);
+}
+
+// The source word and mask of pair n (f < 5) or the assembled spare pair.
+template <int N>
+__device__ __forceinline__ uint32_t raw3_pair(uint32_t D0, uint32_t D1, uint32_t D2) {
+  if constexpr (N == 15) {
+    uint32_t t = bfi(0x00200020u, D1 >> 10, D0 >> 11);
+    t = bfi(0x00400040u, D2 >> 9, t);
+    return and_or_s(t, U3_M4, U3_ONE);
+  } else {
+    constexpr int j = N / 5, f = N % 5;
+    const uint32_t D = (j == 0) ? D0 : (j == 1 ? D1 : D2);
+    if constexpr (f == 0) return and_or_s(D << 4, U3_M4, U3_ONE);
+    else if constexpr (f == 1) return and_or_s(D << 4, U3_M7, U3_ONE);
+    else if constexpr (f == 2) return and_or_s(D, U3_M6, U3_ONE);
+    else if constexpr (f == 3) return and_or_s(D >> 5, U3_M4, U3_ONE);
+    else return and_or_s(D >> 5, U3_M7, U3_ONE);
+  }
+}
+
+// The raw A operand (1 + q c per half) of step S of a unit.
+template <int S>
+__device__ __forceinline__ u32x4 raw3_step(uint32_t D0, uint32_t D1, uint32_t D2) {
+  u32x4 r;
+  r[0] = raw3_pair<4 * S + 0>(D0, D1, D2);
+  r[1] = raw3_pair<4 * S + 1>(D0, D1, D2);
+  r[2] = raw3_pair<4 * S + 2>(D0, D1, D2);
+  r[3] = raw3_pair<4 * S + 3>(D0, D1, D2);
+  return r;
+}
+
+// The codes q0 | q1 << 16 of pair n (for table dequantization).
+template <int N>
+__device__ __forceinline__ uint32_t codes3_pair(uint32_t D0, uint32_t D1, uint32_t D2) {
+  if constexpr (N == 15) {
+    uint32_t t = bfi(0x00200020u, D1 >> 10, D0 >> 11);
+    t = bfi(0x00400040u, D2 >> 9, t);
+    return (t >> 4) & 0x00070007u;
+  } else {
+    constexpr int j = N / 5, f = N % 5;
+    const uint32_t D = (j == 0) ? D0 : (j == 1 ? D1 : D2);
+    return (D >> (3 * f)) & 0x00070007u;
+  }
+}
+
+// Per (row, group) constants of the packed dequantization for the 3-bit
+// classes c = 1/64, 1/16, 1/8: (c^-1 s, -(1 + z c)); exact for integer z in
+// 0..7 and |s| < 1024 (as in deq_const).
+struct DeqConst3 {
+  half2v k64, k16, k8;
+};
+__device__ __forceinline__ DeqConst3 deq_const3(uint32_t szw) {
+  const half2v sz = __builtin_bit_cast(half2v, szw);
+  DeqConst3 c;
+  c.k64 = __builtin_elementwise_fma(sz, half2v{(half_t)64.0f, (half_t)-0.015625f},
+                                    half2v{(half_t)-0.0f, (half_t)-1.0f});
+  c.k16 = __builtin_elementwise_fma(c.k64, half2v{(half_t)0.25f, (half_t)4.0f},
+                                    half2v{(half_t)-0.0f, (half_t)3.0f});
+  c.k8 = __builtin_elementwise_fma(c.k16, half2v{(half_t)0.5f, (half_t)2.0f},
+                                   half2v{(half_t)-0.0f, (half_t)1.0f});
+  return c;
+}
+
+template <int N>
+__device__ __forceinline__ half2v k3_of(const DeqConst3& c) {
+  if constexpr (cls3(N) == 4) return c.k64;
+  else if constexpr (cls3(N) == 6) return c.k16;
+  else return c.k8;
+}
+
+// Dequantized A operand RND_f16((q - z) s) of step S of a 3-bit unit.
+template <int S>
+__device__ __forceinline__ half8v deq3_step(uint32_t D0, uint32_t D1, uint32_t D2,
+                                            const DeqConst3& c) {
+  u32x4 r;
+  r[0] = deq_pair(raw3_pair<4 * S + 0>(D0, D1, D2), k3_of<4 * S + 0>(c));
+  r[1] = deq_pair(raw3_pair<4 * S + 1>(D0, D1, D2), k3_of<4 * S + 1>(c));
+  r[2] = deq_pair(raw3_pair<4 * S + 2>(D0, D1, D2), k3_of<4 * S + 2>(c));
+  r[3] = deq_pair(raw3_pair<4 * S + 3>(D0, D1, D2), k3_of<4 * S + 3>(c));
+  return as_half8(r);
+}
+
+// Table dequantization for 3-bit codes (any finite scale and zero point):
+// the eight values RND_f16(fl32(fl32(q - z) * s)) as byte tables, low bytes
+// of q = 0..3 / 4..7 in lo0 / lo1, high bytes in hi0 / hi1.  A pair takes its
+// low bytes from lo (selector bytes q0, 12, q1, 12; 12 selects a zero byte)
+// and its high bytes from hi (12, q0, 12, q1).
+struct DeqLut3 {
+  uint32_t lo0, lo1, hi0, hi1;
+};
+__device__ __forceinline__ DeqLut3 deq_lut3(uint32_t szw) {
+  const float s = (float)__builtin_bit_cast(half_t, (uint16_t)(szw & 0xFFFFu));
+  const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(szw >> 16));
+  uint32_t h[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) h[q] = deq_bits((float)q, z, s);
+  DeqLut3 t;
+  const uint32_t h01 = h[0] | (h[1] << 16), h23 = h[2] | (h[3] << 16);
+  const uint32_t h45 = h[4] | (h[5] << 16), h67 = h[6] | (h[7] << 16);
+  t.lo0 = __builtin_amdgcn_perm(h23, h01, 0x06040200u);
+  t.hi0 = __builtin_amdgcn_perm(h23, h01, 0x07050301u);
+  t.lo1 = __builtin_amdgcn_perm(h67, h45, 0x06040200u);
+  t.hi1 = __builtin_amdgcn_perm(h67, h45, 0x07050301u);
+  return t;
+}
+__device__ __forceinline__ uint32_t lut3_pair(uint32_t x, const DeqLut3& t) {
+  const uint32_t r1 = __builtin_amdgcn_perm(t.lo1, t.lo0, x | 0x0C000C00u);
+  const uint32_t r2 = __builtin_amdgcn_perm(t.hi1, t.hi0, (x << 8) | 0x000C000Cu);
+  return r1 | r2;
+}
+template <int S>
+__device__ __forceinline__ half8v lut3_step(uint32_t D0, uint32_t D1, uint32_t D2,
+                                            const DeqLut3& t) {
+  u32x4 r;
+  r[0] = lut3_pair(codes3_pair<4 * S + 0>(D0, D1, D2), t);
+  r[1] = lut3_pair(codes3_pair<4 * S + 1>(D0, D1, D2), t);
+  r[2] = lut3_pair(codes3_pair<4 * S + 2>(D0, D1, D2), t);
+  r[3] = lut3_pair(codes3_pair<4 * S + 3>(D0, D1, D2), t);
+  return as_half8(r);
 }
 
 // ---- reductions -----------------------------------------------------------

@@ -26,6 +26,8 @@ enum Act { ACT_F16 = 0, ACT_BF16 = 1 };
 //   sigma : [r_pad] f32, zero padded
 struct ProjDev {
   int K, M, N, d_in, d_out, rank, r_pad, group, ng, nrb, nsteps;
+  int bits;       // residual code width: 2, or 3 (codes in the 3-bit layout of
+                  // repack_codes3_kernel, upload.hip)
   int deq_lut;    // 1: some scale or zero point is outside the packed dequantization's
                   // range (zero point not an integer in 0..3, or |s| >= 1024); the
                   // prefill kernels then dequantize through byte tables (deq_lut)
@@ -145,8 +147,16 @@ struct GemmArgs {
 };
 // prefill grouped GEMM; A is fp16 (bfloat16 rows converted by rows_to_f16,
 // exponents in ex); tiles of 128 slots (route bm_gemm = 128)
-void launch_gemm_prefill(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
-                         hipStream_t s);
+// (the kernels of each code width live in their own translation unit)
+void launch_gemm_prefill_b2(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
+                            hipStream_t s);
+void launch_gemm_prefill_b3(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
+                            hipStream_t s);
+inline void launch_gemm_prefill(const GemmArgs& a, GemmMode mode, Act act, int max_tiles,
+                                hipStream_t s) {
+  if (a.p[0].bits == 3) launch_gemm_prefill_b3(a, mode, act, max_tiles, s);
+  else launch_gemm_prefill_b2(a, mode, act, max_tiles, s);
+}
 // bfloat16 rows -> fp16 rows scaled by 2^-E, max|row| * 2^-E in [2^14, 2^15)
 void launch_rows_to_f16(const void* X, int rows, int d, const int* row_src, int* ex,
                         void* Y, hipStream_t s);
@@ -178,14 +188,16 @@ struct DecArgs {
   const int* arec;               // active-expert records (compact mapping) or nullptr
 };
 void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s);
-// true when 8-wave decode workgroups of np projections and this group size
-// run two per CU
-bool decode_dual(int np, int group);
+// true when 8-wave decode workgroups of np projections, this group size and
+// code width run two per CU
+bool decode_dual(int np, int group, int bits);
 
 // ---- activation preparation for the decode kernel ---------------------------
 struct PrepArgs {
   const void* X;                 // [*][d] act
   int d, G;
+  int bits;                      // code width of the projection reading the rows (class pattern)
+  uint64_t cls_exp;              // set by the launcher: class exponents of that pattern
   const int* row_src;            // output row -> input row (nullptr: identity)
   void* Xp;                      // [rows][d] f16: x~ / c
   float* sums;                   // [rows][d/G][2]
@@ -236,10 +248,10 @@ struct DenseArgs {
 void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s);
 
 // ---- upload-time kernels --------------------------------------------------
-void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, int d_in,
+void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, int d_in, int bits,
                          hipStream_t s);
 void launch_pack_sz(const uint16_t* scales, const uint16_t* zeros, uint32_t* dst,
-                    int K, int d_out, int ng, int* bad, hipStream_t s);
+                    int K, int d_out, int ng, int bits, int* bad, hipStream_t s);
 // per-expert bound on the effective weight's row sums of |W| (upload time)
 struct RowBoundArgs {
   const uint32_t* codes;         // user layout [K][d_out][d_in/16]
@@ -250,7 +262,7 @@ struct RowBoundArgs {
   const void* V;                 // [N*d_in][r]
   const int* m_of;               // [K] device
   const int* n_of;
-  int K, N, d_out, d_in, G, r, bf;
+  int K, N, d_out, d_in, G, r, bf, bits;
   float* vn;                     // scratch [N][r]
   float* l1max;                  // [K], zero on entry
 };

@@ -45,21 +45,86 @@ __global__ void repack_codes_kernel(const uint32_t* __restrict__ src, uint32_t* 
   }
 }
 
-void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, int d_in,
+// 3-bit code of input k from a row of the stored bit string (bits 3k .. 3k+2)
+__device__ __forceinline__ uint32_t code3_at(const uint32_t* row, int k) {
+  const int n = 3 * k, w = n >> 5, b = n & 31;
+  uint64_t v = row[w];
+  if (b > 29) v |= (uint64_t)row[w + 1] << 32;
+  return (uint32_t)(v >> b) & 7u;
+}
+
+// 3-bit repacked layout, per row block of 16 rows: for each group of 8 MFMA
+// k-steps, 1536 bytes: [64 lanes][dwords 0..3] (16 B per lane), then dword 4
+// of the 64 lanes, then dword 5; a trailing group of 4 k-steps is three
+// planes [dword j][64 lanes].  Dwords 0..2 are the unit of steps 0..3 of the
+// group, dwords 3..5 the unit of steps 4..7 (see raw3_pair for the bits).
+// One thread per output dword.
+__global__ void repack_codes3_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                     int K, int d_out, int d_in) {
+  const int nsteps = d_in >> 5;
+  const size_t words_in_row = (size_t)3 * d_in / 32;
+  const size_t words_per_rb = (size_t)nsteps * 48;      // 16 rows x 32 inputs x 3 bits / 32 per step
+  const size_t total = (size_t)K * (d_out >> 4) * words_per_rb;
+  const int nfull = nsteps >> 3;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const size_t erb = idx / words_per_rb;               // expert * nrb + rb
+    const int w = (int)(idx - erb * words_per_rb);
+    const int e = (int)(erb / (d_out >> 4)), rb = (int)(erb % (d_out >> 4));
+    const int sg = w / 384;                              // 384 dwords per full group
+    const int wi = w - sg * 384;
+    int lane, m;
+    if (sg < nfull) {
+      if (wi < 256) {
+        lane = wi >> 2;
+        m = wi & 3;
+      } else {
+        lane = (wi - 256) & 63;
+        m = 4 + ((wi - 256) >> 6);
+      }
+    } else {                                             // 4-step tail: three planes
+      lane = wi & 63;
+      m = wi >> 6;
+    }
+    const int u = m / 3, j = m - 3 * u;                  // unit, dword within unit
+    const int row = rb * 16 + (lane & 15), lg = lane >> 4;
+    const uint32_t* srow = src + ((size_t)e * d_out + row) * words_in_row;
+    uint32_t out = 0u;
+    for (int f = 0; f < 5; ++f) {
+      const int n = 5 * j + f, st = sg * 8 + 4 * u + (n >> 2), v = n & 3;
+      const int k = st * 32 + 8 * lg + 2 * v;
+      out |= code3_at(srow, k) << (3 * f);
+      out |= code3_at(srow, k + 1) << (16 + 3 * f);
+    }
+    {
+      const int st = sg * 8 + 4 * u + 3;                 // pair 15: step 3, inputs 6 and 7
+      const int k = st * 32 + 8 * lg + 6;
+      out |= ((code3_at(srow, k) >> j) & 1u) << 15;
+      out |= ((code3_at(srow, k + 1) >> j) & 1u) << 31;
+    }
+    dst[idx] = out;
+  }
+}
+
+void launch_repack_codes(const uint32_t* src, uint32_t* dst, int K, int d_out, int d_in, int bits,
                          hipStream_t s) {
-  const size_t total = (size_t)K * d_out * (d_in >> 4);
+  const size_t total = (size_t)K * d_out * bits * (d_in >> 5);
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL(repack_codes_kernel, dim3(blocks), dim3(256), 0, s, src, dst, K, d_out, d_in);
+  if (bits == 3)
+    hipLaunchKernelGGL(repack_codes3_kernel, dim3(blocks), dim3(256), 0, s, src, dst, K, d_out, d_in);
+  else
+    hipLaunchKernelGGL(repack_codes_kernel, dim3(blocks), dim3(256), 0, s, src, dst, K, d_out, d_in);
 }
 
 // scales/zeros [K][d_out][ng] -> [K][nrb][ng][16] (s | z << 16).  Flags in
 // *bad: 1 a scale or zero point that is not finite, 2 a dequantized weight
 // RND_f16((q - z) s) that overflows fp16 for some code q (the prefill kernels
 // multiply fp16 weights), 4 a group outside the packed dequantization's range
-// (zero point not an integer in 0..3, or |s| >= 1024): the projection then
-// dequantizes through byte tables.
+// (zero point not an integer in 0..qmax, or |s| >= 1024): the projection then
+// dequantizes through byte tables.  qmax = 3 (2-bit) or 7 (3-bit codes).
 __global__ void pack_sz_kernel(const uint16_t* __restrict__ sc, const uint16_t* __restrict__ zr,
-                               uint32_t* __restrict__ dst, int K, int d_out, int ng, int* bad) {
+                               uint32_t* __restrict__ dst, int K, int d_out, int ng, int qmax,
+                               int* bad) {
   const size_t total = (size_t)K * d_out * ng;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
@@ -71,16 +136,11 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ sc, const uint16_t* 
     const float z = (float)__builtin_bit_cast(half_t, zb);
     int flag = 0;
     if (!(fabsf(s) <= 65504.0f) || !(fabsf(z) <= 65504.0f)) flag |= 1;   // inf or nan
-    if (!(fabsf(s) < 1024.0f) || !(z == rintf(z) && z >= 0.0f && z <= 3.0f)) flag |= 4;
+    if (!(fabsf(s) < 1024.0f) || !(z == rintf(z) && z >= 0.0f && z <= (float)qmax)) flag |= 4;
     if (!(flag & 1)) {
-      const uint32_t w = (uint32_t)sb | ((uint32_t)zb << 16);
-      const DeqLut t = deq_lut(w);
       // an fp16 infinity has all exponent bits set and a zero mantissa
-      const uint32_t h[2] = {t.lo, t.hi};
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t v = ((h[0] >> (8 * q)) & 0xFFu) | (((h[1] >> (8 * q)) & 0xFFu) << 8);
-        if ((v & 0x7FFFu) == 0x7C00u) flag |= 2;
-      }
+      for (int q = 0; q <= qmax; ++q)
+        if ((deq_bits((float)q, z, s) & 0x7FFFu) == 0x7C00u) flag |= 2;
     }
     if (flag) atomicOr(bad, flag);
     const size_t out = (((size_t)e * (d_out >> 4) + (o >> 4)) * ng + g) * 16 + (o & 15);
@@ -89,11 +149,11 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ sc, const uint16_t* 
 }
 
 void launch_pack_sz(const uint16_t* scales, const uint16_t* zeros, uint32_t* dst, int K,
-                    int d_out, int ng, int* bad, hipStream_t s) {
+                    int d_out, int ng, int bits, int* bad, hipStream_t s) {
   const size_t total = (size_t)K * d_out * ng;
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
   hipLaunchKernelGGL(pack_sz_kernel, dim3(blocks), dim3(256), 0, s, scales, zeros, dst, K,
-                     d_out, ng, bad);
+                     d_out, ng, (1 << bits) - 1, bad);
 }
 
 // U [rows][r] -> [rows][r_pad] zero padded (2-byte elements)
@@ -196,22 +256,35 @@ __global__ __launch_bounds__(256) void row_l1_kernel(const uint32_t* __restrict_
                                                      const float* __restrict__ vn,
                                                      const int* __restrict__ m_of,
                                                      const int* __restrict__ n_of, int K, int d_out,
-                                                     int d_in, int G, int r, int bf,
+                                                     int d_in, int G, int r, int bf, int bits,
                                                      uint32_t* __restrict__ l1max) {
   const int lane = threadIdx.x & 63;
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (size_t)K * d_out) return;
   const int e = (int)(row / d_out), o = (int)(row % d_out);
-  const int nw = d_in >> 4, ng = d_in / G;
+  const int ng = d_in / G;
   float acc = 0.f;
-  for (int w = lane; w < nw; w += 64) {
-    const uint32_t word = codes[row * nw + w];
-    const int g = (w << 4) / G;                   // G % 16 == 0: one group per word
-    const float sa = fabsf((float)__builtin_bit_cast(half_t, (uint16_t)(scales[row * ng + g])));
-    const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(zeros[row * ng + g]));
-    float cnt = 0.f;
-    for (int j = 0; j < 16; ++j) cnt += fabsf((float)((word >> (2 * j)) & 3u) - z);
-    acc += sa * cnt;
+  if (bits == 3) {
+    const uint32_t* crow = codes + row * (size_t)(3 * d_in / 32);
+    for (int c = lane; c < (d_in >> 4); c += 64) {       // 16 inputs per lane step
+      const int g = (c << 4) / G;
+      const float sa = fabsf((float)__builtin_bit_cast(half_t, (uint16_t)(scales[row * ng + g])));
+      const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(zeros[row * ng + g]));
+      float cnt = 0.f;
+      for (int j = 0; j < 16; ++j) cnt += fabsf((float)code3_at(crow, 16 * c + j) - z);
+      acc += sa * cnt;
+    }
+  } else {
+    const int nw = d_in >> 4;
+    for (int w = lane; w < nw; w += 64) {
+      const uint32_t word = codes[row * nw + w];
+      const int g = (w << 4) / G;                   // G % 16 == 0: one group per word
+      const float sa = fabsf((float)__builtin_bit_cast(half_t, (uint16_t)(scales[row * ng + g])));
+      const float z = (float)__builtin_bit_cast(half_t, (uint16_t)(zeros[row * ng + g]));
+      float cnt = 0.f;
+      for (int j = 0; j < 16; ++j) cnt += fabsf((float)((word >> (2 * j)) & 3u) - z);
+      acc += sa * cnt;
+    }
   }
   if (r > 0) {
     const size_t urow = (size_t)m_of[e] * d_out + o;
@@ -234,7 +307,7 @@ void launch_row_bound(const RowBoundArgs& b, hipStream_t s) {
   const size_t rows = (size_t)b.K * b.d_out;
   hipLaunchKernelGGL(row_l1_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, b.codes,
                      b.scales, b.zeros, reinterpret_cast<const uint16_t*>(b.U), b.sigma, b.vn,
-                     b.m_of, b.n_of, b.K, b.d_out, b.d_in, b.G, b.r, b.bf,
+                     b.m_of, b.n_of, b.K, b.d_out, b.d_in, b.G, b.r, b.bf, b.bits,
                      reinterpret_cast<uint32_t*>(b.l1max));
 }
 
@@ -247,14 +320,42 @@ __global__ void debug_dequant_kernel(ProjDev p, int e, half_t* __restrict__ w) {
   if (item >= p.nrb * nsg) return;
   const int rb = item / nsg, sg = item - rb * nsg;
   const int gs = min(8, p.nsteps - (sg << 3));
+  const int row = rb * 16 + (lane & 15);
+  const int gsteps = p.group >> 5;
+  const size_t zb = (((size_t)e * p.nrb + rb) * p.ng) * 16 + (lane & 15);
+  half_t* orow = w + (size_t)row * p.d_in + 8 * (lane >> 4);
+  if (p.bits == 3) {
+    const uint32_t* gbase = p.codes + (size_t)e * p.d_out * (3 * p.d_in / 32) +
+                            (size_t)rb * p.nsteps * 48 + (size_t)sg * 384;
+    for (int u = 0; u < (gs >> 2); ++u) {
+      uint32_t D[3];
+      for (int j = 0; j < 3; ++j) {
+        const int m = 3 * u + j;
+        D[j] = (gs == 4) ? gbase[j * 64 + lane] : (m < 4 ? gbase[lane * 4 + m] : gbase[256 + (m - 4) * 64 + lane]);
+      }
+      const int s0 = (sg << 3) + 4 * u;
+      half8v a[4];
+      if (p.deq_lut) {
+        a[0] = lut3_step<0>(D[0], D[1], D[2], deq_lut3(p.sz[zb + (size_t)((s0 + 0) / gsteps) * 16]));
+        a[1] = lut3_step<1>(D[0], D[1], D[2], deq_lut3(p.sz[zb + (size_t)((s0 + 1) / gsteps) * 16]));
+        a[2] = lut3_step<2>(D[0], D[1], D[2], deq_lut3(p.sz[zb + (size_t)((s0 + 2) / gsteps) * 16]));
+        a[3] = lut3_step<3>(D[0], D[1], D[2], deq_lut3(p.sz[zb + (size_t)((s0 + 3) / gsteps) * 16]));
+      } else {
+        a[0] = deq3_step<0>(D[0], D[1], D[2], deq_const3(p.sz[zb + (size_t)((s0 + 0) / gsteps) * 16]));
+        a[1] = deq3_step<1>(D[0], D[1], D[2], deq_const3(p.sz[zb + (size_t)((s0 + 1) / gsteps) * 16]));
+        a[2] = deq3_step<2>(D[0], D[1], D[2], deq_const3(p.sz[zb + (size_t)((s0 + 2) / gsteps) * 16]));
+        a[3] = deq3_step<3>(D[0], D[1], D[2], deq_const3(p.sz[zb + (size_t)((s0 + 3) / gsteps) * 16]));
+      }
+      for (int st = 0; st < 4; ++st)
+        *reinterpret_cast<half8v*>(orow + (s0 + st) * 32) = a[st];
+    }
+    return;
+  }
   const size_t codes_per_expert = (size_t)p.d_out * (p.d_in >> 4);
   const uint32_t* base = p.codes + (size_t)e * codes_per_expert +
                          (((size_t)rb * p.nsteps + (sg << 3)) * 64 + lane * gs) / 2;
-  const int row = rb * 16 + (lane & 15);
-  const int gsteps = p.group >> 5;
   for (int d = 0; d < (gs >> 1); ++d) {
     const int s0 = (sg << 3) + 2 * d;
-    const size_t zb = (((size_t)e * p.nrb + rb) * p.ng) * 16 + (lane & 15);
     const uint32_t w0 = p.sz[zb + (size_t)(s0 / gsteps) * 16];
     const uint32_t w1 = p.sz[zb + (size_t)((s0 + 1) / gsteps) * 16];
     half8v a0, a1;
@@ -263,9 +364,8 @@ __global__ void debug_dequant_kernel(ProjDev p, int e, half_t* __restrict__ w) {
     } else {
       deq_dword(base[d], deq_const(w0), deq_const(w1), a0, a1);
     }
-    half_t* out = w + (size_t)row * p.d_in + s0 * 32 + 8 * (lane >> 4);
-    *reinterpret_cast<half8v*>(out) = a0;
-    *reinterpret_cast<half8v*>(out + 32) = a1;
+    *reinterpret_cast<half8v*>(orow + s0 * 32) = a0;
+    *reinterpret_cast<half8v*>(orow + s0 * 32 + 32) = a1;
   }
 }
 

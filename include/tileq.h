@@ -17,7 +17,7 @@
  *     in one batched product.
  *
  * Two calls carry the method: tq_upload_proj() (the tile map, the shared
- * factors and the packed 2-bit residual of one projection) and tq_forward()
+ * factors and the packed 2- or 3-bit residual of one projection) and tq_forward()
  * (token activations plus top-k routing).  Everything else is set-up,
  * workspace sizing and test hooks.
  *
@@ -71,15 +71,19 @@ typedef enum { TQ_SINGLE = 0, TQ_SWIGLU = 1 } tq_kind;
  * d_in and d_out the projection's input and output widths, rank r >= 0,
  * residual group size G along d_in, code width `bits`.  Requirements:
  * d_in % 128 == 0, d_out % 16 == 0, G % 32 == 0, d_in % G == 0, r <= 128,
- * bits == 2.
+ * bits 2 or 3 (3: G a power of two, 32 .. 256).
  *   tile_of_expert HOST   int32 [K]: tile index m*N + n of each expert;
  *                         must be injective and in [0, M*N) (empty tiles allowed).
  *   U      DEVICE act   [M*d_out][r] row-major; block m = rows m*d_out ...
  *   sigma  DEVICE sigma_dtype [r] (the diagonal of Sigma, any order);
  *          sigma_dtype TQ_F16 or TQ_F32 (kept as f32 either way, exactly)
  *   V      DEVICE act   [N*d_in][r]  row-major; block n = rows n*d_in ...
- *   codes  DEVICE u32   [K][d_out][d_in/16]: 2-bit code of input i at bits
- *                       2*(i%16) .. 2*(i%16)+1 of word i/16
+ *   codes  DEVICE u32   bits 2: [K][d_out][d_in/16], the code of input i at
+ *                       bits 2*(i%16) .. 2*(i%16)+1 of word i/16;
+ *                       bits 3 (the pages' 3-bit setting, section 4):
+ *                       [K][d_out][3*d_in/32], each row one little-endian
+ *                       bit string with the code of input i at bits 3i ..
+ *                       3i+2 (bit n = bit n%32 of word n/32)
  *   scales DEVICE f16   [K][d_out][d_in/G]   any finite value
  *   zeros  DEVICE f16   [K][d_out][d_in/G]   any finite value (fractional too)
  * The residual weight is R_e[o][i] = s[e][o][i/G] * (q[e][o][i] - z[e][o][i/G]).
@@ -117,7 +121,8 @@ tq_status tq_layer_create(tq_kind kind, tq_dtype act, int32_t d_model, int32_t d
  * Errors: TQ_EINVAL (non-injective or out-of-range map, NULL pointers, bad
  * sigma_dtype, a scale or zero point that is not finite or whose dequantized
  * weight overflows fp16), TQ_ESHAPE (sizes inconsistent with the layer or the
- * requirements above), TQ_EUNSUPPORTED (bits other than 2), TQ_ENOMEM, TQ_EHIP. */
+ * requirements above), TQ_EUNSUPPORTED (bits other than 2 or 3; 3-bit codes with
+ * a group size that is not a power of two from 32 to 256), TQ_ENOMEM, TQ_EHIP. */
 tq_status tq_upload_proj(tq_layer *L, int32_t which, const tq_proj_desc *d, void *stream);
 
 /* Optional dense shared expert, added to every token with weight 1 (SWIGLU
@@ -151,7 +156,8 @@ tq_status tq_workspace_size(const tq_layer *L, int32_t T, int32_t topk, size_t *
  * when they use distinct workspaces.
  * Errors (all checked before any launch): TQ_EINVAL (NULL pointers, y_dtype),
  * TQ_ESHAPE (T, topk, ws_bytes too small), TQ_ESTATE, TQ_EUNSUPPORTED
- * (T * d_model * 2 >= 2^31 bytes of activations), TQ_EHIP (launch failure). */
+ * (T * d_model * 2 >= 2^31 bytes of activations; gate and up uploaded with
+ * different code widths), TQ_EHIP (launch failure). */
 tq_status tq_forward(const tq_layer *L, const void *x, int32_t T, const int32_t *topk_ids,
                      const float *topk_w, int32_t topk, void *y, tq_dtype y_dtype,
                      void *ws, size_t ws_bytes, void *stream);

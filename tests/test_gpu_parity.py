@@ -592,3 +592,157 @@ def test_mixtral_prefill16k_bf16_every_expert_tile():
     ref = R.forward(layer, x, ids, g, tokens=tok, keep_weights=False)
     assert_parity(y32[tok], ref, "f32", what="mixtral prefill16k bf16 (y f32)")
     assert_parity(yb[tok], ref, "bf16", what="mixtral prefill16k bf16 (y bf16)")
+
+
+# ---------------------------------------------------------------------------
+# 3-bit residual codes (the pages' 3-bit setting, technical summary section 4)
+
+
+def test_dequant3_exhaustive_fp16_scales():
+    """3-bit codes: every finite fp16 scale with |s| < 1024 (both signs) x
+    every integer zero point 0..7 x every code, through the forward's own
+    unpack path (packed dequantization), bit-exact."""
+    sbits = np.concatenate([np.arange(0x0000, 0x6400), np.arange(0x8000, 0xE400)]).astype(np.uint16)
+    rows, G, d_in = len(sbits), 32, 256
+    s = np.repeat(sbits[:, None], 8, axis=1).view(np.float16)[None]
+    z = np.tile(np.arange(8, dtype=np.float16), (rows, 1))[None]
+    i = np.arange(d_in)[None, :]
+    o = np.arange(rows)[:, None]
+    q = ((i + o + i // 8) % 8)[None]
+    p = pins.proj_from(q, s, z, np.zeros((rows, 0), np.float16), [],
+                       np.zeros((d_in, 0), np.float16), [0], 1, 1, G, bits=3)
+    L = tqio.upload_layer(single_layer_from(p))
+    w = torch.empty((rows, d_in), dtype=torch.float16, device="cuda")
+    L.debug_dequant(0, 0, w)
+    torch.cuda.synchronize()
+    got = w.cpu().numpy().view(np.uint16)
+    want = R.deq_canonical(q[0], s[0], z[0], G, "f16").astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5])
+
+
+@pytest.mark.parametrize("zset", range(len(ZERO_SETS)))
+def test_dequant3_exhaustive_general(zset):
+    """3-bit codes through the table dequantization: every finite fp16 scale
+    against fractional and out-of-range zero points wherever the weights stay
+    finite, bit-exact; d_in = 384 has a 4-step tail group."""
+    zs = np.array(ZERO_SETS[zset] + ZERO_SETS[(zset + 1) % len(ZERO_SETS)], np.float16)
+    sbits = np.concatenate([np.arange(0x0000, 0x7C00), np.arange(0x8000, 0xFC00)]).astype(np.uint16)
+    sv = sbits.view(np.float16)
+    q8 = np.arange(8)[None, None, :]
+    deq = R.deq_canonical(np.broadcast_to(q8, (len(sv), 8, 8)).reshape(len(sv), 64),
+                          np.repeat(sv[:, None], 8, axis=1), np.tile(zs, (len(sv), 1)), 8)
+    sv = sv[np.all(np.isfinite(deq), axis=1)]
+    rows = len(sv) - len(sv) % 16
+    sv = sv[:rows]
+    G, d_in = 32, 384
+    ng = d_in // G
+    s = np.repeat(sv[:, None], ng, axis=1)[None]
+    z = np.tile(np.resize(zs, ng), (rows, 1))[None]
+    i = np.arange(d_in)[None, :]
+    o = np.arange(rows)[:, None]
+    q = ((3 * i + o + i // 8) % 8)[None]
+    p = pins.proj_from(q, s, z, np.zeros((rows, 0), np.float16), [],
+                       np.zeros((d_in, 0), np.float16), [0], 1, 1, G, bits=3)
+    say(f"  3-bit, zero points {tuple(float(v) for v in zs)}: {rows} scales")
+    L = tqio.upload_layer(single_layer_from(p))
+    w = torch.empty((rows, d_in), dtype=torch.float16, device="cuda")
+    L.debug_dequant(0, 0, w)
+    torch.cuda.synchronize()
+    got = w.cpu().numpy().view(np.uint16)
+    want = R.deq_canonical(q[0], s[0], z[0], G, "f16").astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5])
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_special_cases_single_3bit(path):
+    """3-bit residuals: zero rank, zero residual, a 4-step tail group
+    (d_in = 384), group sizes 32 and 128, ragged slot tiles, duplicates,
+    fractional zero points (table dequantization)."""
+    cases = {
+        "rank0": pins.random_struct(8, 2, 4, 256, 64, 0, 64, seed=131, bits=3)[0],
+        "zero_residual": pins.random_struct(8, 2, 4, 256, 64, 16, 64, seed=132, zero_res=True,
+                                            bits=3)[0],
+        "tail_G128": pins.random_struct(4, 2, 2, 384, 48, 20, 128, seed=133, bits=3)[0],
+        "r48_G32": pins.random_struct(6, 3, 3, 1408, 80, 48, 32, seed=134, bits=3)[0],
+    }
+    p = dict(cases["r48_G32"])
+    rng = np.random.default_rng(135)
+    p["zeros"] = rng.uniform(-2.0, 9.0, p["zeros"].shape).astype(np.float16)
+    cases["fractional_z"] = p
+    for name, p in cases.items():
+        L = tqio.upload_layer(single_layer_from(p))
+        L.set_path(path)
+        for T, k in [(1, 1), (37, 2), (200, 1)]:
+            x, ids, g = pins.tokens(p["d_in"], p["K"], k, T, seed=T + k)
+            y, _ = run_forward(L, x, ids, g, "f16")
+            assert_parity(y, R.forward_single(p, x, ids, g), what=f"3-bit {name} T={T} k={k}")
+        x, ids1, g1 = pins.tokens(p["d_in"], p["K"], 1, 9, seed=99)
+        ids = np.ascontiguousarray(np.concatenate([ids1, ids1], axis=1))
+        g = np.ascontiguousarray(np.concatenate([g1, 0.5 * g1], axis=1))
+        y, _ = run_forward(L, x, ids, g, "f16")
+        assert_parity(y, R.forward_single(p, x, ids, g), what=f"3-bit {name} duplicates")
+
+
+def small_swiglu_bits(act, seed, bits, K=8, M=2, N=4, d_model=256, d_ff=384, r=16, G=64):
+    ss = np.random.SeedSequence(seed).spawn(3)
+    proj = {n: synth.make_proj(K, M, N, di, do, r, G, act, s, bits=b)
+            for (n, (di, do)), s, b in zip([("gate", (d_model, d_ff)), ("up", (d_model, d_ff)),
+                                            ("down", (d_ff, d_model))], ss, bits)}
+    return dict(kind="swiglu", act=act, K=K, d_model=d_model, d_ff=d_ff, proj=proj, shared=None)
+
+
+@pytest.mark.parametrize("bits", [(3, 3, 3), (3, 3, 2), (2, 2, 3)])
+@pytest.mark.parametrize("act", ["f16", "bf16"])
+@pytest.mark.parametrize("path", [1, 2])
+def test_small_swiglu_3bit(bits, act, path):
+    """SwiGLU with 3-bit residuals, alone and with the down projection at
+    the other width (gate and up share one fused kernel and one width)."""
+    layer = small_swiglu_bits(act, 171, bits)
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    for T, k in [(1, 2), (45, 2), (300, 3)]:
+        x, ids, g = synth.make_custom_tokens(256, 8, k, T, act, seed=T + 5)
+        y, _ = run_forward(L, x, ids, g, act, "f32")
+        assert_parity(y, R.forward(layer, x, ids, g),
+                      what=f"swiglu bits={bits} {act} path={path} T={T}")
+
+
+def test_gate_up_widths_must_match():
+    layer = small_swiglu_bits("f16", 172, (2, 3, 3))
+    L = tqio.upload_layer(layer)
+    x, ids, g = synth.make_custom_tokens(256, 8, 2, 4, "f16", seed=3)
+    with pytest.raises(tq.TileQError, match="one width"):
+        run_forward(L, x, ids, g, "f16", "f32", ws=torch.empty(1 << 20, dtype=torch.uint8,
+                                                               device="cuda"))
+
+
+@pytest.fixture(scope="module")
+def mixtral_3bit():
+    cfg = synth.CONFIG_BY_NAME["mixtral8x7b_decode"]
+    layer = synth.make_layer(cfg, bits=3)
+    x, ids, g = synth.make_tokens(cfg, 64)
+    say("  oracle (Mixtral-shaped layer, 3-bit residuals, all 64 tokens)")
+    ref = R.forward(layer, x, ids, g, keep_weights=False)
+    return cfg, layer, tqio.upload_layer(layer), ref
+
+
+@pytest.mark.parametrize("B", [1, 32, 64])
+def test_mixtral_decode_3bit(mixtral_3bit, B):
+    cfg, layer, L, ref = mixtral_3bit
+    x, ids, g = synth.make_tokens(cfg, B)
+    y, _ = run_forward(L, x, ids, g, cfg.act, "f16")
+    assert_parity(y, ref[:B], "f16", what=f"mixtral decode 3-bit B={B} (all tokens)")
+
+
+def test_mixtral_prefill16k_bf16_3bit_every_expert_tile():
+    cfg = synth.CONFIG_BY_NAME["mixtral8x7b_prefill16k_bf16"]
+    layer = synth.make_layer(cfg, bits=3)
+    x, ids, g = synth.make_tokens(cfg, 16384)
+    L = tqio.upload_layer(layer)
+    y32, _ = run_forward(L, x, ids, g, cfg.act, "f32")
+    tok = tile_tokens(ids, cfg.K)
+    say(f"  3-bit 16k prefill: oracle on {len(tok)} tokens (every expert's first, full and last tile)")
+    ref = R.forward(layer, x, ids, g, tokens=tok, keep_weights=False)
+    assert_parity(y32[tok], ref, "f32", what="mixtral prefill16k bf16 3-bit (y f32)")
