@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtileq.so")
 
-TQ_F16, TQ_BF16, TQ_F32 = 0, 1, 2
+TQ_F16, TQ_BF16, TQ_F32, TQ_F64 = 0, 1, 2, 3
 TQ_SINGLE, TQ_SWIGLU = 0, 1
 P_SINGLE, P_GATE, P_UP, P_DOWN = 0, 0, 1, 2
 STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHIP",
@@ -24,7 +24,7 @@ STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHI
 EXPORTS = ["tq_layer_create", "tq_upload_proj", "tq_upload_shared_expert",
            "tq_workspace_size", "tq_forward", "tq_forward_from_logits", "tq_forward_noalloc", "tq_layer_destroy", "tq_last_error",
            "tq_abi_version", "tq_layer_set_path", "tq_forward_path", "tq_debug_route", "tq_debug_dequant", "tq_debug_row_bound", "tq_router_topk",
-           "tq_profile_enable", "tq_profile_read"]
+           "tq_profile_enable", "tq_profile_read", "tq_pack_workspace_size", "tq_pack_proj"]
 STAGES = ["route", "row_exponent", "column_stage_in", "gemm_in", "column_stage_down",
           "shared_expert", "gemm_down", "combine"]
 
@@ -43,6 +43,20 @@ class ProjDesc(ctypes.Structure):
                 ("tile_of_expert", ctypes.POINTER(ctypes.c_int32)),
                 ("U", ctypes.c_void_p), ("sigma", ctypes.c_void_p),
                 ("sigma_dtype", ctypes.c_int32), ("V", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p)]
+
+
+class PackDesc(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("group", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("sketch", ctypes.c_int32), ("power_iters", ctypes.c_int32),
+                ("act", ctypes.c_int32),
+                ("tile_of_expert", ctypes.POINTER(ctypes.c_int32)),
+                ("W", ctypes.c_void_p), ("w_dtype", ctypes.c_int32),
+                ("omega", ctypes.c_void_p),
+                ("U", ctypes.c_void_p), ("sigma", ctypes.c_void_p), ("V", ctypes.c_void_p),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p)]
 
@@ -76,6 +90,8 @@ def lib():
         L.tq_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.tq_profile_enable.argtypes = [vp, i32]
         L.tq_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
+        L.tq_pack_workspace_size.argtypes = [ctypes.POINTER(PackDesc), ctypes.POINTER(sz)]
+        L.tq_pack_proj.argtypes = [ctypes.POINTER(PackDesc), vp, sz, vp]
         for name in EXPORTS:
             if name not in ("tq_last_error", "tq_abi_version"):
                 getattr(L, name).restype = i32
@@ -107,6 +123,25 @@ def router_topk(logits, k, ids, weights, stream=None):
     T, K = logits.shape
     _check("tq_router_topk", lib().tq_router_topk(_ptr(logits), T, K, k, _ptr(ids), _ptr(weights),
                                                   _stream(stream)))
+
+
+def pack_proj(*, K, M, N, d_in, d_out, rank, group, bits, sketch, power_iters, act,
+              tile_of_expert, W, w_dtype, omega, U, sigma, V, codes, scales, zeros, ws=None,
+              stream=None):
+    """Offline packer on the device (tq_pack_proj): W (device [K][d_out][d_in]
+    of w_dtype) and omega (device f64 [N*d_in][sketch]) in; U, sigma, V,
+    codes, scales, zeros (caller-allocated device tensors) out.  Synchronous."""
+    tiles = (ctypes.c_int32 * len(tile_of_expert))(*[int(t) for t in tile_of_expert])
+    d = PackDesc(K, M, N, d_in, d_out, rank, group, bits, sketch, power_iters, act,
+                 ctypes.cast(tiles, ctypes.POINTER(ctypes.c_int32)), _ptr(W), w_dtype, _ptr(omega),
+                 _ptr(U), _ptr(sigma), _ptr(V), _ptr(codes), _ptr(scales), _ptr(zeros))
+    n = ctypes.c_size_t()
+    _check("tq_pack_workspace_size", lib().tq_pack_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    if ws is None:
+        import torch
+        ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device="cuda")
+    _check("tq_pack_proj", lib().tq_pack_proj(ctypes.byref(d), _ptr(ws), ws.numel() * ws.element_size(),
+                                              _stream(stream)))
 
 
 class Layer:

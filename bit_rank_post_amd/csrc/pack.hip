@@ -1,0 +1,659 @@
+// Offline packer on the GPU: dense expert weights in, the stored form of one
+// projection out (the input of tq_upload_proj).
+//
+// "TileQ" technical summary, section 2.1 step 4: the K experts are tiles of
+// one block matrix W_big on the M x N grid (a tile without an expert is a zero
+// block); step 5: W_big gets a global low-rank decomposition U Sigma V^T
+// approximated by Gaussian sketching instead of a full SVD, the factors are
+// stored, and each expert's residual is quantized.
+//
+// The sketch is the randomized range finder with a small SVD, all in fp64:
+//   Y = W_big Omega                                (Omega [n][l] given)
+//   Q = Y T, T = P diag(lambda^-1/2) from the eigendecomposition of Y^T Y
+//       (directions with lambda below 1e-13 lambda_max dropped), done twice
+//   power iterations: Y = W_big (W_big^T Q), orthonormalised again
+//   Z = W_big^T Q  (= B^T, B = Q^T W_big)
+//   Z^T Z = B B^T = U~ diag(s^2) U~^T (eigendecomposition, descending)
+//   U = Q U~_r, sigma = s_r, V = Z U~_r diag(1 / s_r)
+// The factors are stored as U, V in the activation format and sigma in fp32;
+// each expert's residual W_e - U_m diag(sigma) V_n^T is taken against those
+// stored values and quantized by asymmetric round to nearest per group of G
+// inputs (the forward's residual format): s = RND_f16((mx - mn) / Q) with
+// mn = min(min w, 0), mx = max(max w, 0) (1 when 0), z = clamp(rint(-mn / s)),
+// q = clamp(rint(w / s) + z), in fp64.
+//
+// Kernels: an LDS-tiled fp64 GEMM with operand readers for W_big (gathered
+// from the expert tiles, converted from the weights' dtype on load), its
+// transpose and dense arrays (split-K into slabs for the Gram matrices); a
+// one-workgroup cyclic Jacobi eigensolver for the l x l symmetric matrices
+// (l <= 136, the matrix in LDS); small elementwise kernels; the residual
+// quantizer that packs the codes.  fp64 runs on the vector ALUs: on gfx950 the
+// fp64 matrix rate equals the vector rate.
+#include "tq_device.h"
+
+namespace tq {
+
+constexpr int PK_T = 256;      // threads per workgroup
+constexpr int PK_TM = 64, PK_TN = 64, PK_TK = 16;
+constexpr int PK_LMAX = 136;   // largest sketch width (rank 128 + 8)
+
+// value of the weights' storage type as fp64
+__device__ __forceinline__ double w_at(const void* W, int wdt, size_t idx) {
+  switch (wdt) {
+    case 0: return (double)(float)reinterpret_cast<const half_t*>(W)[idx];
+    case 1: return (double)__uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(W)[idx] << 16);
+    case 2: return (double)reinterpret_cast<const float*>(W)[idx];
+    default: return reinterpret_cast<const double*>(W)[idx];
+  }
+}
+
+enum { AM_DENSE = 0, AM_DENSE_T = 1, AM_WBIG = 2, AM_WBIG_T = 3 };
+enum { BM_DENSE = 0, BM_DENSE_T = 1 };
+
+struct PkGemm {
+  int M, N, K;
+  const double* A;
+  int lda;
+  const void* W;                 // AM_WBIG(_T): expert weights [K][d_out][d_in], dtype wdt
+  int wdt, d_out, d_in, Ng;      // Ng: grid columns
+  const int* emap;               // [Mg * Ng] expert at each tile, -1 for an empty tile
+  const double* B;
+  int ldb;
+  double* C;
+  int ldc;
+  size_t slab;                   // split-K: slab z at C + z * slab
+  int kchunk;                    // split-K: K range of one slab (multiple of PK_TK)
+};
+
+// W_big(i, k): row i of the M d_out rows, column k of the N d_in columns
+__device__ __forceinline__ double wbig_at(const PkGemm& g, int i, int k) {
+  const int mt = i / g.d_out, o = i - mt * g.d_out;
+  const int nt = k / g.d_in, ii = k - nt * g.d_in;
+  const int e = g.emap[mt * g.Ng + nt];
+  if (e < 0) return 0.0;
+  return w_at(g.W, g.wdt, ((size_t)e * g.d_out + o) * g.d_in + ii);
+}
+
+// C[i][j] = sum_k A(i, k) B(k, j) over this slab's K range; 64 x 64 tiles,
+// each thread a 4 x 4 block, K in chunks of 16 staged through LDS.
+template <int AM, int BM>
+__global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
+  __shared__ double sA[PK_TK][PK_TM + 2];
+  __shared__ double sB[PK_TK][PK_TN + 2];
+  const int tid = threadIdx.x;
+  const int i0 = blockIdx.y * PK_TM, j0 = blockIdx.x * PK_TN;
+  const int k_begin = blockIdx.z * g.kchunk;
+  const int k_end = min(g.K, k_begin + g.kchunk);
+  const int ty = tid >> 4, tx = tid & 15;
+  double acc[4][4] = {};
+  for (int k0 = k_begin; k0 < k_end; k0 += PK_TK) {
+    // A tile [16 k][64 i]: the reader walks the operand's contiguous axis
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      int i, kk;
+      if constexpr (AM == AM_DENSE || AM == AM_WBIG) {
+        kk = tid & 15;
+        i = (tid >> 4) + 16 * s;
+      } else {
+        i = tid & 63;
+        kk = (tid >> 6) + 4 * s;
+      }
+      const int gi = i0 + i, gk = k0 + kk;
+      double v = 0.0;
+      if (gi < g.M && gk < k_end) {
+        if constexpr (AM == AM_DENSE) v = g.A[(size_t)gi * g.lda + gk];
+        else if constexpr (AM == AM_DENSE_T) v = g.A[(size_t)gk * g.lda + gi];
+        else if constexpr (AM == AM_WBIG) v = wbig_at(g, gi, gk);
+        else v = wbig_at(g, gk, gi);
+      }
+      sA[kk][i] = v;
+    }
+    // B tile [16 k][64 j]
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      int j, kk;
+      if constexpr (BM == BM_DENSE) {
+        j = tid & 63;
+        kk = (tid >> 6) + 4 * s;
+      } else {
+        kk = tid & 15;
+        j = (tid >> 4) + 16 * s;
+      }
+      const int gj = j0 + j, gk = k0 + kk;
+      double v = 0.0;
+      if (gj < g.N && gk < k_end) {
+        if constexpr (BM == BM_DENSE) v = g.B[(size_t)gk * g.ldb + gj];
+        else v = g.B[(size_t)gj * g.ldb + gk];
+      }
+      sB[kk][j] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < PK_TK; ++kk) {
+      double a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = sA[kk][ty * 4 + u];
+        b[u] = sB[kk][tx * 4 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+  double* C = g.C + (size_t)blockIdx.z * g.slab;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int gi = i0 + ty * 4 + u;
+    if (gi >= g.M) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int gj = j0 + tx * 4 + v;
+      if (gj < g.N) C[(size_t)gi * g.ldc + gj] = acc[u][v];
+    }
+  }
+}
+
+// K range of one split-K slab and the number of slabs for `splits` requested
+static int pk_kchunk(int K, int splits) {
+  splits = std::max(1, splits);
+  return std::max(PK_TK, ((K + splits - 1) / splits + PK_TK - 1) / PK_TK * PK_TK);
+}
+static int pk_nslab(int K, int splits) {
+  const int kc = pk_kchunk(K, splits);
+  return std::max(1, (K + kc - 1) / kc);
+}
+
+void launch_pk_gemm(const PkGemm& g0, int amode, int bmode, int splits, hipStream_t s) {
+  PkGemm g = g0;
+  g.kchunk = pk_kchunk(g.K, splits);
+  splits = pk_nslab(g.K, splits);
+  const dim3 grid((g.N + PK_TN - 1) / PK_TN, (g.M + PK_TM - 1) / PK_TM, std::max(1, splits));
+#define PK_L(A, B) hipLaunchKernelGGL((pk_gemm_kernel<A, B>), grid, dim3(PK_T), 0, s, g)
+  if (bmode == BM_DENSE) {
+    switch (amode) {
+      case AM_DENSE: PK_L(AM_DENSE, BM_DENSE); break;
+      case AM_DENSE_T: PK_L(AM_DENSE_T, BM_DENSE); break;
+      case AM_WBIG: PK_L(AM_WBIG, BM_DENSE); break;
+      default: PK_L(AM_WBIG_T, BM_DENSE); break;
+    }
+  } else {
+    PK_L(AM_DENSE, BM_DENSE_T);
+  }
+#undef PK_L
+}
+
+// ---- symmetric eigendecomposition of an l x l matrix (one workgroup) -------
+// The matrix is the sum of `nslab` slabs (split-K partial Gram matrices) of
+// which the upper triangle is read.  Cyclic Jacobi with the round-robin
+// (circle) ordering: each round rotates l/2 disjoint pairs (p, q) at once --
+// rows of A, then columns, then columns of the eigenvector matrix E (in
+// global memory) -- and a sweep is l - 1 rounds; sweeps stop when the
+// off-diagonal mass is below 1e-28 of the total, or when a sweep no longer
+// halves it (the rounding floor), at most 40.  The rotation
+// for a pair zeroes a_pq: theta = (a_qq - a_pp) / (2 a_pq),
+// t = sign(theta) / (|theta| + sqrt(theta^2 + 1)), c = 1 / sqrt(t^2 + 1),
+// s = t c.  Output: eigenvalues descending in eval, eigenvector j in column j
+// of evec (ties in index order).
+__global__ __launch_bounds__(PK_T) void pk_jacobi_kernel(const double* __restrict__ G, int l,
+                                                         int nslab, size_t slab,
+                                                         double* __restrict__ E,
+                                                         double* __restrict__ evec,
+                                                         double* __restrict__ eval) {
+  __shared__ double sA[PK_LMAX * PK_LMAX];
+  __shared__ double s_c[PK_LMAX / 2 + 1], s_s[PK_LMAX / 2 + 1];
+  __shared__ int s_p[PK_LMAX / 2 + 1], s_q[PK_LMAX / 2 + 1];
+  __shared__ double s_red[PK_T / 64][2];
+  __shared__ int s_stop;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int idx = tid; idx < l * l; idx += PK_T) {
+    const int a = idx / l, b = idx - a * l;
+    const int r0 = min(a, b), c0 = max(a, b);
+    double v = 0.0;
+    for (int z = 0; z < nslab; ++z) v += G[z * slab + (size_t)r0 * l + c0];
+    sA[idx] = v;
+    E[idx] = (a == b) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  const int le = l + (l & 1);          // even number of players (one dummy when l is odd)
+  const int np = le / 2;
+  double prev_off = -1.0;              // (thread 0) off-diagonal mass of the previous sweep
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    // convergence: off-diagonal against total squared mass
+    double off = 0.0, tot = 0.0;
+    for (int idx = tid; idx < l * l; idx += PK_T) {
+      const double v = sA[idx];
+      tot += v * v;
+      if (idx / l != idx % l) off += v * v;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o, 64);
+      tot += __shfl_xor(tot, o, 64);
+    }
+    if (lane == 0) {
+      s_red[wv][0] = off;
+      s_red[wv][1] = tot;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double o2 = 0.0, t2 = 0.0;
+      for (int w = 0; w < PK_T / 64; ++w) {
+        o2 += s_red[w][0];
+        t2 += s_red[w][1];
+      }
+      // converged, or at the rounding floor (the last sweep did not halve it)
+      s_stop = (o2 <= 1e-28 * t2 || (prev_off >= 0.0 && o2 > 0.5 * prev_off)) ? 1 : 0;
+      prev_off = o2;
+    }
+    __syncthreads();
+    if (s_stop) break;
+    for (int round = 0; round < le - 1; ++round) {
+      // circle method: player 0 fixed, the others rotate
+      if (tid < np) {
+        auto pos = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + round) % (le - 1); };
+        int p = pos(tid), q = pos(le - 1 - tid);
+        if (p > q) {
+          const int t = p;
+          p = q;
+          q = t;
+        }
+        double c = 1.0, sn = 0.0;
+        if (q < l) {
+          const double apq = sA[p * l + q];
+          if (apq != 0.0) {
+            const double theta = (sA[q * l + q] - sA[p * l + p]) / (2.0 * apq);
+            const double t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            c = 1.0 / sqrt(t * t + 1.0);
+            sn = t * c;
+          }
+        }
+        s_p[tid] = p;
+        s_q[tid] = (q < l) ? q : -1;
+        s_c[tid] = c;
+        s_s[tid] = sn;
+      }
+      __syncthreads();
+      // rows p, q of A (J^T A)
+      for (int idx = tid; idx < np * l; idx += PK_T) {
+        const int k = idx / l, j = idx - k * l;
+        const int p = s_p[k], q = s_q[k];
+        if (q < 0) continue;
+        const double c = s_c[k], sn = s_s[k];
+        const double ap = sA[p * l + j], aq = sA[q * l + j];
+        sA[p * l + j] = c * ap - sn * aq;
+        sA[q * l + j] = sn * ap + c * aq;
+      }
+      __syncthreads();
+      // columns p, q of A (A J) and of E (E J)
+      for (int idx = tid; idx < np * l; idx += PK_T) {
+        const int k = idx / l, j = idx - k * l;
+        const int p = s_p[k], q = s_q[k];
+        if (q < 0) continue;
+        const double c = s_c[k], sn = s_s[k];
+        const double ap = sA[j * l + p], aq = sA[j * l + q];
+        sA[j * l + p] = c * ap - sn * aq;
+        sA[j * l + q] = sn * ap + c * aq;
+        const double ep = E[(size_t)j * l + p], eq = E[(size_t)j * l + q];
+        E[(size_t)j * l + p] = c * ep - sn * eq;
+        E[(size_t)j * l + q] = sn * ep + c * eq;
+      }
+      __threadfence_block();
+      __syncthreads();
+    }
+  }
+  // descending order: rank of eigenvalue j (ties by index)
+  for (int j = tid; j < l; j += PK_T) {
+    const double v = sA[j * l + j];
+    int rank = 0;
+    for (int i = 0; i < l; ++i) {
+      const double w = sA[i * l + i];
+      rank += (w > v || (w == v && i < j)) ? 1 : 0;
+    }
+    eval[rank] = v;
+    for (int a = 0; a < l; ++a) evec[(size_t)a * l + rank] = E[(size_t)a * l + j];
+  }
+}
+
+// T[a][j] = evec[a][j] / sqrt(eval[j]) for eval[j] > rel * eval[0], else 0
+// (orthonormalisation transform of a basis from its Gram matrix)
+__global__ void pk_whiten_kernel(const double* __restrict__ evec, const double* __restrict__ eval,
+                                 int l, double rel, double* __restrict__ T) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= l * l) return;
+  const int j = idx % l;
+  const double lam = eval[j], top = eval[0];
+  T[idx] = (top > 0.0 && lam > rel * top) ? evec[idx] / sqrt(lam) : 0.0;
+}
+
+// The leading r columns of U~ scaled for V: S[a][c] = evec[a][c] / s_c with
+// s_c = sqrt(eval[c]) (0 where s_c is 0), and sigma64[c] = s_c.
+__global__ void pk_vscale_kernel(const double* __restrict__ evec, const double* __restrict__ eval,
+                                 int l, int r, double* __restrict__ Sv, double* __restrict__ sig64) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= l * r) return;
+  const int a = idx / r, c = idx - a * r;
+  const double sv = sqrt(fmax(eval[c], 0.0));
+  Sv[idx] = (sv > 0.0) ? evec[(size_t)a * l + c] / sv : 0.0;
+  if (a == 0) sig64[c] = sv;
+}
+
+// fp64 -> fp16 / bf16 bits, one rounding to nearest even (the format's grid:
+// 11 or 8 significant bits, smallest normal exponent -14 or -126, quantum
+// 2^-24 or 2^-133 below it; overflow to infinity)
+__device__ __forceinline__ uint16_t rnd_f64_to(double v, int bf) {
+  const int bits = bf ? 8 : 11, emin = bf ? -126 : -14;
+  const double vmax = bf ? 3.3895313892515355e38 : 65504.0;
+  const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  int ex;
+  frexp(a, &ex);                                   // a = m 2^ex, m in [0.5, 1)
+  const int qexp = max(ex - 1, emin) - (bits - 1);
+  const double r = ldexp(rint(ldexp(a, -qexp)), qexp);
+  const double limit = vmax + ldexp(1.0, (bf ? 127 : 15) - bits);   // halfway above vmax
+  if (a >= limit) return sign | (bf ? 0x7F80u : 0x7C00u);
+  // r is exactly representable: take its fp32 bits (bf16 = high half; fp16 by conversion)
+  const float rf = (float)r;
+  if (bf) return sign | (uint16_t)(__float_as_uint(rf) >> 16);
+  return sign | (uint16_t)__builtin_bit_cast(uint16_t, (half_t)rf);
+}
+
+// U or V columns 0..r-1 from an fp64 [rows][ld] array to the activation format
+// [rows][r]; and the fp64 values of the stored numbers (times sigma32 when
+// given) for the residual.
+__global__ void pk_store_kernel(const double* __restrict__ X, int rows, int ld, int r, int bf,
+                                uint16_t* __restrict__ out, const float* __restrict__ sig32,
+                                double* __restrict__ x64) {
+  const size_t total = (size_t)rows * r;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const size_t i = idx / r;
+    const int c = (int)(idx - i * r);
+    const uint16_t h = rnd_f64_to(X[i * ld + c], bf);
+    out[idx] = h;
+    const double v = bf ? (double)__uint_as_float((uint32_t)h << 16)
+                        : (double)(float)__builtin_bit_cast(half_t, h);
+    x64[idx] = sig32 ? v * (double)sig32[c] : v;
+  }
+}
+
+__global__ void pk_sigma_kernel(const double* __restrict__ sig64, int r, float* __restrict__ sig32) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c < r) sig32[c] = (float)sig64[c];
+}
+
+// Residual of expert e, w = W_e[o][i] - L[o][i] (L its block of the stored
+// low-rank product), quantized per group: one thread per (row, group); the
+// group's codes go to the output words (2-bit: 16 per word; 3-bit: the row's
+// bit string, 32 codes in 3 words -- G % 32 == 0 keeps a group's words whole).
+__global__ void pk_rtn_kernel(const void* __restrict__ W, int wdt, int e, int d_out, int d_in, int G,
+                              int bits, const double* __restrict__ L, uint32_t* __restrict__ codes,
+                              uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
+  const int ng = d_in / G;
+  const size_t item = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= (size_t)d_out * ng) return;
+  const int o = (int)(item / ng), g = (int)(item - (size_t)o * ng);
+  const size_t wrow = ((size_t)e * d_out + o) * d_in + (size_t)g * G;
+  const double* lrow = L + (size_t)o * d_in + (size_t)g * G;
+  double mn = 0.0, mx = 0.0;
+  for (int i = 0; i < G; ++i) {
+    const double w = w_at(W, wdt, wrow + i) - lrow[i];
+    mn = fmin(mn, w);
+    mx = fmax(mx, w);
+  }
+  const int qmax = (1 << bits) - 1;
+  const uint16_t sb = rnd_f64_to((mx - mn) / (double)qmax, 0);
+  double s = (double)(float)__builtin_bit_cast(half_t, sb);
+  uint16_t sbits = sb;
+  if (s == 0.0) {
+    s = 1.0;
+    sbits = 0x3C00u;
+  }
+  const double z = fmin(fmax(rint(-mn / s), 0.0), (double)qmax);
+  const size_t sz = ((size_t)e * d_out + o) * ng + g;
+  scales[sz] = sbits;
+  zeros[sz] = __builtin_bit_cast(uint16_t, (half_t)(float)z);
+  const size_t wpr = (size_t)bits * d_in / 32;                 // words per row
+  uint32_t* crow = codes + ((size_t)e * d_out + o) * wpr + (size_t)g * G * bits / 32;
+  for (int c0 = 0; c0 < G; c0 += 32) {                          // 32 codes at a time
+    uint32_t wd[3] = {0u, 0u, 0u};
+    for (int j = 0; j < 32; ++j) {
+      const double w = w_at(W, wdt, wrow + c0 + j) - lrow[c0 + j];
+      const uint32_t q = (uint32_t)fmin(fmax(rint(w / s) + z, 0.0), (double)qmax);
+      const int b = bits * j;
+      wd[b >> 5] |= q << (b & 31);
+      if ((b & 31) + bits > 32) wd[(b >> 5) + 1] |= q >> (32 - (b & 31));
+    }
+    for (int t = 0; t < bits; ++t) crow[(size_t)c0 * bits / 32 + t] = wd[t];
+  }
+}
+
+// ---- the pipeline ----------------------------------------------------------
+struct PackPlan {
+  size_t emap, Y, Q, Z, Gp, E, evec, eval, T, Sv, sig64, U64, V64, L, total;
+  int gsplit;
+};
+
+PackPlan pack_plan(int M, int N, int d_in, int d_out, int r, int l) {
+  PackPlan p{};
+  const size_t m = (size_t)M * d_out, n = (size_t)N * d_in;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = (o + bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  p.gsplit = (int)std::min<size_t>(64, std::max<size_t>(1, std::max(m, n) / 512));
+  p.emap = take((size_t)M * N * 4);
+  p.Y = take(m * l * 8);
+  p.Q = take(m * l * 8);
+  p.Z = take(n * l * 8);
+  p.Gp = take((size_t)p.gsplit * l * l * 8);
+  p.E = take((size_t)l * l * 8);
+  p.evec = take((size_t)l * l * 8);
+  p.eval = take((size_t)l * 8);
+  p.T = take((size_t)l * l * 8);
+  p.Sv = take((size_t)l * std::max(r, 1) * 8);
+  p.sig64 = take((size_t)std::max(r, 1) * 8);
+  p.U64 = take(m * std::max(r, 1) * 8);
+  p.V64 = take(n * std::max(r, 1) * 8);
+  p.L = take((size_t)d_out * d_in * 8);
+  p.total = o;
+  return p;
+}
+
+template <typename X>
+static X* at_ws(void* ws, size_t off) {
+  return reinterpret_cast<X*>(reinterpret_cast<char*>(ws) + off);
+}
+
+// Gram matrix X^T X of X [rows][l] into split-K slabs, then its
+// eigendecomposition and the whitening transform; Xo = X T.
+static void orthonormalise(const double* X, size_t rows, int l, double* Xo, const PackPlan& p,
+                           void* ws, hipStream_t s) {
+  PkGemm g{};
+  g.M = l;
+  g.N = l;
+  g.K = (int)rows;
+  g.A = X;
+  g.lda = l;
+  g.B = X;
+  g.ldb = l;
+  g.C = at_ws<double>(ws, p.Gp);
+  g.ldc = l;
+  g.slab = (size_t)l * l;
+  launch_pk_gemm(g, AM_DENSE_T, BM_DENSE, p.gsplit, s);
+  const int nslab = pk_nslab((int)rows, p.gsplit);
+  hipLaunchKernelGGL(pk_jacobi_kernel, dim3(1), dim3(PK_T), 0, s, at_ws<double>(ws, p.Gp), l, nslab,
+                     (size_t)l * l, at_ws<double>(ws, p.E), at_ws<double>(ws, p.evec),
+                     at_ws<double>(ws, p.eval));
+  hipLaunchKernelGGL(pk_whiten_kernel, dim3((l * l + 255) / 256), dim3(256), 0, s,
+                     at_ws<double>(ws, p.evec), at_ws<double>(ws, p.eval), l, 1e-13,
+                     at_ws<double>(ws, p.T));
+  PkGemm h{};
+  h.M = (int)rows;
+  h.N = l;
+  h.K = l;
+  h.A = X;
+  h.lda = l;
+  h.B = at_ws<double>(ws, p.T);
+  h.ldb = l;
+  h.C = Xo;
+  h.ldc = l;
+  launch_pk_gemm(h, AM_DENSE, BM_DENSE, 1, s);
+}
+
+void run_pack(const PackArgs& a, void* ws, hipStream_t s) {
+  const PackPlan p = pack_plan(a.M, a.N, a.d_in, a.d_out, a.rank, a.l);
+  int* emap = at_ws<int>(ws, p.emap);
+  (void)hipMemcpyAsync(emap, a.emap_host, sizeof(int) * a.M * a.N, hipMemcpyHostToDevice, s);
+  const size_t m = (size_t)a.M * a.d_out, n = (size_t)a.N * a.d_in;
+  const int l = a.l, r = a.rank;
+  double* Y = at_ws<double>(ws, p.Y);
+  double* Q = at_ws<double>(ws, p.Q);
+  double* Z = at_ws<double>(ws, p.Z);
+  PkGemm wb{};
+  wb.W = a.W;
+  wb.wdt = a.wdt;
+  wb.d_out = a.d_out;
+  wb.d_in = a.d_in;
+  wb.Ng = a.N;
+  wb.emap = emap;
+  // Y = W_big Omega
+  {
+    PkGemm g = wb;
+    g.M = (int)m;
+    g.N = l;
+    g.K = (int)n;
+    g.B = a.omega;
+    g.ldb = l;
+    g.C = Y;
+    g.ldc = l;
+    launch_pk_gemm(g, AM_WBIG, BM_DENSE, 1, s);
+  }
+  orthonormalise(Y, m, l, Q, p, ws, s);
+  orthonormalise(Q, m, l, Y, p, ws, s);      // second pass: the basis is in Y
+  double* Qb = Y;
+  double* Qs = Q;
+  auto wt_times = [&](const double* X, double* out) {   // out [n][l] = W_big^T X
+    PkGemm g = wb;
+    g.M = (int)n;
+    g.N = l;
+    g.K = (int)m;
+    g.B = X;
+    g.ldb = l;
+    g.C = out;
+    g.ldc = l;
+    launch_pk_gemm(g, AM_WBIG_T, BM_DENSE, 1, s);
+  };
+  for (int it = 0; it < a.power_iters; ++it) {
+    wt_times(Qb, Z);
+    PkGemm g = wb;                              // Y' = W_big Z
+    g.M = (int)m;
+    g.N = l;
+    g.K = (int)n;
+    g.B = Z;
+    g.ldb = l;
+    g.C = Qs;
+    g.ldc = l;
+    launch_pk_gemm(g, AM_WBIG, BM_DENSE, 1, s);
+    orthonormalise(Qs, m, l, Qb, p, ws, s);
+    orthonormalise(Qb, m, l, Qs, p, ws, s);
+    std::swap(Qb, Qs);
+  }
+  // Z = W_big^T Q (= B^T); Z^T Z = B B^T
+  wt_times(Qb, Z);
+  {
+    PkGemm g{};
+    g.M = l;
+    g.N = l;
+    g.K = (int)n;
+    g.A = Z;
+    g.lda = l;
+    g.B = Z;
+    g.ldb = l;
+    g.C = at_ws<double>(ws, p.Gp);
+    g.ldc = l;
+    g.slab = (size_t)l * l;
+    launch_pk_gemm(g, AM_DENSE_T, BM_DENSE, p.gsplit, s);
+    const int nslab = pk_nslab((int)n, p.gsplit);
+    hipLaunchKernelGGL(pk_jacobi_kernel, dim3(1), dim3(PK_T), 0, s, at_ws<double>(ws, p.Gp), l,
+                       nslab, (size_t)l * l, at_ws<double>(ws, p.E), at_ws<double>(ws, p.evec),
+                       at_ws<double>(ws, p.eval));
+  }
+  if (r > 0) {
+    double* Sv = at_ws<double>(ws, p.Sv);
+    double* sig64 = at_ws<double>(ws, p.sig64);
+    hipLaunchKernelGGL(pk_vscale_kernel, dim3((l * r + 255) / 256), dim3(256), 0, s,
+                       at_ws<double>(ws, p.evec), at_ws<double>(ws, p.eval), l, r, Sv, sig64);
+    hipLaunchKernelGGL(pk_sigma_kernel, dim3(1), dim3(256), 0, s, sig64, r, a.sigma);
+    // U = Q U~_r (into Z's space is not free: use U64 as the fp64 staging)
+    double* U64 = at_ws<double>(ws, p.U64);
+    double* V64 = at_ws<double>(ws, p.V64);
+    {
+      PkGemm g{};
+      g.M = (int)m;
+      g.N = r;
+      g.K = l;
+      g.A = Qb;
+      g.lda = l;
+      g.B = at_ws<double>(ws, p.evec);
+      g.ldb = l;
+      g.C = U64;
+      g.ldc = r;
+      launch_pk_gemm(g, AM_DENSE, BM_DENSE, 1, s);
+      PkGemm h{};
+      h.M = (int)n;
+      h.N = r;
+      h.K = l;
+      h.A = Z;
+      h.lda = l;
+      h.B = Sv;
+      h.ldb = r;
+      h.C = V64;
+      h.ldc = r;
+      launch_pk_gemm(h, AM_DENSE, BM_DENSE, 1, s);
+    }
+    // stored factors, and their fp64 values (U times sigma32) in place
+    const int bf = a.act_bf16;
+    hipLaunchKernelGGL(pk_store_kernel, dim3((unsigned)std::min<size_t>((m * r + 255) / 256, 65536)),
+                       dim3(256), 0, s, U64, (int)m, r, r, bf, reinterpret_cast<uint16_t*>(a.U),
+                       a.sigma, U64);
+    hipLaunchKernelGGL(pk_store_kernel, dim3((unsigned)std::min<size_t>((n * r + 255) / 256, 65536)),
+                       dim3(256), 0, s, V64, (int)n, r, r, bf, reinterpret_cast<uint16_t*>(a.V),
+                       nullptr, V64);
+  }
+  // per expert: L = block (m, n) of the stored low-rank product, then the
+  // quantized residual
+  double* Lb = at_ws<double>(ws, p.L);
+  for (int e = 0; e < a.K; ++e) {
+    const int mt = a.tile_host[e] / a.N, nt = a.tile_host[e] % a.N;
+    if (r > 0) {
+      PkGemm g{};
+      g.M = a.d_out;
+      g.N = a.d_in;
+      g.K = r;
+      g.A = at_ws<double>(ws, p.U64) + (size_t)mt * a.d_out * r;
+      g.lda = r;
+      g.B = at_ws<double>(ws, p.V64) + (size_t)nt * a.d_in * r;
+      g.ldb = r;
+      g.C = Lb;
+      g.ldc = a.d_in;
+      launch_pk_gemm(g, AM_DENSE, BM_DENSE_T, 1, s);
+    } else {
+      (void)hipMemsetAsync(Lb, 0, (size_t)a.d_out * a.d_in * 8, s);
+    }
+    const size_t items = (size_t)a.d_out * (a.d_in / a.group);
+    hipLaunchKernelGGL(pk_rtn_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, a.W,
+                       a.wdt, e, a.d_out, a.d_in, a.group, a.bits, Lb, a.codes, a.scales, a.zeros);
+  }
+}
+
+size_t pack_workspace_bytes(int M, int N, int d_in, int d_out, int r, int l) {
+  return pack_plan(M, N, d_in, d_out, r, l).total;
+}
+
+}  // namespace tq

@@ -1209,6 +1209,99 @@ tq_status tq_router_topk(const float* logits, int32_t T, int32_t K, int32_t k, i
   return TQ_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+tq_status pack_check(const tq_pack_desc* d) {
+  if (!d) return fail(TQ_EINVAL, "descriptor is NULL");
+  if (d->K <= 0 || d->M <= 0 || d->N <= 0 || d->d_in <= 0 || d->d_out <= 0)
+    return fail(TQ_ESHAPE, "sizes must be positive");
+  if ((long)d->M * d->N > 1024 || d->K > d->M * d->N || d->K > 256 || d->N > 32)
+    return fail(TQ_ESHAPE, "K = %d experts on a %d x %d grid not supported", d->K, d->M, d->N);
+  if (d->d_in % 128 || d->d_out % 16) return fail(TQ_ESHAPE, "d_in %% 128 and d_out %% 16 must be 0");
+  if (d->group <= 0 || d->group % 32 || d->d_in % d->group)
+    return fail(TQ_ESHAPE, "group = %d must be a multiple of 32 dividing d_in", d->group);
+  if (d->bits != 2 && d->bits != 3) return fail(TQ_EUNSUPPORTED, "bits = %d", d->bits);
+  if (d->bits == 3 && (d->group > 256 || (d->group & (d->group - 1)) != 0))
+    return fail(TQ_EUNSUPPORTED, "group = %d: 3-bit codes need a power-of-two group of 32 to 256",
+                d->group);
+  if (d->rank < 0 || d->rank > 128) return fail(TQ_ESHAPE, "rank = %d outside [0, 128]", d->rank);
+  if (d->sketch < std::max(d->rank, 1) || d->sketch > PACK_SKETCH_MAX)
+    return fail(TQ_ESHAPE, "sketch = %d outside [max(rank, 1), %d]", d->sketch, PACK_SKETCH_MAX);
+  if (d->power_iters < 0 || d->power_iters > 16) return fail(TQ_ESHAPE, "power_iters = %d", d->power_iters);
+  if (d->act != TQ_F16 && d->act != TQ_BF16) return fail(TQ_EINVAL, "act must be TQ_F16 or TQ_BF16");
+  if (d->w_dtype != TQ_F16 && d->w_dtype != TQ_BF16 && d->w_dtype != TQ_F32 && d->w_dtype != TQ_F64)
+    return fail(TQ_EINVAL, "w_dtype must be TQ_F16, TQ_BF16, TQ_F32 or TQ_F64");
+  if ((long)d->M * d->d_out * d->sketch * 8 >= (1L << 40)) return fail(TQ_ESHAPE, "sketch too large");
+  if (!d->tile_of_expert || !d->W || !d->omega || !d->codes || !d->scales || !d->zeros)
+    return fail(TQ_EINVAL, "NULL pointer");
+  if (d->rank > 0 && (!d->U || !d->V || !d->sigma)) return fail(TQ_EINVAL, "U/V/sigma NULL");
+  std::vector<int> seen(d->M * d->N, -1);
+  for (int e = 0; e < d->K; ++e) {
+    const int t = d->tile_of_expert[e];
+    if (t < 0 || t >= d->M * d->N) return fail(TQ_EINVAL, "expert %d: tile %d out of range", e, t);
+    if (seen[t] >= 0) return fail(TQ_EINVAL, "experts %d and %d share tile %d", seen[t], e, t);
+    seen[t] = e;
+  }
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_pack_workspace_size(const tq_pack_desc* d, size_t* bytes) {
+  tq_status st = pack_check(d);
+  if (st != TQ_OK) return st;
+  if (!bytes) return fail(TQ_EINVAL, "bytes is NULL");
+  *bytes = pack_workspace_bytes(d->M, d->N, d->d_in, d->d_out, d->rank, d->sketch);
+  return TQ_OK;
+}
+
+tq_status tq_pack_proj(const tq_pack_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  tq_status st = pack_check(d);
+  if (st != TQ_OK) return st;
+  const size_t need = pack_workspace_bytes(d->M, d->N, d->d_in, d->d_out, d->rank, d->sketch);
+  if (!ws) return fail(TQ_EINVAL, "ws is NULL");
+  if (ws_bytes < need) return fail(TQ_ESHAPE, "ws_bytes = %zu < %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(TQ_EINVAL, "ws not 256-byte aligned");
+  std::vector<int> emap(d->M * d->N, -1);
+  for (int e = 0; e < d->K; ++e) emap[d->tile_of_expert[e]] = e;
+  PackArgs a{};
+  a.K = d->K;
+  a.M = d->M;
+  a.N = d->N;
+  a.d_in = d->d_in;
+  a.d_out = d->d_out;
+  a.rank = d->rank;
+  a.group = d->group;
+  a.bits = d->bits;
+  a.l = d->sketch;
+  a.power_iters = d->power_iters;
+  a.act_bf16 = d->act == TQ_BF16 ? 1 : 0;
+  a.W = d->W;
+  a.wdt = (int)d->w_dtype;
+  a.tile_host = d->tile_of_expert;
+  a.emap_host = emap.data();
+  a.omega = d->omega;
+  a.U = d->U;
+  a.sigma = d->sigma;
+  a.V = d->V;
+  a.codes = d->codes;
+  a.scales = d->scales;
+  a.zeros = d->zeros;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  run_pack(a, ws, s);
+  HIPCHK(hipGetLastError());
+  HIPCHK(hipStreamSynchronize(s));
+  return TQ_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
 tq_status tq_debug_row_bound(const tq_layer* L, int32_t which, float* l1_out) {
   if (!L) return fail(TQ_EINVAL, "layer is NULL");
   if (which < 0 || which >= nproj(L)) return fail(TQ_EINVAL, "projection %d not in layer", which);

@@ -277,4 +277,27 @@ void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_
                         hipStream_t s);
 void launch_debug_dequant(const ProjDev& p, int expert, void* w_out, hipStream_t s);
 
+// ---- offline packer (pack.hip) -----------------------------------------------
+struct PackArgs {
+  int K, M, N, d_in, d_out, rank, group, bits;
+  int l;                         // sketch width (rank + oversampling), <= 136
+  int power_iters;
+  int act_bf16;                  // U, V stored as bf16 (else fp16)
+  const void* W;                 // [K][d_out][d_in] expert weights
+  int wdt;                       // 0 f16, 1 bf16, 2 f32, 3 f64
+  const int* tile_host;          // HOST [K] tile of each expert
+  const int* emap_host;          // HOST [M*N] expert at each tile, -1 empty
+  const double* omega;           // [N*d_in][l]
+  void* U;                       // outputs in tq_proj_desc's layout
+  float* sigma;
+  void* V;
+  uint32_t* codes;
+  uint16_t* scales;
+  uint16_t* zeros;
+};
+// enqueue the packer on s (the caller synchronizes before emap_host goes away)
+void run_pack(const PackArgs& a, void* ws, hipStream_t s);
+size_t pack_workspace_bytes(int M, int N, int d_in, int d_out, int r, int l);
+constexpr int PACK_SKETCH_MAX = 136;
+
 }  // namespace tq

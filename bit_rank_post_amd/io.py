@@ -63,3 +63,38 @@ def tokens_to_device(x, ids, gates, act):
 def workspace(L: Layer, T: int, topk: int):
     n = L.workspace_size(T, topk)
     return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+
+
+W_DTYPES = {np.dtype(np.float16): 0, np.dtype(np.float32): 2, np.dtype(np.float64): 3}
+
+
+def pack_proj(W: np.ndarray, tiles, M: int, N: int, rank: int, group: int, bits: int,
+              omega: np.ndarray, act: str = "f16", power_iters: int = 0, w_bf16: bool = False):
+    """Pack dense expert weights W [K][d_out][d_in] (float16/32/64, or bf16 bit
+    patterns as uint16 with w_bf16) on the device; returns the projection in
+    the upload format (host arrays, as synth.make_proj lays them out)."""
+    from . import TQ_F16, TQ_BF16, pack_proj as _pack
+    K, d_out, d_in = W.shape
+    wdt = 1 if w_bf16 else W_DTYPES[np.asarray(W).dtype]
+    Wd = torch.from_numpy(np.ascontiguousarray(W).view(np.int16) if w_bf16 else np.ascontiguousarray(W)).cuda()
+    od = torch.from_numpy(np.ascontiguousarray(omega, np.float64)).cuda()
+    r = max(rank, 1)
+    dev = dict(U=torch.zeros((M * d_out, r), dtype=torch.int16, device="cuda"),
+               sigma=torch.zeros(r, dtype=torch.float32, device="cuda"),
+               V=torch.zeros((N * d_in, r), dtype=torch.int16, device="cuda"),
+               codes=torch.zeros((K, d_out, bits * d_in // 32), dtype=torch.int32, device="cuda"),
+               scales=torch.zeros((K, d_out, d_in // group), dtype=torch.int16, device="cuda"),
+               zeros=torch.zeros((K, d_out, d_in // group), dtype=torch.int16, device="cuda"))
+    _pack(K=K, M=M, N=N, d_in=d_in, d_out=d_out, rank=rank, group=group, bits=bits,
+          sketch=omega.shape[1], power_iters=power_iters, act=TQ_BF16 if act == "bf16" else TQ_F16,
+          tile_of_expert=tiles, W=Wd, w_dtype=wdt, omega=od, **dev)
+    h = {k: v.cpu().numpy() for k, v in dev.items()}
+    U = h["U"][:, :rank].view(np.uint16)
+    V = h["V"][:, :rank].view(np.uint16)
+    if act == "f16":
+        U, V = U.view(np.float16), V.view(np.float16)
+    return dict(K=K, M=M, N=N, d_in=d_in, d_out=d_out, rank=rank, group=group, bits=bits, act=act,
+                tile_of_expert=np.asarray(tiles, np.int32), U=np.ascontiguousarray(U),
+                sigma=h["sigma"][:rank].copy(), V=np.ascontiguousarray(V),
+                codes=h["codes"].view(np.uint32), scales=h["scales"].view(np.float16),
+                zeros=h["zeros"].view(np.float16))

@@ -52,7 +52,7 @@ typedef enum {
   TQ_ESTATE = 6         /* call order (e.g. forward before every upload)     */
 } tq_status;
 
-typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2 } tq_dtype;
+typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2, TQ_F64 = 3 } tq_dtype;
 
 /* TQ_SINGLE: one projection  y_t = sum_j g_tj W_e x_t.
  * TQ_SWIGLU: gate, up and down projections,
@@ -251,6 +251,56 @@ tq_status tq_debug_dequant(const tq_layer *L, int32_t which, int32_t expert, voi
  * [1, 256], k outside [1, min(K, 32)]), TQ_EHIP. */
 tq_status tq_router_topk(const float *logits, int32_t T, int32_t K, int32_t k, int32_t *ids,
                          float *weights, void *stream);
+
+/* ---- offline packer ----------------------------------------------------- */
+
+/* Dense expert weights in, one projection's stored form out (the input of
+ * tq_upload_proj): TileQ technical summary, section 2.1 step 4 (the experts
+ * are tiles of W_big; a tile without an expert is a zero block) and step 5
+ * (a global low-rank decomposition of W_big approximated by Gaussian
+ * sketching instead of a full SVD; the factors are stored; each expert's
+ * residual is quantized).  All arithmetic in fp64 on the device:
+ *   Y = W_big Omega, an orthonormal basis Q of range(Y) (power_iters times
+ *   refined by Y = W_big (W_big^T Q)), the small SVD of B = Q^T W_big, the
+ *   rank leading triplets stored as U, V (act) and sigma (f32); each expert's
+ *   residual against those stored factors quantized by asymmetric
+ *   round-to-nearest per group: s = RND_f16((mx - mn) / (2^bits - 1)) with
+ *   mn = min(min w, 0), mx = max(max w, 0) (1 when 0), z = clamp(rint(-mn/s)),
+ *   q = clamp(rint(w/s) + z).  (The pages quantize the residual with
+ *   calibration-based GPTQ/GPTVQ; this is the calibration-free reading.)
+ * Fields: sizes and requirements as tq_proj_desc (K <= M*N, injective map);
+ *   sketch   columns of Omega (rank + oversampling), rank <= sketch <= 136
+ *   power_iters >= 0; act TQ_F16 or TQ_BF16 (storage of U and V)
+ *   tile_of_expert HOST int32 [K]
+ *   W        DEVICE w_dtype [K][d_out][d_in], w_dtype F16, BF16, F32 or F64
+ *   omega    DEVICE f64 [N*d_in][sketch] (the sketch's random numbers, given)
+ *   outputs  DEVICE, caller-owned, in tq_proj_desc's layouts: U [M*d_out][rank]
+ *            act, sigma [rank] f32 (descending), V [N*d_in][rank] act, codes,
+ *            scales, zeros.
+ * The call enqueues on `stream` and synchronizes it before returning.
+ * Errors: TQ_EINVAL (NULL pointers, dtypes, map), TQ_ESHAPE (sizes, sketch,
+ * ws_bytes), TQ_EUNSUPPORTED (bits), TQ_EHIP. */
+typedef struct {
+  int32_t K, M, N, d_in, d_out, rank, group, bits;
+  int32_t sketch, power_iters;
+  tq_dtype act;
+  const int32_t *tile_of_expert;
+  const void *W;
+  tq_dtype w_dtype;
+  const double *omega;
+  void *U;
+  float *sigma;
+  void *V;
+  uint32_t *codes;
+  uint16_t *scales;
+  uint16_t *zeros;
+} tq_pack_desc;
+
+/* Bytes of device workspace tq_pack_proj needs (fp64 sketch, basis and
+ * Gram matrices, the fp64 stored factors, one expert's low-rank block).
+ * Errors: as tq_pack_proj's size checks. */
+tq_status tq_pack_workspace_size(const tq_pack_desc *d, size_t *bytes);
+tq_status tq_pack_proj(const tq_pack_desc *d, void *ws, size_t ws_bytes, void *stream);
 
 /* Copy the per-expert row bound of one projection to l1_out (HOST f32 [K]):
  * an upper bound on max_o sum_i |W_e[o][i]| of the effective weight
