@@ -47,6 +47,8 @@ WORKLOADS = {
     "qwen15_prefill512": ("qwen15_moe_prefill512", 512),
     "fine64_mixed4160": ("fine64_zipf_mixed4160", 4160),
     "mixtral_prefill16k": ("mixtral8x7b_prefill16k_bf16", 16384),
+    "mixtral_decode_3bit": ("mixtral8x7b_decode", 32, 3),
+    "mixtral_prefill16k_3bit": ("mixtral8x7b_prefill16k_bf16", 16384, 3),
     "tiny": ("tiny", 64),
 }
 
@@ -101,7 +103,7 @@ def proj_work(p, rows_used, cols_used, slots, col_rows):
     the active experts, U blocks of active grid rows, V blocks of active grid
     columns; flops of the residual and both low-rank products."""
     d_in, d_out, r, G = p["d_in"], p["d_out"], p["rank"], p["group"]
-    res_bytes = d_out * d_in / 4 + 4.0 * d_out * d_in / G
+    res_bytes = d_out * d_in * p.get("bits", 2) / 8 + 4.0 * d_out * d_in / G
     return dict(res_bytes=res_bytes, u_bytes=d_out * r * 2.0 * len(rows_used),
                 v_bytes=d_in * r * 2.0 * len(cols_used),
                 res_flops=2.0 * d_in * d_out * slots, col_flops=2.0 * r * d_in * col_rows)
@@ -207,10 +209,11 @@ def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
     def say(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    cfg_name, T = WORKLOADS[workload]
+    cfg_name, T = WORKLOADS[workload][:2]
+    bits = WORKLOADS[workload][2] if len(WORKLOADS[workload]) > 2 else 2
     cfg = synth.CONFIG_BY_NAME[cfg_name]
-    say(f"generating {cfg_name} (T={T})")
-    layer = synth.make_layer(cfg, scheme=scheme)
+    say(f"generating {cfg_name} (T={T}, {bits}-bit residuals)")
+    layer = synth.make_layer(cfg, scheme=scheme, bits=bits)
     pg = layer["proj"]["single" if cfg.kind == "single" else "gate"]
     x, ids, gates = synth.make_tokens(cfg, T)
     copies = max(1, copies)
@@ -331,7 +334,7 @@ def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
         "workload": f"{cfg_name}: {cfg.K} experts on {pg['M']}x{pg['N']} grid"
                     f"{'' if scheme == 'tileq' else ' (' + scheme + ')'}, "
                     f"d_model {cfg.d_model}, d_ff {cfg.d_ff}, rank {pg['rank']}, "
-                    f"2-bit group-{cfg.group} residual, top-{cfg.topk}, "
+                    f"{bits}-bit group-{cfg.group} residual, top-{cfg.topk}, "
                     f"{cfg.act} activations, T={T} tokens, {path_name} path",
         "T": T, "dtype": cfg.act, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
         "roofline": roof, "execution": "hip_graph_replay" if use_graph else "eager",
@@ -352,12 +355,63 @@ def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
     return rec, (layer, x, ids, gates)
 
 
+def bench_pack(steps, warmup):
+    """The offline packer on the Mixtral-shaped gate projection: 8 experts on
+    the 2 x 4 grid, d_out 14336, d_in 4096, rank 64 with a sketch of 72
+    columns, one power iteration, 2-bit group-128 residuals, fp16 weights in.
+    Returns a record with the pack time and its fp64 rate against the
+    published fp64 peak (78.6 TFLOP/s)."""
+    import torch
+
+    import bit_rank_post_amd as tq
+    import synth
+    K, M, N, d_out, d_in, r, l, G, q = 8, 2, 4, 14336, 4096, 64, 72, 128, 1
+    print("[bench] generating dense Mixtral-shaped gate experts", file=sys.stderr, flush=True)
+    W, tiles = synth.make_dense_experts(K, M, N, d_out, d_in, r, seed=31)
+    Wd = torch.from_numpy(W).cuda()
+    omega = torch.from_numpy(np.random.default_rng(32).standard_normal((N * d_in, l))).cuda()
+    m, n = M * d_out, N * d_in
+    out = dict(U=torch.empty((m, r), dtype=torch.float16, device="cuda"),
+               sigma=torch.empty(r, dtype=torch.float32, device="cuda"),
+               V=torch.empty((n, r), dtype=torch.float16, device="cuda"),
+               codes=torch.empty((K, d_out, d_in // 16), dtype=torch.int32, device="cuda"),
+               scales=torch.empty((K, d_out, d_in // G), dtype=torch.float16, device="cuda"),
+               zeros=torch.empty((K, d_out, d_in // G), dtype=torch.float16, device="cuda"))
+    ws = None
+    args = dict(K=K, M=M, N=N, d_in=d_in, d_out=d_out, rank=r, group=G, bits=2, sketch=l,
+                power_iters=q, act=tq.TQ_F16, tile_of_expert=tiles, W=Wd, w_dtype=tq.TQ_F16,
+                omega=omega, **out)
+    for _ in range(warmup):
+        tq.pack_proj(**args, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        tq.pack_proj(**args, ws=ws)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    flops = (2.0 * m * n * l * (2 + 2 * q)          # W_big products: sketch, power, Z
+             + 8.0 * m * l * l * (1 + q) + 2.0 * n * l * l   # Gram matrices and whitening
+             + 2.0 * m * l * r + 2.0 * n * l * r             # U, V
+             + 2.0 * K * d_out * d_in * r)                   # each expert's low-rank block
+    wbytes = K * d_out * d_in * 2.0
+    return {"workload": f"offline packer, Mixtral-shaped gate projection: {K} experts on "
+                        f"{M}x{N}, d_out {d_out}, d_in {d_in}, rank {r}, sketch {l}, "
+                        f"{q} power iteration, 2-bit group-{G} residual, fp16 weights",
+            "ms_per_pack": round(ms, 3), "steps": steps,
+            "fp64_flops_per_pack": flops,
+            "achieved_fp64_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "peak_fp64_TFLOPs": 78.6,
+            "frac": round(flops / (ms * 1e-3) / 1e12 / 78.6, 4),
+            "weight_bytes_read_per_W_pass": wbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="mixtral_decode",
+                    choices=sorted(WORKLOADS) + ["pack_mixtral_gate"])
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--scheme", default="tileq",
                     choices=("tileq", "rank0", "per_expert", "shared_u", "shared_v"),
@@ -380,6 +434,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.workload == "pack_mixtral_gate":
+        print(json.dumps(bench_pack(min(args.steps, 5), min(args.warmup, 1))))
+        return
     rec, (layer, x, ids, gates) = measure(args.workload, args.steps, args.warmup, args.copies,
                                           args.scheme)
 

@@ -37,14 +37,14 @@ constexpr int PK_T = 256;      // threads per workgroup
 constexpr int PK_TM = 64, PK_TN = 64, PK_TK = 16;
 constexpr int PK_LMAX = 136;   // largest sketch width (rank 128 + 8)
 
-// value of the weights' storage type as fp64
-__device__ __forceinline__ double w_at(const void* W, int wdt, size_t idx) {
-  switch (wdt) {
-    case 0: return (double)(float)reinterpret_cast<const half_t*>(W)[idx];
-    case 1: return (double)__uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(W)[idx] << 16);
-    case 2: return (double)reinterpret_cast<const float*>(W)[idx];
-    default: return reinterpret_cast<const double*>(W)[idx];
-  }
+// value of the weights' storage type as fp64 (WDT 0 f16, 1 bf16, 2 f32, 3 f64)
+template <int WDT>
+__device__ __forceinline__ double w_at(const void* W, size_t idx) {
+  if constexpr (WDT == 0) return (double)(float)reinterpret_cast<const half_t*>(W)[idx];
+  else if constexpr (WDT == 1)
+    return (double)__uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(W)[idx] << 16);
+  else if constexpr (WDT == 2) return (double)reinterpret_cast<const float*>(W)[idx];
+  else return reinterpret_cast<const double*>(W)[idx];
 }
 
 enum { AM_DENSE = 0, AM_DENSE_T = 1, AM_WBIG = 2, AM_WBIG_T = 3 };
@@ -65,59 +65,100 @@ struct PkGemm {
   int kchunk;                    // split-K: K range of one slab (multiple of PK_TK)
 };
 
-// W_big(i, k): row i of the M d_out rows, column k of the N d_in columns
-__device__ __forceinline__ double wbig_at(const PkGemm& g, int i, int k) {
-  const int mt = i / g.d_out, o = i - mt * g.d_out;
-  const int nt = k / g.d_in, ii = k - nt * g.d_in;
-  const int e = g.emap[mt * g.Ng + nt];
-  if (e < 0) return 0.0;
-  return w_at(g.W, g.wdt, ((size_t)e * g.d_out + o) * g.d_in + ii);
-}
-
-// C[i][j] = sum_k A(i, k) B(k, j) over this slab's K range; 64 x 64 tiles,
-// each thread a 4 x 4 block, K in chunks of 16 staged through LDS.
-template <int AM, int BM>
+// C[i][j] = sum_k A(i, k) B(k, j) over this slab's K range.  Tiles of 64 rows
+// x 16 NC columns (NC = 4: several column tiles; NC = 5 or 9: one tile of up
+// to 80 or 144 columns, the sketch's width), each thread 4 rows x NC columns,
+// K in chunks of 16 staged through LDS, the next chunk's loads in flight
+// during the current chunk's arithmetic.  W_big readers: a chunk of 16 k never
+// crosses a tile (d_in % 128 == 0, d_out % 16 == 0), so the tile and its
+// expert are found once per chunk and row (no division per element).
+template <int AM, int BM, int NC, int WDT>
 __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
+  constexpr int TN = 16 * NC;
   __shared__ double sA[PK_TK][PK_TM + 2];
-  __shared__ double sB[PK_TK][PK_TN + 2];
+  __shared__ double sB[PK_TK][TN + 2];
   const int tid = threadIdx.x;
-  const int i0 = blockIdx.y * PK_TM, j0 = blockIdx.x * PK_TN;
+  const int i0 = blockIdx.y * PK_TM, j0 = blockIdx.x * TN;
   const int k_begin = blockIdx.z * g.kchunk;
   const int k_end = min(g.K, k_begin + g.kchunk);
   const int ty = tid >> 4, tx = tid & 15;
-  double acc[4][4] = {};
-  for (int k0 = k_begin; k0 < k_end; k0 += PK_TK) {
-    // A tile [16 k][64 i]: the reader walks the operand's contiguous axis
+  // W_big readers: the parts of the address fixed for the whole kernel
+  //   AM_WBIG:   rows i = (tid >> 4) + 16 s (4 per thread): tile row and row in tile
+  //   AM_WBIG_T: column i = tid & 63 of A is a column of W_big: tile column, input
+  int rt_m[4] = {0, 0, 0, 0}, rt_o[4] = {0, 0, 0, 0};
+  int ct_n = 0, ct_i = 0;
+  if constexpr (AM == AM_WBIG) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      int i, kk;
-      if constexpr (AM == AM_DENSE || AM == AM_WBIG) {
-        kk = tid & 15;
-        i = (tid >> 4) + 16 * s;
-      } else {
-        i = tid & 63;
-        kk = (tid >> 6) + 4 * s;
-      }
-      const int gi = i0 + i, gk = k0 + kk;
-      double v = 0.0;
-      if (gi < g.M && gk < k_end) {
-        if constexpr (AM == AM_DENSE) v = g.A[(size_t)gi * g.lda + gk];
-        else if constexpr (AM == AM_DENSE_T) v = g.A[(size_t)gk * g.lda + gi];
-        else if constexpr (AM == AM_WBIG) v = wbig_at(g, gi, gk);
-        else v = wbig_at(g, gk, gi);
-      }
-      sA[kk][i] = v;
+      const int gi = min(i0 + (tid >> 4) + 16 * s, g.M - 1);
+      rt_m[s] = gi / g.d_out;
+      rt_o[s] = gi - rt_m[s] * g.d_out;
     }
-    // B tile [16 k][64 j]
+  } else if constexpr (AM == AM_WBIG_T) {
+    const int gi = min(i0 + (tid & 63), g.M - 1);
+    ct_n = gi / g.d_in;
+    ct_i = gi - ct_n * g.d_in;
+  }
+  // A and B values of a K chunk, loaded into registers one chunk ahead of
+  // the arithmetic (the global loads of chunk k0 + 16 are in flight while
+  // chunk k0 is multiplied from LDS)
+  double ra[4], rb[NC];
+  auto load_chunk = [&](int k0) {
+    if constexpr (AM == AM_WBIG) {
+      const int nt = k0 / g.d_in, ii0 = k0 - nt * g.d_in;
+      const int kk = tid & 15;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 4; ++s) {
+        const int i = (tid >> 4) + 16 * s;
+        double v = 0.0;
+        if (i0 + i < g.M && k0 + kk < k_end) {
+          const int e = g.emap[rt_m[s] * g.Ng + nt];
+          if (e >= 0) v = w_at<WDT>(g.W, ((size_t)e * g.d_out + rt_o[s]) * g.d_in + ii0 + kk);
+        }
+        ra[s] = v;
+      }
+    } else if constexpr (AM == AM_WBIG_T) {
+      const int mt = k0 / g.d_out, o0 = k0 - mt * g.d_out;
+      const int e = g.emap[mt * g.Ng + ct_n];
+      const int i = tid & 63;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int kk = (tid >> 6) + 4 * s;
+        double v = 0.0;
+        if (i0 + i < g.M && k0 + kk < k_end && e >= 0)
+          v = w_at<WDT>(g.W, ((size_t)e * g.d_out + o0 + kk) * g.d_in + ct_i);
+        ra[s] = v;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        int i, kk;
+        if constexpr (AM == AM_DENSE) {
+          kk = tid & 15;
+          i = (tid >> 4) + 16 * s;
+        } else {
+          i = tid & 63;
+          kk = (tid >> 6) + 4 * s;
+        }
+        const int gi = i0 + i, gk = k0 + kk;
+        double v = 0.0;
+        if (gi < g.M && gk < k_end) {
+          if constexpr (AM == AM_DENSE) v = g.A[(size_t)gi * g.lda + gk];
+          else v = g.A[(size_t)gk * g.lda + gi];
+        }
+        ra[s] = v;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      const int idx = tid + PK_T * t;            // 16 TN = 256 NC elements
       int j, kk;
       if constexpr (BM == BM_DENSE) {
-        j = tid & 63;
-        kk = (tid >> 6) + 4 * s;
+        j = idx % TN;
+        kk = idx / TN;
       } else {
-        kk = tid & 15;
-        j = (tid >> 4) + 16 * s;
+        kk = idx & 15;
+        j = idx >> 4;
       }
       const int gj = j0 + j, gk = k0 + kk;
       double v = 0.0;
@@ -125,21 +166,39 @@ __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
         if constexpr (BM == BM_DENSE) v = g.B[(size_t)gk * g.ldb + gj];
         else v = g.B[(size_t)gj * g.ldb + gk];
       }
-      sB[kk][j] = v;
+      rb[t] = v;
     }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if constexpr (AM == AM_DENSE || AM == AM_WBIG) sA[tid & 15][(tid >> 4) + 16 * s] = ra[s];
+      else sA[(tid >> 6) + 4 * s][tid & 63] = ra[s];
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      const int idx = tid + PK_T * t;
+      if constexpr (BM == BM_DENSE) sB[idx / TN][idx % TN] = rb[t];
+      else sB[idx & 15][idx >> 4] = rb[t];
+    }
+  };
+  double acc[4][NC] = {};
+  if (k_begin < k_end) load_chunk(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += PK_TK) {
+    store_chunk();
     __syncthreads();
+    if (k0 + PK_TK < k_end) load_chunk(k0 + PK_TK);
 #pragma unroll
     for (int kk = 0; kk < PK_TK; ++kk) {
-      double a[4], b[4];
+      double a[4], b[NC];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = sA[kk][ty * 4 + u];
-        b[u] = sB[kk][tx * 4 + u];
-      }
+      for (int u = 0; u < 4; ++u) a[u] = sA[kk][ty * 4 + u];
+#pragma unroll
+      for (int v = 0; v < NC; ++v) b[v] = sB[kk][tx + 16 * v];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+        for (int v = 0; v < NC; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
     }
     __syncthreads();
   }
@@ -149,8 +208,8 @@ __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
     const int gi = i0 + ty * 4 + u;
     if (gi >= g.M) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int gj = j0 + tx * 4 + v;
+    for (int v = 0; v < NC; ++v) {
+      const int gj = j0 + tx + 16 * v;
       if (gj < g.N) C[(size_t)gi * g.ldc + gj] = acc[u][v];
     }
   }
@@ -166,67 +225,137 @@ static int pk_nslab(int K, int splits) {
   return std::max(1, (K + kc - 1) / kc);
 }
 
+template <int AM, int BM, int NC>
+static void pk_launch_w(const PkGemm& g, dim3 grid, hipStream_t s) {
+  if constexpr (AM == AM_WBIG || AM == AM_WBIG_T) {
+    switch (g.wdt) {
+      case 0: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 0>), grid, dim3(PK_T), 0, s, g); break;
+      case 1: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 1>), grid, dim3(PK_T), 0, s, g); break;
+      case 2: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 2>), grid, dim3(PK_T), 0, s, g); break;
+      default: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 3>), grid, dim3(PK_T), 0, s, g); break;
+    }
+  } else {
+    hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 3>), grid, dim3(PK_T), 0, s, g);
+  }
+}
+
+template <int NC>
+static void pk_launch_nc(const PkGemm& g, int amode, int bmode, dim3 grid, hipStream_t s) {
+  if (bmode == BM_DENSE_T) {
+    pk_launch_w<AM_DENSE, BM_DENSE_T, NC>(g, grid, s);
+    return;
+  }
+  switch (amode) {
+    case AM_DENSE: pk_launch_w<AM_DENSE, BM_DENSE, NC>(g, grid, s); break;
+    case AM_DENSE_T: pk_launch_w<AM_DENSE_T, BM_DENSE, NC>(g, grid, s); break;
+    case AM_WBIG: pk_launch_w<AM_WBIG, BM_DENSE, NC>(g, grid, s); break;
+    default: pk_launch_w<AM_WBIG_T, BM_DENSE, NC>(g, grid, s); break;
+  }
+}
+
+// out[i] = sum over slabs z of C[z * slab + i] (slab order fixed: deterministic)
+__global__ void pk_sum_slabs_kernel(const double* __restrict__ C, int nslab, size_t slab, size_t count,
+                                    double* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (size_t)gridDim.x * blockDim.x) {
+    double v = 0.0;
+    for (int z = 0; z < nslab; ++z) v += C[z * slab + i];
+    out[i] = v;
+  }
+}
+
 void launch_pk_gemm(const PkGemm& g0, int amode, int bmode, int splits, hipStream_t s) {
   PkGemm g = g0;
   g.kchunk = pk_kchunk(g.K, splits);
   splits = pk_nslab(g.K, splits);
-  const dim3 grid((g.N + PK_TN - 1) / PK_TN, (g.M + PK_TM - 1) / PK_TM, std::max(1, splits));
-#define PK_L(A, B) hipLaunchKernelGGL((pk_gemm_kernel<A, B>), grid, dim3(PK_T), 0, s, g)
-  if (bmode == BM_DENSE) {
-    switch (amode) {
-      case AM_DENSE: PK_L(AM_DENSE, BM_DENSE); break;
-      case AM_DENSE_T: PK_L(AM_DENSE_T, BM_DENSE); break;
-      case AM_WBIG: PK_L(AM_WBIG, BM_DENSE); break;
-      default: PK_L(AM_WBIG_T, BM_DENSE); break;
-    }
-  } else {
-    PK_L(AM_DENSE, BM_DENSE_T);
-  }
-#undef PK_L
+  // one column tile for the sketch's widths (up to 144), else tiles of 64
+  const int nc = (g.N <= 64) ? 4 : (g.N <= 80 ? 5 : (g.N <= 144 ? 9 : 4));
+  const dim3 grid((g.N + 16 * nc - 1) / (16 * nc), (g.M + PK_TM - 1) / PK_TM, std::max(1, splits));
+  if (nc == 5) pk_launch_nc<5>(g, amode, bmode, grid, s);
+  else if (nc == 9) pk_launch_nc<9>(g, amode, bmode, grid, s);
+  else pk_launch_nc<4>(g, amode, bmode, grid, s);
+}
+
+// The same product into `out` (ldc = N) through `splits` split-K slabs at
+// `slabs` ([splits][M][N]) summed in slab order: more workgroups for the
+// long-K products of W_big.
+static void launch_pk_gemm_split(const PkGemm& g0, int amode, int splits, double* slabs, double* out,
+                                 hipStream_t s) {
+  PkGemm g = g0;
+  g.C = slabs;
+  g.ldc = g.N;
+  g.slab = (size_t)g.M * g.N;
+  launch_pk_gemm(g, amode, BM_DENSE, splits, s);
+  const int nslab = pk_nslab(g.K, splits);
+  const size_t count = (size_t)g.M * g.N;
+  hipLaunchKernelGGL(pk_sum_slabs_kernel, dim3((unsigned)std::min<size_t>((count + 255) / 256, 8192)),
+                     dim3(256), 0, s, slabs, nslab, g.slab, count, out);
 }
 
 // ---- symmetric eigendecomposition of an l x l matrix (one workgroup) -------
 // The matrix is the sum of `nslab` slabs (split-K partial Gram matrices) of
 // which the upper triangle is read.  Cyclic Jacobi with the round-robin
 // (circle) ordering: each round rotates l/2 disjoint pairs (p, q) at once --
-// rows of A, then columns, then columns of the eigenvector matrix E (in
-// global memory) -- and a sweep is l - 1 rounds; sweeps stop when the
-// off-diagonal mass is below 1e-28 of the total, or when a sweep no longer
-// halves it (the rounding floor), at most 40.  The rotation
-// for a pair zeroes a_pq: theta = (a_qq - a_pp) / (2 a_pq),
-// t = sign(theta) / (|theta| + sqrt(theta^2 + 1)), c = 1 / sqrt(t^2 + 1),
-// s = t c.  Output: eigenvalues descending in eval, eigenvector j in column j
-// of evec (ties in index order).
-__global__ __launch_bounds__(PK_T) void pk_jacobi_kernel(const double* __restrict__ G, int l,
+// rows of A, then columns of A and rows of the transposed eigenvector matrix
+// E^T (in LDS for l <= 96, else global memory) -- and a sweep is l - 1
+// rounds; sweeps stop when the off-diagonal mass is below `tol` of the total
+// (1e-24: off-diagonal entries ~1e-12 of the matrix, eigenvalues to ~1e-24,
+// vectors to ~1e-12), or when a sweep no longer halves it (the rounding
+// floor), at most 40.  The rotation for a pair zeroes a_pq:
+// theta = (a_qq - a_pp) / (2 a_pq), t = sign(theta) / (|theta| + sqrt(theta^2 + 1)),
+// c = 1 / sqrt(t^2 + 1), s = t c.  Output: eigenvalues descending in eval,
+// eigenvector j in column j of evec (ties in index order).
+// Rows of A and E^T are `ld` = l | 1 doubles apart: an odd stride keeps a
+// column walk (one row per lane) free of LDS bank conflicts.
+// LM: the largest l of the instance; ELDS: E in LDS too (l <= 96), else in
+// global memory (l x ld doubles at Eg).
+constexpr int PK_JT = 1024;    // threads of the eigensolver's workgroup
+
+template <int LM, bool ELDS>
+__global__ __launch_bounds__(PK_JT) void pk_jacobi_kernel(const double* __restrict__ G, int l,
                                                          int nslab, size_t slab,
-                                                         double* __restrict__ E,
+                                                         double* __restrict__ Eg,
                                                          double* __restrict__ evec,
-                                                         double* __restrict__ eval) {
-  __shared__ double sA[PK_LMAX * PK_LMAX];
-  __shared__ double s_c[PK_LMAX / 2 + 1], s_s[PK_LMAX / 2 + 1];
-  __shared__ int s_p[PK_LMAX / 2 + 1], s_q[PK_LMAX / 2 + 1];
-  __shared__ double s_red[PK_T / 64][2];
+                                                         double* __restrict__ eval, double tol) {
+  constexpr int LDM = LM | 1;
+  __shared__ double sA[LM * LDM];
+  __shared__ double sE[ELDS ? LM * LDM : 1];
+  __shared__ double s_c[LM / 2 + 1], s_s[LM / 2 + 1];
+  __shared__ int s_p[LM / 2 + 1], s_q[LM / 2 + 1];
+  double* const Et = ELDS ? sE : Eg;
+  __shared__ double s_red[PK_JT / 64][2];
   __shared__ int s_stop;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int idx = tid; idx < l * l; idx += PK_T) {
+  const int ld = l | 1;
+  for (int idx = tid; idx < l * l; idx += PK_JT) {
     const int a = idx / l, b = idx - a * l;
     const int r0 = min(a, b), c0 = max(a, b);
     double v = 0.0;
     for (int z = 0; z < nslab; ++z) v += G[z * slab + (size_t)r0 * l + c0];
-    sA[idx] = v;
-    E[idx] = (a == b) ? 1.0 : 0.0;
+    sA[a * ld + b] = v;
+    Et[(size_t)a * ld + b] = (a == b) ? 1.0 : 0.0;
   }
   __syncthreads();
   const int le = l + (l & 1);          // even number of players (one dummy when l is odd)
   const int np = le / 2;
+  // this thread's (pair, index) work items of a round, the same every round
+  constexpr int NW = (LM / 2 * LM + PK_JT - 1) / PK_JT;
+  int wk[NW], wj[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int idx = tid + PK_JT * w;
+    wk[w] = idx / l;
+    wj[w] = idx - wk[w] * l;
+  }
   double prev_off = -1.0;              // (thread 0) off-diagonal mass of the previous sweep
   for (int sweep = 0; sweep < 40; ++sweep) {
     // convergence: off-diagonal against total squared mass
     double off = 0.0, tot = 0.0;
-    for (int idx = tid; idx < l * l; idx += PK_T) {
-      const double v = sA[idx];
+    for (int idx = tid; idx < l * l; idx += PK_JT) {
+      const int a = idx / l, b = idx - a * l;
+      const double v = sA[a * ld + b];
       tot += v * v;
-      if (idx / l != idx % l) off += v * v;
+      if (a != b) off += v * v;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -240,12 +369,12 @@ __global__ __launch_bounds__(PK_T) void pk_jacobi_kernel(const double* __restric
     __syncthreads();
     if (tid == 0) {
       double o2 = 0.0, t2 = 0.0;
-      for (int w = 0; w < PK_T / 64; ++w) {
+      for (int w = 0; w < PK_JT / 64; ++w) {
         o2 += s_red[w][0];
         t2 += s_red[w][1];
       }
       // converged, or at the rounding floor (the last sweep did not halve it)
-      s_stop = (o2 <= 1e-28 * t2 || (prev_off >= 0.0 && o2 > 0.5 * prev_off)) ? 1 : 0;
+      s_stop = (o2 <= tol * t2 || (prev_off >= 0.0 && o2 > 0.5 * prev_off)) ? 1 : 0;
       prev_off = o2;
     }
     __syncthreads();
@@ -254,67 +383,79 @@ __global__ __launch_bounds__(PK_T) void pk_jacobi_kernel(const double* __restric
       // circle method: player 0 fixed, the others rotate
       if (tid < np) {
         auto pos = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + round) % (le - 1); };
-        int p = pos(tid), q = pos(le - 1 - tid);
-        if (p > q) {
-          const int t = p;
-          p = q;
-          q = t;
-        }
+        const int a0 = pos(tid), b0 = pos(le - 1 - tid);
+        const int p = min(a0, b0), q = max(a0, b0);
         double c = 1.0, sn = 0.0;
         if (q < l) {
-          const double apq = sA[p * l + q];
+          const double apq = sA[p * ld + q];
           if (apq != 0.0) {
-            const double theta = (sA[q * l + q] - sA[p * l + p]) / (2.0 * apq);
+            const double theta = (sA[q * ld + q] - sA[p * ld + p]) / (2.0 * apq);
             const double t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
             c = 1.0 / sqrt(t * t + 1.0);
             sn = t * c;
           }
         }
         s_p[tid] = p;
-        s_q[tid] = (q < l) ? q : -1;
+        s_q[tid] = (q < l) ? q : -1;             // -1: the dummy player, no rotation
         s_c[tid] = c;
         s_s[tid] = sn;
       }
       __syncthreads();
-      // rows p, q of A (J^T A)
-      for (int idx = tid; idx < np * l; idx += PK_T) {
-        const int k = idx / l, j = idx - k * l;
+      // rows p, q of A (J^T A) and of E^T (J^T E^T = (E J)^T)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int idx = tid + PK_JT * w;
+        if (idx >= np * l) continue;
+        const int k = wk[w], j = wj[w];
         const int p = s_p[k], q = s_q[k];
         if (q < 0) continue;
         const double c = s_c[k], sn = s_s[k];
-        const double ap = sA[p * l + j], aq = sA[q * l + j];
-        sA[p * l + j] = c * ap - sn * aq;
-        sA[q * l + j] = sn * ap + c * aq;
+        const double ap = sA[p * ld + j], aq = sA[q * ld + j];
+        sA[p * ld + j] = c * ap - sn * aq;
+        sA[q * ld + j] = sn * ap + c * aq;
+        const double ep = Et[(size_t)p * ld + j], eq = Et[(size_t)q * ld + j];
+        Et[(size_t)p * ld + j] = c * ep - sn * eq;
+        Et[(size_t)q * ld + j] = sn * ep + c * eq;
       }
       __syncthreads();
-      // columns p, q of A (A J) and of E (E J)
-      for (int idx = tid; idx < np * l; idx += PK_T) {
-        const int k = idx / l, j = idx - k * l;
+      // columns p, q of A (A J)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int idx = tid + PK_JT * w;
+        if (idx >= np * l) continue;
+        const int k = wk[w], j = wj[w];
         const int p = s_p[k], q = s_q[k];
         if (q < 0) continue;
         const double c = s_c[k], sn = s_s[k];
-        const double ap = sA[j * l + p], aq = sA[j * l + q];
-        sA[j * l + p] = c * ap - sn * aq;
-        sA[j * l + q] = sn * ap + c * aq;
-        const double ep = E[(size_t)j * l + p], eq = E[(size_t)j * l + q];
-        E[(size_t)j * l + p] = c * ep - sn * eq;
-        E[(size_t)j * l + q] = sn * ep + c * eq;
+        const double ap = sA[j * ld + p], aq = sA[j * ld + q];
+        sA[j * ld + p] = c * ap - sn * aq;
+        sA[j * ld + q] = sn * ap + c * aq;
       }
-      __threadfence_block();
+      if constexpr (!ELDS) __threadfence_block();
       __syncthreads();
     }
   }
   // descending order: rank of eigenvalue j (ties by index)
-  for (int j = tid; j < l; j += PK_T) {
-    const double v = sA[j * l + j];
+  for (int j = tid; j < l; j += PK_JT) {
+    const double v = sA[j * ld + j];
     int rank = 0;
     for (int i = 0; i < l; ++i) {
-      const double w = sA[i * l + i];
+      const double w = sA[i * ld + i];
       rank += (w > v || (w == v && i < j)) ? 1 : 0;
     }
     eval[rank] = v;
-    for (int a = 0; a < l; ++a) evec[(size_t)a * l + rank] = E[(size_t)a * l + j];
+    for (int a = 0; a < l; ++a) evec[(size_t)a * l + rank] = Et[(size_t)j * ld + a];
   }
+}
+
+static void launch_pk_jacobi(const double* G, int l, int nslab, size_t slab, double* E, double* evec,
+                             double* eval, double tol, hipStream_t s) {
+  if (l <= 96)
+    hipLaunchKernelGGL((pk_jacobi_kernel<96, true>), dim3(1), dim3(PK_JT), 0, s, G, l, nslab, slab, E,
+                       evec, eval, tol);
+  else
+    hipLaunchKernelGGL((pk_jacobi_kernel<PK_LMAX, false>), dim3(1), dim3(PK_JT), 0, s, G, l, nslab,
+                       slab, E, evec, eval, tol);
 }
 
 // T[a][j] = evec[a][j] / sqrt(eval[j]) for eval[j] > rel * eval[0], else 0
@@ -386,56 +527,138 @@ __global__ void pk_sigma_kernel(const double* __restrict__ sig64, int r, float* 
 }
 
 // Residual of expert e, w = W_e[o][i] - L[o][i] (L its block of the stored
-// low-rank product), quantized per group: one thread per (row, group); the
-// group's codes go to the output words (2-bit: 16 per word; 3-bit: the row's
-// bit string, 32 codes in 3 words -- G % 32 == 0 keeps a group's words whole).
-__global__ void pk_rtn_kernel(const void* __restrict__ W, int wdt, int e, int d_out, int d_in, int G,
-                              int bits, const double* __restrict__ L, uint32_t* __restrict__ codes,
-                              uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
-  const int ng = d_in / G;
-  const size_t item = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (item >= (size_t)d_out * ng) return;
-  const int o = (int)(item / ng), g = (int)(item - (size_t)o * ng);
-  const size_t wrow = ((size_t)e * d_out + o) * d_in + (size_t)g * G;
-  const double* lrow = L + (size_t)o * d_in + (size_t)g * G;
-  double mn = 0.0, mx = 0.0;
-  for (int i = 0; i < G; ++i) {
-    const double w = w_at(W, wdt, wrow + i) - lrow[i];
-    mn = fmin(mn, w);
-    mx = fmax(mx, w);
-  }
+// low-rank product), quantized per group.  One thread per 32 consecutive
+// inputs of a row (the residual kept in registers); the LPG = G / 32 threads
+// of a group (a power of two, aligned inside a wave) meet by xor shuffles for
+// the group's min and max; each thread packs its 32 codes into its own words
+// (2-bit: 2 words, code i at bits 2 (i % 16); 3-bit: 3 words of the row's bit
+// string).  LPG = 0: any G, one thread per group looping over it.
+template <int LPG, int WDT>
+__global__ __launch_bounds__(256) void pk_rtn_kernel(const void* __restrict__ W, int e, int d_out,
+                                                     int d_in, int G, int bits,
+                                                     const double* __restrict__ L,
+                                                     uint32_t* __restrict__ codes,
+                                                     uint16_t* __restrict__ scales,
+                                                     uint16_t* __restrict__ zeros) {
   const int qmax = (1 << bits) - 1;
-  const uint16_t sb = rnd_f64_to((mx - mn) / (double)qmax, 0);
-  double s = (double)(float)__builtin_bit_cast(half_t, sb);
-  uint16_t sbits = sb;
-  if (s == 0.0) {
-    s = 1.0;
-    sbits = 0x3C00u;
-  }
-  const double z = fmin(fmax(rint(-mn / s), 0.0), (double)qmax);
-  const size_t sz = ((size_t)e * d_out + o) * ng + g;
-  scales[sz] = sbits;
-  zeros[sz] = __builtin_bit_cast(uint16_t, (half_t)(float)z);
-  const size_t wpr = (size_t)bits * d_in / 32;                 // words per row
-  uint32_t* crow = codes + ((size_t)e * d_out + o) * wpr + (size_t)g * G * bits / 32;
-  for (int c0 = 0; c0 < G; c0 += 32) {                          // 32 codes at a time
+  const int ng = d_in / G;
+  const size_t wpr = (size_t)bits * d_in / 32;                 // code words per row
+  auto finish_scale = [&](double mn, double mx, double* s, double* z, int o, int g) {
+    const uint16_t sb = rnd_f64_to((mx - mn) / (double)qmax, 0);
+    double sv = (double)(float)__builtin_bit_cast(half_t, sb);
+    uint16_t sbits = sb;
+    if (sv == 0.0) {
+      sv = 1.0;
+      sbits = 0x3C00u;
+    }
+    *s = sv;
+    *z = fmin(fmax(rint(-mn / sv), 0.0), (double)qmax);
+    const size_t sz = ((size_t)e * d_out + o) * ng + g;
+    scales[sz] = sbits;
+    zeros[sz] = __builtin_bit_cast(uint16_t, (half_t)(float)*z);
+  };
+  // the 32 codes of inputs c0 .. c0 + 31 of row o into the row's words
+  auto emit = [&](const double* w, double s, double z, int o, int c0) {
     uint32_t wd[3] = {0u, 0u, 0u};
+#pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const double w = w_at(W, wdt, wrow + c0 + j) - lrow[c0 + j];
-      const uint32_t q = (uint32_t)fmin(fmax(rint(w / s) + z, 0.0), (double)qmax);
+      const uint32_t q = (uint32_t)fmin(fmax(rint(w[j] / s) + z, 0.0), (double)qmax);
       const int b = bits * j;
       wd[b >> 5] |= q << (b & 31);
       if ((b & 31) + bits > 32) wd[(b >> 5) + 1] |= q >> (32 - (b & 31));
     }
-    for (int t = 0; t < bits; ++t) crow[(size_t)c0 * bits / 32 + t] = wd[t];
+    uint32_t* crow = codes + ((size_t)e * d_out + o) * wpr + (size_t)c0 * bits / 32;
+    for (int t = 0; t < bits; ++t) crow[t] = wd[t];
+  };
+  if constexpr (LPG > 0) {
+    const int nch = d_in >> 5;
+    const size_t item = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = item < (size_t)d_out * nch;
+    const int o = live ? (int)(item / nch) : 0;
+    const int c = live ? (int)(item - (size_t)o * nch) : 0;
+    double w[32];
+    double mn = 0.0, mx = 0.0;
+    if (live) {
+      const size_t base = ((size_t)e * d_out + o) * d_in + (size_t)c * 32;
+      const double* lrow = L + (size_t)o * d_in + (size_t)c * 32;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        w[j] = w_at<WDT>(W, base + j) - lrow[j];
+        mn = fmin(mn, w[j]);
+        mx = fmax(mx, w[j]);
+      }
+    }
+#pragma unroll
+    for (int off = LPG / 2; off > 0; off >>= 1) {
+      mn = fmin(mn, __shfl_xor(mn, off, 64));
+      mx = fmax(mx, __shfl_xor(mx, off, 64));
+    }
+    if (!live) return;
+    double sv, zv;
+    const int g = c / LPG;
+    finish_scale(mn, mx, &sv, &zv, o, g);           // every lane of the group: the same values
+    emit(w, sv, zv, o, c * 32);
+  } else {
+    const size_t item = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (item >= (size_t)d_out * ng) return;
+    const int o = (int)(item / ng), g = (int)(item - (size_t)o * ng);
+    const size_t wrow = ((size_t)e * d_out + o) * d_in + (size_t)g * G;
+    const double* lrow = L + (size_t)o * d_in + (size_t)g * G;
+    double mn = 0.0, mx = 0.0;
+    for (int i = 0; i < G; ++i) {
+      const double w = w_at<WDT>(W, wrow + i) - lrow[i];
+      mn = fmin(mn, w);
+      mx = fmax(mx, w);
+    }
+    double sv, zv;
+    finish_scale(mn, mx, &sv, &zv, o, g);
+    for (int c0 = 0; c0 < G; c0 += 32) {
+      double w[32];
+      for (int j = 0; j < 32; ++j) w[j] = w_at<WDT>(W, wrow + c0 + j) - lrow[c0 + j];
+      emit(w, sv, zv, o, g * G + c0);
+    }
+  }
+}
+
+template <int WDT>
+static void pk_rtn_w(const PackArgs& a, int e, const double* L, hipStream_t s) {
+  const int lpg = a.group / 32;
+  const size_t chunks = (size_t)a.d_out * (a.d_in / 32);
+  const dim3 gc((unsigned)((chunks + 255) / 256));
+#define PK_R(N) hipLaunchKernelGGL((pk_rtn_kernel<N, WDT>), gc, dim3(256), 0, s, a.W, e, a.d_out, \
+                                   a.d_in, a.group, a.bits, L, a.codes, a.scales, a.zeros)
+  switch (lpg) {
+    case 1: PK_R(1); break;
+    case 2: PK_R(2); break;
+    case 4: PK_R(4); break;
+    case 8: PK_R(8); break;
+    case 16: PK_R(16); break;
+    case 32: PK_R(32); break;
+    case 64: PK_R(64); break;
+    default: {
+      const size_t items = (size_t)a.d_out * (a.d_in / a.group);
+      hipLaunchKernelGGL((pk_rtn_kernel<0, WDT>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                         s, a.W, e, a.d_out, a.d_in, a.group, a.bits, L, a.codes, a.scales, a.zeros);
+    }
+  }
+#undef PK_R
+}
+
+static void launch_pk_rtn(const PackArgs& a, int e, const double* L, hipStream_t s) {
+  switch (a.wdt) {
+    case 0: pk_rtn_w<0>(a, e, L, s); break;
+    case 1: pk_rtn_w<1>(a, e, L, s); break;
+    case 2: pk_rtn_w<2>(a, e, L, s); break;
+    default: pk_rtn_w<3>(a, e, L, s); break;
   }
 }
 
 // ---- the pipeline ----------------------------------------------------------
 struct PackPlan {
-  size_t emap, Y, Q, Z, Gp, E, evec, eval, T, Sv, sig64, U64, V64, L, total;
+  size_t emap, Y, Q, Z, Gp, E, evec, eval, T, Sv, sig64, U64, V64, L, slabs, total;
   int gsplit;
 };
+constexpr int PK_WSPLIT = 4;     // split-K slabs of the W_big products
 
 PackPlan pack_plan(int M, int N, int d_in, int d_out, int r, int l) {
   PackPlan p{};
@@ -452,7 +675,7 @@ PackPlan pack_plan(int M, int N, int d_in, int d_out, int r, int l) {
   p.Q = take(m * l * 8);
   p.Z = take(n * l * 8);
   p.Gp = take((size_t)p.gsplit * l * l * 8);
-  p.E = take((size_t)l * l * 8);
+  p.E = take((size_t)l * (l | 1) * 8);
   p.evec = take((size_t)l * l * 8);
   p.eval = take((size_t)l * 8);
   p.T = take((size_t)l * l * 8);
@@ -461,6 +684,7 @@ PackPlan pack_plan(int M, int N, int d_in, int d_out, int r, int l) {
   p.U64 = take(m * std::max(r, 1) * 8);
   p.V64 = take(n * std::max(r, 1) * 8);
   p.L = take((size_t)d_out * d_in * 8);
+  p.slabs = take((size_t)PK_WSPLIT * std::max(m, n) * l * 8);
   p.total = o;
   return p;
 }
@@ -487,9 +711,8 @@ static void orthonormalise(const double* X, size_t rows, int l, double* Xo, cons
   g.slab = (size_t)l * l;
   launch_pk_gemm(g, AM_DENSE_T, BM_DENSE, p.gsplit, s);
   const int nslab = pk_nslab((int)rows, p.gsplit);
-  hipLaunchKernelGGL(pk_jacobi_kernel, dim3(1), dim3(PK_T), 0, s, at_ws<double>(ws, p.Gp), l, nslab,
-                     (size_t)l * l, at_ws<double>(ws, p.E), at_ws<double>(ws, p.evec),
-                     at_ws<double>(ws, p.eval));
+  launch_pk_jacobi(at_ws<double>(ws, p.Gp), l, nslab, (size_t)l * l, at_ws<double>(ws, p.E),
+                   at_ws<double>(ws, p.evec), at_ws<double>(ws, p.eval), 1e-24, s);
   hipLaunchKernelGGL(pk_whiten_kernel, dim3((l * l + 255) / 256), dim3(256), 0, s,
                      at_ws<double>(ws, p.evec), at_ws<double>(ws, p.eval), l, 1e-13,
                      at_ws<double>(ws, p.T));
@@ -530,9 +753,7 @@ void run_pack(const PackArgs& a, void* ws, hipStream_t s) {
     g.K = (int)n;
     g.B = a.omega;
     g.ldb = l;
-    g.C = Y;
-    g.ldc = l;
-    launch_pk_gemm(g, AM_WBIG, BM_DENSE, 1, s);
+    launch_pk_gemm_split(g, AM_WBIG, PK_WSPLIT, at_ws<double>(ws, p.slabs), Y, s);
   }
   orthonormalise(Y, m, l, Q, p, ws, s);
   orthonormalise(Q, m, l, Y, p, ws, s);      // second pass: the basis is in Y
@@ -545,9 +766,7 @@ void run_pack(const PackArgs& a, void* ws, hipStream_t s) {
     g.K = (int)m;
     g.B = X;
     g.ldb = l;
-    g.C = out;
-    g.ldc = l;
-    launch_pk_gemm(g, AM_WBIG_T, BM_DENSE, 1, s);
+    launch_pk_gemm_split(g, AM_WBIG_T, PK_WSPLIT, at_ws<double>(ws, p.slabs), out, s);
   };
   for (int it = 0; it < a.power_iters; ++it) {
     wt_times(Qb, Z);
@@ -557,9 +776,7 @@ void run_pack(const PackArgs& a, void* ws, hipStream_t s) {
     g.K = (int)n;
     g.B = Z;
     g.ldb = l;
-    g.C = Qs;
-    g.ldc = l;
-    launch_pk_gemm(g, AM_WBIG, BM_DENSE, 1, s);
+    launch_pk_gemm_split(g, AM_WBIG, PK_WSPLIT, at_ws<double>(ws, p.slabs), Qs, s);
     orthonormalise(Qs, m, l, Qb, p, ws, s);
     orthonormalise(Qb, m, l, Qs, p, ws, s);
     std::swap(Qb, Qs);
@@ -580,9 +797,8 @@ void run_pack(const PackArgs& a, void* ws, hipStream_t s) {
     g.slab = (size_t)l * l;
     launch_pk_gemm(g, AM_DENSE_T, BM_DENSE, p.gsplit, s);
     const int nslab = pk_nslab((int)n, p.gsplit);
-    hipLaunchKernelGGL(pk_jacobi_kernel, dim3(1), dim3(PK_T), 0, s, at_ws<double>(ws, p.Gp), l,
-                       nslab, (size_t)l * l, at_ws<double>(ws, p.E), at_ws<double>(ws, p.evec),
-                       at_ws<double>(ws, p.eval));
+    launch_pk_jacobi(at_ws<double>(ws, p.Gp), l, nslab, (size_t)l * l, at_ws<double>(ws, p.E),
+                     at_ws<double>(ws, p.evec), at_ws<double>(ws, p.eval), 1e-24, s);
   }
   if (r > 0) {
     double* Sv = at_ws<double>(ws, p.Sv);
@@ -646,9 +862,7 @@ void run_pack(const PackArgs& a, void* ws, hipStream_t s) {
     } else {
       (void)hipMemsetAsync(Lb, 0, (size_t)a.d_out * a.d_in * 8, s);
     }
-    const size_t items = (size_t)a.d_out * (a.d_in / a.group);
-    hipLaunchKernelGGL(pk_rtn_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, a.W,
-                       a.wdt, e, a.d_out, a.d_in, a.group, a.bits, Lb, a.codes, a.scales, a.zeros);
+    launch_pk_rtn(a, e, Lb, s);
   }
 }
 

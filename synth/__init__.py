@@ -323,3 +323,29 @@ def make_custom_tokens(d_model, K, topk, T, act, seed, routing="uniform"):
     x = np.random.default_rng(a).standard_normal((T, d_model), dtype=np.float32)
     ids, gates = make_routing(K, topk, T, routing, b)
     return to_act(x, act), ids, gates
+
+
+# ----------------------------------------------------------------------------
+# dense expert weights (input of the offline packer)
+
+
+def make_dense_experts(K, M, N, d_out, d_in, rank, seed, noise=0.02, tiles=None,
+                       dtype=np.float16):
+    """Dense expert weights W [K][d_out][d_in]: the expert's block of a
+    random global low-rank matrix (columns N(0, 1/d) in std, singular values
+    log-uniform over [0.1, 10], descending) plus N(0, noise) per element, and
+    the expert -> tile map (random injective by default).  Random numbers and
+    storage only."""
+    rng = np.random.default_rng(seed)
+    if tiles is None:
+        tiles = rng.permutation(M * N)[:K].astype(np.int32)
+    A = (rng.standard_normal((M * d_out, rank), dtype=np.float32) / np.float32(np.sqrt(d_out)))
+    B = (rng.standard_normal((N * d_in, rank), dtype=np.float32) / np.float32(np.sqrt(d_in)))
+    sv = np.sort(np.exp(rng.uniform(np.log(0.1), np.log(10.0), rank)))[::-1].astype(np.float32)
+    W = np.empty((K, d_out, d_in), dtype)
+    for e, t in enumerate(tiles):
+        m, n = divmod(int(t), N)
+        blk = (A[m * d_out:(m + 1) * d_out] * sv) @ B[n * d_in:(n + 1) * d_in].T
+        blk += np.float32(noise) * rng.standard_normal((d_out, d_in), dtype=np.float32)
+        W[e] = blk.astype(dtype)
+    return W, np.asarray(tiles, np.int32)

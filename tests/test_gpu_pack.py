@@ -166,3 +166,39 @@ def test_pack_rejects_bad_arguments():
         with pytest.raises(tq.TileQError, match=text):
             tq.pack_proj(**args)
     del ctypes
+
+
+def test_pack_mixtral_gate_full_size():
+    """The packer at the Mixtral-shaped gate projection's size (8 experts on
+    2 x 4, d_out 14336, d_in 4096, rank 64, sketch 72, one power iteration,
+    fp16 weights): factors against the oracle in full, the quantization on
+    256 rows of every expert spread over the row range."""
+    import synth
+    K, M, N, d_out, d_in, r, l, G = 8, 2, 4, 14336, 4096, 64, 72, 128
+    W16, tiles = synth.make_dense_experts(K, M, N, d_out, d_in, r, seed=31)
+    omega = np.random.default_rng(32).standard_normal((N * d_in, l))
+    say("  device packer (Mixtral-shaped gate)")
+    dev = tqio.pack_proj(W16, tiles, M, N, r, G, 2, omega, act="f16", power_iters=1)
+    say("  oracle sketch")
+    W = W16.astype(np.float64)
+    big = P.assemble_wbig(W, tiles, M, N)
+    U, S, V = P.sketch_svd(big, omega, r, power_iters=1)
+    del big
+    Ur, Sr, Vr, S32 = P.stored_factors(U, S, V, "f16")
+    orc = dict(sigma=S32, U=P.to_storage(Ur, "f16"), V=P.to_storage(Vr, "f16"))
+    check_factors(dev, orc, "f16")
+    rows = np.linspace(0, d_out - 1, 256).astype(int)
+    Ud = act_values(dev["U"], "f16") * dev["sigma"].astype(np.float64)[None, :]
+    Vd = act_values(dev["V"], "f16")
+    for e in range(K):
+        m, n = divmod(int(tiles[e]), N)
+        res = W[e][rows] - Ud[m * d_out + rows] @ Vd[n * d_in:(n + 1) * d_in].T
+        q, s, z = P.quantize_rtn(res, G, 2)
+        assert np.array_equal(dev["scales"][e][rows].view(np.uint16), s.view(np.uint16)), e
+        assert np.array_equal(dev["zeros"][e][rows].view(np.uint16), z.view(np.uint16)), e
+        qd = R.unpack_codes(dev["codes"][e][rows], d_in, 2)
+        bad = qd != q
+        if bad.any():
+            t = res / np.repeat(s.astype(np.float64), G, axis=1) + np.repeat(z.astype(np.float64), G, axis=1)
+            gap = np.abs(t - np.floor(t) - 0.5)
+            assert np.all(gap[bad] < 1e-9), (e, int(bad.sum()))
