@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtileq.so")
+# TILEQ_LIB_PATH selects another build of the same library (the sanitizer build)
+LIB_PATH = os.environ.get("TILEQ_LIB_PATH") or os.path.join(HERE, "libtileq.so")
 
 TQ_F16, TQ_BF16, TQ_F32, TQ_F64 = 0, 1, 2, 3
 TQ_SINGLE, TQ_SWIGLU = 0, 1

@@ -1,6 +1,7 @@
 """Build libtileq.so (all HIP kernels + the C ABI host runtime) for gfx950.
 
     python -m bit_rank_post_amd.build        # or __graft_entry__.build()
+    python -m bit_rank_post_amd.build --asan # host-sanitized variant (CPU tests)
 
 Every source is compiled with hipcc for --offload-arch=gfx950 in parallel into
 _build/, then linked into bit_rank_post_amd/libtileq.so (in-tree, so it ships
@@ -73,5 +74,54 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libtileq_asan.so")
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (preloaded into the
+    uninstrumented Python that loads the sanitizer build)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang++"
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         stdout=subprocess.PIPE, check=True).stdout.decode().strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return out
+
+
+def build_asan() -> str:
+    """Host-sanitized variant of the library: the host runtime (argument
+    checks, planning, allocation, launch set-up) compiled with
+    AddressSanitizer and UndefinedBehaviorSanitizer, linked with the ordinary
+    kernel objects.  The sanitizers apply to host code only; it is meant for
+    CPU runs of the host-side tests (TILEQ_LIB_PATH=<this library>, the
+    runtime of asan_runtime() preloaded)."""
+    if not all(os.path.exists(os.path.join(BUILD, n + ".o")) for _, n, _ in SOURCES):
+        build()
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    cc = hipcc()
+    obj = os.path.join(ASAN_DIR, "tileq_host.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    cmd = [cc] + flags() + san + ["-x", "hip", "-c", os.path.join(CSRC, "tileq_host.cpp"), "-o", obj]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc (sanitized host) failed:\n" + r.stdout.decode(errors="replace"))
+    objs = [obj] + [os.path.join(BUILD, n + ".o") for _, n, _ in SOURCES if n != "tileq_host"]
+    tmp = ASAN_LIB + ".tmp"
+    r = subprocess.run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs,
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -42,7 +42,16 @@ extern "C" {
 
 typedef struct tq_layer tq_layer; /* opaque; owns the uploaded device weights */
 
-typedef enum {
+/* The enumerations are 32-bit integers on both sides of the boundary; any
+ * int32 value may be passed and out-of-range ones are rejected (C++ sees them
+ * with a fixed int32_t underlying type, so such a value is well defined). */
+#ifdef __cplusplus
+#define TQ_ENUM(tag) enum tag : int32_t
+#else
+#define TQ_ENUM(tag) enum tag
+#endif
+
+typedef TQ_ENUM(tq_status_e) {
   TQ_OK = 0,
   TQ_EINVAL = 1,        /* invalid argument value (map, pointer, dtype, ...) */
   TQ_ESHAPE = 2,        /* shapes inconsistent or unsupported sizes          */
@@ -52,13 +61,13 @@ typedef enum {
   TQ_ESTATE = 6         /* call order (e.g. forward before every upload)     */
 } tq_status;
 
-typedef enum { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2, TQ_F64 = 3 } tq_dtype;
+typedef TQ_ENUM(tq_dtype_e) { TQ_F16 = 0, TQ_BF16 = 1, TQ_F32 = 2, TQ_F64 = 3 } tq_dtype;
 
 /* TQ_SINGLE: one projection  y_t = sum_j g_tj W_e x_t.
  * TQ_SWIGLU: gate, up and down projections,
  *            h = RND_act(silu(W_gate,e x) * (W_up,e x)),
  *            y_t = sum_j g_tj W_down,e h_tj  (+ optional dense shared expert). */
-typedef enum { TQ_SINGLE = 0, TQ_SWIGLU = 1 } tq_kind;
+typedef TQ_ENUM(tq_kind_e) { TQ_SINGLE = 0, TQ_SWIGLU = 1 } tq_kind;
 
 /* projection selectors */
 #define TQ_P_SINGLE 0

@@ -120,3 +120,55 @@ def test_forward_variants_validate_on_host(L):
     assert L.tq_forward_path(h, 4, 2, ctypes.byref(ctypes.c_int32())) == 6
     assert L.tq_workspace_size(h, 4, 2, ctypes.byref(n)) == 6
     assert L.tq_layer_destroy(h) == 0
+
+
+def pack_desc(**kw):
+    base = dict(K=2, M=1, N=2, d_in=128, d_out=64, rank=4, group=32, bits=2, sketch=8,
+                power_iters=0, act=tq.TQ_F16, w_dtype=tq.TQ_F32)
+    tiles = kw.pop("tiles", [0, 1])
+    base.update(kw)
+    arr = (ctypes.c_int32 * len(tiles))(*tiles)
+    d = tq.PackDesc(base["K"], base["M"], base["N"], base["d_in"], base["d_out"], base["rank"],
+                    base["group"], base["bits"], base["sketch"], base["power_iters"], base["act"],
+                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), FAKE, base["w_dtype"],
+                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    d._keep = arr
+    return d
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(sketch=3), 2, b"sketch"),                       # fewer columns than the rank
+    (dict(sketch=137), 2, b"sketch"),
+    (dict(tiles=[1, 1]), 1, b"share tile"),
+    (dict(tiles=[0, 2]), 1, b"out of range"),
+    (dict(bits=4), 5, b"bits = 4"),
+    (dict(bits=3, group=96, d_in=384), 5, b"power-of-two"),
+    (dict(w_dtype=7), 1, b"w_dtype"),
+    (dict(act=tq.TQ_F32), 1, b"act"),
+    (dict(rank=129, sketch=136), 2, b"rank"),
+    (dict(power_iters=17), 2, b"power_iters"),
+    (dict(d_in=96), 2, b"d_in"),
+    (dict(K=3), 2, b"grid"),
+])
+def test_pack_validation(L, kw, code, text):
+    n = ctypes.c_size_t()
+    d = pack_desc(**kw)
+    assert L.tq_pack_workspace_size(ctypes.byref(d), ctypes.byref(n)) == code, L.tq_last_error()
+    assert text in L.tq_last_error(), L.tq_last_error()
+    assert L.tq_pack_proj(ctypes.byref(d), FAKE, 1 << 30, None) == code
+
+
+def test_pack_workspace_grows_with_sketch(L):
+    n8, n64 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.tq_pack_workspace_size(ctypes.byref(pack_desc()), ctypes.byref(n8)) == 0
+    assert L.tq_pack_workspace_size(ctypes.byref(pack_desc(sketch=64)), ctypes.byref(n64)) == 0
+    assert 0 < n8.value < n64.value
+    # a workspace smaller than the size asked for is refused before device work
+    assert L.tq_pack_proj(ctypes.byref(pack_desc()), FAKE, n8.value - 1, None) == 2
+
+
+@pytest.mark.parametrize("T,K,k,code", [(-1, 8, 2, 2), (4, 0, 1, 2), (4, 257, 2, 2),
+                                        (4, 8, 0, 2), (4, 8, 9, 2), (4, 64, 33, 2),
+                                        (0, 8, 2, 0)])
+def test_router_validation(L, T, K, k, code):
+    assert L.tq_router_topk(FAKE, T, K, k, FAKE, FAKE, None) == code, L.tq_last_error()
