@@ -423,10 +423,11 @@ void gemm_dec_kernel(DecArgs a) {
 #pragma unroll
         for (int u = 0; u < NSLOT; ++u) {
           const int tau = t + u;
-          // first round: at most u * NI loads were issued after batch u's
-          // last one whichever way the prologue went; later rounds: the
-          // DEPTH - 1 newer batches
-          if (t == 0 && u < DEPTH - 1) wait_vm_first<SL::NI, DEPTH - 1>(u);
+          // first round: the prologue issued batches 0 .. DEPTH-1 whole, or
+          // (first tile, weights requested early) every batch's code and
+          // scale/zero loads first and then its NACT + 1 activation and
+          // group-sum loads; later rounds: the DEPTH - 1 newer batches
+          if (t == 0 && u < DEPTH - 1) wait_vm_first<SL::NI, SL::NACT + 1, DEPTH>(u);
           else wait_vm<SL::NI * (DEPTH - 1)>();
           wait_lgkm0();          // this wave's reads of the slot refilled below are done
           bar_nofence();

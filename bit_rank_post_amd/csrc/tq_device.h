@@ -102,13 +102,17 @@ __device__ __forceinline__ void wait_vm() {
 // wait until every LDS / scalar-memory operation of this wave has completed
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// wait_vm<u * NI>() for u in [0, UMAX); u must fold to a constant (an
-// unrolled loop index)
-template <int NI, int UMAX, int U = 0>
+// First round of a load ring whose prologue issued batches 0 .. D-1 either
+// whole (NI loads each) or as all their early loads first and then the other
+// NX loads of each: after batch u's last load at least (D - 1 - u) NX + u NI
+// loads were issued either way (u NI by the ring's own stages), so
+// wait_vm<(D - 1 - u) NX + u NI>() leaves batch u landed.  u in [0, D - 1)
+// must fold to a constant (an unrolled loop index).
+template <int NI, int NX, int D, int U = 0>
 __device__ __forceinline__ void wait_vm_first(int u) {
-  if constexpr (U < UMAX) {
-    if (u == U) wait_vm<U * NI>();
-    else wait_vm_first<NI, UMAX, U + 1>(u);
+  if constexpr (U < D - 1) {
+    if (u == U) wait_vm<(D - 1 - U) * NX + U * NI>();
+    else wait_vm_first<NI, NX, D, U + 1>(u);
   }
 }
 
