@@ -431,7 +431,11 @@ void gemm_dec_kernel(DecArgs a) {
           else wait_vm<SL::NI * (DEPTH - 1)>();
           wait_lgkm0();          // this wave's reads of the slot refilled below are done
           bar_nofence();
+          // the next batch's loads go out at raised wave priority, ahead of
+          // the other workgroup's arithmetic on the same SIMDs
+          __builtin_amdgcn_s_setprio(3);
           issue(tau + DEPTH, slot[(u + DEPTH) % NSLOT]);
+          __builtin_amdgcn_s_setprio(0);
           if (tau < ntau && rvalid) compute(slot[u]);
         }
       }

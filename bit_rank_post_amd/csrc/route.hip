@@ -101,8 +101,10 @@ __global__ __launch_bounds__(RM_NT) void route_count_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
+  // chunk counts expert-major ([K][W]): the scan reads each expert's run
+  // of chunk counts with consecutive lanes on consecutive chunks
   if (w < W)
-    for (int i = lane; i < K; i += 64) a.cntw[(size_t)w * K + i] = s_cnt[wave][i];
+    for (int i = lane; i < K; i += 64) a.cntw[(size_t)i * W + w] = s_cnt[wave][i];
   if (tid < a.ncol * 32) {
     const int c = tid >> 5, n = tid & 31;
     a.wgcnt[(c * nb + b) * 32 + n] = s_col[c][n];
@@ -123,63 +125,48 @@ __global__ __launch_bounds__(RM_NT) void route_scan_kernel(RouteArgs a, int nb) 
     d = wave_sum_i(d);
     if (lane == 0) a.flags[0] = d;
   }
-  // (B) per expert, exclusive prefix of the chunk counts over chunks: a wave
-  //     per expert, lanes own contiguous chunk ranges.  A wave takes its
-  //     experts EB at a time with every load of the batch in flight at once
-  //     and the values kept for the second pass (up to 8 chunks per lane).
+  // (B) per expert, exclusive prefix of the chunk counts over chunks (table
+  //     [K][W], chunk-minor): a wave per expert, lane l owning chunks
+  //     64 u + l, so every load and store is coalesced; the prefix is a wave
+  //     scan per group of 64 chunks plus the running total of the groups.  A
+  //     wave takes its experts EB at a time with every load of the batch in
+  //     flight at once (up to CH groups, W <= 64 CH; longer tables loop).
   constexpr int EB = 4, CH = 8;
-  const int seglen = (W + 63) >> 6;
-  if (seglen <= CH) {
+  const int ngrp = (W + 63) >> 6;
+  if (ngrp <= CH) {
     for (int e0 = wave * EB; e0 < K; e0 += NW * EB) {
       int v[EB][CH];
 #pragma unroll
       for (int q = 0; q < EB; ++q)
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
-          const int w = lane * seglen + u;
-          v[q][u] = (e0 + q < K && u < seglen && w < W) ? a.cntw[(size_t)w * K + e0 + q] : 0;
+          const int w = 64 * u + lane;
+          v[q][u] = (e0 + q < K && w < W) ? a.cntw[(size_t)(e0 + q) * W + w] : 0;
         }
 #pragma unroll
       for (int q = 0; q < EB; ++q) {
-        int sum = 0;
-#pragma unroll
-        for (int u = 0; u < CH; ++u) sum += v[q][u];
-        const int inc = wave_incl_scan_i(sum, lane);
-        int run = inc - sum;
+        int run = 0;
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
-          const int w = lane * seglen + u;
-          if (e0 + q < K && u < seglen && w < W) a.cntw[(size_t)w * K + e0 + q] = run;
-          run += v[q][u];
+          const int w = 64 * u + lane;
+          const int inc = wave_incl_scan_i(v[q][u], lane);
+          if (e0 + q < K && w < W) a.cntw[(size_t)(e0 + q) * W + w] = run + inc - v[q][u];
+          run += __shfl(inc, 63, 64);
         }
-        if (lane == 63 && e0 + q < K) s_tot[e0 + q] = inc;
+        if (lane == 0 && e0 + q < K) s_tot[e0 + q] = run;
       }
     }
   } else {
     for (int e = wave; e < K; e += NW) {
-      const int w0 = lane * seglen, w1 = min(W, w0 + seglen);
-      int sum = 0;
-      for (int wb = w0; wb < w1; wb += 8) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (wb + u < w1) ? a.cntw[(size_t)(wb + u) * K + e] : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) sum += v[u];
+      int run = 0;
+      for (int w0 = 0; w0 < W; w0 += 64) {
+        const int w = w0 + lane;
+        const int v = (w < W) ? a.cntw[(size_t)e * W + w] : 0;
+        const int inc = wave_incl_scan_i(v, lane);
+        if (w < W) a.cntw[(size_t)e * W + w] = run + inc - v;
+        run += __shfl(inc, 63, 64);
       }
-      const int inc = wave_incl_scan_i(sum, lane);
-      int run = inc - sum;
-      for (int wb = w0; wb < w1; wb += 8) {
-        int v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (wb + u < w1) ? a.cntw[(size_t)(wb + u) * K + e] : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (wb + u < w1) {
-            a.cntw[(size_t)(wb + u) * K + e] = run;
-            run += v[u];
-          }
-      }
-      if (lane == 63) s_tot[e] = inc;
+      if (lane == 0) s_tot[e] = run;
     }
   }
   // per (projection, grid column): exclusive prefix of the workgroup counts,
@@ -253,7 +240,7 @@ __global__ __launch_bounds__(RM_NT) void route_place_kernel(RouteArgs a) {
     const int e = a.ids[s];
     if (e >= 0 && e < K) {
       const int o = a.off[e];
-      const int c = a.cntw[(size_t)(s >> 6) * K + e] + a.rank[s];
+      const int c = a.cntw[(size_t)e * ((S + 63) >> 6) + (s >> 6)] + a.rank[s];
       const int p = o + c;
       a.perm[p] = s;
       a.inv[s] = p;

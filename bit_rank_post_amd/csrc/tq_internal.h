@@ -73,7 +73,7 @@ struct RouteArgs {
   int* col_tok[2];               // [S]
   int* slot2col[2];              // [S]
   int* tile_col[2];              // [N+1] prefix of ceil(col count/rt_col)
-  int* cntw;                     // scratch [ceil(S/64)][K]
+  int* cntw;                     // scratch chunk counts: [ceil(S/64)][K] (one-workgroup routing), [K][ceil(S/64)] (multi-workgroup)
   int* rank;                     // scratch [S]
   int* colmask;                  // scratch [2][T]
   int* wgcnt;                    // scratch [2][ceil(S/1024)][32] (multi-workgroup path)
