@@ -6,7 +6,11 @@
 //
 // Work: a workgroup of WAVES waves, rows_per of which own a row fragment (16
 // rows each) of one expert -- in MODE_GATEUP the gate and the up rows
-// together -- walks a range of k-stages (8 MFMA k-steps = 256 inputs each).  Everything a stage
+// together -- walks a range of k-stages (8 MFMA k-steps = 256 inputs each)
+// for a column tile of 16 of the expert's slots.  With NCT = 2 (many slots
+// per expert) the waves form two groups that take two column tiles at once,
+// reading each stage's codes from LDS once loaded: the codes are streamed
+// once for 32 slots.  Everything a stage
 // needs (each wave's codes, the stage's activations shared by all waves, the
 // scale/zero words and the activation group sums) is brought straight into
 // LDS by buffer loads with the LDS destination (no registers in between), in
@@ -35,26 +39,34 @@
 namespace tq {
 
 // LDS slot layout (bytes) for NP projections, WAVES waves, NG groups/stage,
-// BITS-bit codes
-template <int NP, int WAVES, int NG, int BITS>
+// BITS-bit codes and NCT column tiles of 16 slots: the waves form NCT groups
+// of WR = WAVES / NCT (group c computes column tile c); wave slot w of every
+// group owns row fragment w, whose codes all groups read, each wave loading
+// those of NPL projections
+template <int NP, int WAVES, int NG, int BITS, int NCT = 1>
 struct DecSlot {
+  static constexpr int WR = WAVES / NCT;
+  static constexpr int NPL = (NP + NCT - 1) / NCT;
   // codes of a wave and projection per stage: 2-bit 64 lanes x 16 B; 3-bit
   // 64 lanes x 16 B (dwords 0..3) then dwords 4 and 5 of the 64 lanes
   static constexpr int CB = (BITS == 3) ? 1536 : 1024;
   static constexpr int NCL = (BITS == 3) ? 3 : 1;    // code loads per projection
   // scale/zero words of a stage: per projection a [WAVES][NG][16 rows] table,
   // brought in by 64-word loads that the waves share out
-  static constexpr int NSZP = (WAVES * NG + 3) / 4;  // 64-word loads per projection
+  static constexpr int NSZP = (WR * NG + 3) / 4;     // 64-word loads per projection
   static constexpr int NSZW = (NP * NSZP + WAVES - 1) / WAVES;   // ... per wave
-  static constexpr int NSUM = NG >= 2 ? NG / 2 : 1;  // dword loads of the group sums
-  static constexpr int NACT = (8 + WAVES - 1) / WAVES;   // activation loads per wave
-  static constexpr int CODE = 0;                     // [WAVES][NP] x CB
-  static constexpr int ACT = CODE + WAVES * NP * CB;     // [8 k-steps][64 lanes] x 16 B
-  static constexpr int SZ = ACT + 8 * 1024;          // [NP][NSZP * 64] x 4 B
-  static constexpr int SUM = SZ + NP * NSZP * 256;   // [NG][16 cols] float2
-  static constexpr int BYTES = SUM + NSUM * 256;
+  static constexpr int NSUM = NG >= 2 ? NG / 2 : 1;  // dword loads of the group sums per tile
+  static constexpr int NACT = (8 * NCT + WAVES - 1) / WAVES;   // activation loads per wave
+  static constexpr int CODE = 0;                     // [WR][NP] x CB
+  static constexpr int ACT = CODE + WR * NP * CB;    // [NCT][8 k-steps][64 lanes] x 16 B
+  static constexpr int SZ = ACT + NCT * 8 * 1024;    // [NP][NSZP * 64] x 4 B
+  static constexpr int SUM = SZ + NP * NSZP * 256;   // [NCT][NG][16 cols] float2
+  static constexpr int BYTES = SUM + NCT * NSUM * 256;
   // loads per wave per stage (the same for every wave)
-  static constexpr int NI = NP * NCL + NACT + NSZW + 1;
+  static constexpr int NI = NPL * NCL + NACT + NSZW + 1;
+  // two tiles: wave w loads k-steps w NACT .. w NACT + NACT - 1 of the
+  // activations, all of its own tile
+  static_assert(NCT == 1 || NACT * WR == 8, "activation loads of a tile group");
 };
 
 // Two workgroups share a CU when an 8-wave workgroup's ring of three slots
@@ -73,9 +85,9 @@ constexpr int ring_depth() {
   return (budget / BYTES - 1 < DMAX) ? budget / BYTES - 1 : DMAX;
 }
 
-template <int MODE, int GS, int WAVES, int BITS>
+template <int MODE, int GS, int WAVES, int BITS, int NCT = 1>
 constexpr bool dec_dual_cfg() {
-  return dec_dual<DecSlot<(MODE == MODE_GATEUP) ? 2 : 1, WAVES, 8 / GS, BITS>::BYTES, WAVES>();
+  return dec_dual<DecSlot<(MODE == MODE_GATEUP) ? 2 : 1, WAVES, 8 / GS, BITS, NCT>::BYTES, WAVES>();
 }
 
 // Raw A operand (1 + q c per fp16 half) of k-step J of a stage from the
@@ -96,13 +108,14 @@ __device__ __forceinline__ u32x4 dec_raw(int J, const u32x4& c, uint32_t c4, uin
   }
 }
 
-template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS>
-__global__ __launch_bounds__(64 * WAVES, (dec_dual_cfg<MODE, GS, WAVES, BITS>() ? 4 : 1))
+template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS, int NCT>
+__global__ __launch_bounds__(64 * WAVES, (dec_dual_cfg<MODE, GS, WAVES, BITS, NCT>() ? 4 : 1))
 void gemm_dec_kernel(DecArgs a) {
   typedef typename Vec8<T>::type V8;
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
   constexpr int NG = 8 / GS;             // groups per stage
-  typedef DecSlot<NP, WAVES, NG, BITS> SL;
+  typedef DecSlot<NP, WAVES, NG, BITS, NCT> SL;
+  constexpr int WR = SL::WR;
   constexpr bool DUAL = dec_dual<SL::BYTES, WAVES>();
   constexpr int DEPTH = ring_depth<SL::BYTES, DMAX, DUAL>();
   constexpr int NSLOT = DEPTH + 1;
@@ -121,7 +134,7 @@ void gemm_dec_kernel(DecArgs a) {
   __shared__ __attribute__((aligned(16))) char s7[NSLOT > 7 ? SL::BYTES : 16];
   // target of unused loads (activation loads past the 8th k-step are 16 B
   // per lane, the others 4 B)
-  __shared__ __attribute__((aligned(16))) char s_dummy[WAVES * SL::NACT > 8 ? 1024 : 256];
+  __shared__ __attribute__((aligned(16))) char s_dummy[(WAVES * SL::NACT > 8 * NCT || NCT > 1) ? 1024 : 256];
   char* const slot[8] = {s0, s1, s2, s3, s4, s5, s6, s7};
 
   // Workgroup -> (expert, row-fragment group, k-chunk).  Consecutive
@@ -163,8 +176,10 @@ void gemm_dec_kernel(DecArgs a) {
     if (by >= nby) return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int rb_raw = by * rpw + wave;
-  const bool rvalid = wave < rpw && rb_raw < nrb;
+  // row-fragment slot and column tile of this wave
+  const int wr = (NCT == 1) ? wave : wave % WR, wc = (NCT == 1) ? 0 : wave / WR;
+  const int rb_raw = by * rpw + wr;
+  const bool rvalid = wr < rpw && rb_raw < nrb;
   const int rb = rvalid ? rb_raw : nrb - 1;          // clamped: loads stay in bounds
   const int nsteps = a.d_in >> 5;
   const int nfull = nsteps >> 3;
@@ -220,12 +235,17 @@ void gemm_dec_kernel(DecArgs a) {
     tr = (tr >= ntau) ? tr - ntau : tr;
     const int st = live ? k0 + tr : 0;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      char* cb = base + SL::CODE + (wave * NP + p) * SL::CB;
-      dma16(rc[p], cb, (live && rvalid) ? lane * 16u : OOB, st * (uint32_t)SL::CB);
+    for (int i = 0; i < SL::NPL; ++i) {
+      // projection p of this wave's row fragment (none: a load of nothing)
+      const int p = wc * SL::NPL + i;
+      const bool has = p < NP;
+      const int pc = has ? p : 0;
+      char* cb = has ? base + SL::CODE + (wr * NP + pc) * SL::CB : s_dummy;
+      const bool ld = live && rvalid && has;
+      dma16(rc[pc], cb, ld ? lane * 16u : OOB, st * (uint32_t)SL::CB);
       if constexpr (BITS == 3) {
-        dma4(rc[p], cb + 1024, (live && rvalid) ? 1024u + lane * 4u : OOB, st * (uint32_t)SL::CB);
-        dma4(rc[p], cb + 1280, (live && rvalid) ? 1280u + lane * 4u : OOB, st * (uint32_t)SL::CB);
+        dma4(rc[pc], has ? cb + 1024 : s_dummy, ld ? 1024u + lane * 4u : OOB, st * (uint32_t)SL::CB);
+        dma4(rc[pc], has ? cb + 1280 : s_dummy, ld ? 1280u + lane * 4u : OOB, st * (uint32_t)SL::CB);
       }
     }
 #pragma unroll
@@ -242,11 +262,14 @@ void gemm_dec_kernel(DecArgs a) {
     const int st = live ? k0 + tr : 0;
 #pragma unroll
     for (int i = 0; i < SL::NACT; ++i) {
-      const int j = wave * SL::NACT + i;      // k-step; loads past the 8th step load nothing
-      dma16(rx, j < 8 ? base + SL::ACT + j * 1024 : s_dummy,
-            (live && j < 8 && act_vo != OOB) ? act_vo + j * 64u : OOB, st * 512u);
+      // k-step j of tile j / 8 (the wave's own tile); loads past the last
+      // step load nothing
+      const int j = wave * SL::NACT + i;
+      dma16(rx, j < 8 * NCT ? base + SL::ACT + j * 1024 : s_dummy,
+            (live && j < 8 * NCT && act_vo != OOB) ? act_vo + (j & 7) * 64u : OOB, st * 512u);
     }
-    dma4(rsm, wave < SL::NSUM ? base + SL::SUM + wave * 256 : s_dummy,
+    // group sums of the wave's tile: the first NSUM waves of each group
+    dma4(rsm, wr < SL::NSUM ? base + SL::SUM + (wc * SL::NSUM + wr) * 256 : s_dummy,
          live ? sum_vo : OOB, st * NG * 8u);
   };
 
@@ -286,13 +309,19 @@ void gemm_dec_kernel(DecArgs a) {
   // loop header, the compiler's waits would count loads of an earlier tile
   // and stall on the code loads in flight.
   auto tile = [&](const int t0) __attribute__((always_inline)) {
-    const int ncol = min(16, cnt - t0);
+    // this wave's column tile starts at position tt0; an empty one (second
+    // tile past the count) reads the group's first tile instead and computes
+    // nothing
+    const int tt0 = t0 + 16 * wc;
+    const int ncol = max(0, min(16, cnt - tt0));
+    const bool tlive = ncol > 0;
+    const int ts = tlive ? tt0 : t0;
     const bool cvalid = l16 < ncol;
-    const int pos = offe + t0 + (cvalid ? l16 : 0);
+    const int pos = offe + ts + (cvalid ? l16 : 0);
     // (no cross-lane reads here: an LDS-pipe instruction would make the
     // compiler wait for the code loads above to land)
-    const int* slp = (rec && t0 == 0) ? rec + 4 : etab + t0;   // slot ids from position t0
-    int slotid = (t0 == 0) ? sl_first : sload16(slp, 0, l16);
+    const int* slp = (rec && ts == 0) ? rec + 4 : etab + ts;   // slot ids from position ts
+    int slotid = (ts == 0) ? sl_first : sload16(slp, 0, l16);
     slotid = cvalid ? slotid : sload(slp, 0);            // column 0 always holds a slot
     const int arow = a.gather ? slotid / a.topk : pos;
     const int E = a.ex[arow];              // row exponent, used by the epilogue
@@ -301,13 +330,14 @@ void gemm_dec_kernel(DecArgs a) {
     // their MFMA columns are never stored, and columns do not mix)
     // activations: lane = (lg, col) of k-step j; the k-step adds 64 bytes
     act_vo = cvalid ? ((uint32_t)arow * a.d_in + 8 * lg) * 2u : OOB;
-    // group sums: word w = 64 * wave + lane of the stage's [NG][16][2] table
+    // group sums: word w = 64 * wr + lane of the stage's [NG][16][2] table
+    // of the wave's tile
     sum_vo = OOB;
     {
-      const int w = 64 * wave + lane;
+      const int w = 64 * wr + lane;
       const int gi = w >> 5, col = (w >> 1) & 15, comp = w & 1;
-      const int r = a.gather ? sload16(slp, 0, col) / a.topk : offe + t0 + col;
-      if (wave < SL::NSUM && gi < NG && col < ncol) sum_vo = (((uint32_t)r * ng + gi) * 2u + comp) * 4u;
+      const int r = a.gather ? sload16(slp, 0, col) / a.topk : offe + ts + col;
+      if (wr < SL::NSUM && gi < NG && col < ncol) sum_vo = (((uint32_t)r * ng + gi) * 2u + comp) * 4u;
     }
     auto issue = [&](int b, char* base) {
       issue_w(b, base);
@@ -337,7 +367,7 @@ void gemm_dec_kernel(DecArgs a) {
       uint32_t cw[NP][NCORR];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const char* cb = base + SL::CODE + (wave * NP + p) * SL::CB;
+        const char* cb = base + SL::CODE + (wr * NP + p) * SL::CB;
         code[p] = *reinterpret_cast<const u32x4*>(cb + lane * 16);
         code4[p] = code5[p] = 0u;
         if constexpr (BITS == 3) {
@@ -347,24 +377,25 @@ void gemm_dec_kernel(DecArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        bv[j] = *reinterpret_cast<const half8v*>(base + SL::ACT + lane * 16 + j * 1024);
+        bv[j] = *reinterpret_cast<const half8v*>(base + SL::ACT + lane * 16 + (wc * 8 + j) * 1024);
 #pragma unroll
       for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
           szw[p][gi] = *reinterpret_cast<const u32x4*>(
-              base + SL::SZ + (p * SL::NSZP * 64 + (wave * NG + gi) * 16 + 4 * lg) * 4);
+              base + SL::SZ + (p * SL::NSZP * 64 + (wr * NG + gi) * 16 + 4 * lg) * 4);
 #pragma unroll
       for (int m = 0; m < NCORR; ++m) {
         const int t = 4 * m + lg;
         const int g = (t < NG) ? t : t - NG;
         cbx[m] = 0.f;
         if (t < 2 * NG)
-          cbx[m] = *reinterpret_cast<const float*>(base + SL::SUM + ((g * 16 + l16) * 2 + (t < NG)) * 4);
+          cbx[m] = *reinterpret_cast<const float*>(base + SL::SUM + wc * SL::NSUM * 256 +
+                                                   ((g * 16 + l16) * 2 + (t < NG)) * 4);
 #pragma unroll
         for (int p = 0; p < NP; ++p)
           cw[p][m] = (t < 2 * NG) ? *reinterpret_cast<const uint32_t*>(
-                                        base + SL::SZ + (p * SL::NSZP * 64 + (wave * NG + g) * 16 + l16) * 4)
+                                        base + SL::SZ + (p * SL::NSZP * 64 + (wr * NG + g) * 16 + l16) * 4)
                                   : 0u;
       }
 
@@ -436,7 +467,7 @@ void gemm_dec_kernel(DecArgs a) {
           __builtin_amdgcn_s_setprio(3);
           issue(tau + DEPTH, slot[(u + DEPTH) % NSLOT]);
           __builtin_amdgcn_s_setprio(0);
-          if (tau < ntau && rvalid) compute(slot[u]);
+          if (tau < ntau && rvalid && tlive) compute(slot[u]);
         }
       }
       // every load has landed and every wave is done with the ring before
@@ -447,7 +478,8 @@ void gemm_dec_kernel(DecArgs a) {
     }
 
     // 4-step tail stage (d_in % 256 == 128; then GS <= 4): direct loads
-    if (tail && rvalid) {
+    // (two column tiles are only launched without it)
+    if (NCT == 1 && tail && rvalid) {
       // addresses from opaque copies: computed here, not held across the ring
       const int st = nfull;
       const int lane_t = opaque(lane), lg_t = lane_t >> 4, arow_t = opaque(arow);
@@ -508,24 +540,24 @@ void gemm_dec_kernel(DecArgs a) {
     // halves of the activation type: the gate/up projections of MODE_GATEUP,
     // and in MODE_RES the projection when P is given, done by the workgroups
     // of the first k-chunk.  P row of a column: its (tile column, token) pair
-    // when ap_T > 0, else the slot's position.  The workgroup's columns
-    // are the same for every wave, so Sigma p is gathered once per workgroup:
+    // when ap_T > 0, else the slot's position.  The columns are the same for
+    // every wave of a tile group, so Sigma p is gathered once per group:
     // every thread loads whole float4 runs of all split-K slabs at once
     // (slabs past the count read zeros), adds them in slab order and writes
-    // hi/lo into slot 0 of the (drained) ring.  The U fragments of each wave
+    // hi/lo into slot c of the (drained) ring for tile c.  The U fragments of each wave
     // go out right after, in the same round trip.  Every address here
     // derives from an opaque copy of the thread id, so none of it is computed
     // ahead and held in registers across the ring.
     constexpr int RC = 4;                  // rank chunks of 32 (r_pad <= 128)
-    constexpr int NTH = 64 * WAVES;
+    constexpr int NTH = 64 * WR;           // threads of a tile group
     constexpr int IMAX = (16 * 32 + NTH - 1) / NTH;   // float4 runs per thread
-    constexpr int SPMAX = (NP == 2) ? 4 : 16;          // slabs loaded together
+    constexpr int SPMAX = (NP == 2) ? (IMAX > 1 ? 2 : 4) : (IMAX > 1 ? 4 : 16);   // slabs loaded together
     V8 uf[NP][RC];
     const bool rowstage = (MODE == MODE_GATEUP) || (ks == 0 && a.P[0] != nullptr && a.p[0].rank > 0);
     if (rowstage) {
-      const int tid_e = opaque(tid);
+      const int tid_e = opaque(tid) % NTH;  // thread of the tile group
       const int l16e = tid_e & 15, lge = (tid_e >> 4) & 3;
-      T* sh = reinterpret_cast<T*>(s0);    // [NP][hi, lo][16 columns][r_pad + 8]
+      T* sh = reinterpret_cast<T*>(wc == 0 ? s0 : s1);   // [NP][hi, lo][16 columns][r_pad + 8]
       const int tok = slotid / a.topk;
       const int ns = a.p_nsplit;
       f32x4 ld[NP][IMAX][SPMAX];
@@ -597,8 +629,8 @@ void gemm_dec_kernel(DecArgs a) {
         for (int v = 0; v < 4; ++v) acc[p][v] = ldexpf(acc[p][v] - corr[p][v], E);
       const int o = rb * 16 + 4 * lg;
       if (rowstage) {
-        const T* sh = reinterpret_cast<const T*>(s0);
-        const int tid_e = opaque(tid);
+        const T* sh = reinterpret_cast<const T*>(wc == 0 ? s0 : s1);
+        const int tid_e = opaque(tid) % NTH;
         const int l16e = tid_e & 15, lge = (tid_e >> 4) & 3;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -632,43 +664,55 @@ void gemm_dec_kernel(DecArgs a) {
         }
       }
     }
-    // slot 0 holds the gathered Sigma p until every wave has used it
-    if (rowstage && t0 + 16 < cnt) __syncthreads();
+    // slots 0 .. NCT-1 hold the gathered Sigma p until every wave has used it
+    if (rowstage && t0 + 16 * NCT < cnt) __syncthreads();
   };
   tile(0);
-  for (int t0 = 16; t0 < cnt; t0 += 16) tile(t0);
+  for (int t0 = 16 * NCT; t0 < cnt; t0 += 16 * NCT) tile(t0);
 }
 
-template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS>
+template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS, int NCT = 1>
 static void dec_launch(const DecArgs& a, hipStream_t s) {
   constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
-  constexpr int BYTES = DecSlot<NP, WAVES, 8 / GS, BITS>::BYTES;
+  constexpr int BYTES = DecSlot<NP, WAVES, 8 / GS, BITS, NCT>::BYTES;
   if constexpr (WAVES > 8 && ring_depth<BYTES, DMAX, false>() < 2) {
-    // slots too large for a ring of three: fall back to 8 waves
-    dec_launch<T, MODE, GS, 8, DMAX, BITS>(a, s);
-  } else {
+    // slots too large for a ring of three: fall back to 8 waves, one tile
     DecArgs b = a;
-    b.rows_per = (a.rows_per >= 1 && a.rows_per <= WAVES) ? a.rows_per : WAVES;
+    b.nct = 1;
+    dec_launch<T, MODE, GS, 8, DMAX, BITS>(b, s);
+  } else {
+    constexpr int WR = WAVES / NCT;
+    DecArgs b = a;
+    b.rows_per = (a.rows_per >= 1 && a.rows_per <= WR) ? a.rows_per : WR;
     const int nrb = b.d_out >> 4;
     const int nby = (nrb + b.rows_per - 1) / b.rows_per;
     const dim3 grid(b.K * ((nby + 7) / 8) * 8 * b.nks);
-    hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, GS, WAVES, DMAX, BITS>), grid, dim3(64 * WAVES), 0,
-                       s, b);
+    hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, GS, WAVES, DMAX, BITS, NCT>), grid, dim3(64 * WAVES),
+                       0, s, b);
   }
 }
 
-template <typename T, int MODE, int WAVES, int DMAX, int BITS>
+template <typename T, int MODE, int WAVES, int DMAX, int BITS, int NCT = 1>
 static void dec_gs(const DecArgs& a, hipStream_t s) {
   switch (a.p[0].group >> 5) {
-    case 1: dec_launch<T, MODE, 1, WAVES, DMAX, BITS>(a, s); break;
-    case 2: dec_launch<T, MODE, 2, WAVES, DMAX, BITS>(a, s); break;
-    case 4: dec_launch<T, MODE, 4, WAVES, DMAX, BITS>(a, s); break;
-    default: dec_launch<T, MODE, 8, WAVES, DMAX, BITS>(a, s); break;
+    case 1: dec_launch<T, MODE, 1, WAVES, DMAX, BITS, NCT>(a, s); break;
+    case 2: dec_launch<T, MODE, 2, WAVES, DMAX, BITS, NCT>(a, s); break;
+    case 4: dec_launch<T, MODE, 4, WAVES, DMAX, BITS, NCT>(a, s); break;
+    default: dec_launch<T, MODE, 8, WAVES, DMAX, BITS, NCT>(a, s); break;
   }
 }
 
 template <typename T, int MODE, int BITS>
 static void dec_waves(const DecArgs& a, hipStream_t s) {
+  if constexpr (MODE == MODE_GATEUP && BITS == 2) {
+    if (a.nct == 2 && decode_two_tiles_ok(2, a.p[0].group, a.p[0].bits, a.d_in)) {
+      // two column tiles of 16 slots: two groups of waves share each
+      // stage's codes (two 8-wave workgroups per CU, groups of 4 waves)
+      if ((a.p[0].group >> 5) == 4) dec_launch<T, MODE, 4, 8, 6, BITS, 2>(a, s);
+      else dec_launch<T, MODE, 8, 8, 6, BITS, 2>(a, s);
+      return;
+    }
+  }
   if constexpr (MODE == MODE_GATEUP) {
     switch (a.waves) {
       case 16: dec_gs<T, MODE, 16, 6, BITS>(a, s); break;
@@ -694,6 +738,14 @@ static bool dual_gs(int group) {
     case 4: return dec_dual_cfg<MODE, 4, 8, BITS>();
     default: return dec_dual_cfg<MODE, 8, 8, BITS>();
   }
+}
+
+// Two column tiles per workgroup (two groups of 4 or 8 waves) for gate/up
+// with 2-bit codes, groups of 128 or 256 inputs (the instances that keep to
+// the register budget) and no 4-step tail stage.  (The down projection's
+// split-K launch measured slower with two tiles.)
+bool decode_two_tiles_ok(int np, int group, int bits, int d_in) {
+  return np == 2 && bits == 2 && (group == 128 || group == 256) && d_in % 256 == 0;
 }
 
 bool decode_dual(int np, int group, int bits) {

@@ -926,6 +926,27 @@ tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_
       da.p_nsplit = p.nsplit[0];
       da.p_rows_cap = p.rows_cap;
       choose_waves(L, 0, p.S, 1, 2, &da.waves, &da.rows_per);
+      // at 16 or more slots per active expert on average, most experts
+      // fill a second 16-slot column tile: take both tiles in one pass over
+      // the codes (two groups of 8 waves)
+      const ProjDev& g0 = L->proj[0].dev;
+      if (p.S >= 16L * std::min(K, p.S) && g0.group == L->proj[1].dev.group &&
+          decode_two_tiles_ok(2, g0.group, g0.bits, g0.d_in)) {
+        // two 8-wave workgroups per CU, each two groups of 4 waves; row
+        // fragments per group by whole rounds, cost as in choose_waves
+        da.nct = 2;
+        da.waves = 8;
+        const long active = std::min(K, p.S), cus = device_cus();
+        long best = -1;
+        for (int r = 4; r >= 3; --r) {
+          const long wgs = active * ((g0.nrb + r - 1) / r);
+          const long cost = ((wgs + 2 * cus - 1) / (2 * cus)) * (r * 2 * g0.bits + 16);
+          if (best < 0 || cost < best) {
+            best = cost;
+            da.rows_per = r;
+          }
+        }
+      }
       launch_gemm_decode(da, MODE_GATEUP, act, s);
     } else {
       da.dres = dres;

@@ -181,7 +181,9 @@ struct DecArgs {
   int nks;                       // k-chunks (RES; 1 for GATEUP)
   int S;                         // slots (slab stride of dres)
   int waves;                     // waves per workgroup: 8, 12, 14 or 16 (GATEUP), 8 or 16
-  int rows_per;                  // waves that own a 16-row fragment (<= waves)
+  int rows_per;                  // waves that own a 16-row fragment (<= waves / nct)
+  int nct;                       // column tiles of 16 slots per pass: 1, or 2 (16 waves in two
+                                 // groups of 8 sharing each stage's codes; no 4-step tail)
   int ap_T;                      // GATEUP: P rows are (column, token) pairs n * ap_T + t
   int p_nsplit, p_rows_cap;      // GATEUP: P slabs to add, rows per slab
   int spec;                      // 1: request the first stages' codes before the routing reads return
@@ -191,6 +193,9 @@ void launch_gemm_decode(const DecArgs& a, GemmMode mode, Act act, hipStream_t s)
 // true when 8-wave decode workgroups of np projections, this group size and
 // code width run two per CU
 bool decode_dual(int np, int group, int bits);
+// true when the decode kernel can take two 16-slot column tiles per
+// workgroup for np projections of this group size, code width and d_in
+bool decode_two_tiles_ok(int np, int group, int bits, int d_in);
 
 // ---- activation preparation for the decode kernel ---------------------------
 struct PrepArgs {

@@ -333,6 +333,23 @@ def test_small_swiglu(act, path):
 
 
 @pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_decode_two_column_tiles(act):
+    """Decode gate/up with two 16-slot column tiles per workgroup (taken when
+    the slots average 16 or more per active expert, 2-bit codes, group 128):
+    skewed routings give experts with an empty second tile, with both tiles
+    full, and with more than two tiles (the workgroup's second pass)."""
+    layer = small_swiglu(act, 77, G=128)
+    L = tqio.upload_layer(layer)
+    L.set_path(1)
+    for T, k, routing in [(64, 2, "zipf1.1"), (100, 3, "hot70"), (96, 2, "uniform")]:
+        x, ids, g = synth.make_custom_tokens(256, 8, k, T, act, seed=T + k, routing=routing)
+        counts = np.bincount(ids.reshape(-1), minlength=8)
+        y, _ = run_forward(L, x, ids, g, act, "f32")
+        assert_parity(y, R.forward(layer, x, ids, g),
+                      what=f"two column tiles {act} T={T} k={k} {routing} slots/expert {counts.tolist()}")
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
 def test_row_bound(act):
     """The per-expert bound on sum_i |W_e[o][i]| of the effective weight: the
     triangle-inequality sum recomputed here from the stored arrays, and not
