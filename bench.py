@@ -195,11 +195,13 @@ def cpu_baseline(layer, x, ids, gates, n_tok, min_s=10.0):
                        f"building each used expert weight explicitly per chunk ({dt:.1f} s wall)")
 
 
-def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
+def measure(workload, steps, warmup, copies, scheme="tileq", log=None, keep=None):
     """Time `steps` forwards of a workload (eager launches, then the same steps
     replayed from HIP graphs), then a profiled pass for the stage durations.
     Returns the fields of a bench record (without the CPU baseline) and the
-    generated arrays."""
+    generated arrays.  `keep` (a dict) holds the generated layer and its
+    uploaded copies for the next call with the same configuration (then the
+    copies are not freed here)."""
     import torch
 
     import bit_rank_post_amd as tq
@@ -212,12 +214,21 @@ def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
     cfg_name, T = WORKLOADS[workload][:2]
     bits = WORKLOADS[workload][2] if len(WORKLOADS[workload]) > 2 else 2
     cfg = synth.CONFIG_BY_NAME[cfg_name]
-    say(f"generating {cfg_name} (T={T}, {bits}-bit residuals)")
-    layer = synth.make_layer(cfg, scheme=scheme, bits=bits)
+    copies = max(1, copies)
+    key = (cfg_name, bits, scheme, copies)
+    if keep is not None and keep.get("key") == key:
+        layer, Ls = keep["layer"], keep["Ls"]
+        say(f"reusing {cfg_name} (T={T}, {bits}-bit residuals)")
+    else:
+        say(f"generating {cfg_name} (T={T}, {bits}-bit residuals)")
+        layer = synth.make_layer(cfg, scheme=scheme, bits=bits)
+        Ls = [tqio.upload_layer(layer) for _ in range(copies)]
+        if keep is not None:
+            for L in keep.get("Ls", []):
+                L.close()
+            keep.update(key=key, layer=layer, Ls=Ls)
     pg = layer["proj"]["single" if cfg.kind == "single" else "gate"]
     x, ids, gates = synth.make_tokens(cfg, T)
-    copies = max(1, copies)
-    Ls = [tqio.upload_layer(layer) for _ in range(copies)]
     xd, idd, gd = tqio.tokens_to_device(x, ids, gates, cfg.act)
     k = cfg.topk
     d_out = cfg.d_ff if cfg.kind == "single" else cfg.d_model
@@ -350,8 +361,9 @@ def measure(workload, steps, warmup, copies, scheme="tileq", log=None):
         "kernel_source_sha256": kernel_hash(path_name),
         "grid": (pg["M"], pg["N"]),
     }
-    for L in Ls:
-        L.close()
+    if keep is None:
+        for L in Ls:
+            L.close()
     return rec, (layer, x, ids, gates)
 
 
@@ -437,8 +449,25 @@ def main():
     if args.workload == "pack_mixtral_gate":
         print(json.dumps(bench_pack(min(args.steps, 5), min(args.warmup, 1))))
         return
+    keep = {}
     rec, (layer, x, ids, gates) = measure(args.workload, args.steps, args.warmup, args.copies,
-                                          args.scheme)
+                                          args.scheme, keep=keep)
+    # the other decode batch sizes of the metric (B = 1 .. 64), same layer
+    # and weight copies, each its own timing
+    batches = None
+    if not args.no_prefill and args.workload == "mixtral_decode" and args.scheme == "tileq":
+        batches = {}
+        for b, wl in ((1, "mixtral_decode_b1"), (8, "mixtral_decode_b8"), (64, "mixtral_decode_b64")):
+            r, _ = measure(wl, min(args.steps, 100), min(args.warmup, 10), args.copies, keep=keep)
+            batches[str(b)] = {"ms_per_step": round(r["ms_per_step"], 5),
+                               "tokens_per_s": round(r["tokens_per_s"], 1),
+                               "execution": r["execution"],
+                               "roofline": {kk: r["roofline"][kk] for kk in
+                                            ("bound", "achieved", "peak", "unit", "frac",
+                                             "kernel_ms", "algorithmic_bytes_per_launch")}}
+    for L in keep.get("Ls", []):
+        L.close()
+    keep.clear()
 
     if args.calibrate_copy:
         # one elementwise kernel of known traffic (reads 256 MiB, writes
@@ -493,6 +522,7 @@ def main():
         "whole_forward": rec["whole_forward"],
         "kernel_source_sha256": rec["kernel_source_sha256"],
         "prefill": prefill,
+        "decode_batches": batches,
     }
     print(json.dumps(out))
 
