@@ -34,6 +34,7 @@
 namespace tq {
 
 constexpr int PK_T = 256;      // threads per workgroup
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int PK_TM = 64, PK_TN = 64, PK_TK = 16;
 constexpr int PK_LMAX = 136;   // largest sketch width (rank 128 + 8)
 
@@ -45,6 +46,37 @@ __device__ __forceinline__ double w_at(const void* W, size_t idx) {
     return (double)__uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(W)[idx] << 16);
   else if constexpr (WDT == 2) return (double)reinterpret_cast<const float*>(W)[idx];
   else return reinterpret_cast<const double*>(W)[idx];
+}
+
+// eight consecutive weights (16-byte aligned for 2-byte types) as fp64
+template <int WDT>
+__device__ __forceinline__ void w_at8(const void* W, size_t idx, double* v) {
+  if constexpr (WDT == 0 || WDT == 1) {
+    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(W) + idx);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint16_t h = (uint16_t)(w[u >> 1] >> (16 * (u & 1)));
+      if constexpr (WDT == 0) v[u] = (double)(float)__builtin_bit_cast(half_t, h);
+      else v[u] = (double)__uint_as_float((uint32_t)h << 16);
+    }
+  } else if constexpr (WDT == 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 q = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(W) + idx + 4 * h);
+      v[4 * h] = q.x;
+      v[4 * h + 1] = q.y;
+      v[4 * h + 2] = q.z;
+      v[4 * h + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const double2 q = *reinterpret_cast<const double2*>(reinterpret_cast<const double*>(W) + idx + 2 * h);
+      v[2 * h] = q.x;
+      v[2 * h + 1] = q.y;
+    }
+  }
 }
 
 enum { AM_DENSE = 0, AM_DENSE_T = 1, AM_WBIG = 2, AM_WBIG_T = 3 };
@@ -62,7 +94,7 @@ struct PkGemm {
   double* C;
   int ldc;
   size_t slab;                   // split-K: slab z at C + z * slab
-  int kchunk;                    // split-K: K range of one slab (multiple of PK_TK)
+  int kchunk;                    // split-K: K range of one slab (multiple of the kernel's TK)
 };
 
 // C[i][j] = sum_k A(i, k) B(k, j) over this slab's K range.  Tiles of 64 rows
@@ -72,13 +104,22 @@ struct PkGemm {
 // during the current chunk's arithmetic.  W_big readers: a chunk of 16 k never
 // crosses a tile (d_in % 128 == 0, d_out % 16 == 0), so the tile and its
 // expert are found once per chunk and row (no division per element).
-template <int AM, int BM, int NC, int WDT>
+// TK: the K chunk, 16, or 32 for the W_big readers when every chunk stays
+// inside one tile: then each thread reads eight consecutive weights of one
+// row with one 16-byte load (the 2-byte weights would otherwise take one
+// load instruction each).
+template <int AM, int BM, int NC, int WDT, int TK = PK_TK>
 __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
   constexpr int TN = 16 * NC;
-  __shared__ double sA[PK_TK][PK_TM + 2];
-  __shared__ double sB[PK_TK][TN + 2];
+  constexpr bool WV = (AM == AM_WBIG || AM == AM_WBIG_T) && TK == 32;   // vector W loads
+  static_assert(TK == 16 || WV, "32-input chunks for the W_big readers only");
+  constexpr int TM = WV ? 2 * PK_TM : PK_TM;      // rows of the tile (W_big: 128, fewer B reads)
+  constexpr int NA = WV ? 16 : 4;                // A values per thread and chunk
+  constexpr int NB = NC * TK / 16;               // B values per thread and chunk
+  __shared__ double sA[TK][TM + 2];
+  __shared__ double sB[TK][TN + 2];
   const int tid = threadIdx.x;
-  const int i0 = blockIdx.y * PK_TM, j0 = blockIdx.x * TN;
+  const int i0 = blockIdx.y * TM, j0 = blockIdx.x * TN;
   const int k_begin = blockIdx.z * g.kchunk;
   const int k_end = min(g.K, k_begin + g.kchunk);
   const int ty = tid >> 4, tx = tid & 15;
@@ -87,7 +128,21 @@ __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
   //   AM_WBIG_T: column i = tid & 63 of A is a column of W_big: tile column, input
   int rt_m[4] = {0, 0, 0, 0}, rt_o[4] = {0, 0, 0, 0};
   int ct_n = 0, ct_i = 0;
-  if constexpr (AM == AM_WBIG) {
+  if constexpr (WV && AM == AM_WBIG) {
+    // rows i = (tid >> 2) + 64 h (h = 0, 1), inputs 8 (tid & 3) .. + 7 of the chunk
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int gi = min(i0 + (tid >> 2) + 64 * h, g.M - 1);
+      rt_m[h] = gi / g.d_out;
+      rt_o[h] = gi - rt_m[h] * g.d_out;
+    }
+  } else if constexpr (WV && AM == AM_WBIG_T) {
+    // columns i0 + 8 (tid & 15) .. + 7 of W_big (one tile column), rows
+    // (tid >> 4) + 16 h of the chunk
+    const int gi = min(i0 + 8 * (tid & 15), g.M - 1);
+    ct_n = gi / g.d_in;
+    ct_i = gi - ct_n * g.d_in;
+  } else if constexpr (AM == AM_WBIG) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int gi = min(i0 + (tid >> 4) + 16 * s, g.M - 1);
@@ -102,9 +157,36 @@ __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
   // A and B values of a K chunk, loaded into registers one chunk ahead of
   // the arithmetic (the global loads of chunk k0 + 16 are in flight while
   // chunk k0 is multiplied from LDS)
-  double ra[4], rb[NC];
+  double ra[NA], rb[NB];
   auto load_chunk = [&](int k0) {
-    if constexpr (AM == AM_WBIG) {
+    if constexpr (WV && AM == AM_WBIG) {
+      const int nt = k0 / g.d_in, q = tid & 3;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = (tid >> 2) + 64 * h;
+        const int e = (i0 + i < g.M && k0 + 8 * q < k_end) ? g.emap[rt_m[h] * g.Ng + nt] : -1;
+        if (e >= 0) {
+          w_at8<WDT>(g.W, ((size_t)e * g.d_out + rt_o[h]) * g.d_in + (k0 - nt * g.d_in) + 8 * q,
+                     ra + 8 * h);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) ra[8 * h + u] = 0.0;
+        }
+      }
+    } else if constexpr (WV && AM == AM_WBIG_T) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = (tid >> 4) + 16 * h;
+        const int mt = (k0 + kk) / g.d_out, o = k0 + kk - mt * g.d_out;
+        const int e = (i0 + 8 * (tid & 15) < g.M && k0 + kk < k_end) ? g.emap[mt * g.Ng + ct_n] : -1;
+        if (e >= 0) {
+          w_at8<WDT>(g.W, ((size_t)e * g.d_out + o) * g.d_in + ct_i, ra + 8 * h);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) ra[8 * h + u] = 0.0;
+        }
+      }
+    } else if constexpr (AM == AM_WBIG) {
       const int nt = k0 / g.d_in, ii0 = k0 - nt * g.d_in;
       const int kk = tid & 15;
 #pragma unroll
@@ -150,8 +232,8 @@ __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < NC; ++t) {
-      const int idx = tid + PK_T * t;            // 16 TN = 256 NC elements
+    for (int t = 0; t < NB; ++t) {
+      const int idx = tid + PK_T * t;            // TK TN = 256 NB elements
       int j, kk;
       if constexpr (BM == BM_DENSE) {
         j = idx % TN;
@@ -170,39 +252,93 @@ __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
     }
   };
   auto store_chunk = [&]() {
+    if constexpr (WV && AM == AM_WBIG) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if constexpr (AM == AM_DENSE || AM == AM_WBIG) sA[tid & 15][(tid >> 4) + 16 * s] = ra[s];
-      else sA[(tid >> 6) + 4 * s][tid & 63] = ra[s];
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sA[8 * (tid & 3) + u][(tid >> 2) + 64 * h] = ra[8 * h + u];
+    } else if constexpr (WV && AM == AM_WBIG_T) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sA[(tid >> 4) + 16 * h][8 * (tid & 15) + u] = ra[8 * h + u];
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if constexpr (AM == AM_DENSE || AM == AM_WBIG) sA[tid & 15][(tid >> 4) + 16 * s] = ra[s];
+        else sA[(tid >> 6) + 4 * s][tid & 63] = ra[s];
+      }
     }
 #pragma unroll
-    for (int t = 0; t < NC; ++t) {
+    for (int t = 0; t < NB; ++t) {
       const int idx = tid + PK_T * t;
       if constexpr (BM == BM_DENSE) sB[idx / TN][idx % TN] = rb[t];
       else sB[idx & 15][idx >> 4] = rb[t];
     }
   };
+  // The W_big products run on the fp64 matrix cores: wave w takes rows
+  // 32 w .. 32 w + 31 of the tile (two row tiles) against all NC column tiles,
+  // v_mfma_f64_16x16x4f64 per 4 k (lane l: A[l % 16][l / 16], B[l / 16][l % 16];
+  // result element j of lane l at row 4 j + l / 16, column l % 16).  Other
+  // products: 4 x NC fp64 FMAs per thread.
+  constexpr bool MF = WV;
   double acc[4][NC] = {};
+  f64x4 macc[MF ? 2 : 1][MF ? NC : 1];
+#pragma unroll
+  for (int r = 0; r < (MF ? 2 : 1); ++r)
+#pragma unroll
+    for (int v = 0; v < (MF ? NC : 1); ++v) macc[r][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const int lane = tid & 63, wv = tid >> 6;
   if (k_begin < k_end) load_chunk(k_begin);
-  for (int k0 = k_begin; k0 < k_end; k0 += PK_TK) {
+  for (int k0 = k_begin; k0 < k_end; k0 += TK) {
     store_chunk();
     __syncthreads();
-    if (k0 + PK_TK < k_end) load_chunk(k0 + PK_TK);
+    if (k0 + TK < k_end) load_chunk(k0 + TK);
+    if constexpr (MF) {
 #pragma unroll
-    for (int kk = 0; kk < PK_TK; ++kk) {
-      double a[4], b[NC];
+      for (int k4 = 0; k4 < TK; k4 += 4) {
+        double b[NC];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] = sA[kk][ty * 4 + u];
+        for (int v = 0; v < NC; ++v) b[v] = sB[k4 + (lane >> 4)][16 * v + (lane & 15)];
 #pragma unroll
-      for (int v = 0; v < NC; ++v) b[v] = sB[kk][tx + 16 * v];
+        for (int r = 0; r < 2; ++r) {
+          const double a = sA[k4 + (lane >> 4)][32 * wv + 16 * r + (lane & 15)];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+          for (int v = 0; v < NC; ++v)
+            macc[r][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[v], macc[r][v], 0, 0, 0);
+        }
+      }
+    } else {
 #pragma unroll
-        for (int v = 0; v < NC; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+      for (int kk = 0; kk < TK; ++kk) {
+        double a[4], b[NC];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = sA[kk][ty * 4 + u];
+#pragma unroll
+        for (int v = 0; v < NC; ++v) b[v] = sB[kk][tx + 16 * v];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < NC; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+      }
     }
     __syncthreads();
   }
   double* C = g.C + (size_t)blockIdx.z * g.slab;
+  if constexpr (MF) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int v = 0; v < NC; ++v) {
+        const int gj = j0 + 16 * v + (lane & 15);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int gi = i0 + 32 * wv + 16 * r + 4 * j + (lane >> 4);
+          if (gi < g.M && gj < g.N) C[(size_t)gi * g.ldc + gj] = macc[r][v][j];
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int gi = i0 + ty * 4 + u;
@@ -216,24 +352,37 @@ __global__ __launch_bounds__(PK_T) void pk_gemm_kernel(PkGemm g) {
 }
 
 // K range of one split-K slab and the number of slabs for `splits` requested
-static int pk_kchunk(int K, int splits) {
+static int pk_kchunk(int K, int splits, int tk = PK_TK) {
   splits = std::max(1, splits);
-  return std::max(PK_TK, ((K + splits - 1) / splits + PK_TK - 1) / PK_TK * PK_TK);
+  return std::max(tk, ((K + splits - 1) / splits + tk - 1) / tk * tk);
 }
-static int pk_nslab(int K, int splits) {
-  const int kc = pk_kchunk(K, splits);
+static int pk_nslab(int K, int splits, int tk = PK_TK) {
+  const int kc = pk_kchunk(K, splits, tk);
   return std::max(1, (K + kc - 1) / kc);
+}
+// K chunk of a product: 32 for the W_big readers whose chunks stay inside a
+// tile (along d_in always; along d_out when it is a multiple of 32)
+static int pk_tk(const PkGemm& g, int amode) {
+  if (amode == AM_WBIG) return 32;
+  if (amode == AM_WBIG_T && g.d_out % 32 == 0) return 32;
+  return PK_TK;
+}
+
+template <int AM, int BM, int NC, int TK>
+static void pk_launch_wdt(const PkGemm& g, dim3 grid, hipStream_t s) {
+  switch (g.wdt) {
+    case 0: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 0, TK>), grid, dim3(PK_T), 0, s, g); break;
+    case 1: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 1, TK>), grid, dim3(PK_T), 0, s, g); break;
+    case 2: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 2, TK>), grid, dim3(PK_T), 0, s, g); break;
+    default: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 3, TK>), grid, dim3(PK_T), 0, s, g); break;
+  }
 }
 
 template <int AM, int BM, int NC>
 static void pk_launch_w(const PkGemm& g, dim3 grid, hipStream_t s) {
   if constexpr (AM == AM_WBIG || AM == AM_WBIG_T) {
-    switch (g.wdt) {
-      case 0: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 0>), grid, dim3(PK_T), 0, s, g); break;
-      case 1: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 1>), grid, dim3(PK_T), 0, s, g); break;
-      case 2: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 2>), grid, dim3(PK_T), 0, s, g); break;
-      default: hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 3>), grid, dim3(PK_T), 0, s, g); break;
-    }
+    if (pk_tk(g, AM) == 32) pk_launch_wdt<AM, BM, NC, 32>(g, grid, s);
+    else pk_launch_wdt<AM, BM, NC, PK_TK>(g, grid, s);
   } else {
     hipLaunchKernelGGL((pk_gemm_kernel<AM, BM, NC, 3>), grid, dim3(PK_T), 0, s, g);
   }
@@ -266,11 +415,13 @@ __global__ void pk_sum_slabs_kernel(const double* __restrict__ C, int nslab, siz
 
 void launch_pk_gemm(const PkGemm& g0, int amode, int bmode, int splits, hipStream_t s) {
   PkGemm g = g0;
-  g.kchunk = pk_kchunk(g.K, splits);
-  splits = pk_nslab(g.K, splits);
+  const int tk = pk_tk(g, amode);
+  g.kchunk = pk_kchunk(g.K, splits, tk);
+  splits = pk_nslab(g.K, splits, tk);
   // one column tile for the sketch's widths (up to 144), else tiles of 64
   const int nc = (g.N <= 64) ? 4 : (g.N <= 80 ? 5 : (g.N <= 144 ? 9 : 4));
-  const dim3 grid((g.N + 16 * nc - 1) / (16 * nc), (g.M + PK_TM - 1) / PK_TM, std::max(1, splits));
+  const int tm = (tk == 32) ? 2 * PK_TM : PK_TM;   // rows per tile (as the kernel's TM)
+  const dim3 grid((g.N + 16 * nc - 1) / (16 * nc), (g.M + tm - 1) / tm, std::max(1, splits));
   if (nc == 5) pk_launch_nc<5>(g, amode, bmode, grid, s);
   else if (nc == 9) pk_launch_nc<9>(g, amode, bmode, grid, s);
   else pk_launch_nc<4>(g, amode, bmode, grid, s);
@@ -286,7 +437,7 @@ static void launch_pk_gemm_split(const PkGemm& g0, int amode, int splits, double
   g.ldc = g.N;
   g.slab = (size_t)g.M * g.N;
   launch_pk_gemm(g, amode, BM_DENSE, splits, s);
-  const int nslab = pk_nslab(g.K, splits);
+  const int nslab = pk_nslab(g.K, splits, pk_tk(g, amode));
   const size_t count = (size_t)g.M * g.N;
   hipLaunchKernelGGL(pk_sum_slabs_kernel, dim3((unsigned)std::min<size_t>((count + 255) / 256, 8192)),
                      dim3(256), 0, s, slabs, nslab, g.slab, count, out);
