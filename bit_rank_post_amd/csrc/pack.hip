@@ -533,7 +533,11 @@ __global__ __launch_bounds__(PK_JT) void pk_jacobi_kernel(const double* __restri
     for (int round = 0; round < le - 1; ++round) {
       // circle method: player 0 fixed, the others rotate
       if (tid < np) {
-        auto pos = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + round) % (le - 1); };
+        // (x - 1 + round < 2 (le - 1): the remainder is one conditional subtraction)
+        auto pos = [&](int x) {
+          const int t = x - 1 + round;
+          return x == 0 ? 0 : 1 + (t >= le - 1 ? t - (le - 1) : t);
+        };
         const int a0 = pos(tid), b0 = pos(le - 1 - tid);
         const int p = min(a0, b0), q = max(a0, b0);
         double c = 1.0, sn = 0.0;
