@@ -350,6 +350,42 @@ def test_decode_two_column_tiles(act):
 
 
 @pytest.mark.parametrize("act", ["f16", "bf16"])
+def test_decode_workspace_poisoned(act):
+    """Decode batches (at most 16 slots per expert on average) on a workspace
+    filled with NaN bytes beforehand: nothing the forward reads may be left
+    over from earlier contents.  Routings: an expert with more than 32 slots
+    (several column tiles), dropped ids (positions past the valid ones), a
+    single token, and Zipf top-4."""
+    layer = small_swiglu(act, 91, G=128)
+    L = tqio.upload_layer(layer)
+    L.set_path(1)
+    rng = np.random.default_rng(5)
+    cases = []
+    x, ids, g = synth.make_custom_tokens(256, 8, 2, 64, act, seed=11, routing="hot70")
+    cases.append(("hot70 T=64", x, ids, g))
+    x, ids, g = synth.make_custom_tokens(256, 8, 2, 40, act, seed=12)
+    ids = ids.copy()
+    ids[rng.choice(40, 6, replace=False), rng.integers(0, 2, 6)] = rng.choice([-1, 8, 1000], 6)
+    cases.append(("dropped T=40", x, ids, g))
+    x, ids, g = synth.make_custom_tokens(256, 8, 2, 1, act, seed=13)
+    cases.append(("T=1", x, ids, g))
+    x, ids, g = synth.make_custom_tokens(256, 8, 4, 32, act, seed=14, routing="zipf1.1")
+    cases.append(("zipf top-4 T=32", x, ids, g))
+    for what, x, ids, g in cases:
+        T, k = ids.shape
+        assert T * k <= 16 * 8
+        ws = tqio.workspace(L, T, k)
+        ws.fill_(0xFF)
+        counts = np.bincount(ids[(ids >= 0) & (ids < 8)], minlength=8)
+        y, dropped = run_forward(L, x, ids, g, act, "f32", ws=ws)
+        assert dropped == int(((ids < 0) | (ids >= 8)).sum())
+        assert np.all(np.isfinite(y)), what
+        assert_parity(y, R.forward(layer, x, ids, g),
+                      what=f"poisoned workspace {act} {what} slots/expert {counts.tolist()}")
+    L.close()
+
+
+@pytest.mark.parametrize("act", ["f16", "bf16"])
 def test_row_bound(act):
     """The per-expert bound on sum_i |W_e[o][i]| of the effective weight: the
     triangle-inequality sum recomputed here from the stored arrays, and not
