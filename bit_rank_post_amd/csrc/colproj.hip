@@ -38,7 +38,6 @@ namespace tq {
 enum RgMode { RG_COL = 0, RG_DUAL = 1, RG_PLAIN = 2 };
 constexpr int RG_WAVES = 8;
 constexpr int RG_NSLOT = 4, RG_DEPTH = 3;
-constexpr int RG_COL_KS = 1;                     // column stage: 16 KB slots, two workgroups per CU
 constexpr int RG_A = 0;                          // [KS][8 frags][64 lanes] x 16 B, then
                                                  // the activations, the same
 
@@ -305,8 +304,18 @@ void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
   // z: the projection (gate, up), or the k-split of a single projection
   const int nz = nproj > 1 ? nproj : (a[0].nsplit > 1 ? a[0].nsplit : 1);
   const dim3 grid((unsigned)(((max_tiles + 7) / 8) * 8), 1, nz);
-  if (act == ACT_F16) hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_COL, RG_COL_KS>), grid, dim3(64 * RG_WAVES), 0, s, args);
-  else hipLaunchKernelGGL((rowgemm_kernel<__bf16, RG_COL, RG_COL_KS>), grid, dim3(64 * RG_WAVES), 0, s, args);
+  // A grid that fits one workgroup per CU streams each workgroup's long
+  // k-range in stages of 64 inputs (32 KB slots; half the ring round trips
+  // per input; d_in a multiple of 64); a larger grid keeps stages of 32
+  // inputs and 16 KB slots, so that two workgroups share a CU.
+  const bool d64 = (a[0].d_in % 64) == 0 && (nproj < 2 || (a[1].d_in % 64) == 0);
+  if (d64 && (long)grid.x * nz <= device_cus()) {
+    if (act == ACT_F16) hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_COL, 2>), grid, dim3(64 * RG_WAVES), 0, s, args);
+    else hipLaunchKernelGGL((rowgemm_kernel<__bf16, RG_COL, 2>), grid, dim3(64 * RG_WAVES), 0, s, args);
+  } else {
+    if (act == ACT_F16) hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_COL, 1>), grid, dim3(64 * RG_WAVES), 0, s, args);
+    else hipLaunchKernelGGL((rowgemm_kernel<__bf16, RG_COL, 1>), grid, dim3(64 * RG_WAVES), 0, s, args);
+  }
 }
 
 void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s) {

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -79,6 +80,23 @@ struct tq_layer {
   hipEvent_t ev[9] = {};
 };
 
+namespace tq {
+// Compute units of the current device (cached per device id; concurrent
+// first calls store the same value).
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace tq
+
 namespace {
 
 int nproj(const tq_layer* L) { return L->kind == TQ_SINGLE ? 1 : 3; }
@@ -139,9 +157,6 @@ int choose_path(const tq_layer* L, int T, int k) {
   return path;
 }
 
-// column stage split-K for decode: slabs of 1024 inputs
-int device_cus();
-
 // Column-stage k-splits.  Decode: see decode_col_splits.  Prefill: only the
 // projection whose rank vectors go to the combine as fp32 (down, or the
 // single projection) is split, when its row tiles (about rows / 128 + K)
@@ -185,20 +200,6 @@ int choose_nks(const tq_layer* L, int q, int S) {
   int nks = 1;
   while (nks < 8 && active * d.nrb * (2L * nks) <= 16L * cus && nfull / (2 * nks) >= 4) nks *= 2;
   return nks;
-}
-
-// Compute units of the current device (cached per device id).
-int device_cus() {
-  static int cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
 }
 
 // Waves per decode workgroup and how many of them own a 16-row fragment.

@@ -112,6 +112,8 @@ struct ColArgs {
 // tiles of 128 rows (route rt_col 128)
 void launch_colproj(const ColArgs* a, int nproj, int rt, int max_tiles, Act act,
                     hipStream_t s);
+// compute units of the current device (cached per device id)
+int device_cus();
 
 // ---- residual grouped GEMM (+ low-rank K-extension, SwiGLU) ---------------
 enum GemmMode { MODE_GATEUP = 0, MODE_RES = 1 };
