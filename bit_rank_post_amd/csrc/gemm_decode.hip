@@ -10,7 +10,9 @@
 // for a column tile of 16 of the expert's slots.  With NCT = 2 (many slots
 // per expert) the waves form two groups that take two column tiles at once,
 // reading each stage's codes from LDS once loaded: the codes are streamed
-// once for 32 slots.  Everything a stage
+// once for 32 slots.  For a single projection (down) a wave may instead own
+// two adjacent fragments in the places of gate and up (MODE_RES2), so each
+// stage streams twice the code bytes.  Everything a stage
 // needs (each wave's codes, the stage's activations shared by all waves, the
 // scale/zero words and the activation group sums) is brought straight into
 // LDS by buffer loads with the LDS destination (no registers in between), in
@@ -37,6 +39,13 @@
 #include "tq_device.h"
 
 namespace tq {
+
+// Kernel-internal mode: one projection (as MODE_RES) with two row fragments
+// per wave, 2 u and 2 u + 1 of row unit u, in the places the gate and up
+// fragments take in MODE_GATEUP: each wave streams twice the code bytes per
+// stage for the same fixed costs per stage.
+constexpr int MODE_RES2 = 2;
+template <int MODE> constexpr int dec_np() { return MODE == MODE_RES ? 1 : 2; }
 
 // LDS slot layout (bytes) for NP projections, WAVES waves, NG groups/stage,
 // BITS-bit codes and NCT column tiles of 16 slots: the waves form NCT groups
@@ -87,7 +96,7 @@ constexpr int ring_depth() {
 
 template <int MODE, int GS, int WAVES, int BITS, int NCT = 1>
 constexpr bool dec_dual_cfg() {
-  return dec_dual<DecSlot<(MODE == MODE_GATEUP) ? 2 : 1, WAVES, 8 / GS, BITS, NCT>::BYTES, WAVES>();
+  return dec_dual<DecSlot<dec_np<MODE>(), WAVES, 8 / GS, BITS, NCT>::BYTES, WAVES>();
 }
 
 // Raw A operand (1 + q c per fp16 half) of k-step J of a stage from the
@@ -112,7 +121,9 @@ template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS, int NCT>
 __global__ __launch_bounds__(64 * WAVES, (dec_dual_cfg<MODE, GS, WAVES, BITS, NCT>() ? 4 : 1))
 void gemm_dec_kernel(DecArgs a) {
   typedef typename Vec8<T>::type V8;
-  constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
+  constexpr int NP = dec_np<MODE>();
+  constexpr bool PAIR = MODE == MODE_RES2;   // the NP "projections" are two row fragments
+  constexpr int NPG = PAIR ? 1 : NP;         // projections whose Sigma p the row stage gathers
   constexpr int NG = 8 / GS;             // groups per stage
   typedef DecSlot<NP, WAVES, NG, BITS, NCT> SL;
   constexpr int WR = SL::WR;
@@ -145,10 +156,12 @@ void gemm_dec_kernel(DecArgs a) {
   // the routing's record says which expert that is, and the workgroups past
   // the active ones end at once instead of being interleaved with the work.
   const int nrb = a.d_out >> 4;
-  // a.rows_per (<= WAVES) waves of a workgroup own row fragments; the others
+  // row units of a wave: a 16-row fragment, or (PAIR) two
+  const int nun = PAIR ? (nrb + 1) >> 1 : nrb;
+  // a.rows_per (<= WAVES) waves of a workgroup own row units; the others
   // only help with the shared loads
   const int rpw = a.rows_per;
-  const int nby = (nrb + rpw - 1) / rpw;
+  const int nby = (nun + rpw - 1) / rpw;
   const int nby8 = (nby + 7) >> 3;
   const int wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -179,8 +192,17 @@ void gemm_dec_kernel(DecArgs a) {
   // row-fragment slot and column tile of this wave
   const int wr = (NCT == 1) ? wave : wave % WR, wc = (NCT == 1) ? 0 : wave / WR;
   const int rb_raw = by * rpw + wr;
-  const bool rvalid = wr < rpw && rb_raw < nrb;
-  const int rb = rvalid ? rb_raw : nrb - 1;          // clamped: loads stay in bounds
+  const bool rvalid = wr < rpw && rb_raw < nun;
+  const int rb = rvalid ? rb_raw : nun - 1;          // clamped: loads stay in bounds
+  // row fragment of "projection" p (PAIR: 2 rb + p, clamped; the second of
+  // an odd count is computed but not stored)
+  int rbp[NP];
+  bool fvalid[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    rbp[p] = PAIR ? min(2 * rb + p, nrb - 1) : rb;
+    fvalid[p] = rvalid && (!PAIR || 2 * rb_raw + p < nrb);
+  }
   const int nsteps = a.d_in >> 5;
   const int nfull = nsteps >> 3;
   // k-chunk of this workgroup: stages [k0, k0 + ntau); the 4-step tail stage
@@ -203,10 +225,11 @@ void gemm_dec_kernel(DecArgs a) {
   const uint32_t* szb[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    cbase[p] = a.p[p].codes + (size_t)e * cpe + (size_t)rb * nsteps * WPS;
-    szb[p] = a.p[p].sz + ((size_t)e * nrb + rb) * ng * 16;
+    const ProjDev& pd = a.p[PAIR ? 0 : p];
+    cbase[p] = pd.codes + (size_t)e * cpe + (size_t)rbp[p] * nsteps * WPS;
+    szb[p] = pd.sz + ((size_t)e * nrb + rbp[p]) * ng * 16;
     rc[p] = make_rsrc(cbase[p], (uint32_t)nsteps * WPS * 4u);
-    rs[p] = make_rsrc(a.p[p].sz + (size_t)e * nrb * ng * 16, (uint32_t)nrb * ng * 64u);
+    rs[p] = make_rsrc(pd.sz + (size_t)e * nrb * ng * 16, (uint32_t)nrb * ng * 64u);
   }
   // scale/zero loads of this wave: load i = wave + WAVES * k of the stage
   // covers words 64 (i mod NSZP) + lane of projection i / NSZP's table, i.e.
@@ -221,7 +244,7 @@ void gemm_dec_kernel(DecArgs a) {
     sz_lds[k] = ok ? SL::SZ + i * 256 : -1;
     const int w = (ok ? i - sz_p[k] * SL::NSZP : 0) * 64 + lane;
     const int wv = w / (16 * NG), g = (w / 16) % NG, row = w & 15;
-    const int rbw = min(by * rpw + wv, nrb - 1);
+    const int rbw = min(PAIR ? 2 * (by * rpw + wv) + sz_p[k] : by * rpw + wv, nrb - 1);
     sz_vo[k] = (ok && wv < rpw) ? (((uint32_t)rbw * ng + g) * 16u + row) * 4u : OOB;
   }
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.Xp, (uint32_t)a.rows * a.d_in * 2u);
@@ -564,7 +587,7 @@ void gemm_dec_kernel(DecArgs a) {
       int cix[NP][IMAX], kix[NP][IMAX];
       bool ok[NP][IMAX];
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
+      for (int p = 0; p < NPG; ++p) {
         const ProjDev& pd = a.p[p];
         const int rp = pd.r_pad, q4 = rp >> 2;
         const int prow = (a.ap_T > 0) ? n_e[p] * a.ap_T + tok : pos;
@@ -590,17 +613,18 @@ void gemm_dec_kernel(DecArgs a) {
       }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const ProjDev& pd = a.p[p];
+        const int pp = PAIR ? 0 : p;
+        const ProjDev& pd = a.p[pp];
         if (pd.rank == 0) continue;
         const int rp = pd.r_pad;
         const T* up = reinterpret_cast<const T*>(pd.U) +
-                      ((size_t)m_e[p] * a.d_out + rb * 16 + l16e) * rp + 8 * lge;
+                      ((size_t)m_e[pp] * a.d_out + rbp[p] * 16 + l16e) * rp + 8 * lge;
 #pragma unroll
         for (int c = 0; c < RC; ++c)
           if (32 * c < rp) uf[p][c] = *reinterpret_cast<const V8*>(up + 32 * c);
       }
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
+      for (int p = 0; p < NPG; ++p) {
         const int rps = a.p[p].r_pad + 8;
 #pragma unroll
         for (int j = 0; j < IMAX; ++j) {
@@ -634,10 +658,11 @@ void gemm_dec_kernel(DecArgs a) {
         const int l16e = tid_e & 15, lge = (tid_e >> 4) & 3;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const ProjDev& pd = a.p[p];
+          const int pp = PAIR ? 0 : p;
+          const ProjDev& pd = a.p[pp];
           if (pd.rank == 0) continue;
           const int rp = pd.r_pad, rps = rp + 8;
-          const T* bh = sh + ((2 * p) * 16 + l16e) * rps + 8 * lge;
+          const T* bh = sh + ((2 * pp) * 16 + l16e) * rps + 8 * lge;
 #pragma unroll
           for (int c = 0; c < RC; ++c) {
             if (32 * c < rp) {
@@ -657,6 +682,15 @@ void gemm_dec_kernel(DecArgs a) {
           *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(a.h) + (size_t)pos_e * a.d_out + o_e) =
               __builtin_bit_cast(u32x2, hv);
         }
+      } else if constexpr (PAIR) {
+        if (cvalid) {
+          const float g = a.gates[opaque(slotid)];
+#pragma unroll
+          for (int p = 0; p < NP; ++p)
+            if (fvalid[p])
+              *reinterpret_cast<f32x4*>(a.dres + ((size_t)ks * a.S + pos_e) * a.d_out + opaque(rbp[p] * 16 + 4 * lg)) =
+                  acc[p] * g;
+        }
       } else {
         if (cvalid) {
           const float g = a.gates[opaque(slotid)];
@@ -673,7 +707,7 @@ void gemm_dec_kernel(DecArgs a) {
 
 template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS, int NCT = 1>
 static void dec_launch(const DecArgs& a, hipStream_t s) {
-  constexpr int NP = (MODE == MODE_GATEUP) ? 2 : 1;
+  constexpr int NP = dec_np<MODE>();
   constexpr int BYTES = DecSlot<NP, WAVES, 8 / GS, BITS, NCT>::BYTES;
   if constexpr (WAVES > 8 && ring_depth<BYTES, DMAX, false>() < 2) {
     // slots too large for a ring of three: fall back to 8 waves, one tile
@@ -685,7 +719,8 @@ static void dec_launch(const DecArgs& a, hipStream_t s) {
     DecArgs b = a;
     b.rows_per = (a.rows_per >= 1 && a.rows_per <= WR) ? a.rows_per : WR;
     const int nrb = b.d_out >> 4;
-    const int nby = (nrb + b.rows_per - 1) / b.rows_per;
+    const int nun = (MODE == MODE_RES2) ? (nrb + 1) >> 1 : nrb;   // row units
+    const int nby = (nun + b.rows_per - 1) / b.rows_per;
     const dim3 grid(b.K * ((nby + 7) / 8) * 8 * b.nks);
     hipLaunchKernelGGL((gemm_dec_kernel<T, MODE, GS, WAVES, DMAX, BITS, NCT>), grid, dim3(64 * WAVES),
                        0, s, b);
@@ -757,9 +792,11 @@ template <typename T>
 static void dec_bits(const DecArgs& a, GemmMode mode, hipStream_t s) {
   if (a.p[0].bits == 3) {
     if (mode == MODE_GATEUP) dec_waves<T, MODE_GATEUP, 3>(a, s);
+    else if (a.pair) dec_waves<T, MODE_RES2, 3>(a, s);
     else dec_waves<T, MODE_RES, 3>(a, s);
   } else {
     if (mode == MODE_GATEUP) dec_waves<T, MODE_GATEUP, 2>(a, s);
+    else if (a.pair) dec_waves<T, MODE_RES2, 2>(a, s);
     else dec_waves<T, MODE_RES, 2>(a, s);
   }
 }

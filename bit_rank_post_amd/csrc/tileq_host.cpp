@@ -115,6 +115,7 @@ void proj_dims(const tq_layer* L, int which, int* d_in, int* d_out) {
 struct Plan {
   int T, k, S, path, bm_gemm, rt_col, max_tiles_gemm, max_col_tiles;
   int nks;                       // k-chunks (fp32 slabs) of the last projection's residual
+  bool pair;                     // decode: two 16-row fragments per wave in that residual
   int ap_T;                      // decode: column stage over all (column, token) pairs
   int col_tiles_x, col_tiles_down;   // decode column-stage tiles
   size_t flags, cnt, off, perm, inv, etab, arec, tile_gemm, tile_colx, colmask, cntw, rank, wgcnt, dropw;
@@ -188,18 +189,30 @@ int choose_nsplit(const tq_layer* L, int q, int path, long rows, int d_in) {
 // k-chunks of the decode kernel for a down / single projection: the most
 // (up to 8, each chunk keeping at least 4 stages) for which the active
 // experts' 16-row fragments times the chunks still fit one round of the grid
-// (16 rows per CU: two 8-wave workgroups or one of 16 waves).  A second round
-// costs more than longer chunks: every workgroup pays a fixed start (routing
-// reads, first batch) and epilogue.  Each chunk writes its own fp32 slab of
-// per-slot outputs.
-int choose_nks(const tq_layer* L, int q, int S) {
+// (16 fragments per CU: two 8-wave workgroups or one of 16 waves; with two
+// fragments per wave, 32).  A second round costs more than longer chunks:
+// every workgroup pays a fixed start (routing reads, first batch) and
+// epilogue.  Each chunk writes its own fp32 slab of per-slot outputs.
+int choose_nks(const tq_layer* L, int q, int S, bool pair) {
   const ProjDev& d = L->proj[q].dev;
   const long active = std::min<long>(L->K, S);
   const long cus = device_cus();
   const int nfull = (d.d_in >> 5) >> 3;
+  const long per_cu = pair ? 32 : 16;
   int nks = 1;
-  while (nks < 8 && active * d.nrb * (2L * nks) <= 16L * cus && nfull / (2 * nks) >= 4) nks *= 2;
+  while (nks < 8 && active * d.nrb * (2L * nks) <= per_cu * cus && nfull / (2 * nks) >= 4) nks *= 2;
   return nks;
+}
+
+// Two 16-row fragments per wave for a down / single projection at decode
+// batch sizes (2-bit codes, where such 8-wave workgroups run two per CU):
+// taken when it allows more k-chunks in one round than one fragment per
+// wave.  Each stage then streams twice the code bytes for the same fixed
+// costs, in shorter chunks.
+bool choose_pair(const tq_layer* L, int q, int S) {
+  const ProjDev& d = L->proj[q].dev;
+  if (d.bits != 2 || !decode_dual(2, d.group, d.bits) || (long)S > 16L * L->K) return false;
+  return choose_nks(L, q, S, true) > choose_nks(L, q, S, false);
 }
 
 // Waves per decode workgroup and how many of them own a 16-row fragment.
@@ -314,7 +327,8 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.h = take(L->kind == TQ_SWIGLU ? (size_t)S * L->d_ff * 2 : 0);
   int d_in_last, d_out_last;
   proj_dims(L, nproj(L) - 1, &d_in_last, &d_out_last);
-  p.nks = (path == 1) ? choose_nks(L, nproj(L) - 1, S) : 1;
+  p.pair = path == 1 && choose_pair(L, nproj(L) - 1, S);
+  p.nks = (path == 1) ? choose_nks(L, nproj(L) - 1, S, p.pair) : 1;
   p.dres = take((size_t)p.nks * S * d_out_last * sizeof(float));
   p.nys = 1;
   if (L->shared.d_ff > 0) {
@@ -959,7 +973,13 @@ tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_
       da.ap_T = p.ap_T;
       da.p_nsplit = p.nsplit[0];
       da.p_rows_cap = p.rows_cap;
-      choose_waves(L, 0, p.S, p.nks, 1, &da.waves, &da.rows_per);
+      if (p.pair) {
+        da.pair = 1;
+        da.waves = 8;
+        da.rows_per = 8;
+      } else {
+        choose_waves(L, 0, p.S, p.nks, 1, &da.waves, &da.rows_per);
+      }
       launch_gemm_decode(da, MODE_RES, act, s);
     }
   } else {
@@ -1052,7 +1072,13 @@ tq_status forward_impl(const tq_layer* L, const void* x, int32_t T, const int32_
       da.ap_T = 0;
       da.p_nsplit = p.nsplit[2];
       da.p_rows_cap = p.rows_cap;
-      choose_waves(L, 2, p.S, p.nks, 1, &da.waves, &da.rows_per);
+      if (p.pair) {
+        da.pair = 1;
+        da.waves = 8;
+        da.rows_per = 8;
+      } else {
+        choose_waves(L, 2, p.S, p.nks, 1, &da.waves, &da.rows_per);
+      }
       launch_gemm_decode(da, MODE_RES, act, s);
     } else {
       GemmArgs ga{};

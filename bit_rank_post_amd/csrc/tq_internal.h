@@ -183,11 +183,12 @@ struct DecArgs {
   int nks;                       // k-chunks (RES; 1 for GATEUP)
   int S;                         // slots (slab stride of dres)
   int waves;                     // waves per workgroup: 8, 12, 14 or 16 (GATEUP), 8 or 16
-  int rows_per;                  // waves that own a 16-row fragment (<= waves / nct)
+  int rows_per;                  // waves that own a row unit: a 16-row fragment, or two with pair (<= waves / nct)
   int nct;                       // column tiles of 16 slots per pass: 1, or 2 (16 waves in two
                                  // groups of 8 sharing each stage's codes; no 4-step tail)
   int ap_T;                      // GATEUP: P rows are (column, token) pairs n * ap_T + t
   int p_nsplit, p_rows_cap;      // GATEUP: P slabs to add, rows per slab
+  int pair;                      // RES: 1 = each wave takes two 16-row fragments (row units of 32 rows)
   int spec;                      // 1: request the first stages' codes before the routing reads return
   const int* arec;               // active-expert records (compact mapping) or nullptr
 };

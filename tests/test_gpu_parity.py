@@ -349,6 +349,36 @@ def test_decode_two_column_tiles(act):
                       what=f"two column tiles {act} T={T} k={k} {routing} slots/expert {counts.tolist()}")
 
 
+@pytest.mark.parametrize("kind", ["single", "swiglu"])
+def test_decode_two_fragments_per_wave(kind):
+    """Decode residual of a down / single projection with two 16-row
+    fragments per wave (taken at decode batch sizes when it allows more
+    k-chunks in one round: here 136 or 131 fragments per expert, 8 experts):
+    several k-chunks, the 4-step tail stage (d_in % 256 == 128) in the last
+    chunk, and for the single layer an odd fragment count (the last wave's
+    second fragment is computed but not stored)."""
+    ss = np.random.SeedSequence(2024 if kind == "single" else 2025).spawn(3)
+    if kind == "single":
+        proj = synth.make_proj(8, 2, 4, 4224, 2096, 32, 128, "f16", ss[0])
+        layer = dict(kind="single", act="f16", K=8, d_model=4224, d_ff=2096,
+                     proj=dict(single=proj), shared=None)
+        d_in = 4224
+    else:
+        proj = {n: synth.make_proj(8, 2, 4, di, do, 32, 128, "f16", q)
+                for (n, (di, do)), q in zip([("gate", (2176, 4224)), ("up", (2176, 4224)),
+                                             ("down", (4224, 2176))], ss)}
+        layer = dict(kind="swiglu", act="f16", K=8, d_model=2176, d_ff=4224, proj=proj, shared=None)
+        d_in = 2176
+    L = tqio.upload_layer(layer)
+    L.set_path(1)
+    for T, routing in [(40, "uniform"), (64, "hot70"), (3, "uniform")]:
+        x, ids, g = synth.make_custom_tokens(d_in, 8, 2, T, "f16", seed=T, routing=routing)
+        y, _ = run_forward(L, x, ids, g, "f16", "f32")
+        assert_parity(y, R.forward(layer, x, ids, g, keep_weights=False),
+                      what=f"two fragments per wave {kind} T={T} {routing}")
+    L.close()
+
+
 @pytest.mark.parametrize("act", ["f16", "bf16"])
 def test_decode_workspace_poisoned(act):
     """Decode batches (at most 16 slots per expert on average) on a workspace
