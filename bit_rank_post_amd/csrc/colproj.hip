@@ -37,9 +37,8 @@ namespace tq {
 //             over blockIdx.z into separate slabs.
 enum RgMode { RG_COL = 0, RG_DUAL = 1, RG_PLAIN = 2 };
 constexpr int RG_WAVES = 8;
-constexpr int RG_NSLOT = 4, RG_DEPTH = 3;
-constexpr int RG_A = 0;                          // [KS][8 frags][64 lanes] x 16 B, then
-                                                 // the activations, the same
+constexpr int RG_A = 0;                          // [KS][4 FA frags][64 lanes] x 16 B, then
+                                                 // the activations, [KS][8 frags][64 lanes]
 
 struct RgArgs {
   ColArgs c[2];                  // RG_COL: per projection (blockIdx.z)
@@ -49,22 +48,29 @@ struct RgArgs {
 };
 
 // KS: MFMA k-steps (32 inputs) per stage: 2 (32 KB slots, one workgroup per
-// CU) or 1 (16 KB slots, two workgroups per CU)
-template <typename T, int MODE, int KS>
+// CU) or 1 (16 KB slots, two workgroups per CU).  FA: weight fragments per
+// wave, 2 (a tile of 128 weight rows) or 4 (256 rows, dense modes: half the
+// LDS reads per MFMA; 48 KB slots, a ring of three).
+template <typename T, int MODE, int KS, int FA = 2>
 __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   typedef typename Vec8<T>::type V8;
+  static_assert(FA == 2 || (FA == 4 && MODE != RG_COL), "weight fragments per wave");
   constexpr int RG_KS = KS;
-  constexpr int RG_B = RG_KS * 8 * 1024;
-  constexpr int RG_BYTES = 2 * RG_KS * 8 * 1024;
-  constexpr int RG_NI = 2 * RG_KS * 8 / RG_WAVES;   // loads per wave per stage
+  constexpr int NFA = 4 * FA;                        // weight fragments of the tile
+  constexpr int RG_B = RG_KS * NFA * 1024;
+  constexpr int RG_BYTES = RG_KS * (NFA + 8) * 1024;
+  constexpr int RG_NI = RG_KS * (NFA + 8) / RG_WAVES;   // loads per wave per stage
   constexpr int SIN = 32 * KS;                       // inputs per stage
+  constexpr int RG_NSLOT = (3 * RG_BYTES > 96 * 1024) ? 3 : 4, RG_DEPTH = RG_NSLOT - 1;
+  static_assert(RG_NSLOT * RG_BYTES <= 150 * 1024, "LDS budget");
+  static_assert(RG_NI * RG_WAVES == RG_KS * (NFA + 8), "loads split evenly over the waves");
   __shared__ __attribute__((aligned(16))) char s0[RG_BYTES];
   __shared__ __attribute__((aligned(16))) char s1[RG_BYTES];
   __shared__ __attribute__((aligned(16))) char s2[RG_BYTES];
-  __shared__ __attribute__((aligned(16))) char s3[RG_BYTES];
+  __shared__ __attribute__((aligned(16))) char s3[RG_NSLOT > 3 ? RG_BYTES : 16];
   __shared__ int s_src[128];
   __shared__ int s_res;
-  char* const slot[RG_NSLOT] = {s0, s1, s2, s3};
+  char* const slot[4] = {s0, s1, s2, s3};
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
@@ -137,34 +143,36 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
       s_src[tid] = (n < n_end) ? n : -1;
     }
   }
-  // weight rows of this M tile: RG_DUAL 64 output rows (x2 matrices), else 128
-  const int m0 = blockIdx.y * (MODE == RG_DUAL ? 64 : 128);
+  // weight rows of this M tile: RG_DUAL 32 FA output rows (x2 matrices),
+  // else 64 FA
+  const int m0 = blockIdx.y * (MODE == RG_DUAL ? 32 * FA : 64 * FA);
   __syncthreads();
   const int nv = min(128, n_end - n0);
   // (uniform: the activation buffer resource lives in scalar registers)
   const int row_lo = __builtin_amdgcn_readfirstlane(s_src[0]);
   const int row_hi = __builtin_amdgcn_readfirstlane(s_src[max(nv - 1, 0)]);
 
-  // per-lane offsets of this wave's loads: load q = wave * NI + i; q < 8 KS:
-  // weight fragment (k-step q / 8, fragment q % 8), else activation fragment
+  // per-lane offsets of this wave's loads: load q = wave * NI + i; q < NFA
+  // KS: weight fragment (k-step q / NFA, fragment q % NFA), else activation
+  // fragment (k-step, fragment q % 8 of the rest)
   uint32_t vo[RG_NI];
   bool isw[RG_NI];
   int wsel[RG_NI], ks_of[RG_NI], fr_of[RG_NI];
 #pragma unroll
   for (int i = 0; i < RG_NI; ++i) {
     const int q = wave * RG_NI + i;
-    const bool w = q < 8 * RG_KS;
-    const int qq = w ? q : q - 8 * RG_KS;
-    const int ks = qq >> 3, f = qq & 7;
+    const bool w = q < NFA * RG_KS;
+    const int qq = w ? q : q - NFA * RG_KS;
+    const int ks = w ? qq / NFA : qq >> 3, f = w ? qq % NFA : qq & 7;
     isw[i] = w;
     ks_of[i] = ks;
     fr_of[i] = f;
     if (w) {
-      // weight row of fragment f
+      // weight row of fragment f (dual: the first half gate, the second up)
       int m;
       if (MODE == RG_DUAL) {
-        wsel[i] = f >> 2;
-        m = m0 + 16 * (f & 3) + l16;
+        wsel[i] = f / (NFA / 2);
+        m = m0 + 16 * (f % (NFA / 2)) + l16;
       } else {
         wsel[i] = 0;
         m = m0 + 16 * f + l16;
@@ -191,7 +199,8 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
     const int st = __builtin_amdgcn_readfirstlane(st0 + (live ? b : 0));   // a scalar offset
 #pragma unroll
     for (int i = 0; i < RG_NI; ++i) {
-      char* dst = base + (isw[i] ? RG_A : RG_B) + (ks_of[i] * 8 + fr_of[i]) * 1024;
+      char* dst = isw[i] ? base + RG_A + (ks_of[i] * NFA + fr_of[i]) * 1024
+                         : base + RG_B + (ks_of[i] * 8 + fr_of[i]) * 1024;
       if (isw[i]) {
         // k-step offset: blocked V^T layout moves by whole k-step blocks,
         // row-major weights by 128 bytes per stage
@@ -204,26 +213,29 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
     }
   };
 
-  f32x4 acc[2][4];
+  // wave (wm, wn): weight fragments wm + 4 i (i < FA) against activation
+  // fragments 4 wn + j (j < 4)
+  f32x4 acc[FA][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FA; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const char* base) {
 #pragma unroll
     for (int ks = 0; ks < RG_KS; ++ks) {
-      const V8 a0 = *reinterpret_cast<const V8*>(base + RG_A + (ks * 8 + wm) * 1024 + lane * 16);
-      const V8 a1 = *reinterpret_cast<const V8*>(base + RG_A + (ks * 8 + wm + 4) * 1024 + lane * 16);
+      V8 av[FA];
+#pragma unroll
+      for (int i = 0; i < FA; ++i)
+        av[i] = *reinterpret_cast<const V8*>(base + RG_A + (ks * NFA + wm + 4 * i) * 1024 + lane * 16);
       V8 b[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         b[j] = *reinterpret_cast<const V8*>(base + RG_B + (ks * 8 + 4 * wn + j) * 1024 + lane * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[0][j] = mfma16(a0, b[j], acc[0][j]);
-        acc[1][j] = mfma16(a1, b[j], acc[1][j]);
-      }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < FA; ++i) acc[i][j] = mfma16(av[i], b[j], acc[i][j]);
     }
   };
 
@@ -274,19 +286,23 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
         }
       }
     } else if constexpr (MODE == RG_DUAL) {
+      // gate fragment wm + 4 i pairs with up fragment wm + 4 i + NFA / 2
       const DenseArgs& a = args.d;
-      const int o = m0 + 16 * wm + 4 * lg;
-      if (o >= a.d_out) continue;
-      half_t hv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) hv[v] = (half_t)(silu_f(acc[0][j][v]) * acc[1][j][v]);
-      *reinterpret_cast<u32x2*>(reinterpret_cast<half_t*>(a.out_h) + (size_t)n * a.d_out + o) =
-          __builtin_bit_cast(u32x2, hv);
+      for (int i = 0; i < FA / 2; ++i) {
+        const int o = m0 + 16 * (wm + 4 * i) + 4 * lg;
+        if (o >= a.d_out) continue;
+        half_t hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) hv[v] = (half_t)(silu_f(acc[i][j][v]) * acc[i + FA / 2][j][v]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<half_t*>(a.out_h) + (size_t)n * a.d_out + o) =
+            __builtin_bit_cast(u32x2, hv);
+      }
     } else {
       const DenseArgs& a = args.d;
       float* out = a.out_f + (size_t)blockIdx.z * a.T * a.d_out;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < FA; ++i) {
         const int o = m0 + 16 * (wm + 4 * i) + 4 * lg;
         if (o >= a.d_out) continue;
         *reinterpret_cast<f32x4*>(out + (size_t)n * a.d_out + o) = acc[i][j];
@@ -324,12 +340,13 @@ void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s) {
   args.nsplit = dual ? 1 : nsplit;
   args.ntiles = (a.T + 127) / 128;
   const unsigned gx = (unsigned)(((args.ntiles + 7) / 8) * 8);
+  // 256 weight rows per workgroup (128 output rows of the dual gate/up)
   if (dual) {
-    const dim3 grid(gx, (a.d_out + 63) / 64, 1);
-    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_DUAL, 2>), grid, dim3(64 * RG_WAVES), 0, s, args);
+    const dim3 grid(gx, (a.d_out + 127) / 128, 1);
+    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_DUAL, 2, 4>), grid, dim3(64 * RG_WAVES), 0, s, args);
   } else {
-    const dim3 grid(gx, (a.d_out + 127) / 128, args.nsplit);
-    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_PLAIN, 2>), grid, dim3(64 * RG_WAVES), 0, s, args);
+    const dim3 grid(gx, (a.d_out + 255) / 256, args.nsplit);
+    hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_PLAIN, 2, 4>), grid, dim3(64 * RG_WAVES), 0, s, args);
   }
 }
 

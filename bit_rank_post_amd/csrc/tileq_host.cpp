@@ -332,11 +332,13 @@ Plan make_plan(const tq_layer* L, int T, int k, int path) {
   p.dres = take((size_t)p.nks * S * d_out_last * sizeof(float));
   p.nys = 1;
   if (L->shared.d_ff > 0) {
-    // shared down projection: k-splits until the grid has about one
-    // workgroup per CU, each split keeping at least 8 stages of 64 inputs
-    const long tiles = (long)(L->d_model / 128) * ((T + 127) / 128);
+    // shared down projection (256 output rows x 128 tokens per workgroup):
+    // k-splits until the grid has about one workgroup per CU, at most 4
+    // (each adds a T x d_model fp32 slab for the combine; more measured no
+    // faster), each split keeping at least 8 stages of 64 inputs
+    const long tiles = (long)((L->d_model + 255) / 256) * ((T + 127) / 128);
     const int nst = L->shared.d_ff / 64;
-    while (p.nys < 16 && tiles * p.nys * 2 <= device_cus() && nst / (2 * p.nys) >= 8) p.nys *= 2;
+    while (p.nys < 4 && tiles * p.nys * 2 <= device_cus() && nst / (2 * p.nys) >= 8) p.nys *= 2;
     p.hs = take((size_t)T * L->shared.d_ff * 2);
     p.ys = take((size_t)p.nys * T * L->d_model * sizeof(float));
   }
