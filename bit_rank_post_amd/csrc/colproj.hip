@@ -31,8 +31,12 @@ namespace tq {
 // 4 wn .. 4 wn + 3.
 //   RG_COL:   column stage, W = V_n^T of the row's segment (rank rows), out =
 //             Sigma-scaled rank vectors (fp32, or high/low parts).
-//   RG_DUAL:  dense SwiGLU input: fragments 0-3 from W0 (gate), 4-7 from W1
-//             (up) for the same 64 output rows; out = RND_act(silu(g) u).
+//   RG_DUAL:  dense SwiGLU input: the first half of the weight fragments
+//             from W0 (gate), the second from W1 (up) for the same output
+//             rows; out = RND_act(silu(g) u).
+// Weights of every mode are stored in k-step blocks ([d_in / 32][rows][32]:
+// V^T at upload, dense weights by launch_block_rows), so each fragment load
+// reads 1 KB of contiguous memory.
 //   RG_PLAIN: dense single projection, 128 output rows, fp32 out; split-K
 //             over blockIdx.z into separate slabs.
 enum RgMode { RG_COL = 0, RG_DUAL = 1, RG_PLAIN = 2 };
@@ -130,9 +134,10 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
     X = a.X;
     wbase[0] = reinterpret_cast<const char*>(a.W0);
     wbase[1] = reinterpret_cast<const char*>(MODE == RG_DUAL ? a.W1 : a.W0);
+    // k-step-blocked weights (launch_block_rows), like V^T above
     wbytes = (uint32_t)((size_t)M * d_in * 2);
-    wrs = (uint32_t)d_in * 2u;
-    wks = 64u;
+    wrs = 64u;
+    wks = (uint32_t)M * 64u;
     const int nst = d_in / SIN;
     // (uniform: the division may be done in vector registers)
     const int sps = __builtin_amdgcn_readfirstlane((nst + args.nsplit - 1) / args.nsplit);
@@ -177,9 +182,8 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
         wsel[i] = 0;
         m = m0 + 16 * f + l16;
       }
-      // blocked V^T: the k-step goes into the uniform offset
-      vo[i] = (m < M) ? (uint32_t)m * wrs + (MODE == RG_COL ? 0u : (uint32_t)ks * 64u) + lg * 16u
-                      : OOB;
+      // k-step-blocked weights: the k-step goes into the uniform offset
+      vo[i] = (m < M) ? (uint32_t)m * wrs + lg * 16u : OOB;
     } else {
       wsel[i] = 0;
       const int src = s_src[16 * f + l16];
@@ -202,10 +206,8 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
       char* dst = isw[i] ? base + RG_A + (ks_of[i] * NFA + fr_of[i]) * 1024
                          : base + RG_B + (ks_of[i] * 8 + fr_of[i]) * 1024;
       if (isw[i]) {
-        // k-step offset: blocked V^T layout moves by whole k-step blocks,
-        // row-major weights by 128 bytes per stage
-        const uint32_t so = (MODE == RG_COL) ? (uint32_t)(KS * st + ks_of[i]) * wks
-                                             : (uint32_t)st * (SIN * 2u);
+        // k-step offset: whole k-step blocks of the blocked weights
+        const uint32_t so = (uint32_t)(KS * st + ks_of[i]) * wks;
         dma16(wsel[i] ? rw[1] : rw[0], dst, live ? vo[i] : OOB, so);
       } else {
         dma16(rx, dst, live ? vo[i] : OOB, (uint32_t)st * (SIN * 2u));

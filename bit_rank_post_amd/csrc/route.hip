@@ -10,8 +10,9 @@
 //     computed once per pair, shared by every expert of column n the token
 //     routes to;
 //   * tile prefixes telling each GEMM / column-stage workgroup its segment.
-// Up to 64 tokens: one workgroup of 1024 threads; more: three launches over
-// 1024-slot workgroups.  Every list is unique and the result deterministic
+// Up to 1024 tokens (when S, T and the chunk-count table fit 4096 entries):
+// one workgroup of 1024 threads; more: three launches over 1024-slot
+// workgroups.  Every list is unique and the result deterministic
 // (ranks come from wave ballots, counts are integer sums).
 #include "route_body.h"
 
@@ -312,15 +313,21 @@ bool route_fits(const RouteArgs& a, int smax) {
 }
 
 void launch_route(const RouteArgs& a, hipStream_t s) {
-  if (a.T > 64 && a.K <= RM_KMAX && !a.arec) {
+  // one workgroup while every list fits its LDS and a thread holds at most
+  // one token (no global round trips between the phases, one launch);
+  // otherwise the three-launch path
+  if (a.T <= 1024 && route_fits(a, SMALL_S)) {
+    hipLaunchKernelGGL(route_kernel<SMALL_S>, dim3(1), dim3(1024), 0, s, a);
+  } else if (a.K <= RM_KMAX && !a.arec) {
     const int nb = (a.S + RM_NT - 1) / RM_NT;
     hipLaunchKernelGGL(route_count_kernel, dim3(nb), dim3(RM_NT), 0, s, a);
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(RM_NT), 0, s, a, nb);
     hipLaunchKernelGGL(route_place_kernel, dim3(nb), dim3(RM_NT), 0, s, a);
-  } else if (route_fits(a, SMALL_S))
+  } else if (route_fits(a, SMALL_S)) {
     hipLaunchKernelGGL(route_kernel<SMALL_S>, dim3(1), dim3(1024), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL(route_kernel<0>, dim3(1), dim3(1024), 0, s, a);
+  }
 }
 
 }  // namespace tq

@@ -214,6 +214,93 @@ __device__ void route_block(const RouteArgs& a, int* lds) {
     }
     return;
   }
+  if (SMALL && T <= NT) {
+    // one token per thread: per wave and grid column the number of the
+    // wave's tokens that reach the column (one ballot each), a prefix over
+    // (column, wave) in LDS, then every entry's index in one pass -- two
+    // barriers per projection instead of a block scan per column.  The
+    // chunk-count table is done with (phase C read it before the barrier).
+    static_assert(!SMALL || SMAX >= NW * 32 + 33, "LDS of the column lists");
+    int* s_wc = s_cntw;              // [NW][32] per-wave counts -> prefixes
+    int* s_cb = s_cntw + NW * 32;    // [33] column offsets
+    const int t = tid;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // grid column of every expert, both projections (s_seg: free after phase C)
+    int* s_nof = s_seg;              // [2][256]
+    __syncthreads();
+    for (int i = tid; i < a.ncol * 256; i += NT)
+      if ((i & 255) < K) s_nof[i] = a.n_of[i >> 8][i & 255];
+    for (int c = 0; c < a.ncol; ++c) {
+      const int N = a.N[c];
+      const int* n_of = s_nof + 256 * c;
+      __syncthreads();               // the tables, phase C's reads, or the last projection's
+      // grid column of each of the token's slots (-1: dropped id); the
+      // first 8 in registers, further ones re-read
+      unsigned m = 0u;
+      int nj[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        nj[j] = -1;
+        if (t < T && j < k) {
+          const int e = ids[t * k + j];
+          if (e >= 0 && e < K) nj[j] = n_of[e];
+        }
+        if (nj[j] >= 0) m |= 1u << nj[j];
+      }
+      for (int j = 8; t < T && j < k; ++j) {
+        const int e = ids[t * k + j];
+        if (e >= 0 && e < K) m |= 1u << n_of[e];
+      }
+      for (int n = 0; n < N; ++n) {
+        const uint64_t bb = __ballot((m >> n) & 1u);
+        if (lane == 0) s_wc[wave * 32 + n] = __popcll(bb);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane n < N: prefix of column n over the waves; then the column
+        // offsets and tile prefixes over the columns
+        int tot = 0;
+        if (lane < N)
+          for (int w = 0; w < NW; ++w) {
+            const int v = s_wc[w * 32 + lane];
+            s_wc[w * 32 + lane] = tot;
+            tot += v;
+          }
+        const int tl = (tot + a.rt_col - 1) / a.rt_col;
+        const int ic = wave_incl_scan_i(tot, lane), it = wave_incl_scan_i(tl, lane);
+        if (lane < N) {
+          s_cb[lane] = ic - tot;
+          a.col_off[c][lane] = ic - tot;
+          a.tile_col[c][lane] = it - tl;
+        }
+        if (lane == N - 1) {
+          a.col_off[c][N] = ic;
+          a.tile_col[c][N] = it;
+        }
+      }
+      __syncthreads();
+      for (int n = 0; n < N; ++n) {
+        const bool f = (m >> n) & 1u;
+        const uint64_t bb = __ballot(f);
+        if (!f) continue;
+        const int idx = s_cb[n] + s_wc[wave * 32 + n] + __popcll(bb & lt);
+        a.col_tok[c][idx] = t;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (nj[j] == n) a.slot2col[c][t * k + j] = idx;
+        for (int j = 8; j < k; ++j) {
+          const int e = ids[t * k + j];
+          if (e >= 0 && e < K && n_of[e] == n) a.slot2col[c][t * k + j] = idx;
+        }
+      }
+      // slots routed nowhere have no column entry
+      for (int q = tid; q < S; q += NT) {
+        const int e = ids[q];
+        if (!(e >= 0 && e < K)) a.slot2col[c][q] = -1;
+      }
+    }
+    return;
+  }
   const int tpt = (T + NT - 1) / NT;
   const int t0 = tid * tpt, t1 = min(T, t0 + tpt);
   for (int c = 0; c < a.ncol; ++c) {

@@ -731,9 +731,11 @@ tq_status tq_upload_shared_expert(tq_layer* L, int32_t d_ff_shared, const void* 
   SHCHK(hipMalloc(&sd.wg, n));
   SHCHK(hipMalloc(&sd.wu, n));
   SHCHK(hipMalloc(&sd.wd, n));
-  SHCHK(hipMemcpyAsync(sd.wg, wg, n, hipMemcpyDeviceToDevice, s));
-  SHCHK(hipMemcpyAsync(sd.wu, wu, n, hipMemcpyDeviceToDevice, s));
-  SHCHK(hipMemcpyAsync(sd.wd, wd, n, hipMemcpyDeviceToDevice, s));
+  // k-step-blocked copies (contiguous fragment loads in the dense GEMM)
+  launch_block_rows(wg, sd.wg, d_ff_shared, L->d_model, s);
+  launch_block_rows(wu, sd.wu, d_ff_shared, L->d_model, s);
+  launch_block_rows(wd, sd.wd, L->d_model, d_ff_shared, s);
+  SHCHK(hipGetLastError());
   SHCHK(hipStreamSynchronize(s));
   if (!L->side) SHCHK(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
   if (!L->fork_ev) SHCHK(hipEventCreateWithFlags(&L->fork_ev, hipEventDisableTiming));

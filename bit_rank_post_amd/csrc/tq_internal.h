@@ -246,7 +246,7 @@ void launch_combine(const CombineArgs& a, Act act, hipStream_t s);
 struct DenseArgs {
   int T, d_in, d_out;
   const void* X;                 // [T][d_in] f16
-  const void* W0;                // [d_out][d_in] f16
+  const void* W0;                // [d_in / 32][d_out][32] f16 (k-step blocks, launch_block_rows)
   const void* W1;                // second weight (dual SwiGLU) or nullptr
   void* out_h;                   // dual: [T][d_out] f16
   float* out_f;                  // single: [T][d_out] f32
@@ -283,6 +283,8 @@ void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStrea
 void launch_sigma_to_f32(const void* src, int f16, float* dst, int r, int r_pad, hipStream_t s);
 void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_pad,
                         hipStream_t s);
+// row-major f16 [rows][d_in] (d_in % 32 == 0) -> k-step blocks [d_in / 32][rows][32]
+void launch_block_rows(const void* W, void* dst, int rows, int d_in, hipStream_t s);
 void launch_debug_dequant(const ProjDev& p, int expert, void* w_out, hipStream_t s);
 
 // ---- offline packer (pack.hip) -----------------------------------------------

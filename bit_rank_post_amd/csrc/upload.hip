@@ -218,6 +218,33 @@ void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_
                      d_in, r, r_pad);
 }
 
+// Dense weight rows re-laid-out in k-step blocks: block s holds inputs
+// 32 s .. 32 s + 31 of every row, 64 contiguous bytes per row, so that a
+// 16-row MFMA fragment of one k-step is one contiguous 1 KB load and a tile
+// of consecutive rows reads one contiguous range per k-step (a row-major
+// matrix would give 64-byte pieces 2 d_in bytes apart).  One thread per
+// 16-byte chunk of the output.
+__global__ void block_rows_kernel(const uint4* __restrict__ W, uint4* __restrict__ dst, int rows,
+                                  int d_in) {
+  const size_t total = (size_t)rows * (d_in >> 3);
+  const int cpr = d_in >> 3;                     // 16-byte chunks per row
+  for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(o & 3);
+    const size_t q = o >> 2;
+    const int m = (int)(q % rows);
+    const int st = (int)(q / rows);
+    dst[o] = W[(size_t)m * cpr + st * 4 + c];
+  }
+}
+
+void launch_block_rows(const void* W, void* dst, int rows, int d_in, hipStream_t s) {
+  const size_t total = (size_t)rows * (d_in >> 3);
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(block_rows_kernel, dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(W), reinterpret_cast<uint4*>(dst), rows, d_in);
+}
+
 // Bound on the effective weight's rows, W_e = U_m Sigma V_n^T + R_e (the
 // tiled decomposition of section 2.1): for every expert, an upper bound on
 // max_o sum_i |W_e[o][i]| by the triangle inequality,

@@ -137,7 +137,8 @@ tq_status tq_upload_proj(tq_layer *L, int32_t which, const tq_proj_desc *d, void
 /* Optional dense shared expert, added to every token with weight 1 (SWIGLU
  * layers with act = TQ_F16 only): wg, wu DEVICE f16 [d_ff_shared][d_model],
  * wd DEVICE f16 [d_model][d_ff_shared]; d_ff_shared % 128 == 0.  Copied like
- * tq_upload_proj.  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EUNSUPPORTED, TQ_ENOMEM, TQ_EHIP. */
+ * tq_upload_proj (re-laid-out in blocks of 32 inputs per row; the call
+ * synchronizes `stream`, after which the caller may free its arrays).  Errors: TQ_EINVAL, TQ_ESHAPE, TQ_EUNSUPPORTED, TQ_ENOMEM, TQ_EHIP. */
 tq_status tq_upload_shared_expert(tq_layer *L, int32_t d_ff_shared, const void *wg,
                                   const void *wu, const void *wd, void *stream);
 

@@ -220,6 +220,13 @@ def test_route_bitexact_cases():
     _, ids, _ = synth.make_tokens(cfg, 4160)                           # Zipf(1.1) top-6
     check_route_device(L64, p64, ids)
     check_route_device(L64, p64, rng.integers(0, 64, (1, 6)))
+    # one-workgroup lists at the largest token count it takes, and a
+    # Qwen-shaped batch (60 experts on 8 x 8, top-4, 512 tokens)
+    check_route_device(L8, p8, rng.integers(0, 8, (1024, 4)))
+    L60, p60 = route_layer(60, 8, 8, 13)
+    qcfg = synth.CONFIG_BY_NAME["qwen15_moe_prefill512"]
+    _, qids, _ = synth.make_tokens(qcfg, 512)
+    check_route_device(L60, p60, qids)
 
 
 def test_dropped_ids_counted():
