@@ -367,6 +367,39 @@ def measure(workload, steps, warmup, copies, scheme="tileq", log=None, keep=None
     return rec, (layer, x, ids, gates)
 
 
+def attainable_read(nbytes, copies=4, iters=40):
+    """GB/s of a plain streaming read of nbytes (tq_calibrate_read: 16-byte
+    loads over the whole grid), over `copies` buffers in rotation so that the
+    Infinity Cache cannot serve them: the read rate this device attains, the
+    practical ceiling beside the nominal HBM peak."""
+    import torch
+    import bit_rank_post_amd as tq
+    nbytes = (int(nbytes) + 15) // 16 * 16
+    bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(copies)]
+    scratch = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(2 * copies):
+        tq.calibrate_read(bufs[i % copies], scratch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        tq.calibrate_read(bufs[i % copies], scratch)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / iters
+    del bufs
+    return {"GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "us_per_read": round(us, 2),
+            "bytes": nbytes,
+            "how": f"plain streaming read of the kernel's algorithmic bytes (tq_calibrate_read, "
+                   f"{copies} buffers rotated), mean of {iters} launches"}
+
+
+def with_attainable(roof, cal):
+    """The roofline dict with the attainable-read rate and the fraction of it."""
+    r = dict(roof)
+    r["attainable"] = dict(cal, frac=round(roof["achieved"] / cal["GBps"], 4))
+    return r
+
+
 def bench_pack(steps, warmup):
     """The offline packer on the Mixtral-shaped gate projection: 8 experts on
     the 2 x 4 grid, d_out 14336, d_in 4096, rank 64 with a sketch of 72
@@ -468,6 +501,12 @@ def main():
     for L in keep.get("Ls", []):
         L.close()
     keep.clear()
+    if rec["roofline"]["bound"] == "hbm":
+        rec["roofline"] = with_attainable(rec["roofline"],
+                                          attainable_read(rec["roofline"]["algorithmic_bytes_per_launch"]))
+        for b in (batches or {}).values():
+            b["roofline"] = with_attainable(
+                b["roofline"], attainable_read(b["roofline"]["algorithmic_bytes_per_launch"]))
 
     if args.calibrate_copy:
         # one elementwise kernel of known traffic (reads 256 MiB, writes

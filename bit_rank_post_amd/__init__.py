@@ -25,7 +25,8 @@ STATUS = {0: "TQ_OK", 1: "TQ_EINVAL", 2: "TQ_ESHAPE", 3: "TQ_ENOMEM", 4: "TQ_EHI
 EXPORTS = ["tq_layer_create", "tq_upload_proj", "tq_upload_shared_expert",
            "tq_workspace_size", "tq_forward", "tq_forward_from_logits", "tq_forward_noalloc", "tq_layer_destroy", "tq_last_error",
            "tq_abi_version", "tq_layer_set_path", "tq_forward_path", "tq_debug_route", "tq_debug_dequant", "tq_debug_row_bound", "tq_router_topk",
-           "tq_profile_enable", "tq_profile_read", "tq_pack_workspace_size", "tq_pack_proj"]
+           "tq_profile_enable", "tq_profile_read", "tq_pack_workspace_size", "tq_pack_proj",
+           "tq_calibrate_read"]
 STAGES = ["route", "row_exponent", "column_stage_in", "gemm_in", "column_stage_down",
           "shared_expert", "gemm_down", "combine"]
 
@@ -91,6 +92,7 @@ def lib():
         L.tq_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.tq_profile_enable.argtypes = [vp, i32]
         L.tq_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_float)]
+        L.tq_calibrate_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
         L.tq_pack_workspace_size.argtypes = [ctypes.POINTER(PackDesc), ctypes.POINTER(sz)]
         L.tq_pack_proj.argtypes = [ctypes.POINTER(PackDesc), vp, sz, vp]
         for name in EXPORTS:
@@ -116,6 +118,13 @@ def _stream(stream):
         import torch
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+
+
+def calibrate_read(buf, scratch, stream=None):
+    """One plain streaming read of the device tensor buf (benchmark
+    calibration); scratch is a device int32 tensor of at least one element."""
+    _check("tq_calibrate_read", lib().tq_calibrate_read(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(scratch), _stream(stream)))
 
 
 def router_topk(logits, k, ids, weights, stream=None):

@@ -25,7 +25,7 @@ SOURCES = [("route.hip", "route", []), ("colproj.hip", "colproj", []),
            ("gemm_prefill.hip", "gemm_prefill3", ["-DTQ_PREFILL_BITS=3"]),
            ("gemm_decode.hip", "gemm_decode", []), ("decode_stages.hip", "decode_stages", []),
            ("combine.hip", "combine", []), ("upload.hip", "upload", []),
-           ("router.hip", "router", []), ("pack.hip", "pack", []),
+           ("router.hip", "router", []), ("pack.hip", "pack", []), ("calib.hip", "calib", []),
            ("tileq_host.cpp", "tileq_host", [])]
 
 

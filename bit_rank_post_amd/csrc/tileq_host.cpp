@@ -1178,6 +1178,15 @@ tq_status tq_profile_read(const tq_layer* L, float* stage_ms) {
   return TQ_OK;
 }
 
+tq_status tq_calibrate_read(const void* buf, size_t bytes, uint32_t* scratch, void* stream) {
+  if (!buf || !scratch) return fail(TQ_EINVAL, "NULL argument");
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) || (bytes & 15))
+    return fail(TQ_EINVAL, "buf and bytes must be multiples of 16");
+  launch_stream_read(buf, bytes, scratch, reinterpret_cast<hipStream_t>(stream));
+  HIPCHK(hipGetLastError());
+  return TQ_OK;
+}
+
 tq_status tq_layer_destroy(tq_layer* L) {
   if (!L) return TQ_OK;
   (void)hipDeviceSynchronize();

@@ -283,6 +283,8 @@ void launch_pad_u(const void* U, void* dst, int rows, int r, int r_pad, hipStrea
 void launch_sigma_to_f32(const void* src, int f16, float* dst, int r, int r_pad, hipStream_t s);
 void launch_transpose_v(const void* V, void* dst, int N, int d_in, int r, int r_pad,
                         hipStream_t s);
+// benchmark calibration: one plain streaming read of bytes (a multiple of 16)
+void launch_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t s);
 // row-major f16 [rows][d_in] (d_in % 32 == 0) -> k-step blocks [d_in / 32][rows][32]
 void launch_block_rows(const void* W, void* dst, int rows, int d_in, hipStream_t s);
 void launch_debug_dequant(const ProjDev& p, int expert, void* w_out, hipStream_t s);

@@ -334,6 +334,15 @@ tq_status tq_debug_row_bound(const tq_layer *L, int32_t which, float *l1_out);
 tq_status tq_profile_enable(tq_layer *L, int32_t on);
 tq_status tq_profile_read(const tq_layer *L, float *stage_ms);
 
+/* Benchmark calibration, not part of the method: enqueue on `stream` one
+ * plain streaming read of `bytes` bytes of DEVICE memory at `buf` (16-byte
+ * loads over the whole grid; nothing is written in practice: `scratch` is a
+ * DEVICE uint32 that the kernel may write only for one fixed data pattern).
+ * Timing such launches gives the read bandwidth the device attains, the
+ * practical ceiling beside the nominal HBM peak.
+ * Errors: TQ_EINVAL (NULL pointer, buf or bytes not a multiple of 16), TQ_EHIP. */
+tq_status tq_calibrate_read(const void *buf, size_t bytes, uint32_t *scratch, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -172,3 +172,12 @@ def test_pack_workspace_grows_with_sketch(L):
                                         (0, 8, 2, 0)])
 def test_router_validation(L, T, K, k, code):
     assert L.tq_router_topk(FAKE, T, K, k, FAKE, FAKE, None) == code, L.tq_last_error()
+
+
+def test_calibrate_read_validation(L):
+    scratch = ctypes.c_void_p(0x2000)
+    assert L.tq_calibrate_read(None, 64, scratch, None) == 1
+    assert L.tq_calibrate_read(FAKE, 64, None, None) == 1
+    assert L.tq_calibrate_read(ctypes.c_void_p(0x1008), 64, scratch, None) == 1
+    assert L.tq_calibrate_read(FAKE, 60, scratch, None) == 1
+    assert b"multiples of 16" in L.tq_last_error()
