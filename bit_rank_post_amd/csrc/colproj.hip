@@ -49,6 +49,7 @@ struct RgArgs {
   DenseArgs d;                   // RG_DUAL / RG_PLAIN
   int nsplit;                    // RG_PLAIN: k-splits (blockIdx.z), slab stride T * d_out
   int ntiles;                    // row tiles of the grid (before the XCD remap)
+  int nwt;                       // RG_DUAL / RG_PLAIN: weight tiles
 };
 
 // KS: MFMA k-steps (32 inputs) per stage: 2 (32 KB slots, one workgroup per
@@ -80,10 +81,30 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int wm = wave & 3, wn = wave >> 2;
 
-  // row tile: consecutive tiles on one XCD (workgroup W runs on XCD W mod 8),
-  // so the workgroups of one segment share its weights in that XCD's L2
-  const int per = (args.ntiles + 7) >> 3;
-  const int tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  // Workgroup W runs on XCD W mod 8.  Column stage: consecutive row tiles on
+  // one XCD, so the workgroups of one segment share its weights in that
+  // XCD's L2.  Dense modes (1D grid): the row tiles of one weight tile on
+  // one XCD (its weights come from HBM once into that L2), the weight tiles
+  // dealt to the 8 XCDs in turn, so every XCD gets an equal share even when
+  // there are fewer row tiles than XCDs.
+  int tile, wtile;
+  if constexpr (MODE == RG_COL) {
+    // the routed tile count (the last tile prefix; the grid covers the
+    // bound args.ntiles): each XCD takes an equal run of the routed tiles
+    const int* toff = blockIdx.z ? args.c[1].tile_off : args.c[0].tile_off;
+    const int nseg = blockIdx.z ? args.c[1].nseg : args.c[0].nseg;
+    const int ntot = min(args.ntiles, sload(toff, nseg));
+    const int per = (ntot + 7) >> 3;
+    if ((int)(blockIdx.x >> 3) >= per) return;
+    tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    wtile = blockIdx.y;
+    if (tile >= ntot) return;
+  } else {
+    const int j = blockIdx.x >> 3;
+    tile = j % args.ntiles;
+    wtile = (j / args.ntiles) * 8 + (blockIdx.x & 7);
+    if (wtile >= args.nwt) return;
+  }
   if (tile >= args.ntiles) return;
 
   int n0, n_end, d_in, M, lda;
@@ -150,7 +171,7 @@ __global__ __launch_bounds__(64 * RG_WAVES) void rowgemm_kernel(RgArgs args) {
   }
   // weight rows of this M tile: RG_DUAL 32 FA output rows (x2 matrices),
   // else 64 FA
-  const int m0 = blockIdx.y * (MODE == RG_DUAL ? 32 * FA : 64 * FA);
+  const int m0 = wtile * (MODE == RG_DUAL ? 32 * FA : 64 * FA);
   __syncthreads();
   const int nv = min(128, n_end - n0);
   // (uniform: the activation buffer resource lives in scalar registers)
@@ -341,13 +362,14 @@ void launch_dense(const DenseArgs& a, int dual, int nsplit, hipStream_t s) {
   args.d = a;
   args.nsplit = dual ? 1 : nsplit;
   args.ntiles = (a.T + 127) / 128;
-  const unsigned gx = (unsigned)(((args.ntiles + 7) / 8) * 8);
   // 256 weight rows per workgroup (128 output rows of the dual gate/up)
   if (dual) {
-    const dim3 grid(gx, (a.d_out + 127) / 128, 1);
+    args.nwt = (a.d_out + 127) / 128;
+    const dim3 grid(8 * args.ntiles * ((args.nwt + 7) / 8), 1, 1);
     hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_DUAL, 2, 4>), grid, dim3(64 * RG_WAVES), 0, s, args);
   } else {
-    const dim3 grid(gx, (a.d_out + 255) / 256, args.nsplit);
+    args.nwt = (a.d_out + 255) / 256;
+    const dim3 grid(8 * args.ntiles * ((args.nwt + 7) / 8), 1, args.nsplit);
     hipLaunchKernelGGL((rowgemm_kernel<half_t, RG_PLAIN, 2, 4>), grid, dim3(64 * RG_WAVES), 0, s, args);
   }
 }
