@@ -90,26 +90,39 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pre_kernel(GemmArgs a) {
   const int nrb = a.d_out >> 4;
   const int rows_per_wg = 16 * RF * PF_WAVES;
   const int nrt = (a.d_out + rows_per_wg - 1) / rows_per_wg;
-  // Workgroup -> (row tile rt, slot-tile unit tq).  Work items are ordered
-  // by super-blocks of SBR row tiles x SBC slot tiles (item i: super-block
-  // i / (SBR SBC), row tile fastest inside it); super-blocks step over the
-  // row tiles first.  Workgroup W runs on XCD W mod 8 and is the (W / 8)-th
-  // of its XCD; each XCD takes an equal run of consecutive items of the
-  // routed tiles (the grid covers the bound a.ntq), so the workgroups that
-  // run together on one XCD share a super-block's codes (per row tile) and
-  // activations (per slot tile) through its L2, and every XCD gets the same
-  // number of items however few super-blocks the routing produced.
+  // Workgroup -> (row tile rt, slot-tile unit tq).  Items are grouped in
+  // super-blocks of SBR row tiles x SBC slot tiles (row tile fastest inside
+  // one; super-blocks step over the row tiles first); the 32 workgroups of a
+  // super-block run together on one XCD, on the same stage order, so each
+  // stage's codes (per row tile) and activations (per slot tile) come from
+  // HBM once per XCD and are shared through its L2.  Workgroup W runs on XCD
+  // W mod 8.  When the routed tiles (the grid covers the bound a.ntq) make
+  // at least four super-blocks per XCD, they are dealt to the XCDs in turn
+  // (all XCDs then work on neighbouring super-blocks at any time); with
+  // fewer, each XCD takes an equal run of consecutive items in whole
+  // slot-tile columns, so that no XCD idles while another works on one more
+  // super-block (the 512-token Qwen-shaped batch makes 12).
   int sbr, sbc;
   pf_superblock(nrt, &sbr, &sbc);
   const int nrtb = (nrt + sbr - 1) / sbr;
   const int nreal = min(a.ntq, sload(a.tile_off, a.K) << (a.tile_half ? 1 : 0));
-  const int nitems = nrtb * ((nreal + sbc - 1) / sbc) * (sbr * sbc);
-  const int per = (nitems + 7) >> 3;
+  const int nsb = nrtb * ((nreal + sbc - 1) / sbc);
   const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
-  if (li >= per) return;
-  const int item = xcd * per + li;
-  if (item >= nitems) return;
-  const int sb = item / (sbr * sbc), within = item - sb * (sbr * sbc);
+  int sb, within;
+  if (nsb >= 32) {
+    const int sbl = li / (sbr * sbc);
+    within = li - sbl * (sbr * sbc);
+    sb = sbl * 8 + xcd;
+    if (sb >= nsb) return;
+  } else {
+    const int nitems = nsb * (sbr * sbc);
+    const int per = ((((nitems + 7) >> 3) + sbr - 1) / sbr) * sbr;
+    if (li >= per) return;
+    const int item = xcd * per + li;
+    if (item >= nitems) return;
+    sb = item / (sbr * sbc);
+    within = item - sb * (sbr * sbc);
+  }
   const int rt = (sb % nrtb) * sbr + within % sbr;
   const int tq = (sb / nrtb) * sbc + within / sbr;
   if (rt >= nrt || tq >= nreal) return;
