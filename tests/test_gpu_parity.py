@@ -600,6 +600,20 @@ def test_small_swiglu_with_shared_expert(path, T):
     assert_parity(y, R.forward(layer, x, ids, g), what=f"swiglu + shared path={path} T={T}")
 
 
+@pytest.mark.parametrize("path,T", [(1, 40), (2, 200)])
+def test_shared_expert_partial_tiles(path, T):
+    """Dense shared expert whose down projection ends in a partial 256-row
+    weight tile (d_model 384), 5 dual weight tiles dealt over the 8 XCDs,
+    and a ragged last 128-token tile."""
+    layer = small_swiglu("f16", 21, d_model=384)
+    layer["shared"] = synth.make_shared(384, 640, np.random.SeedSequence(22))
+    L = tqio.upload_layer(layer)
+    L.set_path(path)
+    x, ids, g = synth.make_custom_tokens(384, 8, 2, T, "f16", seed=T + 3)
+    y, _ = run_forward(L, x, ids, g, "f16", "f32")
+    assert_parity(y, R.forward(layer, x, ids, g), what=f"shared partial tiles path={path} T={T}")
+
+
 def test_qwen15_prefill512_with_shared_expert():
     cfg = synth.CONFIG_BY_NAME["qwen15_moe_prefill512"]
     layer = synth.make_layer(cfg)
