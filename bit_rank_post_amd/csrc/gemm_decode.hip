@@ -121,6 +121,17 @@ template <typename T, int MODE, int GS, int WAVES, int DMAX, int BITS, int NCT>
 __global__ __launch_bounds__(64 * WAVES, (dec_dual_cfg<MODE, GS, WAVES, BITS, NCT>() ? 4 : 1))
 void gemm_dec_kernel(DecArgs a) {
   typedef typename Vec8<T>::type V8;
+  // The kernel arguments read before the first stage, requested together:
+  // the empty asm needs them all in scalar registers, so their loads go out
+  // at once with one wait, instead of one round trip per use site.
+  asm volatile("" ::"s"(a.K), "s"(a.d_in), "s"(a.d_out), "s"(a.rows_per), "s"(a.nks),
+               "s"(a.spec), "s"(a.arec), "s"(a.etab), "s"(a.S), "s"(a.off), "s"(a.cnt));
+  asm volatile("" ::"s"(a.p[0].ng), "s"(a.p[0].codes), "s"(a.p[0].sz), "s"(a.p[0].rank),
+               "s"(a.p[0].m_of), "s"(a.p[0].n_of), "s"(a.P[0]), "s"(a.Xp), "s"(a.rows),
+               "s"(a.sums), "s"(a.gather), "s"(a.topk), "s"(a.ex));
+  if constexpr (dec_np<MODE>() > 1)
+    asm volatile("" ::"s"(a.p[1].codes), "s"(a.p[1].sz), "s"(a.p[1].rank), "s"(a.p[1].m_of),
+                 "s"(a.p[1].n_of), "s"(a.P[1]));
   constexpr int NP = dec_np<MODE>();
   constexpr bool PAIR = MODE == MODE_RES2;   // the NP "projections" are two row fragments
   constexpr int NPG = PAIR ? 1 : NP;         // projections whose Sigma p the row stage gathers
@@ -315,12 +326,17 @@ void gemm_dec_kernel(DecArgs a) {
     offe = sload(a.off, e);
   }
   const int sl_first = rec ? sload16(rec + 4, 0, l16) : sload16(etab, 0, l16);
+  // (the tile row / column loads are unconditional -- every uploaded
+  // projection has its maps -- so that all of these go out together
+  // instead of behind a branch each)
   int m_e[NP], n_e[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
+    const ProjDev& pm = a.p[PAIR ? 0 : p];
     const bool lr = a.P[p] != nullptr && a.p[p].rank > 0;
-    m_e[p] = lr ? sload(a.p[p].m_of, e) : 0;
-    n_e[p] = lr ? sload(a.p[p].n_of, e) : 0;
+    const int mv = sload(pm.m_of, e), nv = sload(pm.n_of, e);
+    m_e[p] = lr ? mv : 0;
+    n_e[p] = lr ? nv : 0;
   }
   if (cnt == 0) {
     wait_vm<0>();                          // no load may land after the workgroup ends
